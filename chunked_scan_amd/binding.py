@@ -1,0 +1,231 @@
+"""ctypes binding of liblachunk.so (C ABI in include/la_chunk.h).
+
+Argument marshalling only: tensors are checked (device, dtype, layout, shape), outputs are
+allocated when not given, the ``la_shape`` struct is filled in, and the call is enqueued on the
+current torch stream.  Every step of the computation runs in the HIP kernels of the library;
+there is no CPU or PyTorch fallback, and calling any function without the built library raises.
+
+Per-segment state arrays ([B,H,P,dk,dv]) and segment-total arrays ([B,H,P,dk]) may be strided
+views whose (b,h) blocks are evenly spaced -- e.g. slot 1 of a [B,H,2,dk,dv] scan buffer -- and
+are passed as a base pointer plus the ``state_stride`` / ``total_stride`` of the C ABI.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblachunk.so")
+
+LA_F32, LA_BF16 = 0, 1
+MODES = {"none": 0, "head": 1, "gate": 2}
+STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_SHAPE", -3: "LA_ERR_DTYPE", -4: "LA_ERR_ALIAS",
+          -5: "LA_ERR_UNSUPPORTED", -6: "LA_ERR_LAUNCH", -7: "LA_ERR_DECAY"}
+EXPORTS = ("la_chunk_fwd", "la_state_scan", "la_state_correct", "la_cumdecay", "la_status_str",
+           "la_supported", "la_version")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("L", ctypes.c_int64),
+        ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("nseg", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("decay_mode", ctypes.c_int32),
+        ("gate_norm", ctypes.c_float), ("seg_begin", ctypes.c_int32), ("state_stride", ctypes.c_int64),
+        ("total_stride", ctypes.c_int64), ("subseg_chunks", ctypes.c_int32), ("stream", ctypes.c_void_p),
+    ]
+
+
+class LaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblachunk.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                               "g.build()'` (hipcc, gfx950). There is no fallback path.")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.c_void_p, ctypes.POINTER(Shape)
+        L.la_chunk_fwd.argtypes = [P, P, P, P, P, P, P, S, ctypes.c_int32]
+        L.la_state_scan.argtypes = [P, P, ctypes.c_int32, P, S]
+        L.la_state_correct.argtypes = [P, P, P, P, S]
+        L.la_cumdecay.argtypes = [P, P, P, S]
+        L.la_supported.argtypes = [S, ctypes.c_int32]
+        L.la_status_str.argtypes = [ctypes.c_int]
+        L.la_status_str.restype = ctypes.c_char_p
+        for f in (L.la_chunk_fwd, L.la_state_scan, L.la_state_correct, L.la_cumdecay, L.la_supported,
+                  L.la_version):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise LaError(fn, status, lib().la_status_str(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None, contiguous=True):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _bh_stride(t: torch.Tensor, name: str, inner: int) -> int:
+    """Stride between (b,h) blocks of a [B,H,P,...] view whose per-(b,h) block of P*inner
+    elements is dense and whose (b,h) blocks are evenly spaced; 0 when the whole view is dense."""
+    if t.is_contiguous():
+        return 0
+    B, H, P = t.shape[:3]
+    dense_tail = list(torch.empty(t.shape[2:], device="meta").stride())
+    if list(t.stride()[2:]) != dense_tail:
+        raise ValueError(f"{name}: each (b,h) block must be dense")
+    s1 = t.stride(1) if H > 1 else t.stride(0) // max(H, 1)
+    if B > 1 and t.stride(0) != H * s1:
+        raise ValueError(f"{name}: (b,h) blocks must be evenly spaced")
+    if s1 < P * inner:
+        raise ValueError(f"{name}: (b,h) blocks overlap")
+    return s1
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LA_F32
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def mode_code(mode: Optional[str], decay: Optional[torch.Tensor]) -> int:
+    if mode is None:
+        mode = "none" if decay is None else ("head" if decay.dim() == 1 else "gate")
+    return MODES[mode]
+
+
+def make_shape(B, H, L, dk, dv, *, nseg=1, dtype=LA_BF16, mode=0, gate_norm=16.0, seg_begin=0,
+               state_stride=0, total_stride=0, subseg_chunks=0, stream=None) -> Shape:
+    return Shape(B, H, L, dk, dv, nseg, dtype, dtype, mode, gate_norm, seg_begin, state_stride,
+                 total_stride, subseg_chunks, stream)
+
+
+def la_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch.Tensor] = None,
+                 s_in: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                 s_out: Optional[torch.Tensor] = None, *, mode: Optional[str] = None, nseg: int = 1,
+                 chunk: int = 64, gate_norm: float = 16.0, subseg_chunks: int = 0, want_state: bool = True,
+                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise forward.  q, k [B,H,L,dk], v [B,H,L,dv] (f32 or bf16); decay None / [H] / [B,H,L,dk];
+    s_in [B,H,dk,dv] f32 or None.  Returns (o [B,H,L,dv], s_out [B,H,nseg,dk,dv] f32 or None);
+    s_out may be a view with evenly spaced dense (b,h) blocks."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    _dev(q, "q")
+    _dev(k, "k", q.dtype, (B, H, L, dk))
+    _dev(v, "v", q.dtype, (B, H, L, dv))
+    m = mode_code(mode, decay)
+    if decay is not None:
+        _dev(decay, "decay", torch.float32)
+    if s_in is not None:
+        _dev(s_in, "s_in", torch.float32, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    _dev(o, "o", q.dtype, (B, H, L, dv))
+    if s_out is None and want_state:
+        s_out = torch.empty((B, H, nseg, dk, dv), dtype=torch.float32, device=q.device)
+    stride = 0
+    if s_out is not None:
+        _dev(s_out, "s_out", torch.float32, (B, H, nseg, dk, dv), contiguous=False)
+        stride = _bh_stride(s_out, "s_out", dk * dv)
+    shp = make_shape(B, H, L, dk, dv, nseg=nseg, dtype=_dtype_code(q), mode=m, gate_norm=gate_norm,
+                     state_stride=stride, subseg_chunks=subseg_chunks, stream=_stream(stream))
+    _check("la_chunk_fwd", lib().la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(o),
+                                              _ptr(s_out), ctypes.byref(shp), chunk))
+    return o, s_out
+
+
+def la_state_scan(seg_states: torch.Tensor, seg_decay: torch.Tensor, out_states: Optional[torch.Tensor] = None,
+                  *, stream=None) -> torch.Tensor:
+    """Inclusive scan over axis 2: seg_states [B,H,P,dk,dv] f32, seg_decay [B,H,P,dk] f32 (dense).
+    out_states may be seg_states itself (in place)."""
+    B, H, P, dk, dv = seg_states.shape
+    _dev(seg_states, "seg_states", torch.float32)
+    _dev(seg_decay, "seg_decay", torch.float32, (B, H, P, dk))
+    if out_states is None:
+        out_states = torch.empty_like(seg_states)
+    _dev(out_states, "out_states", torch.float32, (B, H, P, dk, dv))
+    shp = make_shape(B, H, 0, dk, dv, stream=_stream(stream))
+    _check("la_state_scan", lib().la_state_scan(_ptr(seg_states), _ptr(seg_decay), P, _ptr(out_states),
+                                                ctypes.byref(shp)))
+    return out_states
+
+
+def la_state_correct(q: torch.Tensor, cumdecay: Optional[torch.Tensor], s_recv: torch.Tensor, o: torch.Tensor, *,
+                     mode: Optional[str] = None, nseg: int = 1, seg_begin: int = 0, stream=None) -> torch.Tensor:
+    """o += (q * cum) @ s_recv[p - seg_begin] for segments p >= seg_begin, in place.
+    cumdecay: None (none), [H] log-decay (head) or [B,H,L,dk] cumulative decay (gate).
+    s_recv: f32 [B,H,nseg-seg_begin,dk,dv], possibly a view with evenly spaced dense (b,h) blocks."""
+    B, H, L, dk = q.shape
+    dv = o.shape[-1]
+    _dev(q, "q")
+    _dev(o, "o", q.dtype, (B, H, L, dv))
+    if cumdecay is not None:
+        _dev(cumdecay, "cumdecay", torch.float32)
+    m = mode_code(mode, cumdecay)
+    np_ = nseg - seg_begin
+    _dev(s_recv, "s_recv", torch.float32, (B, H, np_, dk, dv), contiguous=False)
+    stride = _bh_stride(s_recv, "s_recv", dk * dv)
+    shp = make_shape(B, H, L, dk, dv, nseg=nseg, dtype=_dtype_code(q), mode=m, seg_begin=seg_begin,
+                     state_stride=stride, stream=_stream(stream))
+    _check("la_state_correct", lib().la_state_correct(_ptr(q), _ptr(cumdecay), _ptr(s_recv), _ptr(o),
+                                                      ctypes.byref(shp)))
+    return o
+
+
+def la_cumdecay(decay: Optional[torch.Tensor], B: int, H: int, L: int, dk: int, *, mode: Optional[str] = None,
+                nseg: int = 1, gate_norm: float = 16.0, cum: Optional[torch.Tensor] = None,
+                total: Optional[torch.Tensor] = None, want_cum: bool = True, want_total: bool = True,
+                device=None, stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Returns (cumdecay [B,H,L,dk] or None, total [B,H,nseg,dk] or None), both f32.  total may be a
+    view with evenly spaced dense (b,h) blocks."""
+    m = mode_code(mode, decay)
+    dev = decay.device if decay is not None else (device or torch.device("cuda"))
+    if decay is not None:
+        _dev(decay, "decay", torch.float32)
+    if cum is None and want_cum:
+        cum = torch.empty((B, H, L, dk), dtype=torch.float32, device=dev)
+    if cum is not None:
+        _dev(cum, "cum", torch.float32, (B, H, L, dk))
+    if total is None and want_total:
+        total = torch.empty((B, H, nseg, dk), dtype=torch.float32, device=dev)
+    tstride = 0
+    if total is not None:
+        _dev(total, "total", torch.float32, (B, H, nseg, dk), contiguous=False)
+        tstride = _bh_stride(total, "total", dk)
+    shp = make_shape(B, H, L, dk, dk, nseg=nseg, mode=m, gate_norm=gate_norm, total_stride=tstride,
+                     stream=_stream(stream))
+    _check("la_cumdecay", lib().la_cumdecay(_ptr(decay), _ptr(cum), _ptr(total), ctypes.byref(shp)))
+    return cum, total

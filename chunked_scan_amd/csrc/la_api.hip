@@ -1,0 +1,236 @@
+// la_api.hip -- the C ABI of liblachunk.so (declared in include/la_chunk.h).
+//
+// Every entry point validates all of its arguments on the host before the first HIP call, so a
+// rejected call enqueues nothing and touches no device state.  Validation order: shape pointer,
+// sizes, dtypes, decay mode, required pointers, aliasing; the first failure is returned.
+#include <math.h>
+#include <stdint.h>
+
+#include "la_chunk.h"
+#include "la_internal.h"
+
+namespace {
+
+using la::CorrectArgs;
+using la::FwdArgs;
+
+constexpr int64_t kMaxElems = (int64_t)1 << 60;  // keeps every byte count below 2^63
+
+bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+size_t esize(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
+
+// Overflow-safe product of non-negative sizes; -1 if it exceeds kMaxElems.
+int64_t prod(int64_t a, int64_t b) {
+    if (a == 0 || b == 0) return 0;
+    if (a > kMaxElems / b) return -1;
+    return a * b;
+}
+int64_t prod4(int64_t a, int64_t b, int64_t c, int64_t d) {
+    int64_t x = prod(a, b);
+    if (x < 0) return -1;
+    x = prod(x, c);
+    if (x < 0) return -1;
+    return prod(x, d);
+}
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+bool overlap(Span a, Span b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    uintptr_t x = (uintptr_t)a.p, y = (uintptr_t)b.p;
+    return x < y + b.bytes && y < x + a.bytes;
+}
+
+la_status check_common(const la_shape* s) {
+    if (!s) return LA_ERR_NULL;
+    if (s->B < 0 || s->H < 0 || s->L < 0 || s->nseg < 1 || s->dk <= 0 || s->dv <= 0) return LA_ERR_SHAPE;
+    if (s->L % s->nseg != 0) return LA_ERR_SHAPE;
+    if (prod4(s->B, s->H, s->L, s->dk > s->dv ? s->dk : s->dv) < 0) return LA_ERR_SHAPE;
+    if (prod4(s->B, s->H, s->nseg, (int64_t)s->dk * s->dv) < 0) return LA_ERR_SHAPE;
+    if (!head_dim_ok(s->dk) || !head_dim_ok(s->dv)) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
+la_status check_dtype(const la_shape* s) {
+    if (s->in_dtype != LA_F32 && s->in_dtype != LA_BF16) return LA_ERR_DTYPE;
+    if (s->out_dtype != s->in_dtype) return LA_ERR_DTYPE;
+    return LA_OK;
+}
+
+la_status check_decay_mode(const la_shape* s) {
+    if (s->decay_mode != LA_DECAY_NONE && s->decay_mode != LA_DECAY_HEAD && s->decay_mode != LA_DECAY_GATE)
+        return LA_ERR_DECAY;
+    if (s->decay_mode == LA_DECAY_GATE && !(s->gate_norm > 0.f && isfinite(s->gate_norm))) return LA_ERR_DECAY;
+    return LA_OK;
+}
+
+// Bytes of the decay argument for this shape and mode.
+size_t decay_bytes(const la_shape* s) {
+    if (s->decay_mode == LA_DECAY_HEAD) return sizeof(float) * (size_t)s->H;
+    if (s->decay_mode == LA_DECAY_GATE) return sizeof(float) * (size_t)(s->B * s->H * s->L * s->dk);
+    return 0;
+}
+
+la_status validate_fwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
+                       const void* o, const float* s_out, const la_shape* s, int chunk) {
+    la_status st = check_common(s);
+    if (st != LA_OK) return st;
+    if (chunk <= 0 || s->subseg_chunks < 0 || s->state_stride < 0) return LA_ERR_SHAPE;
+    if (s->state_stride && s->state_stride < (int64_t)s->nseg * s->dk * s->dv) return LA_ERR_SHAPE;
+    if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
+    if ((st = check_dtype(s)) != LA_OK) return st;
+    if ((st = check_decay_mode(s)) != LA_OK) return st;
+    if (s->decay_mode == LA_DECAY_NONE && decay) return LA_ERR_DECAY;
+    const int64_t nqk = s->B * s->H * s->L * s->dk;
+    const int64_t nv = s->B * s->H * s->L * s->dv;
+    if (nqk > 0 && (!q || !k || !v || !o)) return LA_ERR_NULL;
+    if (s->decay_mode == LA_DECAY_HEAD && s->H > 0 && !decay) return LA_ERR_NULL;
+    if (s->decay_mode == LA_DECAY_GATE && nqk > 0 && !decay) return LA_ERR_NULL;
+    const size_t es = esize(s->in_dtype);
+    const int64_t BH = s->B * s->H;
+    const int64_t per_seg = (int64_t)s->dk * s->dv;
+    const int64_t so_stride = s->state_stride ? s->state_stride : s->nseg * per_seg;
+    const size_t st_bytes = sizeof(float) * (size_t)(BH * per_seg);
+    const size_t so_bytes = BH > 0 ? sizeof(float) * (size_t)((BH - 1) * so_stride + s->nseg * per_seg) : 0;
+    Span sq{q, es * nqk}, sk{k, es * nqk}, sv{v, es * nv}, sd{decay, decay_bytes(s)}, si{s_in, s_in ? st_bytes : 0};
+    Span so{o, es * nv}, sso{s_out, s_out ? so_bytes : 0};
+    for (Span in : {sq, sk, sv, sd, si})
+        if (overlap(so, in) || overlap(sso, in)) return LA_ERR_ALIAS;
+    if (overlap(so, sso)) return LA_ERR_ALIAS;
+    return LA_OK;
+}
+
+la_status from_hip(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t la_version(void) { return (1 << 16) | 0; }
+
+const char* la_status_str(la_status s) {
+    switch (s) {
+        case LA_OK: return "ok";
+        case LA_ERR_NULL: return "a required pointer is NULL";
+        case LA_ERR_SHAPE: return "invalid or inconsistent sizes";
+        case LA_ERR_DTYPE: return "unsupported dtype combination";
+        case LA_ERR_ALIAS: return "an output overlaps an input";
+        case LA_ERR_UNSUPPORTED: return "no kernel for this head dim / chunk / layout";
+        case LA_ERR_LAUNCH: return "HIP launch or workspace allocation failed";
+        case LA_ERR_DECAY: return "invalid decay mode or gate_norm";
+    }
+    return "unknown status";
+}
+
+int32_t la_supported(const la_shape* s, int32_t chunk) {
+    if (check_common(s) != LA_OK || chunk <= 0 || !chunk_ok(chunk) || s->subseg_chunks < 0) return 0;
+    if (check_dtype(s) != LA_OK || check_decay_mode(s) != LA_OK) return 0;
+    return 1;
+}
+
+la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in, void* o,
+                       float* s_out, const la_shape* s, int32_t chunk) {
+    la_status st = validate_fwd(q, k, v, decay, s_in, o, s_out, s, chunk);
+    if (st != LA_OK) return st;
+    hipStream_t stream = (hipStream_t)s->stream;
+    const int64_t so_stride = s->state_stride ? s->state_stride : (int64_t)s->nseg * s->dk * s->dv;
+    if (s->B * s->H == 0) return LA_OK;
+    if (s->L == 0) {
+        if (!s_out) return LA_OK;
+        return from_hip(la::launch_empty_states(s_in, s_out, so_stride, s->B * s->H, s->nseg, s->dk, s->dv, stream));
+    }
+    FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.decay = decay; a.s_in = s_in; a.o = o; a.s_out = s_out;
+    a.s_out_stride = so_stride;
+    a.B = s->B; a.H = s->H; a.L = s->L;
+    a.dk = s->dk; a.dv = s->dv; a.nseg = s->nseg; a.chunk = chunk;
+    a.bf16 = s->in_dtype == LA_BF16;
+    a.mode = s->decay_mode;
+    a.inv_norm = s->decay_mode == LA_DECAY_GATE ? 1.f / s->gate_norm : 1.f;
+    a.subseg_chunks = s->subseg_chunks;
+    a.stream = stream;
+    if (a.bf16 && a.dk == 128 && a.dv == 128 && chunk == 64) return from_hip(la::launch_chunk_fwd_mfma(a));
+    return from_hip(la::launch_chunk_fwd_generic(a));
+}
+
+la_status la_state_scan(const float* seg_states, const float* seg_decay, int32_t P, float* out_states,
+                        const la_shape* s) {
+    if (!s) return LA_ERR_NULL;
+    if (s->B < 0 || s->H < 0 || P < 1 || s->dk <= 0 || s->dv <= 0) return LA_ERR_SHAPE;
+    const int64_t nst = prod4(s->B, s->H, P, (int64_t)s->dk * s->dv);
+    if (nst < 0) return LA_ERR_SHAPE;
+    if (s->dv % 4 != 0) return LA_ERR_UNSUPPORTED;
+    if (nst > 0 && (!seg_states || !seg_decay || !out_states)) return LA_ERR_NULL;
+    if (((uintptr_t)seg_states | (uintptr_t)out_states) % 16 != 0) return LA_ERR_UNSUPPORTED;
+    Span sx{seg_states, sizeof(float) * (size_t)nst}, sy{out_states, sizeof(float) * (size_t)nst};
+    Span sl{seg_decay, sizeof(float) * (size_t)(s->B * s->H * P * s->dk)};
+    if (seg_states != out_states && overlap(sx, sy)) return LA_ERR_ALIAS;
+    if (overlap(sl, sy)) return LA_ERR_ALIAS;
+    if (nst == 0) return LA_OK;
+    return from_hip(la::launch_state_scan(seg_states, seg_decay, out_states, s->B * s->H, P, s->dk, s->dv,
+                                          (hipStream_t)s->stream));
+}
+
+la_status la_state_correct(const void* q, const float* cumdecay, const float* s_recv, void* o, const la_shape* s) {
+    la_status st = check_common(s);
+    if (st != LA_OK) return st;
+    if (s->seg_begin < 0 || s->seg_begin > s->nseg || s->state_stride < 0) return LA_ERR_SHAPE;
+    if ((st = check_dtype(s)) != LA_OK) return st;
+    if ((st = check_decay_mode(s)) != LA_OK) return st;
+    if (s->decay_mode == LA_DECAY_NONE && cumdecay) return LA_ERR_DECAY;
+    const int64_t np = s->nseg - s->seg_begin;
+    const int64_t per_state = (int64_t)s->dk * s->dv;
+    const int64_t stride = s->state_stride ? s->state_stride : np * per_state;
+    if (s->state_stride && s->state_stride < np * per_state) return LA_ERR_SHAPE;
+    const int64_t BH = s->B * s->H;
+    const int64_t Ls = s->L / s->nseg;
+    const int64_t nq = BH * s->L * s->dk;
+    const int64_t ncorr = BH * np * Ls;  // tokens to correct
+    if (ncorr > 0 && (!q || !s_recv || !o)) return LA_ERR_NULL;
+    if (ncorr > 0 && s->decay_mode != LA_DECAY_NONE && !cumdecay) return LA_ERR_NULL;
+    const size_t es = esize(s->in_dtype);
+    size_t cum_bytes = s->decay_mode == LA_DECAY_HEAD ? sizeof(float) * (size_t)s->H
+                       : s->decay_mode == LA_DECAY_GATE ? sizeof(float) * (size_t)nq : 0;
+    size_t recv_bytes = BH > 0 ? sizeof(float) * (size_t)((BH - 1) * stride + np * per_state) : 0;
+    Span so{o, es * (size_t)(BH * s->L * s->dv)};
+    if (overlap(so, Span{q, es * (size_t)nq}) || overlap(so, Span{cumdecay, cum_bytes}) ||
+        overlap(so, Span{s_recv, recv_bytes}))
+        return LA_ERR_ALIAS;
+    if (ncorr == 0) return LA_OK;
+    CorrectArgs a;
+    a.q = q; a.cum = cumdecay; a.s_recv = s_recv; a.o = o;
+    a.B = s->B; a.H = s->H; a.L = s->L;
+    a.dk = s->dk; a.dv = s->dv; a.nseg = s->nseg; a.seg_begin = s->seg_begin;
+    a.state_stride = stride;
+    a.bf16 = s->in_dtype == LA_BF16;
+    a.mode = s->decay_mode;
+    a.stream = (hipStream_t)s->stream;
+    return from_hip(la::launch_state_correct(a));
+}
+
+la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const la_shape* s) {
+    la_status st = check_common(s);
+    if (st != LA_OK) return st;
+    if ((st = check_decay_mode(s)) != LA_OK) return st;
+    if (s->decay_mode == LA_DECAY_NONE && decay) return LA_ERR_DECAY;
+    const int64_t BH = s->B * s->H;
+    const int64_t ncum = BH * s->L * s->dk;
+    const int64_t ntot = BH * s->nseg * s->dk;
+    if (s->total_stride < 0 || (s->total_stride && s->total_stride < (int64_t)s->nseg * s->dk)) return LA_ERR_SHAPE;
+    const int64_t tstride = s->total_stride ? s->total_stride : (int64_t)s->nseg * s->dk;
+    const bool need = (cumdecay && ncum > 0) || (total && ntot > 0);
+    if (need && s->decay_mode == LA_DECAY_HEAD && !decay) return LA_ERR_NULL;
+    if (need && s->decay_mode == LA_DECAY_GATE && ncum > 0 && !decay) return LA_ERR_NULL;
+    Span sd{decay, decay_bytes(s)}, sc{cumdecay, cumdecay ? sizeof(float) * (size_t)ncum : 0};
+    Span stt{total, (total && BH > 0) ? sizeof(float) * (size_t)((BH - 1) * tstride + s->nseg * s->dk) : 0};
+    if (overlap(sc, sd) || overlap(stt, sd) || overlap(sc, stt)) return LA_ERR_ALIAS;
+    if (!need) return LA_OK;
+    const float inv_norm = s->decay_mode == LA_DECAY_GATE ? 1.f / s->gate_norm : 1.f;
+    return from_hip(la::launch_cumdecay(decay, cumdecay, total, tstride, s->B, s->H, s->L, s->dk, s->nseg,
+                                        s->decay_mode, inv_norm, (hipStream_t)s->stream));
+}
+
+}  // extern "C"

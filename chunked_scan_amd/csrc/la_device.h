@@ -1,0 +1,47 @@
+// la_device.h -- device-side helpers shared by the HIP kernels of liblachunk (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum { DECAY_NONE = 0, DECAY_HEAD = 1, DECAY_GATE = 2 };
+
+// bf16 <-> f32.  The widening is exact; the narrowing rounds to nearest even (gfx950 has a
+// native packed instruction for it, which the compiler selects for this cast).
+__device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
+__device__ __forceinline__ __bf16 f2bf(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ float bits_lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bits_hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <typename T> struct io;
+template <> struct io<float> {
+    __device__ static __forceinline__ float ld(const float* p) { return *p; }
+    __device__ static __forceinline__ void st(float* p, float x) { *p = x; }
+};
+template <> struct io<__bf16> {
+    __device__ static __forceinline__ float ld(const __bf16* p) { return (float)*p; }
+    __device__ static __forceinline__ void st(__bf16* p, float x) { *p = (__bf16)x; }
+};
+
+// Per-token log-decay of the gate mode: log sigmoid(g) / norm = -softplus(-g) / norm, written
+// so that neither branch overflows: softplus(x) = max(x, 0) + log1p(exp(-|x|)).
+__device__ __forceinline__ float gate_logdecay(float g, float inv_norm) {
+    float x = -g;
+    float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+    return -sp * inv_norm;
+}
+
+// a^m for a per-token log-decay lam and a token distance m >= 0, with a^0 = 1 exactly even when
+// lam = -inf (a = 0).
+__device__ __forceinline__ float decay_pow(float lam, int m) { return m == 0 ? 1.f : expf(lam * (float)m); }
+
+}  // namespace la

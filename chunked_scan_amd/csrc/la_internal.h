@@ -1,0 +1,63 @@
+// la_internal.h -- host-side interface between the C-ABI layer (la_api.hip) and the kernel
+// launchers.  Arguments have already been validated when a launcher is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* decay;
+    const float* s_in;
+    void* o;
+    float* s_out;
+    int64_t s_out_stride;  // elements between (b,h) blocks of s_out
+    int64_t B, H, L;
+    int dk, dv, nseg, chunk;
+    bool bf16;
+    int mode;
+    float inv_norm;      // 1 / gate_norm (gate mode)
+    int subseg_chunks;   // 0 = automatic
+    hipStream_t stream;
+};
+
+struct CorrectArgs {
+    const void* q;
+    const float* cum;    // NONE: null; HEAD: [H] log-decay; GATE: [B,H,L,dk] cumulative decay
+    const float* s_recv;
+    void* o;
+    int64_t B, H, L;
+    int dk, dv, nseg, seg_begin;
+    int64_t state_stride;
+    bool bf16;
+    int mode;
+    hipStream_t stream;
+};
+
+// Generic chunked forward: fp32 arithmetic on VALU, q/k/v/o in f32 or bf16, dk, dv in
+// {16,32,64,128}, chunk in {16,32,64}.
+hipError_t launch_chunk_fwd_generic(const FwdArgs& a);
+
+// bf16 MFMA chunked forward for dk = dv = 128, chunk = 64, with intra-GPU sub-segment splitting.
+hipError_t launch_chunk_fwd_mfma(const FwdArgs& a);
+
+// out[n,p] = diag(lam[n,p]) out[n,p-1] + x[n,p] for n < nstates, p < P.  x may equal out.
+hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64_t nstates, int P,
+                             int dk, int dv, hipStream_t stream);
+
+// Output correction: MFMA kernel for bf16 with dk = dv = 128, generic fp32-arithmetic kernel otherwise.
+hipError_t launch_state_correct(const CorrectArgs& a);
+hipError_t launch_state_correct_generic(const CorrectArgs& a);
+
+// total of segment p of (b,h) goes to total[bh * total_stride + p * dk].
+hipError_t launch_cumdecay(const float* decay, float* cum, float* total, int64_t total_stride, int64_t B, int64_t H,
+                           int64_t L, int dk, int nseg, int mode, float inv_norm, hipStream_t stream);
+
+// s_out[b,h,p] = (p == 0 && s_in) ? s_in[b,h] : 0 -- the final states of empty segments.
+hipError_t launch_empty_states(const float* s_in, float* s_out, int64_t s_out_stride, int64_t BH, int nseg, int dk,
+                               int dv, hipStream_t stream);
+
+}  // namespace la

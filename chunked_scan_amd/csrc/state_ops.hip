@@ -1,0 +1,282 @@
+// state_ops.hip -- the segment-level kernels of the decomposition: the segmented state scan
+// (All-Scan on one GPU), the cumulative-decay helper, the generic output correction, and the
+// final states of empty segments.  All of them are HBM-bound streaming kernels.
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+// ---------------------------------------------------------------------------------------------
+// Segmented state scan.  Thread = 4 consecutive state elements (one float4) of one (b,h); it
+// walks the P segments in order:  y = diag(lam[p]) y + x[p];  out[p] = y.
+// Loads of a batch of SCAN_BATCH segments are issued before any of their stores so several
+// HBM reads are in flight per thread; out may alias x because every element is read before the
+// same thread overwrites it.
+constexpr int SCAN_BATCH = 8;
+
+__global__ __launch_bounds__(256) void state_scan_kernel(const float* x, const float* __restrict__ lam,
+                                                         float* out, int P, int dk, int dv,
+                                                         int64_t vec_per_state, int vblocks) {
+    const int64_t n = blockIdx.x / vblocks;  // state index: (b,h) or (b,h,segment)
+    const int64_t e4 = (int64_t)(blockIdx.x % vblocks) * blockDim.x + threadIdx.x;
+    if (e4 >= vec_per_state) return;
+    const int d = (int)((e4 * 4) / dv);
+    const int64_t SZ = (int64_t)dk * dv;
+    const float4* xs = reinterpret_cast<const float4*>(x + n * (int64_t)P * SZ) + e4;
+    float4* ys = reinterpret_cast<float4*>(out + n * (int64_t)P * SZ) + e4;
+    const float* ls = lam + n * (int64_t)P * dk + d;
+    const int64_t pstride = SZ / 4;
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = 0; p0 < P; p0 += SCAN_BATCH) {
+        float4 xb[SCAN_BATCH];
+        float lb[SCAN_BATCH];
+        const int nb = min(SCAN_BATCH, P - p0);
+#pragma unroll
+        for (int j = 0; j < SCAN_BATCH; j++) {
+            if (j < nb) {
+                xb[j] = xs[(int64_t)(p0 + j) * pstride];
+                lb[j] = ls[(int64_t)(p0 + j) * dk];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < SCAN_BATCH; j++) {
+            if (j < nb) {
+                if (p0 + j == 0) {
+                    y = xb[j];  // out[-1] = 0: the decay of segment 0 is never applied
+                } else {
+                    y.x = lb[j] * y.x + xb[j].x;
+                    y.y = lb[j] * y.y + xb[j].y;
+                    y.z = lb[j] * y.z + xb[j].z;
+                    y.w = lb[j] * y.w + xb[j].w;
+                }
+                ys[(int64_t)(p0 + j) * pstride] = y;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Cumulative decay.  HEAD and NONE have closed forms; GATE needs a running sum of log a over the
+// segment, done in two passes over blocks of CUM_TB tokens: block sums, then a prefix over the
+// block sums plus a running sum inside each block.
+constexpr int CUM_TB = 256;
+
+__global__ __launch_bounds__(256) void cumdecay_closed_kernel(const float* __restrict__ lamh, float* __restrict__ cum,
+                                                              float* __restrict__ total, int64_t total_stride,
+                                                              int64_t H, int64_t L, int dk, int nseg, int64_t n_cum,
+                                                              int64_t n_tot, int mode) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t Ls = L / nseg;
+    if (cum && i < n_cum) {
+        const int64_t row = i / dk;  // (b,h,t)
+        const int64_t t = row % L;
+        const int64_t h = (row / L) % H;
+        const int64_t tau = t % Ls + 1;
+        cum[i] = (mode == DECAY_HEAD) ? expf(lamh[h] * (float)tau) : 1.f;
+    }
+    if (total && i < n_tot) {
+        const int64_t bh = i / ((int64_t)dk * nseg);
+        const int64_t h = bh % H;
+        total[bh * total_stride + i % ((int64_t)dk * nseg)] =
+            (mode == DECAY_HEAD) ? (Ls == 0 ? 1.f : expf(lamh[h] * (float)Ls)) : 1.f;
+    }
+}
+
+// partial[(bh*nseg + p)*nblk + blk][d] = sum of log a over the block's tokens.
+__global__ __launch_bounds__(256) void cumdecay_gate_blocksum_kernel(const float* __restrict__ g, float* __restrict__ partial,
+                                                                     int64_t L, int dk, int nseg, int nblk,
+                                                                     int64_t nthreads, float inv_norm) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nthreads) return;
+    const int d = (int)(i % dk);
+    const int64_t r = i / dk;  // ((bh*nseg + p)*nblk + blk)
+    const int blk = (int)(r % nblk);
+    const int64_t bhp = r / nblk;
+    const int p = (int)(bhp % nseg);
+    const int64_t bh = bhp / nseg;
+    const int64_t Ls = L / nseg;
+    const int64_t t0 = (int64_t)p * Ls + (int64_t)blk * CUM_TB;
+    const int64_t t1 = min(t0 + CUM_TB, (int64_t)(p + 1) * Ls);
+    float s = 0.f;
+    for (int64_t t = t0; t < t1; t++) s += gate_logdecay(g[(bh * L + t) * dk + d], inv_norm);
+    partial[i] = s;
+}
+
+__global__ __launch_bounds__(256) void cumdecay_gate_scan_kernel(const float* __restrict__ g, const float* __restrict__ partial,
+                                                                 float* __restrict__ cum, float* __restrict__ total,
+                                                                 int64_t total_stride, int64_t L, int dk, int nseg, int nblk,
+                                                                 int64_t nthreads, float inv_norm) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nthreads) return;
+    const int d = (int)(i % dk);
+    const int64_t r = i / dk;
+    const int blk = (int)(r % nblk);
+    const int64_t bhp = r / nblk;
+    const int p = (int)(bhp % nseg);
+    const int64_t bh = bhp / nseg;
+    const int64_t Ls = L / nseg;
+    float run = 0.f;
+    for (int b = 0; b < blk; b++) run += partial[(bhp * nblk + b) * dk + d];
+    const int64_t t0 = (int64_t)p * Ls + (int64_t)blk * CUM_TB;
+    const int64_t t1 = min(t0 + CUM_TB, (int64_t)(p + 1) * Ls);
+    if (cum) {
+        for (int64_t t = t0; t < t1; t++) {
+            run += gate_logdecay(g[(bh * L + t) * dk + d], inv_norm);
+            cum[(bh * L + t) * dk + d] = expf(run);
+        }
+    } else {
+        run += partial[i];
+    }
+    if (total && blk == nblk - 1) total[bh * total_stride + (int64_t)p * dk + d] = expf(run);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Generic output correction (fp32 arithmetic): block = (b,h,segment, 64-token tile, 32-wide
+// dv slice).  o_t[c] += sum_d q_t[d] cum_t[d] S[d][c].
+constexpr int CT = 64;
+constexpr int CDVT = 32;
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(256) void state_correct_generic_kernel(
+    const T* __restrict__ q, const float* __restrict__ cum, const float* __restrict__ s_recv, T* __restrict__ o,
+    int64_t H, int64_t L, int dk, int dv, int nseg, int seg_begin, int64_t state_stride, int ntiles) {
+    __shared__ float Ss[128 * CDVT];
+    __shared__ float Qs[CT * 128];
+    const int tid = threadIdx.x;
+    int64_t r = blockIdx.x;
+    const int tile = (int)(r % ntiles);
+    r /= ntiles;
+    const int np = nseg - seg_begin;
+    const int p = seg_begin + (int)(r % np);
+    const int64_t bh = r / np;
+    const int64_t h = bh % H;
+    const int c0 = blockIdx.y * CDVT;
+    const int nc = min(CDVT, dv - c0);
+    const int64_t Ls = L / nseg;
+    const int64_t tt0 = (int64_t)tile * CT;  // offset inside the segment
+    const int n = (int)min((int64_t)CT, Ls - tt0);
+    if (n <= 0) return;
+    const int64_t row0 = bh * L + (int64_t)p * Ls + tt0;
+    const float* S = s_recv + bh * state_stride + (int64_t)(p - seg_begin) * dk * dv;
+    for (int e = tid; e < dk * nc; e += 256) {
+        int d = e / nc, c = e % nc;
+        Ss[d * CDVT + c] = S[d * dv + c0 + c];
+    }
+    const float lam = (MODE == DECAY_HEAD) ? cum[h] : 0.f;
+    for (int e = tid; e < n * dk; e += 256) {
+        int i = e / dk, d = e % dk;
+        float w = io<T>::ld(q + (row0 + i) * dk + d);
+        if (MODE == DECAY_HEAD) w *= expf(lam * (float)(tt0 + i + 1));
+        if (MODE == DECAY_GATE) w *= cum[(row0 + i) * dk + d];
+        Qs[i * 128 + d] = w;
+    }
+    __syncthreads();
+    for (int e = tid; e < n * nc; e += 256) {
+        int i = e / nc, c = e % nc;
+        float acc = 0.f;
+        for (int d = 0; d < dk; d++) acc += Qs[i * 128 + d] * Ss[d * CDVT + c];
+        T* po = o + (row0 + i) * dv + c0 + c;
+        io<T>::st(po, io<T>::ld(po) + acc);
+    }
+}
+
+template <typename T>
+hipError_t correct_typed(const CorrectArgs& a) {
+    const int64_t Ls = a.L / a.nseg;
+    const int ntiles = (int)((Ls + CT - 1) / CT);
+    const int64_t nblk = a.B * a.H * (int64_t)(a.nseg - a.seg_begin) * ntiles;
+    if (nblk == 0) return hipSuccess;
+    dim3 grid((unsigned)nblk, (unsigned)((a.dv + CDVT - 1) / CDVT));
+    const T* q = (const T*)a.q;
+    T* o = (T*)a.o;
+    const int64_t ss = a.state_stride;
+    switch (a.mode) {
+        case DECAY_HEAD:
+            state_correct_generic_kernel<T, DECAY_HEAD><<<grid, 256, 0, a.stream>>>(
+                q, a.cum, a.s_recv, o, a.H, a.L, a.dk, a.dv, a.nseg, a.seg_begin, ss, ntiles);
+            break;
+        case DECAY_GATE:
+            state_correct_generic_kernel<T, DECAY_GATE><<<grid, 256, 0, a.stream>>>(
+                q, a.cum, a.s_recv, o, a.H, a.L, a.dk, a.dv, a.nseg, a.seg_begin, ss, ntiles);
+            break;
+        default:
+            state_correct_generic_kernel<T, DECAY_NONE><<<grid, 256, 0, a.stream>>>(
+                q, a.cum, a.s_recv, o, a.H, a.L, a.dk, a.dv, a.nseg, a.seg_begin, ss, ntiles);
+            break;
+    }
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void empty_states_kernel(const float* __restrict__ s_in, float* __restrict__ s_out,
+                                                           int64_t s_out_stride, int nseg, int64_t SZ, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int64_t e = i % SZ;
+    const int64_t bhp = i / SZ;
+    const int p = (int)(bhp % nseg);
+    const int64_t bh = bhp / nseg;
+    s_out[bh * s_out_stride + (int64_t)p * SZ + e] = (p == 0 && s_in) ? s_in[bh * SZ + e] : 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64_t nstates, int P, int dk, int dv,
+                             hipStream_t stream) {
+    if (nstates == 0 || P == 0) return hipSuccess;
+    const int64_t vec = (int64_t)dk * dv / 4;
+    const int vblocks = (int)((vec + 255) / 256);
+    state_scan_kernel<<<(unsigned)(nstates * vblocks), 256, 0, stream>>>(x, lam, out, P, dk, dv, vec, vblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_cumdecay(const float* decay, float* cum, float* total, int64_t total_stride, int64_t B, int64_t H,
+                           int64_t L, int dk, int nseg, int mode, float inv_norm, hipStream_t stream) {
+    const int64_t n_cum = B * H * L * dk;
+    const int64_t n_tot = B * H * (int64_t)nseg * dk;
+    if (mode != DECAY_GATE) {
+        const int64_t n = max(cum ? n_cum : 0, total ? n_tot : 0);
+        if (n == 0) return hipSuccess;
+        cumdecay_closed_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(decay, cum, total, total_stride, H, L,
+                                                                               dk, nseg, n_cum, n_tot, mode);
+        return hipGetLastError();
+    }
+    const int64_t Ls = L / nseg;
+    if (Ls == 0) {  // empty segments: cumulative decay is the empty product
+        if (!total || n_tot == 0) return hipSuccess;
+        cumdecay_closed_kernel<<<(unsigned)((n_tot + 255) / 256), 256, 0, stream>>>(
+            decay, nullptr, total, total_stride, H, L, dk, nseg, 0, n_tot, DECAY_NONE);
+        return hipGetLastError();
+    }
+    const int nblk = (int)((Ls + CUM_TB - 1) / CUM_TB);
+    const int64_t nthreads = B * H * (int64_t)nseg * nblk * dk;
+    if (nthreads == 0) return hipSuccess;
+    float* partial = nullptr;
+    hipError_t e = hipMallocAsync((void**)&partial, sizeof(float) * (size_t)nthreads, stream);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)((nthreads + 255) / 256);
+    cumdecay_gate_blocksum_kernel<<<grid, 256, 0, stream>>>(decay, partial, L, dk, nseg, nblk, nthreads, inv_norm);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+        cumdecay_gate_scan_kernel<<<grid, 256, 0, stream>>>(decay, partial, cum, total, total_stride, L, dk, nseg,
+                                                            nblk, nthreads, inv_norm);
+        e = hipGetLastError();
+    }
+    hipError_t f = hipFreeAsync(partial, stream);
+    return e != hipSuccess ? e : f;
+}
+
+hipError_t launch_state_correct_generic(const CorrectArgs& a) {
+    return a.bf16 ? correct_typed<__bf16>(a) : correct_typed<float>(a);
+}
+
+hipError_t launch_empty_states(const float* s_in, float* s_out, int64_t s_out_stride, int64_t BH, int nseg, int dk,
+                               int dv, hipStream_t stream) {
+    const int64_t SZ = (int64_t)dk * dv;
+    const int64_t n = BH * nseg * SZ;
+    if (n == 0) return hipSuccess;
+    empty_states_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(s_in, s_out, s_out_stride, nseg, SZ, n);
+    return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,192 @@
+/*
+ * la_chunk.h -- C ABI of liblachunk.so: chunked causal linear attention with a segmented state
+ * scan, hand-written for AMD MI355X (gfx950).
+ *
+ * What is computed.  Per (batch b, head h) sequence of L tokens with queries q_t, keys k_t in
+ * R^dk, values v_t in R^dv and per-token decay a_t in (0,1]^dk, the linear-attention state
+ * recurrence
+ *        S_t = diag(a_t) S_{t-1} + k_t v_t^T,     o_t = S_t^T q_t,          S in R^{dk x dv}
+ * (review page "ZeCO: Zero Communication Overhead Sequence Parallelism for Linear Attention":
+ * linear attention as a fixed-size state recurrence, pith_extraction.supporting_citations[0];
+ * the gated, GLA-style chunkwise form, supporting_citations[1]; S is the only object that
+ * crosses a device boundary, pith_extraction.core_discovery).  The library evaluates it chunk
+ * by chunk, and splits it over sequence segments with the linear-decomposition identity of the
+ * same page (pith_extraction.key_machinery): the state at the end of a segment is the segment's
+ * cumulative decay applied to the incoming state plus the segment's locally computed state, and
+ * the outputs take the matching rank-dk correction.
+ *
+ * Memory.  Every pointer is a device pointer (HBM) owned by the caller; the library never
+ * frees or keeps one past the call.  Tensors are dense, row-major, in the layouts stated per
+ * argument.  la_chunk_fwd may allocate temporary device workspace, stream-ordered on the
+ * caller's stream, and returns it to the pool before returning; the other calls allocate
+ * nothing.
+ *
+ * Execution.  Calls validate every argument on the host first, then enqueue kernels on
+ * shape->stream (a hipStream_t; NULL = the default stream) and return without waiting.  A
+ * fault inside a kernel is reported by the caller's next synchronisation, not by the call.
+ * Calls touching the same buffers must be ordered by the caller (same stream or events).
+ * The library holds no mutable global state; concurrent calls from several host threads are
+ * safe.
+ *
+ * Errors.  A call returns LA_OK or a negative la_status and, on error, enqueues nothing.
+ */
+#ifndef LA_CHUNK_H
+#define LA_CHUNK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum la_status {
+    LA_OK = 0,
+    LA_ERR_NULL = -1,        /* a required pointer is NULL (or shape is NULL) */
+    LA_ERR_SHAPE = -2,       /* a size is negative / zero where it must not be, or does not divide */
+    LA_ERR_DTYPE = -3,       /* unknown dtype, or a dtype combination that is not supported */
+    LA_ERR_ALIAS = -4,       /* an output overlaps an input it may not overlap */
+    LA_ERR_UNSUPPORTED = -5, /* valid request that this build has no kernel for (e.g. dk > 128) */
+    LA_ERR_LAUNCH = -6,      /* the HIP runtime refused a launch or a workspace allocation */
+    LA_ERR_DECAY = -7        /* unknown decay mode, or gate_norm <= 0 in gate mode */
+} la_status;
+
+typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* How the per-token decay a_t in R^dk is given (argument `decay`):
+ *   LA_DECAY_NONE : a_t = 1; decay must be NULL.
+ *   LA_DECAY_HEAD : one log-decay per head, decay = float[H] holding lambda_h <= 0, a_t = exp(lambda_h)
+ *                   for every token and key dimension (per-head scalar decay, RetNet/Lightning style).
+ *   LA_DECAY_GATE : per token and key dimension, decay = float[B,H,L,dk] holding the raw gate g,
+ *                   a_t[d] = sigmoid(g_t[d])^(1/gate_norm) (GLA style).  Evaluated in log space:
+ *                   log a = -softplus(-g) / gate_norm, summed within each chunk. */
+typedef enum la_decay_mode { LA_DECAY_NONE = 0, LA_DECAY_HEAD = 1, LA_DECAY_GATE = 2 } la_decay_mode;
+
+typedef struct la_shape {
+    int64_t B;            /* batch size, >= 0 */
+    int64_t H;            /* heads, >= 0 */
+    int64_t L;            /* tokens per (b,h) sequence, >= 0; L % nseg == 0 */
+    int32_t dk;           /* key/query head dim: 16, 32, 64 or 128 */
+    int32_t dv;           /* value head dim: 16, 32, 64 or 128 */
+    int32_t nseg;         /* independent segments per sequence, >= 1, each L/nseg tokens */
+    int32_t in_dtype;     /* la_dtype of q, k, v */
+    int32_t out_dtype;    /* la_dtype of o (must equal in_dtype in this build) */
+    int32_t decay_mode;   /* la_decay_mode */
+    float gate_norm;      /* LA_DECAY_GATE only: exponent 1/gate_norm on the sigmoid, > 0 */
+    int32_t seg_begin;    /* la_state_correct only: first segment to correct, 0 <= seg_begin <= nseg */
+    int64_t state_stride; /* elements between consecutive (b,h) blocks of a per-segment state
+                             array: s_out of la_chunk_fwd (0 = dense, nseg*dk*dv) and s_recv of
+                             la_state_correct (0 = dense, (nseg - seg_begin)*dk*dv).  Lets the
+                             local state land directly in a slot of a larger scan buffer. */
+    int64_t total_stride; /* la_cumdecay only: elements between consecutive (b,h) blocks of total;
+                             0 = dense, nseg*dk */
+    int32_t subseg_chunks;/* la_chunk_fwd only: chunks per internal sub-segment when one segment is
+                             split across compute units (the decomposition identity applied inside
+                             the GPU); 0 = choose automatically, >= 1 forces that length.  Changes
+                             the rounding order only, never the mathematical result. */
+    void* stream;         /* hipStream_t the work is enqueued on; NULL = default stream */
+} la_shape;
+/* A zero-initialised la_shape plus B, H, L, dk, dv, nseg = 1 and the dtypes is a valid
+ * description for every call; the other fields only matter to the calls that name them. */
+
+/*
+ * Chunkwise forward of the recurrence over every segment of every (b,h) sequence.
+ *
+ * Per chunk of `chunk` tokens it computes the intra-chunk "diagonal" term -- the causal
+ * (j <= i, diagonal included), decay-weighted Q K^T of the chunk times V -- plus the inter-chunk
+ * term Q-bar S_{c-1}, and carries the state S_c = diag(Lambda_c) S_{c-1} + K-tilde^T V across
+ * chunks, where Lambda_c is the chunk's cumulative decay and K-tilde scales each key by the decay
+ * from its token to the chunk end (page "ZeCO ...": the diagonal P computation,
+ * skeptic_critique.concrete_test and pith_extraction.core_discovery; the decay vectors Lambda,
+ * Gamma and K-bar of referee_report.minor_comments[3]).  The result equals the token-by-token
+ * recurrence up to floating-point rounding.
+ *
+ *   q, k   : [B,H,L,dk] in_dtype        v : [B,H,L,dv] in_dtype        (read only)
+ *   decay  : see la_decay_mode                                          (read only)
+ *   s_in   : float[B,H,dk,dv] initial state of segment 0 of each sequence, or NULL for zero.
+ *            Segments 1..nseg-1 always start from zero (each is a device's local share).
+ *   o      : [B,H,L,dv] out_dtype, written (every element); must not overlap q, k, v, decay, s_in.
+ *   s_out  : float, final local state of every segment, or NULL to skip it: segment p of (b,h)
+ *            at s_out + (b*H + h) * state_stride + p * dk * dv (dense [B,H,nseg,dk,dv] when
+ *            state_stride = 0); must not overlap any other argument.
+ *   chunk  : chunk length in tokens: 16, 32 or 64 (64 is the production size).
+ * A partial last chunk (L/nseg not a multiple of chunk) is allowed.  In gate mode the
+ * per-chunk, per-key-dim log-decay sum must stay above -80 (strong enough decays would push the
+ * chunk-relative key scaling outside float range).
+ * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_DECAY, LA_ERR_ALIAS,
+ * LA_ERR_UNSUPPORTED or LA_ERR_LAUNCH.
+ */
+la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float* decay,
+                       const float* s_in, void* o, float* s_out, const la_shape* shape,
+                       int32_t chunk);
+
+/*
+ * Segmented state scan: the All-Scan of ZeCO reproduced on one GPU (page "ZeCO ...",
+ * pith_extraction.key_machinery: each device applies the update
+ * S_p = (segment decay) * S_{p-1} + S_local,p to the state it receives and passes the result on;
+ * the accumulated state is what moves on, referee_report.major_comments[3]).  For each (b,h):
+ *        out[p] = diag(seg_decay[p]) out[p-1] + seg_states[p],   p = 0..P-1,   out[-1] = 0,
+ * i.e. an inclusive scan; out[p] is the state at the end of segment p, the incoming state of
+ * segment p+1.  Accumulates in fp32 in order of p.
+ *
+ *   seg_states : float[B,H,P,dk,dv]   seg_decay : float[B,H,P,dk] multiplicative per-segment
+ *                total decay (a vector over key dims; broadcast a scalar yourself); the entry of
+ *                segment 0 only ever multiplies the zero state and is not applied.
+ *   out_states : float[B,H,P,dk,dv]; may be the same pointer as seg_states (in place), must not
+ *                otherwise overlap it, nor seg_decay.
+ * Uses shape->B, H, dk, dv, stream; P is the argument (not shape->nseg).
+ * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_ALIAS, LA_ERR_UNSUPPORTED or LA_ERR_LAUNCH.
+ */
+la_status la_state_scan(const float* seg_states, const float* seg_decay, int32_t P,
+                        float* out_states, const la_shape* shape);
+
+/*
+ * Output correction with an incoming state: the rank-dk term of the decomposition identity
+ * (page "ZeCO ...", pith_extraction.key_machinery).  For every segment p >= shape->seg_begin and
+ * every token t of it:
+ *        o_t += (q_t (*) cum_t)^T s_recv[b,h,p - seg_begin]
+ * where cum_t[d] is the product of a_s[d] from the segment's first token to t inclusive.
+ *
+ *   q        : [B,H,L,dk] in_dtype (read only)
+ *   cumdecay : by decay_mode -- NONE: NULL (cum = 1);  HEAD: float[H] log-decays lambda_h, the
+ *              cumulative decay exp(lambda_h * (t - segment start + 1)) is formed in the kernel;
+ *              GATE: float[B,H,L,dk] cumulative decay values as written by la_cumdecay.
+ *   s_recv   : float, incoming state of segment p of (b,h) at
+ *              s_recv + (b*H + h) * state_stride + (p - seg_begin) * dk * dv, each dk x dv row-major.
+ *   o        : [B,H,L,dv] out_dtype, updated in place (o = round(o + correction) in fp32);
+ *              must not overlap q, cumdecay, s_recv.
+ * Tokens whose cumulative decay is exactly zero in fp32 receive an exactly-zero correction.
+ * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_DECAY, LA_ERR_ALIAS,
+ * LA_ERR_UNSUPPORTED or LA_ERR_LAUNCH.
+ */
+la_status la_state_correct(const void* q, const float* cumdecay, const float* s_recv, void* o,
+                           const la_shape* shape);
+
+/*
+ * Cumulative decay helper (not one of the three core calls; it prepares their decay inputs).
+ * For every segment p of every (b,h):
+ *   cumdecay[b,h,t,d] = prod_{s = first token of p .. t} a_s[d]          (inclusive)
+ *   total[b,h,p,d]    = prod over all tokens of segment p of a_s[d]      (= Lambda of segment p)
+ * Either output may be NULL.  In HEAD mode the values are the closed forms exp(lambda_h * n);
+ * in GATE mode they are exp of an fp32 running sum of log a within the segment; in NONE mode 1.
+ *   decay    : as for la_chunk_fwd
+ *   cumdecay : float[B,H,L,dk] or NULL
+ *   total    : float or NULL; segment p of (b,h) at total + (b*H + h) * total_stride + p * dk
+ *              (dense [B,H,nseg,dk] when total_stride = 0)
+ * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DECAY, LA_ERR_ALIAS or LA_ERR_LAUNCH.
+ */
+la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const la_shape* shape);
+
+/* Static description of a status code; never NULL. */
+const char* la_status_str(la_status s);
+
+/* 1 if la_chunk_fwd has a kernel for this shape and chunk (validation passes), else 0. */
+int32_t la_supported(const la_shape* shape, int32_t chunk);
+
+/* Library ABI version, (major << 16) | minor. */
+int32_t la_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_CHUNK_H */

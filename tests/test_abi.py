@@ -1,0 +1,164 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol include/la_chunk.h
+declares, the struct layout matches, and argument validation returns the documented codes.
+
+Only calls that fail validation are made here (validation happens on the host before any HIP
+call); the pointers are fake addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_scan_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la_chunk.h")
+
+OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, LAUNCH, DECAY = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("liblachunk.so is not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def _declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(la_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.la_version() >> 16 == 1
+    for code in (OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, LAUNCH, DECAY, 12345):
+        assert lib.la_status_str(code)
+
+
+def test_shape_struct_layout():
+    # offsets follow the C layout of la_shape in include/la_chunk.h
+    assert B.Shape.dk.offset == 24 and B.Shape.gate_norm.offset == 48
+    assert B.Shape.state_stride.offset == 56 and B.Shape.total_stride.offset == 64
+    assert B.Shape.subseg_chunks.offset == 72
+    assert B.Shape.stream.offset == 80 and ctypes.sizeof(B.Shape) == 88
+
+
+# fake device addresses, far apart, never dereferenced
+Q, K, V, O, S_IN, S_OUT, DEC = (0x10000000000 * (i + 1) for i in range(7))
+
+
+def fwd(lib, shp, q=Q, k=K, v=V, dec=None, s_in=None, o=O, s_out=S_OUT, chunk=64):
+    P = ctypes.c_void_p
+    return lib.la_chunk_fwd(P(q), P(k), P(v), P(dec), P(s_in), P(o), P(s_out), ctypes.byref(shp), chunk)
+
+
+def shape(**kw):
+    d = dict(B=1, H=2, L=128, dk=64, dv=64, nseg=1, dtype=B.LA_BF16, mode=0)
+    d.update(kw)
+    return B.make_shape(d.pop("B"), d.pop("H"), d.pop("L"), d.pop("dk"), d.pop("dv"), **d)
+
+
+def test_fwd_validation(lib):
+    assert lib.la_chunk_fwd(None, None, None, None, None, None, None, None, 64) == NULL
+    assert fwd(lib, shape(L=-1)) == SHAPE
+    assert fwd(lib, shape(B=-1)) == SHAPE
+    assert fwd(lib, shape(nseg=0)) == SHAPE
+    assert fwd(lib, shape(L=100, nseg=3)) == SHAPE          # L % nseg != 0
+    assert fwd(lib, shape(dk=0)) == SHAPE
+    assert fwd(lib, shape(dk=96)) == UNSUP
+    assert fwd(lib, shape(dv=256)) == UNSUP
+    assert fwd(lib, shape(), chunk=0) == SHAPE
+    assert fwd(lib, shape(), chunk=48) == UNSUP
+    assert fwd(lib, shape(), chunk=128) == UNSUP
+    assert fwd(lib, shape(subseg_chunks=-1)) == SHAPE
+    bad = shape()
+    bad.in_dtype = 7
+    bad.out_dtype = 7
+    assert fwd(lib, bad) == DTYPE
+    mixed = shape()
+    mixed.out_dtype = B.LA_F32
+    assert fwd(lib, mixed) == DTYPE
+    assert fwd(lib, shape(mode=3)) == DECAY
+    assert fwd(lib, shape(mode=2, gate_norm=0.0)) == DECAY
+    assert fwd(lib, shape(mode=2, gate_norm=float("nan")), dec=DEC) == DECAY
+    assert fwd(lib, shape(mode=0), dec=DEC) == DECAY           # none mode takes no decay
+    assert fwd(lib, shape(mode=1)) == NULL                     # head mode needs lambda_h
+    assert fwd(lib, shape(mode=2)) == NULL                     # gate mode needs g
+    assert fwd(lib, shape(), q=0) == NULL
+    assert fwd(lib, shape(), o=0) == NULL
+    assert fwd(lib, shape(), o=Q + 64) == ALIAS                # o overlaps q
+    assert fwd(lib, shape(), s_out=V) == ALIAS                 # s_out overlaps v
+    assert fwd(lib, shape(), s_in=S_IN, s_out=S_IN + 16) == ALIAS
+    assert fwd(lib, shape(), o=S_OUT) == ALIAS                 # o overlaps s_out
+    assert fwd(lib, shape(B=1 << 40, H=1 << 20)) == SHAPE      # byte counts would overflow
+    # empty problems validate and enqueue nothing
+    assert fwd(lib, shape(B=0), q=0, k=0, v=0, o=0, s_out=0) == OK
+    assert fwd(lib, shape(H=0), q=0, k=0, v=0, o=0, s_out=0) == OK
+
+
+def test_supported(lib):
+    assert lib.la_supported(ctypes.byref(shape()), 64) == 1
+    assert lib.la_supported(ctypes.byref(shape(dk=128, dv=128)), 64) == 1
+    assert lib.la_supported(ctypes.byref(shape(dtype=B.LA_F32, dk=16, dv=16)), 16) == 1
+    assert lib.la_supported(ctypes.byref(shape(dk=256)), 64) == 0
+    assert lib.la_supported(ctypes.byref(shape()), 128) == 0
+    assert lib.la_supported(None, 64) == 0
+
+
+def test_scan_validation(lib):
+    P = ctypes.c_void_p
+    s = shape()
+    assert lib.la_state_scan(P(Q), P(DEC), 4, P(S_OUT), None) == NULL
+    assert lib.la_state_scan(P(Q), P(DEC), 0, P(S_OUT), ctypes.byref(s)) == SHAPE
+    assert lib.la_state_scan(None, P(DEC), 4, P(S_OUT), ctypes.byref(s)) == NULL
+    assert lib.la_state_scan(P(Q), P(DEC), 4, P(Q + 64), ctypes.byref(s)) == ALIAS   # partial overlap
+    assert lib.la_state_scan(P(Q), P(S_OUT + 16), 4, P(S_OUT), ctypes.byref(s)) == ALIAS
+    assert lib.la_state_scan(P(Q + 4), P(DEC), 4, P(S_OUT), ctypes.byref(s)) == UNSUP  # not 16-byte aligned
+    assert lib.la_state_scan(P(Q), P(DEC), 4, P(S_OUT), ctypes.byref(shape(dv=6))) == UNSUP
+    assert lib.la_state_scan(P(Q), P(DEC), 4, P(S_OUT), ctypes.byref(shape(B=0))) == OK
+
+
+def test_correct_validation(lib):
+    P = ctypes.c_void_p
+
+    def call(shp, q=Q, cum=None, s=S_IN, o=O):
+        return lib.la_state_correct(P(q), P(cum), P(s), P(o), ctypes.byref(shp))
+
+    assert lib.la_state_correct(P(Q), None, P(S_IN), P(O), None) == NULL
+    assert call(shape(seg_begin=2)) == SHAPE
+    assert call(shape(seg_begin=-1)) == SHAPE
+    assert call(shape(nseg=4, seg_begin=1, state_stride=64 * 64)) == SHAPE   # stride smaller than 3 states
+    assert call(shape(mode=1)) == NULL
+    assert call(shape(mode=0), cum=DEC) == DECAY
+    assert call(shape(), o=Q + 2) == ALIAS
+    assert call(shape(), s=O + 100) == ALIAS
+    assert call(shape(), q=0) == NULL
+    assert call(shape(seg_begin=1), q=0, s=0, o=0) == OK                   # nothing to correct
+    mixed = shape()
+    mixed.out_dtype = B.LA_F32
+    assert call(mixed) == DTYPE
+
+
+def test_cumdecay_validation(lib):
+    P = ctypes.c_void_p
+    assert lib.la_cumdecay(P(DEC), P(Q), P(K), None) == NULL
+    assert lib.la_cumdecay(None, P(Q), P(K), ctypes.byref(shape(mode=1))) == NULL
+    assert lib.la_cumdecay(P(DEC), P(Q), P(K), ctypes.byref(shape(mode=0))) == DECAY
+    assert lib.la_cumdecay(P(DEC), P(DEC + 4), None, ctypes.byref(shape(mode=2))) == ALIAS
+    assert lib.la_cumdecay(P(DEC), None, None, ctypes.byref(shape(mode=1))) == OK    # nothing requested
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()

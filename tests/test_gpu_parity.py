@@ -1,0 +1,304 @@
+"""GPU parity: every C-ABI call against the fp64 CPU oracle on the same seeded inputs.
+
+Sizes here are ones the oracle finishes in seconds while still spanning several chunks,
+several internal sub-segments and a ragged tail.  Full-size workloads are covered in
+test_gpu_workloads.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_scan_amd import binding as lb
+from chunked_scan_amd import pipeline
+from chunked_scan_amd.inputs import WORKLOADS, make_inputs
+
+from gpu_util import ORC_MODE, TOL, host32, note, oracle_run, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W0, W2, W3 = WORKLOADS[0], WORKLOADS[2], WORKLOADS[3]
+
+
+def _fwd(inp, w, nseg=1, chunk=None, subseg=0, s_in=True):
+    return lb.la_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"] if s_in else None,
+                           mode=w.mode, nseg=nseg, chunk=chunk or w.chunk, gate_norm=w.gate_norm,
+                           subseg_chunks=subseg)
+
+
+def test_workload0_tiny_fp32():
+    note("workload 0 (tiny fp32, head decay, s_in), la_chunk_fwd direct")
+    w = W0
+    inp = make_inputs(w, "cpu")
+    o_ref, s_ref = oracle_run(inp, w)
+    d = to_dev(inp)
+    o, s = _fwd(d, w)
+    torch.cuda.synchronize()
+    assert rel_err(o, o_ref) <= TOL["f32"]
+    assert rel_err(s, s_ref) <= TOL["f32"]
+    note("workload 0 device step (local + combine + correct)")
+    o2, s2 = pipeline.device_step(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode=w.mode, chunk=w.chunk)
+    torch.cuda.synchronize()
+    assert rel_err(o2, o_ref) <= TOL["f32"]
+    assert rel_err(s2, s_ref[:, :, 0]) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("dk,dv,L,chunk", [(16, 16, 200, 16), (32, 64, 301, 32), (64, 32, 130, 64),
+                                            (128, 128, 160, 64), (16, 128, 77, 32)])
+def test_generic_fp32(mode, dk, dv, L, chunk):
+    decay = {"none": "none", "head": "head_uniform", "gate": "gate"}[mode]
+    w = W0.scaled(B=2, H=2, L=L, dk=dk, dv=dv, decay=decay, chunk=chunk, seed=100 + dk + L)
+    note(f"generic fp32 mode={mode} dk={dk} dv={dv} L={L} chunk={chunk}")
+    inp = make_inputs(w, "cpu")
+    o_ref, s_ref = oracle_run(inp, w)
+    o, s = _fwd(to_dev(inp), w)
+    torch.cuda.synchronize()
+    assert rel_err(o, o_ref) <= TOL["f32"]
+    assert rel_err(s, s_ref) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("L,subseg", [(64 * 9 + 17, 0), (64 * 12, 3), (64 * 7, 1), (33, 0), (64 * 20 + 5, 8)])
+def test_bf16_d128(mode, L, subseg):
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    w = W2.scaled(B=2, H=3, L=L, decay=decay, s_in_std=0.05, seed=200 + L + subseg)
+    note(f"bf16 d128 chunk64 mode={mode} L={L} subseg_chunks={subseg}")
+    inp = make_inputs(w, "cpu")
+    o_ref, s_ref = oracle_run(inp, w)
+    o, s = _fwd(to_dev(inp), w, subseg=subseg)
+    torch.cuda.synchronize()
+    assert rel_err(o, o_ref) <= TOL["bf16"]
+    assert rel_err(s, s_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+def test_bf16_generic_other_dims(mode):
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    w = W2.scaled(B=1, H=2, L=300, dk=64, dv=32, decay=decay, chunk=32, s_in_std=0.05, seed=7)
+    note(f"bf16 generic dk=64 dv=32 chunk=32 mode={mode}")
+    inp = make_inputs(w, "cpu")
+    o_ref, s_ref = oracle_run(inp, w)
+    o, s = _fwd(to_dev(inp), w)
+    torch.cuda.synchronize()
+    assert rel_err(o, o_ref) <= TOL["bf16"]
+    assert rel_err(s, s_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+def test_segmented_nseg(mode):
+    """la_chunk_fwd with nseg > 1 treats segments as independent sequences."""
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    w = W2.scaled(B=1, H=2, L=6 * 200, decay=decay, s_in_std=0.05, seed=31)
+    note(f"la_chunk_fwd nseg=6 mode={mode}")
+    inp = make_inputs(w, "cpu")
+    o_ref, s_ref = oracle_run(inp, w, nseg=6)
+    o, s = _fwd(to_dev(inp), w, nseg=6)
+    torch.cuda.synchronize()
+    assert rel_err(o, o_ref) <= TOL["bf16"]
+    assert rel_err(s, s_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_segmented_pipeline_equals_one_pass(mode, dtype):
+    """The P-segment pipeline (local pass, state scan, correction) reproduces the one-pass
+    recurrence over the whole sequence: outputs and the final state."""
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    dk = 128 if dtype == "bf16" else 32
+    w = W2.scaled(B=1, H=2, L=8 * 192, dk=dk, dv=dk, dtype=dtype, decay=decay, s_in_std=0.05, seed=41)
+    note(f"segmented pipeline P=8 mode={mode} dtype={dtype}")
+    inp = make_inputs(w, "cpu")
+    o_ref, s_ref = oracle_run(inp, w, nseg=1)
+    d = to_dev(inp)
+    o, states = pipeline.segmented_forward(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode=w.mode, nseg=8)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert rel_err(o, o_ref) <= tol
+    assert rel_err(states[:, :, -1], s_ref[:, :, 0]) <= tol
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+def test_device_step_combine(mode):
+    """Local pass from zero + two-entry scan with S_recv + correction == one pass from S_recv."""
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    w = W2.scaled(B=2, H=2, L=700, decay=decay, s_in_std=0.05, seed=51)
+    note(f"device step combine mode={mode}")
+    inp = make_inputs(w, "cpu")
+    o_ref, s_ref = oracle_run(inp, w)
+    d = to_dev(inp)
+    o, s = pipeline.device_step(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode=w.mode)
+    torch.cuda.synchronize()
+    assert rel_err(o, o_ref) <= TOL["bf16"]
+    assert rel_err(s, s_ref[:, :, 0]) <= TOL["bf16"]
+
+
+def test_state_scan_matches_oracle():
+    note("la_state_scan random P=13")
+    g = torch.Generator().manual_seed(5)
+    B, H, P, dk, dv = 2, 3, 13, 64, 32
+    x = torch.randn((B, H, P, dk, dv), generator=g)
+    lam = torch.rand((B, H, P, dk), generator=g)
+    ref = oracle.state_scan(x.double().numpy(), lam.double().numpy())
+    out = lb.la_state_scan(x.cuda(), lam.cuda())
+    torch.cuda.synchronize()
+    assert rel_err(out, ref) <= 1e-6
+    xi = x.cuda().clone()
+    lb.la_state_scan(xi, lam.cuda(), xi)  # in place
+    torch.cuda.synchronize()
+    assert torch.equal(xi, out)
+    # integer states with unit decay: an exact running sum
+    xint = torch.randint(-8, 9, (B, H, P, dk, dv), generator=g).float()
+    out = lb.la_state_scan(xint.cuda(), torch.ones((B, H, P, dk)).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), torch.cumsum(xint, dim=2))
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64), ("bf16", 32)])
+def test_state_correct_matches_oracle(mode, dtype, dk):
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    P = 3
+    w = W2.scaled(B=2, H=2, L=P * 150, dk=dk, dv=dk, dtype=dtype, decay=decay, s_in_std=0.05, seed=61)
+    note(f"la_state_correct mode={mode} dtype={dtype} dk={dk}")
+    inp = make_inputs(w, "cpu")
+    g = torch.Generator().manual_seed(62)
+    s_recv = torch.randn((w.B, w.H, P - 1, dk, dk), generator=g) * 0.05
+    o0 = (torch.randn((w.B, w.H, w.L, dk), generator=g) * 0.1).to(inp["q"].dtype)
+    cum_ref, _ = oracle.cumdecay(w.B, w.H, w.L, dk, ORC_MODE[w.mode], host32(inp["decay"]), nseg=P,
+                                 gate_norm=w.gate_norm)
+    ref = oracle.state_correct(host32(inp["q"]), cum_ref, s_recv.double().numpy(), host32(o0), nseg=P, seg_begin=1)
+    d = to_dev(inp)
+    cum = None
+    if w.mode == "gate":
+        cum, _ = lb.la_cumdecay(d["decay"], w.B, w.H, w.L, dk, mode="gate", nseg=P, want_total=False)
+    elif w.mode == "head":
+        cum = d["decay"]
+    o = o0.cuda()
+    lb.la_state_correct(d["q"], cum, s_recv.cuda(), o, mode=w.mode, nseg=P, seg_begin=1)
+    torch.cuda.synchronize()
+    assert rel_err(o, ref) <= TOL[dtype]
+    # segment 0 is untouched bit-for-bit
+    assert torch.equal(o[:, :, :150].cpu(), o0[:, :, :150])
+    # a zero incoming state leaves the outputs bit-identical (the reviewers' S_recv = 0 ablation)
+    o2 = o0.cuda()
+    lb.la_state_correct(d["q"], cum, torch.zeros_like(s_recv).cuda(), o2, mode=w.mode, nseg=P, seg_begin=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.cpu(), o0)
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+def test_cumdecay_matches_oracle(mode):
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    P = 4
+    w = W2.scaled(B=2, H=3, L=P * 700, dk=64, dv=64, decay=decay, seed=71)
+    note(f"la_cumdecay mode={mode}")
+    inp = make_inputs(w, "cpu")
+    cref, tref = oracle.cumdecay(w.B, w.H, w.L, w.dk, ORC_MODE[w.mode], host32(inp["decay"]), nseg=P,
+                                 gate_norm=w.gate_norm)
+    cum, tot = lb.la_cumdecay(to_dev(inp)["decay"], w.B, w.H, w.L, w.dk, mode=w.mode, nseg=P, device="cuda")
+    torch.cuda.synchronize()
+    # per element relative error (values span many decades)
+    c = cum.cpu().double().numpy()
+    assert np.max(np.abs(c - cref) / np.maximum(np.abs(cref), 1e-30)) < 2e-4
+    t = tot.cpu().double().numpy()
+    assert np.max(np.abs(t - tref) / np.maximum(np.abs(tref), 1e-30)) < 2e-4
+
+
+@pytest.mark.parametrize("path", ["f32_d16", "bf16_d128"])
+def test_integer_inputs_bit_exact(path):
+    """a = 1, q, k, v in {-1, 0, 1}, integer s_in with |s_in| <= 8.  Every intermediate is an integer
+    below 2^24 (and below 256 where the bf16 path rounds operands), so the GPU must reproduce the
+    exact result, rounded once to the output dtype, whatever its summation order."""
+    g = torch.Generator().manual_seed(81)
+    if path == "f32_d16":
+        B, H, L, d, dt = 1, 2, 1000, 16, torch.float32
+    else:
+        B, H, L, d, dt = 1, 2, 192, 128, torch.bfloat16
+    note(f"integer bit-exact {path}")
+    q, k, v = (torch.randint(-1, 2, (B, H, L, d), generator=g).to(dt) for _ in range(3))
+    s_in = torch.randint(-8, 9, (B, H, d, d), generator=g).float()
+    o_ref, s_ref = oracle.recurrence(host32(q), host32(k), host32(v), oracle.NONE, None, s_in.double().numpy())
+    for subseg in (0, 1):
+        o, s = lb.la_chunk_fwd(q.cuda(), k.cuda(), v.cuda(), None, s_in.cuda(), mode="none", subseg_chunks=subseg)
+        torch.cuda.synchronize()
+        assert torch.equal(o.cpu(), torch.from_numpy(o_ref).to(dt)), subseg
+        assert torch.equal(s.cpu().double(), torch.from_numpy(s_ref)), subseg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_impulse_causality_and_determinism(dtype):
+    """Changing token j leaves o_t bit-identical for every t < j; two runs are bit-identical."""
+    dk = 128 if dtype == "bf16" else 32
+    w = W2.scaled(B=1, H=2, L=1000, dk=dk, dv=dk, dtype=dtype, decay="head_pow2", seed=91)
+    note(f"impulse/causality {dtype}")
+    d = to_dev(make_inputs(w, "cpu"))
+    o1, s1 = _fwd(d, w)
+    o1b, s1b = _fwd(d, w)
+    for j in (0, 63, 64, 65, 500, 999):
+        d2 = {k: (None if t is None else t.clone()) for k, t in d.items()}
+        for key in ("q", "k", "v"):
+            d2[key][:, :, j] += 0.5
+        o2, _ = _fwd(d2, w)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[:, :, :j], o2[:, :, :j]), j
+        assert not torch.equal(o1[:, :, j:], o2[:, :, j:]), j
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o1b) and torch.equal(s1, s1b)
+
+
+def test_chunk_and_split_invariance():
+    """Chunk length and internal sub-segment length change rounding only."""
+    w = W3.scaled(B=1, H=2, L=2048, dtype="f32", dk=32, dv=32, seed=95)
+    note("chunk-size invariance fp32 gate")
+    d = to_dev(make_inputs(w, "cpu"))
+    outs = [_fwd(d, w, chunk=c)[0] for c in (16, 32, 64)]
+    torch.cuda.synchronize()
+    ref = outs[0].double().cpu().numpy()
+    for o in outs[1:]:
+        assert rel_err(o, ref) <= 1e-5
+    w = W3.scaled(B=1, H=2, L=64 * 40, seed=96)
+    note("sub-segment invariance bf16 gate d128")
+    d = to_dev(make_inputs(w, "cpu"))
+    o_ref, _ = oracle_run(make_inputs(w, "cpu"), w)
+    for subseg in (0, 1, 2, 5, 40, 1000):
+        o, _ = _fwd(d, w, subseg=subseg)
+        torch.cuda.synchronize()
+        assert rel_err(o, o_ref) <= TOL["bf16"], subseg
+    o32, _ = _fwd(d, w, chunk=32)  # generic bf16 path
+    torch.cuda.synchronize()
+    assert rel_err(o32, o_ref) <= TOL["bf16"]
+
+
+def test_edge_cases():
+    note("edge cases: empty L, B=0, L < chunk, L=1, a=1 head, a=0 head")
+    w = W2.scaled(B=2, H=2, L=0, s_in_std=0.05, seed=99)
+    d = to_dev(make_inputs(w, "cpu"))
+    o, s = _fwd(d, w, nseg=3)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    assert torch.equal(s[:, :, 0], d["s_in"]) and torch.all(s[:, :, 1:] == 0)
+    w = W2.scaled(B=0, L=100, seed=99)
+    d = to_dev(make_inputs(w, "cpu"))
+    o, s = _fwd(d, w)
+    assert o.numel() == 0
+    for L in (1, 5, 63):
+        w = W2.scaled(B=1, H=2, L=L, s_in_std=0.05, seed=100 + L)
+        inp = make_inputs(w, "cpu")
+        o_ref, s_ref = oracle_run(inp, w)
+        o, s = _fwd(to_dev(inp), w)
+        torch.cuda.synchronize()
+        assert rel_err(o, o_ref) <= TOL["bf16"] and rel_err(s, s_ref) <= TOL["bf16"], L
+    # head mode with lambda = 0 equals no decay; lambda = -inf gives a = 0
+    w = W2.scaled(B=1, H=2, L=300, s_in_std=0.05, seed=111)
+    inp = make_inputs(w, "cpu")
+    d = to_dev(inp)
+    for lam, ref_mode in ((0.0, "none"), (-float("inf"), "zero")):
+        dec = torch.full((2,), lam, device="cuda")
+        o, s = lb.la_chunk_fwd(d["q"], d["k"], d["v"], dec, d["s_in"], mode="head")
+        torch.cuda.synchronize()
+        dec_h = np.full(2, lam, np.float32)
+        o_ref, s_ref = oracle.recurrence(host32(inp["q"]), host32(inp["k"]), host32(inp["v"]), oracle.HEAD, dec_h,
+                                         host32(inp["s_in"]).astype(np.float64))
+        assert rel_err(o, o_ref) <= TOL["bf16"], lam
+        assert rel_err(s, s_ref) <= TOL["bf16"], lam
