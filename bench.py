@@ -1,0 +1,210 @@
+"""Throughput of one device's share of ZeCO causal linear attention on one MI355X.
+
+A step is one pass of the whole per-device path over one batch of synthetic input at the
+pages' per-device shape (B=1, H=16, L=16384, dk=dv=128, bf16, chunk 64, no decay, S_recv = 0):
+  la_chunk_fwd     local chunked forward from a zero state  -> O_local, S_loc
+  la_cumdecay      the segment's total decay Lambda
+  la_state_scan    All-Scan update S_out = Lambda S_recv + S_loc (two-entry scan)
+  la_state_correct O += (Q * cumulative decay) S_recv
+Prints one JSON line.  Per-kernel durations come from HIP events that the library records
+around every kernel on the stream it launches them on (la_trace); the dominant kernel's
+roofline uses its algorithmic bytes (q, k, v read + o written) over its mean duration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_fwd_mfma_output_pass.json")
+KERNEL_SRC = os.path.join(ROOT, "chunked_scan_amd", "csrc", "chunk_fwd_mfma.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic(w, mode_bytes_gate: int):
+    """Per token-head algorithmic bytes and flops of the local forward (q, k, v read, o written;
+    QK^T, PV, QS and K^T V on full 64 x 64 chunk tiles)."""
+    es = 2 if w.dtype == "bf16" else 4
+    by = es * (2 * w.dk + 2 * w.dv) + mode_bytes_gate
+    fl = 2 * w.chunk * w.dk + 2 * w.chunk * w.dv + 2 * w.dk * w.dv + 2 * w.dk * w.dv
+    return by, fl
+
+
+def cpu_baseline(w, inp):
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import HEAD, NONE, GATE
+
+    threads = min(16, oracle.default_threads())
+    f32 = lambda t: None if t is None else t.to("cpu", torch.float32).numpy()  # noqa: E731
+    q, k, v = f32(inp["q"]), f32(inp["k"]), f32(inp["v"])
+    mode = {"none": NONE, "head": HEAD, "gate": GATE}[w.mode]
+    s_in = None if inp["s_in"] is None else f32(inp["s_in"]).astype(np.float64)
+    oracle.build(force=False)
+    # the whole workload is the sample; it is repeated until about 10 s of CPU time have passed
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o_ref, s_ref = oracle.recurrence(q, k, v, mode, f32(inp["decay"]), s_in, threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or reps >= 100:
+            break
+    items = w.B * w.H * ((w.dv + 15) // 16)
+    used = min(threads, items)
+    return dict(value=reps * w.B * w.L / dt, unit="tokens/s", cores=used, kind="oracle",
+                sample=f"whole workload (B={w.B} H={w.H} L={w.L} d={w.dk}) x {reps} repetitions, fp64 "
+                       f"token-by-token recurrence in C, {dt:.1f} s on {used} threads "
+                       f"({platform.processor() or 'host'})"), (o_ref, s_ref)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, help="index into chunked_scan_amd.inputs.WORKLOADS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on one "
+              "GPU and needs no collectives).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from chunked_scan_amd import binding
+    from chunked_scan_amd.inputs import WORKLOADS, make_inputs
+    from chunked_scan_amd.pipeline import DeviceStep
+
+    w = WORKLOADS[args.workload]
+    if w.nseg != 1:
+        raise SystemExit("bench.py times the single-segment device step; pick a one-segment workload")
+    torch.cuda.set_device(0)
+    log(f"[bench] workload {args.workload} {w.name}: generating inputs on cuda:0")
+    inp = make_inputs(w, "cuda")
+    step = DeviceStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk,
+                      gate_norm=w.gate_norm)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    # --- timed region 1: the step as a user runs it (no per-kernel events)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+
+    # --- timed region 2: the same steps with HIP events around every kernel (la_trace)
+    timers = [{c: binding.KernelTimer(4) for c in ("fwd", "cum", "scan", "corr")} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step.run(timers=timers[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_traced = e0.elapsed_time(e1) / args.steps
+    per_kernel = {}
+    for tset in timers:
+        for c in ("fwd", "cum", "scan", "corr"):
+            for name, ms in tset[c].harvest():
+                per_kernel.setdefault(name, []).append(ms)
+    kernels = {n: dict(mean_us=1e3 * sum(v) / len(v), launches_per_step=len(v) / args.steps,
+                       min_us=1e3 * min(v)) for n, v in per_kernel.items()}
+    log("[bench] per kernel: " + ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in kernels.items()))
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+
+    tokens = w.B * w.L
+    gate_bytes = 4 * w.dk if w.mode == "gate" else 0
+    by_tok, fl_tok = algorithmic(w, gate_bytes)
+    dom = max(kernels, key=lambda n: kernels[n]["mean_us"] * kernels[n]["launches_per_step"])
+    dom_us = kernels[dom]["mean_us"]
+    traffic = None
+    if dom == "chunk_fwd_mfma_output_pass" and os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_sha256_16") == source_hash() and tr.get("workload") == w.name:
+            traffic = tr["bytes_per_launch"]
+    alg_bytes = tokens * w.H * by_tok if dom == "chunk_fwd_mfma_output_pass" else None
+    roof = None
+    if alg_bytes is not None:
+        achieved = alg_bytes / (dom_us * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=dom,
+                    kernel_mean_us=round(dom_us, 2), algorithmic_bytes=alg_bytes,
+                    mfma_frac=round(tokens * w.H * fl_tok / (dom_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        cpu, (o_ref, s_ref) = cpu_baseline(w, inp)
+        o, s_out = step.run()
+        torch.cuda.synchronize()
+        import numpy as np
+        err_o = float(np.max(np.abs(o.float().cpu().numpy() - o_ref)) / np.max(np.abs(o_ref)))
+        err_s = float(np.max(np.abs(s_out.cpu().numpy() - s_ref[:, :, 0])) / max(np.max(np.abs(s_ref)), 1e-30))
+        cpu["parity_err_o"], cpu["parity_err_s"] = err_o, err_s
+        log(f"[bench] oracle {cpu['value']:.3e} tokens/s; full-size parity err O {err_o:.2e} S {err_s:.2e}")
+
+    out = {
+        "metric": "tokens/s per GPU, linear-attn fwd (L=16k,H=16,dk=128) + % MFMA/HBM peak",
+        "value": round(tokens / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: device step = local chunked fwd + All-Scan state combine + "
+                               f"output correction", "B": w.B, "H": w.H, "L": w.L, "dk": w.dk, "dv": w.dv,
+                   "chunk": w.chunk, "decay": w.decay, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": {n: {k: round(v, 2) for k, v in d.items()} for n, d in kernels.items()},
+        "ms_per_step_with_kernel_events": round(ms_traced, 5),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

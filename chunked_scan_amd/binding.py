@@ -28,6 +28,15 @@ EXPORTS = ("la_chunk_fwd", "la_state_scan", "la_state_correct", "la_cumdecay", "
            "la_supported", "la_version")
 
 
+TRACE_MAX = 8
+
+
+class Trace(ctypes.Structure):
+    """la_trace: caller-created HIP events the library records around each kernel it enqueues."""
+    _fields_ = [("start", ctypes.c_void_p * TRACE_MAX), ("stop", ctypes.c_void_p * TRACE_MAX),
+                ("capacity", ctypes.c_int32), ("count", ctypes.c_int32), ("name", ctypes.c_char_p * TRACE_MAX)]
+
+
 class Shape(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("L", ctypes.c_int64),
@@ -35,7 +44,30 @@ class Shape(ctypes.Structure):
         ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("decay_mode", ctypes.c_int32),
         ("gate_norm", ctypes.c_float), ("seg_begin", ctypes.c_int32), ("state_stride", ctypes.c_int64),
         ("total_stride", ctypes.c_int64), ("subseg_chunks", ctypes.c_int32), ("stream", ctypes.c_void_p),
+        ("trace", ctypes.POINTER(Trace)),
     ]
+
+
+class KernelTimer:
+    """Per-kernel HIP-event timing through la_trace.  ``attach(shape)`` hooks a call; after the
+    stream is synchronised ``harvest()`` returns [(kernel name, ms)] for the last hooked call."""
+
+    def __init__(self, capacity: int = TRACE_MAX):
+        self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(capacity)]
+        for a, b in self.events:  # torch creates the HIP event on first record
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        self.trace = Trace()
+        self.trace.capacity = capacity
+        for i, (a, b) in enumerate(self.events):
+            self.trace.start[i] = a.cuda_event
+            self.trace.stop[i] = b.cuda_event
+
+    def harvest(self):
+        return [(self.trace.name[i].decode(), self.events[i][0].elapsed_time(self.events[i][1]))
+                for i in range(self.trace.count)]
 
 
 class LaError(RuntimeError):
@@ -128,16 +160,19 @@ def mode_code(mode: Optional[str], decay: Optional[torch.Tensor]) -> int:
 
 
 def make_shape(B, H, L, dk, dv, *, nseg=1, dtype=LA_BF16, mode=0, gate_norm=16.0, seg_begin=0,
-               state_stride=0, total_stride=0, subseg_chunks=0, stream=None) -> Shape:
-    return Shape(B, H, L, dk, dv, nseg, dtype, dtype, mode, gate_norm, seg_begin, state_stride,
-                 total_stride, subseg_chunks, stream)
+               state_stride=0, total_stride=0, subseg_chunks=0, stream=None, timer=None) -> Shape:
+    s = Shape(B, H, L, dk, dv, nseg, dtype, dtype, mode, gate_norm, seg_begin, state_stride,
+              total_stride, subseg_chunks, stream)
+    if timer is not None:
+        s.trace = ctypes.pointer(timer.trace)
+    return s
 
 
 def la_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch.Tensor] = None,
                  s_in: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
                  s_out: Optional[torch.Tensor] = None, *, mode: Optional[str] = None, nseg: int = 1,
                  chunk: int = 64, gate_norm: float = 16.0, subseg_chunks: int = 0, want_state: bool = True,
-                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                 stream=None, timer=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise forward.  q, k [B,H,L,dk], v [B,H,L,dv] (f32 or bf16); decay None / [H] / [B,H,L,dk];
     s_in [B,H,dk,dv] f32 or None.  Returns (o [B,H,L,dv], s_out [B,H,nseg,dk,dv] f32 or None);
     s_out may be a view with evenly spaced dense (b,h) blocks."""
@@ -161,14 +196,14 @@ def la_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optio
         _dev(s_out, "s_out", torch.float32, (B, H, nseg, dk, dv), contiguous=False)
         stride = _bh_stride(s_out, "s_out", dk * dv)
     shp = make_shape(B, H, L, dk, dv, nseg=nseg, dtype=_dtype_code(q), mode=m, gate_norm=gate_norm,
-                     state_stride=stride, subseg_chunks=subseg_chunks, stream=_stream(stream))
+                     state_stride=stride, subseg_chunks=subseg_chunks, stream=_stream(stream), timer=timer)
     _check("la_chunk_fwd", lib().la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(o),
                                               _ptr(s_out), ctypes.byref(shp), chunk))
     return o, s_out
 
 
 def la_state_scan(seg_states: torch.Tensor, seg_decay: torch.Tensor, out_states: Optional[torch.Tensor] = None,
-                  *, stream=None) -> torch.Tensor:
+                  *, stream=None, timer=None) -> torch.Tensor:
     """Inclusive scan over axis 2: seg_states [B,H,P,dk,dv] f32, seg_decay [B,H,P,dk] f32 (dense).
     out_states may be seg_states itself (in place)."""
     B, H, P, dk, dv = seg_states.shape
@@ -177,14 +212,15 @@ def la_state_scan(seg_states: torch.Tensor, seg_decay: torch.Tensor, out_states:
     if out_states is None:
         out_states = torch.empty_like(seg_states)
     _dev(out_states, "out_states", torch.float32, (B, H, P, dk, dv))
-    shp = make_shape(B, H, 0, dk, dv, stream=_stream(stream))
+    shp = make_shape(B, H, 0, dk, dv, stream=_stream(stream), timer=timer)
     _check("la_state_scan", lib().la_state_scan(_ptr(seg_states), _ptr(seg_decay), P, _ptr(out_states),
                                                 ctypes.byref(shp)))
     return out_states
 
 
 def la_state_correct(q: torch.Tensor, cumdecay: Optional[torch.Tensor], s_recv: torch.Tensor, o: torch.Tensor, *,
-                     mode: Optional[str] = None, nseg: int = 1, seg_begin: int = 0, stream=None) -> torch.Tensor:
+                     mode: Optional[str] = None, nseg: int = 1, seg_begin: int = 0, stream=None,
+                     timer=None) -> torch.Tensor:
     """o += (q * cum) @ s_recv[p - seg_begin] for segments p >= seg_begin, in place.
     cumdecay: None (none), [H] log-decay (head) or [B,H,L,dk] cumulative decay (gate).
     s_recv: f32 [B,H,nseg-seg_begin,dk,dv], possibly a view with evenly spaced dense (b,h) blocks."""
@@ -199,7 +235,7 @@ def la_state_correct(q: torch.Tensor, cumdecay: Optional[torch.Tensor], s_recv: 
     _dev(s_recv, "s_recv", torch.float32, (B, H, np_, dk, dv), contiguous=False)
     stride = _bh_stride(s_recv, "s_recv", dk * dv)
     shp = make_shape(B, H, L, dk, dv, nseg=nseg, dtype=_dtype_code(q), mode=m, seg_begin=seg_begin,
-                     state_stride=stride, stream=_stream(stream))
+                     state_stride=stride, stream=_stream(stream), timer=timer)
     _check("la_state_correct", lib().la_state_correct(_ptr(q), _ptr(cumdecay), _ptr(s_recv), _ptr(o),
                                                       ctypes.byref(shp)))
     return o
@@ -208,7 +244,7 @@ def la_state_correct(q: torch.Tensor, cumdecay: Optional[torch.Tensor], s_recv: 
 def la_cumdecay(decay: Optional[torch.Tensor], B: int, H: int, L: int, dk: int, *, mode: Optional[str] = None,
                 nseg: int = 1, gate_norm: float = 16.0, cum: Optional[torch.Tensor] = None,
                 total: Optional[torch.Tensor] = None, want_cum: bool = True, want_total: bool = True,
-                device=None, stream=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+                device=None, stream=None, timer=None) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Returns (cumdecay [B,H,L,dk] or None, total [B,H,nseg,dk] or None), both f32.  total may be a
     view with evenly spaced dense (b,h) blocks."""
     m = mode_code(mode, decay)
@@ -226,6 +262,6 @@ def la_cumdecay(decay: Optional[torch.Tensor], B: int, H: int, L: int, dk: int, 
         _dev(total, "total", torch.float32, (B, H, nseg, dk), contiguous=False)
         tstride = _bh_stride(total, "total", dk)
     shp = make_shape(B, H, L, dk, dk, nseg=nseg, mode=m, gate_norm=gate_norm, total_stride=tstride,
-                     stream=_stream(stream))
+                     stream=_stream(stream), timer=timer)
     _check("la_cumdecay", lib().la_cumdecay(_ptr(decay), _ptr(cum), _ptr(total), ctypes.byref(shp)))
     return cum, total

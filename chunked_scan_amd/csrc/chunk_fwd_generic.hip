@@ -144,16 +144,16 @@ hipError_t launch_typed(const FwdArgs& a) {
     T* o = (T*)a.o;
     switch (a.mode) {
         case DECAY_HEAD:
-            chunk_fwd_generic_kernel<T, DECAY_HEAD><<<grid, 256, 0, a.stream>>>(
-                q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, a.H, a.L, a.dk, a.dv, a.nseg, a.chunk, a.inv_norm);
+            LA_TRACED(a.tr, "chunk_fwd_generic", chunk_fwd_generic_kernel<T, DECAY_HEAD><<<grid, 256, 0, a.stream>>>(
+                q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, a.H, a.L, a.dk, a.dv, a.nseg, a.chunk, a.inv_norm));
             break;
         case DECAY_GATE:
-            chunk_fwd_generic_kernel<T, DECAY_GATE><<<grid, 256, 0, a.stream>>>(
-                q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, a.H, a.L, a.dk, a.dv, a.nseg, a.chunk, a.inv_norm);
+            LA_TRACED(a.tr, "chunk_fwd_generic", chunk_fwd_generic_kernel<T, DECAY_GATE><<<grid, 256, 0, a.stream>>>(
+                q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, a.H, a.L, a.dk, a.dv, a.nseg, a.chunk, a.inv_norm));
             break;
         default:
-            chunk_fwd_generic_kernel<T, DECAY_NONE><<<grid, 256, 0, a.stream>>>(
-                q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, a.H, a.L, a.dk, a.dv, a.nseg, a.chunk, a.inv_norm);
+            LA_TRACED(a.tr, "chunk_fwd_generic", chunk_fwd_generic_kernel<T, DECAY_NONE><<<grid, 256, 0, a.stream>>>(
+                q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, a.H, a.L, a.dk, a.dv, a.nseg, a.chunk, a.inv_norm));
             break;
     }
     return hipGetLastError();

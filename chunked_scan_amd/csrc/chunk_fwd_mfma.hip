@@ -1,5 +1,5 @@
-// chunk_fwd_mfma.hip -- bf16 matrix-core (MFMA) chunked forward for dk = dv = 128, chunk = 64,
-// and the bf16 output correction, for gfx950.
+// chunk_fwd_mfma.hip -- bf16 matrix-core (MFMA) chunked forward for dk = dv = 128, chunk = 64
+// on gfx950.
 //
 // Work unit.  One workgroup (4 waves, 256 lanes) owns one sub-segment of one (b, h, segment) and
 // walks its 64-token chunks in order.  The fp32 state S (128 x 128) lives in accumulator
@@ -398,7 +398,7 @@ hipMemPool_t workspace_pool(int dev) {
         hipMemPool_t p = nullptr;
         if (hipMemPoolCreate(&p, &props) != hipSuccess) return nullptr;
         uint64_t keep = ~0ull;
-        hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+        (void)hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
         pools[dev] = p;
     }
     return pools[dev];
@@ -412,17 +412,19 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
     const __bf16* v = (const __bf16*)a.v;
     __bf16* o = (__bf16*)a.o;
     if (G > 1) {
-        mfma_fwd_kernel<MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
-            q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H, a.L,
-            a.nseg, G, cps, a.inv_norm);
+        LA_TRACED(a.tr, "chunk_fwd_mfma_state_pass",
+                  mfma_fwd_kernel<MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
+                      q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
+                      a.L, a.nseg, G, cps, a.inv_norm));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream);
+        e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream, a.tr);
         if (e != hipSuccess) return e;
     }
-    mfma_fwd_kernel<MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
-        q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, nullptr, part_state, a.H, a.L, a.nseg, G,
-        cps, a.inv_norm);
+    LA_TRACED(a.tr, "chunk_fwd_mfma_output_pass",
+              mfma_fwd_kernel<MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
+                  q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, nullptr, part_state, a.H, a.L,
+                  a.nseg, G, cps, a.inv_norm));
     return hipGetLastError();
 }
 
@@ -479,7 +481,5 @@ hipError_t launch_chunk_fwd_mfma(const FwdArgs& a) {
     }
     return e;
 }
-
-hipError_t launch_state_correct(const CorrectArgs& a) { return launch_state_correct_generic(a); }
 
 }  // namespace la

@@ -105,6 +105,24 @@ la_status validate_fwd(const void* q, const void* k, const void* v, const float*
 
 la_status from_hip(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH; }
 
+la_status check_trace(const la_shape* s) {
+    la_trace* t = s->trace;
+    if (!t) return LA_OK;
+    if (t->capacity < 0 || t->capacity > LA_TRACE_MAX_KERNELS) return LA_ERR_SHAPE;
+    for (int i = 0; i < t->capacity; i++)
+        if (!t->start[i] || !t->stop[i]) return LA_ERR_NULL;
+    return LA_OK;
+}
+
+// A tracer bound to the call's stream; resets the trace's count.
+la::Tracer make_tracer(const la_shape* s) {
+    la::Tracer tr;
+    tr.t = s->trace;
+    tr.s = (hipStream_t)s->stream;
+    if (tr.t) tr.t->count = 0;
+    return tr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,12 +153,15 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float*
                        float* s_out, const la_shape* s, int32_t chunk) {
     la_status st = validate_fwd(q, k, v, decay, s_in, o, s_out, s, chunk);
     if (st != LA_OK) return st;
+    if ((st = check_trace(s)) != LA_OK) return st;
+    la::Tracer tr = make_tracer(s);
     hipStream_t stream = (hipStream_t)s->stream;
     const int64_t so_stride = s->state_stride ? s->state_stride : (int64_t)s->nseg * s->dk * s->dv;
     if (s->B * s->H == 0) return LA_OK;
     if (s->L == 0) {
         if (!s_out) return LA_OK;
-        return from_hip(la::launch_empty_states(s_in, s_out, so_stride, s->B * s->H, s->nseg, s->dk, s->dv, stream));
+        return from_hip(
+            la::launch_empty_states(s_in, s_out, so_stride, s->B * s->H, s->nseg, s->dk, s->dv, stream, &tr));
     }
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.decay = decay; a.s_in = s_in; a.o = o; a.s_out = s_out;
@@ -152,6 +173,7 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float*
     a.inv_norm = s->decay_mode == LA_DECAY_GATE ? 1.f / s->gate_norm : 1.f;
     a.subseg_chunks = s->subseg_chunks;
     a.stream = stream;
+    a.tr = &tr;
     if (a.bf16 && a.dk == 128 && a.dv == 128 && chunk == 64) return from_hip(la::launch_chunk_fwd_mfma(a));
     return from_hip(la::launch_chunk_fwd_generic(a));
 }
@@ -169,9 +191,12 @@ la_status la_state_scan(const float* seg_states, const float* seg_decay, int32_t
     Span sl{seg_decay, sizeof(float) * (size_t)(s->B * s->H * P * s->dk)};
     if (seg_states != out_states && overlap(sx, sy)) return LA_ERR_ALIAS;
     if (overlap(sl, sy)) return LA_ERR_ALIAS;
+    la_status st = check_trace(s);
+    if (st != LA_OK) return st;
+    la::Tracer tr = make_tracer(s);
     if (nst == 0) return LA_OK;
     return from_hip(la::launch_state_scan(seg_states, seg_decay, out_states, s->B * s->H, P, s->dk, s->dv,
-                                          (hipStream_t)s->stream));
+                                          (hipStream_t)s->stream, &tr));
 }
 
 la_status la_state_correct(const void* q, const float* cumdecay, const float* s_recv, void* o, const la_shape* s) {
@@ -199,6 +224,8 @@ la_status la_state_correct(const void* q, const float* cumdecay, const float* s_
     if (overlap(so, Span{q, es * (size_t)nq}) || overlap(so, Span{cumdecay, cum_bytes}) ||
         overlap(so, Span{s_recv, recv_bytes}))
         return LA_ERR_ALIAS;
+    if ((st = check_trace(s)) != LA_OK) return st;
+    la::Tracer tr = make_tracer(s);
     if (ncorr == 0) return LA_OK;
     CorrectArgs a;
     a.q = q; a.cum = cumdecay; a.s_recv = s_recv; a.o = o;
@@ -208,6 +235,7 @@ la_status la_state_correct(const void* q, const float* cumdecay, const float* s_
     a.bf16 = s->in_dtype == LA_BF16;
     a.mode = s->decay_mode;
     a.stream = (hipStream_t)s->stream;
+    a.tr = &tr;
     return from_hip(la::launch_state_correct(a));
 }
 
@@ -227,10 +255,12 @@ la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const l
     Span sd{decay, decay_bytes(s)}, sc{cumdecay, cumdecay ? sizeof(float) * (size_t)ncum : 0};
     Span stt{total, (total && BH > 0) ? sizeof(float) * (size_t)((BH - 1) * tstride + s->nseg * s->dk) : 0};
     if (overlap(sc, sd) || overlap(stt, sd) || overlap(sc, stt)) return LA_ERR_ALIAS;
+    if ((st = check_trace(s)) != LA_OK) return st;
+    la::Tracer tr = make_tracer(s);
     if (!need) return LA_OK;
     const float inv_norm = s->decay_mode == LA_DECAY_GATE ? 1.f / s->gate_norm : 1.f;
     return from_hip(la::launch_cumdecay(decay, cumdecay, total, tstride, s->B, s->H, s->L, s->dk, s->nseg,
-                                        s->decay_mode, inv_norm, (hipStream_t)s->stream));
+                                        s->decay_mode, inv_norm, (hipStream_t)s->stream, &tr));
 }
 
 }  // extern "C"

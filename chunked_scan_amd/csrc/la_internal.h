@@ -4,7 +4,40 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "la_chunk.h"
+
 namespace la {
+
+
+
+// Brackets each enqueued kernel with the caller's trace events (no-op without a trace).
+struct Tracer {
+    la_trace* t = nullptr;
+    hipStream_t s = nullptr;
+    bool open = false;
+    void begin(const char* name) {
+        open = t && t->count < t->capacity;
+        if (open) {
+            t->name[t->count] = name;
+            (void)hipEventRecord((hipEvent_t)t->start[t->count], s);
+        }
+    }
+    void end() {
+        if (open) {
+            (void)hipEventRecord((hipEvent_t)t->stop[t->count], s);
+            t->count++;
+            open = false;
+        }
+    }
+};
+
+// Launches a kernel between the tracer's events: LA_TRACED(tr, "name", kernel<<<...>>>(...));
+#define LA_TRACED(tr, name, ...)        \
+    do {                                \
+        if (tr) (tr)->begin(name);      \
+        __VA_ARGS__;                    \
+        if (tr) (tr)->end();            \
+    } while (0)
 
 struct FwdArgs {
     const void* q;
@@ -22,6 +55,7 @@ struct FwdArgs {
     float inv_norm;      // 1 / gate_norm (gate mode)
     int subseg_chunks;   // 0 = automatic
     hipStream_t stream;
+    Tracer* tr;
 };
 
 struct CorrectArgs {
@@ -35,6 +69,7 @@ struct CorrectArgs {
     bool bf16;
     int mode;
     hipStream_t stream;
+    Tracer* tr;
 };
 
 // Generic chunked forward: fp32 arithmetic on VALU, q/k/v/o in f32 or bf16, dk, dv in
@@ -46,7 +81,7 @@ hipError_t launch_chunk_fwd_mfma(const FwdArgs& a);
 
 // out[n,p] = diag(lam[n,p]) out[n,p-1] + x[n,p] for n < nstates, p < P.  x may equal out.
 hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64_t nstates, int P,
-                             int dk, int dv, hipStream_t stream);
+                             int dk, int dv, hipStream_t stream, Tracer* tr);
 
 // Output correction: MFMA kernel for bf16 with dk = dv = 128, generic fp32-arithmetic kernel otherwise.
 hipError_t launch_state_correct(const CorrectArgs& a);
@@ -54,10 +89,10 @@ hipError_t launch_state_correct_generic(const CorrectArgs& a);
 
 // total of segment p of (b,h) goes to total[bh * total_stride + p * dk].
 hipError_t launch_cumdecay(const float* decay, float* cum, float* total, int64_t total_stride, int64_t B, int64_t H,
-                           int64_t L, int dk, int nseg, int mode, float inv_norm, hipStream_t stream);
+                           int64_t L, int dk, int nseg, int mode, float inv_norm, hipStream_t stream, Tracer* tr);
 
 // s_out[b,h,p] = (p == 0 && s_in) ? s_in[b,h] : 0 -- the final states of empty segments.
 hipError_t launch_empty_states(const float* s_in, float* s_out, int64_t s_out_stride, int64_t BH, int nseg, int dk,
-                               int dv, hipStream_t stream);
+                               int dv, hipStream_t stream, Tracer* tr);
 
 }  // namespace la

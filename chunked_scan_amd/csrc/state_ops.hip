@@ -193,16 +193,16 @@ hipError_t correct_typed(const CorrectArgs& a) {
     const int64_t ss = a.state_stride;
     switch (a.mode) {
         case DECAY_HEAD:
-            state_correct_generic_kernel<T, DECAY_HEAD><<<grid, 256, 0, a.stream>>>(
-                q, a.cum, a.s_recv, o, a.H, a.L, a.dk, a.dv, a.nseg, a.seg_begin, ss, ntiles);
+            LA_TRACED(a.tr, "state_correct_generic", state_correct_generic_kernel<T, DECAY_HEAD><<<grid, 256, 0, a.stream>>>(
+                q, a.cum, a.s_recv, o, a.H, a.L, a.dk, a.dv, a.nseg, a.seg_begin, ss, ntiles));
             break;
         case DECAY_GATE:
-            state_correct_generic_kernel<T, DECAY_GATE><<<grid, 256, 0, a.stream>>>(
-                q, a.cum, a.s_recv, o, a.H, a.L, a.dk, a.dv, a.nseg, a.seg_begin, ss, ntiles);
+            LA_TRACED(a.tr, "state_correct_generic", state_correct_generic_kernel<T, DECAY_GATE><<<grid, 256, 0, a.stream>>>(
+                q, a.cum, a.s_recv, o, a.H, a.L, a.dk, a.dv, a.nseg, a.seg_begin, ss, ntiles));
             break;
         default:
-            state_correct_generic_kernel<T, DECAY_NONE><<<grid, 256, 0, a.stream>>>(
-                q, a.cum, a.s_recv, o, a.H, a.L, a.dk, a.dv, a.nseg, a.seg_begin, ss, ntiles);
+            LA_TRACED(a.tr, "state_correct_generic", state_correct_generic_kernel<T, DECAY_NONE><<<grid, 256, 0, a.stream>>>(
+                q, a.cum, a.s_recv, o, a.H, a.L, a.dk, a.dv, a.nseg, a.seg_begin, ss, ntiles));
             break;
     }
     return hipGetLastError();
@@ -222,30 +222,33 @@ __global__ __launch_bounds__(256) void empty_states_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64_t nstates, int P, int dk, int dv,
-                             hipStream_t stream) {
+                             hipStream_t stream, Tracer* tr) {
     if (nstates == 0 || P == 0) return hipSuccess;
     const int64_t vec = (int64_t)dk * dv / 4;
     const int vblocks = (int)((vec + 255) / 256);
-    state_scan_kernel<<<(unsigned)(nstates * vblocks), 256, 0, stream>>>(x, lam, out, P, dk, dv, vec, vblocks);
+    LA_TRACED(tr, "state_scan",
+              state_scan_kernel<<<(unsigned)(nstates * vblocks), 256, 0, stream>>>(x, lam, out, P, dk, dv, vec, vblocks));
     return hipGetLastError();
 }
 
 hipError_t launch_cumdecay(const float* decay, float* cum, float* total, int64_t total_stride, int64_t B, int64_t H,
-                           int64_t L, int dk, int nseg, int mode, float inv_norm, hipStream_t stream) {
+                           int64_t L, int dk, int nseg, int mode, float inv_norm, hipStream_t stream, Tracer* tr) {
     const int64_t n_cum = B * H * L * dk;
     const int64_t n_tot = B * H * (int64_t)nseg * dk;
     if (mode != DECAY_GATE) {
         const int64_t n = max(cum ? n_cum : 0, total ? n_tot : 0);
         if (n == 0) return hipSuccess;
-        cumdecay_closed_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(decay, cum, total, total_stride, H, L,
-                                                                               dk, nseg, n_cum, n_tot, mode);
+        LA_TRACED(tr, "cumdecay_closed",
+                  cumdecay_closed_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
+                      decay, cum, total, total_stride, H, L, dk, nseg, n_cum, n_tot, mode));
         return hipGetLastError();
     }
     const int64_t Ls = L / nseg;
     if (Ls == 0) {  // empty segments: cumulative decay is the empty product
         if (!total || n_tot == 0) return hipSuccess;
-        cumdecay_closed_kernel<<<(unsigned)((n_tot + 255) / 256), 256, 0, stream>>>(
-            decay, nullptr, total, total_stride, H, L, dk, nseg, 0, n_tot, DECAY_NONE);
+        LA_TRACED(tr, "cumdecay_closed",
+                  cumdecay_closed_kernel<<<(unsigned)((n_tot + 255) / 256), 256, 0, stream>>>(
+                      decay, nullptr, total, total_stride, H, L, dk, nseg, 0, n_tot, DECAY_NONE));
         return hipGetLastError();
     }
     const int nblk = (int)((Ls + CUM_TB - 1) / CUM_TB);
@@ -255,11 +258,14 @@ hipError_t launch_cumdecay(const float* decay, float* cum, float* total, int64_t
     hipError_t e = hipMallocAsync((void**)&partial, sizeof(float) * (size_t)nthreads, stream);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((nthreads + 255) / 256);
-    cumdecay_gate_blocksum_kernel<<<grid, 256, 0, stream>>>(decay, partial, L, dk, nseg, nblk, nthreads, inv_norm);
+    LA_TRACED(tr, "cumdecay_gate_blocksum",
+              cumdecay_gate_blocksum_kernel<<<grid, 256, 0, stream>>>(decay, partial, L, dk, nseg, nblk, nthreads,
+                                                                      inv_norm));
     e = hipGetLastError();
     if (e == hipSuccess) {
-        cumdecay_gate_scan_kernel<<<grid, 256, 0, stream>>>(decay, partial, cum, total, total_stride, L, dk, nseg,
-                                                            nblk, nthreads, inv_norm);
+        LA_TRACED(tr, "cumdecay_gate_scan",
+                  cumdecay_gate_scan_kernel<<<grid, 256, 0, stream>>>(decay, partial, cum, total, total_stride, L, dk,
+                                                                      nseg, nblk, nthreads, inv_norm));
         e = hipGetLastError();
     }
     hipError_t f = hipFreeAsync(partial, stream);
@@ -271,11 +277,13 @@ hipError_t launch_state_correct_generic(const CorrectArgs& a) {
 }
 
 hipError_t launch_empty_states(const float* s_in, float* s_out, int64_t s_out_stride, int64_t BH, int nseg, int dk,
-                               int dv, hipStream_t stream) {
+                               int dv, hipStream_t stream, Tracer* tr) {
     const int64_t SZ = (int64_t)dk * dv;
     const int64_t n = BH * nseg * SZ;
     if (n == 0) return hipSuccess;
-    empty_states_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(s_in, s_out, s_out_stride, nseg, SZ, n);
+    LA_TRACED(tr, "empty_states",
+              empty_states_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(s_in, s_out, s_out_stride, nseg,
+                                                                                   SZ, n));
     return hipGetLastError();
 }
 

@@ -45,15 +45,18 @@ class DeviceStep:
         self.totals = torch.ones((B, H, 2, dk), dtype=torch.float32, device=dev)
         self.cum = torch.empty((B, H, L, dk), dtype=torch.float32, device=dev) if mode == "gate" else None
 
-    def run(self):
+    def run(self, timers: Optional[dict] = None):
+        """One step.  ``timers`` optionally maps "fwd", "cum", "scan", "corr" to KernelTimers."""
         B, H, L, dk, dv = self.shape
+        t = timers or {}
         la_chunk_fwd(self.q, self.k, self.v, self.decay, None, self.o, self.states[:, :, 1:2], mode=self.mode,
-                     chunk=self.chunk, gate_norm=self.gate_norm, subseg_chunks=self.subseg_chunks)
+                     chunk=self.chunk, gate_norm=self.gate_norm, subseg_chunks=self.subseg_chunks,
+                     timer=t.get("fwd"))
         la_cumdecay(self.decay, B, H, L, dk, mode=self.mode, gate_norm=self.gate_norm, cum=self.cum,
-                    total=self.totals[:, :, 1:2], want_cum=self.mode == "gate")
-        la_state_scan(self.states, self.totals, self.states)
+                    total=self.totals[:, :, 1:2], want_cum=self.mode == "gate", timer=t.get("cum"))
+        la_state_scan(self.states, self.totals, self.states, timer=t.get("scan"))
         la_state_correct(self.q, _corr_decay(self.mode, self.decay, self.cum), self.states[:, :, 0:1], self.o,
-                         mode=self.mode)
+                         mode=self.mode, timer=t.get("corr"))
         return self.o, self.states[:, :, 1]
 
 
@@ -81,17 +84,20 @@ class SegmentedForward:
         self.totals = torch.empty((B, H, nseg, dk), dtype=torch.float32, device=dev)
         self.cum = torch.empty((B, H, L, dk), dtype=torch.float32, device=dev) if mode == "gate" else None
 
-    def run(self):
+    def run(self, timers: Optional[dict] = None):
+        """One pass.  ``timers`` optionally maps "fwd", "cum", "scan", "corr" to KernelTimers."""
         B, H, L, dk, dv = self.shape
         P = self.nseg
+        t = timers or {}
         la_chunk_fwd(self.q, self.k, self.v, self.decay, self.s_in, self.o, self.states, mode=self.mode, nseg=P,
-                     chunk=self.chunk, gate_norm=self.gate_norm, subseg_chunks=self.subseg_chunks)
+                     chunk=self.chunk, gate_norm=self.gate_norm, subseg_chunks=self.subseg_chunks,
+                     timer=t.get("fwd"))
         la_cumdecay(self.decay, B, H, L, dk, mode=self.mode, nseg=P, gate_norm=self.gate_norm, cum=self.cum,
-                    total=self.totals, want_cum=self.mode == "gate")
-        la_state_scan(self.states, self.totals, self.states)
+                    total=self.totals, want_cum=self.mode == "gate", timer=t.get("cum"))
+        la_state_scan(self.states, self.totals, self.states, timer=t.get("scan"))
         if P > 1:
             la_state_correct(self.q, _corr_decay(self.mode, self.decay, self.cum), self.states[:, :, : P - 1], self.o,
-                             mode=self.mode, nseg=P, seg_begin=1)
+                             mode=self.mode, nseg=P, seg_begin=1, timer=t.get("corr"))
         return self.o, self.states
 
 

@@ -61,6 +61,19 @@ typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
  *                   log a = -softplus(-g) / gate_norm, summed within each chunk. */
 typedef enum la_decay_mode { LA_DECAY_NONE = 0, LA_DECAY_HEAD = 1, LA_DECAY_GATE = 2 } la_decay_mode;
 
+/* Optional per-kernel timing.  Each call that is handed an la_trace sets count = 0, then for
+ * every kernel it enqueues (up to capacity) records start[i] just before and stop[i] just after
+ * the launch on the call's stream and stores a static kernel name in name[i].  The events are
+ * caller-created hipEvent_t handles; the caller reads them after synchronising. */
+#define LA_TRACE_MAX_KERNELS 8
+typedef struct la_trace {
+    void* start[LA_TRACE_MAX_KERNELS];
+    void* stop[LA_TRACE_MAX_KERNELS];
+    int32_t capacity;                       /* usable entries, 0..LA_TRACE_MAX_KERNELS */
+    int32_t count;                          /* out: kernels bracketed by the last call */
+    const char* name[LA_TRACE_MAX_KERNELS]; /* out */
+} la_trace;
+
 typedef struct la_shape {
     int64_t B;            /* batch size, >= 0 */
     int64_t H;            /* heads, >= 0 */
@@ -84,6 +97,7 @@ typedef struct la_shape {
                              the GPU); 0 = choose automatically, >= 1 forces that length.  Changes
                              the rounding order only, never the mathematical result. */
     void* stream;         /* hipStream_t the work is enqueued on; NULL = default stream */
+    la_trace* trace;      /* optional per-kernel event recording (NULL = off); see la_trace */
 } la_shape;
 /* A zero-initialised la_shape plus B, H, L, dk, dv, nseg = 1 and the dtypes is a valid
  * description for every call; the other fields only matter to the calls that name them. */

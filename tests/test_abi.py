@@ -49,7 +49,8 @@ def test_shape_struct_layout():
     assert B.Shape.dk.offset == 24 and B.Shape.gate_norm.offset == 48
     assert B.Shape.state_stride.offset == 56 and B.Shape.total_stride.offset == 64
     assert B.Shape.subseg_chunks.offset == 72
-    assert B.Shape.stream.offset == 80 and ctypes.sizeof(B.Shape) == 88
+    assert B.Shape.stream.offset == 80 and B.Shape.trace.offset == 88 and ctypes.sizeof(B.Shape) == 96
+    assert B.Trace.capacity.offset == 128 and B.Trace.name.offset == 136 and ctypes.sizeof(B.Trace) == 200
 
 
 # fake device addresses, far apart, never dereferenced
@@ -155,6 +156,16 @@ def test_cumdecay_validation(lib):
     assert lib.la_cumdecay(P(DEC), P(Q), P(K), ctypes.byref(shape(mode=0))) == DECAY
     assert lib.la_cumdecay(P(DEC), P(DEC + 4), None, ctypes.byref(shape(mode=2))) == ALIAS
     assert lib.la_cumdecay(P(DEC), None, None, ctypes.byref(shape(mode=1))) == OK    # nothing requested
+
+
+def test_trace_validation(lib):
+    t = B.Trace()
+    t.capacity = 9  # more than LA_TRACE_MAX_KERNELS
+    s = shape()
+    s.trace = ctypes.pointer(t)
+    assert fwd(lib, s) == SHAPE
+    t.capacity = 2  # events missing
+    assert fwd(lib, s) == NULL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
