@@ -25,8 +25,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_fwd_mfma_output_pass.json")
-KERNEL_SRC = os.path.join(ROOT, "chunked_scan_amd", "csrc", "chunk_fwd_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_output_pass_plain_B1_H16_L16k_d128.json")
+KERNEL_SRCS = [os.path.join(ROOT, "chunked_scan_amd", "csrc", f) for f in ("chunk_fwd_mfma.hip", "chunk_fwd_pipe.hip")]
 
 
 def log(*a):
@@ -34,8 +34,12 @@ def log(*a):
 
 
 def source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward-kernel sources: counter data taken on other sources is stale."""
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic(w, mode_bytes_gate: int):
@@ -156,12 +160,12 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n]["mean_us"] * kernels[n]["launches_per_step"])
     dom_us = kernels[dom]["mean_us"]
     traffic = None
-    if dom == "chunk_fwd_mfma_output_pass" and os.path.exists(TRAFFIC_FILE):
+    if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("source_sha256_16") == source_hash() and tr.get("workload") == w.name:
+        if tr.get("source_sha256_16") == source_hash() and tr.get("workload") == w.name and tr.get("kernel") == dom:
             traffic = tr["bytes_per_launch"]
-    alg_bytes = tokens * w.H * by_tok if dom == "chunk_fwd_mfma_output_pass" else None
+    alg_bytes = tokens * w.H * by_tok if dom.endswith("_output_pass") else None
     roof = None
     if alg_bytes is not None:
         achieved = alg_bytes / (dom_us * 1e-6) / 1e9

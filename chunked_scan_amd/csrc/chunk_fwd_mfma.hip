@@ -430,8 +430,10 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
 
 }  // namespace
 
-// Sub-segment length in chunks: enough units for two workgroups per compute unit, but at least
-// four chunks each so that the extra state traffic stays small next to the token traffic.
+// Sub-segment length in chunks: about one workgroup per compute unit (256 on MI355X) in one
+// round -- a second round costs a full extra sub-segment walk, and more sub-segments lengthen the
+// state scan -- but at least four chunks each so that the state traffic stays small next to the
+// token traffic.
 void mfma_split(const FwdArgs& a, int* G_out, int* cps_out) {
     const int64_t units = a.B * a.H * a.nseg;
     const int64_t Lseg = a.L / a.nseg;
@@ -440,7 +442,7 @@ void mfma_split(const FwdArgs& a, int* G_out, int* cps_out) {
     if (a.subseg_chunks > 0) {
         cps = a.subseg_chunks;
     } else {
-        const int64_t target = 512;
+        const int64_t target = 256;
         const int64_t g_want = (target + units - 1) / units;
         cps = (nch + g_want - 1) / g_want;
         if (cps < 4) cps = 4;
@@ -471,9 +473,9 @@ hipError_t launch_chunk_fwd_mfma(const FwdArgs& a) {
     }
     hipError_t e;
     switch (a.mode) {
-        case DECAY_HEAD: e = launch_mode<DECAY_HEAD>(a, G, cps, part_state, part_decay); break;
+        case DECAY_HEAD: e = launch_chunk_fwd_pipe(a, G, cps, part_state, part_decay); break;
         case DECAY_GATE: e = launch_mode<DECAY_GATE>(a, G, cps, part_state, part_decay); break;
-        default: e = launch_mode<DECAY_NONE>(a, G, cps, part_state, part_decay); break;
+        default: e = launch_chunk_fwd_pipe(a, G, cps, part_state, part_decay); break;
     }
     if (part_state) {
         hipError_t f = hipFreeAsync(part_state, a.stream);

@@ -1,0 +1,343 @@
+// chunk_fwd_pipe.hip -- bf16 MFMA chunked forward for dk = dv = 128, chunk = 64, decay modes
+// none and per-head, with the chunk tiles streamed HBM -> LDS by asynchronous DMA.
+//
+// Same mathematics and the same sub-segment split as chunk_fwd_mfma.hip (pass 1 local states,
+// internal state scan, pass 2 outputs from exact incoming states).  What differs is the data
+// path, designed around the MFMA register layouts so that almost nothing but MFMA operands
+// moves per chunk:
+//
+// * Streaming.  In these two modes the tiles are used exactly as stored (all decay factors are
+//   applied to products in registers), so q, k, v go straight from HBM into LDS with
+//   global_load_lds_dwordx4.  Three stage buffers (48 KiB each) form a ring: while chunk c is
+//   computed, chunks c+1 and c+2 are in flight.  The loop is unrolled by three so that each stage
+//   buffer is a distinct LDS object for the compiler's wait-count tracking.
+// * Swizzle.  Tiles are unpadded (one DMA instruction writes 1 KiB contiguous), so the 16-byte
+//   slots of a row are XOR-swizzled with a row-dependent 4-bit pattern chosen to make both the
+//   16-byte row reads (16 lanes, 16 consecutive rows) and the transposing 8-byte reads (16 lanes,
+//   4 consecutive rows x 2 adjacent slots) free of bank conflicts.
+// * Transposed outputs.  Each wave owns 32 value columns c and computes O^T = S^T Qbar^T +
+//   V^T P^T for them.  The score block P^T = K Q^T is computed by every wave with the key rows
+//   read in an order sigma (bits 2 and 3 of the row index swapped); with that order the score
+//   accumulator of each lane is exactly the B operand the V^T P^T product needs, so scores never
+//   go through LDS and a chunk needs a single barrier.
+// * State row order.  The state accumulator S (key rows x this wave's value columns) is built
+//   from transposing reads of K whose column starts follow the same sigma; then every state slab
+//   is directly the A operand of S^T Qbar^T and its Q operand is the same 16-byte row read the
+//   score product uses.
+// * Head decay: scores get exp(lambda (i-j)), the inter-chunk part of output column i gets the
+//   per-lane scalar exp(lambda (i+1)), and K^T V becomes K^T diag(w) V with the key-to-chunk-end
+//   weights w_j = exp(lambda (n-1-j)) on the V operand.  Every factor is <= 1.
+// * Outputs are written with 8-byte stores (4 consecutive value columns of one token per lane).
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int C = 64;
+constexpr int D = 128;
+constexpr int NT = 256;
+constexpr int TE = C * D;  // elements of one unpadded tile
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ bf16x4 lds_tr16(const __bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((__attribute__((address_space(3))) __bf16*)p));
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// row swizzle: bit0 <- row bit2, bits1-2 <- row bits0-1, bit3 <- row bit3
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8); }
+// element offset of logical (row, col) in a swizzled tile
+__device__ __forceinline__ int sw(int row, int col) { return row * D + ((((col >> 3) ^ swz(row))) << 3) + (col & 7); }
+// sigma: swap bits 2 and 3 (an involution on 0..31)
+__device__ __forceinline__ int sigma(int x) { return (x & 0x13) | ((x & 4) << 1) | ((x & 8) >> 1); }
+// accumulator element i of a 32x32 MFMA tile -> its row, for lane group kg
+__device__ __forceinline__ int acc_row(int i, int kg) { return (i >> 2) * 8 + kg * 4 + (i & 3); }
+
+// s_waitcnt with vmcnt = N, lgkmcnt = Lg, expcnt left alone
+template <int N, int Lg>
+__device__ __forceinline__ void waitcnt() {
+    static_assert(N >= 0 && N < 64 && Lg >= 0 && Lg < 16, "counter range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (Lg << 8));
+}
+
+struct Ring {
+    __bf16* q;
+    __bf16* k;
+    __bf16* v;
+};
+
+template <bool STATE_ONLY>
+struct Dma {
+    static constexpr int NDMA = (STATE_ONLY ? 2 : 3) * 4;  // DMA instructions per chunk per wave
+    // Every wave issues exactly NDMA instructions per chunk; rows past the chunk end re-read the
+    // chunk's last valid row and are zeroed before use.
+    __device__ static __forceinline__ void issue(const __bf16* q, const __bf16* k, const __bf16* v, Ring r,
+                                                 int64_t row0, int n, int w, int lane) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int R = (4 * w + j) * 4 + (lane >> 4);
+            const int ls = (lane & 15) ^ swz(R);
+            const int64_t off = (row0 + min(R, n - 1)) * D + ls * 8;
+            const int dst = (4 * w + j) * 512;
+            if (!STATE_ONLY)
+                __builtin_amdgcn_global_load_lds((const void*)(q + off), (lds_void*)(r.q + dst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(k + off), (lds_void*)(r.k + dst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(v + off), (lds_void*)(r.v + dst), 16, 0, 0);
+        }
+    }
+};
+
+// NST is the number of stage buffers: 3 (a ring, one workgroup per compute unit) is what is
+// launched; 1 (two workgroups per compute unit hiding each other's DMA latency) measured slower.
+template <int MODE, bool STATE_ONLY, int NST>
+__global__ __launch_bounds__(NT, NST == 1 ? 2 : 1) void pipe_fwd_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const float* __restrict__ decay, const float* __restrict__ s_in, __bf16* __restrict__ o,
+    float* __restrict__ s_out, int64_t s_out_stride, float* __restrict__ part_state,
+    float* __restrict__ part_decay, const float* __restrict__ init_state, int64_t H, int64_t L, int nseg, int G,
+    int cps) {
+    __shared__ __attribute__((aligned(16))) __bf16 st0[3 * TE];
+    __shared__ __attribute__((aligned(16))) __bf16 st1[NST == 3 ? 3 * TE : 8];
+    __shared__ __attribute__((aligned(16))) __bf16 st2[NST == 3 ? 3 * TE : 8];
+    using DM = Dma<STATE_ONLY>;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, n32 = lane & 31, kg = lane >> 5;
+    const int G16 = lane >> 4, i16 = lane & 15;
+
+    const int64_t u = blockIdx.x;
+    const int gper = STATE_ONLY ? (G - 1) : G;
+    const int g = (int)(u % gper);
+    const int64_t ub = u / gper;
+    const int seg = (int)(ub % nseg);
+    const int64_t bh = ub / nseg;
+    const int64_t h = bh % H;
+    const int64_t Lseg = L / nseg;
+    const int64_t t_begin = (int64_t)seg * Lseg + (int64_t)g * cps * C;
+    const int64_t t_end = min(t_begin + (int64_t)cps * C, (int64_t)(seg + 1) * Lseg);
+    const int64_t row_base = bh * L;
+    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
+    const int nch = (int)((t_end - t_begin + C - 1) / C);
+
+    const Ring R0{st0, st0 + TE, st0 + 2 * TE}, R1{st1, st1 + TE, st1 + 2 * TE}, R2{st2, st2 + TE, st2 + 2 * TE};
+
+    DM::issue(q, k, v, R0, row_base + t_begin, (int)min((int64_t)C, t_end - t_begin), w, lane);
+    if (NST == 3 && nch > 1)
+        DM::issue(q, k, v, R1, row_base + t_begin + C, (int)min((int64_t)C, t_end - t_begin - C), w, lane);
+
+    // state tile m: accumulator element i <-> key row 32m + sigma(acc_row(i)), value column 32w + n32
+    f32x16 S[4];
+    {
+        const float* src = nullptr;
+        if (g == 0) {
+            if (seg == 0 && s_in) src = s_in + bh * (int64_t)D * D;
+        } else if (!STATE_ONLY) {
+            src = init_state + (ub * (G - 1) + (g - 1)) * (int64_t)D * D;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                S[m][i] = src ? src[(32 * m + sigma(acc_row(i, kg))) * D + 32 * w + n32] : 0.f;
+    }
+
+    // per-lane LDS offsets that do not depend on the chunk
+    int voff[4][2];      // transposing reads of V: tokens 16ks + kg*8 + {0..3 | 4..7}, column 32w + n32
+    int ktoff[4][4][2];  // transposing reads of K for the state: key column 32m + sigma(n32)
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+        const int tb = 16 * ks + (G16 >> 1) * 8 + (i16 >> 2);
+        const int vcol = 32 * w + (G16 & 1) * 16 + (i16 & 3) * 4;
+        voff[ks][0] = sw(tb, vcol);
+        voff[ks][1] = sw(tb + 4, vcol);
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const int kcol = 32 * m + (G16 & 1) * 16 + 4 * (((i16 & 1) << 1) | ((i16 >> 1) & 1));
+            ktoff[ks][m][0] = sw(tb, kcol);
+            ktoff[ks][m][1] = sw(tb + 4, kcol);
+        }
+    }
+
+    auto body = [&](const Ring cur, const Ring nxt2, int c) {
+        const int64_t t0 = t_begin + (int64_t)c * C;
+        const int n = (int)min((int64_t)C, t_end - t0);
+        if (NST == 3 && c + 1 < nch) waitcnt<DM::NDMA, 15>();  // this wave's DMA of chunk c has landed
+        else waitcnt<0, 15>();
+        __builtin_amdgcn_s_barrier();  // every wave's part has landed; chunk c-1 is finished
+        if (n < C) {  // ragged last chunk: zero the rows past its end
+            for (int e = tid; e < (C - n) * 16; e += NT) {
+                const int off = (n + (e >> 4)) * D + (e & 15) * 8;
+                if (!STATE_ONLY) *(u32x4*)(cur.q + off) = u32x4{0, 0, 0, 0};
+                *(u32x4*)(cur.k + off) = u32x4{0, 0, 0, 0};
+                *(u32x4*)(cur.v + off) = u32x4{0, 0, 0, 0};
+            }
+            waitcnt<63, 0>();
+            __builtin_amdgcn_s_barrier();
+        }
+        if (NST == 3 && c + 2 < nch)
+            DM::issue(q, k, v, nxt2, row_base + t0 + 2 * C, (int)min((int64_t)C, t_end - t0 - 2 * C), w, lane);
+
+        // V operand: tokens 16ks + kg*8 + jj (plain order), this wave's column 32w + n32
+        bf16x8 vb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) vb[ks] = cat(lds_tr16(cur.v + voff[ks][0]), lds_tr16(cur.v + voff[ks][1]));
+
+        if (!STATE_ONLY) {
+            // the state as A operands of S^T Qbar^T: slab (m, hh) holds key dims 32m + 16hh + kg*8 + jj
+            bf16x8 sa[4][2];
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++) {
+                    bf16x8 x;
+#pragma unroll
+                    for (int jj = 0; jj < 8; jj++) x[jj] = (__bf16)S[m][8 * hh + jj];
+                    sa[m][hh] = x;
+                }
+#pragma unroll
+            for (int ib = 0; ib < 2; ib++) {
+                const int itok = ib * 32 + n32;
+                // Q operand (B of both products): token itok, key dims ks*16 + kg*8 .. +8
+                bf16x8 qb[8];
+#pragma unroll
+                for (int ks = 0; ks < 8; ks++) qb[ks] = *(const bf16x8*)(cur.q + sw(itok, ks * 16 + kg * 8));
+                // scores P^T = K Q^T on the causal blocks (jb <= ib); key rows in sigma order, so
+                // element 8hh + jj of lane (itok, kg) is key jb*32 + 16hh + kg*8 + jj
+                bf16x8 pt[4];  // 16-key slabs: B operand of V^T P^T
+#pragma unroll
+                for (int jb = 0; jb <= ib; jb++) {
+                    f32x16 sc = {};
+                    const int krow = jb * 32 + sigma(n32);
+#pragma unroll
+                    for (int ks = 0; ks < 8; ks++)
+                        sc = mfma(*(const bf16x8*)(cur.k + sw(krow, ks * 16 + kg * 8)), qb[ks], sc);
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++) {
+                        bf16x8 x;
+#pragma unroll
+                        for (int jj = 0; jj < 8; jj++) {
+                            const int jtok = jb * 32 + 16 * hh + kg * 8 + jj;
+                            float val = sc[8 * hh + jj];
+                            if (MODE == DECAY_HEAD) val *= decay_pow(lam, max(itok - jtok, 0));
+                            if (jb == ib && jtok > itok) val = 0.f;
+                            x[jj] = (__bf16)val;
+                        }
+                        pt[2 * jb + hh] = x;
+                    }
+                }
+                // O^T for this wave's 32 value columns and the 32 tokens of block ib
+                f32x16 acc = {};
+#pragma unroll
+                for (int m = 0; m < 4; m++)
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++) acc = mfma(sa[m][hh], qb[2 * m + hh], acc);
+                if (MODE == DECAY_HEAD) {
+                    const float f = decay_pow(lam, itok + 1);
+#pragma unroll
+                    for (int i = 0; i < 16; i++) acc[i] *= f;
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 2 * (ib + 1); s2++) acc = mfma(vb[s2], pt[s2], acc);
+                if (itok < n) {
+                    __bf16* orow = o + (row_base + t0 + itok) * D + 32 * w + kg * 4;
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; g4++) {
+                        const bf16x4 x = {(__bf16)acc[4 * g4], (__bf16)acc[4 * g4 + 1], (__bf16)acc[4 * g4 + 2],
+                                          (__bf16)acc[4 * g4 + 3]};
+                        *(bf16x4*)(orow + g4 * 8) = x;
+                    }
+                }
+            }
+        }
+
+        // state: S <- decay(chunk) S + K^T diag(w) V
+        if (MODE == DECAY_HEAD) {
+            const float fh = decay_pow(lam, n);
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) S[m][i] *= fh;
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+                for (int jj = 0; jj < 8; jj++) {
+                    const int t = 16 * ks + kg * 8 + jj;
+                    vb[ks][jj] = (__bf16)((float)vb[ks][jj] * decay_pow(lam, max(n - 1 - t, 0)));
+                }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {
+                const bf16x8 a = cat(lds_tr16(cur.k + ktoff[ks][m][0]), lds_tr16(cur.k + ktoff[ks][m][1]));
+                S[m] = mfma(a, vb[ks], S[m]);
+            }
+        if (NST == 1 && c + 1 < nch) {  // every wave is done with the stage: request the next chunk
+            waitcnt<63, 0>();
+            __builtin_amdgcn_s_barrier();
+            DM::issue(q, k, v, cur, row_base + t0 + C, (int)min((int64_t)C, t_end - t0 - C), w, lane);
+        }
+    };
+
+    if (NST == 3) {
+        for (int c = 0; c < nch; c += 3) {
+            body(R0, R2, c);
+            if (c + 1 < nch) body(R1, R0, c + 1);
+            if (c + 2 < nch) body(R2, R1, c + 2);
+        }
+    } else {
+        for (int c = 0; c < nch; c++) body(R0, R0, c);
+    }
+
+    float* dst = nullptr;
+    if (STATE_ONLY) dst = part_state + (ub * (G - 1) + g) * (int64_t)D * D;
+    else if (g == G - 1 && s_out) dst = s_out + bh * s_out_stride + (int64_t)seg * D * D;
+    if (dst) {
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) dst[(32 * m + sigma(acc_row(i, kg))) * D + 32 * w + n32] = S[m][i];
+    }
+    if (STATE_ONLY && tid < D)
+        part_decay[(ub * (G - 1) + g) * D + tid] = (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
+}
+
+template <int MODE, int NST>
+hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
+    const int64_t ub = a.B * a.H * a.nseg;
+    const __bf16* q = (const __bf16*)a.q;
+    const __bf16* k = (const __bf16*)a.k;
+    const __bf16* v = (const __bf16*)a.v;
+    __bf16* o = (__bf16*)a.o;
+    if (G > 1) {
+        LA_TRACED(a.tr, "chunk_fwd_pipe_state_pass",
+                  pipe_fwd_kernel<MODE, true, NST><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
+                      q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
+                      a.L, a.nseg, G, cps));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream, a.tr);
+        if (e != hipSuccess) return e;
+    }
+    LA_TRACED(a.tr, "chunk_fwd_pipe_output_pass",
+              pipe_fwd_kernel<MODE, false, NST><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
+                  q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, nullptr, part_state, a.H, a.L,
+                  a.nseg, G, cps));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
+    return a.mode == DECAY_HEAD ? launch_mode<DECAY_HEAD, 3>(a, G, cps, part_state, part_decay)
+                                : launch_mode<DECAY_NONE, 3>(a, G, cps, part_state, part_decay);
+}
+
+}  // namespace la
