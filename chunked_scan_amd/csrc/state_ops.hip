@@ -8,49 +8,39 @@ namespace la {
 namespace {
 
 // ---------------------------------------------------------------------------------------------
-// Segmented state scan.  Thread = 4 consecutive state elements (one float4) of one (b,h); it
-// walks the P segments in order:  y = diag(lam[p]) y + x[p];  out[p] = y.
-// Loads of a batch of SCAN_BATCH segments are issued before any of their stores so several
-// HBM reads are in flight per thread; out may alias x because every element is read before the
-// same thread overwrites it.
-constexpr int SCAN_BATCH = 8;
+// Segmented state scan.  Thread = one state element of one (b,h); it walks the P segments in
+// order:  y = lam[p] * y + x[p];  out[p] = y.  The state chain is serial but its loads are not:
+// a batch of SCAN_BATCH segments is loaded before any of them is combined, so each thread keeps
+// that many HBM reads in flight.  out may alias x: every element is read before the same thread
+// overwrites it.
+constexpr int SCAN_BATCH = 16;
 
 __global__ __launch_bounds__(256) void state_scan_kernel(const float* x, const float* __restrict__ lam,
-                                                         float* out, int P, int dk, int dv,
-                                                         int64_t vec_per_state, int vblocks) {
+                                                         float* out, int P, int dk, int dv, int64_t per_state,
+                                                         int vblocks) {
     const int64_t n = blockIdx.x / vblocks;  // state index: (b,h) or (b,h,segment)
-    const int64_t e4 = (int64_t)(blockIdx.x % vblocks) * blockDim.x + threadIdx.x;
-    if (e4 >= vec_per_state) return;
-    const int d = (int)((e4 * 4) / dv);
-    const int64_t SZ = (int64_t)dk * dv;
-    const float4* xs = reinterpret_cast<const float4*>(x + n * (int64_t)P * SZ) + e4;
-    float4* ys = reinterpret_cast<float4*>(out + n * (int64_t)P * SZ) + e4;
+    const int64_t e = (int64_t)(blockIdx.x % vblocks) * blockDim.x + threadIdx.x;
+    if (e >= per_state) return;
+    const int d = (int)(e / dv);
+    const float* xs = x + n * (int64_t)P * per_state + e;
+    float* ys = out + n * (int64_t)P * per_state + e;
     const float* ls = lam + n * (int64_t)P * dk + d;
-    const int64_t pstride = SZ / 4;
-    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+    float y = 0.f;
     for (int p0 = 0; p0 < P; p0 += SCAN_BATCH) {
-        float4 xb[SCAN_BATCH];
-        float lb[SCAN_BATCH];
+        float xb[SCAN_BATCH], lb[SCAN_BATCH];
         const int nb = min(SCAN_BATCH, P - p0);
 #pragma unroll
         for (int j = 0; j < SCAN_BATCH; j++) {
             if (j < nb) {
-                xb[j] = xs[(int64_t)(p0 + j) * pstride];
+                xb[j] = xs[(int64_t)(p0 + j) * per_state];
                 lb[j] = ls[(int64_t)(p0 + j) * dk];
             }
         }
 #pragma unroll
         for (int j = 0; j < SCAN_BATCH; j++) {
             if (j < nb) {
-                if (p0 + j == 0) {
-                    y = xb[j];  // out[-1] = 0: the decay of segment 0 is never applied
-                } else {
-                    y.x = lb[j] * y.x + xb[j].x;
-                    y.y = lb[j] * y.y + xb[j].y;
-                    y.z = lb[j] * y.z + xb[j].z;
-                    y.w = lb[j] * y.w + xb[j].w;
-                }
-                ys[(int64_t)(p0 + j) * pstride] = y;
+                y = (p0 + j == 0) ? xb[j] : lb[j] * y + xb[j];  // out[-1] = 0: segment 0's decay is never applied
+                ys[(int64_t)(p0 + j) * per_state] = y;
             }
         }
     }
@@ -224,10 +214,11 @@ __global__ __launch_bounds__(256) void empty_states_kernel(const float* __restri
 hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64_t nstates, int P, int dk, int dv,
                              hipStream_t stream, Tracer* tr) {
     if (nstates == 0 || P == 0) return hipSuccess;
-    const int64_t vec = (int64_t)dk * dv / 4;
-    const int vblocks = (int)((vec + 255) / 256);
+    const int64_t per_state = (int64_t)dk * dv;
+    const int vblocks = (int)((per_state + 255) / 256);
     LA_TRACED(tr, "state_scan",
-              state_scan_kernel<<<(unsigned)(nstates * vblocks), 256, 0, stream>>>(x, lam, out, P, dk, dv, vec, vblocks));
+              state_scan_kernel<<<(unsigned)(nstates * vblocks), 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state,
+                                                                                 vblocks));
     return hipGetLastError();
 }
 
