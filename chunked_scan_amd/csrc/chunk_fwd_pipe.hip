@@ -60,13 +60,6 @@ __device__ __forceinline__ int sigma(int x) { return (x & 0x13) | ((x & 4) << 1)
 // accumulator element i of a 32x32 MFMA tile -> its row, for lane group kg
 __device__ __forceinline__ int acc_row(int i, int kg) { return (i >> 2) * 8 + kg * 4 + (i & 3); }
 
-// s_waitcnt with vmcnt = N, lgkmcnt = Lg, expcnt left alone
-template <int N, int Lg>
-__device__ __forceinline__ void waitcnt() {
-    static_assert(N >= 0 && N < 64 && Lg >= 0 && Lg < 16, "counter range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (Lg << 8));
-}
-
 struct Ring {
     __bf16* q;
     __bf16* k;

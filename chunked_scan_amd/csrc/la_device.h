@@ -44,4 +44,21 @@ __device__ __forceinline__ float gate_logdecay(float g, float inv_norm) {
 // lam = -inf (a = 0).
 __device__ __forceinline__ float decay_pow(float lam, int m) { return m == 0 ? 1.f : expf(lam * (float)m); }
 
+// s_waitcnt with vmcnt = N (outstanding vector memory operations of this wave) and lgkmcnt = Lg
+// (outstanding LDS operations), expcnt left alone.  Used with a bare s_barrier where a full
+// __syncthreads would also drain this wave's global loads that are meant to stay in flight.
+template <int N, int Lg>
+__device__ __forceinline__ void waitcnt() {
+    static_assert(N >= 0 && N < 64 && Lg >= 0 && Lg < 16, "counter range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (Lg << 8));
+}
+
+// Workgroup barrier that orders LDS accesses only: LDS writes before it are visible to every wave
+// after it, while this wave's global loads stay in flight (a full __syncthreads drains them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace la
