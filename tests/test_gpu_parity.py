@@ -188,6 +188,48 @@ def test_state_correct_matches_oracle(mode, dtype, dk):
 
 
 @pytest.mark.parametrize("mode", ["none", "head", "gate"])
+def test_state_correct_many_tiles_per_workgroup(mode):
+    """bf16 d=128 correction with about five 64-token tiles per workgroup: ragged segments (2565
+    tokens), incoming states that change inside a workgroup's range, and (head mode) decays that
+    underflow to exactly zero part-way through a segment, whose tokens must stay bit-identical."""
+    H, P, Ls, d = 4, 9, 2565, 128
+    L = P * Ls
+    note(f"la_state_correct many tiles mode={mode} H={H} P={P} Ls={Ls}")
+    g = torch.Generator().manual_seed(63)
+    q = torch.randn((1, H, L, d), generator=g).bfloat16()
+    o0 = (torch.randn((1, H, L, d), generator=g) * 0.1).bfloat16()
+    s_recv = torch.randn((1, H, P - 1, d, d), generator=g) * 0.05
+    if mode == "head":
+        decay = torch.tensor([0.0, -1e-3, -0.05, -0.5])  # the last two reach exactly zero in fp32
+    elif mode == "gate":
+        decay = torch.randn((1, H, L, d), generator=g) + 3.0
+    else:
+        decay = None
+    cum_ref, _ = oracle.cumdecay(1, H, L, d, ORC_MODE[mode], None if decay is None else decay.numpy(), nseg=P)
+    ref = oracle.state_correct(host32(q), cum_ref, s_recv.double().numpy(), host32(o0), nseg=P, seg_begin=1)
+    cum = None
+    if mode == "gate":
+        cum, _ = lb.la_cumdecay(decay.cuda(), 1, H, L, d, mode="gate", nseg=P, want_total=False)
+    elif mode == "head":
+        cum = decay.cuda()
+    o = o0.cuda()
+    lb.la_state_correct(q.cuda(), cum, s_recv.cuda(), o, mode=mode, nseg=P, seg_begin=1)
+    torch.cuda.synchronize()
+    o = o.cpu()
+    assert rel_err(o, ref) <= TOL["bf16"]
+    assert torch.equal(o[:, :, :Ls], o0[:, :, :Ls])
+    if mode == "head":
+        # tokens whose factor exp(lambda * tau) is exactly zero in fp32 keep their bits
+        tau = torch.arange(1, Ls + 1, dtype=torch.float32)
+        for h in (2, 3):
+            dead = torch.exp(decay[h] * tau) == 0
+            assert dead.any()
+            for p in range(1, P):
+                seg = o[0, h, p * Ls:(p + 1) * Ls]
+                assert torch.equal(seg[dead], o0[0, h, p * Ls:(p + 1) * Ls][dead]), (h, p)
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
 def test_cumdecay_matches_oracle(mode):
     decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
     P = 4
