@@ -6,20 +6,28 @@
 // path, designed around the MFMA register layouts so that almost nothing but MFMA operands
 // moves per chunk:
 //
-// * Streaming.  In these two modes the tiles are used exactly as stored (all decay factors are
-//   applied to products in registers), so q, k, v go straight from HBM into LDS with
-//   global_load_lds_dwordx4.  Three stage buffers (48 KiB each) form a ring: while chunk c is
-//   computed, chunks c+1 and c+2 are in flight.  The loop is unrolled by three so that each stage
-//   buffer is a distinct LDS object for the compiler's wait-count tracking.
+// * Loader and compute waves.  In these two modes the tiles are used exactly as stored (all decay
+//   factors are applied to products in registers), so q, k, v go straight from HBM into LDS with
+//   global_load_lds_dwordx4, issued by four loader waves that do nothing else: their waits count
+//   exactly their own DMA.  The stage buffers form a ring over all 160 KiB of LDS: three stages of
+//   q, k, v (two chunks in flight while one is computed) in the output pass, five of k, v (four in
+//   flight) in the state pass, whose compute per chunk is light.  The four compute waves issue no global loads
+//   after their start, so their output stores never make them wait; one barrier per chunk
+//   hands a landed stage to them and frees the stage they finished.
+// * Ragged chunks.  DMA rows past a chunk's end re-read its last row, which only reaches output
+//   rows that are never stored; the state update zeroes those tokens' V operand in registers.
 // * Swizzle.  Tiles are unpadded (one DMA instruction writes 1 KiB contiguous), so the 16-byte
 //   slots of a row are XOR-swizzled with a row-dependent 4-bit pattern chosen to make both the
 //   16-byte row reads (16 lanes, 16 consecutive rows) and the transposing 8-byte reads (16 lanes,
 //   4 consecutive rows x 2 adjacent slots) free of bank conflicts.
-// * Transposed outputs.  Each wave owns 32 value columns c and computes O^T = S^T Qbar^T +
+// * Transposed outputs.  Each compute wave owns 32 value columns and computes O^T = S^T Qbar^T +
 //   V^T P^T for them.  The score block P^T = K Q^T is computed by every wave with the key rows
 //   read in an order sigma (bits 2 and 3 of the row index swapped); with that order the score
 //   accumulator of each lane is exactly the B operand the V^T P^T product needs, so scores never
-//   go through LDS and a chunk needs a single barrier.
+//   go through LDS.
+// * Value column order.  Index r of the wave's 32 value columns is column 32 w + sigma(r) (the
+//   V operand's transposing reads choose their 4-column groups accordingly); then each lane's
+//   output accumulators are 2 runs of 8 consecutive columns, written with two 16-byte stores.
 // * State row order.  The state accumulator S (key rows x this wave's value columns) is built
 //   from transposing reads of K whose column starts follow the same sigma; then every state slab
 //   is directly the A operand of S^T Qbar^T and its Q operand is the same 16-byte row read the
@@ -27,7 +35,6 @@
 // * Head decay: scores get exp(lambda (i-j)), the inter-chunk part of output column i gets the
 //   per-lane scalar exp(lambda (i+1)), and K^T V becomes K^T diag(w) V with the key-to-chunk-end
 //   weights w_j = exp(lambda (n-1-j)) on the V operand.  Every factor is <= 1.
-// * Outputs are written with 8-byte stores (4 consecutive value columns of one token per lane).
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -36,8 +43,9 @@ namespace {
 
 constexpr int C = 64;
 constexpr int D = 128;
-constexpr int NT = 256;
+constexpr int NT = 512;    // four compute waves, then four loader waves
 constexpr int TE = C * D;  // elements of one unpadded tile
+constexpr int LDS_TILES = 10;  // 160 KiB: the stage ring holds 3 stages of q, k, v or 5 of k, v
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -68,17 +76,17 @@ struct Ring {
 
 template <bool STATE_ONLY>
 struct Dma {
-    static constexpr int NDMA = (STATE_ONLY ? 2 : 3) * 4;  // DMA instructions per chunk per wave
-    // Every wave issues exactly NDMA instructions per chunk; rows past the chunk end re-read the
-    // chunk's last valid row and are zeroed before use.
+    static constexpr int NDMA = (STATE_ONLY ? 2 : 3) * 4;  // DMA instructions per chunk per loader wave
+    // Loader wave lw fills rows 16 lw .. 16 lw + 15 of each tile; rows past the chunk end re-read
+    // the chunk's last valid row.
     __device__ static __forceinline__ void issue(const __bf16* q, const __bf16* k, const __bf16* v, Ring r,
-                                                 int64_t row0, int n, int w, int lane) {
+                                                 int64_t row0, int n, int lw, int lane) {
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const int R = (4 * w + j) * 4 + (lane >> 4);
+            const int R = (4 * lw + j) * 4 + (lane >> 4);
             const int ls = (lane & 15) ^ swz(R);
             const int64_t off = (row0 + min(R, n - 1)) * D + ls * 8;
-            const int dst = (4 * w + j) * 512;
+            const int dst = (4 * lw + j) * 512;
             if (!STATE_ONLY)
                 __builtin_amdgcn_global_load_lds((const void*)(q + off), (lds_void*)(r.q + dst), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((const void*)(k + off), (lds_void*)(r.k + dst), 16, 0, 0);
@@ -87,24 +95,19 @@ struct Dma {
     }
 };
 
-// NST is the number of stage buffers: 3 (a ring, one workgroup per compute unit) is what is
-// launched; 1 (two workgroups per compute unit hiding each other's DMA latency) measured slower.
-template <int MODE, bool STATE_ONLY, int NST>
-__global__ __launch_bounds__(NT, NST == 1 ? 2 : 1) void pipe_fwd_kernel(
+template <int MODE, bool STATE_ONLY>
+__global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ decay, const float* __restrict__ s_in, __bf16* __restrict__ o,
     float* __restrict__ s_out, int64_t s_out_stride, float* __restrict__ part_state,
     float* __restrict__ part_decay, const float* __restrict__ init_state, int64_t H, int64_t L, int nseg, int G,
     int cps) {
-    __shared__ __attribute__((aligned(16))) __bf16 st0[3 * TE];
-    __shared__ __attribute__((aligned(16))) __bf16 st1[NST == 3 ? 3 * TE : 8];
-    __shared__ __attribute__((aligned(16))) __bf16 st2[NST == 3 ? 3 * TE : 8];
+    constexpr int SLOT = STATE_ONLY ? 2 : 3;  // tiles per stage
+    constexpr int NST = LDS_TILES / SLOT;     // ring stages: NST - 1 chunks in flight
+    __shared__ __attribute__((aligned(16))) __bf16 ring[NST * SLOT * TE];
     using DM = Dma<STATE_ONLY>;
 
-    const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, n32 = lane & 31, kg = lane >> 5;
-    const int G16 = lane >> 4, i16 = lane & 15;
-
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t u = blockIdx.x;
     const int gper = STATE_ONLY ? (G - 1) : G;
     const int g = (int)(u % gper);
@@ -116,16 +119,38 @@ __global__ __launch_bounds__(NT, NST == 1 ? 2 : 1) void pipe_fwd_kernel(
     const int64_t t_begin = (int64_t)seg * Lseg + (int64_t)g * cps * C;
     const int64_t t_end = min(t_begin + (int64_t)cps * C, (int64_t)(seg + 1) * Lseg);
     const int64_t row_base = bh * L;
-    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
     const int nch = (int)((t_end - t_begin + C - 1) / C);
+    auto stage = [&](int c) {
+        __bf16* b = ring + (c % NST) * SLOT * TE;
+        return Ring{b, b + (SLOT - 2) * TE, b + (SLOT - 1) * TE};  // q is unused in the state pass
+    };
+    auto chunk_len = [&](int c) { return (int)min((int64_t)C, t_end - t_begin - (int64_t)c * C); };
 
-    const Ring R0{st0, st0 + TE, st0 + 2 * TE}, R1{st1, st1 + TE, st1 + 2 * TE}, R2{st2, st2 + TE, st2 + 2 * TE};
+    if (wave >= 4) {
+        // ---- loader wave: chunk c + 2 is requested as soon as every wave is done with chunk c - 1
+        const int lw = wave - 4;
+        int issued = 0;
+        for (; issued < NST - 1 && issued < nch; issued++)
+            DM::issue(q, k, v, stage(issued), row_base + t_begin + (int64_t)issued * C, chunk_len(issued), lw, lane);
+        for (int c = 0; c < nch; c++) {
+            wait_batches<DM::NDMA>(issued - c - 1);  // this wave's part of chunk c has landed
+            __builtin_amdgcn_s_barrier();
+            if (issued < nch) {
+                DM::issue(q, k, v, stage(issued), row_base + t_begin + (int64_t)issued * C, chunk_len(issued), lw,
+                          lane);
+                issued++;
+            }
+        }
+        return;
+    }
 
-    DM::issue(q, k, v, R0, row_base + t_begin, (int)min((int64_t)C, t_end - t_begin), w, lane);
-    if (NST == 3 && nch > 1)
-        DM::issue(q, k, v, R1, row_base + t_begin + C, (int)min((int64_t)C, t_end - t_begin - C), w, lane);
+    // ---- compute wave w: value columns 32 w + sigma(0..31)
+    const int w = wave, n32 = lane & 31, kg = lane >> 5;
+    const int G16 = lane >> 4, i16 = lane & 15;
+    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
+    const int vcol_lane = 32 * w + sigma(n32);
 
-    // state tile m: accumulator element i <-> key row 32m + sigma(acc_row(i)), value column 32w + n32
+    // state tile m: accumulator element i <-> key row 32m + sigma(acc_row(i)), value column vcol_lane
     f32x16 S[4];
     {
         const float* src = nullptr;
@@ -137,50 +162,40 @@ __global__ __launch_bounds__(NT, NST == 1 ? 2 : 1) void pipe_fwd_kernel(
 #pragma unroll
         for (int m = 0; m < 4; m++)
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-                S[m][i] = src ? src[(32 * m + sigma(acc_row(i, kg))) * D + 32 * w + n32] : 0.f;
+            for (int i = 0; i < 16; i++) S[m][i] = src ? src[(32 * m + sigma(acc_row(i, kg))) * D + vcol_lane] : 0.f;
     }
 
-    // per-lane LDS offsets that do not depend on the chunk
-    int voff[4][2];      // transposing reads of V: tokens 16ks + kg*8 + {0..3 | 4..7}, column 32w + n32
-    int ktoff[4][4][2];  // transposing reads of K for the state: key column 32m + sigma(n32)
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-        const int tb = 16 * ks + (G16 >> 1) * 8 + (i16 >> 2);
-        const int vcol = 32 * w + (G16 & 1) * 16 + (i16 & 3) * 4;
-        voff[ks][0] = sw(tb, vcol);
-        voff[ks][1] = sw(tb + 4, vcol);
+    // per-lane LDS offsets of the transposing reads for the first 16-token slab (tokens kg*8 +
+    // {0..3 | 4..7}); slab ks adds 16 ks rows, which leaves the swizzle (row bits 0-3) unchanged.
+    // The 4-column group a = i16 % 4 that a read fetches is placed at 4 (bits of a swapped), the
+    // sigma order.
+    const int quad = 4 * (((i16 & 1) << 1) | ((i16 >> 1) & 1));
+    const int tb = (G16 >> 1) * 8 + (i16 >> 2);
+    int voff[2];      // V: value column vcol_lane
+    int ktoff[4][2];  // K for the state: key column 32m + sigma(n32)
+    {
+        const int vcol = 32 * w + (G16 & 1) * 16 + quad;
+        voff[0] = sw(tb, vcol);
+        voff[1] = sw(tb + 4, vcol);
 #pragma unroll
         for (int m = 0; m < 4; m++) {
-            const int kcol = 32 * m + (G16 & 1) * 16 + 4 * (((i16 & 1) << 1) | ((i16 >> 1) & 1));
-            ktoff[ks][m][0] = sw(tb, kcol);
-            ktoff[ks][m][1] = sw(tb + 4, kcol);
+            const int kcol = 32 * m + (G16 & 1) * 16 + quad;
+            ktoff[m][0] = sw(tb, kcol);
+            ktoff[m][1] = sw(tb + 4, kcol);
         }
     }
 
-    auto body = [&](const Ring cur, const Ring nxt2, int c) {
+    for (int c = 0; c < nch; c++) {
+        const Ring cur = stage(c);
         const int64_t t0 = t_begin + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, t_end - t0);
-        if (NST == 3 && c + 1 < nch) waitcnt<DM::NDMA, 15>();  // this wave's DMA of chunk c has landed
-        else waitcnt<0, 15>();
-        __builtin_amdgcn_s_barrier();  // every wave's part has landed; chunk c-1 is finished
-        if (n < C) {  // ragged last chunk: zero the rows past its end
-            for (int e = tid; e < (C - n) * 16; e += NT) {
-                const int off = (n + (e >> 4)) * D + (e & 15) * 8;
-                if (!STATE_ONLY) *(u32x4*)(cur.q + off) = u32x4{0, 0, 0, 0};
-                *(u32x4*)(cur.k + off) = u32x4{0, 0, 0, 0};
-                *(u32x4*)(cur.v + off) = u32x4{0, 0, 0, 0};
-            }
-            waitcnt<63, 0>();
-            __builtin_amdgcn_s_barrier();
-        }
-        if (NST == 3 && c + 2 < nch)
-            DM::issue(q, k, v, nxt2, row_base + t0 + 2 * C, (int)min((int64_t)C, t_end - t0 - 2 * C), w, lane);
+        const int n = chunk_len(c);
+        lds_barrier();  // chunk c has landed; every wave is done with chunk c - 1
 
-        // V operand: tokens 16ks + kg*8 + jj (plain order), this wave's column 32w + n32
+        // V operand: tokens 16ks + kg*8 + jj (plain order), value column vcol_lane
         bf16x8 vb[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++) vb[ks] = cat(lds_tr16(cur.v + voff[ks][0]), lds_tr16(cur.v + voff[ks][1]));
+        for (int ks = 0; ks < 4; ks++)
+            vb[ks] = cat(lds_tr16(cur.v + 16 * ks * D + voff[0]), lds_tr16(cur.v + 16 * ks * D + voff[1]));
 
         if (!STATE_ONLY) {
             // the state as A operands of S^T Qbar^T: slab (m, hh) holds key dims 32m + 16hh + kg*8 + jj
@@ -238,19 +253,22 @@ __global__ __launch_bounds__(NT, NST == 1 ? 2 : 1) void pipe_fwd_kernel(
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < 2 * (ib + 1); s2++) acc = mfma(vb[s2], pt[s2], acc);
+                // accumulators 0..7 are value columns 32w + 8kg + 0..7, 8..15 are 32w + 16 + 8kg + 0..7
                 if (itok < n) {
-                    __bf16* orow = o + (row_base + t0 + itok) * D + 32 * w + kg * 4;
+                    __bf16* orow = o + (row_base + t0 + itok) * D + 32 * w + 8 * kg;
+                    bf16x8 x0, x1;
 #pragma unroll
-                    for (int g4 = 0; g4 < 4; g4++) {
-                        const bf16x4 x = {(__bf16)acc[4 * g4], (__bf16)acc[4 * g4 + 1], (__bf16)acc[4 * g4 + 2],
-                                          (__bf16)acc[4 * g4 + 3]};
-                        *(bf16x4*)(orow + g4 * 8) = x;
+                    for (int e = 0; e < 8; e++) {
+                        x0[e] = (__bf16)acc[e];
+                        x1[e] = (__bf16)acc[8 + e];
                     }
+                    *(bf16x8*)orow = x0;
+                    *(bf16x8*)(orow + 16) = x1;
                 }
             }
         }
 
-        // state: S <- decay(chunk) S + K^T diag(w) V
+        // state: S <- decay(chunk) S + K^T diag(w) V over the chunk's n tokens
         if (MODE == DECAY_HEAD) {
             const float fh = decay_pow(lam, n);
 #pragma unroll
@@ -262,31 +280,22 @@ __global__ __launch_bounds__(NT, NST == 1 ? 2 : 1) void pipe_fwd_kernel(
 #pragma unroll
                 for (int jj = 0; jj < 8; jj++) {
                     const int t = 16 * ks + kg * 8 + jj;
-                    vb[ks][jj] = (__bf16)((float)vb[ks][jj] * decay_pow(lam, max(n - 1 - t, 0)));
+                    vb[ks][jj] = (t < n) ? (__bf16)((float)vb[ks][jj] * decay_pow(lam, n - 1 - t)) : (__bf16)0.f;
                 }
+        } else if (n < C) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+                for (int jj = 0; jj < 8; jj++)
+                    if (16 * ks + kg * 8 + jj >= n) vb[ks][jj] = (__bf16)0.f;
         }
 #pragma unroll
         for (int m = 0; m < 4; m++)
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) {
-                const bf16x8 a = cat(lds_tr16(cur.k + ktoff[ks][m][0]), lds_tr16(cur.k + ktoff[ks][m][1]));
+                const bf16x8 a = cat(lds_tr16(cur.k + 16 * ks * D + ktoff[m][0]), lds_tr16(cur.k + 16 * ks * D + ktoff[m][1]));
                 S[m] = mfma(a, vb[ks], S[m]);
             }
-        if (NST == 1 && c + 1 < nch) {  // every wave is done with the stage: request the next chunk
-            waitcnt<63, 0>();
-            __builtin_amdgcn_s_barrier();
-            DM::issue(q, k, v, cur, row_base + t0 + C, (int)min((int64_t)C, t_end - t0 - C), w, lane);
-        }
-    };
-
-    if (NST == 3) {
-        for (int c = 0; c < nch; c += 3) {
-            body(R0, R2, c);
-            if (c + 1 < nch) body(R1, R0, c + 1);
-            if (c + 2 < nch) body(R2, R1, c + 2);
-        }
-    } else {
-        for (int c = 0; c < nch; c++) body(R0, R0, c);
     }
 
     float* dst = nullptr;
@@ -296,13 +305,14 @@ __global__ __launch_bounds__(NT, NST == 1 ? 2 : 1) void pipe_fwd_kernel(
 #pragma unroll
         for (int m = 0; m < 4; m++)
 #pragma unroll
-            for (int i = 0; i < 16; i++) dst[(32 * m + sigma(acc_row(i, kg))) * D + 32 * w + n32] = S[m][i];
+            for (int i = 0; i < 16; i++) dst[(32 * m + sigma(acc_row(i, kg))) * D + vcol_lane] = S[m][i];
     }
-    if (STATE_ONLY && tid < D)
-        part_decay[(ub * (G - 1) + g) * D + tid] = (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
+    if (STATE_ONLY && threadIdx.x < D)
+        part_decay[(ub * (G - 1) + g) * D + threadIdx.x] =
+            (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
 }
 
-template <int MODE, int NST>
+template <int MODE>
 hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
     const int64_t ub = a.B * a.H * a.nseg;
     const __bf16* q = (const __bf16*)a.q;
@@ -311,7 +321,7 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
     __bf16* o = (__bf16*)a.o;
     if (G > 1) {
         LA_TRACED(a.tr, "chunk_fwd_pipe_state_pass",
-                  pipe_fwd_kernel<MODE, true, NST><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
+                  pipe_fwd_kernel<MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
                       q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
                       a.L, a.nseg, G, cps));
         hipError_t e = hipGetLastError();
@@ -320,7 +330,7 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
         if (e != hipSuccess) return e;
     }
     LA_TRACED(a.tr, "chunk_fwd_pipe_output_pass",
-              pipe_fwd_kernel<MODE, false, NST><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
+              pipe_fwd_kernel<MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
                   q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, nullptr, part_state, a.H, a.L,
                   a.nseg, G, cps));
     return hipGetLastError();
@@ -329,8 +339,8 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
 }  // namespace
 
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
-    return a.mode == DECAY_HEAD ? launch_mode<DECAY_HEAD, 3>(a, G, cps, part_state, part_decay)
-                                : launch_mode<DECAY_NONE, 3>(a, G, cps, part_state, part_decay);
+    return a.mode == DECAY_HEAD ? launch_mode<DECAY_HEAD>(a, G, cps, part_state, part_decay)
+                                : launch_mode<DECAY_NONE>(a, G, cps, part_state, part_decay);
 }
 
 }  // namespace la

@@ -53,6 +53,17 @@ __device__ __forceinline__ void waitcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (Lg << 8));
 }
 
+// Wait until at most `younger` batches of NPER vector memory operations issued after the batch
+// of interest are outstanding (younger < 4).
+template <int NPER>
+__device__ __forceinline__ void wait_batches(int younger) {
+    static_assert(3 * NPER < 64, "counter range");
+    if (younger >= 3) waitcnt<3 * NPER, 15>();
+    else if (younger == 2) waitcnt<2 * NPER, 15>();
+    else if (younger == 1) waitcnt<NPER, 15>();
+    else waitcnt<0, 15>();
+}
+
 // Workgroup barrier that orders LDS accesses only: LDS writes before it are visible to every wave
 // after it, while this wave's global loads stay in flight (a full __syncthreads drains them).
 __device__ __forceinline__ void lds_barrier() {

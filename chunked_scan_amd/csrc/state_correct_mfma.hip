@@ -37,7 +37,7 @@ constexpr int QPITCH = 136;   // bf16 pitch of the register-staged query tile (c
 constexpr int CPITCH = 132;   // fp32 pitch of the staged correction (conflict-free 16-byte column writes)
 constexpr int NT = 256;       // gate kernel: four compute waves
 constexpr int NT_WS = 512;    // loader / compute kernel: four of each
-constexpr int NST = 4;        // ring stages of the loader / compute kernel
+constexpr int NST = 5;        // ring stages of the loader / compute kernel (160 KiB of LDS)
 constexpr int PIECES = TT * D / 8 / NT;  // 16-byte pieces of a tile per compute thread
 constexpr int NDMA = 2 * TT * D / 8 / 64 / 4;  // DMA instructions per tile per loader wave (q and o)
 
@@ -169,11 +169,8 @@ __global__ __launch_bounds__(NT_WS, 1) void state_correct_ws_kernel(
         }
         for (int k = 0; k < issued; k++) {
             // tile k has landed once at most (issued - k - 1) younger tiles are outstanding
-            const int younger = issued - k - 1;
-            static_assert(NST == 4, "wait counts below assume four stages");
-            if (younger >= 2) waitcnt<2 * NDMA, 15>();
-            else if (younger == 1) waitcnt<NDMA, 15>();
-            else waitcnt<0, 15>();
+            static_assert(NST <= 5, "at most three younger tiles in flight");
+            wait_batches<NDMA>(issued - k - 1);
             __builtin_amdgcn_s_barrier();  // B1: tile k is in LDS; stage (k - 1) % NST is free
             if (!walk.done()) {
                 issue(walk.tile(), issued % NST);
