@@ -3,7 +3,7 @@
 A step is one pass of the whole per-device path over one batch of synthetic input at the
 pages' per-device shape (B=1, H=16, L=16384, dk=dv=128, bf16, chunk 64, no decay, S_recv = 0):
   la_chunk_fwd     local chunked forward from a zero state  -> O_local, S_loc
-  la_cumdecay      the segment's total decay Lambda
+  la_cumdecay      the segment's total decay Lambda (decay modes only; without decay Lambda = 1)
   la_state_scan    All-Scan update S_out = Lambda S_recv + S_loc (two-entry scan)
   la_state_correct O += (Q * cumulative decay) S_recv
 Prints one JSON line.  Per-kernel durations come from HIP events that the library records

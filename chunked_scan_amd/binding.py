@@ -202,13 +202,14 @@ def la_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optio
     return o, s_out
 
 
-def la_state_scan(seg_states: torch.Tensor, seg_decay: torch.Tensor, out_states: Optional[torch.Tensor] = None,
-                  *, stream=None, timer=None) -> torch.Tensor:
-    """Inclusive scan over axis 2: seg_states [B,H,P,dk,dv] f32, seg_decay [B,H,P,dk] f32 (dense).
-    out_states may be seg_states itself (in place)."""
+def la_state_scan(seg_states: torch.Tensor, seg_decay: Optional[torch.Tensor],
+                  out_states: Optional[torch.Tensor] = None, *, stream=None, timer=None) -> torch.Tensor:
+    """Inclusive scan over axis 2: seg_states [B,H,P,dk,dv] f32, seg_decay [B,H,P,dk] f32 (dense) or
+    None (no decay).  out_states may be seg_states itself (in place)."""
     B, H, P, dk, dv = seg_states.shape
     _dev(seg_states, "seg_states", torch.float32)
-    _dev(seg_decay, "seg_decay", torch.float32, (B, H, P, dk))
+    if seg_decay is not None:
+        _dev(seg_decay, "seg_decay", torch.float32, (B, H, P, dk))
     if out_states is None:
         out_states = torch.empty_like(seg_states)
     _dev(out_states, "out_states", torch.float32, (B, H, P, dk, dv))

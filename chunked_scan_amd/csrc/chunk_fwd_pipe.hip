@@ -8,12 +8,13 @@
 //
 // * Loader and compute waves.  In these two modes the tiles are used exactly as stored (all decay
 //   factors are applied to products in registers), so q, k, v go straight from HBM into LDS with
-//   global_load_lds_dwordx4, issued by four loader waves that do nothing else: their waits count
-//   exactly their own DMA.  The stage buffers form a ring over all 160 KiB of LDS: three stages of
-//   q, k, v (two chunks in flight while one is computed) in the output pass, five of k, v (four in
-//   flight) in the state pass, whose compute per chunk is light.  The four compute waves issue no global loads
-//   after their start, so their output stores never make them wait; one barrier per chunk
-//   hands a landed stage to them and frees the stage they finished.
+//   global_load_lds_dwordx4, issued by four loader waves.  The stage buffers form a ring: three
+//   stages of q, k, v (two chunks in flight while one is computed) in the output pass, five of
+//   k, v (four in flight) in the state pass, whose compute per chunk is light.  The compute waves
+//   touch no global memory after their start: they write each chunk's outputs into an LDS tile,
+//   which the loader waves store row-major (1 KiB contiguous per instruction).  Per chunk one
+//   barrier hands a landed stage to the compute waves and frees the stage they finished, and (in
+//   the output pass) a second one hands the output tile to the loader waves.
 // * Ragged chunks.  DMA rows past a chunk's end re-read its last row, which only reaches output
 //   rows that are never stored; the state update zeroes those tokens' V operand in registers.
 // * Swizzle.  Tiles are unpadded (one DMA instruction writes 1 KiB contiguous), so the 16-byte
@@ -27,7 +28,8 @@
 //   go through LDS.
 // * Value column order.  Index r of the wave's 32 value columns is column 32 w + sigma(r) (the
 //   V operand's transposing reads choose their 4-column groups accordingly); then each lane's
-//   output accumulators are 2 runs of 8 consecutive columns, written with two 16-byte stores.
+//   output accumulators are 2 runs of 8 consecutive columns, written to the output tile with two
+//   16-byte stores.
 // * State row order.  The state accumulator S (key rows x this wave's value columns) is built
 //   from transposing reads of K whose column starts follow the same sigma; then every state slab
 //   is directly the A operand of S^T Qbar^T and its Q operand is the same 16-byte row read the
@@ -45,7 +47,7 @@ constexpr int C = 64;
 constexpr int D = 128;
 constexpr int NT = 512;    // four compute waves, then four loader waves
 constexpr int TE = C * D;  // elements of one unpadded tile
-constexpr int LDS_TILES = 10;  // 160 KiB: the stage ring holds 3 stages of q, k, v or 5 of k, v
+constexpr int LDS_TILES = 10;  // 160 KiB: 3 stages of q, k, v plus the output tile, or 5 stages of k, v
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -102,9 +104,11 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     float* __restrict__ s_out, int64_t s_out_stride, float* __restrict__ part_state,
     float* __restrict__ part_decay, const float* __restrict__ init_state, int64_t H, int64_t L, int nseg, int G,
     int cps) {
-    constexpr int SLOT = STATE_ONLY ? 2 : 3;  // tiles per stage
-    constexpr int NST = LDS_TILES / SLOT;     // ring stages: NST - 1 chunks in flight
+    constexpr int SLOT = STATE_ONLY ? 2 : 3;                        // tiles per stage
+    constexpr int NST = (LDS_TILES - (STATE_ONLY ? 0 : 1)) / SLOT;  // ring stages: NST - 1 chunks in flight
     __shared__ __attribute__((aligned(16))) __bf16 ring[NST * SLOT * TE];
+    // the chunk's outputs, rows unpadded with 16-byte slot s of row r at s ^ (r % 16)
+    __shared__ __attribute__((aligned(16))) __bf16 otile[STATE_ONLY ? 8 : TE];
     using DM = Dma<STATE_ONLY>;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -133,12 +137,27 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
         for (; issued < NST - 1 && issued < nch; issued++)
             DM::issue(q, k, v, stage(issued), row_base + t_begin + (int64_t)issued * C, chunk_len(issued), lw, lane);
         for (int c = 0; c < nch; c++) {
-            wait_batches<DM::NDMA>(issued - c - 1);  // this wave's part of chunk c has landed
-            __builtin_amdgcn_s_barrier();
+            // this wave's part of chunk c has landed.  Only the younger DMA batches are allowed to be
+            // outstanding: loads complete in order, so while any load of chunk c is pending all
+            // younger loads are too and the count cannot drop that low, whatever the stores do.
+            wait_batches<DM::NDMA>(issued - c - 1);
+            __builtin_amdgcn_s_barrier();  // chunk c is handed to the compute waves
             if (issued < nch) {
                 DM::issue(q, k, v, stage(issued), row_base + t_begin + (int64_t)issued * C, chunk_len(issued), lw,
                           lane);
                 issued++;
+            }
+            if (!STATE_ONLY) {
+                lds_barrier();  // the compute waves have written chunk c's outputs
+                const int n = chunk_len(c);
+                const int64_t r0 = row_base + t_begin + (int64_t)c * C;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int pc = (threadIdx.x - 256) + 256 * r;
+                    const int row = pc >> 4, sl = pc & 15;
+                    const u32x4 y = *(const u32x4*)(otile + row * D + ((sl ^ (row & 15)) << 3));
+                    if (row < n) *(u32x4*)(o + (r0 + row) * D + sl * 8) = y;
+                }
             }
         }
         return;
@@ -187,7 +206,6 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 
     for (int c = 0; c < nch; c++) {
         const Ring cur = stage(c);
-        const int64_t t0 = t_begin + (int64_t)c * C;
         const int n = chunk_len(c);
         lds_barrier();  // chunk c has landed; every wave is done with chunk c - 1
 
@@ -253,20 +271,23 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < 2 * (ib + 1); s2++) acc = mfma(vb[s2], pt[s2], acc);
-                // accumulators 0..7 are value columns 32w + 8kg + 0..7, 8..15 are 32w + 16 + 8kg + 0..7
-                if (itok < n) {
-                    __bf16* orow = o + (row_base + t0 + itok) * D + 32 * w + 8 * kg;
+                // accumulators 0..7 are value columns 32w + 8kg + 0..7 (slot 4w + kg), 8..15 are
+                // 32w + 16 + 8kg + 0..7 (slot 4w + 2 + kg)
+                {
+                    __bf16* orow = otile + itok * D;
                     bf16x8 x0, x1;
 #pragma unroll
                     for (int e = 0; e < 8; e++) {
                         x0[e] = (__bf16)acc[e];
                         x1[e] = (__bf16)acc[8 + e];
                     }
-                    *(bf16x8*)orow = x0;
-                    *(bf16x8*)(orow + 16) = x1;
+                    *(bf16x8*)(orow + (((4 * w + kg) ^ (itok & 15)) << 3)) = x0;
+                    *(bf16x8*)(orow + (((4 * w + 2 + kg) ^ (itok & 15)) << 3)) = x1;
                 }
             }
         }
+
+        if (!STATE_ONLY) lds_barrier();  // the output tile is complete; the loader waves store it
 
         // state: S <- decay(chunk) S + K^T diag(w) V over the chunk's n tokens
         if (MODE == DECAY_HEAD) {

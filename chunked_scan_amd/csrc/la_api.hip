@@ -185,12 +185,12 @@ la_status la_state_scan(const float* seg_states, const float* seg_decay, int32_t
     const int64_t nst = prod4(s->B, s->H, P, (int64_t)s->dk * s->dv);
     if (nst < 0) return LA_ERR_SHAPE;
     if (s->dv % 4 != 0) return LA_ERR_UNSUPPORTED;
-    if (nst > 0 && (!seg_states || !seg_decay || !out_states)) return LA_ERR_NULL;
+    if (nst > 0 && (!seg_states || !out_states)) return LA_ERR_NULL;  // seg_decay NULL: no decay
     if (((uintptr_t)seg_states | (uintptr_t)out_states) % 16 != 0) return LA_ERR_UNSUPPORTED;
     Span sx{seg_states, sizeof(float) * (size_t)nst}, sy{out_states, sizeof(float) * (size_t)nst};
     Span sl{seg_decay, sizeof(float) * (size_t)(s->B * s->H * P * s->dk)};
     if (seg_states != out_states && overlap(sx, sy)) return LA_ERR_ALIAS;
-    if (overlap(sl, sy)) return LA_ERR_ALIAS;
+    if (seg_decay && overlap(sl, sy)) return LA_ERR_ALIAS;
     la_status st = check_trace(s);
     if (st != LA_OK) return st;
     la::Tracer tr = make_tracer(s);

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(const float* x, const f
     const int d = (int)(e / dv);
     const float* xs = x + n * (int64_t)P * per_state + e;
     float* ys = out + n * (int64_t)P * per_state + e;
-    const float* ls = lam + n * (int64_t)P * dk + d;
+    const float* ls = lam ? lam + n * (int64_t)P * dk + d : nullptr;  // null: no decay
     float y = 0.f;
     for (int p0 = 0; p0 < P; p0 += SCAN_BATCH) {
         float xb[SCAN_BATCH], lb[SCAN_BATCH];
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(const float* x, const f
         for (int j = 0; j < SCAN_BATCH; j++) {
             if (j < nb) {
                 xb[j] = xs[(int64_t)(p0 + j) * per_state];
-                lb[j] = ls[(int64_t)(p0 + j) * dk];
+                lb[j] = ls ? ls[(int64_t)(p0 + j) * dk] : 1.f;
             }
         }
 #pragma unroll

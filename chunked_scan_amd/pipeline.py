@@ -9,7 +9,8 @@ correction.
 
 ``device_step``   -- one device holding one segment: local forward, then the All-Scan update
                      S_out = Lambda_total S_recv + S_loc (a two-entry state scan), then
-                     O += (Q * cumulative decay) S_recv.
+                     O += (Q * cumulative decay) S_recv.  Without decay there is no decay to
+                     prepare (Lambda = 1, cumulative decay = 1): the scan runs as a plain sum.
 ``segmented_forward`` -- P devices emulated on one GPU: the local forward of all P segments in
                      one launch, the P-entry state scan, and the correction of segments 1..P-1.
 """
@@ -52,9 +53,10 @@ class DeviceStep:
         la_chunk_fwd(self.q, self.k, self.v, self.decay, None, self.o, self.states[:, :, 1:2], mode=self.mode,
                      chunk=self.chunk, gate_norm=self.gate_norm, subseg_chunks=self.subseg_chunks,
                      timer=t.get("fwd"))
-        la_cumdecay(self.decay, B, H, L, dk, mode=self.mode, gate_norm=self.gate_norm, cum=self.cum,
-                    total=self.totals[:, :, 1:2], want_cum=self.mode == "gate", timer=t.get("cum"))
-        la_state_scan(self.states, self.totals, self.states, timer=t.get("scan"))
+        if self.mode != "none":
+            la_cumdecay(self.decay, B, H, L, dk, mode=self.mode, gate_norm=self.gate_norm, cum=self.cum,
+                        total=self.totals[:, :, 1:2], want_cum=self.mode == "gate", timer=t.get("cum"))
+        la_state_scan(self.states, self.totals if self.mode != "none" else None, self.states, timer=t.get("scan"))
         la_state_correct(self.q, _corr_decay(self.mode, self.decay, self.cum), self.states[:, :, 0:1], self.o,
                          mode=self.mode, timer=t.get("corr"))
         return self.o, self.states[:, :, 1]
@@ -92,9 +94,10 @@ class SegmentedForward:
         la_chunk_fwd(self.q, self.k, self.v, self.decay, self.s_in, self.o, self.states, mode=self.mode, nseg=P,
                      chunk=self.chunk, gate_norm=self.gate_norm, subseg_chunks=self.subseg_chunks,
                      timer=t.get("fwd"))
-        la_cumdecay(self.decay, B, H, L, dk, mode=self.mode, nseg=P, gate_norm=self.gate_norm, cum=self.cum,
-                    total=self.totals, want_cum=self.mode == "gate", timer=t.get("cum"))
-        la_state_scan(self.states, self.totals, self.states, timer=t.get("scan"))
+        if self.mode != "none":
+            la_cumdecay(self.decay, B, H, L, dk, mode=self.mode, nseg=P, gate_norm=self.gate_norm, cum=self.cum,
+                        total=self.totals, want_cum=self.mode == "gate", timer=t.get("cum"))
+        la_state_scan(self.states, self.totals if self.mode != "none" else None, self.states, timer=t.get("scan"))
         if P > 1:
             la_state_correct(self.q, _corr_decay(self.mode, self.decay, self.cum), self.states[:, :, : P - 1], self.o,
                              mode=self.mode, nseg=P, seg_begin=1, timer=t.get("corr"))

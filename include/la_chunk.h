@@ -144,7 +144,8 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float*
  *
  *   seg_states : float[B,H,P,dk,dv]   seg_decay : float[B,H,P,dk] multiplicative per-segment
  *                total decay (a vector over key dims; broadcast a scalar yourself); the entry of
- *                segment 0 only ever multiplies the zero state and is not applied.
+ *                segment 0 only ever multiplies the zero state and is not applied.  NULL means
+ *                no decay (every entry 1), the plain running sum.
  *   out_states : float[B,H,P,dk,dv]; may be the same pointer as seg_states (in place), must not
  *                otherwise overlap it, nor seg_decay.
  * Uses shape->B, H, dk, dv, stream; P is the argument (not shape->nseg).

@@ -152,6 +152,10 @@ def test_state_scan_matches_oracle():
     out = lb.la_state_scan(xint.cuda(), torch.ones((B, H, P, dk)).cuda())
     torch.cuda.synchronize()
     assert torch.equal(out.cpu(), torch.cumsum(xint, dim=2))
+    # no decay (NULL seg_decay) is the same running sum
+    out = lb.la_state_scan(xint.cuda(), None)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), torch.cumsum(xint, dim=2))
 
 
 @pytest.mark.parametrize("mode", ["none", "head", "gate"])
