@@ -207,6 +207,14 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     for (int c = 0; c < nch; c++) {
         const Ring cur = stage(c);
         const int n = chunk_len(c);
+        // Head decay: the factors exp(lambda d) are recomputed every chunk from a few base-2
+        // exponentials and chains of multiplications by exp(lambda) (every factor <= 1).  Hiding
+        // lambda's value from the optimiser each chunk keeps these loop invariants from being
+        // hoisted into registers for the whole loop.
+        float lamc = lam;
+        if (MODE == DECAY_HEAD) asm volatile("" : "+s"(lamc));
+        lamc *= LOG2E;
+        const float e1 = (MODE == DECAY_HEAD) ? decay_pow2(lamc, 1) : 1.f;
         lds_barrier();  // chunk c has landed; every wave is done with chunk c - 1
 
         // V operand: tokens 16ks + kg*8 + jj (plain order), value column vcol_lane
@@ -230,6 +238,12 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 #pragma unroll
             for (int ib = 0; ib < 2; ib++) {
                 const int itok = ib * 32 + n32;
+                // the diagonal block's decay factors are the same for both halves: recomputing them
+                // is cheaper than keeping them live
+                float lamb = lam;
+                if (MODE == DECAY_HEAD) asm volatile("" : "+s"(lamb));
+                lamb *= LOG2E;
+                const float e1b = (MODE == DECAY_HEAD) ? decay_pow2(lamb, 1) : 1.f;
                 // Q operand (B of both products): token itok, key dims ks*16 + kg*8 .. +8
                 bf16x8 qb[8];
 #pragma unroll
@@ -246,12 +260,25 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                         sc = mfma(*(const bf16x8*)(cur.k + sw(krow, ks * 16 + kg * 8)), qb[ks], sc);
 #pragma unroll
                     for (int hh = 0; hh < 2; hh++) {
+                        // head decay: fac[jj] = exp(lambda max(itok - jtok, 0)); itok - jtok grows by one
+                        // from jj = 7 down to jj = 0
+                        float fac[8];
+                        if (MODE == DECAY_HEAD) {
+                            const int d7 = 32 * (ib - jb) + n32 - 16 * hh - 8 * kg - 7;
+                            float gch = decay_pow2(lamb, max(d7, 0));
+                            fac[7] = gch;
+#pragma unroll
+                            for (int jj = 6; jj >= 0; jj--) {
+                                gch = (d7 + 7 - jj > 0) ? gch * e1b : 1.f;
+                                fac[jj] = gch;
+                            }
+                        }
                         bf16x8 x;
 #pragma unroll
                         for (int jj = 0; jj < 8; jj++) {
                             const int jtok = jb * 32 + 16 * hh + kg * 8 + jj;
                             float val = sc[8 * hh + jj];
-                            if (MODE == DECAY_HEAD) val *= decay_pow(lam, max(itok - jtok, 0));
+                            if (MODE == DECAY_HEAD) val *= fac[jj];
                             if (jb == ib && jtok > itok) val = 0.f;
                             x[jj] = (__bf16)val;
                         }
@@ -265,7 +292,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 #pragma unroll
                     for (int hh = 0; hh < 2; hh++) acc = mfma(sa[m][hh], qb[2 * m + hh], acc);
                 if (MODE == DECAY_HEAD) {
-                    const float f = decay_pow(lam, itok + 1);
+                    const float f = decay_pow2(lamb, itok + 1);
 #pragma unroll
                     for (int i = 0; i < 16; i++) acc[i] *= f;
                 }
@@ -291,18 +318,24 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 
         // state: S <- decay(chunk) S + K^T diag(w) V over the chunk's n tokens
         if (MODE == DECAY_HEAD) {
-            const float fh = decay_pow(lam, n);
+            const float fh = decay_pow2(lamc, n);
 #pragma unroll
             for (int m = 0; m < 4; m++)
 #pragma unroll
                 for (int i = 0; i < 16; i++) S[m][i] *= fh;
+            // token t = 16 ks + kg*8 + jj gets exp(lambda (n - 1 - t)), or 0 past the chunk's end;
+            // the exponent grows by one from jj = 7 down to jj = 0
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++)
+            for (int ks = 0; ks < 4; ks++) {
+                const int e7 = n - 1 - (16 * ks + kg * 8 + 7);
+                float gch = decay_pow2(lamc, max(e7, 0));
 #pragma unroll
-                for (int jj = 0; jj < 8; jj++) {
-                    const int t = 16 * ks + kg * 8 + jj;
-                    vb[ks][jj] = (t < n) ? (__bf16)((float)vb[ks][jj] * decay_pow(lam, n - 1 - t)) : (__bf16)0.f;
+                for (int jj = 7; jj >= 0; jj--) {
+                    const int e = e7 + 7 - jj;
+                    if (jj < 7) gch = (e > 0) ? gch * e1 : 1.f;
+                    vb[ks][jj] = (e >= 0) ? (__bf16)((float)vb[ks][jj] * gch) : (__bf16)0.f;
                 }
+            }
         } else if (n < C) {
 #pragma unroll
             for (int ks = 0; ks < 4; ks++)

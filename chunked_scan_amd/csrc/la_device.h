@@ -44,6 +44,13 @@ __device__ __forceinline__ float gate_logdecay(float g, float inv_norm) {
 // lam = -inf (a = 0).
 __device__ __forceinline__ float decay_pow(float lam, int m) { return m == 0 ? 1.f : expf(lam * (float)m); }
 
+// The same power through the hardware base-2 exponential (one instruction, about 1 ulp):
+// lam2 = lam * log2(e); a^0 = 1 exactly, also for lam2 = -inf.
+__device__ __forceinline__ float decay_pow2(float lam2, int m) {
+    return m == 0 ? 1.f : __builtin_amdgcn_exp2f(lam2 * (float)m);
+}
+constexpr float LOG2E = 1.44269504088896340736f;
+
 // s_waitcnt with vmcnt = N (outstanding vector memory operations of this wave) and lgkmcnt = Lg
 // (outstanding LDS operations), expcnt left alone.  Used with a bare s_barrier where a full
 // __syncthreads would also drain this wave's global loads that are meant to stay in flight.
