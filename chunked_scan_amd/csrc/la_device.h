@@ -14,6 +14,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum { DECAY_NONE = 0, DECAY_HEAD = 1, DECAY_GATE = 2 };
 
+constexpr float LOG2E = 1.44269504088896340736f;
+constexpr float LN2 = 0.69314718055994530942f;
+
 // bf16 <-> f32.  The widening is exact; the narrowing rounds to nearest even (gfx950 has a
 // native packed instruction for it, which the compiler selects for this cast).
 __device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
@@ -33,10 +36,13 @@ template <> struct io<__bf16> {
 };
 
 // Per-token log-decay of the gate mode: log sigmoid(g) / norm = -softplus(-g) / norm, written
-// so that neither branch overflows: softplus(x) = max(x, 0) + log1p(exp(-|x|)).
+// so that neither branch overflows: softplus(x) = max(x, 0) + log(1 + exp(-|x|)).  The hardware
+// base-2 exponential and logarithm (about 1 ulp each) evaluate it; 1 + exp(-|x|) lies in (1, 2],
+// so rounding it costs at most 2^-24 in absolute terms, which is what the cumulative sums see.
 __device__ __forceinline__ float gate_logdecay(float g, float inv_norm) {
-    float x = -g;
-    float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+    const float x = -g;
+    const float y = __builtin_amdgcn_exp2f(-fabsf(x) * LOG2E);
+    const float sp = fmaxf(x, 0.f) + LN2 * __builtin_amdgcn_logf(1.f + y);
     return -sp * inv_norm;
 }
 
@@ -49,7 +55,6 @@ __device__ __forceinline__ float decay_pow(float lam, int m) { return m == 0 ? 1
 __device__ __forceinline__ float decay_pow2(float lam2, int m) {
     return m == 0 ? 1.f : __builtin_amdgcn_exp2f(lam2 * (float)m);
 }
-constexpr float LOG2E = 1.44269504088896340736f;
 
 // s_waitcnt with vmcnt = N (outstanding vector memory operations of this wave) and lgkmcnt = Lg
 // (outstanding LDS operations), expcnt left alone.  Used with a bare s_barrier where a full

@@ -48,9 +48,8 @@ __global__ __launch_bounds__(256) void state_scan_kernel(const float* x, const f
 
 // ---------------------------------------------------------------------------------------------
 // Cumulative decay.  HEAD and NONE have closed forms; GATE needs a running sum of log a over the
-// segment, done in two passes over blocks of CUM_TB tokens: block sums, then a prefix over the
-// block sums plus a running sum inside each block.
-constexpr int CUM_TB = 256;
+// segment (below).
+constexpr int CUM_TB = 64;
 
 __global__ __launch_bounds__(256) void cumdecay_closed_kernel(const float* __restrict__ lamh, float* __restrict__ cum,
                                                               float* __restrict__ total, int64_t total_stride,
@@ -73,24 +72,89 @@ __global__ __launch_bounds__(256) void cumdecay_closed_kernel(const float* __res
     }
 }
 
-// partial[(bh*nseg + p)*nblk + blk][d] = sum of log a over the block's tokens.
+// Gate mode, three passes over blocks of CUM_TB tokens of a segment:
+//   1. partial[(bh*nseg + p)*nblk + blk][d] = sum of log a over the block's tokens;
+//   2. the partials of each (b,h,segment) replaced in place by their exclusive prefix;
+//   3. cum = exp(prefix + running sum inside the block) for every token, and the segment total.
+// A thread owns one key dim of one block; consecutive threads take consecutive key dims, so every
+// load and store of a token row is contiguous.  Each thread issues its loads GBATCH at a time
+// before using any of them, so a block costs CUM_TB / GBATCH memory round trips.
+constexpr int GBATCH = 16;
+
+struct GateBlock {
+    int64_t bh, bhp;
+    int p, blk, d;
+    int64_t t0, t1;
+};
+__device__ __forceinline__ GateBlock gate_block(int64_t i, int64_t L, int dk, int nseg, int nblk) {
+    GateBlock x;
+    x.d = (int)(i % dk);
+    const int64_t r = i / dk;  // (bh*nseg + p)*nblk + blk
+    x.blk = (int)(r % nblk);
+    x.bhp = r / nblk;
+    x.p = (int)(x.bhp % nseg);
+    x.bh = x.bhp / nseg;
+    const int64_t Ls = L / nseg;
+    x.t0 = (int64_t)x.p * Ls + (int64_t)x.blk * CUM_TB;
+    x.t1 = min(x.t0 + CUM_TB, (int64_t)(x.p + 1) * Ls);
+    return x;
+}
+
 __global__ __launch_bounds__(256) void cumdecay_gate_blocksum_kernel(const float* __restrict__ g, float* __restrict__ partial,
                                                                      int64_t L, int dk, int nseg, int nblk,
                                                                      int64_t nthreads, float inv_norm) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nthreads) return;
-    const int d = (int)(i % dk);
-    const int64_t r = i / dk;  // ((bh*nseg + p)*nblk + blk)
-    const int blk = (int)(r % nblk);
-    const int64_t bhp = r / nblk;
-    const int p = (int)(bhp % nseg);
-    const int64_t bh = bhp / nseg;
-    const int64_t Ls = L / nseg;
-    const int64_t t0 = (int64_t)p * Ls + (int64_t)blk * CUM_TB;
-    const int64_t t1 = min(t0 + CUM_TB, (int64_t)(p + 1) * Ls);
+    const GateBlock x = gate_block(i, L, dk, nseg, nblk);
+    const float* gp = g + (x.bh * L) * dk + x.d;
     float s = 0.f;
-    for (int64_t t = t0; t < t1; t++) s += gate_logdecay(g[(bh * L + t) * dk + d], inv_norm);
+    for (int64_t t = x.t0; t < x.t1; t += GBATCH) {
+        float gv[GBATCH];
+#pragma unroll
+        for (int j = 0; j < GBATCH; j++) gv[j] = gp[min(t + j, x.t1 - 1) * dk];
+#pragma unroll
+        for (int j = 0; j < GBATCH; j++)
+            if (t + j < x.t1) s += gate_logdecay(gv[j], inv_norm);
+    }
     partial[i] = s;
+}
+
+// One workgroup per (b,h,segment) and 32 key dims: eight parts of the block list each sum their
+// share, exchange the part sums through LDS, and write their blocks' exclusive prefixes.
+__global__ __launch_bounds__(256) void cumdecay_gate_prefix_kernel(float* __restrict__ partial, int dk, int nblk) {
+    __shared__ float part_sum[8][32];
+    const int dl = threadIdx.x & 31, part = threadIdx.x >> 5;
+    const int dgroups = (dk + 31) / 32;
+    const int64_t bhp = blockIdx.x / dgroups;
+    const int d = (int)(blockIdx.x % dgroups) * 32 + dl;
+    const int per = (nblk + 7) / 8;
+    const int b0 = min(nblk, part * per), b1 = min(nblk, b0 + per);
+    float* base = partial + bhp * (int64_t)nblk * dk + min(d, dk - 1);
+    float s = 0.f;
+    for (int b = b0; b < b1; b += GBATCH) {
+        float v[GBATCH];
+#pragma unroll
+        for (int j = 0; j < GBATCH; j++) v[j] = base[(int64_t)min(b + j, b1 - 1) * dk];
+#pragma unroll
+        for (int j = 0; j < GBATCH; j++)
+            if (b + j < b1) s += v[j];
+    }
+    part_sum[part][dl] = s;
+    __syncthreads();
+    float run = 0.f;
+    for (int j = 0; j < part; j++) run += part_sum[j][dl];
+    if (d >= dk) return;
+    for (int b = b0; b < b1; b += GBATCH) {
+        float v[GBATCH];
+#pragma unroll
+        for (int j = 0; j < GBATCH; j++) v[j] = base[(int64_t)min(b + j, b1 - 1) * dk];
+#pragma unroll
+        for (int j = 0; j < GBATCH; j++)
+            if (b + j < b1) {
+                base[(int64_t)(b + j) * dk] = run;
+                run += v[j];
+            }
+    }
 }
 
 __global__ __launch_bounds__(256) void cumdecay_gate_scan_kernel(const float* __restrict__ g, const float* __restrict__ partial,
@@ -99,26 +163,25 @@ __global__ __launch_bounds__(256) void cumdecay_gate_scan_kernel(const float* __
                                                                  int64_t nthreads, float inv_norm) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nthreads) return;
-    const int d = (int)(i % dk);
-    const int64_t r = i / dk;
-    const int blk = (int)(r % nblk);
-    const int64_t bhp = r / nblk;
-    const int p = (int)(bhp % nseg);
-    const int64_t bh = bhp / nseg;
-    const int64_t Ls = L / nseg;
-    float run = 0.f;
-    for (int b = 0; b < blk; b++) run += partial[(bhp * nblk + b) * dk + d];
-    const int64_t t0 = (int64_t)p * Ls + (int64_t)blk * CUM_TB;
-    const int64_t t1 = min(t0 + CUM_TB, (int64_t)(p + 1) * Ls);
-    if (cum) {
-        for (int64_t t = t0; t < t1; t++) {
-            run += gate_logdecay(g[(bh * L + t) * dk + d], inv_norm);
-            cum[(bh * L + t) * dk + d] = expf(run);
+    const GateBlock x = gate_block(i, L, dk, nseg, nblk);
+    float run = partial[i];  // exclusive prefix of this block
+    const float* gp = g + (x.bh * L) * dk + x.d;
+    float* cp = cum ? cum + (x.bh * L) * dk + x.d : nullptr;
+    const bool last = x.blk == nblk - 1;
+    if (cp || last) {
+        for (int64_t t = x.t0; t < x.t1; t += GBATCH) {
+            float gv[GBATCH];
+#pragma unroll
+            for (int j = 0; j < GBATCH; j++) gv[j] = gp[min(t + j, x.t1 - 1) * dk];
+#pragma unroll
+            for (int j = 0; j < GBATCH; j++)
+                if (t + j < x.t1) {
+                    run += gate_logdecay(gv[j], inv_norm);
+                    if (cp) cp[(t + j) * dk] = __builtin_amdgcn_exp2f(run * LOG2E);
+                }
         }
-    } else {
-        run += partial[i];
     }
-    if (total && blk == nblk - 1) total[bh * total_stride + (int64_t)p * dk + d] = expf(run);
+    if (total && last) total[x.bh * total_stride + (int64_t)x.p * dk + x.d] = __builtin_amdgcn_exp2f(run * LOG2E);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -253,6 +316,13 @@ hipError_t launch_cumdecay(const float* decay, float* cum, float* total, int64_t
               cumdecay_gate_blocksum_kernel<<<grid, 256, 0, stream>>>(decay, partial, L, dk, nseg, nblk, nthreads,
                                                                       inv_norm));
     e = hipGetLastError();
+    if (e == hipSuccess) {
+        const int64_t nbhp = B * H * (int64_t)nseg;
+        LA_TRACED(tr, "cumdecay_gate_prefix",
+                  cumdecay_gate_prefix_kernel<<<(unsigned)(nbhp * ((dk + 31) / 32)), 256, 0, stream>>>(partial, dk,
+                                                                                                       nblk));
+        e = hipGetLastError();
+    }
     if (e == hipSuccess) {
         LA_TRACED(tr, "cumdecay_gate_scan",
                   cumdecay_gate_scan_kernel<<<grid, 256, 0, stream>>>(decay, partial, cum, total, total_stride, L, dk,
