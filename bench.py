@@ -9,6 +9,10 @@ pages' per-device shape (B=1, H=16, L=16384, dk=dv=128, bf16, chunk 64, no decay
 Prints one JSON line.  Per-kernel durations come from HIP events that the library records
 around every kernel on the stream it launches them on (la_trace); the dominant kernel's
 roofline uses its algorithmic bytes (q, k, v read + o written) over its mean duration.
+Per-step statistics (median, mean, std, min) are given warm and cold (a 512 MiB buffer written
+before each step evicts the 256 MB last-level cache).  The head-decay and gate workloads
+(device step, B = 2 and 4) and the 1M-token 64-segment pass are timed alongside, unless
+--no-alongside.
 """
 from __future__ import annotations
 
@@ -51,6 +55,52 @@ def algorithmic(w, mode_bytes_gate: int):
     return by, fl
 
 
+def step_stats(step, steps, stream, scratch=None):
+    """Per-step times (us) with events around each step; with ``scratch``, the buffer is rewritten
+    before every step so that the step starts with a cold last-level cache."""
+    import statistics
+
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if scratch is not None:
+            scratch.fill_(1.0)
+        a.record(stream)
+        step.run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = [1e3 * a.elapsed_time(b) for a, b in evs]
+    return dict(median_us=round(statistics.median(t), 2), mean_us=round(statistics.mean(t), 2),
+                std_us=round(statistics.pstdev(t), 2), min_us=round(min(t), 2))
+
+
+def kernel_stats(step, steps, stream):
+    """Mean duration of every library kernel over ``steps`` steps, from the events the library
+    records around each kernel on its stream."""
+    import torch
+
+    from chunked_scan_amd import binding
+
+    timers = [{c: binding.KernelTimer(4) for c in ("fwd", "cum", "scan", "corr")} for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        step.run(timers=timers[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for tset in timers:
+        for c in ("fwd", "cum", "scan", "corr"):
+            for name, ms in tset[c].harvest():
+                per_kernel.setdefault(name, []).append(ms)
+    kernels = {n: dict(mean_us=1e3 * sum(v) / len(v), launches_per_step=len(v) / steps, min_us=1e3 * min(v))
+               for n, v in per_kernel.items()}
+    return kernels, e0.elapsed_time(e1) / steps
+
+
 def cpu_baseline(w, inp):
     import numpy as np
     import torch
@@ -87,6 +137,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1, help="index into chunked_scan_amd.inputs.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-alongside", action="store_true",
+                    help="skip the decay and segmented workloads reported next to the headline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -99,7 +151,7 @@ def main():
 
     from chunked_scan_amd import binding
     from chunked_scan_amd.inputs import WORKLOADS, make_inputs
-    from chunked_scan_amd.pipeline import DeviceStep
+    from chunked_scan_amd.pipeline import DeviceStep, SegmentedForward
 
     w = WORKLOADS[args.workload]
     if w.nseg != 1:
@@ -110,6 +162,8 @@ def main():
     step = DeviceStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk,
                       gate_norm=w.gate_norm)
     stream = torch.cuda.current_stream()
+    # writing this buffer evicts the 256 MB last-level cache before a "cold" step
+    scratch = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
 
     for _ in range(args.warmup):
         step.run()
@@ -127,23 +181,44 @@ def main():
     ms_per_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
 
-    # --- timed region 2: the same steps with HIP events around every kernel (la_trace)
-    timers = [{c: binding.KernelTimer(4) for c in ("fwd", "cum", "scan", "corr")} for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        step.run(timers=timers[i])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_traced = e0.elapsed_time(e1) / args.steps
-    per_kernel = {}
-    for tset in timers:
-        for c in ("fwd", "cum", "scan", "corr"):
-            for name, ms in tset[c].harvest():
-                per_kernel.setdefault(name, []).append(ms)
-    kernels = {n: dict(mean_us=1e3 * sum(v) / len(v), launches_per_step=len(v) / args.steps,
-                       min_us=1e3 * min(v)) for n, v in per_kernel.items()}
+    # --- timed region 2: every step bracketed by its own events, warm and cold
+    warm = step_stats(step, args.steps, stream)
+    cold = step_stats(step, args.steps, stream, scratch)
+    log(f"[bench] per step: warm median {warm['median_us']:.1f} us, cold median {cold['median_us']:.1f} us")
+
+    # --- timed region 3: the same steps with HIP events around every kernel (la_trace)
+    kernels, ms_traced = kernel_stats(step, args.steps, stream)
     log("[bench] per kernel: " + ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in kernels.items()))
+
+    alongside = {}
+    if not args.no_alongside:
+        for wid in (2, 3, 4):
+            if wid == args.workload:
+                continue
+            wa = WORKLOADS[wid]
+            log(f"[bench] alongside: workload {wid} {wa.name}")
+            ia = make_inputs(wa, "cuda")
+            if wa.nseg == 1:
+                sa = DeviceStep(ia["q"], ia["k"], ia["v"], ia["decay"], ia["s_in"], mode=wa.mode, chunk=wa.chunk,
+                                gate_norm=wa.gate_norm)
+            else:
+                sa = SegmentedForward(ia["q"], ia["k"], ia["v"], ia["decay"], ia["s_in"], mode=wa.mode,
+                                      nseg=wa.nseg, chunk=wa.chunk, gate_norm=wa.gate_norm)
+            for _ in range(3):
+                sa.run()
+            torch.cuda.synchronize()
+            n_al = 10 if wa.nseg > 1 else 20
+            st = step_stats(sa, n_al, stream)
+            ks, _ = kernel_stats(sa, n_al, stream)
+            alongside[wa.name] = dict(
+                step=("segmented pass over %d segments" % wa.nseg) if wa.nseg > 1 else "device step",
+                B=wa.B, H=wa.H, L=wa.L, decay=wa.decay, tokens_per_s=round(wa.B * wa.L / (st["median_us"] * 1e-6), 1),
+                per_step_us=st, kernels={n: {k: round(v, 2) for k, v in d.items()} for n, d in ks.items()})
+            log(f"[bench]   {wa.name}: median {st['median_us']:.1f} us/step, "
+                f"{alongside[wa.name]['tokens_per_s']:.3e} tokens/s; " +
+                ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in ks.items()))
+            del sa, ia
+            torch.cuda.empty_cache()
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -204,8 +279,10 @@ def main():
                    "chunk": w.chunk, "decay": w.decay, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "per_step_us": {"warm": warm, "cold": cold},
         "kernels": {n: {k: round(v, 2) for k, v in d.items()} for n, d in kernels.items()},
         "ms_per_step_with_kernel_events": round(ms_traced, 5),
+        "alongside": alongside,
     }
     print(json.dumps(out), flush=True)
 
