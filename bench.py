@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_output_pass_plain_B1_H16_L16k_d128.json")
-KERNEL_SRCS = [os.path.join(ROOT, "chunked_scan_amd", "csrc", f) for f in ("chunk_fwd_mfma.hip", "chunk_fwd_pipe.hip")]
+KERNEL_SRCS = [os.path.join(ROOT, "chunked_scan_amd", "csrc", f) for f in ("chunk_fwd_split.hip", "chunk_fwd_pipe.hip")]
 
 
 def log(*a):

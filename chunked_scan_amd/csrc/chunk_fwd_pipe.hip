@@ -1,20 +1,38 @@
-// chunk_fwd_pipe.hip -- bf16 MFMA chunked forward for dk = dv = 128, chunk = 64, decay modes
-// none and per-head, with the chunk tiles streamed HBM -> LDS by asynchronous DMA.
+// chunk_fwd_pipe.hip -- bf16 MFMA chunked forward for dk = dv = 128, chunk = 64, all three
+// decay modes, with the chunk tiles streamed HBM -> LDS ahead of the matrix cores.
 //
-// Same mathematics and the same sub-segment split as chunk_fwd_mfma.hip (pass 1 local states,
-// internal state scan, pass 2 outputs from exact incoming states).  What differs is the data
-// path, designed around the MFMA register layouts so that almost nothing but MFMA operands
-// moves per chunk:
+// One workgroup owns one sub-segment of one (b, h, segment) (the split is in chunk_fwd_split.hip)
+// and walks its 64-token chunks in order; the fp32 state S (128 x 128) lives in MFMA accumulator
+// registers for the whole walk.  Per chunk of n <= 64 tokens, with B_i the inclusive in-chunk
+// cumulative log-decay (per key dim in gate mode, lambda*(i+1) in head mode):
+//   P[i][j] = sum_d qbar_i[d] kbar_j[d]     masked to j <= i            (intra-chunk "diagonal")
+//   O       = diag-scaled (Qbar S) + P V                                 (inter + intra)
+//   S      <- diag(exp(B_{n-1})) S + Ktilde^T V,   Ktilde_j = k_j * exp(B_{n-1} - B_j)
+// Head/none modes compute P from raw q, k and apply exp(lambda (i-j)) elementwise, and scale the
+// rows of Q S by exp(lambda (i+1)) after the product, so every factor is <= 1.  Gate mode must put
+// the per-key-dim decay inside the contraction: qbar = q*exp(B_i) (<= 1), kbar = k*exp(-B_j)
+// (>= 1, bounded by the chunk's decay span), as in the K-bar / Lambda / Gamma vectors that the
+// ZeCO review page discusses (referee_report.minor_comments[3]); its state update is written
+// S <- diag(exp(B_{n-1})) (S + Kbar^T V), which needs no third key tile.
 //
-// * Loader and compute waves.  In these two modes the tiles are used exactly as stored (all decay
-//   factors are applied to products in registers), so q, k, v go straight from HBM into LDS with
-//   global_load_lds_dwordx4, issued by four loader waves.  The stage buffers form a ring: three
-//   stages of q, k, v (two chunks in flight while one is computed) in the output pass, five of
-//   k, v (four in flight) in the state pass, whose compute per chunk is light.  The compute waves
-//   touch no global memory after their start: they write each chunk's outputs into an LDS tile,
-//   which the loader waves store row-major (1 KiB contiguous per instruction).  Per chunk one
-//   barrier hands a landed stage to the compute waves and frees the stage they finished, and (in
-//   the output pass) a second one hands the output tile to the loader waves.
+// The data path is designed around the MFMA register layouts so that almost nothing but MFMA
+// operands moves per chunk:
+//
+// * Loader and compute waves.  Without decay and with head decay the tiles are used exactly as
+//   stored (all decay factors are applied to products in registers), so q, k, v go straight from
+//   HBM into LDS with global_load_lds_dwordx4, issued by four loader waves.  The stage buffers
+//   form a ring: three stages of q, k, v (two chunks in flight while one is computed) in the
+//   output pass, five of k, v (four in flight) in the state pass, whose compute per chunk is
+//   light.  The compute waves touch no global memory after their start: they write each chunk's
+//   outputs into an LDS tile, which the loader waves store row-major (1 KiB contiguous per
+//   instruction).  Per chunk one barrier hands a landed stage to the compute waves and frees the
+//   stage they finished, and (in the output pass) a second one hands the output tile over.
+// * Gate mode.  The loader waves load q, k, v and g into registers two chunks ahead and, while
+//   the compute waves work on chunk c, prepare chunk c + 1 in its stage: the in-chunk cumulative
+//   log-decay (a per-lane prefix plus a DPP scan across lanes), qbar, kbar, v and the chunk's
+//   decay per key dim.  The compute waves then run the no-decay products and scale their state
+//   rows by the chunk decay; they store their outputs themselves (the prepared stages leave no
+//   room for an output tile).
 // * Ragged chunks.  DMA rows past a chunk's end re-read its last row, which only reaches output
 //   rows that are never stored; the state update zeroes those tokens' V operand in registers.
 // * Swizzle.  Tiles are unpadded (one DMA instruction writes 1 KiB contiguous), so the 16-byte
@@ -74,6 +92,7 @@ struct Ring {
     __bf16* q;
     __bf16* k;
     __bf16* v;
+    float* el;  // gate mode: the chunk's decay per key dim, exp(B of its last token)
 };
 
 template <bool STATE_ONLY>
@@ -83,16 +102,17 @@ struct Dma {
     // the chunk's last valid row.
     __device__ static __forceinline__ void issue(const __bf16* q, const __bf16* k, const __bf16* v, Ring r,
                                                  int64_t row0, int n, int lw, int lane) {
+        // a wave-uniform base plus a 32-bit lane offset per instruction
+        const int64_t base = row0 * D;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const int R = (4 * lw + j) * 4 + (lane >> 4);
-            const int ls = (lane & 15) ^ swz(R);
-            const int64_t off = (row0 + min(R, n - 1)) * D + ls * 8;
+            const int off = min(R, n - 1) * D + (((lane & 15) ^ swz(R)) << 3);
             const int dst = (4 * lw + j) * 512;
             if (!STATE_ONLY)
-                __builtin_amdgcn_global_load_lds((const void*)(q + off), (lds_void*)(r.q + dst), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(k + off), (lds_void*)(r.k + dst), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(v + off), (lds_void*)(r.v + dst), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)(q + base + off), (lds_void*)(r.q + dst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(k + base + off), (lds_void*)(r.k + dst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(v + base + off), (lds_void*)(r.v + dst), 16, 0, 0);
         }
     }
 };
@@ -103,12 +123,16 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     const float* __restrict__ decay, const float* __restrict__ s_in, __bf16* __restrict__ o,
     float* __restrict__ s_out, int64_t s_out_stride, float* __restrict__ part_state,
     float* __restrict__ part_decay, const float* __restrict__ init_state, int64_t H, int64_t L, int nseg, int G,
-    int cps) {
-    constexpr int SLOT = STATE_ONLY ? 2 : 3;                        // tiles per stage
-    constexpr int NST = (LDS_TILES - (STATE_ONLY ? 0 : 1)) / SLOT;  // ring stages: NST - 1 chunks in flight
-    __shared__ __attribute__((aligned(16))) __bf16 ring[NST * SLOT * TE];
+    int cps, float inv_norm) {
+    constexpr bool GATE = MODE == DECAY_GATE;
+    constexpr bool OTILE = !STATE_ONLY && !GATE;  // outputs leave through an LDS tile stored by the loaders
+    constexpr int SLOT = STATE_ONLY ? 2 : 3;      // tiles per stage
+    constexpr int STAGE = SLOT * TE + (GATE ? 2 * D : 0);  // gate: D floats of chunk decay after the tiles
+    // ring stages: NST - 1 chunks in flight (gate: the loaders prepare one stage ahead, so three)
+    constexpr int NST = GATE ? 3 : (LDS_TILES - (OTILE ? 1 : 0)) / SLOT;
+    __shared__ __attribute__((aligned(16))) __bf16 ring[NST * STAGE];
     // the chunk's outputs, rows unpadded with 16-byte slot s of row r at s ^ (r % 16)
-    __shared__ __attribute__((aligned(16))) __bf16 otile[STATE_ONLY ? 8 : TE];
+    __shared__ __attribute__((aligned(16))) __bf16 otile[OTILE ? TE : 8];
     using DM = Dma<STATE_ONLY>;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -125,11 +149,148 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     const int64_t row_base = bh * L;
     const int nch = (int)((t_end - t_begin + C - 1) / C);
     auto stage = [&](int c) {
-        __bf16* b = ring + (c % NST) * SLOT * TE;
-        return Ring{b, b + (SLOT - 2) * TE, b + (SLOT - 1) * TE};  // q is unused in the state pass
+        __bf16* b = ring + (c % NST) * STAGE;
+        // q is unused in the state pass
+        return Ring{b, b + (SLOT - 2) * TE, b + (SLOT - 1) * TE, (float*)(b + SLOT * TE)};
     };
     auto chunk_len = [&](int c) { return (int)min((int64_t)C, t_end - t_begin - (int64_t)c * C); };
 
+    if (wave >= 4 && GATE) {
+        // ---- gate-mode loader wave lw.  Its lanes load q, k, v and g two chunks ahead into
+        // registers (plain loads: a wave that mixes LDS DMA with reads of what it loaded gets every
+        // wait widened to the whole queue), and while the compute waves work on chunk c it prepares
+        // chunk c + 1 in its stage: B = inclusive in-chunk sum of log2 a per key dim, q exp2(B),
+        // k exp2(-B) and v written to the tiles, el = exp2(B of the last token).  Lane: key dims
+        // 8 o8 .. +7 of tokens 4 tg .. +3; the 16 token groups of a dim octet are one 16-lane row,
+        // so the scan over them is DPP.
+        const int lw = wave - 4;
+        const int o8 = 4 * lw + (lane >> 4);
+        const int tg = lane & 15;
+        struct Raw {
+            u32x4 q[4], k[4], v[4];
+            f32x4 g[8];
+        };
+        Raw rA, rB;
+        float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // state pass: sum of the chunk totals
+        int issued = 0;
+        // token row r of chunk `issued` into x (5 loads); the chunk counts as issued after row 3
+        auto load_row = [&](Raw& x, int r) {
+            const int n = chunk_len(issued);
+            const int64_t base = (row_base + t_begin + (int64_t)issued * C) * D;
+            const int off = min(4 * tg + r, n - 1) * D + 8 * o8;
+            if (!STATE_ONLY) x.q[r] = *(const u32x4*)(q + base + off);
+            x.k[r] = *(const u32x4*)(k + base + off);
+            x.v[r] = *(const u32x4*)(v + base + off);
+            x.g[2 * r] = *(const f32x4*)(decay + base + off);
+            x.g[2 * r + 1] = *(const f32x4*)(decay + base + off + 4);
+            if (r == 3) issued++;
+        };
+        auto load = [&](Raw& x) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) load_row(x, r);
+        };
+        // Prepares chunk cc from x while (if more) the rows of the next chunk load into fill, one row
+        // between the steps of the preparation: the wave keeps the memory pipeline fed instead of
+        // stalling on a burst of loads.
+        auto prep = [&](const Raw& x, int cc, bool more, Raw& fill) {
+            const int n = chunk_len(cc);
+            const Ring st = stage(cc);
+            float b[4][8];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    // computed for every row (past the end, g is a copy of the last row), then selected
+                    const float la = gate_logdecay(x.g[2 * r + (e >> 2)][e & 3], inv_norm) * LOG2E;
+                    b[r][e] = (r ? b[r - 1][e] : 0.f) + (4 * tg + r < n ? la : 0.f);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (more && r < 3) load_row(fill, r);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // exclusive prefix of the lane totals over the 16 token groups: an inclusive scan along
+            // the 16-lane row (row_shr by 1, 2, 4, 8; lanes shifted in from outside the row add 0)
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                float y = b[3][e];
+                y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0x111, 0xf, 0xf, true));
+                y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0x112, 0xf, 0xf, true));
+                y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0x114, 0xf, 0xf, true));
+                y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0x118, 0xf, 0xf, true));
+                const float ex = y - b[3][e];
+#pragma unroll
+                for (int r = 0; r < 4; r++) b[r][e] += ex;
+            }
+            // the chunk's decay per key dim: B of its last token (lane 15 of the row for a full chunk)
+            float bl[8];
+            if (n == C) {
+                const int row = lane >> 4;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const int r0v = __builtin_amdgcn_readlane(__float_as_int(b[3][e]), 15);
+                    const int r1v = __builtin_amdgcn_readlane(__float_as_int(b[3][e]), 31);
+                    const int r2v = __builtin_amdgcn_readlane(__float_as_int(b[3][e]), 47);
+                    const int r3v = __builtin_amdgcn_readlane(__float_as_int(b[3][e]), 63);
+                    bl[e] = __int_as_float(row == 0 ? r0v : row == 1 ? r1v : row == 2 ? r2v : r3v);
+                }
+            } else {
+                const int tl = n - 1, src = (lane & 48) + (tl >> 2), rl = tl & 3;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float sel = rl == 0 ? b[0][e] : rl == 1 ? b[1][e] : rl == 2 ? b[2][e] : b[3][e];
+                    bl[e] = __shfl(sel, src);
+                }
+            }
+            if (tg == 0) {
+                f32x4 e0, e1;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    e0[e] = __builtin_amdgcn_exp2f(bl[e]);
+                    e1[e] = __builtin_amdgcn_exp2f(bl[4 + e]);
+                }
+                *(f32x4*)(st.el + 8 * o8) = e0;
+                *(f32x4*)(st.el + 8 * o8 + 4) = e1;
+#pragma unroll
+                for (int e = 0; e < 8; e++) tot[e] += bl[e];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) load_row(fill, 3);
+            __builtin_amdgcn_sched_barrier(0);
+            // the prepared rows; past the chunk's end every tile row is zero
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int t = 4 * tg + r;
+                const int off = sw(t, 8 * o8);
+                const bool in = t < n;
+                float fk[8], fq[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    fk[e] = in ? __builtin_amdgcn_exp2f(-b[r][e]) : 0.f;
+                    fq[e] = in ? __builtin_amdgcn_exp2f(b[r][e]) : 0.f;
+                }
+                *(u32x4*)(st.k + off) = scale8(x.k[r], fk);
+                *(u32x4*)(st.v + off) = in ? x.v[r] : u32x4{0, 0, 0, 0};
+                if (!STATE_ONLY) *(u32x4*)(st.q + off) = scale8(x.q[r], fq);
+            }
+        };
+        load(rA);
+        prep(rA, 0, nch > 1, rB);  // chunk 1 loads meanwhile
+        // chunk j's raw data lives in rA for even j, rB for odd j
+        auto step = [&](int c, Raw& fill, const Raw& pre) {
+            lds_barrier();  // chunk c (prepared) is handed to the compute waves; stage (c - 1) % NST is free
+            if (c + 1 < nch) prep(pre, c + 1, issued < nch, fill);  // chunk c + 2 loads meanwhile
+        };
+        for (int c = 0; c < nch; c += 2) {
+            step(c, rA, rB);
+            if (c + 1 < nch) step(c + 1, rB, rA);
+        }
+        if (STATE_ONLY && tg == 0) {
+            float* pd = part_decay + (ub * (G - 1) + g) * D + 8 * o8;
+#pragma unroll
+            for (int e = 0; e < 8; e++) pd[e] = __builtin_amdgcn_exp2f(tot[e]);
+        }
+        return;
+    }
     if (wave >= 4) {
         // ---- loader wave: chunk c + 2 is requested as soon as every wave is done with chunk c - 1
         const int lw = wave - 4;
@@ -147,8 +308,8 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                           lane);
                 issued++;
             }
-            if (!STATE_ONLY) {
-                lds_barrier();  // the compute waves have written chunk c's outputs
+            if (OTILE) {
+                lds_barrier_keep_dma();  // the compute waves have written chunk c's outputs
                 const int n = chunk_len(c);
                 const int64_t r0 = row_base + t_begin + (int64_t)c * C;
 #pragma unroll
@@ -301,20 +462,26 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                 // accumulators 0..7 are value columns 32w + 8kg + 0..7 (slot 4w + kg), 8..15 are
                 // 32w + 16 + 8kg + 0..7 (slot 4w + 2 + kg)
                 {
-                    __bf16* orow = otile + itok * D;
                     bf16x8 x0, x1;
 #pragma unroll
                     for (int e = 0; e < 8; e++) {
                         x0[e] = (__bf16)acc[e];
                         x1[e] = (__bf16)acc[8 + e];
                     }
-                    *(bf16x8*)(orow + (((4 * w + kg) ^ (itok & 15)) << 3)) = x0;
-                    *(bf16x8*)(orow + (((4 * w + 2 + kg) ^ (itok & 15)) << 3)) = x1;
+                    if (OTILE) {
+                        __bf16* orow = otile + itok * D;
+                        *(bf16x8*)(orow + (((4 * w + kg) ^ (itok & 15)) << 3)) = x0;
+                        *(bf16x8*)(orow + (((4 * w + 2 + kg) ^ (itok & 15)) << 3)) = x1;
+                    } else if (itok < n) {  // gate mode: no room for the tile beside the prepared stages
+                        __bf16* orow = o + (row_base + t_begin + (int64_t)c * C + itok) * D + 32 * w + 8 * kg;
+                        *(bf16x8*)orow = x0;
+                        *(bf16x8*)(orow + 16) = x1;
+                    }
                 }
             }
         }
 
-        if (!STATE_ONLY) lds_barrier();  // the output tile is complete; the loader waves store it
+        if (OTILE) lds_barrier();  // the output tile is complete; the loader waves store it
 
         // state: S <- decay(chunk) S + K^T diag(w) V over the chunk's n tokens
         if (MODE == DECAY_HEAD) {
@@ -350,6 +517,19 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                 const bf16x8 a = cat(lds_tr16(cur.k + 16 * ks * D + ktoff[m][0]), lds_tr16(cur.k + 16 * ks * D + ktoff[m][1]));
                 S[m] = mfma(a, vb[ks], S[m]);
             }
+        if (GATE) {
+            // S <- diag(exp(B_end)) (S + Kbar^T V), Kbar = K exp(-B): the same as decaying S and adding
+            // (K exp(B_end - B))^T V.  Rows 4 at a time: element 4 g4 + e of tile m is key row
+            // 32m + sigma(8 g4 + 4 kg) + e.
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; g4++) {
+                    const f32x4 f = *(const f32x4*)(cur.el + 32 * m + sigma(8 * g4 + 4 * kg));
+#pragma unroll
+                    for (int e = 0; e < 4; e++) S[m][4 * g4 + e] *= f[e];
+                }
+        }
     }
 
     float* dst = nullptr;
@@ -361,7 +541,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 #pragma unroll
             for (int i = 0; i < 16; i++) dst[(32 * m + sigma(acc_row(i, kg))) * D + vcol_lane] = S[m][i];
     }
-    if (STATE_ONLY && threadIdx.x < D)
+    if (STATE_ONLY && !GATE && threadIdx.x < D)
         part_decay[(ub * (G - 1) + g) * D + threadIdx.x] =
             (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
 }
@@ -377,7 +557,7 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
         LA_TRACED(a.tr, "chunk_fwd_pipe_state_pass",
                   pipe_fwd_kernel<MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
                       q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
-                      a.L, a.nseg, G, cps));
+                      a.L, a.nseg, G, cps, a.inv_norm));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream, a.tr);
@@ -386,15 +566,18 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
     LA_TRACED(a.tr, "chunk_fwd_pipe_output_pass",
               pipe_fwd_kernel<MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
                   q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, nullptr, part_state, a.H, a.L,
-                  a.nseg, G, cps));
+                  a.nseg, G, cps, a.inv_norm));
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
-    return a.mode == DECAY_HEAD ? launch_mode<DECAY_HEAD>(a, G, cps, part_state, part_decay)
-                                : launch_mode<DECAY_NONE>(a, G, cps, part_state, part_decay);
+    switch (a.mode) {
+        case DECAY_HEAD: return launch_mode<DECAY_HEAD>(a, G, cps, part_state, part_decay);
+        case DECAY_GATE: return launch_mode<DECAY_GATE>(a, G, cps, part_state, part_decay);
+        default: return launch_mode<DECAY_NONE>(a, G, cps, part_state, part_decay);
+    }
 }
 
 }  // namespace la

@@ -25,6 +25,18 @@ __device__ __forceinline__ __bf16 f2bf(float x) { return (__bf16)x; }
 __device__ __forceinline__ float bits_lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bits_hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// 8 bf16 (one 16-byte word) scaled by 8 fp32 factors, rounded to nearest even.
+__device__ __forceinline__ u32x4 scale8(u32x4 w, const float* f) {
+    u32x4 r;
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        const __bf16 lo = (__bf16)(bits_lo_bf16(w[h]) * f[2 * h]);
+        const __bf16 hi = (__bf16)(bits_hi_bf16(w[h]) * f[2 * h + 1]);
+        r[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return r;
+}
+
 template <typename T> struct io;
 template <> struct io<float> {
     __device__ static __forceinline__ float ld(const float* p) { return *p; }
@@ -82,6 +94,16 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The same barrier for a wave that has LDS DMA (global loads into LDS) in flight: an LDS fence
+// would wait for those too, because they write LDS.  This waits only for the wave's own LDS
+// instructions; the empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier_keep_dma() {
+    asm volatile("" ::: "memory");
+    waitcnt<63, 0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 }  // namespace la

@@ -76,10 +76,11 @@ struct CorrectArgs {
 // {16,32,64,128}, chunk in {16,32,64}.
 hipError_t launch_chunk_fwd_generic(const FwdArgs& a);
 
-// bf16 MFMA chunked forward for dk = dv = 128, chunk = 64, with intra-GPU sub-segment splitting.
+// bf16 MFMA chunked forward for dk = dv = 128, chunk = 64, with intra-GPU sub-segment splitting
+// (chunk_fwd_split.hip), all decay modes.
 hipError_t launch_chunk_fwd_mfma(const FwdArgs& a);
-// Its none / per-head decay variant with DMA-streamed chunk tiles; G sub-segments of cps chunks,
-// part_state / part_decay the workspace of the sub-segment scan (unused when G == 1).
+// Its kernels: G sub-segments of cps chunks; part_state / part_decay the workspace of the
+// sub-segment scan (unused when G == 1).
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
 
 // out[n,p] = diag(lam[n,p]) out[n,p-1] + x[n,p] for n < nstates, p < P.  x may equal out.
