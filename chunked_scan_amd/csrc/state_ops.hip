@@ -10,11 +10,10 @@ namespace {
 // ---------------------------------------------------------------------------------------------
 // Segmented state scan.  Thread = one state element of one (b,h); it walks the P segments in
 // order:  y = lam[p] * y + x[p];  out[p] = y.  The state chain is serial but its loads are not:
-// a batch of SCAN_BATCH segments is loaded before any of them is combined, so each thread keeps
-// that many HBM reads in flight.  out may alias x: every element is read before the same thread
-// overwrites it.
-constexpr int SCAN_BATCH = 16;
-
+// a batch of BATCH segments is loaded before any of them is combined, so each thread keeps that
+// many HBM reads in flight (up to 64 segments cost one memory round trip).  out may alias x:
+// every element is read before the same thread overwrites it.
+template <int BATCH>
 __global__ __launch_bounds__(256) void state_scan_kernel(const float* x, const float* __restrict__ lam,
                                                          float* out, int P, int dk, int dv, int64_t per_state,
                                                          int vblocks) {
@@ -26,24 +25,73 @@ __global__ __launch_bounds__(256) void state_scan_kernel(const float* x, const f
     float* ys = out + n * (int64_t)P * per_state + e;
     const float* ls = lam ? lam + n * (int64_t)P * dk + d : nullptr;  // null: no decay
     float y = 0.f;
-    for (int p0 = 0; p0 < P; p0 += SCAN_BATCH) {
-        float xb[SCAN_BATCH], lb[SCAN_BATCH];
-        const int nb = min(SCAN_BATCH, P - p0);
+    for (int p0 = 0; p0 < P; p0 += BATCH) {
+        float xb[BATCH], lb[BATCH];
+        const int nb = min(BATCH, P - p0);
 #pragma unroll
-        for (int j = 0; j < SCAN_BATCH; j++) {
+        for (int j = 0; j < BATCH; j++) {
             if (j < nb) {
                 xb[j] = xs[(int64_t)(p0 + j) * per_state];
                 lb[j] = ls ? ls[(int64_t)(p0 + j) * dk] : 1.f;
             }
         }
 #pragma unroll
-        for (int j = 0; j < SCAN_BATCH; j++) {
+        for (int j = 0; j < BATCH; j++) {
             if (j < nb) {
                 y = (p0 + j == 0) ? xb[j] : lb[j] * y + xb[j];  // out[-1] = 0: segment 0's decay is never applied
                 ys[(int64_t)(p0 + j) * per_state] = y;
             }
         }
     }
+}
+
+// Long scans (16 < P <= 64): four threads share an element's chain, each owning 16 consecutive
+// segments.  Each computes its part as an affine map of the incoming value (local inclusive scan
+// from zero, and the product of its decays), the four maps are composed in order through LDS, and
+// each thread applies its carry to its outputs: one memory round trip per thread, every element
+// read and written once.  Threads of a workgroup: 64 consecutive elements x 4 parts.
+__global__ __launch_bounds__(256) void state_scan4_kernel(const float* x, const float* __restrict__ lam, float* out,
+                                                          int P, int dk, int dv, int64_t per_state, int vblocks) {
+    constexpr int PER = 16;
+    __shared__ float loc_last[4][64], dec_last[4][64];
+    const int el = threadIdx.x & 63, part = threadIdx.x >> 6;
+    const int64_t n = blockIdx.x / vblocks;
+    const int64_t e = (int64_t)(blockIdx.x % vblocks) * 64 + el;
+    const bool active = e < per_state;
+    const int64_t ec = active ? e : per_state - 1;  // inactive lanes read a valid element, write nothing
+    const int d = (int)(ec / dv);
+    const float* xs = x + n * (int64_t)P * per_state + ec;
+    float* ys = out + n * (int64_t)P * per_state + ec;
+    const float* ls = lam ? lam + n * (int64_t)P * dk + d : nullptr;  // null: no decay
+    const int p0 = part * PER, nb = max(0, min(PER, P - p0));
+    float xb[PER], lb[PER];
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+        const int pp = min(p0 + j, P - 1);
+        xb[j] = xs[(int64_t)pp * per_state];
+        lb[j] = (ls && pp > 0) ? ls[(int64_t)pp * dk] : 1.f;  // segment 0's decay only meets out[-1] = 0
+    }
+    // local inclusive scan from zero and the running product of the decays
+    float loc[PER], dec[PER];
+    float y = 0.f, dd = 1.f;
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+        if (j < nb) {
+            y = lb[j] * y + xb[j];
+            dd *= lb[j];
+        }
+        loc[j] = y;
+        dec[j] = dd;
+    }
+    loc_last[part][el] = y;
+    dec_last[part][el] = dd;
+    __syncthreads();
+    float c = 0.f;  // out[p0 - 1]
+    for (int q = 0; q < part; q++) c = dec_last[q][el] * c + loc_last[q][el];
+    if (!active) return;
+#pragma unroll
+    for (int j = 0; j < PER; j++)
+        if (j < nb) ys[(int64_t)(p0 + j) * per_state] = loc[j] + dec[j] * c;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -279,9 +327,17 @@ hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64
     if (nstates == 0 || P == 0) return hipSuccess;
     const int64_t per_state = (int64_t)dk * dv;
     const int vblocks = (int)((per_state + 255) / 256);
-    LA_TRACED(tr, "state_scan",
-              state_scan_kernel<<<(unsigned)(nstates * vblocks), 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state,
-                                                                                 vblocks));
+    const unsigned grid = (unsigned)(nstates * vblocks);
+    if (P <= 4)
+        LA_TRACED(tr, "state_scan", state_scan_kernel<4><<<grid, 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state, vblocks));
+    else if (P <= 16)
+        LA_TRACED(tr, "state_scan", state_scan_kernel<16><<<grid, 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state, vblocks));
+    else if (P <= 64) {
+        const int vb64 = (int)((per_state + 63) / 64);
+        LA_TRACED(tr, "state_scan", state_scan4_kernel<<<(unsigned)(nstates * vb64), 256, 0, stream>>>(
+                                        x, lam, out, P, dk, dv, per_state, vb64));
+    } else
+        LA_TRACED(tr, "state_scan", state_scan_kernel<16><<<grid, 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state, vblocks));
     return hipGetLastError();
 }
 

@@ -133,10 +133,14 @@ def test_device_step_combine(mode):
     assert rel_err(s, s_ref[:, :, 0]) <= TOL["bf16"]
 
 
-def test_state_scan_matches_oracle():
-    note("la_state_scan random P=13")
+# P spans every launch shape: short (<= 4), medium (<= 16), split into four parts (<= 64), long
+# (dk x dv = 480 leaves a partial block of elements)
+@pytest.mark.parametrize("P,dk,dv", [(1, 64, 32), (4, 64, 32), (13, 64, 32), (16, 64, 32), (17, 20, 24), (40, 64, 32),
+                                     (64, 20, 24), (100, 64, 32)])
+def test_state_scan_matches_oracle(P, dk, dv):
+    note(f"la_state_scan random P={P} dk={dk} dv={dv}")
     g = torch.Generator().manual_seed(5)
-    B, H, P, dk, dv = 2, 3, 13, 64, 32
+    B, H = 2, 3
     x = torch.randn((B, H, P, dk, dv), generator=g)
     lam = torch.rand((B, H, P, dk), generator=g)
     ref = oracle.state_scan(x.double().numpy(), lam.double().numpy())
