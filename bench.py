@@ -154,13 +154,17 @@ def main():
     from chunked_scan_amd.pipeline import DeviceStep, SegmentedForward
 
     w = WORKLOADS[args.workload]
-    if w.nseg != 1:
-        raise SystemExit("bench.py times the single-segment device step; pick a one-segment workload")
     torch.cuda.set_device(0)
     log(f"[bench] workload {args.workload} {w.name}: generating inputs on cuda:0")
     inp = make_inputs(w, "cuda")
-    step = DeviceStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk,
-                      gate_norm=w.gate_norm)
+    if w.nseg == 1:
+        step = DeviceStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk,
+                          gate_norm=w.gate_norm)
+    else:  # a sequence split into segments, all on this device: the All-Scan as a segmented scan
+        if not args.no_cpu_baseline:
+            raise SystemExit("the CPU baseline is timed on the one-segment device step only")
+        step = SegmentedForward(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode,
+                                nseg=w.nseg, chunk=w.chunk, gate_norm=w.gate_norm)
     stream = torch.cuda.current_stream()
     # writing this buffer evicts the 256 MB last-level cache before a "cold" step
     scratch = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
@@ -274,8 +278,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: device step = local chunked fwd + All-Scan state combine + "
-                               f"output correction", "B": w.B, "H": w.H, "L": w.L, "dk": w.dk, "dv": w.dv,
+        "config": {"workload": (f"{w.name}: device step = local chunked fwd + All-Scan state combine + "
+                                f"output correction") if w.nseg == 1 else
+                               (f"{w.name}: {w.nseg} segments on one device = local chunked fwd + segmented "
+                                f"state scan + output correction"), "B": w.B, "H": w.H, "L": w.L, "dk": w.dk, "dv": w.dv,
                    "chunk": w.chunk, "decay": w.decay, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
