@@ -24,8 +24,8 @@ LA_F32, LA_BF16 = 0, 1
 MODES = {"none": 0, "head": 1, "gate": 2}
 STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_SHAPE", -3: "LA_ERR_DTYPE", -4: "LA_ERR_ALIAS",
           -5: "LA_ERR_UNSUPPORTED", -6: "LA_ERR_LAUNCH", -7: "LA_ERR_DECAY"}
-EXPORTS = ("la_chunk_fwd", "la_state_scan", "la_state_correct", "la_cumdecay", "la_status_str",
-           "la_supported", "la_version")
+EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_decayed", "la_state_scan", "la_state_correct", "la_cumdecay",
+           "la_status_str", "la_supported", "la_version")
 
 
 TRACE_MAX = 8
@@ -89,14 +89,15 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, S = ctypes.c_void_p, ctypes.POINTER(Shape)
         L.la_chunk_fwd.argtypes = [P, P, P, P, P, P, P, S, ctypes.c_int32]
+        L.la_chunk_fwd_decayed.argtypes = [P, P, P, P, P, P, P, P, P, S, ctypes.c_int32]
         L.la_state_scan.argtypes = [P, P, ctypes.c_int32, P, S]
         L.la_state_correct.argtypes = [P, P, P, P, S]
         L.la_cumdecay.argtypes = [P, P, P, S]
         L.la_supported.argtypes = [S, ctypes.c_int32]
         L.la_status_str.argtypes = [ctypes.c_int]
         L.la_status_str.restype = ctypes.c_char_p
-        for f in (L.la_chunk_fwd, L.la_state_scan, L.la_state_correct, L.la_cumdecay, L.la_supported,
-                  L.la_version):
+        for f in (L.la_chunk_fwd, L.la_chunk_fwd_decayed, L.la_state_scan, L.la_state_correct, L.la_cumdecay,
+                  L.la_supported, L.la_version):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -200,6 +201,53 @@ def la_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optio
     _check("la_chunk_fwd", lib().la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(o),
                                               _ptr(s_out), ctypes.byref(shp), chunk))
     return o, s_out
+
+
+def la_chunk_fwd_decayed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch.Tensor] = None,
+                         s_in: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                         s_out: Optional[torch.Tensor] = None, q_decayed: Optional[torch.Tensor] = None,
+                         total: Optional[torch.Tensor] = None, *, mode: Optional[str] = None, nseg: int = 1,
+                         chunk: int = 64, gate_norm: float = 16.0, subseg_chunks: int = 0, want_state: bool = True,
+                         want_q_decayed: bool = True, want_total: bool = True, stream=None, timer=None):
+    """la_chunk_fwd plus q_decayed [B,H,L,dk] (q times its cumulative decay from the segment start,
+    q's dtype) and total [B,H,nseg,dk] f32 (each segment's total decay; may be a view with evenly
+    spaced dense (b,h) blocks).  Returns (o, s_out, q_decayed, total); unrequested ones are None."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    _dev(q, "q")
+    _dev(k, "k", q.dtype, (B, H, L, dk))
+    _dev(v, "v", q.dtype, (B, H, L, dv))
+    m = mode_code(mode, decay)
+    if decay is not None:
+        _dev(decay, "decay", torch.float32)
+    if s_in is not None:
+        _dev(s_in, "s_in", torch.float32, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    _dev(o, "o", q.dtype, (B, H, L, dv))
+    if s_out is None and want_state:
+        s_out = torch.empty((B, H, nseg, dk, dv), dtype=torch.float32, device=q.device)
+    stride = 0
+    if s_out is not None:
+        _dev(s_out, "s_out", torch.float32, (B, H, nseg, dk, dv), contiguous=False)
+        stride = _bh_stride(s_out, "s_out", dk * dv)
+    if q_decayed is None and want_q_decayed:
+        q_decayed = torch.empty_like(q)
+    if q_decayed is not None:
+        _dev(q_decayed, "q_decayed", q.dtype, (B, H, L, dk))
+    if total is None and want_total:
+        total = torch.empty((B, H, nseg, dk), dtype=torch.float32, device=q.device)
+    tstride = 0
+    if total is not None:
+        _dev(total, "total", torch.float32, (B, H, nseg, dk), contiguous=False)
+        tstride = _bh_stride(total, "total", dk)
+    shp = make_shape(B, H, L, dk, dv, nseg=nseg, dtype=_dtype_code(q), mode=m, gate_norm=gate_norm,
+                     state_stride=stride, total_stride=tstride, subseg_chunks=subseg_chunks, stream=_stream(stream),
+                     timer=timer)
+    _check("la_chunk_fwd_decayed", lib().la_chunk_fwd_decayed(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in),
+                                                              _ptr(o), _ptr(s_out), _ptr(q_decayed), _ptr(total),
+                                                              ctypes.byref(shp), chunk))
+    return o, s_out, q_decayed, total
 
 
 def la_state_scan(seg_states: torch.Tensor, seg_decay: Optional[torch.Tensor],

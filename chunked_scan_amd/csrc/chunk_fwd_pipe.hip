@@ -123,7 +123,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     const float* __restrict__ decay, const float* __restrict__ s_in, __bf16* __restrict__ o,
     float* __restrict__ s_out, int64_t s_out_stride, float* __restrict__ part_state,
     float* __restrict__ part_decay, const float* __restrict__ init_state, int64_t H, int64_t L, int nseg, int G,
-    int cps, float inv_norm) {
+    int cps, float inv_norm, __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride) {
     constexpr bool GATE = MODE == DECAY_GATE;
     constexpr bool OTILE = !STATE_ONLY && !GATE;  // outputs leave through an LDS tile stored by the loaders
     constexpr int SLOT = STATE_ONLY ? 2 : 3;      // tiles per stage
@@ -171,7 +171,16 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
             f32x4 g[8];
         };
         Raw rA, rB;
-        float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // state pass: sum of the chunk totals
+        // log2 of the decay from the segment's first token (state pass: the sub-segment's first
+        // token) to the end of the last prepared chunk, per key dim of the lane; the output pass
+        // starts it from the totals of the sub-segments before this one
+        float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (!STATE_ONLY && (q_dec || total))
+            for (int gg = 0; gg < g; gg++) {
+                const float* pd = part_decay + (ub * (G - 1) + gg) * D + 8 * o8;
+#pragma unroll
+                for (int e = 0; e < 8; e++) run[e] += __builtin_amdgcn_logf(pd[e]);
+            }
         int issued = 0;
         // token row r of chunk `issued` into x (5 loads); the chunk counts as issued after row 3
         auto load_row = [&](Raw& x, int r) {
@@ -250,8 +259,13 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                 }
                 *(f32x4*)(st.el + 8 * o8) = e0;
                 *(f32x4*)(st.el + 8 * o8 + 4) = e1;
+            }
+            // decay from the segment start to this chunk's start (for q times the cumulative decay)
+            float cf[8];
 #pragma unroll
-                for (int e = 0; e < 8; e++) tot[e] += bl[e];
+            for (int e = 0; e < 8; e++) {
+                cf[e] = (!STATE_ONLY && q_dec) ? __builtin_amdgcn_exp2f(run[e]) : 0.f;
+                run[e] += bl[e];
             }
             __builtin_amdgcn_sched_barrier(0);
             if (more) load_row(fill, 3);
@@ -271,6 +285,13 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                 *(u32x4*)(st.k + off) = scale8(x.k[r], fk);
                 *(u32x4*)(st.v + off) = in ? x.v[r] : u32x4{0, 0, 0, 0};
                 if (!STATE_ONLY) *(u32x4*)(st.q + off) = scale8(x.q[r], fq);
+                if (!STATE_ONLY && q_dec && in) {
+                    // q times its cumulative decay from the segment start, rounded once
+                    float fd[8];
+#pragma unroll
+                    for (int e = 0; e < 8; e++) fd[e] = fq[e] * cf[e];
+                    *(u32x4*)(q_dec + (row_base + t_begin + (int64_t)cc * C + t) * D + 8 * o8) = scale8(x.q[r], fd);
+                }
             }
         };
         load(rA);
@@ -287,7 +308,12 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
         if (STATE_ONLY && tg == 0) {
             float* pd = part_decay + (ub * (G - 1) + g) * D + 8 * o8;
 #pragma unroll
-            for (int e = 0; e < 8; e++) pd[e] = __builtin_amdgcn_exp2f(tot[e]);
+            for (int e = 0; e < 8; e++) pd[e] = __builtin_amdgcn_exp2f(run[e]);
+        }
+        if (!STATE_ONLY && total && g == G - 1 && tg == 0) {  // the segment's total decay
+            float* tt = total + bh * total_stride + (int64_t)seg * D + 8 * o8;
+#pragma unroll
+            for (int e = 0; e < 8; e++) tt[e] = __builtin_amdgcn_exp2f(run[e]);
         }
         return;
     }
@@ -549,6 +575,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 template <int MODE>
 hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
     const int64_t ub = a.B * a.H * a.nseg;
+    const bool fused = MODE == DECAY_GATE;  // q times cumulative decay and the segment totals come from the loaders
     const __bf16* q = (const __bf16*)a.q;
     const __bf16* k = (const __bf16*)a.k;
     const __bf16* v = (const __bf16*)a.v;
@@ -557,7 +584,7 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
         LA_TRACED(a.tr, "chunk_fwd_pipe_state_pass",
                   pipe_fwd_kernel<MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
                       q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
-                      a.L, a.nseg, G, cps, a.inv_norm));
+                      a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream, a.tr);
@@ -565,8 +592,9 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
     }
     LA_TRACED(a.tr, "chunk_fwd_pipe_output_pass",
               pipe_fwd_kernel<MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
-                  q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, nullptr, part_state, a.H, a.L,
-                  a.nseg, G, cps, a.inv_norm));
+                  q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, part_decay, part_state, a.H, a.L,
+                  a.nseg, G, cps, a.inv_norm, fused ? (__bf16*)a.q_dec : nullptr, fused ? a.total : nullptr,
+                  a.total_stride));
     return hipGetLastError();
 }
 

@@ -75,7 +75,8 @@ size_t decay_bytes(const la_shape* s) {
 }
 
 la_status validate_fwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
-                       const void* o, const float* s_out, const la_shape* s, int chunk) {
+                       const void* o, const float* s_out, const la_shape* s, int chunk,
+                       const void* q_dec = nullptr, const float* total = nullptr) {
     la_status st = check_common(s);
     if (st != LA_OK) return st;
     if (chunk <= 0 || s->subseg_chunks < 0 || s->state_stride < 0) return LA_ERR_SHAPE;
@@ -100,6 +101,15 @@ la_status validate_fwd(const void* q, const void* k, const void* v, const float*
     for (Span in : {sq, sk, sv, sd, si})
         if (overlap(so, in) || overlap(sso, in)) return LA_ERR_ALIAS;
     if (overlap(so, sso)) return LA_ERR_ALIAS;
+    // the optional outputs of la_chunk_fwd_decayed
+    if (total && (s->total_stride < 0 || (s->total_stride && s->total_stride < (int64_t)s->nseg * s->dk)))
+        return LA_ERR_SHAPE;
+    const int64_t tstride = s->total_stride ? s->total_stride : (int64_t)s->nseg * s->dk;
+    Span sqd{q_dec, q_dec ? es * nqk : 0};
+    Span stt{total, (total && BH > 0) ? sizeof(float) * (size_t)((BH - 1) * tstride + s->nseg * s->dk) : 0};
+    for (Span x : {sq, sk, sv, sd, si, so, sso})
+        if (overlap(sqd, x) || overlap(stt, x)) return LA_ERR_ALIAS;
+    if (overlap(sqd, stt)) return LA_ERR_ALIAS;
     return LA_OK;
 }
 
@@ -149,20 +159,20 @@ int32_t la_supported(const la_shape* s, int32_t chunk) {
     return 1;
 }
 
-la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in, void* o,
-                       float* s_out, const la_shape* s, int32_t chunk) {
-    la_status st = validate_fwd(q, k, v, decay, s_in, o, s_out, s, chunk);
+}  // extern "C"
+
+namespace {
+
+// The forward of la_chunk_fwd, plus the optional outputs of la_chunk_fwd_decayed (q_dec, total).
+la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* decay, const float* s_in, void* o,
+                         float* s_out, void* q_dec, float* total, const la_shape* s, int32_t chunk) {
+    la_status st = validate_fwd(q, k, v, decay, s_in, o, s_out, s, chunk, q_dec, total);
     if (st != LA_OK) return st;
     if ((st = check_trace(s)) != LA_OK) return st;
     la::Tracer tr = make_tracer(s);
     hipStream_t stream = (hipStream_t)s->stream;
     const int64_t so_stride = s->state_stride ? s->state_stride : (int64_t)s->nseg * s->dk * s->dv;
     if (s->B * s->H == 0) return LA_OK;
-    if (s->L == 0) {
-        if (!s_out) return LA_OK;
-        return from_hip(
-            la::launch_empty_states(s_in, s_out, so_stride, s->B * s->H, s->nseg, s->dk, s->dv, stream, &tr));
-    }
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.decay = decay; a.s_in = s_in; a.o = o; a.s_out = s_out;
     a.s_out_stride = so_stride;
@@ -174,8 +184,35 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float*
     a.subseg_chunks = s->subseg_chunks;
     a.stream = stream;
     a.tr = &tr;
-    if (a.bf16 && a.dk == 128 && a.dv == 128 && chunk == 64) return from_hip(la::launch_chunk_fwd_mfma(a));
-    return from_hip(la::launch_chunk_fwd_generic(a));
+    a.q_dec = q_dec;
+    a.total = total;
+    a.total_stride = s->total_stride ? s->total_stride : (int64_t)s->nseg * s->dk;
+    hipError_t e = hipSuccess;
+    bool fused = false;  // the forward itself wrote q_dec and total
+    if (s->L == 0) {
+        if (s_out) e = la::launch_empty_states(s_in, s_out, so_stride, s->B * s->H, s->nseg, s->dk, s->dv, stream, &tr);
+    } else if (a.bf16 && a.dk == 128 && a.dv == 128 && chunk == 64) {
+        e = la::launch_chunk_fwd_mfma(a);
+        fused = a.mode == LA_DECAY_GATE;
+    } else {
+        e = la::launch_chunk_fwd_generic(a);
+    }
+    if (e == hipSuccess && !fused && (q_dec || total)) e = la::launch_decayed_q(a);
+    return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in, void* o,
+                       float* s_out, const la_shape* s, int32_t chunk) {
+    return chunk_fwd_impl(q, k, v, decay, s_in, o, s_out, nullptr, nullptr, s, chunk);
+}
+
+la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
+                               void* o, float* s_out, void* q_decayed, float* total, const la_shape* s, int32_t chunk) {
+    return chunk_fwd_impl(q, k, v, decay, s_in, o, s_out, q_decayed, total, s, chunk);
 }
 
 la_status la_state_scan(const float* seg_states, const float* seg_decay, int32_t P, float* out_states,

@@ -56,6 +56,9 @@ struct FwdArgs {
     int subseg_chunks;   // 0 = automatic
     hipStream_t stream;
     Tracer* tr;
+    void* q_dec = nullptr;     // optional: q times its cumulative decay from the segment start
+    float* total = nullptr;    // optional: each segment's total decay
+    int64_t total_stride = 0;  // elements between (b,h) blocks of total
 };
 
 struct CorrectArgs {
@@ -94,6 +97,10 @@ hipError_t launch_state_correct_generic(const CorrectArgs& a);
 // total of segment p of (b,h) goes to total[bh * total_stride + p * dk].
 hipError_t launch_cumdecay(const float* decay, float* cum, float* total, int64_t total_stride, int64_t B, int64_t H,
                            int64_t L, int dk, int nseg, int mode, float inv_norm, hipStream_t stream, Tracer* tr);
+
+// a.q_dec = q times its cumulative decay from the segment start and a.total = each segment's
+// total decay (either may be null), for the shapes whose forward does not emit them itself.
+hipError_t launch_decayed_q(const FwdArgs& a);
 
 // s_out[b,h,p] = (p == 0 && s_in) ? s_in[b,h] : 0 -- the final states of empty segments.
 hipError_t launch_empty_states(const float* s_in, float* s_out, int64_t s_out_stride, int64_t BH, int nseg, int dk,

@@ -320,6 +320,45 @@ __global__ __launch_bounds__(256) void empty_states_kernel(const float* __restri
     s_out[bh * s_out_stride + (int64_t)p * SZ + e] = (p == 0 && s_in) ? s_in[bh * SZ + e] : 0.f;
 }
 
+// q times its cumulative decay from the segment start, and the segment totals, where the forward
+// does not emit them itself.  Thread = one key dim of one (b,h,segment), walking the segment's
+// tokens in order: gate mode keeps an fp32 running sum of log a and exponentiates it per token,
+// head mode uses the closed form exp(lambda_h * tau), no decay copies q.  Consecutive threads take
+// consecutive key dims, so each token row is one contiguous access.
+template <typename T>
+__global__ __launch_bounds__(256) void decayed_q_kernel(const T* __restrict__ q, const float* __restrict__ decay,
+                                                        T* __restrict__ q_dec, float* __restrict__ total,
+                                                        int64_t total_stride, int64_t H, int64_t L, int dk, int nseg,
+                                                        int64_t n, int mode, float inv_norm) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int d = (int)(i % dk);
+    const int64_t bhp = i / dk;
+    const int p = (int)(bhp % nseg);
+    const int64_t bh = bhp / nseg;
+    const int64_t Ls = L / nseg;
+    const int64_t r0 = bh * L + (int64_t)p * Ls;  // the segment's first token row
+    const float lam = mode == DECAY_HEAD ? decay[bh % H] : 0.f;
+    float run = 0.f;
+    if (q_dec)
+        for (int64_t t = 0; t < Ls; t++) {
+            const int64_t idx = (r0 + t) * dk + d;
+            float c = 1.f;
+            if (mode == DECAY_GATE) {
+                run += gate_logdecay(decay[idx], inv_norm);
+                c = expf(run);
+            } else if (mode == DECAY_HEAD) {
+                c = expf(lam * (float)(t + 1));
+            }
+            q_dec[idx] = (T)((float)q[idx] * c);
+        }
+    else if (mode == DECAY_GATE)
+        for (int64_t t = 0; t < Ls; t++) run += gate_logdecay(decay[(r0 + t) * dk + d], inv_norm);
+    if (total)
+        total[bh * total_stride + (int64_t)p * dk + d] =
+            mode == DECAY_GATE ? expf(run) : (mode == DECAY_HEAD && Ls > 0) ? expf(lam * (float)Ls) : 1.f;
+}
+
 }  // namespace
 
 hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64_t nstates, int P, int dk, int dv,
@@ -338,6 +377,23 @@ hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64
                                         x, lam, out, P, dk, dv, per_state, vb64));
     } else
         LA_TRACED(tr, "state_scan", state_scan_kernel<16><<<grid, 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state, vblocks));
+    return hipGetLastError();
+}
+
+hipError_t launch_decayed_q(const FwdArgs& a) {
+    const int64_t n = a.B * a.H * (int64_t)a.nseg * a.dk;
+    if (n == 0 || (!a.q_dec && !a.total)) return hipSuccess;
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    if (a.bf16)
+        LA_TRACED(a.tr, "decayed_q",
+                  decayed_q_kernel<__bf16><<<grid, 256, 0, a.stream>>>(
+                      (const __bf16*)a.q, a.decay, (__bf16*)a.q_dec, a.total, a.total_stride, a.H, a.L, a.dk, a.nseg,
+                      n, a.mode, a.inv_norm));
+    else
+        LA_TRACED(a.tr, "decayed_q",
+                  decayed_q_kernel<float><<<grid, 256, 0, a.stream>>>((const float*)a.q, a.decay, (float*)a.q_dec,
+                                                                      a.total, a.total_stride, a.H, a.L, a.dk,
+                                                                      a.nseg, n, a.mode, a.inv_norm));
     return hipGetLastError();
 }
 

@@ -11,6 +11,10 @@ correction.
                      S_out = Lambda_total S_recv + S_loc (a two-entry state scan), then
                      O += (Q * cumulative decay) S_recv.  Without decay there is no decay to
                      prepare (Lambda = 1, cumulative decay = 1): the scan runs as a plain sum.
+                     Head decay: Lambda_total from the closed form, the cumulative decay formed
+                     inside the correction.  Gate decay: the forward itself emits Q * cumulative
+                     decay and Lambda_total (la_chunk_fwd_decayed), and the correction adds
+                     (Q * cum) S_recv as a plain product.
 ``segmented_forward`` -- P devices emulated on one GPU: the local forward of all P segments in
                      one launch, the P-entry state scan, and the correction of segments 1..P-1.
 """
@@ -20,11 +24,32 @@ from typing import Optional
 
 import torch
 
-from .binding import la_chunk_fwd, la_cumdecay, la_state_correct, la_state_scan
+from .binding import la_chunk_fwd, la_chunk_fwd_decayed, la_cumdecay, la_state_correct, la_state_scan
 
 
-def _corr_decay(mode: str, decay, cum):
-    return None if mode == "none" else (decay if mode == "head" else cum)
+def _forward(step, s_in, s_out, totals, nseg, timers):
+    """The local forward and the decay quantities the scan and the correction need."""
+    B, H, L, dk, dv = step.shape
+    kw = dict(mode=step.mode, nseg=nseg, chunk=step.chunk, gate_norm=step.gate_norm,
+              subseg_chunks=step.subseg_chunks)
+    if step.mode == "gate":
+        la_chunk_fwd_decayed(step.q, step.k, step.v, step.decay, s_in, step.o, s_out, step.qd, totals,
+                             timer=timers.get("fwd"), **kw)
+        return
+    la_chunk_fwd(step.q, step.k, step.v, step.decay, s_in, step.o, s_out, timer=timers.get("fwd"), **kw)
+    if step.mode == "head":
+        la_cumdecay(step.decay, B, H, L, dk, mode="head", nseg=nseg, total=totals, want_cum=False,
+                    timer=timers.get("cum"))
+
+
+def _correct(step, s_recv, nseg, seg_begin, timers):
+    """O += (Q * cumulative decay) S_recv; in gate mode Q * cum is the forward's q_decayed."""
+    if step.mode == "gate":
+        la_state_correct(step.qd, None, s_recv, step.o, mode="none", nseg=nseg, seg_begin=seg_begin,
+                         timer=timers.get("corr"))
+    else:
+        la_state_correct(step.q, step.decay if step.mode == "head" else None, s_recv, step.o, mode=step.mode,
+                         nseg=nseg, seg_begin=seg_begin, timer=timers.get("corr"))
 
 
 class DeviceStep:
@@ -44,21 +69,14 @@ class DeviceStep:
         if s_recv is not None:
             self.states[:, :, 0].copy_(s_recv)
         self.totals = torch.ones((B, H, 2, dk), dtype=torch.float32, device=dev)
-        self.cum = torch.empty((B, H, L, dk), dtype=torch.float32, device=dev) if mode == "gate" else None
+        self.qd = torch.empty_like(q) if mode == "gate" else None  # q times its cumulative decay
 
     def run(self, timers: Optional[dict] = None):
         """One step.  ``timers`` optionally maps "fwd", "cum", "scan", "corr" to KernelTimers."""
-        B, H, L, dk, dv = self.shape
         t = timers or {}
-        la_chunk_fwd(self.q, self.k, self.v, self.decay, None, self.o, self.states[:, :, 1:2], mode=self.mode,
-                     chunk=self.chunk, gate_norm=self.gate_norm, subseg_chunks=self.subseg_chunks,
-                     timer=t.get("fwd"))
-        if self.mode != "none":
-            la_cumdecay(self.decay, B, H, L, dk, mode=self.mode, gate_norm=self.gate_norm, cum=self.cum,
-                        total=self.totals[:, :, 1:2], want_cum=self.mode == "gate", timer=t.get("cum"))
+        _forward(self, None, self.states[:, :, 1:2], self.totals[:, :, 1:2], 1, t)
         la_state_scan(self.states, self.totals if self.mode != "none" else None, self.states, timer=t.get("scan"))
-        la_state_correct(self.q, _corr_decay(self.mode, self.decay, self.cum), self.states[:, :, 0:1], self.o,
-                         mode=self.mode, timer=t.get("corr"))
+        _correct(self, self.states[:, :, 0:1], 1, 0, t)
         return self.o, self.states[:, :, 1]
 
 
@@ -84,23 +102,16 @@ class SegmentedForward:
         self.o = torch.empty((B, H, L, dv), dtype=q.dtype, device=dev)
         self.states = torch.empty((B, H, nseg, dk, dv), dtype=torch.float32, device=dev)
         self.totals = torch.empty((B, H, nseg, dk), dtype=torch.float32, device=dev)
-        self.cum = torch.empty((B, H, L, dk), dtype=torch.float32, device=dev) if mode == "gate" else None
+        self.qd = torch.empty_like(q) if mode == "gate" else None  # q times its cumulative decay
 
     def run(self, timers: Optional[dict] = None):
         """One pass.  ``timers`` optionally maps "fwd", "cum", "scan", "corr" to KernelTimers."""
-        B, H, L, dk, dv = self.shape
         P = self.nseg
         t = timers or {}
-        la_chunk_fwd(self.q, self.k, self.v, self.decay, self.s_in, self.o, self.states, mode=self.mode, nseg=P,
-                     chunk=self.chunk, gate_norm=self.gate_norm, subseg_chunks=self.subseg_chunks,
-                     timer=t.get("fwd"))
-        if self.mode != "none":
-            la_cumdecay(self.decay, B, H, L, dk, mode=self.mode, nseg=P, gate_norm=self.gate_norm, cum=self.cum,
-                        total=self.totals, want_cum=self.mode == "gate", timer=t.get("cum"))
+        _forward(self, self.s_in, self.states, self.totals, P, t)
         la_state_scan(self.states, self.totals if self.mode != "none" else None, self.states, timer=t.get("scan"))
         if P > 1:
-            la_state_correct(self.q, _corr_decay(self.mode, self.decay, self.cum), self.states[:, :, : P - 1], self.o,
-                             mode=self.mode, nseg=P, seg_begin=1, timer=t.get("corr"))
+            _correct(self, self.states[:, :, : P - 1], P, 1, t)
         return self.o, self.states
 
 

@@ -90,8 +90,8 @@ typedef struct la_shape {
                              array: s_out of la_chunk_fwd (0 = dense, nseg*dk*dv) and s_recv of
                              la_state_correct (0 = dense, (nseg - seg_begin)*dk*dv).  Lets the
                              local state land directly in a slot of a larger scan buffer. */
-    int64_t total_stride; /* la_cumdecay only: elements between consecutive (b,h) blocks of total;
-                             0 = dense, nseg*dk */
+    int64_t total_stride; /* la_cumdecay and la_chunk_fwd_decayed: elements between consecutive
+                             (b,h) blocks of total; 0 = dense, nseg*dk */
     int32_t subseg_chunks;/* la_chunk_fwd only: chunks per internal sub-segment when one segment is
                              split across compute units (the decomposition identity applied inside
                              the GPU); 0 = choose automatically, >= 1 forces that length.  Changes
@@ -132,6 +132,32 @@ typedef struct la_shape {
 la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float* decay,
                        const float* s_in, void* o, float* s_out, const la_shape* shape,
                        int32_t chunk);
+
+/*
+ * la_chunk_fwd plus the two decay quantities that the rest of a device's step needs, emitted by
+ * the same pass, so that no separate cumulative-decay pass is needed.  In the decomposition
+ * identity of the ZeCO review page (pith_extraction.key_machinery) the incoming state reaches
+ * the outputs through q_t scaled by the decay accumulated since the segment start, and reaches
+ * the outgoing state through the segment's total decay:
+ *   q_decayed[b,h,t,:] = q_t (*) cum_t, cum_t[d] = prod of a_s[d] from the first token of t's
+ *                        segment to t inclusive; [B,H,L,dk] in_dtype, rounded once from fp32;
+ *                        or NULL.  Then la_state_correct(q_decayed, NULL, ...) with decay_mode
+ *                        NONE adds exactly the correction la_state_correct(q, cumdecay, ...)
+ *                        adds in the shape's own mode.
+ *   total              = Lambda of every segment, as la_cumdecay writes it (segment p of (b,h)
+ *                        at total + (b*H + h) * total_stride + p * dk; dense [B,H,nseg,dk] when
+ *                        shape->total_stride = 0); or NULL.
+ * Every other argument, and every result la_chunk_fwd writes, is as for la_chunk_fwd.  In gate
+ * mode with bf16, dk = dv = 128 and chunk 64 both come out of the forward's own decay
+ * preparation (cum = exp2 of an fp32 running sum of log2 a); otherwise one extra streaming pass
+ * forms them (gate: exp of an fp32 running sum of log a; head: exp(lambda_h * tau); none: cum = 1,
+ * q_decayed = q).  Neither output may overlap any other argument.
+ * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_DECAY, LA_ERR_ALIAS,
+ * LA_ERR_UNSUPPORTED or LA_ERR_LAUNCH.
+ */
+la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, const float* decay,
+                               const float* s_in, void* o, float* s_out, void* q_decayed,
+                               float* total, const la_shape* shape, int32_t chunk);
 
 /*
  * Segmented state scan: the All-Scan of ZeCO reproduced on one GPU (page "ZeCO ...",

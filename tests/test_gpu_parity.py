@@ -255,6 +255,47 @@ def test_cumdecay_matches_oracle(mode):
     assert np.max(np.abs(t - tref) / np.maximum(np.abs(tref), 1e-30)) < 2e-4
 
 
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("path,L,nseg,subseg", [("bf16_d128", 64 * 9 + 17, 1, 3), ("bf16_d128", 6 * 200, 6, 0),
+                                                ("bf16_d128", 64 * 20, 2, 2), ("f32_d32", 3 * 150, 3, 0)])
+def test_chunk_fwd_decayed(mode, path, L, nseg, subseg):
+    """la_chunk_fwd_decayed: o and s_out exactly as la_chunk_fwd; q_decayed = q * cumdecay and total
+    = each segment's decay against the oracle.  In gate mode with bf16 d=128 the forward's loaders
+    emit them (several sub-segments, a ragged last chunk); elsewhere the separate pass does."""
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    bf = path.startswith("bf16")
+    dk = 128 if bf else 32
+    w = W2.scaled(B=2, H=3, L=L, dk=dk, dv=dk, dtype="bf16" if bf else "f32", decay=decay, s_in_std=0.05,
+                  seed=300 + L + nseg)
+    note(f"la_chunk_fwd_decayed {path} mode={mode} L={L} nseg={nseg} subseg_chunks={subseg}")
+    inp = make_inputs(w, "cpu")
+    d = to_dev(inp)
+    kw = dict(mode=w.mode, nseg=nseg, gate_norm=w.gate_norm, subseg_chunks=subseg)
+    o0, s0 = lb.la_chunk_fwd(d["q"], d["k"], d["v"], d["decay"], d["s_in"], **kw)
+    o, s, qd, tot = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"], **kw)
+    # each optional output alone
+    _, _, qd_only, none_tot = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"],
+                                                      want_total=False, **kw)
+    _, _, none_qd, tot_only = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"],
+                                                      want_q_decayed=False, **kw)
+    torch.cuda.synchronize()
+    assert none_tot is None and none_qd is None
+    assert torch.equal(o, o0) and torch.equal(s, s0)
+    assert torch.equal(qd_only, qd) and torch.equal(tot_only, tot)
+    cref, tref = oracle.cumdecay(w.B, w.H, w.L, w.dk, ORC_MODE[w.mode], host32(inp["decay"]), nseg=nseg,
+                                 gate_norm=w.gate_norm)
+    ref = host32(inp["q"]).astype(np.float64) * cref
+    got = qd.cpu().double().numpy()
+    if mode == "none":
+        assert torch.equal(qd, d["q"])
+    # one rounding to the storage dtype on top of the fp32 cumulative decay's own error; values
+    # that fall below the fp32 normal range may flush to zero
+    rnd = 2.0 ** -8 if bf else 2.0 ** -23
+    assert np.all(np.abs(got - ref) <= (rnd + 2e-4) * np.abs(ref) + 1e-35)
+    t = tot.cpu().double().numpy()
+    assert np.max(np.abs(t - tref) / np.maximum(np.abs(tref), 1e-30)) < 2e-4
+
+
 @pytest.mark.parametrize("path", ["f32_d16", "bf16_d128"])
 def test_integer_inputs_bit_exact(path):
     """a = 1, q, k, v in {-1, 0, 1}, integer s_in with |s_in| <= 8.  Every intermediate is an integer
