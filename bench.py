@@ -1,11 +1,14 @@
 """Throughput of one device's share of ZeCO causal linear attention on one MI355X.
 
 A step is one pass of the whole per-device path over one batch of synthetic input at the
-pages' per-device shape (B=1, H=16, L=16384, dk=dv=128, bf16, chunk 64, no decay, S_recv = 0):
-  la_chunk_fwd     local chunked forward from a zero state  -> O_local, S_loc
-  la_cumdecay      the segment's total decay Lambda (decay modes only; without decay Lambda = 1)
-  la_state_scan    All-Scan update S_out = Lambda S_recv + S_loc (two-entry scan)
-  la_state_correct O += (Q * cumulative decay) S_recv
+pages' per-device shape (B=1, H=16, L=16384, dk=dv=128, bf16, chunk 64, no decay, S_recv = 0),
+with the device's segment cut into G sub-segments (G = 16 here, one workgroup each per head):
+  la_chunk_fwd     local chunked forward of every sub-segment from a zero state -> O_local, S_loc
+  la_cumdecay      each sub-segment's total decay Lambda (head decay; gate decay takes it and
+                   Q * cumulative decay from la_chunk_fwd_decayed; without decay Lambda = 1)
+  la_state_scan    All-Scan over [S_recv, S_loc,1..G]: every sub-segment's incoming state, and
+                   S_out = Lambda S_recv + S_loc as its last entry
+  la_state_correct O += (Q * cumulative decay) S_in for every sub-segment
 Prints one JSON line.  Per-kernel durations come from HIP events that the library records
 around every kernel on the stream it launches them on (la_trace); the dominant kernel's
 roofline uses its algorithmic bytes (q, k, v read + o written) over its mean duration.
@@ -174,7 +177,17 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
-    # --- timed region 1: the step as a user runs it (no per-kernel events)
+    # --- every step bracketed by its own events, cold then warm
+    cold = step_stats(step, args.steps, stream, scratch)
+    warm = step_stats(step, args.steps, stream)
+    log(f"[bench] per step: warm median {warm['median_us']:.1f} us, cold median {cold['median_us']:.1f} us")
+
+    # --- the same steps with HIP events around every kernel (la_trace)
+    kernels, ms_traced = kernel_stats(step, args.steps, stream)
+    log("[bench] per kernel: " + ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in kernels.items()))
+
+    # --- the headline: K steps back to back as a user runs them (no per-kernel events), timed last
+    # so that the GPU has left its idle clocks behind
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -184,15 +197,6 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
-
-    # --- timed region 2: every step bracketed by its own events, warm and cold
-    warm = step_stats(step, args.steps, stream)
-    cold = step_stats(step, args.steps, stream, scratch)
-    log(f"[bench] per step: warm median {warm['median_us']:.1f} us, cold median {cold['median_us']:.1f} us")
-
-    # --- timed region 3: the same steps with HIP events around every kernel (la_trace)
-    kernels, ms_traced = kernel_stats(step, args.steps, stream)
-    log("[bench] per kernel: " + ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in kernels.items()))
 
     alongside = {}
     if not args.no_alongside:

@@ -10,9 +10,9 @@ namespace {
 // ---------------------------------------------------------------------------------------------
 // Segmented state scan.  Thread = one state element of one (b,h); it walks the P segments in
 // order:  y = lam[p] * y + x[p];  out[p] = y.  The state chain is serial but its loads are not:
-// a batch of BATCH segments is loaded before any of them is combined, so each thread keeps that
-// many HBM reads in flight (up to 64 segments cost one memory round trip).  out may alias x:
-// every element is read before the same thread overwrites it.
+// a batch of BATCH segments is loaded before any of them is combined (loads past P repeat the
+// last segment, so the batch is branch-free), and each thread keeps that many HBM reads in
+// flight.  out may alias x: every element is read before the same thread overwrites it.
 template <int BATCH>
 __global__ __launch_bounds__(256) void state_scan_kernel(const float* x, const float* __restrict__ lam,
                                                          float* out, int P, int dk, int dv, int64_t per_state,
@@ -30,10 +30,9 @@ __global__ __launch_bounds__(256) void state_scan_kernel(const float* x, const f
         const int nb = min(BATCH, P - p0);
 #pragma unroll
         for (int j = 0; j < BATCH; j++) {
-            if (j < nb) {
-                xb[j] = xs[(int64_t)(p0 + j) * per_state];
-                lb[j] = ls ? ls[(int64_t)(p0 + j) * dk] : 1.f;
-            }
+            const int pp = p0 + min(j, nb - 1);
+            xb[j] = xs[(int64_t)pp * per_state];
+            lb[j] = ls ? ls[(int64_t)pp * dk] : 1.f;
         }
 #pragma unroll
         for (int j = 0; j < BATCH; j++) {
@@ -45,14 +44,14 @@ __global__ __launch_bounds__(256) void state_scan_kernel(const float* x, const f
     }
 }
 
-// Long scans (16 < P <= 64): four threads share an element's chain, each owning 16 consecutive
+// Long scans (16 < P <= 4 PER): four threads share an element's chain, each owning PER consecutive
 // segments.  Each computes its part as an affine map of the incoming value (local inclusive scan
 // from zero, and the product of its decays), the four maps are composed in order through LDS, and
 // each thread applies its carry to its outputs: one memory round trip per thread, every element
 // read and written once.  Threads of a workgroup: 64 consecutive elements x 4 parts.
+template <int PER>
 __global__ __launch_bounds__(256) void state_scan4_kernel(const float* x, const float* __restrict__ lam, float* out,
                                                           int P, int dk, int dv, int64_t per_state, int vblocks) {
-    constexpr int PER = 16;
     __shared__ float loc_last[4][64], dec_last[4][64];
     const int el = threadIdx.x & 63, part = threadIdx.x >> 6;
     const int64_t n = blockIdx.x / vblocks;
@@ -65,9 +64,10 @@ __global__ __launch_bounds__(256) void state_scan4_kernel(const float* x, const 
     const float* ls = lam ? lam + n * (int64_t)P * dk + d : nullptr;  // null: no decay
     const int p0 = part * PER, nb = max(0, min(PER, P - p0));
     float xb[PER], lb[PER];
+    const int plast = max(0, min(p0 + PER, P) - 1);  // loads past the part's end repeat its last segment
 #pragma unroll
     for (int j = 0; j < PER; j++) {
-        const int pp = min(p0 + j, P - 1);
+        const int pp = min(p0 + j, plast);
         xb[j] = xs[(int64_t)pp * per_state];
         lb[j] = (ls && pp > 0) ? ls[(int64_t)pp * dk] : 1.f;  // segment 0's decay only meets out[-1] = 0
     }
@@ -369,11 +369,17 @@ hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64
     const unsigned grid = (unsigned)(nstates * vblocks);
     if (P <= 4)
         LA_TRACED(tr, "state_scan", state_scan_kernel<4><<<grid, 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state, vblocks));
+    else if (P <= 8)
+        LA_TRACED(tr, "state_scan", state_scan_kernel<8><<<grid, 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state, vblocks));
     else if (P <= 16)
         LA_TRACED(tr, "state_scan", state_scan_kernel<16><<<grid, 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state, vblocks));
-    else if (P <= 64) {
+    else if (P <= 32) {
         const int vb64 = (int)((per_state + 63) / 64);
-        LA_TRACED(tr, "state_scan", state_scan4_kernel<<<(unsigned)(nstates * vb64), 256, 0, stream>>>(
+        LA_TRACED(tr, "state_scan", state_scan4_kernel<8><<<(unsigned)(nstates * vb64), 256, 0, stream>>>(
+                                        x, lam, out, P, dk, dv, per_state, vb64));
+    } else if (P <= 64) {
+        const int vb64 = (int)((per_state + 63) / 64);
+        LA_TRACED(tr, "state_scan", state_scan4_kernel<16><<<(unsigned)(nstates * vb64), 256, 0, stream>>>(
                                         x, lam, out, P, dk, dv, per_state, vb64));
     } else
         LA_TRACED(tr, "state_scan", state_scan_kernel<16><<<grid, 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state, vblocks));

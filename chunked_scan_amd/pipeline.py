@@ -7,14 +7,19 @@ Attention" (pith_extraction.key_machinery): local work runs from a zero state, t
 state is folded into the state by the All-Scan update and into the outputs by a rank-dk
 correction.
 
-``device_step``   -- one device holding one segment: local forward, then the All-Scan update
-                     S_out = Lambda_total S_recv + S_loc (a two-entry state scan), then
-                     O += (Q * cumulative decay) S_recv.  Without decay there is no decay to
-                     prepare (Lambda = 1, cumulative decay = 1): the scan runs as a plain sum.
-                     Head decay: Lambda_total from the closed form, the cumulative decay formed
-                     inside the correction.  Gate decay: the forward itself emits Q * cumulative
-                     decay and Lambda_total (la_chunk_fwd_decayed), and the correction adds
-                     (Q * cum) S_recv as a plain product.
+``device_step``   -- one device holding one segment, given the state S_recv it receives.  The
+                     segment is cut into G sub-segments, each treated as one more device of the
+                     same identity: the local forward of every sub-segment from a zero state (one
+                     launch, no second pass over K and V), then one inclusive scan over
+                     [S_recv, S_loc,1, ..., S_loc,G] that yields every sub-segment's exact incoming
+                     state (its last entry is the All-Scan update S_out = Lambda S_recv + S_loc),
+                     then one correction pass O += (Q * cumulative decay) S_in over every
+                     sub-segment.  With G = 1 this is the plain form: local forward, two-entry scan,
+                     correction by S_recv.  Without decay there is no decay to prepare (Lambda = 1,
+                     cumulative decay = 1): the scan runs as a plain sum.  Head decay: Lambda from
+                     the closed form, the cumulative decay formed inside the correction.  Gate
+                     decay: the forward itself emits Q * cumulative decay and Lambda
+                     (la_chunk_fwd_decayed), and the correction adds a plain product.
 ``segmented_forward`` -- P devices emulated on one GPU: the local forward of all P segments in
                      one launch, the P-entry state scan, and the correction of segments 1..P-1.
 """
@@ -52,39 +57,57 @@ def _correct(step, s_recv, nseg, seg_begin, timers):
                          nseg=nseg, seg_begin=seg_begin, timer=timers.get("corr"))
 
 
+def subsegments(B: int, H: int, L: int, target_units: int = 256, min_len: int = 256) -> int:
+    """Sub-segments per sequence for a device step: about ``target_units`` (b,h,sub-segment) units
+    in all (one round of workgroups on the compute units), each at least ``min_len`` tokens; G must
+    divide L, and lengths that are whole 64-token chunks are preferred."""
+    want = max(1, -(-target_units // max(1, B * H)))
+    cands = [g for g in range(1, want + 1) if L % g == 0 and (g == 1 or L // g >= min_len)]
+    whole = [g for g in cands if (L // g) % 64 == 0]
+    return max(whole or cands)
+
+
 class DeviceStep:
-    """Buffers and call sequence of one device step; ``run()`` may be timed or graph-captured."""
+    """Buffers and call sequence of one device step; ``run()`` may be timed or graph-captured.
+    ``subseg`` fixes the number G of sub-segments (0 = ``subsegments()``)."""
 
     def __init__(self, q, k, v, decay, s_recv, *, mode: str, chunk: int = 64, gate_norm: float = 16.0,
-                 subseg_chunks: int = 0):
+                 subseg_chunks: int = 0, subseg: int = 0):
         B, H, L, dk = q.shape
         dv = v.shape[-1]
         dev = q.device
+        G = subseg or subsegments(B, H, L)
+        if L % G:
+            raise ValueError(f"{G} sub-segments do not divide L = {L}")
         self.q, self.k, self.v, self.decay = q, k, v, decay
         self.mode, self.chunk, self.gate_norm, self.subseg_chunks = mode, chunk, gate_norm, subseg_chunks
+        self.G = G
         self.shape = (B, H, L, dk, dv)
         self.o = torch.empty((B, H, L, dv), dtype=q.dtype, device=dev)
-        # scan buffer: slot 0 = incoming state (what the previous device sends), slot 1 = local state
-        self.states = torch.zeros((B, H, 2, dk, dv), dtype=torch.float32, device=dev)
+        # scan buffer: slot 0 = incoming state (what the previous device sends), slots 1..G = local
+        # states of the sub-segments; after the scan slot p is the incoming state of sub-segment p
+        # and slot G the outgoing state
+        self.states = torch.zeros((B, H, G + 1, dk, dv), dtype=torch.float32, device=dev)
         if s_recv is not None:
             self.states[:, :, 0].copy_(s_recv)
-        self.totals = torch.ones((B, H, 2, dk), dtype=torch.float32, device=dev)
+        self.totals = torch.ones((B, H, G + 1, dk), dtype=torch.float32, device=dev)
         self.qd = torch.empty_like(q) if mode == "gate" else None  # q times its cumulative decay
 
     def run(self, timers: Optional[dict] = None):
         """One step.  ``timers`` optionally maps "fwd", "cum", "scan", "corr" to KernelTimers."""
         t = timers or {}
-        _forward(self, None, self.states[:, :, 1:2], self.totals[:, :, 1:2], 1, t)
+        G = self.G
+        _forward(self, None, self.states[:, :, 1:], self.totals[:, :, 1:], G, t)
         la_state_scan(self.states, self.totals if self.mode != "none" else None, self.states, timer=t.get("scan"))
-        _correct(self, self.states[:, :, 0:1], 1, 0, t)
-        return self.o, self.states[:, :, 1]
+        _correct(self, self.states[:, :, 0:G], G, 0, t)
+        return self.o, self.states[:, :, G]
 
 
 def device_step(q, k, v, decay, s_recv, *, mode: str, chunk: int = 64, gate_norm: float = 16.0,
-                subseg_chunks: int = 0):
+                subseg_chunks: int = 0, subseg: int = 0):
     """Returns (o, s_out) of one device that receives s_recv (None = zero)."""
     return DeviceStep(q, k, v, decay, s_recv, mode=mode, chunk=chunk, gate_norm=gate_norm,
-                      subseg_chunks=subseg_chunks).run()
+                      subseg_chunks=subseg_chunks, subseg=subseg).run()
 
 
 class SegmentedForward:

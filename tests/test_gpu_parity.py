@@ -119,15 +119,18 @@ def test_segmented_pipeline_equals_one_pass(mode, dtype):
 
 
 @pytest.mark.parametrize("mode", ["none", "head", "gate"])
-def test_device_step_combine(mode):
-    """Local pass from zero + two-entry scan with S_recv + correction == one pass from S_recv."""
+@pytest.mark.parametrize("L,subseg", [(700, 0), (768, 1), (768, 3), (64 * 12, 12)])
+def test_device_step_combine(mode, L, subseg):
+    """G sub-segments from zero + one scan over [S_recv, S_loc...] + one correction pass == one
+    pass from S_recv (G = 1: local pass, two-entry scan, correction; G = 12: one-chunk
+    sub-segments; L = 700 chooses G = 2 with ragged chunks)."""
     decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
-    w = W2.scaled(B=2, H=2, L=700, decay=decay, s_in_std=0.05, seed=51)
-    note(f"device step combine mode={mode}")
+    w = W2.scaled(B=2, H=2, L=L, decay=decay, s_in_std=0.05, seed=51 + L + subseg)
+    note(f"device step combine mode={mode} L={L} subseg={subseg}")
     inp = make_inputs(w, "cpu")
     o_ref, s_ref = oracle_run(inp, w)
     d = to_dev(inp)
-    o, s = pipeline.device_step(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode=w.mode)
+    o, s = pipeline.device_step(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode=w.mode, subseg=subseg)
     torch.cuda.synchronize()
     assert rel_err(o, o_ref) <= TOL["bf16"]
     assert rel_err(s, s_ref[:, :, 0]) <= TOL["bf16"]
