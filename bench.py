@@ -104,6 +104,39 @@ def kernel_stats(step, steps, stream):
     return kernels, e0.elapsed_time(e1) / steps
 
 
+def epsilon(w, inp, step, stream, steps: int = 20):
+    """The single-GPU analogue of the reviewers' overhead question on this workload: the same
+    exact result three ways, each step timed with events (median us).
+      zeco_step        the device step (local forward from zero, scan, correction by S_recv)
+      one_call_exact   one la_chunk_fwd from S_recv (what a single device without sequence
+                       parallelism runs; intra-GPU split with exact incoming states, no correction)
+      two_pass_chunk_states  la_chunk_fwd from S_recv with every chunk's state stored to HBM, scanned
+                       and reloaded (the pages' two-pass schedule, one sub-segment per chunk)"""
+    import torch
+
+    from chunked_scan_amd import binding
+
+    s_recv = step.states[:, :, 0].clone()
+    o = torch.empty_like(step.o)
+    s_out = torch.empty((w.B, w.H, 1, w.dk, w.dv), dtype=torch.float32, device="cuda")
+
+    class Call:
+        def __init__(self, subseg):
+            self.subseg = subseg
+
+        def run(self):
+            binding.la_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["decay"], s_recv, o, s_out, mode=w.mode,
+                                 chunk=w.chunk, gate_norm=w.gate_norm, subseg_chunks=self.subseg)
+
+    out = {"zeco_step": step_stats(step, steps, stream)["median_us"]}
+    for name, sub in (("one_call_exact", 0), ("two_pass_chunk_states", 1)):
+        c = Call(sub)
+        for _ in range(2):
+            c.run()
+        out[name] = step_stats(c, steps, stream)["median_us"]
+    return out
+
+
 def cpu_baseline(w, inp):
     import numpy as np
     import torch
@@ -197,6 +230,11 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+
+    eps = None
+    if w.nseg == 1:
+        eps = epsilon(w, inp, step, stream)
+        log("[bench] same result three ways (median us/step): " + ", ".join(f"{k} {v:.1f}" for k, v in eps.items()))
 
     alongside = {}
     if not args.no_alongside:
@@ -292,6 +330,7 @@ def main():
         "per_step_us": {"warm": warm, "cold": cold},
         "kernels": {n: {k: round(v, 2) for k, v in d.items()} for n, d in kernels.items()},
         "ms_per_step_with_kernel_events": round(ms_traced, 5),
+        "overhead_one_gpu_us": eps,
         "alongside": alongside,
     }
     print(json.dumps(out), flush=True)
