@@ -15,7 +15,9 @@ roofline uses its algorithmic bytes (q, k, v read + o written) over its mean dur
 Per-step statistics (median, mean, std, min) are given warm and cold (a 512 MiB buffer written
 before each step evicts the 256 MB last-level cache).  The head-decay and gate workloads
 (device step, B = 2 and 4) and the 1M-token 64-segment pass are timed alongside, unless
---no-alongside.
+--no-alongside.  Every workload is warmed up with at least ~20 ms of steps first: the GPU's
+clocks take about 10 ms of sustained work to settle (the plain step runs ~105 us before, ~93 us
+after).
 """
 from __future__ import annotations
 
@@ -170,7 +172,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first; the GPU's clocks take ~10 ms of sustained work to settle")
     ap.add_argument("--workload", type=int, default=1, help="index into chunked_scan_amd.inputs.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alongside", action="store_true",
@@ -210,17 +213,10 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
-    # --- every step bracketed by its own events, cold then warm
-    cold = step_stats(step, args.steps, stream, scratch)
+    # --- every step bracketed by its own events (warm: back to back on the same inputs)
     warm = step_stats(step, args.steps, stream)
-    log(f"[bench] per step: warm median {warm['median_us']:.1f} us, cold median {cold['median_us']:.1f} us")
 
-    # --- the same steps with HIP events around every kernel (la_trace)
-    kernels, ms_traced = kernel_stats(step, args.steps, stream)
-    log("[bench] per kernel: " + ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in kernels.items()))
-
-    # --- the headline: K steps back to back as a user runs them (no per-kernel events), timed last
-    # so that the GPU has left its idle clocks behind
+    # --- the headline: K steps back to back as a user runs them (no per-kernel events)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -230,6 +226,15 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+
+    # --- the same steps with HIP events around every kernel (la_trace)
+    kernels, ms_traced = kernel_stats(step, args.steps, stream)
+    log("[bench] per kernel: " + ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in kernels.items()))
+
+    # --- cold: the last-level cache evicted before every step (last: the 512 MiB writes between
+    # steps change the GPU's power state for the regions after them)
+    cold = step_stats(step, args.steps, stream, scratch)
+    log(f"[bench] per step: warm median {warm['median_us']:.1f} us, cold median {cold['median_us']:.1f} us")
 
     eps = None
     if w.nseg == 1:
@@ -250,10 +255,10 @@ def main():
             else:
                 sa = SegmentedForward(ia["q"], ia["k"], ia["v"], ia["decay"], ia["s_in"], mode=wa.mode,
                                       nseg=wa.nseg, chunk=wa.chunk, gate_norm=wa.gate_norm)
-            for _ in range(3):
+            for _ in range(4 if wa.nseg > 1 else 100):  # >= 20 ms of work: settled clocks
                 sa.run()
             torch.cuda.synchronize()
-            n_al = 10 if wa.nseg > 1 else 20
+            n_al = 10 if wa.nseg > 1 else 50
             st = step_stats(sa, n_al, stream)
             ks, _ = kernel_stats(sa, n_al, stream)
             alongside[wa.name] = dict(

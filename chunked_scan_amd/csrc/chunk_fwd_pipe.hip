@@ -431,6 +431,9 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                 if (MODE == DECAY_HEAD) asm volatile("" : "+s"(lamb));
                 lamb *= LOG2E;
                 const float e1b = (MODE == DECAY_HEAD) ? decay_pow2(lamb, 1) : 1.f;
+                const float einv = (MODE == DECAY_HEAD) ? __builtin_amdgcn_exp2f(-lamb) : 1.f;
+                // the upward chain below needs exp(31 lambda) to stay a normal float
+                const bool up = lamb >= -4.f;
                 // Q operand (B of both products): token itok, key dims ks*16 + kg*8 .. +8
                 bf16x8 qb[8];
 #pragma unroll
@@ -447,17 +450,40 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                         sc = mfma(*(const bf16x8*)(cur.k + sw(krow, ks * 16 + kg * 8)), qb[ks], sc);
 #pragma unroll
                     for (int hh = 0; hh < 2; hh++) {
-                        // head decay: fac[jj] = exp(lambda max(itok - jtok, 0)); itok - jtok grows by one
-                        // from jj = 7 down to jj = 0
+                        // head decay: fac[jj] = exp(lambda (itok - jtok)) where itok >= jtok.  The distance
+                        // shrinks by one per jj.  Off the diagonal it is always positive: a plain chain.
+                        // On the diagonal, for moderate decay, the chain starts at jj = 0 (the largest
+                        // distance, at most 31) and multiplies by exp(-lambda): every kept element is
+                        // reached before any masked one (negative distance), whose factor may grow but is
+                        // discarded by the causal mask below.  For stronger decay (exp(31 lambda) could
+                        // underflow) the chain runs downward and restarts at 1 where the distance
+                        // reaches 0.
                         float fac[8];
                         if (MODE == DECAY_HEAD) {
-                            const int d7 = 32 * (ib - jb) + n32 - 16 * hh - 8 * kg - 7;
-                            float gch = decay_pow2(lamb, max(d7, 0));
-                            fac[7] = gch;
+                            const int d0 = 32 * (ib - jb) + n32 - 16 * hh - 8 * kg;
+                            if (jb < ib) {
+                                float gch = decay_pow2(lamb, d0 - 7);
 #pragma unroll
-                            for (int jj = 6; jj >= 0; jj--) {
-                                gch = (d7 + 7 - jj > 0) ? gch * e1b : 1.f;
-                                fac[jj] = gch;
+                                for (int jj = 7; jj >= 0; jj--) {
+                                    fac[jj] = gch;
+                                    gch *= e1b;
+                                }
+                            } else if (up) {
+                                float gch = decay_pow2(lamb, max(d0, 0));
+#pragma unroll
+                                for (int jj = 0; jj < 8; jj++) {
+                                    fac[jj] = gch;
+                                    gch *= einv;
+                                }
+                            } else {
+                                const int d7 = d0 - 7;
+                                float gch = decay_pow2(lamb, max(d7, 0));
+                                fac[7] = gch;
+#pragma unroll
+                                for (int jj = 6; jj >= 0; jj--) {
+                                    gch = (d7 + 7 - jj > 0) ? gch * e1b : 1.f;
+                                    fac[jj] = gch;
+                                }
                             }
                         }
                         bf16x8 x;
@@ -518,15 +544,29 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                 for (int i = 0; i < 16; i++) S[m][i] *= fh;
             // token t = 16 ks + kg*8 + jj gets exp(lambda (n - 1 - t)), or 0 past the chunk's end;
             // the exponent grows by one from jj = 7 down to jj = 0
+            if (n == C) {  // every chunk but a ragged last one: no token past the end
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                const int e7 = n - 1 - (16 * ks + kg * 8 + 7);
-                float gch = decay_pow2(lamc, max(e7, 0));
+                for (int ks = 0; ks < 4; ks++) {
+                    float gch = decay_pow2(lamc, C - 1 - (16 * ks + kg * 8 + 7));
+                    float f[8];
 #pragma unroll
-                for (int jj = 7; jj >= 0; jj--) {
-                    const int e = e7 + 7 - jj;
-                    if (jj < 7) gch = (e > 0) ? gch * e1 : 1.f;
-                    vb[ks][jj] = (e >= 0) ? (__bf16)((float)vb[ks][jj] * gch) : (__bf16)0.f;
+                    for (int jj = 7; jj >= 0; jj--) {
+                        f[jj] = gch;
+                        gch *= e1;
+                    }
+                    vb[ks] = __builtin_bit_cast(bf16x8, scale8(__builtin_bit_cast(u32x4, vb[ks]), f));
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) {
+                    const int e7 = n - 1 - (16 * ks + kg * 8 + 7);
+                    float gch = decay_pow2(lamc, max(e7, 0));
+#pragma unroll
+                    for (int jj = 7; jj >= 0; jj--) {
+                        const int e = e7 + 7 - jj;
+                        if (jj < 7) gch = (e > 0) ? gch * e1 : 1.f;
+                        vb[ks][jj] = (e >= 0) ? (__bf16)((float)vb[ks][jj] * gch) : (__bf16)0.f;
+                    }
                 }
             }
         } else if (n < C) {
