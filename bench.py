@@ -177,7 +177,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1, help="index into chunked_scan_amd.inputs.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alongside", action="store_true",
-                    help="skip the decay and segmented workloads reported next to the headline")
+                    help="skip the decay and segmented workloads and the three-way comparison reported next "
+                         "to the headline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -237,7 +238,7 @@ def main():
     log(f"[bench] per step: warm median {warm['median_us']:.1f} us, cold median {cold['median_us']:.1f} us")
 
     eps = None
-    if w.nseg == 1:
+    if w.nseg == 1 and not args.no_alongside:
         eps = epsilon(w, inp, step, stream)
         log("[bench] same result three ways (median us/step): " + ", ".join(f"{k} {v:.1f}" for k, v in eps.items()))
 
