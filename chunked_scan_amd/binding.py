@@ -24,8 +24,8 @@ LA_F32, LA_BF16 = 0, 1
 MODES = {"none": 0, "head": 1, "gate": 2}
 STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_SHAPE", -3: "LA_ERR_DTYPE", -4: "LA_ERR_ALIAS",
           -5: "LA_ERR_UNSUPPORTED", -6: "LA_ERR_LAUNCH", -7: "LA_ERR_DECAY"}
-EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_decayed", "la_state_scan", "la_state_correct", "la_cumdecay",
-           "la_status_str", "la_supported", "la_version")
+EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_decayed", "la_state_scan", "la_state_correct", "la_state_correct_live",
+           "la_cumdecay", "la_status_str", "la_supported", "la_version")
 
 
 TRACE_MAX = 8
@@ -89,15 +89,16 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, S = ctypes.c_void_p, ctypes.POINTER(Shape)
         L.la_chunk_fwd.argtypes = [P, P, P, P, P, P, P, S, ctypes.c_int32]
-        L.la_chunk_fwd_decayed.argtypes = [P, P, P, P, P, P, P, P, P, S, ctypes.c_int32]
+        L.la_chunk_fwd_decayed.argtypes = [P, P, P, P, P, P, P, P, P, P, S, ctypes.c_int32]
+        L.la_state_correct_live.argtypes = [P, P, P, P, P, S]
         L.la_state_scan.argtypes = [P, P, ctypes.c_int32, P, S]
         L.la_state_correct.argtypes = [P, P, P, P, S]
         L.la_cumdecay.argtypes = [P, P, P, S]
         L.la_supported.argtypes = [S, ctypes.c_int32]
         L.la_status_str.argtypes = [ctypes.c_int]
         L.la_status_str.restype = ctypes.c_char_p
-        for f in (L.la_chunk_fwd, L.la_chunk_fwd_decayed, L.la_state_scan, L.la_state_correct, L.la_cumdecay,
-                  L.la_supported, L.la_version):
+        for f in (L.la_chunk_fwd, L.la_chunk_fwd_decayed, L.la_state_scan, L.la_state_correct,
+                  L.la_state_correct_live, L.la_cumdecay, L.la_supported, L.la_version):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -206,12 +207,15 @@ def la_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optio
 def la_chunk_fwd_decayed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch.Tensor] = None,
                          s_in: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
                          s_out: Optional[torch.Tensor] = None, q_decayed: Optional[torch.Tensor] = None,
-                         total: Optional[torch.Tensor] = None, *, mode: Optional[str] = None, nseg: int = 1,
-                         chunk: int = 64, gate_norm: float = 16.0, subseg_chunks: int = 0, want_state: bool = True,
-                         want_q_decayed: bool = True, want_total: bool = True, stream=None, timer=None):
+                         total: Optional[torch.Tensor] = None, tile_live: Optional[torch.Tensor] = None, *,
+                         mode: Optional[str] = None, nseg: int = 1, chunk: int = 64, gate_norm: float = 16.0,
+                         subseg_chunks: int = 0, want_state: bool = True, want_q_decayed: bool = True,
+                         want_total: bool = True, want_tile_live: bool = False, stream=None, timer=None):
     """la_chunk_fwd plus q_decayed [B,H,L,dk] (q times its cumulative decay from the segment start,
-    q's dtype) and total [B,H,nseg,dk] f32 (each segment's total decay; may be a view with evenly
-    spaced dense (b,h) blocks).  Returns (o, s_out, q_decayed, total); unrequested ones are None."""
+    q's dtype), total [B,H,nseg,dk] f32 (each segment's total decay; may be a view with evenly
+    spaced dense (b,h) blocks) and tile_live [B,H,nseg,ceil(L/nseg/64)] int32 (0: the 64-token tile
+    of q_decayed is exactly zero).  Returns (o, s_out, q_decayed, total, tile_live); unrequested
+    ones are None."""
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     _dev(q, "q")
@@ -241,13 +245,18 @@ def la_chunk_fwd_decayed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, deca
     if total is not None:
         _dev(total, "total", torch.float32, (B, H, nseg, dk), contiguous=False)
         tstride = _bh_stride(total, "total", dk)
+    ntile = (L // nseg + 63) // 64 if nseg else 0
+    if tile_live is None and want_tile_live:
+        tile_live = torch.empty((B, H, nseg, ntile), dtype=torch.int32, device=q.device)
+    if tile_live is not None:
+        _dev(tile_live, "tile_live", torch.int32, (B, H, nseg, ntile))
     shp = make_shape(B, H, L, dk, dv, nseg=nseg, dtype=_dtype_code(q), mode=m, gate_norm=gate_norm,
                      state_stride=stride, total_stride=tstride, subseg_chunks=subseg_chunks, stream=_stream(stream),
                      timer=timer)
     _check("la_chunk_fwd_decayed", lib().la_chunk_fwd_decayed(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in),
                                                               _ptr(o), _ptr(s_out), _ptr(q_decayed), _ptr(total),
-                                                              ctypes.byref(shp), chunk))
-    return o, s_out, q_decayed, total
+                                                              _ptr(tile_live), ctypes.byref(shp), chunk))
+    return o, s_out, q_decayed, total, tile_live
 
 
 def la_state_scan(seg_states: torch.Tensor, seg_decay: Optional[torch.Tensor],
@@ -268,11 +277,13 @@ def la_state_scan(seg_states: torch.Tensor, seg_decay: Optional[torch.Tensor],
 
 
 def la_state_correct(q: torch.Tensor, cumdecay: Optional[torch.Tensor], s_recv: torch.Tensor, o: torch.Tensor, *,
-                     mode: Optional[str] = None, nseg: int = 1, seg_begin: int = 0, stream=None,
-                     timer=None) -> torch.Tensor:
+                     mode: Optional[str] = None, nseg: int = 1, seg_begin: int = 0,
+                     tile_live: Optional[torch.Tensor] = None, stream=None, timer=None) -> torch.Tensor:
     """o += (q * cum) @ s_recv[p - seg_begin] for segments p >= seg_begin, in place.
     cumdecay: None (none), [H] log-decay (head) or [B,H,L,dk] cumulative decay (gate).
-    s_recv: f32 [B,H,nseg-seg_begin,dk,dv], possibly a view with evenly spaced dense (b,h) blocks."""
+    s_recv: f32 [B,H,nseg-seg_begin,dk,dv], possibly a view with evenly spaced dense (b,h) blocks.
+    tile_live: int32 [B,H,nseg,ceil(L/nseg/64)] from la_chunk_fwd_decayed, or None; with it
+    la_state_correct_live skips the tiles flagged zero (whose correction is exactly zero)."""
     B, H, L, dk = q.shape
     dv = o.shape[-1]
     _dev(q, "q")
@@ -285,8 +296,13 @@ def la_state_correct(q: torch.Tensor, cumdecay: Optional[torch.Tensor], s_recv: 
     stride = _bh_stride(s_recv, "s_recv", dk * dv)
     shp = make_shape(B, H, L, dk, dv, nseg=nseg, dtype=_dtype_code(q), mode=m, seg_begin=seg_begin,
                      state_stride=stride, stream=_stream(stream), timer=timer)
-    _check("la_state_correct", lib().la_state_correct(_ptr(q), _ptr(cumdecay), _ptr(s_recv), _ptr(o),
-                                                      ctypes.byref(shp)))
+    if tile_live is None:
+        _check("la_state_correct", lib().la_state_correct(_ptr(q), _ptr(cumdecay), _ptr(s_recv), _ptr(o),
+                                                          ctypes.byref(shp)))
+    else:
+        _dev(tile_live, "tile_live", torch.int32, (B, H, nseg, (L // nseg + 63) // 64))
+        _check("la_state_correct_live", lib().la_state_correct_live(_ptr(q), _ptr(cumdecay), _ptr(s_recv), _ptr(o),
+                                                                    _ptr(tile_live), ctypes.byref(shp)))
     return o
 
 

@@ -123,7 +123,8 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     const float* __restrict__ decay, const float* __restrict__ s_in, __bf16* __restrict__ o,
     float* __restrict__ s_out, int64_t s_out_stride, float* __restrict__ part_state,
     float* __restrict__ part_decay, const float* __restrict__ init_state, int64_t H, int64_t L, int nseg, int G,
-    int cps, float inv_norm, __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride) {
+    int cps, float inv_norm, __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride,
+    uint8_t* __restrict__ tile_live) {
     constexpr bool GATE = MODE == DECAY_GATE;
     constexpr bool OTILE = !STATE_ONLY && !GATE;  // outputs leave through an LDS tile stored by the loaders
     constexpr int SLOT = STATE_ONLY ? 2 : 3;      // tiles per stage
@@ -133,6 +134,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     __shared__ __attribute__((aligned(16))) __bf16 ring[NST * STAGE];
     // the chunk's outputs, rows unpadded with 16-byte slot s of row r at s ^ (r % 16)
     __shared__ __attribute__((aligned(16))) __bf16 otile[OTILE ? TE : 8];
+    __shared__ int first_dead[4];  // gate loader wave lw: its first chunk with zero cumulative decay
     using DM = Dma<STATE_ONLY>;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -175,12 +177,27 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
         // token) to the end of the last prepared chunk, per key dim of the lane; the output pass
         // starts it from the totals of the sub-segments before this one
         float run[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (!STATE_ONLY && (q_dec || total))
+        if (!STATE_ONLY && (q_dec || total || tile_live))
             for (int gg = 0; gg < g; gg++) {
                 const float* pd = part_decay + (ub * (G - 1) + gg) * D + 8 * o8;
 #pragma unroll
                 for (int e = 0; e < 8; e++) run[e] += __builtin_amdgcn_logf(pd[e]);
             }
+        // Tile liveness: chunk c is dead for this wave when the exponential of run (the log2 decay from
+        // the segment start to the chunk's start; the same instruction that scales q) is zero for all
+        // of the wave's key dims, so q times the cumulative decay is exactly zero on them for every
+        // token of the chunk.  run only decreases, so the dead chunks are a suffix: the wave keeps the
+        // first one in LDS (an atomic min, no register held across the walk) and writes its byte of
+        // every chunk's tile word after the walk.
+        const bool flags = !STATE_ONLY && tile_live;
+        if (flags && lane == 0) first_dead[lw] = nch;
+        auto flag_chunk = [&](int c) {
+            // exp2 is monotone: all of the lane's dims are zero exactly when the largest one is
+            float m = run[0];
+#pragma unroll
+            for (int e = 1; e < 8; e++) m = fmaxf(m, run[e]);
+            if (__ballot(__builtin_amdgcn_exp2f(m) != 0.f) == 0 && lane == 0) atomicMin(&first_dead[lw], c);
+        };
         int issued = 0;
         // token row r of chunk `issued` into x (5 loads); the chunk counts as issued after row 3
         auto load_row = [&](Raw& x, int r) {
@@ -202,6 +219,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
         // between the steps of the preparation: the wave keeps the memory pipeline fed instead of
         // stalling on a burst of loads.
         auto prep = [&](const Raw& x, int cc, bool more, Raw& fill) {
+            if (flags) flag_chunk(cc);  // before the next chunk's loads take their registers
             const int n = chunk_len(cc);
             const Ring st = stage(cc);
             float b[4][8];
@@ -267,6 +285,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                 cf[e] = (!STATE_ONLY && q_dec) ? __builtin_amdgcn_exp2f(run[e]) : 0.f;
                 run[e] += bl[e];
             }
+
             __builtin_amdgcn_sched_barrier(0);
             if (more) load_row(fill, 3);
             __builtin_amdgcn_sched_barrier(0);
@@ -290,7 +309,9 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                     float fd[8];
 #pragma unroll
                     for (int e = 0; e < 8; e++) fd[e] = fq[e] * cf[e];
-                    *(u32x4*)(q_dec + (row_base + t_begin + (int64_t)cc * C + t) * D + 8 * o8) = scale8(x.q[r], fd);
+                    // a wave-uniform row base plus a 32-bit lane offset (no 64-bit per-lane address)
+                    __bf16* const qrow = q_dec + (row_base + t_begin + (int64_t)cc * C) * D;
+                    *(u32x4*)(qrow + (t * D + 8 * o8)) = scale8(x.q[r], fd);
                 }
             }
         };
@@ -309,6 +330,11 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
             float* pd = part_decay + (ub * (G - 1) + g) * D + 8 * o8;
 #pragma unroll
             for (int e = 0; e < 8; e++) pd[e] = __builtin_amdgcn_exp2f(run[e]);
+        }
+        if (flags) {
+            const int fd = first_dead[lw];
+            uint8_t* fl = tile_live + ((bh * nseg + seg) * ((Lseg + C - 1) / C) + (int64_t)g * cps) * 4 + lw;
+            for (int c = lane; c < nch; c += 64) fl[4 * c] = c < fd;
         }
         if (!STATE_ONLY && total && g == G - 1 && tg == 0) {  // the segment's total decay
             float* tt = total + bh * total_stride + (int64_t)seg * D + 8 * o8;
@@ -624,7 +650,7 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
         LA_TRACED(a.tr, "chunk_fwd_pipe_state_pass",
                   pipe_fwd_kernel<MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
                       q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
-                      a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0));
+                      a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0, nullptr));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream, a.tr);
@@ -634,7 +660,7 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
               pipe_fwd_kernel<MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
                   q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, part_decay, part_state, a.H, a.L,
                   a.nseg, G, cps, a.inv_norm, fused ? (__bf16*)a.q_dec : nullptr, fused ? a.total : nullptr,
-                  a.total_stride));
+                  a.total_stride, fused ? (uint8_t*)a.tile_live : nullptr));
     return hipGetLastError();
 }
 

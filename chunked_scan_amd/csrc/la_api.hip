@@ -74,9 +74,15 @@ size_t decay_bytes(const la_shape* s) {
     return 0;
 }
 
+// Bytes of a per-tile flag array (one uint32 per 64-token tile of every segment).
+size_t tile_flag_bytes(const la_shape* s) {
+    return sizeof(uint32_t) * (size_t)(s->B * s->H * s->nseg * ((s->L / s->nseg + 63) / 64));
+}
+
 la_status validate_fwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
                        const void* o, const float* s_out, const la_shape* s, int chunk,
-                       const void* q_dec = nullptr, const float* total = nullptr) {
+                       const void* q_dec = nullptr, const float* total = nullptr,
+                       const uint32_t* tile_live = nullptr) {
     la_status st = check_common(s);
     if (st != LA_OK) return st;
     if (chunk <= 0 || s->subseg_chunks < 0 || s->state_stride < 0) return LA_ERR_SHAPE;
@@ -107,9 +113,10 @@ la_status validate_fwd(const void* q, const void* k, const void* v, const float*
     const int64_t tstride = s->total_stride ? s->total_stride : (int64_t)s->nseg * s->dk;
     Span sqd{q_dec, q_dec ? es * nqk : 0};
     Span stt{total, (total && BH > 0) ? sizeof(float) * (size_t)((BH - 1) * tstride + s->nseg * s->dk) : 0};
+    Span stl{tile_live, tile_live ? tile_flag_bytes(s) : 0};
     for (Span x : {sq, sk, sv, sd, si, so, sso})
-        if (overlap(sqd, x) || overlap(stt, x)) return LA_ERR_ALIAS;
-    if (overlap(sqd, stt)) return LA_ERR_ALIAS;
+        if (overlap(sqd, x) || overlap(stt, x) || overlap(stl, x)) return LA_ERR_ALIAS;
+    if (overlap(sqd, stt) || overlap(stl, sqd) || overlap(stl, stt)) return LA_ERR_ALIAS;
     return LA_OK;
 }
 
@@ -165,8 +172,9 @@ namespace {
 
 // The forward of la_chunk_fwd, plus the optional outputs of la_chunk_fwd_decayed (q_dec, total).
 la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* decay, const float* s_in, void* o,
-                         float* s_out, void* q_dec, float* total, const la_shape* s, int32_t chunk) {
-    la_status st = validate_fwd(q, k, v, decay, s_in, o, s_out, s, chunk, q_dec, total);
+                         float* s_out, void* q_dec, float* total, uint32_t* tile_live, const la_shape* s,
+                         int32_t chunk) {
+    la_status st = validate_fwd(q, k, v, decay, s_in, o, s_out, s, chunk, q_dec, total, tile_live);
     if (st != LA_OK) return st;
     if ((st = check_trace(s)) != LA_OK) return st;
     la::Tracer tr = make_tracer(s);
@@ -187,6 +195,7 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const floa
     a.q_dec = q_dec;
     a.total = total;
     a.total_stride = s->total_stride ? s->total_stride : (int64_t)s->nseg * s->dk;
+    a.tile_live = tile_live;
     hipError_t e = hipSuccess;
     bool fused = false;  // the forward itself wrote q_dec and total
     if (s->L == 0) {
@@ -197,7 +206,7 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const floa
     } else {
         e = la::launch_chunk_fwd_generic(a);
     }
-    if (e == hipSuccess && !fused && (q_dec || total)) e = la::launch_decayed_q(a);
+    if (e == hipSuccess && !fused && (q_dec || total || tile_live)) e = la::launch_decayed_q(a);
     return from_hip(e);
 }
 
@@ -207,12 +216,13 @@ extern "C" {
 
 la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in, void* o,
                        float* s_out, const la_shape* s, int32_t chunk) {
-    return chunk_fwd_impl(q, k, v, decay, s_in, o, s_out, nullptr, nullptr, s, chunk);
+    return chunk_fwd_impl(q, k, v, decay, s_in, o, s_out, nullptr, nullptr, nullptr, s, chunk);
 }
 
 la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
-                               void* o, float* s_out, void* q_decayed, float* total, const la_shape* s, int32_t chunk) {
-    return chunk_fwd_impl(q, k, v, decay, s_in, o, s_out, q_decayed, total, s, chunk);
+                               void* o, float* s_out, void* q_decayed, float* total, uint32_t* tile_live,
+                               const la_shape* s, int32_t chunk) {
+    return chunk_fwd_impl(q, k, v, decay, s_in, o, s_out, q_decayed, total, tile_live, s, chunk);
 }
 
 la_status la_state_scan(const float* seg_states, const float* seg_decay, int32_t P, float* out_states,
@@ -236,7 +246,12 @@ la_status la_state_scan(const float* seg_states, const float* seg_decay, int32_t
                                           (hipStream_t)s->stream, &tr));
 }
 
-la_status la_state_correct(const void* q, const float* cumdecay, const float* s_recv, void* o, const la_shape* s) {
+}  // extern "C"
+
+namespace {
+
+la_status state_correct_impl(const void* q, const float* cumdecay, const float* s_recv, void* o,
+                             const uint32_t* tile_live, const la_shape* s) {
     la_status st = check_common(s);
     if (st != LA_OK) return st;
     if (s->seg_begin < 0 || s->seg_begin > s->nseg || s->state_stride < 0) return LA_ERR_SHAPE;
@@ -259,7 +274,7 @@ la_status la_state_correct(const void* q, const float* cumdecay, const float* s_
     size_t recv_bytes = BH > 0 ? sizeof(float) * (size_t)((BH - 1) * stride + np * per_state) : 0;
     Span so{o, es * (size_t)(BH * s->L * s->dv)};
     if (overlap(so, Span{q, es * (size_t)nq}) || overlap(so, Span{cumdecay, cum_bytes}) ||
-        overlap(so, Span{s_recv, recv_bytes}))
+        overlap(so, Span{s_recv, recv_bytes}) || overlap(so, Span{tile_live, tile_live ? tile_flag_bytes(s) : 0}))
         return LA_ERR_ALIAS;
     if ((st = check_trace(s)) != LA_OK) return st;
     la::Tracer tr = make_tracer(s);
@@ -273,7 +288,21 @@ la_status la_state_correct(const void* q, const float* cumdecay, const float* s_
     a.mode = s->decay_mode;
     a.stream = (hipStream_t)s->stream;
     a.tr = &tr;
+    a.tile_live = tile_live;
     return from_hip(la::launch_state_correct(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_state_correct(const void* q, const float* cumdecay, const float* s_recv, void* o, const la_shape* s) {
+    return state_correct_impl(q, cumdecay, s_recv, o, nullptr, s);
+}
+
+la_status la_state_correct_live(const void* q, const float* cumdecay, const float* s_recv, void* o,
+                                const uint32_t* tile_live, const la_shape* s) {
+    return state_correct_impl(q, cumdecay, s_recv, o, tile_live, s);
 }
 
 la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const la_shape* s) {

@@ -59,6 +59,7 @@ struct FwdArgs {
     void* q_dec = nullptr;     // optional: q times its cumulative decay from the segment start
     float* total = nullptr;    // optional: each segment's total decay
     int64_t total_stride = 0;  // elements between (b,h) blocks of total
+    uint32_t* tile_live = nullptr;  // optional: [B,H,nseg,ceil(L/nseg/64)], 0 = the 64-token tile of q_dec is zero
 };
 
 struct CorrectArgs {
@@ -73,6 +74,7 @@ struct CorrectArgs {
     int mode;
     hipStream_t stream;
     Tracer* tr;
+    const uint32_t* tile_live = nullptr;  // optional: [B,H,nseg,ceil(L/nseg/64)]; 0 = skip the tile (q rows zero)
 };
 
 // Generic chunked forward: fp32 arithmetic on VALU, q/k/v/o in f32 or bf16, dk, dv in

@@ -18,7 +18,8 @@
 // compute waves update the o tile in LDS in the transposed layout and then store it row-major.
 // Head mode applies exp(lambda * tau) to each token's product (a per-lane scalar) and skips tiles
 // whose factor is exactly zero in fp32: their correction is exactly zero, so O is bit-identical
-// either way.
+// either way.  With per-tile liveness flags (from the forward that formed q * cum), tiles flagged
+// zero are skipped in every mode, for the same reason.
 //
 // Gate decay: the per-token, per-key cumulative decay is an fp32 tensor twice the size of q, so
 // q * cum is formed in registers on the way into LDS (rounded to bf16 once) and the fp32
@@ -65,15 +66,20 @@ struct Tile {
 template <int MODE>
 struct TileWalk {
     int64_t H, L, Ls, tiles_per_seg;
-    int np, seg_begin;
+    int nseg, np, seg_begin;
     const float* cum;
     int64_t t, end;        // position in the tile list and end of this workgroup's range
     int64_t ti, pidx, bh, h;
+    // optional liveness flags [(b,h), segment, tile] (0: the tile's q rows are exactly zero), read
+    // 64 tiles of the list at a time into a wave-wide bit mask
+    const uint32_t* flags;
+    int64_t wbase = -1;
+    uint64_t wmask = 0;
 
-    __device__ TileWalk(int64_t H_, int64_t L_, int nseg, int seg_begin_, int64_t tps, int64_t total,
-                        const float* cum_)
-        : H(H_), L(L_), Ls(L_ / nseg), tiles_per_seg(tps), np(nseg - seg_begin_), seg_begin(seg_begin_),
-          cum(cum_) {
+    __device__ TileWalk(int64_t H_, int64_t L_, int nseg_, int seg_begin_, int64_t tps, int64_t total,
+                        const float* cum_, const uint32_t* flags_)
+        : H(H_), L(L_), Ls(L_ / nseg_), tiles_per_seg(tps), nseg(nseg_), np(nseg_ - seg_begin_),
+          seg_begin(seg_begin_), cum(cum_), flags(flags_) {
         t = total * blockIdx.x / gridDim.x;
         end = total * (blockIdx.x + 1) / gridDim.x;
         const int64_t sp = t / tps;
@@ -93,9 +99,22 @@ struct TileWalk {
         x.lam = (MODE == DECAY_HEAD) ? cum[h] : 0.f;
         return x;
     }
-    // head mode: tiles whose cumulative decay is exactly zero contribute exactly zero
-    __device__ bool live() const {
-        return MODE != DECAY_HEAD || expf(cum[h] * (float)(ti * TT + 1)) != 0.f;
+    // head mode: tiles whose cumulative decay is exactly zero contribute exactly zero; with flags,
+    // tiles flagged zero likewise.  Called by every lane of a wave with the same state.
+    __device__ bool live() {
+        if (MODE == DECAY_HEAD && expf(cum[h] * (float)(ti * TT + 1)) == 0.f) return false;
+        if (!flags) return true;
+        if (wbase < 0 || t >= wbase + 64) {  // the walk only moves forward
+            wbase = t;
+            const int64_t tl = t + (threadIdx.x & 63);
+            bool f = false;
+            if (tl < end) {
+                const int64_t sp = tl / tiles_per_seg;
+                f = flags[((sp / np) * nseg + seg_begin + sp % np) * tiles_per_seg + tl % tiles_per_seg] != 0;
+            }
+            wmask = __ballot(f);
+        }
+        return (wmask >> (t - wbase)) & 1;
     }
     __device__ void step() {
         t++;
@@ -138,12 +157,12 @@ template <int MODE>
 __global__ __launch_bounds__(NT_WS, 1) void state_correct_ws_kernel(
     const __bf16* __restrict__ q, const float* __restrict__ cum, const float* __restrict__ s_recv,
     __bf16* __restrict__ o, int64_t H, int64_t L, int nseg, int seg_begin, int64_t state_stride,
-    int64_t tiles_per_seg, int64_t total_tiles) {
+    int64_t tiles_per_seg, int64_t total_tiles, const uint32_t* __restrict__ flags) {
     // stage b: q tile at ring + 2 b TE, o tile at ring + (2 b + 1) TE; rows unpadded, slots swizzled
     __shared__ __attribute__((aligned(16))) __bf16 ring[NST * 2 * TE];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    TileWalk<MODE> walk(H, L, nseg, seg_begin, tiles_per_seg, total_tiles, cum);
+    TileWalk<MODE> walk(H, L, nseg, seg_begin, tiles_per_seg, total_tiles, cum, flags);
     if (walk.done()) return;  // every wave of the workgroup sees the same (empty) range
 
     if (wave >= 4) {
@@ -235,13 +254,13 @@ __global__ __launch_bounds__(NT_WS, 1) void state_correct_ws_kernel(
 __global__ __launch_bounds__(NT) void state_correct_gate_kernel(
     const __bf16* __restrict__ q, const float* __restrict__ cum, const float* __restrict__ s_recv,
     __bf16* __restrict__ o, int64_t H, int64_t L, int nseg, int seg_begin, int64_t state_stride,
-    int64_t tiles_per_seg, int64_t total_tiles) {
+    int64_t tiles_per_seg, int64_t total_tiles, const uint32_t* __restrict__ flags) {
     __shared__ __attribute__((aligned(16))) __bf16 sQ[TT * QPITCH];
     __shared__ __attribute__((aligned(16))) float sC[TT * CPITCH];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, n32 = lane & 31, kg = lane >> 5;
-    TileWalk<DECAY_GATE> walk(H, L, nseg, seg_begin, tiles_per_seg, total_tiles, cum);
+    TileWalk<DECAY_GATE> walk(H, L, nseg, seg_begin, tiles_per_seg, total_tiles, cum, flags);
     if (walk.done()) return;
 
     // this thread's 16-byte pieces of a tile: piece r is row (tid + NT r) / 16, columns 8 ((tid + NT r) % 16) + 0..7
@@ -366,7 +385,8 @@ hipError_t launch_correct(K kernel, int threads, const CorrectArgs& a, int64_t t
     const unsigned grid = (unsigned)resident_grid(kernel, threads, total);
     LA_TRACED(a.tr, "state_correct_mfma",
               kernel<<<grid, threads, 0, a.stream>>>((const __bf16*)a.q, a.cum, a.s_recv, (__bf16*)a.o, a.H, a.L,
-                                                     a.nseg, a.seg_begin, a.state_stride, tps, total));
+                                                     a.nseg, a.seg_begin, a.state_stride, tps, total,
+                                                     a.tile_live));
     return hipGetLastError();
 }
 

@@ -325,6 +325,11 @@ __global__ __launch_bounds__(256) void empty_states_kernel(const float* __restri
 // tokens in order: gate mode keeps an fp32 running sum of log a and exponentiates it per token,
 // head mode uses the closed form exp(lambda_h * tau), no decay copies q.  Consecutive threads take
 // consecutive key dims, so each token row is one contiguous access.
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void decayed_q_kernel(const T* __restrict__ q, const float* __restrict__ decay,
                                                         T* __restrict__ q_dec, float* __restrict__ total,
@@ -387,6 +392,15 @@ hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64
 }
 
 hipError_t launch_decayed_q(const FwdArgs& a) {
+    if (a.tile_live) {  // no per-tile knowledge here: every tile may be nonzero
+        const int64_t nt = a.B * a.H * (int64_t)a.nseg * ((a.L / a.nseg + 63) / 64);
+        if (nt > 0) {
+            LA_TRACED(a.tr, "tile_live_fill",
+                      fill_u32_kernel<<<(unsigned)((nt + 255) / 256), 256, 0, a.stream>>>(a.tile_live, nt, 0x01010101u));
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
     const int64_t n = a.B * a.H * (int64_t)a.nseg * a.dk;
     if (n == 0 || (!a.q_dec && !a.total)) return hipSuccess;
     const unsigned grid = (unsigned)((n + 255) / 256);

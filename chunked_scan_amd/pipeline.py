@@ -32,6 +32,11 @@ import torch
 from .binding import la_chunk_fwd, la_chunk_fwd_decayed, la_cumdecay, la_state_correct, la_state_scan
 
 
+def _tile_flags(B, H, L, nseg, dev):
+    """Per-64-token-tile liveness flags of q * cumulative decay, one int32 per tile of each segment."""
+    return torch.empty((B, H, nseg, (L // nseg + 63) // 64), dtype=torch.int32, device=dev)
+
+
 def _forward(step, s_in, s_out, totals, nseg, timers):
     """The local forward and the decay quantities the scan and the correction need."""
     B, H, L, dk, dv = step.shape
@@ -39,7 +44,7 @@ def _forward(step, s_in, s_out, totals, nseg, timers):
               subseg_chunks=step.subseg_chunks)
     if step.mode == "gate":
         la_chunk_fwd_decayed(step.q, step.k, step.v, step.decay, s_in, step.o, s_out, step.qd, totals,
-                             timer=timers.get("fwd"), **kw)
+                             step.live, timer=timers.get("fwd"), **kw)
         return
     la_chunk_fwd(step.q, step.k, step.v, step.decay, s_in, step.o, s_out, timer=timers.get("fwd"), **kw)
     if step.mode == "head":
@@ -48,10 +53,11 @@ def _forward(step, s_in, s_out, totals, nseg, timers):
 
 
 def _correct(step, s_recv, nseg, seg_begin, timers):
-    """O += (Q * cumulative decay) S_recv; in gate mode Q * cum is the forward's q_decayed."""
+    """O += (Q * cumulative decay) S_recv; in gate mode Q * cum is the forward's q_decayed, and the
+    tiles where it is exactly zero (the cumulative decay has underflowed) are skipped."""
     if step.mode == "gate":
         la_state_correct(step.qd, None, s_recv, step.o, mode="none", nseg=nseg, seg_begin=seg_begin,
-                         timer=timers.get("corr"))
+                         tile_live=step.live, timer=timers.get("corr"))
     else:
         la_state_correct(step.q, step.decay if step.mode == "head" else None, s_recv, step.o, mode=step.mode,
                          nseg=nseg, seg_begin=seg_begin, timer=timers.get("corr"))
@@ -92,6 +98,7 @@ class DeviceStep:
             self.states[:, :, 0].copy_(s_recv)
         self.totals = torch.ones((B, H, G + 1, dk), dtype=torch.float32, device=dev)
         self.qd = torch.empty_like(q) if mode == "gate" else None  # q times its cumulative decay
+        self.live = _tile_flags(B, H, L, G, dev) if mode == "gate" else None
 
     def run(self, timers: Optional[dict] = None):
         """One step.  ``timers`` optionally maps "fwd", "cum", "scan", "corr" to KernelTimers."""
@@ -126,6 +133,7 @@ class SegmentedForward:
         self.states = torch.empty((B, H, nseg, dk, dv), dtype=torch.float32, device=dev)
         self.totals = torch.empty((B, H, nseg, dk), dtype=torch.float32, device=dev)
         self.qd = torch.empty_like(q) if mode == "gate" else None  # q times its cumulative decay
+        self.live = _tile_flags(B, H, L, nseg, dev) if mode == "gate" else None
 
     def run(self, timers: Optional[dict] = None):
         """One pass.  ``timers`` optionally maps "fwd", "cum", "scan", "corr" to KernelTimers."""

@@ -147,17 +147,22 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float*
  *   total              = Lambda of every segment, as la_cumdecay writes it (segment p of (b,h)
  *                        at total + (b*H + h) * total_stride + p * dk; dense [B,H,nseg,dk] when
  *                        shape->total_stride = 0); or NULL.
+ *   tile_live          = uint32[B,H,nseg,ceil(L/nseg/64)] or NULL: entry i of segment p covers the
+ *                        segment's tokens 64i .. 64i+63.  Zero promises that q_t (*) cum_t is exactly
+ *                        zero on every one of them (the cumulative decay has underflowed for every
+ *                        key dim); nonzero promises nothing.  For la_state_correct_live.
  * Every other argument, and every result la_chunk_fwd writes, is as for la_chunk_fwd.  In gate
- * mode with bf16, dk = dv = 128 and chunk 64 both come out of the forward's own decay
+ * mode with bf16, dk = dv = 128 and chunk 64 all three come out of the forward's own decay
  * preparation (cum = exp2 of an fp32 running sum of log2 a); otherwise one extra streaming pass
  * forms them (gate: exp of an fp32 running sum of log a; head: exp(lambda_h * tau); none: cum = 1,
- * q_decayed = q).  Neither output may overlap any other argument.
+ * q_decayed = q; every tile_live entry nonzero).  No output may overlap any other argument.
  * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_DECAY, LA_ERR_ALIAS,
  * LA_ERR_UNSUPPORTED or LA_ERR_LAUNCH.
  */
 la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, const float* decay,
                                const float* s_in, void* o, float* s_out, void* q_decayed,
-                               float* total, const la_shape* shape, int32_t chunk);
+                               float* total, uint32_t* tile_live, const la_shape* shape,
+                               int32_t chunk);
 
 /*
  * Segmented state scan: the All-Scan of ZeCO reproduced on one GPU (page "ZeCO ...",
@@ -201,6 +206,21 @@ la_status la_state_scan(const float* seg_states, const float* seg_decay, int32_t
  */
 la_status la_state_correct(const void* q, const float* cumdecay, const float* s_recv, void* o,
                            const la_shape* shape);
+
+/*
+ * la_state_correct that may skip the 64-token tiles (of the segments it corrects) whose tile_live
+ * entry is zero: there q_t (*) cum_t is exactly zero, so the correction is exactly zero and O is
+ * bit-identical either way (the decomposition identity's correction term, page "ZeCO ...",
+ * pith_extraction.key_machinery, vanishes where the cumulative decay has underflowed).
+ *   tile_live : uint32[B,H,nseg,ceil(L/nseg/64)] as la_chunk_fwd_decayed writes it for the same
+ *               B, H, L, nseg (all segments, including those before seg_begin), or NULL (no tile
+ *               skipped: exactly la_state_correct).  Read only; must not overlap o.
+ * Every other argument as for la_state_correct.  A zero entry over rows whose q (*) cum is not
+ * zero is a caller error: those rows then miss their correction.
+ * Returns as la_state_correct.
+ */
+la_status la_state_correct_live(const void* q, const float* cumdecay, const float* s_recv, void* o,
+                                const uint32_t* tile_live, const la_shape* shape);
 
 /*
  * Cumulative decay helper (not one of the three core calls; it prepares their decay inputs).

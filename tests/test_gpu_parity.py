@@ -275,16 +275,24 @@ def test_chunk_fwd_decayed(mode, path, L, nseg, subseg):
     d = to_dev(inp)
     kw = dict(mode=w.mode, nseg=nseg, gate_norm=w.gate_norm, subseg_chunks=subseg)
     o0, s0 = lb.la_chunk_fwd(d["q"], d["k"], d["v"], d["decay"], d["s_in"], **kw)
-    o, s, qd, tot = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"], **kw)
+    o, s, qd, tot, live = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"], want_tile_live=True,
+                                                  **kw)
     # each optional output alone
-    _, _, qd_only, none_tot = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"],
-                                                      want_total=False, **kw)
-    _, _, none_qd, tot_only = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"],
-                                                      want_q_decayed=False, **kw)
+    _, _, qd_only, none_tot, _ = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"],
+                                                         want_total=False, **kw)
+    _, _, none_qd, tot_only, _ = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"],
+                                                         want_q_decayed=False, **kw)
+    _, _, _, _, live_only = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"],
+                                                    want_q_decayed=False, want_total=False, want_tile_live=True, **kw)
     torch.cuda.synchronize()
     assert none_tot is None and none_qd is None
     assert torch.equal(o, o0) and torch.equal(s, s0)
-    assert torch.equal(qd_only, qd) and torch.equal(tot_only, tot)
+    assert torch.equal(qd_only, qd) and torch.equal(tot_only, tot) and torch.equal(live_only, live)
+    # a tile flagged zero holds exactly zero rows of q_decayed
+    Ls = L // nseg
+    qz = torch.nn.functional.pad(qd.reshape(w.B, w.H, nseg, Ls, dk), (0, 0, 0, live.shape[-1] * 64 - Ls))
+    nonzero = qz.reshape(w.B, w.H, nseg, -1, 64 * dk).ne(0).any(-1)
+    assert not torch.any(nonzero & (live == 0))
     cref, tref = oracle.cumdecay(w.B, w.H, w.L, w.dk, ORC_MODE[w.mode], host32(inp["decay"]), nseg=nseg,
                                  gate_norm=w.gate_norm)
     ref = host32(inp["q"]).astype(np.float64) * cref
@@ -297,6 +305,33 @@ def test_chunk_fwd_decayed(mode, path, L, nseg, subseg):
     assert np.all(np.abs(got - ref) <= (rnd + 2e-4) * np.abs(ref) + 1e-35)
     t = tot.cpu().double().numpy()
     assert np.max(np.abs(t - tref) / np.maximum(np.abs(tref), 1e-30)) < 2e-4
+
+
+@pytest.mark.parametrize("nseg,seg_begin", [(1, 0), (2, 1)])
+def test_state_correct_live_skips_dead_tiles(nseg, seg_begin):
+    """Gate decay over 4096-token segments: the cumulative decay underflows after ~1.7k tokens, so
+    la_chunk_fwd_decayed flags later tiles zero (here from several internal sub-segments), and
+    la_state_correct_live, which skips them, gives O bit-identical to la_state_correct."""
+    w = W3.scaled(B=1, H=2, L=4096 * nseg, s_in_std=0.05, seed=401 + nseg)
+    note(f"la_state_correct_live gate nseg={nseg} seg_begin={seg_begin}")
+    inp = make_inputs(w, "cpu")
+    d = to_dev(inp)
+    o, _, qd, _, live = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], None, mode="gate", nseg=nseg,
+                                                gate_norm=w.gate_norm, subseg_chunks=4, want_tile_live=True)
+    g = torch.Generator().manual_seed(9)
+    s_recv = (torch.randn((w.B, w.H, nseg - seg_begin, w.dk, w.dv), generator=g) * 0.05).cuda()
+    o1, o2 = o.clone(), o.clone()
+    lb.la_state_correct(qd, None, s_recv, o1, mode="none", nseg=nseg, seg_begin=seg_begin)
+    lb.la_state_correct(qd, None, s_recv, o2, mode="none", nseg=nseg, seg_begin=seg_begin, tile_live=live)
+    torch.cuda.synchronize()
+    dead = int((live[:, :, seg_begin:] == 0).sum())
+    assert dead > 0.3 * live[:, :, seg_begin:].numel(), dead
+    assert torch.equal(o1, o2)
+    # and against the oracle: the correction of q_decayed rows
+    ref = oracle.state_correct(host32(qd).astype(np.float64), np.ones((w.B, w.H, w.L, w.dk)),
+                               s_recv.cpu().double().numpy(), host32(o).astype(np.float64), nseg=nseg,
+                               seg_begin=seg_begin)
+    assert rel_err(o2, ref) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("path", ["f32_d16", "bf16_d128"])
