@@ -54,7 +54,9 @@ __device__ __forceinline__ int pslot(int r, int s) { return s ^ (r & 15); }
 
 // Tiles are taken in (b, h, segment, tile) order; each workgroup walks a contiguous, balanced
 // range of that list (the grid is sized to fill the machine in one round), advancing a cursor
-// instead of dividing per tile.
+// instead of dividing per tile.  Head mode lists only the tiles whose cumulative decay at their
+// first token is nonzero in fp32 (the others contribute exactly zero): a leading run of every
+// segment, whose length depends on the head only, so the ranges balance the work that remains.
 struct Tile {
     int64_t row;   // global row of the tile's first token
     int64_t tau0;  // position of that token inside its segment
@@ -63,6 +65,18 @@ struct Tile {
     float lam;     // head mode: the head's log-decay
 };
 
+// Head mode: tiles of a segment with a nonzero cumulative decay exp(lam (64 ti + 1)) at their first
+// token -- the same test the kernels' factors use; it only falls as ti grows, so a binary search.
+__device__ __forceinline__ int64_t head_live_tiles(float lam, int64_t tps) {
+    int64_t lo = 0, hi = tps;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (expf(lam * (float)(mid * TT + 1)) != 0.f) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
 template <int MODE>
 struct TileWalk {
     int64_t H, L, Ls, tiles_per_seg;
@@ -70,24 +84,65 @@ struct TileWalk {
     const float* cum;
     int64_t t, end;        // position in the tile list and end of this workgroup's range
     int64_t ti, pidx, bh, h;
+    int64_t nl;            // tiles of the current segment in the list (head mode: its live tiles)
+    int64_t nl_lane = 0;   // head mode with H <= 64: live tiles of head `lane`, looked up by shuffle
     // optional liveness flags [(b,h), segment, tile] (0: the tile's q rows are exactly zero), read
-    // 64 tiles of the list at a time into a wave-wide bit mask
+    // 64 tiles of the list at a time into a wave-wide bit mask; head mode skips by its own test
     const uint32_t* flags;
     int64_t wbase = -1;
     uint64_t wmask = 0;
 
+    __device__ int64_t seg_tiles(int64_t hh) const {
+        if (MODE != DECAY_HEAD) return tiles_per_seg;
+        if (H <= 64) return __shfl(nl_lane, (int)hh);
+        return head_live_tiles(cum[hh], tiles_per_seg);
+    }
+
     __device__ TileWalk(int64_t H_, int64_t L_, int nseg_, int seg_begin_, int64_t tps, int64_t total,
                         const float* cum_, const uint32_t* flags_)
         : H(H_), L(L_), Ls(L_ / nseg_), tiles_per_seg(tps), nseg(nseg_), np(nseg_ - seg_begin_),
-          seg_begin(seg_begin_), cum(cum_), flags(flags_) {
-        t = total * blockIdx.x / gridDim.x;
-        end = total * (blockIdx.x + 1) / gridDim.x;
-        const int64_t sp = t / tps;
-        ti = t % tps;
-        pidx = sp % np;
-        bh = sp / np;
-        h = bh % H;
-        skip_dead();
+          seg_begin(seg_begin_), cum(cum_), flags(MODE == DECAY_HEAD ? nullptr : flags_) {
+        if (MODE == DECAY_HEAD) {
+            // per batch entry the list holds np * sum_h live(h) tiles; lane j finds the live tiles of
+            // heads j, j + 64, ...
+            const int lane = threadIdx.x & 63;
+            int64_t per_b = 0;
+            for (int64_t h0 = 0; h0 < H; h0 += 64) {
+                const int64_t v = (h0 + lane < H) ? head_live_tiles(cum[h0 + lane], tps) : 0;
+                if (h0 == 0) nl_lane = v;
+                int64_t sum = v;
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+                per_b += np * sum;
+            }
+            const int64_t nb = total / (np * tps * H);
+            const int64_t live_total = nb * per_b;
+            t = live_total * blockIdx.x / gridDim.x;
+            end = live_total * (blockIdx.x + 1) / gridDim.x;
+            if (t >= end) return;
+            int64_t r = t - (t / per_b) * per_b;
+            bh = (t / per_b) * H;
+            h = 0;
+            nl = seg_tiles(0);
+            while (r >= np * nl) {  // the head holding list position t
+                r -= np * nl;
+                bh++;
+                h++;
+                nl = seg_tiles(h);
+            }
+            pidx = r / nl;
+            ti = r - pidx * nl;
+        } else {
+            t = total * blockIdx.x / gridDim.x;
+            end = total * (blockIdx.x + 1) / gridDim.x;
+            const int64_t sp = t / tps;
+            ti = t % tps;
+            pidx = sp % np;
+            bh = sp / np;
+            h = bh % H;
+            nl = tps;
+            skip_dead();
+        }
     }
     __device__ bool done() const { return t >= end; }
     __device__ Tile tile() const {
@@ -99,10 +154,8 @@ struct TileWalk {
         x.lam = (MODE == DECAY_HEAD) ? cum[h] : 0.f;
         return x;
     }
-    // head mode: tiles whose cumulative decay is exactly zero contribute exactly zero; with flags,
-    // tiles flagged zero likewise.  Called by every lane of a wave with the same state.
+    // tiles flagged zero contribute exactly zero.  Called by every lane of a wave with the same state.
     __device__ bool live() {
-        if (MODE == DECAY_HEAD && expf(cum[h] * (float)(ti * TT + 1)) == 0.f) return false;
         if (!flags) return true;
         if (wbase < 0 || t >= wbase + 64) {  // the walk only moves forward
             wbase = t;
@@ -118,12 +171,16 @@ struct TileWalk {
     }
     __device__ void step() {
         t++;
-        if (++ti == tiles_per_seg) {
+        if (++ti == nl) {
             ti = 0;
             if (++pidx == np) {
                 pidx = 0;
-                bh++;
-                if (++h == H) h = 0;
+                // next (b, h); head mode passes over heads with no live tile
+                do {
+                    bh++;
+                    if (++h == H) h = 0;
+                    if (MODE == DECAY_HEAD) nl = seg_tiles(h);
+                } while (MODE == DECAY_HEAD && nl == 0 && t < end);
             }
         }
     }
@@ -140,11 +197,15 @@ struct TileWalk {
 // ks*16 + kg*8 + jj of value column 32 cw + n32
 __device__ __forceinline__ void load_state_ops(const float* S, int cw, int n32, int kg, bf16x8 (&shi)[8],
                                                bf16x8 (&slo)[8]) {
+    // the lane's offset, hidden from the optimiser: otherwise the 64 per-lane addresses are hoisted
+    // out of the tile loop as loop invariants and spill
+    int lo = kg * 8 * D + 32 * cw + n32;
+    asm volatile("" : "+v"(lo));
 #pragma unroll
     for (int ks = 0; ks < 8; ks++)
 #pragma unroll
         for (int jj = 0; jj < 8; jj++) {
-            const float x = S[(ks * 16 + kg * 8 + jj) * D + 32 * cw + n32];
+            const float x = S[lo + (ks * 16 + jj) * D];
             const __bf16 hi = (__bf16)x;
             shi[ks][jj] = hi;
             slo[ks][jj] = (__bf16)(x - (float)hi);

@@ -307,6 +307,36 @@ def test_chunk_fwd_decayed(mode, path, L, nseg, subseg):
     assert np.max(np.abs(t - tref) / np.maximum(np.abs(tref), 1e-30)) < 2e-4
 
 
+@pytest.mark.parametrize("H", [5, 70])
+def test_state_correct_head_live_ranges(H):
+    """Head-decay correction lists only tiles with a nonzero cumulative decay and balances the
+    workgroups over them: heads with no live tile at all (a = 0, lambda = -inf), heads that never
+    underflow (lambda = 0) and everything between, with more heads than a wave has lanes (70) and
+    fewer (5).  Tokens whose decay is exactly zero keep O bit-identical."""
+    B, P, Ls, d = 2, 3, 640 + 17, 128
+    L = P * Ls
+    note(f"la_state_correct head live ranges H={H}")
+    g = torch.Generator().manual_seed(64 + H)
+    q = torch.randn((B, H, L, d), generator=g).bfloat16()
+    o0 = (torch.randn((B, H, L, d), generator=g) * 0.1).bfloat16()
+    s_recv = torch.randn((B, H, P - 1, d, d), generator=g) * 0.05
+    decay = -torch.rand(H, generator=g) * 0.6
+    decay[0] = 0.0
+    decay[1] = float("-inf")
+    decay[H // 2] = float("-inf")
+    decay[H - 1] = -2.0
+    cum_ref, _ = oracle.cumdecay(B, H, L, d, ORC_MODE["head"], decay.numpy(), nseg=P)
+    ref = oracle.state_correct(host32(q), cum_ref, s_recv.double().numpy(), host32(o0), nseg=P, seg_begin=1)
+    o = o0.cuda()
+    lb.la_state_correct(q.cuda(), decay.cuda(), s_recv.cuda(), o, mode="head", nseg=P, seg_begin=1)
+    torch.cuda.synchronize()
+    o = o.cpu()
+    assert rel_err(o, ref) <= TOL["bf16"]
+    dead = torch.from_numpy(cum_ref.reshape(B, H, L, d)[..., 0] == 0)
+    assert torch.equal(o[dead], o0[dead])
+    assert torch.equal(o[:, :, :Ls], o0[:, :, :Ls])
+
+
 @pytest.mark.parametrize("nseg,seg_begin", [(1, 0), (2, 1)])
 def test_state_correct_live_skips_dead_tiles(nseg, seg_begin):
     """Gate decay over 4096-token segments: the cumulative decay underflows after ~1.7k tokens, so
