@@ -1,0 +1,401 @@
+// chunk_fwd_small.hip -- bf16 matrix-core (MFMA) chunked forward for dk = dv = 32 or 64, chunk 64.
+//
+// The same chunk algebra as the d = 128 kernel (chunk_fwd_pipe.hip), in a simpler shape sized for
+// small heads: one workgroup of 4 waves per (b, h, segment, sub-segment), the chunk's q, k, v (and
+// g) prefetched into registers one chunk ahead and staged into padded LDS tiles with the decay
+// factors folded in.  Per chunk of n <= 64 tokens, with B_i the inclusive in-chunk cumulative
+// log-decay (per key dim in gate mode, lambda*(i+1) in head mode):
+//   P[i][j] = sum_d qbar_i[d] kbar_j[d]     masked to j <= i            (intra-chunk "diagonal")
+//   O       = diag-scaled (Qbar S) + P V                                 (inter + intra)
+//   S      <- diag(exp(B_{n-1})) S + Ktilde^T V,   Ktilde_j = k_j * exp(B_{n-1} - B_j)
+// (ZeCO review page: the diagonal P term, skeptic_critique.concrete_test; the K-bar / Lambda /
+// Gamma vectors, referee_report.minor_comments[3].)  Head and no-decay modes compute P from raw
+// q, k and apply exp(lambda (i - j)) to the scores and exp(lambda (i + 1)) to the rows of Q S, so
+// every factor is <= 1; gate mode folds the per-key-dim decay into qbar = q exp(B_i) and
+// kbar = k exp(-B_j), which bounds each chunk's per-dim log-decay sum as in the d = 128 kernel.
+//
+// Wave roles.  The D / 32 value-column blocks of the outputs and of the state are spread over the
+// four waves: wave w takes column block w % (D / 32) and, of the chunk's two 32-row output blocks,
+// those congruent to w / (D / 32) modulo 4 / (D / 32) (d = 64: one each; d = 32: waves 0 and 1).
+// Each wave keeps the state columns of its block in MFMA accumulators, all D key rows, so waves
+// that share a column block update identical copies: extra matrix-core work, no state traffic
+// through LDS.  The causal score blocks (0,0), (1,0), (1,1) go to waves 0, 2, 3 through LDS.
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int C = 64;     // chunk length
+constexpr int NT = 256;   // lanes per workgroup
+constexpr int PPITCH = 72;  // bf16 row pitch of P
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ bf16x4 lds_tr16(const __bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((__attribute__((address_space(3))) __bf16*)p));
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ u32x4 scale8s(u32x4 w, float f) {
+    const float ff[8] = {f, f, f, f, f, f, f, f};
+    return scale8(w, ff);
+}
+
+template <int D>
+struct SmallSmem {
+    static constexpr int PITCH = D + 8;  // bf16: 16-byte aligned rows, conflict-free 16-byte row reads
+    static constexpr int TILE = C * PITCH;
+    __bf16 q[TILE];   // qbar (gate) or q
+    __bf16 kp[TILE];  // kbar (gate) or k: the K side of P
+    __bf16 kt[TILE];  // ktilde: keys scaled by the decay to the chunk end
+    __bf16 v[TILE];
+    __bf16 p[C * PPITCH];
+};
+template <int D>
+struct SmallSmemGate {
+    float b[C * D];            // in-chunk inclusive cumulative log-decay
+    float el[D];               // exp(B_{n-1}): the chunk's total decay per key dim
+    float tot[(NT / D) * D];   // per-part totals of the cumsum
+};
+
+template <int D, int MODE, bool STATE_ONLY>
+__global__ __launch_bounds__(NT) void small_fwd_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const float* __restrict__ decay, const float* __restrict__ s_in, __bf16* __restrict__ o,
+    float* __restrict__ s_out, int64_t s_out_stride,
+    float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
+    const float* __restrict__ init_state,                            // output pass inputs (scanned)
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm) {
+    constexpr int NCB = D / 32;       // 32-wide column blocks
+    constexpr int WPC = 4 / NCB;      // waves per column block
+    constexpr int KS = D / 16;        // 16-wide k slabs of a D-long contraction
+    constexpr int PR = C * D / 8 / NT;  // 16-byte pieces of a bf16 tile per lane
+    constexpr int PG = C * D / 4 / NT;  // 16-byte pieces of an fp32 g tile per lane
+    using Sm = SmallSmem<D>;
+    constexpr int PITCH = Sm::PITCH;
+    constexpr int PIECES_ROW = D / 8;   // 16-byte pieces per bf16 row
+    __shared__ __attribute__((aligned(16))) Sm sm;
+    __shared__ __attribute__((aligned(16))) SmallSmemGate<D> sg_[1];  // unused outside gate mode
+    SmallSmemGate<D>& sg = sg_[0];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int n32 = lane & 31;
+    const int kg = lane >> 5;
+    const int cb = w % NCB;    // this wave's value-column block
+    const int rank = w / NCB;  // this wave's rank among the waves of that block
+    // output row blocks of this wave: rb = rank, rank + WPC, ... below 2
+    const int64_t u = blockIdx.x;
+    const int gper = STATE_ONLY ? (G - 1) : G;
+    const int g = (int)(u % gper);
+    const int64_t ub = u / gper;  // (bh, seg)
+    const int seg = (int)(ub % nseg);
+    const int64_t bh = ub / nseg;
+    const int64_t h = bh % H;
+    const int64_t Lseg = L / nseg;
+    const int64_t t_begin = (int64_t)seg * Lseg + (int64_t)g * cps * C;
+    const int64_t t_end = min(t_begin + (int64_t)cps * C, (int64_t)(seg + 1) * Lseg);
+    const int64_t row_base = bh * L;
+    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
+
+    // ---- initial state: key rows 32 m + (i / 4) * 8 + kg * 4 + i % 4, value column 32 cb + n32
+    f32x16 S[NCB];
+    {
+        const float* src = nullptr;
+        if (g == 0) {
+            if (seg == 0 && s_in) src = s_in + bh * (int64_t)D * D;
+        } else if (!STATE_ONLY) {
+            src = init_state + (ub * (G - 1) + (g - 1)) * (int64_t)D * D;
+        }
+#pragma unroll
+        for (int m = 0; m < NCB; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                S[m][i] = src ? src[r * D + 32 * cb + n32] : 0.f;
+            }
+    }
+
+    // ---- register prefetch of one chunk (rows past the end read as zero)
+    u32x4 rq[PR], rk[PR], rv[PR];
+    f32x4 rg[MODE == DECAY_GATE ? PG : 1];
+    auto load_chunk = [&](int64_t t0, int n) {
+#pragma unroll
+        for (int r = 0; r < PR; r++) {
+            const int p = tid + NT * r;
+            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+            const int64_t off = (row_base + t0 + row) * D + c8;
+            const bool ok = row < n;
+            if (!STATE_ONLY) rq[r] = ok ? *(const u32x4*)(q + off) : u32x4{0, 0, 0, 0};
+            rk[r] = ok ? *(const u32x4*)(k + off) : u32x4{0, 0, 0, 0};
+            rv[r] = ok ? *(const u32x4*)(v + off) : u32x4{0, 0, 0, 0};
+        }
+        if (MODE == DECAY_GATE) {
+#pragma unroll
+            for (int r = 0; r < PG; r++) {
+                const int p = tid + NT * r;
+                const int row = p / (D / 4), c4 = (p % (D / 4)) * 4;
+                rg[r] = row < n ? *(const f32x4*)(decay + (row_base + t0 + row) * D + c4) : f32x4{0, 0, 0, 0};
+            }
+        }
+    };
+
+    float gate_total = 0.f;  // state pass, gate mode: running log-decay sum of key dim tid (tid < D)
+    const int nchunks = (int)((t_end - t_begin + C - 1) / C);
+    if (nchunks > 0) load_chunk(t_begin, (int)min((int64_t)C, t_end - t_begin));
+
+    for (int c = 0; c < nchunks; c++) {
+        const int64_t t0 = t_begin + (int64_t)c * C;
+        const int n = (int)min((int64_t)C, t_end - t0);
+        __syncthreads();  // the previous chunk is done with every LDS tile
+
+        // ---- stage the prefetched chunk into LDS, folding in the decay factors
+        if (MODE == DECAY_GATE) {
+#pragma unroll
+            for (int r = 0; r < PG; r++) {
+                const int p = tid + NT * r;
+                const int row = p / (D / 4), c4 = (p % (D / 4)) * 4;
+                f32x4 lg;
+#pragma unroll
+                for (int e = 0; e < 4; e++) lg[e] = row < n ? gate_logdecay(rg[r][e], inv_norm) : 0.f;
+                *(f32x4*)(&sg.b[row * D + c4]) = lg;
+            }
+            __syncthreads();
+            {   // inclusive cumsum over the 64 rows per key dim: NT / D parts of R rows each
+                constexpr int NPART = NT / D, R = C / NPART;
+                const int d = tid % D, part = tid / D;
+                float vals[R];
+#pragma unroll
+                for (int i = 0; i < R; i++) vals[i] = sg.b[(part * R + i) * D + d];
+#pragma unroll
+                for (int i = 1; i < R; i++) vals[i] += vals[i - 1];
+                sg.tot[part * D + d] = vals[R - 1];
+                __syncthreads();
+                float off = 0.f;
+                for (int pp = 0; pp < part; pp++) off += sg.tot[pp * D + d];
+#pragma unroll
+                for (int i = 0; i < R; i++) sg.b[(part * R + i) * D + d] = vals[i] + off;
+                __syncthreads();
+                if (tid < D) {
+                    const float bl = sg.b[(n - 1) * D + tid];
+                    sg.el[tid] = expf(bl);
+                    gate_total += bl;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < PR; r++) {
+                const int p = tid + NT * r;
+                const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+                float eb[8], einv[8], et[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float bi = sg.b[row * D + c8 + e];
+                    const float bl = sg.b[(n - 1) * D + c8 + e];
+                    eb[e] = expf(bi);
+                    einv[e] = expf(-bi);
+                    et[e] = expf(bl - bi);
+                }
+                if (!STATE_ONLY) {
+                    *(u32x4*)(&sm.q[row * PITCH + c8]) = scale8(rq[r], eb);
+                    *(u32x4*)(&sm.kp[row * PITCH + c8]) = scale8(rk[r], einv);
+                }
+                *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8(rk[r], et);
+                *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < PR; r++) {
+                const int p = tid + NT * r;
+                const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+                if (!STATE_ONLY) {
+                    *(u32x4*)(&sm.q[row * PITCH + c8]) = rq[r];
+                    *(u32x4*)(&sm.kp[row * PITCH + c8]) = rk[r];
+                }
+                if (MODE == DECAY_HEAD)
+                    *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(rk[r], decay_pow(lam, max(n - 1 - row, 0)));
+                else
+                    *(u32x4*)(&sm.kt[row * PITCH + c8]) = rk[r];
+                *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
+            }
+        }
+        __syncthreads();
+
+        // ---- prefetch the next chunk while this one is computed
+        if (c + 1 < nchunks) load_chunk(t0 + C, (int)min((int64_t)C, t_end - (t0 + C)));
+
+        // ---- V operand of this wave's 32 value columns, for the 4 token slabs (P V and K^T V)
+        bf16x8 vb[4];
+        {
+            const int G16 = lane >> 4, i16 = lane & 15;
+            const int col = 32 * cb + (G16 & 1) * 16 + (i16 & 3) * 4;
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {
+                const int tb = 16 * ks + (G16 >> 1) * 8 + (i16 >> 2);
+                vb[ks] = cat(lds_tr16(&sm.v[tb * PITCH + col]), lds_tr16(&sm.v[(tb + 4) * PITCH + col]));
+            }
+        }
+
+        if (!STATE_ONLY) {
+            // ---- intra-chunk scores: causal 32x32 blocks (0,0), (1,0), (1,1) on waves 0, 2, 3
+            if (w != 1) {
+                const int rb = w >> 1, sb_ = (w == 3) ? 1 : 0;
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++) {
+                    const bf16x8 a = *(const bf16x8*)(&sm.q[(rb * 32 + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 b = *(const bf16x8*)(&sm.kp[(sb_ * 32 + n32) * PITCH + ks * 16 + kg * 8]);
+                    acc = mfma(a, b, acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int row = rb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
+                    const int col = sb_ * 32 + n32;
+                    float val = acc[i];
+                    if (MODE == DECAY_HEAD) val *= decay_pow(lam, max(row - col, 0));
+                    if (col > row) val = 0.f;
+                    sm.p[row * PPITCH + col] = (__bf16)val;
+                }
+            }
+            // the state as bf16 B operands: slab (m, hh) covers key rows 32m + 16hh + {kg*4 + 0..3, 8 + kg*4 + 0..3}
+            bf16x8 sb[2 * NCB];
+#pragma unroll
+            for (int m = 0; m < NCB; m++)
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++) {
+                    bf16x8 x;
+#pragma unroll
+                    for (int j = 0; j < 8; j++) x[j] = (__bf16)S[m][8 * hh + j];
+                    sb[2 * m + hh] = x;
+                }
+            __syncthreads();  // P complete
+
+            // ---- outputs: this wave's column block, its row blocks
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++) {
+                if (rb % WPC != rank % WPC || (WPC > 2 && rank >= 2)) continue;
+                f32x16 acc = {};
+                const __bf16* qrow = &sm.q[(rb * 32 + n32) * PITCH + kg * 4];
+#pragma unroll
+                for (int m = 0; m < NCB; m++)
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++) {
+                        const int d0 = 32 * m + 16 * hh;
+                        const bf16x4 lo = *(const bf16x4*)(qrow + d0);
+                        const bf16x4 hi = *(const bf16x4*)(qrow + d0 + 8);
+                        acc = mfma(cat(lo, hi), sb[2 * m + hh], acc);
+                    }
+                if (MODE == DECAY_HEAD) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const int row = rb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
+                        acc[i] *= decay_pow(lam, row + 1);
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2 * (rb + 1); ks++) {
+                    const bf16x8 a = *(const bf16x8*)(&sm.p[(rb * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
+                    acc = mfma(a, vb[ks], acc);
+                }
+                // accumulator i: row rb*32 + (i/4)*8 + kg*4 + i%4, column 32 cb + n32
+                __bf16* orow = o + (row_base + t0 + rb * 32) * D + 32 * cb + n32;
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int row = (i >> 2) * 8 + kg * 4 + (i & 3);
+                    if (rb * 32 + row < n) orow[row * D] = (__bf16)acc[i];
+                }
+            }
+        }
+
+        // ---- state update: S <- diag(decay over the chunk) S + Ktilde^T V
+        {
+            const float fh = (MODE == DECAY_HEAD) ? decay_pow(lam, n) : 1.f;
+            const int G16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+            for (int m = 0; m < NCB; m++) {
+                if (MODE == DECAY_GATE) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) S[m][i] *= sg.el[32 * m + (i >> 2) * 8 + kg * 4 + (i & 3)];
+                } else if (MODE == DECAY_HEAD) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) S[m][i] *= fh;
+                }
+                const int col = 32 * m + (G16 & 1) * 16 + (i16 & 3) * 4;
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) {
+                    const int tb = 16 * ks + (G16 >> 1) * 8 + (i16 >> 2);
+                    const bf16x8 a = cat(lds_tr16(&sm.kt[tb * PITCH + col]), lds_tr16(&sm.kt[(tb + 4) * PITCH + col]));
+                    S[m] = mfma(a, vb[ks], S[m]);
+                }
+            }
+        }
+    }
+
+    // ---- the final state, from one wave per column block
+    float* dst = nullptr;
+    if (STATE_ONLY) dst = part_state + (ub * (G - 1) + g) * (int64_t)D * D;
+    else if (g == G - 1 && s_out) dst = s_out + bh * s_out_stride + (int64_t)seg * D * D;
+    if (dst && rank == 0) {
+#pragma unroll
+        for (int m = 0; m < NCB; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                dst[r * D + 32 * cb + n32] = S[m][i];
+            }
+    }
+    if (STATE_ONLY && tid < D) {
+        float tot;
+        if (MODE == DECAY_GATE) tot = expf(gate_total);
+        else if (MODE == DECAY_HEAD) tot = decay_pow(lam, (int)(t_end - t_begin));
+        else tot = 1.f;
+        part_decay[(ub * (G - 1) + g) * D + tid] = tot;
+    }
+}
+
+template <int D, int MODE>
+hipError_t launch_small_mode(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
+    const int64_t ub = a.B * a.H * a.nseg;
+    const __bf16* q = (const __bf16*)a.q;
+    const __bf16* k = (const __bf16*)a.k;
+    const __bf16* v = (const __bf16*)a.v;
+    __bf16* o = (__bf16*)a.o;
+    if (G > 1) {
+        LA_TRACED(a.tr, "chunk_fwd_small_state_pass",
+                  small_fwd_kernel<D, MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
+                      q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
+                      a.L, a.nseg, G, cps, a.inv_norm));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream, a.tr);
+        if (e != hipSuccess) return e;
+    }
+    LA_TRACED(a.tr, "chunk_fwd_small_output_pass",
+              small_fwd_kernel<D, MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
+                  q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, nullptr, part_state, a.H, a.L,
+                  a.nseg, G, cps, a.inv_norm));
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_small_d(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
+    switch (a.mode) {
+        case DECAY_HEAD: return launch_small_mode<D, DECAY_HEAD>(a, G, cps, part_state, part_decay);
+        case DECAY_GATE: return launch_small_mode<D, DECAY_GATE>(a, G, cps, part_state, part_decay);
+        default: return launch_small_mode<D, DECAY_NONE>(a, G, cps, part_state, part_decay);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_fwd_small(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
+    if (a.dk == 64) return launch_small_d<64>(a, G, cps, part_state, part_decay);
+    return launch_small_d<32>(a, G, cps, part_state, part_decay);
+}
+
+}  // namespace la

@@ -1,5 +1,5 @@
-// chunk_fwd_split.hip -- the bf16 MFMA forward for dk = dv = 128, chunk = 64: how a segment is
-// spread over the GPU, and the workspace that takes.
+// chunk_fwd_split.hip -- the bf16 MFMA forward for dk = dv in {32, 64, 128}, chunk = 64: how a
+// segment is spread over the GPU, and the workspace that takes.
 //
 // A (b,h) sequence alone offers one serial chain of chunks, far too few workgroups for 256
 // compute units, so each segment is cut into G sub-segments and the linear-decomposition identity
@@ -10,7 +10,7 @@
 //   pass 2 (outputs):  every sub-segment re-runs its chunks from its exact incoming state and
 //          writes O; the last one writes s_out.
 // Pass 2 therefore needs no output correction.  The cost is one extra read of K and V (and g).
-// The kernels themselves are in chunk_fwd_pipe.hip.
+// The kernels themselves are in chunk_fwd_pipe.hip (d = 128) and chunk_fwd_small.hip (d = 32, 64).
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -19,8 +19,7 @@
 namespace la {
 namespace {
 
-constexpr int C = 64;   // chunk length
-constexpr int D = 128;  // dk = dv
+constexpr int C = 64;  // chunk length
 
 // One stream-ordered memory pool per device for the sub-segment workspace; it keeps what it has
 // allocated (release threshold = max), so after the first call no allocation reaches the driver.
@@ -79,12 +78,14 @@ hipError_t launch_chunk_fwd_mfma(const FwdArgs& a) {
         hipMemPool_t pool = workspace_pool(dev);
         if (!pool) return hipErrorOutOfMemory;
         const size_t n = (size_t)(a.B * a.H * a.nseg) * (G - 1);
+        const size_t D = (size_t)a.dk;
         e = hipMallocFromPoolAsync((void**)&part_state, n * D * D * sizeof(float) + n * D * sizeof(float), pool,
                                    a.stream);
         if (e != hipSuccess) return e;
         part_decay = part_state + n * D * D;
     }
-    hipError_t e = launch_chunk_fwd_pipe(a, G, cps, part_state, part_decay);
+    hipError_t e = a.dk == 128 ? launch_chunk_fwd_pipe(a, G, cps, part_state, part_decay)
+                               : launch_chunk_fwd_small(a, G, cps, part_state, part_decay);
     if (part_state) {
         hipError_t f = hipFreeAsync(part_state, a.stream);
         if (e == hipSuccess) e = f;

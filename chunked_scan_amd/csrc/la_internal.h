@@ -81,12 +81,14 @@ struct CorrectArgs {
 // {16,32,64,128}, chunk in {16,32,64}.
 hipError_t launch_chunk_fwd_generic(const FwdArgs& a);
 
-// bf16 MFMA chunked forward for dk = dv = 128, chunk = 64, with intra-GPU sub-segment splitting
-// (chunk_fwd_split.hip), all decay modes.
+// bf16 MFMA chunked forward for dk = dv in {32, 64, 128}, chunk = 64, with intra-GPU sub-segment
+// splitting (chunk_fwd_split.hip), all decay modes.
 hipError_t launch_chunk_fwd_mfma(const FwdArgs& a);
 // Its kernels: G sub-segments of cps chunks; part_state / part_decay the workspace of the
 // sub-segment scan (unused when G == 1).
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
+// The same for dk = dv = 32 or 64 (chunk_fwd_small.hip).
+hipError_t launch_chunk_fwd_small(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
 
 // out[n,p] = diag(lam[n,p]) out[n,p-1] + x[n,p] for n < nstates, p < P.  x may equal out.
 hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64_t nstates, int P,

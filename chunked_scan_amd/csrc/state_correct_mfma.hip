@@ -423,6 +423,142 @@ __global__ __launch_bounds__(NT) void state_correct_gate_kernel(
     }
 }
 
+// ---------------------------------------------------------------- dk = dv = 32 or 64
+
+// Four waves, register-prefetched tiles (one ahead), q (times cum in gate mode) staged into LDS,
+// the fp32 correction back through LDS for a row-major read-modify-write of O.  Wave w computes
+// the 32 x 32 block (value-column block w % (D / 32), token block w / (D / 32)) of Corr^T = S^T Qc^T
+// (d = 32: waves 0 and 1 only); its slice of S^T is held as hi + lo bf16 A operands.
+template <int D, int MODE>
+__global__ __launch_bounds__(NT) void state_correct_small_kernel(
+    const __bf16* __restrict__ q, const float* __restrict__ cum, const float* __restrict__ s_recv,
+    __bf16* __restrict__ o, int64_t H, int64_t L, int nseg, int seg_begin, int64_t state_stride,
+    int64_t tiles_per_seg, int64_t total_tiles, const uint32_t* __restrict__ flags) {
+    constexpr int NCB = D / 32;
+    constexpr int KS = D / 16;
+    constexpr int QP = D + 8;             // bf16 pitch of the staged queries
+    constexpr int CP = D + 4;             // fp32 pitch of the staged correction
+    constexpr int PR = TT * D / 8 / NT;   // 16-byte bf16 pieces of a tile per lane
+    constexpr int PIECES_ROW = D / 8;
+    __shared__ __attribute__((aligned(16))) __bf16 sQ[TT * QP];
+    __shared__ __attribute__((aligned(16))) float sC[TT * CP];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, n32 = lane & 31, kg = lane >> 5;
+    const int cb = w % NCB, ib = w / NCB;
+    const bool active = ib < 2;  // d = 32: waves 2 and 3 compute nothing
+    TileWalk<MODE> walk(H, L, nseg, seg_begin, tiles_per_seg, total_tiles, cum, flags);
+    if (walk.done()) return;
+
+    auto piece_row = [&](int r) { return (tid + NT * r) / PIECES_ROW; };
+    auto piece_col = [&](int r) { return ((tid + NT * r) % PIECES_ROW) * 8; };
+    // tile loads; rows past the tile's end load its last row (their q is zeroed at staging and
+    // their o is never written)
+    u32x4 rq[PR], ro[PR];
+    f32x4 rc[MODE == DECAY_GATE ? 2 * PR : 1];
+    auto load_tile = [&](int64_t row0, int n) {
+#pragma unroll
+        for (int r = 0; r < PR; r++) {
+            const int64_t off = (row0 + min(piece_row(r), n - 1)) * D + piece_col(r);
+            rq[r] = *(const u32x4*)(q + off);
+            ro[r] = *(const u32x4*)(o + off);
+            if (MODE == DECAY_GATE) {
+                rc[2 * r] = *(const f32x4*)(cum + off);
+                rc[2 * r + 1] = *(const f32x4*)(cum + off + 4);
+            }
+        }
+    };
+    auto stage_tile = [&](int n) {
+#pragma unroll
+        for (int r = 0; r < PR; r++) {
+            u32x4 x = rq[r];
+            if (MODE == DECAY_GATE) {
+                const float cf[8] = {rc[2 * r][0], rc[2 * r][1], rc[2 * r][2], rc[2 * r][3],
+                                     rc[2 * r + 1][0], rc[2 * r + 1][1], rc[2 * r + 1][2], rc[2 * r + 1][3]};
+                x = scale8(x, cf);
+            }
+            if (piece_row(r) >= n) x = u32x4{0, 0, 0, 0};
+            *(u32x4*)(sQ + piece_row(r) * QP + piece_col(r)) = x;
+        }
+    };
+    // S^T slice: k-slab ks holds key dims ks*16 + kg*8 + jj of value column 32 cb + n32
+    bf16x8 shi[KS], slo[KS];
+    auto load_state = [&](const float* S) {
+        int lo = kg * 8 * D + 32 * cb + n32;  // hidden from the optimiser: no hoisted address array
+        asm volatile("" : "+v"(lo));
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++) {
+                const float x = S[lo + (ks * 16 + jj) * D];
+                const __bf16 hi = (__bf16)x;
+                shi[ks][jj] = hi;
+                slo[ks][jj] = (__bf16)(x - (float)hi);
+            }
+    };
+
+    int64_t loaded_sid = -1;
+    Tile cur_t = walk.tile();
+    int64_t cur_bh = walk.bh, cur_pidx = walk.pidx;
+    load_tile(cur_t.row, cur_t.n);
+    while (true) {
+        walk.next();  // the next tile's loads go out while this one is multiplied
+        const bool has_next = !walk.done();
+        if (cur_t.sid != loaded_sid) {
+            load_state(s_recv + cur_bh * state_stride + cur_pidx * D * D);
+            loaded_sid = cur_t.sid;
+        }
+        stage_tile(cur_t.n);
+        u32x4 ov[PR];
+#pragma unroll
+        for (int r = 0; r < PR; r++) ov[r] = ro[r];
+        lds_barrier();  // the staged tile is complete and the previous correction has been consumed
+        Tile nxt_t = cur_t;
+        if (has_next) {
+            nxt_t = walk.tile();
+            load_tile(nxt_t.row, nxt_t.n);
+        }
+        if (active) {
+            const int itok = ib * 32 + n32;
+            f32x16 acc = {};
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) {
+                const bf16x8 b = *(const bf16x8*)(sQ + itok * QP + ks * 16 + kg * 8);
+                acc = mfma(shi[ks], b, acc);
+                acc = mfma(slo[ks], b, acc);
+            }
+            const float f = (MODE == DECAY_HEAD) ? expf(cur_t.lam * (float)(cur_t.tau0 + itok + 1)) : 1.f;
+            // accumulator 4 g4 + e is token itok, value column 32 cb + 8 g4 + 4 kg + e
+#pragma unroll
+            for (int g4 = 0; g4 < 4; g4++)
+                *(f32x4*)(sC + itok * CP + 32 * cb + 8 * g4 + 4 * kg) =
+                    f32x4{f * acc[4 * g4], f * acc[4 * g4 + 1], f * acc[4 * g4 + 2], f * acc[4 * g4 + 3]};
+        }
+        lds_barrier();  // correction tile complete; the query tile is no longer read
+#pragma unroll
+        for (int r = 0; r < PR; r++) {
+            const int row = piece_row(r), c8 = piece_col(r);
+            if (row < cur_t.n) {
+                const f32x4 c0 = *(const f32x4*)(sC + row * CP + c8);
+                const f32x4 c1 = *(const f32x4*)(sC + row * CP + c8 + 4);
+                const float cf[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                u32x4 x;
+#pragma unroll
+                for (int hh = 0; hh < 4; hh++) {
+                    const __bf16 lo = (__bf16)(bits_lo_bf16(ov[r][hh]) + cf[2 * hh]);
+                    const __bf16 hi = (__bf16)(bits_hi_bf16(ov[r][hh]) + cf[2 * hh + 1]);
+                    x[hh] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                }
+                *(u32x4*)(o + (cur_t.row + row) * D + c8) = x;
+            }
+        }
+        if (!has_next) break;
+        cur_t = nxt_t;
+        cur_bh = walk.bh;
+        cur_pidx = walk.pidx;
+    }
+}
+
 // One round of resident workgroups on the current device: compute units x workgroups per unit.
 template <typename K>
 int resident_grid(K kernel, int threads, int64_t total_tiles) {
@@ -451,14 +587,25 @@ hipError_t launch_correct(K kernel, int threads, const CorrectArgs& a, int64_t t
     return hipGetLastError();
 }
 
+template <int DS>
+hipError_t launch_small(const CorrectArgs& a, int64_t tps, int64_t total) {
+    switch (a.mode) {
+        case DECAY_HEAD: return launch_correct(state_correct_small_kernel<DS, DECAY_HEAD>, NT, a, tps, total);
+        case DECAY_GATE: return launch_correct(state_correct_small_kernel<DS, DECAY_GATE>, NT, a, tps, total);
+        default: return launch_correct(state_correct_small_kernel<DS, DECAY_NONE>, NT, a, tps, total);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_state_correct(const CorrectArgs& a) {
-    if (!(a.bf16 && a.dk == D && a.dv == D)) return launch_state_correct_generic(a);
+    const bool small = a.bf16 && a.dk == a.dv && (a.dk == 32 || a.dk == 64);
+    if (!(a.bf16 && a.dk == D && a.dv == D) && !small) return launch_state_correct_generic(a);
     const int64_t Ls = a.L / a.nseg;
     const int64_t tps = (Ls + TT - 1) / TT;
     const int64_t total = a.B * a.H * (int64_t)(a.nseg - a.seg_begin) * tps;
     if (total == 0) return hipSuccess;
+    if (small) return a.dk == 64 ? launch_small<64>(a, tps, total) : launch_small<32>(a, tps, total);
     switch (a.mode) {
         case DECAY_HEAD: return launch_correct(state_correct_ws_kernel<DECAY_HEAD>, NT_WS, a, tps, total);
         case DECAY_GATE: return launch_correct(state_correct_gate_kernel, NT, a, tps, total);

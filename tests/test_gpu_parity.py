@@ -73,6 +73,39 @@ def test_bf16_d128(mode, L, subseg):
 
 
 @pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("L,subseg", [(64 * 9 + 17, 0), (64 * 12, 3), (33, 0), (64 * 20 + 5, 8)])
+def test_bf16_small_heads(mode, d, L, subseg):
+    """bf16 MFMA path for dk = dv = 32 and 64 (chunk 64): ragged last chunks, the intra-GPU split
+    (state pass, sub-segment scan, output pass) and a sequence shorter than one chunk."""
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    w = W2.scaled(B=2, H=3, L=L, dk=d, dv=d, decay=decay, s_in_std=0.05, seed=500 + d + L + subseg)
+    note(f"bf16 d{d} chunk64 mode={mode} L={L} subseg_chunks={subseg}")
+    inp = make_inputs(w, "cpu")
+    o_ref, s_ref = oracle_run(inp, w)
+    o, s = _fwd(to_dev(inp), w, subseg=subseg)
+    torch.cuda.synchronize()
+    assert rel_err(o, o_ref) <= TOL["bf16"]
+    assert rel_err(s, s_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("d", [32, 64])
+def test_device_step_small_heads(mode, d):
+    """The device step (G sub-segments, one scan, one correction) at dk = dv = 32 and 64."""
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    w = W2.scaled(B=2, H=3, L=768, dk=d, dv=d, decay=decay, s_in_std=0.05, seed=600 + d)
+    note(f"device step bf16 d{d} mode={mode}")
+    inp = make_inputs(w, "cpu")
+    o_ref, s_ref = oracle_run(inp, w)
+    dv = to_dev(inp)
+    o, s = pipeline.device_step(dv["q"], dv["k"], dv["v"], dv["decay"], dv["s_in"], mode=w.mode, subseg=3)
+    torch.cuda.synchronize()
+    assert rel_err(o, o_ref) <= TOL["bf16"]
+    assert rel_err(s, s_ref[:, :, 0]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
 def test_bf16_generic_other_dims(mode):
     decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
     w = W2.scaled(B=1, H=2, L=300, dk=64, dv=32, decay=decay, chunk=32, s_in_std=0.05, seed=7)
@@ -166,7 +199,7 @@ def test_state_scan_matches_oracle(P, dk, dv):
 
 
 @pytest.mark.parametrize("mode", ["none", "head", "gate"])
-@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64), ("bf16", 32)])
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64), ("bf16", 32), ("bf16", 64)])
 def test_state_correct_matches_oracle(mode, dtype, dk):
     decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
     P = 3
@@ -260,14 +293,15 @@ def test_cumdecay_matches_oracle(mode):
 
 @pytest.mark.parametrize("mode", ["none", "head", "gate"])
 @pytest.mark.parametrize("path,L,nseg,subseg", [("bf16_d128", 64 * 9 + 17, 1, 3), ("bf16_d128", 6 * 200, 6, 0),
-                                                ("bf16_d128", 64 * 20, 2, 2), ("f32_d32", 3 * 150, 3, 0)])
+                                                ("bf16_d128", 64 * 20, 2, 2), ("f32_d32", 3 * 150, 3, 0),
+                                                ("bf16_d64", 64 * 9 + 17, 1, 3)])
 def test_chunk_fwd_decayed(mode, path, L, nseg, subseg):
     """la_chunk_fwd_decayed: o and s_out exactly as la_chunk_fwd; q_decayed = q * cumdecay and total
     = each segment's decay against the oracle.  In gate mode with bf16 d=128 the forward's loaders
     emit them (several sub-segments, a ragged last chunk); elsewhere the separate pass does."""
     decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
     bf = path.startswith("bf16")
-    dk = 128 if bf else 32
+    dk = int(path.split("_d")[1])
     w = W2.scaled(B=2, H=3, L=L, dk=dk, dv=dk, dtype="bf16" if bf else "f32", decay=decay, s_in_std=0.05,
                   seed=300 + L + nseg)
     note(f"la_chunk_fwd_decayed {path} mode={mode} L={L} nseg={nseg} subseg_chunks={subseg}")
