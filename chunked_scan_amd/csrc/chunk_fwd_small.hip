@@ -58,9 +58,11 @@ struct SmallSmem {
 };
 template <int D>
 struct SmallSmemGate {
-    float b[C * D];            // in-chunk inclusive cumulative log-decay
-    float el[D];               // exp(B_{n-1}): the chunk's total decay per key dim
+    float b[C * D];            // in-chunk inclusive cumulative log2-decay
+    float el[D];               // 2^{B_{n-1}}: the chunk's total decay per key dim
     float tot[(NT / D) * D];   // per-part totals of the cumsum
+    float run[D];              // log2 decay from the segment start to the chunk start
+    float cs[D];               // 2^{run}: the decay from the segment start to the chunk start
 };
 
 template <int D, int MODE, bool STATE_ONLY>
@@ -70,7 +72,8 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
     float* __restrict__ s_out, int64_t s_out_stride,
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
     const float* __restrict__ init_state,                            // output pass inputs (scanned)
-    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm) {
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm,
+    __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride, uint32_t* __restrict__ tile_live) {
     constexpr int NCB = D / 32;       // 32-wide column blocks
     constexpr int WPC = 4 / NCB;      // waves per column block
     constexpr int KS = D / 16;        // 16-wide k slabs of a D-long contraction
@@ -146,7 +149,17 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
         }
     };
 
-    float gate_total = 0.f;  // state pass, gate mode: running log-decay sum of key dim tid (tid < D)
+    float gate_total = 0.f;  // state pass, gate mode: running log2-decay sum of key dim tid (tid < D)
+    // gate outputs of la_chunk_fwd_decayed: q times the decay from the segment start, the
+    // segment's total decay and the tile flags; the output pass starts its running decay from the
+    // totals of the sub-segments before it
+    const bool qdec_out = MODE == DECAY_GATE && !STATE_ONLY && (q_dec || total || tile_live);
+    if (qdec_out && tid < D) {
+        float r0 = 0.f;
+        for (int gg = 0; gg < g; gg++) r0 += __builtin_amdgcn_logf(part_decay[(ub * (G - 1) + gg) * D + tid]);
+        sg.run[tid] = r0;
+    }
+    const int64_t tps = (Lseg + C - 1) / C;
     const int nchunks = (int)((t_end - t_begin + C - 1) / C);
     if (nchunks > 0) load_chunk(t_begin, (int)min((int64_t)C, t_end - t_begin));
 
@@ -163,7 +176,7 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
                 const int row = p / (D / 4), c4 = (p % (D / 4)) * 4;
                 f32x4 lg;
 #pragma unroll
-                for (int e = 0; e < 4; e++) lg[e] = row < n ? gate_logdecay(rg[r][e], inv_norm) : 0.f;
+                for (int e = 0; e < 4; e++) lg[e] = row < n ? gate_logdecay(rg[r][e], inv_norm) * LOG2E : 0.f;
                 *(f32x4*)(&sg.b[row * D + c4]) = lg;
             }
             __syncthreads();
@@ -182,11 +195,23 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
 #pragma unroll
                 for (int i = 0; i < R; i++) sg.b[(part * R + i) * D + d] = vals[i] + off;
                 __syncthreads();
+                bool live = false;
                 if (tid < D) {
                     const float bl = sg.b[(n - 1) * D + tid];
-                    sg.el[tid] = expf(bl);
+                    sg.el[tid] = __builtin_amdgcn_exp2f(bl);
                     gate_total += bl;
+                    if (qdec_out) {
+                        const float cs = __builtin_amdgcn_exp2f(sg.run[tid]);
+                        sg.cs[tid] = cs;
+                        sg.run[tid] += bl;
+                        live = cs != 0.f;
+                    }
                 }
+                // the chunk's tile flag: q times the cumulative decay is exactly zero on the whole
+                // chunk when the decay to its start is zero for every key dim (it only shrinks)
+                const int any_live = __syncthreads_or(live);
+                if (qdec_out && tile_live && tid == 0)
+                    tile_live[(bh * nseg + seg) * tps + (int64_t)g * cps + c] = any_live ? 0x01010101u : 0u;
             }
 #pragma unroll
             for (int r = 0; r < PR; r++) {
@@ -196,14 +221,19 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
                     const float bi = sg.b[row * D + c8 + e];
-                    const float bl = sg.b[(n - 1) * D + c8 + e];
-                    eb[e] = expf(bi);
-                    einv[e] = expf(-bi);
-                    et[e] = expf(bl - bi);
+                    eb[e] = __builtin_amdgcn_exp2f(bi);
+                    einv[e] = __builtin_amdgcn_exp2f(-bi);
+                    et[e] = sg.el[c8 + e] * einv[e];
                 }
                 if (!STATE_ONLY) {
                     *(u32x4*)(&sm.q[row * PITCH + c8]) = scale8(rq[r], eb);
                     *(u32x4*)(&sm.kp[row * PITCH + c8]) = scale8(rk[r], einv);
+                    if (q_dec && row < n) {  // q times its cumulative decay from the segment start
+                        float fd[8];
+#pragma unroll
+                        for (int e = 0; e < 8; e++) fd[e] = eb[e] * sg.cs[c8 + e];
+                        *(u32x4*)(q_dec + (row_base + t0) * D + (row * D + c8)) = scale8(rq[r], fd);
+                    }
                 }
                 *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8(rk[r], et);
                 *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
@@ -349,9 +379,11 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
                 dst[r * D + 32 * cb + n32] = S[m][i];
             }
     }
+    if (qdec_out && total && g == G - 1 && tid < D)  // the segment's total decay
+        total[bh * total_stride + (int64_t)seg * D + tid] = __builtin_amdgcn_exp2f(sg.run[tid]);
     if (STATE_ONLY && tid < D) {
         float tot;
-        if (MODE == DECAY_GATE) tot = expf(gate_total);
+        if (MODE == DECAY_GATE) tot = __builtin_amdgcn_exp2f(gate_total);
         else if (MODE == DECAY_HEAD) tot = decay_pow(lam, (int)(t_end - t_begin));
         else tot = 1.f;
         part_decay[(ub * (G - 1) + g) * D + tid] = tot;
@@ -361,6 +393,7 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
 template <int D, int MODE>
 hipError_t launch_small_mode(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
     const int64_t ub = a.B * a.H * a.nseg;
+    const bool fused = MODE == DECAY_GATE;  // q times cumulative decay, totals and tile flags from the staging
     const __bf16* q = (const __bf16*)a.q;
     const __bf16* k = (const __bf16*)a.k;
     const __bf16* v = (const __bf16*)a.v;
@@ -369,7 +402,7 @@ hipError_t launch_small_mode(const FwdArgs& a, int G, int cps, float* part_state
         LA_TRACED(a.tr, "chunk_fwd_small_state_pass",
                   small_fwd_kernel<D, MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
                       q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
-                      a.L, a.nseg, G, cps, a.inv_norm));
+                      a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0, nullptr));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream, a.tr);
@@ -377,8 +410,9 @@ hipError_t launch_small_mode(const FwdArgs& a, int G, int cps, float* part_state
     }
     LA_TRACED(a.tr, "chunk_fwd_small_output_pass",
               small_fwd_kernel<D, MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
-                  q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, nullptr, part_state, a.H, a.L,
-                  a.nseg, G, cps, a.inv_norm));
+                  q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, part_decay, part_state, a.H, a.L,
+                  a.nseg, G, cps, a.inv_norm, fused ? (__bf16*)a.q_dec : nullptr, fused ? a.total : nullptr,
+                  a.total_stride, fused ? a.tile_live : nullptr));
     return hipGetLastError();
 }
 

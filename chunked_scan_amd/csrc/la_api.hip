@@ -202,7 +202,7 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const floa
         if (s_out) e = la::launch_empty_states(s_in, s_out, so_stride, s->B * s->H, s->nseg, s->dk, s->dv, stream, &tr);
     } else if (a.bf16 && a.dk == a.dv && (a.dk == 32 || a.dk == 64 || a.dk == 128) && chunk == 64) {
         e = la::launch_chunk_fwd_mfma(a);
-        fused = a.mode == LA_DECAY_GATE && a.dk == 128;  // the d = 128 gate loaders emit q_dec themselves
+        fused = a.mode == LA_DECAY_GATE;  // the gate kernels emit q_dec, totals and tile flags themselves
     } else {
         e = la::launch_chunk_fwd_generic(a);
     }

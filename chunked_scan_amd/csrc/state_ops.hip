@@ -232,6 +232,44 @@ __global__ __launch_bounds__(256) void cumdecay_gate_scan_kernel(const float* __
     if (total && last) total[x.bh * total_stride + (int64_t)x.p * dk + x.d] = __builtin_amdgcn_exp2f(run * LOG2E);
 }
 
+// The third gate pass writing q times the cumulative decay instead of the decay itself, the
+// segment totals, and the tile flags: a block is one 64-token tile, live when the decay at its
+// start is nonzero for some key dim (the flags were zeroed first; live dims all write the same
+// word).
+template <typename T>
+__global__ __launch_bounds__(256) void decayed_q_gate_scan_kernel(
+    const T* __restrict__ q, const float* __restrict__ g, const float* __restrict__ partial, T* __restrict__ q_dec,
+    float* __restrict__ total, int64_t total_stride, uint32_t* __restrict__ live, int64_t L, int dk, int nseg,
+    int nblk, int64_t nthreads, float inv_norm) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nthreads) return;
+    const GateBlock x = gate_block(i, L, dk, nseg, nblk);
+    float run = partial[i];  // exclusive prefix of this block
+    if (live && __builtin_amdgcn_exp2f(run * LOG2E) != 0.f) live[x.bhp * nblk + x.blk] = 0x01010101u;
+    const float* gp = g + (x.bh * L) * dk + x.d;
+    const T* qp = q + (x.bh * L) * dk + x.d;
+    T* dp = q_dec ? q_dec + (x.bh * L) * dk + x.d : nullptr;
+    const bool last = x.blk == nblk - 1;
+    if (dp || last) {
+        for (int64_t t = x.t0; t < x.t1; t += GBATCH) {
+            float gv[GBATCH], qv[GBATCH];
+#pragma unroll
+            for (int j = 0; j < GBATCH; j++) {
+                const int64_t tt = min(t + j, x.t1 - 1) * dk;
+                gv[j] = gp[tt];
+                qv[j] = dp ? (float)qp[tt] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < GBATCH; j++)
+                if (t + j < x.t1) {
+                    run += gate_logdecay(gv[j], inv_norm);
+                    if (dp) dp[(t + j) * dk] = (T)(qv[j] * __builtin_amdgcn_exp2f(run * LOG2E));
+                }
+        }
+    }
+    if (total && last) total[x.bh * total_stride + (int64_t)x.p * dk + x.d] = __builtin_amdgcn_exp2f(run * LOG2E);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Generic output correction (fp32 arithmetic): block = (b,h,segment, 64-token tile, 32-wide
 // dv slice).  o_t[c] += sum_d q_t[d] cum_t[d] S[d][c].
@@ -320,48 +358,33 @@ __global__ __launch_bounds__(256) void empty_states_kernel(const float* __restri
     s_out[bh * s_out_stride + (int64_t)p * SZ + e] = (p == 0 && s_in) ? s_in[bh * SZ + e] : 0.f;
 }
 
-// q times its cumulative decay from the segment start, and the segment totals, where the forward
-// does not emit them itself.  Thread = one key dim of one (b,h,segment), walking the segment's
-// tokens in order: gate mode keeps an fp32 running sum of log a and exponentiates it per token,
-// head mode uses the closed form exp(lambda_h * tau), no decay copies q.  Consecutive threads take
-// consecutive key dims, so each token row is one contiguous access.
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = v;
 }
 
+// q times its cumulative decay from the segment start, where the forward does not emit it itself.
+// Head and no-decay modes: one thread per element, the closed form exp(lambda_h * tau).
 template <typename T>
-__global__ __launch_bounds__(256) void decayed_q_kernel(const T* __restrict__ q, const float* __restrict__ decay,
-                                                        T* __restrict__ q_dec, float* __restrict__ total,
-                                                        int64_t total_stride, int64_t H, int64_t L, int dk, int nseg,
-                                                        int64_t n, int mode, float inv_norm) {
+__global__ __launch_bounds__(256) void decayed_q_closed_kernel(const T* __restrict__ q, const float* __restrict__ lamh,
+                                                               T* __restrict__ q_dec, int64_t n, int64_t H, int64_t L,
+                                                               int dk, int nseg, int mode) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const int d = (int)(i % dk);
-    const int64_t bhp = i / dk;
-    const int p = (int)(bhp % nseg);
-    const int64_t bh = bhp / nseg;
-    const int64_t Ls = L / nseg;
-    const int64_t r0 = bh * L + (int64_t)p * Ls;  // the segment's first token row
-    const float lam = mode == DECAY_HEAD ? decay[bh % H] : 0.f;
-    float run = 0.f;
-    if (q_dec)
-        for (int64_t t = 0; t < Ls; t++) {
-            const int64_t idx = (r0 + t) * dk + d;
-            float c = 1.f;
-            if (mode == DECAY_GATE) {
-                run += gate_logdecay(decay[idx], inv_norm);
-                c = expf(run);
-            } else if (mode == DECAY_HEAD) {
-                c = expf(lam * (float)(t + 1));
-            }
-            q_dec[idx] = (T)((float)q[idx] * c);
-        }
-    else if (mode == DECAY_GATE)
-        for (int64_t t = 0; t < Ls; t++) run += gate_logdecay(decay[(r0 + t) * dk + d], inv_norm);
-    if (total)
-        total[bh * total_stride + (int64_t)p * dk + d] =
-            mode == DECAY_GATE ? expf(run) : (mode == DECAY_HEAD && Ls > 0) ? expf(lam * (float)Ls) : 1.f;
+    const int64_t row = i / dk;  // (b,h,t)
+    const int64_t tau = row % L % (L / nseg) + 1;
+    const float c = mode == DECAY_HEAD ? expf(lamh[(row / L) % H] * (float)tau) : 1.f;
+    q_dec[i] = (T)((float)q[i] * c);
+}
+
+// Head and no-decay modes: tile flags from the decay at each 64-token tile's first token.
+__global__ __launch_bounds__(256) void tile_live_closed_kernel(const float* __restrict__ lamh,
+                                                               uint32_t* __restrict__ live, int64_t n, int64_t H,
+                                                               int nseg, int64_t tps, int mode) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int64_t tile = i % tps, h = (i / tps / nseg) % H;
+    live[i] = (mode != DECAY_HEAD || expf(lamh[h] * (float)(tile * 64 + 1)) != 0.f) ? 0x01010101u : 0u;
 }
 
 }  // namespace
@@ -391,30 +414,73 @@ hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64
     return hipGetLastError();
 }
 
-hipError_t launch_decayed_q(const FwdArgs& a) {
-    if (a.tile_live) {  // no per-tile knowledge here: every tile may be nonzero
-        const int64_t nt = a.B * a.H * (int64_t)a.nseg * ((a.L / a.nseg + 63) / 64);
-        if (nt > 0) {
-            LA_TRACED(a.tr, "tile_live_fill",
-                      fill_u32_kernel<<<(unsigned)((nt + 255) / 256), 256, 0, a.stream>>>(a.tile_live, nt, 0x01010101u));
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
+namespace {
+
+template <typename T>
+hipError_t decayed_q_typed(const FwdArgs& a) {
+    const int64_t BH = a.B * a.H;
+    const int64_t Ls = a.L / a.nseg;
+    const int64_t tps = (Ls + 63) / 64;
+    const int64_t ntile = BH * a.nseg * tps;
+    hipError_t e = hipSuccess;
+    if (a.mode != DECAY_GATE || Ls == 0) {
+        const int64_t n = BH * a.L * a.dk;
+        if (a.q_dec && n > 0) {
+            LA_TRACED(a.tr, "decayed_q_closed",
+                      decayed_q_closed_kernel<T><<<(unsigned)((n + 255) / 256), 256, 0, a.stream>>>(
+                          (const T*)a.q, a.decay, (T*)a.q_dec, n, a.H, a.L, a.dk, a.nseg, a.mode));
+            if ((e = hipGetLastError()) != hipSuccess) return e;
         }
+        if (a.tile_live && ntile > 0) {
+            LA_TRACED(a.tr, "tile_live_closed",
+                      tile_live_closed_kernel<<<(unsigned)((ntile + 255) / 256), 256, 0, a.stream>>>(
+                          a.decay, a.tile_live, ntile, a.H, a.nseg, tps, a.mode == DECAY_HEAD ? DECAY_HEAD : DECAY_NONE));
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if (a.total)  // closed forms (gate with empty segments: the empty product)
+            e = launch_cumdecay(a.decay, nullptr, a.total, a.total_stride, a.B, a.H, a.L, a.dk, a.nseg,
+                                a.mode == DECAY_GATE ? DECAY_NONE : a.mode, a.inv_norm, a.stream, a.tr);
+        return e;
     }
-    const int64_t n = a.B * a.H * (int64_t)a.nseg * a.dk;
-    if (n == 0 || (!a.q_dec && !a.total)) return hipSuccess;
-    const unsigned grid = (unsigned)((n + 255) / 256);
-    if (a.bf16)
-        LA_TRACED(a.tr, "decayed_q",
-                  decayed_q_kernel<__bf16><<<grid, 256, 0, a.stream>>>(
-                      (const __bf16*)a.q, a.decay, (__bf16*)a.q_dec, a.total, a.total_stride, a.H, a.L, a.dk, a.nseg,
-                      n, a.mode, a.inv_norm));
-    else
-        LA_TRACED(a.tr, "decayed_q",
-                  decayed_q_kernel<float><<<grid, 256, 0, a.stream>>>((const float*)a.q, a.decay, (float*)a.q_dec,
-                                                                      a.total, a.total_stride, a.H, a.L, a.dk,
-                                                                      a.nseg, n, a.mode, a.inv_norm));
-    return hipGetLastError();
+    // gate: block sums of log a, their exclusive prefix, then the pass over q
+    const int nblk = (int)tps;
+    const int64_t nthreads = BH * a.nseg * nblk * a.dk;
+    float* partial = nullptr;
+    e = hipMallocAsync((void**)&partial, sizeof(float) * (size_t)nthreads, a.stream);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)((nthreads + 255) / 256);
+    if (a.tile_live)
+        LA_TRACED(a.tr, "tile_live_fill",
+                  fill_u32_kernel<<<(unsigned)((ntile + 255) / 256), 256, 0, a.stream>>>(a.tile_live, ntile, 0u));
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+        LA_TRACED(a.tr, "cumdecay_gate_blocksum",
+                  cumdecay_gate_blocksum_kernel<<<grid, 256, 0, a.stream>>>(a.decay, partial, a.L, a.dk, a.nseg, nblk,
+                                                                          nthreads, a.inv_norm));
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) {
+        LA_TRACED(a.tr, "cumdecay_gate_prefix",
+                  cumdecay_gate_prefix_kernel<<<(unsigned)(BH * a.nseg * ((a.dk + 31) / 32)), 256, 0, a.stream>>>(
+                      partial, a.dk, nblk));
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) {
+        LA_TRACED(a.tr, "decayed_q_gate_scan",
+                  decayed_q_gate_scan_kernel<T><<<grid, 256, 0, a.stream>>>(
+                      (const T*)a.q, a.decay, partial, (T*)a.q_dec, a.total, a.total_stride, a.tile_live, a.L, a.dk,
+                      a.nseg, nblk, nthreads, a.inv_norm));
+        e = hipGetLastError();
+    }
+    const hipError_t f = hipFreeAsync(partial, a.stream);
+    return e != hipSuccess ? e : f;
+}
+
+}  // namespace
+
+hipError_t launch_decayed_q(const FwdArgs& a) {
+    if (a.B * a.H * (int64_t)a.nseg * a.dk == 0 || (!a.q_dec && !a.total && !a.tile_live)) return hipSuccess;
+    return a.bf16 ? decayed_q_typed<__bf16>(a) : decayed_q_typed<float>(a);
 }
 
 hipError_t launch_cumdecay(const float* decay, float* cum, float* total, int64_t total_stride, int64_t B, int64_t H,

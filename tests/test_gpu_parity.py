@@ -371,13 +371,15 @@ def test_state_correct_head_live_ranges(H):
     assert torch.equal(o[:, :, :Ls], o0[:, :, :Ls])
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("nseg,seg_begin", [(1, 0), (2, 1)])
-def test_state_correct_live_skips_dead_tiles(nseg, seg_begin):
+def test_state_correct_live_skips_dead_tiles(nseg, seg_begin, d):
     """Gate decay over 4096-token segments: the cumulative decay underflows after ~1.7k tokens, so
-    la_chunk_fwd_decayed flags later tiles zero (here from several internal sub-segments), and
+    la_chunk_fwd_decayed flags later tiles zero (d = 128: the forward's loaders, from several
+    internal sub-segments; d = 64: the separate three-pass computation), and
     la_state_correct_live, which skips them, gives O bit-identical to la_state_correct."""
-    w = W3.scaled(B=1, H=2, L=4096 * nseg, s_in_std=0.05, seed=401 + nseg)
-    note(f"la_state_correct_live gate nseg={nseg} seg_begin={seg_begin}")
+    w = W3.scaled(B=1, H=2, L=4096 * nseg, dk=d, dv=d, s_in_std=0.05, seed=401 + nseg)
+    note(f"la_state_correct_live gate d={d} nseg={nseg} seg_begin={seg_begin}")
     inp = make_inputs(w, "cpu")
     d = to_dev(inp)
     o, _, qd, _, live = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], None, mode="gate", nseg=nseg,
