@@ -12,8 +12,9 @@ with the device's segment cut into G sub-segments (G = 16 here, one workgroup ea
 Prints one JSON line.  Per-kernel durations come from HIP events that the library records
 around every kernel on the stream it launches them on (la_trace); the dominant kernel's
 roofline uses its algorithmic bytes (q, k, v read + o written) over its mean duration.
-Per-step statistics (median, mean, std, min) are given warm and cold (a 512 MiB buffer written
-before each step evicts the 256 MB last-level cache).  The head-decay and gate workloads
+Per-step statistics (median, mean, std, min) are given warm and cold (a 512 MiB buffer read
+before each step evicts the 256 MB last-level cache; reading, not writing, so that the step does
+not also pay for writing back someone else's dirty lines).  The head-decay and gate workloads
 (device step, B = 2 and 4) and the 1M-token 64-segment pass are timed alongside, unless
 --no-alongside.  Every workload is warmed up with at least ~20 ms of steps first: the GPU's
 clocks take about 10 ms of sustained work to settle (the plain step runs ~105 us before, ~93 us
@@ -61,7 +62,7 @@ def algorithmic(w, mode_bytes_gate: int):
 
 
 def step_stats(step, steps, stream, scratch=None):
-    """Per-step times (us) with events around each step; with ``scratch``, the buffer is rewritten
+    """Per-step times (us) with events around each step; with ``scratch``, the buffer is read
     before every step so that the step starts with a cold last-level cache."""
     import statistics
 
@@ -71,7 +72,7 @@ def step_stats(step, steps, stream, scratch=None):
     torch.cuda.synchronize()
     for a, b in evs:
         if scratch is not None:
-            scratch.fill_(1.0)
+            scratch.sum()
         a.record(stream)
         step.run()
         b.record(stream)
@@ -206,8 +207,8 @@ def main():
         step = SegmentedForward(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode,
                                 nseg=w.nseg, chunk=w.chunk, gate_norm=w.gate_norm)
     stream = torch.cuda.current_stream()
-    # writing this buffer evicts the 256 MB last-level cache before a "cold" step
-    scratch = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
+    # reading this buffer evicts the 256 MB last-level cache before a "cold" step
+    scratch = torch.ones(512 << 18, dtype=torch.float32, device="cuda")
 
     for _ in range(args.warmup):
         step.run()
@@ -232,7 +233,7 @@ def main():
     kernels, ms_traced = kernel_stats(step, args.steps, stream)
     log("[bench] per kernel: " + ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in kernels.items()))
 
-    # --- cold: the last-level cache evicted before every step (last: the 512 MiB writes between
+    # --- cold: the last-level cache evicted before every step (last: the 512 MiB reads between
     # steps change the GPU's power state for the regions after them)
     cold = step_stats(step, args.steps, stream, scratch)
     log(f"[bench] per step: warm median {warm['median_us']:.1f} us, cold median {cold['median_us']:.1f} us")
