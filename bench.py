@@ -61,6 +61,33 @@ def algorithmic(w, mode_bytes_gate: int):
     return by, fl
 
 
+def kernel_roofline(w, step, kernels):
+    """Adds algorithmic bytes per launch, achieved GB/s and the fraction of the 8 TB/s peak to the
+    forward's output pass, the state scan and the correction (their per-unit figures: q, k, v read
+    and o written (+ g in gate mode) per token-head; P states read and written (+ their decay
+    vectors); q read and o read and written per corrected token-head, plus the incoming states)."""
+    es = 2 if w.dtype == "bf16" else 4
+    bh = w.B * w.H
+    state = w.dk * w.dv * 4
+    nseg = getattr(step, "nseg", None)
+    if nseg is None:  # device step: G sub-segments, scan over G + 1 entries, every token corrected
+        P, corrected, nstates = step.G + 1, w.B * w.H * w.L, step.G
+    else:             # segmented pass: P segments, segments 1.. corrected
+        P, corrected, nstates = nseg, w.B * w.H * (w.L // nseg) * (nseg - 1), nseg - 1
+    fwd = w.B * w.H * w.L * (es * (2 * w.dk + 2 * w.dv) + (4 * w.dk if w.mode == "gate" else 0))
+    scan = bh * P * (2 * state + (4 * w.dk if w.mode != "none" else 0))
+    corr = corrected * es * (w.dk + 2 * w.dv) + bh * nstates * state
+    for name, d in kernels.items():
+        by = fwd if name.endswith("_output_pass") else scan if name == "state_scan" else \
+            corr if name.startswith("state_correct") else None
+        if by is None:
+            continue
+        if name == "state_scan" and d["launches_per_step"] > 1:
+            continue  # more than one scan per step (an internal split): no single figure
+        gbs = by / (d["mean_us"] * 1e-6) / 1e9
+        d.update(algorithmic_bytes=by, gbps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+
+
 def step_stats(step, steps, stream, scratch=None):
     """Per-step times (us) with events around each step; with ``scratch``, the buffer is read
     before every step so that the step starts with a cold last-level cache."""
@@ -231,7 +258,10 @@ def main():
 
     # --- the same steps with HIP events around every kernel (la_trace)
     kernels, ms_traced = kernel_stats(step, args.steps, stream)
-    log("[bench] per kernel: " + ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in kernels.items()))
+    kernel_roofline(w, step, kernels)
+    log("[bench] per kernel: " + ", ".join(f"{n} {d['mean_us']:.1f} us" + (f" ({d['hbm_frac']:.2f} of HBM peak)"
+                                                                         if "hbm_frac" in d else "")
+                                          for n, d in kernels.items()))
 
     # --- cold: the last-level cache evicted before every step (last: the 512 MiB reads between
     # steps change the GPU's power state for the regions after them)
@@ -263,6 +293,7 @@ def main():
             n_al = 10 if wa.nseg > 1 else 50
             st = step_stats(sa, n_al, stream)
             ks, _ = kernel_stats(sa, n_al, stream)
+            kernel_roofline(wa, sa, ks)
             alongside[wa.name] = dict(
                 step=("segmented pass over %d segments" % wa.nseg) if wa.nseg > 1 else "device step",
                 B=wa.B, H=wa.H, L=wa.L, decay=wa.decay, tokens_per_s=round(wa.B * wa.L / (st["median_us"] * 1e-6), 1),
