@@ -94,6 +94,83 @@ __global__ __launch_bounds__(256) void state_scan4_kernel(const float* x, const 
         if (j < nb) ys[(int64_t)(p0 + j) * per_state] = loc[j] + dec[j] * c;
 }
 
+// Vector form of the same scan for 16-byte aligned states with dv % 4 == 0: a thread owns four
+// consecutive elements of one row d (so one decay serves all four) and moves them as one 16-byte
+// load or store per segment.  The P segments are cut into PARTS parts of ceil(P / PARTS) <= PER
+// segments; each part scans its own segments from zero, keeps the running product of its decays,
+// and the parts' affine maps are composed in order through LDS (as in the kernel above).  More
+// parts means more short chains in flight per element, fewer means fewer threads per element.
+template <int PER, int PARTS>
+__global__ __launch_bounds__(256) void state_scan_vec_kernel(const float* x, const float* __restrict__ lam,
+                                                             float* out, int P, int dk, int dv, int64_t per4,
+                                                             int vblocks) {
+    constexpr int EL = 256 / PARTS;  // float4 columns per workgroup
+    __shared__ float4 loc_last[PARTS][EL];
+    __shared__ float dec_last[PARTS][EL];
+    const int el = threadIdx.x % EL, part = threadIdx.x / EL;
+    const int64_t n = blockIdx.x / vblocks;
+    const int64_t e = (int64_t)(blockIdx.x % vblocks) * EL + el;
+    const bool active = e < per4;
+    const int64_t ec = active ? e : per4 - 1;  // inactive lanes read a valid column, write nothing
+    const int d = (int)(ec * 4 / dv);
+    const float4* xs = reinterpret_cast<const float4*>(x) + n * (int64_t)P * per4 + ec;
+    float4* ys = reinterpret_cast<float4*>(out) + n * (int64_t)P * per4 + ec;
+    const float* ls = lam ? lam + n * (int64_t)P * dk + d : nullptr;  // null: no decay
+    const int per = (P + PARTS - 1) / PARTS;
+    const int p0 = part * per, nb = max(0, min(per, P - p0));
+    float4 xb[PER];
+    float lb[PER];
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+        if (j < nb) {
+            const int pp = p0 + j;
+            xb[j] = xs[(int64_t)pp * per4];
+            lb[j] = (ls && pp > 0) ? ls[(int64_t)pp * dk] : 1.f;  // segment 0's decay only meets out[-1] = 0
+        }
+    }
+    // local inclusive scan from zero (kept in xb) and the running product of the decays (in lb)
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+    float dd = 1.f;
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+        if (j < nb) {
+            y.x = lb[j] * y.x + xb[j].x;
+            y.y = lb[j] * y.y + xb[j].y;
+            y.z = lb[j] * y.z + xb[j].z;
+            y.w = lb[j] * y.w + xb[j].w;
+            dd *= lb[j];
+            xb[j] = y;
+            lb[j] = dd;
+        }
+    }
+    float4 c = make_float4(0.f, 0.f, 0.f, 0.f);  // out[p0 - 1]
+    if (PARTS > 1) {
+        loc_last[part][el] = y;
+        dec_last[part][el] = dd;
+        __syncthreads();
+        for (int q = 0; q < part; q++) {
+            const float4 l = loc_last[q][el];
+            const float dq = dec_last[q][el];
+            c.x = dq * c.x + l.x;
+            c.y = dq * c.y + l.y;
+            c.z = dq * c.z + l.z;
+            c.w = dq * c.w + l.w;
+        }
+    }
+    if (!active) return;
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+        if (j < nb) {
+            float4 o = xb[j];
+            o.x += lb[j] * c.x;
+            o.y += lb[j] * c.y;
+            o.z += lb[j] * c.z;
+            o.w += lb[j] * c.w;
+            ys[(int64_t)(p0 + j) * per4] = o;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Cumulative decay.  HEAD and NONE have closed forms; GATE needs a running sum of log a over the
 // segment (below).
@@ -395,7 +472,22 @@ hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64
     const int64_t per_state = (int64_t)dk * dv;
     const int vblocks = (int)((per_state + 255) / 256);
     const unsigned grid = (unsigned)(nstates * vblocks);
-    if (P <= 4)
+    const bool vec = dv % 4 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)out % 16) == 0;
+    // Segment counts up to 40 take the vector scan (one, four or eight parts); 41..64 the four-part
+    // scalar scan, which measured faster there; longer scans the batched chain.
+    if (vec && P <= 40) {
+        const int64_t per4 = per_state / 4;
+        auto vec_launch = [&](auto kern, int parts) {
+            const int vb = (int)((per4 + 256 / parts - 1) / (256 / parts));
+            kern<<<(unsigned)(nstates * vb), 256, 0, stream>>>(x, lam, out, P, dk, dv, per4, vb);
+        };
+        if (P <= 8)
+            LA_TRACED(tr, "state_scan", vec_launch(state_scan_vec_kernel<8, 1>, 1));
+        else if (P <= 20)
+            LA_TRACED(tr, "state_scan", vec_launch(state_scan_vec_kernel<5, 4>, 4));
+        else
+            LA_TRACED(tr, "state_scan", vec_launch(state_scan_vec_kernel<5, 8>, 8));
+    } else if (P <= 4)
         LA_TRACED(tr, "state_scan", state_scan_kernel<4><<<grid, 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state, vblocks));
     else if (P <= 8)
         LA_TRACED(tr, "state_scan", state_scan_kernel<8><<<grid, 256, 0, stream>>>(x, lam, out, P, dk, dv, per_state, vblocks));

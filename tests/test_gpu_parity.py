@@ -169,10 +169,12 @@ def test_device_step_combine(mode, L, subseg):
     assert rel_err(s, s_ref[:, :, 0]) <= TOL["bf16"]
 
 
-# P spans every launch shape: short (<= 4), medium (<= 16), split into four parts (<= 64), long
-# (dk x dv = 480 leaves a partial block of elements)
-@pytest.mark.parametrize("P,dk,dv", [(1, 64, 32), (4, 64, 32), (13, 64, 32), (16, 64, 32), (17, 20, 24), (40, 64, 32),
-                                     (64, 20, 24), (100, 64, 32)])
+# P spans every launch shape: the vector scan in one, four and eight parts (P <= 8, <= 20, <= 40,
+# each edge and a partial block of columns: dk x dv = 480 or 1152), the four-part scalar scan
+# (<= 64), the batched chain (longer)
+@pytest.mark.parametrize("P,dk,dv", [(1, 64, 32), (4, 64, 32), (5, 32, 36), (8, 64, 32), (9, 20, 24), (13, 64, 32),
+                                     (16, 64, 32), (17, 20, 24), (20, 64, 32), (21, 20, 24), (33, 128, 128),
+                                     (40, 64, 32), (41, 64, 32), (64, 20, 24), (100, 64, 32)])
 def test_state_scan_matches_oracle(P, dk, dv):
     note(f"la_state_scan random P={P} dk={dk} dv={dv}")
     g = torch.Generator().manual_seed(5)
