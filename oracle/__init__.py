@@ -11,6 +11,6 @@ file's header for the definition it follows and the passages of the ZeCO review 
 cites.
 """
 from .oracle import (  # noqa: F401
-    NONE, HEAD, GATE, build, lib_path, recurrence, cumdecay, state_scan, state_correct,
+    NONE, HEAD, GATE, build, lib_path, recurrence, recurrence_bwd, cumdecay, state_scan, state_correct,
     default_threads,
 )

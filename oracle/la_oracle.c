@@ -234,3 +234,160 @@ int orc_state_correct(int64_t B, int64_t H, int64_t L, int dk, int dv, int nseg,
     }
     return 0;
 }
+
+/*
+ * Reverse-mode derivative of the same recurrence, token by token in double (the backward pass the
+ * review page lists as a consequence of the forward design, pith_extraction.forward_implications).
+ * For a loss whose gradients with respect to o and to each segment's final state are given
+ * (d_o: [B,H,L,dv]; ds_out: [B,H,nseg,dk,dv] or NULL for zero), the chain rule applied to
+ *     S_t = diag(a_t) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+ * gives, with G_t the total derivative with respect to S_t (walked from the segment's end):
+ *     G_last = ds_out + q_last d_o_last^T,   G_{t-1} = diag(a_t) G_t + q_{t-1} d_o_{t-1}^T,
+ *     dq_t = S_t d_o_t,   dk_t = G_t v_t,   dv_t = G_t^T k_t,
+ *     da_t[d] = sum_c G_t[d,c] S_{t-1}[d,c],   ds_in = diag(a_first) G_first.
+ * The state trajectory S_t of the segment is kept whole (no recomputation).  The decay parameter's
+ * derivative follows from da by the chain rule of its own definition:
+ *     HEAD: a = exp(lambda_h)            -> d lambda_h = sum over b, t, d of da_t[d] a_t[d]
+ *     GATE: a = sigmoid(g)^(1/gate_norm) -> dg_t[d] = da_t[d] a_t[d] (1 - sigmoid(g_t[d])) / gate_norm
+ * Outputs (all double): dq, dk [B,H,L,dk]; dv [B,H,L,dv]; ddecay: [H] (HEAD), [B,H,L,dk] (GATE) or
+ * NULL (NONE, or not wanted); ds_in: [B,H,nseg,dk,dv] (the derivative with respect to each
+ * segment's initial state, s_in for segment 0 and zero for the others) or NULL.
+ * Returns 0, -1 on a bad argument, -2 if a trajectory buffer cannot be allocated.
+ */
+typedef struct {
+    int64_t B, H, L;
+    int dk, dv, nseg, mode;
+    double gate_norm;
+    const float *q, *k, *v, *decay, *d_o;
+    const double *s_in, *ds_out;
+    double *dq, *dk_out, *dv_out, *ddecay, *ds_in;
+    double* head_part; /* one partial d lambda_h per item (HEAD) */
+    int64_t nitems, next;
+    int failed;
+    pthread_mutex_t mu;
+} bwd_job;
+
+static int bwd_item(bwd_job* J, int64_t item, double* traj, double* G, double* a_all) {
+    const int dk = J->dk, dv = J->dv;
+    const int64_t SZ = (int64_t)dk * dv;
+    const int64_t seg = item % J->nseg, bh = item / J->nseg, h = bh % J->H;
+    const int64_t Ls = J->L / J->nseg, t0 = seg * Ls;
+    /* forward: traj[i] = S after i tokens of the segment (traj[0] = initial state) */
+    for (int64_t e = 0; e < SZ; e++) traj[e] = (seg == 0 && J->s_in) ? J->s_in[bh * SZ + e] : 0.0;
+    for (int64_t i = 0; i < Ls; i++) {
+        const int64_t t = t0 + i;
+        const float* kt = J->k + (bh * J->L + t) * dk;
+        const float* vt = J->v + (bh * J->L + t) * dv;
+        double* a = a_all + i * dk;
+        for (int d = 0; d < dk; d++) a[d] = orc_decay(J->mode, J->decay, J->gate_norm, h, bh, J->L, t, dk, d);
+        const double* Sp = traj + i * SZ;
+        double* Sn = traj + (i + 1) * SZ;
+        for (int d = 0; d < dk; d++)
+            for (int c = 0; c < dv; c++) Sn[d * dv + c] = a[d] * Sp[d * dv + c] + (double)kt[d] * (double)vt[c];
+    }
+    /* backward */
+    for (int64_t e = 0; e < SZ; e++) G[e] = J->ds_out ? J->ds_out[(bh * J->nseg + seg) * SZ + e] : 0.0;
+    double head_acc = 0.0;
+    for (int64_t i = Ls - 1; i >= 0; i--) {
+        const int64_t t = t0 + i, row = bh * J->L + t;
+        const float* qt = J->q + row * dk;
+        const float* kt = J->k + row * dk;
+        const float* vt = J->v + row * dv;
+        const float* dot = J->d_o + row * dv;
+        const double* St = traj + (i + 1) * SZ;
+        const double* Sp = traj + i * SZ;
+        const double* a = a_all + i * dk;
+        for (int d = 0; d < dk; d++)
+            for (int c = 0; c < dv; c++) G[d * dv + c] += (double)qt[d] * (double)dot[c];
+        for (int d = 0; d < dk; d++) {
+            double sq = 0.0, sk = 0.0, da = 0.0;
+            for (int c = 0; c < dv; c++) {
+                sq += St[d * dv + c] * (double)dot[c];
+                sk += G[d * dv + c] * (double)vt[c];
+                da += G[d * dv + c] * Sp[d * dv + c];
+            }
+            J->dq[row * dk + d] = sq;
+            J->dk_out[row * dk + d] = sk;
+            if (J->mode == ORC_HEAD) head_acc += da * a[d];
+            if (J->mode == ORC_GATE && J->ddecay) {
+                const double g = (double)J->decay[row * dk + d];
+                const double sig = 1.0 / (1.0 + exp(-g));
+                J->ddecay[row * dk + d] = da * a[d] * (1.0 - sig) / J->gate_norm;
+            }
+        }
+        for (int c = 0; c < dv; c++) {
+            double s = 0.0;
+            for (int d = 0; d < dk; d++) s += G[d * dv + c] * (double)kt[d];
+            J->dv_out[row * dv + c] = s;
+        }
+        for (int d = 0; d < dk; d++)
+            for (int c = 0; c < dv; c++) G[d * dv + c] *= a[d];
+    }
+    if (J->ds_in)
+        for (int64_t e = 0; e < SZ; e++) J->ds_in[(bh * J->nseg + seg) * SZ + e] = G[e];
+    J->head_part[item] = head_acc;
+    return 0;
+}
+
+static void* bwd_worker(void* arg) {
+    bwd_job* J = (bwd_job*)arg;
+    const int64_t Ls = J->L / J->nseg, SZ = (int64_t)J->dk * J->dv;
+    double* traj = (double*)malloc(sizeof(double) * (size_t)((Ls + 1) * SZ));
+    double* G = (double*)malloc(sizeof(double) * (size_t)SZ);
+    double* a = (double*)malloc(sizeof(double) * (size_t)(Ls * J->dk + 1));
+    if (!traj || !G || !a) {
+        pthread_mutex_lock(&J->mu);
+        J->failed = 1;
+        pthread_mutex_unlock(&J->mu);
+    } else {
+        for (;;) {
+            pthread_mutex_lock(&J->mu);
+            int64_t it = J->next++;
+            pthread_mutex_unlock(&J->mu);
+            if (it >= J->nitems) break;
+            bwd_item(J, it, traj, G, a);
+        }
+    }
+    free(traj);
+    free(G);
+    free(a);
+    return NULL;
+}
+
+int orc_recurrence_bwd(int64_t B, int64_t H, int64_t L, int dk, int dv, int nseg,
+                       const float* q, const float* k, const float* v, int mode, const float* decay,
+                       double gate_norm, const double* s_in, const float* d_o, const double* ds_out,
+                       double* dq, double* dk_out, double* dv_out, double* ddecay, double* ds_in,
+                       int nthreads) {
+    if (B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0 || nseg <= 0 || L % nseg) return -1;
+    if (mode != ORC_NONE && mode != ORC_HEAD && mode != ORC_GATE) return -1;
+    if (mode != ORC_NONE && !decay) return -1;
+    if (mode == ORC_GATE && !(gate_norm > 0)) return -1;
+    if (!q || !k || !v || !d_o || !dq || !dk_out || !dv_out) return -1;
+    bwd_job J;
+    memset(&J, 0, sizeof J);
+    J.B = B; J.H = H; J.L = L; J.dk = dk; J.dv = dv; J.nseg = nseg; J.mode = mode;
+    J.gate_norm = gate_norm;
+    J.q = q; J.k = k; J.v = v; J.decay = decay; J.d_o = d_o; J.s_in = s_in; J.ds_out = ds_out;
+    J.dq = dq; J.dk_out = dk_out; J.dv_out = dv_out; J.ddecay = ddecay; J.ds_in = ds_in;
+    J.nitems = B * H * nseg;
+    J.head_part = (double*)calloc((size_t)(J.nitems + 1), sizeof(double));
+    if (!J.head_part) return -2;
+    pthread_mutex_init(&J.mu, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > J.nitems) nthreads = J.nitems > 0 ? (int)J.nitems : 1;
+    pthread_t th[256];
+    int started = 0;
+    for (int i = 1; i < nthreads; i++)
+        if (pthread_create(&th[started], NULL, bwd_worker, &J) == 0) started++;
+    bwd_worker(&J);
+    for (int i = 0; i < started; i++) pthread_join(th[i], NULL);
+    pthread_mutex_destroy(&J.mu);
+    if (mode == ORC_HEAD && ddecay) {
+        for (int64_t h = 0; h < H; h++) ddecay[h] = 0.0;
+        for (int64_t it = 0; it < J.nitems; it++) ddecay[(it / nseg) % H] += J.head_part[it];
+    }
+    free(J.head_part);
+    return J.failed ? -2 : 0;
+}

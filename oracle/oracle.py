@@ -41,7 +41,10 @@ def _load():
         lib.orc_cumdecay.argtypes = [i64, i64, i64, i32, i32, i32, P, f64, P, P]
         lib.orc_state_scan.argtypes = [i64, i64, i32, i32, i32, P, P, P]
         lib.orc_state_correct.argtypes = [i64, i64, i64, i32, i32, i32, i32, P, P, P, P]
-        for f in (lib.orc_recurrence, lib.orc_cumdecay, lib.orc_state_scan, lib.orc_state_correct):
+        lib.orc_recurrence_bwd.argtypes = [i64, i64, i64, i32, i32, i32, P, P, P, i32, P, f64, P, P, P,
+                                           P, P, P, P, P, i32]
+        for f in (lib.orc_recurrence, lib.orc_cumdecay, lib.orc_state_scan, lib.orc_state_correct,
+                  lib.orc_recurrence_bwd):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -94,6 +97,44 @@ def recurrence(q, k, v, mode=NONE, decay=None, s_in=None, nseg=1, gate_norm=16.0
     if rc != 0:
         raise ValueError("orc_recurrence rejected its arguments")
     return o, s_out
+
+
+def recurrence_bwd(q, k, v, d_o, mode=NONE, decay=None, s_in=None, ds_out=None, nseg=1, gate_norm=16.0,
+                   threads=None):
+    """Derivatives of the recurrence, token by token in fp64 (``orc_recurrence_bwd``).
+
+    d_o: [B,H,L,dv] derivative of the loss with respect to o; ds_out: [B,H,nseg,dk,dv] or None
+    (zero) with respect to each segment's final state.  Returns (dq, dk, dv, ddecay, ds_in):
+    dq, dk [B,H,L,dk], dv [B,H,L,dv], ddecay None (NONE) / [H] with respect to lambda_h (HEAD) /
+    [B,H,L,dk] with respect to the raw gate g (GATE), ds_in [B,H,nseg,dk,dv] with respect to each
+    segment's initial state.
+    """
+    q, k, v, d_o = _f32(q), _f32(k), _f32(v), _f32(d_o)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, H, L) and d_o.shape == v.shape
+    dec = None if mode == NONE else _f32(decay)
+    if mode == HEAD:
+        assert dec.shape == (H,)
+    if mode == GATE:
+        assert dec.shape == (B, H, L, dk)
+    si = None if s_in is None else _f64(s_in)
+    if si is not None:
+        assert si.shape == (B, H, dk, dv)
+    so = None if ds_out is None else _f64(ds_out)
+    if so is not None:
+        assert so.shape == (B, H, nseg, dk, dv)
+    dq = np.zeros((B, H, L, dk))
+    dkk = np.zeros((B, H, L, dk))
+    dvv = np.zeros((B, H, L, dv))
+    dd = None if mode == NONE else np.zeros((H,) if mode == HEAD else (B, H, L, dk))
+    ds_in = np.zeros((B, H, nseg, dk, dv))
+    rc = _load().orc_recurrence_bwd(B, H, L, dk, dv, nseg, _ptr(q), _ptr(k), _ptr(v), mode, _ptr(dec),
+                                    float(gate_norm), _ptr(si), _ptr(d_o), _ptr(so), _ptr(dq), _ptr(dkk),
+                                    _ptr(dvv), _ptr(dd), _ptr(ds_in), threads or default_threads())
+    if rc != 0:
+        raise ValueError("orc_recurrence_bwd failed (%d)" % rc)
+    return dq, dkk, dvv, dd, ds_in
 
 
 def cumdecay(B, H, L, dk, mode=NONE, decay=None, nseg=1, gate_norm=16.0):
