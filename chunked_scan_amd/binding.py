@@ -24,7 +24,7 @@ LA_F32, LA_BF16 = 0, 1
 MODES = {"none": 0, "head": 1, "gate": 2}
 STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_SHAPE", -3: "LA_ERR_DTYPE", -4: "LA_ERR_ALIAS",
           -5: "LA_ERR_UNSUPPORTED", -6: "LA_ERR_LAUNCH", -7: "LA_ERR_DECAY"}
-EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_decayed", "la_state_scan", "la_state_correct", "la_state_correct_live",
+EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_decayed", "la_chunk_bwd", "la_state_scan", "la_state_correct", "la_state_correct_live",
            "la_cumdecay", "la_status_str", "la_supported", "la_version")
 
 
@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
         P, S = ctypes.c_void_p, ctypes.POINTER(Shape)
         L.la_chunk_fwd.argtypes = [P, P, P, P, P, P, P, S, ctypes.c_int32]
         L.la_chunk_fwd_decayed.argtypes = [P, P, P, P, P, P, P, P, P, P, S, ctypes.c_int32]
+        L.la_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, S, ctypes.c_int32]
         L.la_state_correct_live.argtypes = [P, P, P, P, P, S]
         L.la_state_scan.argtypes = [P, P, ctypes.c_int32, P, S]
         L.la_state_correct.argtypes = [P, P, P, P, S]
@@ -202,6 +203,48 @@ def la_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optio
     _check("la_chunk_fwd", lib().la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(o),
                                               _ptr(s_out), ctypes.byref(shp), chunk))
     return o, s_out
+
+
+def la_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tensor,
+                 decay: Optional[torch.Tensor] = None, s_in: Optional[torch.Tensor] = None,
+                 ds_out: Optional[torch.Tensor] = None, *, mode: Optional[str] = None, nseg: int = 1,
+                 chunk: int = 64, gate_norm: float = 16.0, want_decay: bool = True, want_ds_in: bool = True,
+                 dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                 dv: Optional[torch.Tensor] = None, stream=None, timer=None):
+    """Backward of la_chunk_fwd.  d_o [B,H,L,dv] (q's dtype) and ds_out [B,H,nseg,dk,dv] f32 or None are
+    the loss's derivatives with respect to o and to each segment's final state.  Returns
+    (dq, dk, dv, d_decay, ds_in): dq, dk [B,H,L,dk] and dv [B,H,L,dv] in q's dtype; d_decay f32 [H]
+    (head decay: with respect to lambda_h) or [B,H,L,dk] (gate: with respect to g) or None; ds_in
+    f32 [B,H,nseg,dk,dv] with respect to each segment's initial state, or None."""
+    B, H, L, dkk = q.shape
+    dvv = v.shape[-1]
+    _dev(q, "q")
+    _dev(k, "k", q.dtype, (B, H, L, dkk))
+    _dev(v, "v", q.dtype, (B, H, L, dvv))
+    _dev(d_o, "d_o", q.dtype, (B, H, L, dvv))
+    m = mode_code(mode, decay)
+    if decay is not None:
+        _dev(decay, "decay", torch.float32)
+    if s_in is not None:
+        _dev(s_in, "s_in", torch.float32, (B, H, dkk, dvv))
+    if ds_out is not None:
+        _dev(ds_out, "ds_out", torch.float32, (B, H, nseg, dkk, dvv))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _dev(dq, "dq", q.dtype, (B, H, L, dkk))
+    _dev(dk, "dk", q.dtype, (B, H, L, dkk))
+    _dev(dv, "dv", q.dtype, (B, H, L, dvv))
+    d_decay = None
+    if want_decay and m != 0:
+        d_decay = torch.empty(decay.shape, dtype=torch.float32, device=q.device)
+    ds_in = torch.empty((B, H, nseg, dkk, dvv), dtype=torch.float32, device=q.device) if want_ds_in else None
+    shp = make_shape(B, H, L, dkk, dvv, nseg=nseg, dtype=_dtype_code(q), mode=m, gate_norm=gate_norm,
+                     stream=_stream(stream), timer=timer)
+    _check("la_chunk_bwd", lib().la_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(d_o),
+                                              _ptr(ds_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_decay),
+                                              _ptr(ds_in), ctypes.byref(shp), chunk))
+    return dq, dk, dv, d_decay, ds_in
 
 
 def la_chunk_fwd_decayed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch.Tensor] = None,

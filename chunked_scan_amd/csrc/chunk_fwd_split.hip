@@ -21,7 +21,9 @@ namespace {
 
 constexpr int C = 64;  // chunk length
 
-// One stream-ordered memory pool per device for the sub-segment workspace; it keeps what it has
+}  // namespace
+
+// One stream-ordered memory pool per device for temporary workspace; it keeps what it has
 // allocated (release threshold = max), so after the first call no allocation reaches the driver.
 hipMemPool_t workspace_pool(int dev) {
     static std::mutex mu;
@@ -42,8 +44,6 @@ hipMemPool_t workspace_pool(int dev) {
     }
     return pools[dev];
 }
-
-}  // namespace
 
 // Sub-segments: about 256 workgroups in total (one round on the compute units), at least 4
 // chunks each, unless the caller fixes the sub-segment length.

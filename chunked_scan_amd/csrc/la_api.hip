@@ -330,3 +330,64 @@ la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const l
 }
 
 }  // extern "C"
+
+extern "C" {
+
+la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
+                       const void* d_o, const float* ds_out, void* dq, void* dk, void* dv, float* d_decay,
+                       float* ds_in, const la_shape* s, int32_t chunk) {
+    la_status st = check_common(s);
+    if (st != LA_OK) return st;
+    if (chunk <= 0 || s->state_stride < 0) return LA_ERR_SHAPE;
+    const int64_t per_seg = (int64_t)s->dk * s->dv;
+    if (s->state_stride && s->state_stride < (int64_t)s->nseg * per_seg) return LA_ERR_SHAPE;
+    if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
+    if ((st = check_dtype(s)) != LA_OK) return st;
+    if ((st = check_decay_mode(s)) != LA_OK) return st;
+    if (s->decay_mode == LA_DECAY_NONE && (decay || d_decay)) return LA_ERR_DECAY;
+    const int64_t BH = s->B * s->H;
+    const int64_t nqk = BH * s->L * s->dk;
+    const int64_t nv = BH * s->L * s->dv;
+    if (nqk > 0 && (!q || !k || !v || !d_o || !dq || !dk || !dv)) return LA_ERR_NULL;
+    if (s->decay_mode == LA_DECAY_HEAD && s->H > 0 && !decay) return LA_ERR_NULL;
+    if (s->decay_mode == LA_DECAY_GATE && nqk > 0 && !decay) return LA_ERR_NULL;
+    const size_t es = esize(s->in_dtype);
+    const int64_t sstride = s->state_stride ? s->state_stride : (int64_t)s->nseg * per_seg;
+    const size_t st_bytes = BH > 0 ? sizeof(float) * (size_t)((BH - 1) * sstride + s->nseg * per_seg) : 0;
+    const Span ins[] = {{q, es * nqk},
+                        {k, es * nqk},
+                        {v, es * nv},
+                        {decay, decay ? decay_bytes(s) : 0},
+                        {s_in, s_in ? sizeof(float) * (size_t)(BH * per_seg) : 0},
+                        {d_o, es * nv},
+                        {ds_out, ds_out ? st_bytes : 0}};
+    const Span outs[] = {{dq, es * nqk},
+                         {dk, es * nqk},
+                         {dv, es * nv},
+                         {d_decay, d_decay ? decay_bytes(s) : 0},
+                         {ds_in, ds_in ? st_bytes : 0}};
+    for (const Span& o : outs) {
+        for (const Span& i : ins)
+            if (overlap(o, i)) return LA_ERR_ALIAS;
+        for (const Span& p : outs)
+            if (&p != &o && overlap(o, p)) return LA_ERR_ALIAS;
+    }
+    if ((st = check_trace(s)) != LA_OK) return st;
+    la::Tracer tr = make_tracer(s);
+    const bool head_grad = s->decay_mode == LA_DECAY_HEAD && d_decay && s->H > 0;
+    if (BH * s->nseg == 0 && !head_grad) return LA_OK;
+    la::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.decay = decay; a.s_in = s_in; a.d_o = d_o; a.ds_out = ds_out;
+    a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.d_decay = d_decay; a.ds_in = ds_in;
+    a.state_stride = sstride;
+    a.B = s->B; a.H = s->H; a.L = s->L;
+    a.dk = s->dk; a.dv = s->dv; a.nseg = s->nseg; a.chunk = chunk;
+    a.bf16 = s->in_dtype == LA_BF16;
+    a.mode = s->decay_mode;
+    a.inv_norm = s->decay_mode == LA_DECAY_GATE ? 1.f / s->gate_norm : 1.f;
+    a.stream = (hipStream_t)s->stream;
+    a.tr = &tr;
+    return from_hip(la::launch_chunk_bwd_generic(a));
+}
+
+}  // extern "C"

@@ -77,6 +77,36 @@ struct CorrectArgs {
     const uint32_t* tile_live = nullptr;  // optional: [B,H,nseg,ceil(L/nseg/64)]; 0 = skip the tile (q rows zero)
 };
 
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* decay;
+    const float* s_in;
+    const void* d_o;
+    const float* ds_out;   // [b,h] blocks of state_stride elements, segment p at p * dk * dv; may be null
+    void* dq;
+    void* dk_out;
+    void* dv_out;
+    float* d_decay;        // HEAD: [H]; GATE: [B,H,L,dk]; may be null
+    float* ds_in;          // same layout as ds_out; may be null
+    int64_t state_stride;
+    int64_t B, H, L;
+    int dk, dv, nseg, chunk;
+    bool bf16;
+    int mode;
+    float inv_norm;
+    hipStream_t stream;
+    Tracer* tr;
+};
+
+// Stream-ordered workspace pool of a device (chunk_fwd_split.hip).
+hipMemPool_t workspace_pool(int dev);
+
+// Chunked backward with fp32 arithmetic on VALU (chunk_bwd_generic.hip): every shape the generic
+// forward takes.
+hipError_t launch_chunk_bwd_generic(const BwdArgs& a);
+
 // Generic chunked forward: fp32 arithmetic on VALU, q/k/v/o in f32 or bf16, dk, dv in
 // {16,32,64,128}, chunk in {16,32,64}.
 hipError_t launch_chunk_fwd_generic(const FwdArgs& a);

@@ -107,3 +107,19 @@ def make_inputs(w: Workload, device: str = "cpu", seed: Optional[int] = None) ->
         raise ValueError(w.decay)
     s_in = normal((w.B, w.H, w.dk, w.dv), w.s_in_std) if w.s_in_std > 0 else None
     return dict(q=q, k=k, v=v, decay=decay, s_in=s_in)
+
+
+def make_grads(w: Workload, nseg: int = 1, device: str = "cpu", seed: Optional[int] = None,
+               ds_out_std: float = 1.0) -> dict:
+    """Draw the incoming derivatives of a backward pass for workload ``w``: d_o [B,H,L,dv] ~ N(0, 1)
+    in the storage dtype and ds_out [B,H,nseg,dk,dv] ~ N(0, ds_out_std) float32 (None when
+    ds_out_std is 0), from their own generator (default seed: the workload's seed + 1000)."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed((w.seed + 1000) if seed is None else seed)
+    d_o = torch.randn((w.B, w.H, w.L, w.dv), generator=g, device=dev, dtype=torch.float32).to(torch_dtype(w))
+    ds_out = None
+    if ds_out_std > 0:
+        ds_out = torch.randn((w.B, w.H, nseg, w.dk, w.dv), generator=g, device=dev, dtype=torch.float32)
+        ds_out.mul_(ds_out_std)
+    return dict(d_o=d_o, ds_out=ds_out)

@@ -165,6 +165,39 @@ la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, cons
                                int32_t chunk);
 
 /*
+ * Backward pass of la_chunk_fwd: the derivatives of a loss with respect to q, k, v, the decay
+ * parameter and each segment's initial state, given its derivatives with respect to o and to each
+ * segment's final state (the backward pass that the ZeCO review page lists as a consequence of the
+ * forward design, pith_extraction.forward_implications; it runs the chunk recurrence in reverse for
+ * the state derivative next to a forward recomputation of the states).  With G_t the derivative
+ * with respect to S_t, walked from the segment's end (G = ds_out there):
+ *     dq_t = S_t d_o_t,   dk_t = G_t v_t,   dv_t = G_t^T k_t,   ds_in = diag(a_first) G_first,
+ * and for the decay parameter the chain rule through every a_t it sets.  Segments are independent
+ * sequences exactly as in la_chunk_fwd (segment 0 from s_in, the others from zero).
+ *
+ *   q, k, v, decay, s_in : as passed to la_chunk_fwd (read only; the states are recomputed).
+ *   d_o    : [B,H,L,dv] in_dtype, derivative with respect to o (read only).
+ *   ds_out : float, derivative with respect to each segment's final state, in the s_out layout of
+ *            la_chunk_fwd (state_stride), or NULL for zero.
+ *   dq, dk : [B,H,L,dk] in_dtype, written.        dv : [B,H,L,dv] in_dtype, written.
+ *   d_decay: NONE: must be NULL.  HEAD: float[H], the derivative with respect to lambda_h summed
+ *            over batch, segments, tokens and key dims.  GATE: float[B,H,L,dk], the derivative with
+ *            respect to the raw gate g.  NULL skips it (and its workspace).
+ *   ds_in  : float, derivative with respect to each segment's initial state (segment 0's is s_in;
+ *            the others' is what a backward state scan carries between segments), in the
+ *            state_stride layout, or NULL.
+ *   chunk  : 16, 32 or 64.
+ * No output may overlap an input or another output.  Arithmetic is fp32 with fp32 accumulation;
+ * bf16 outputs are rounded once, to nearest even.  May allocate temporary device workspace from
+ * the same stream-ordered pool as la_chunk_fwd (a float per token and key dim in gate mode).
+ * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_DECAY, LA_ERR_ALIAS,
+ * LA_ERR_UNSUPPORTED or LA_ERR_LAUNCH.
+ */
+la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float* decay,
+                       const float* s_in, const void* d_o, const float* ds_out, void* dq, void* dk,
+                       void* dv, float* d_decay, float* ds_in, const la_shape* shape, int32_t chunk);
+
+/*
  * Segmented state scan: the All-Scan of ZeCO reproduced on one GPU (page "ZeCO ...",
  * pith_extraction.key_machinery: each device applies the update
  * S_p = (segment decay) * S_{p-1} + S_local,p to the state it receives and passes the result on;

@@ -1,0 +1,127 @@
+"""GPU parity of the backward pass (la_chunk_bwd) against the fp64 oracle's token-by-token
+derivatives (oracle.recurrence_bwd), on the same seeded inputs.
+
+The kernels form the decay derivative from q * dq - k * dk and reverse running sums; the oracle
+takes it from the definition (da_t = rowsum(G_t * S_{t-1}) and the chain rule), so these tests
+also check that identity.  Sizes span several chunks, a ragged last chunk, both slicings of the
+state (dk, dv up to 128) and two segments.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_scan_amd import binding as lb
+from chunked_scan_amd.inputs import WORKLOADS, make_grads, make_inputs
+
+from gpu_util import ORC_MODE, TOL, host32, note, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W0 = WORKLOADS[0]
+# The decay derivative is formed from q dq - k dk, whose terms largely cancel: d lambda_h sums them
+# (t - t0 + 1)-weighted over whole segments (in fp64), the gate derivative takes reverse running sums
+# (in fp32).  The ~1e-7 relative rounding of dq and dk is magnified by that cancellation: measured up
+# to 7.4e-6 of max|ref| for d lambda_h at L = 192..2048 (1e-6 for the gate), hence 5e-5 here.
+TOL_DECAY = {"f32": 5e-5, "bf16": 5e-5}
+
+
+def _case(mode, dtype, dk, dv, L, chunk, nseg, seed, B=2, H=2, s_in=True, ds_out=True):
+    decay = {"none": "none", "head": "head_uniform", "gate": "gate"}[mode]
+    w = W0.scaled(B=B, H=H, L=L, dk=dk, dv=dv, decay=decay, chunk=chunk, dtype=dtype, seed=seed,
+                  qkv_std=1.0 / np.sqrt(dk), s_in_std=0.1 if s_in else 0.0)
+    inp = make_inputs(w, "cpu")
+    gr = make_grads(w, nseg=nseg, ds_out_std=1.0 if ds_out else 0.0)
+    return w, inp, gr
+
+
+def _oracle(w, inp, gr, nseg):
+    s_in = host32(inp["s_in"])
+    ds_out = host32(gr["ds_out"])
+    return oracle.recurrence_bwd(host32(inp["q"]), host32(inp["k"]), host32(inp["v"]), host32(gr["d_o"]),
+                                 ORC_MODE[w.mode], host32(inp["decay"]),
+                                 None if s_in is None else s_in.astype(np.float64),
+                                 None if ds_out is None else ds_out.astype(np.float64), nseg=nseg,
+                                 gate_norm=w.gate_norm)
+
+
+def _gpu(w, inp, gr, nseg):
+    d = to_dev(inp)
+    g = to_dev(gr)
+    out = lb.la_chunk_bwd(d["q"], d["k"], d["v"], g["d_o"], d["decay"], d["s_in"], g["ds_out"], mode=w.mode,
+                          nseg=nseg, chunk=w.chunk, gate_norm=w.gate_norm)
+    torch.cuda.synchronize()
+    return out
+
+
+def _compare(got, ref, dtype, mode):
+    names = ("dq", "dk", "dv", "d_decay", "ds_in")
+    for name, g, r in zip(names, got, ref):
+        if name == "d_decay":
+            if mode == "none":
+                assert g is None and r is None
+                continue
+            err = rel_err(g, r)
+            assert err <= TOL_DECAY[dtype], (name, err)
+        else:
+            err = rel_err(g, r)
+            assert err <= TOL[dtype], (name, err)
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("dk,dv,L,chunk,nseg", [(16, 16, 200, 16, 1), (32, 64, 301, 32, 1), (64, 32, 130, 64, 2),
+                                                 (128, 128, 160, 64, 1), (16, 128, 154, 32, 2)])
+def test_bwd_fp32(mode, dk, dv, L, chunk, nseg):
+    note(f"la_chunk_bwd fp32 mode={mode} dk={dk} dv={dv} L={L} chunk={chunk} nseg={nseg}")
+    w, inp, gr = _case(mode, "f32", dk, dv, L, chunk, nseg, seed=300 + dk + L)
+    _compare(_gpu(w, inp, gr, nseg), _oracle(w, inp, gr, nseg), "f32", mode)
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("d,L,nseg", [(128, 192, 1), (64, 256, 2), (32, 130, 1)])
+def test_bwd_bf16(mode, d, L, nseg):
+    note(f"la_chunk_bwd bf16 mode={mode} d={d} L={L} nseg={nseg}")
+    w, inp, gr = _case(mode, "bf16", d, d, L, 64, nseg, seed=400 + d + L)
+    _compare(_gpu(w, inp, gr, nseg), _oracle(w, inp, gr, nseg), "bf16", mode)
+
+
+@pytest.mark.parametrize("mode", ["head", "gate"])
+def test_bwd_without_optional_terms(mode):
+    """No s_in, no ds_out, and the decay / ds_in outputs not requested."""
+    note(f"la_chunk_bwd no s_in / ds_out, mode={mode}")
+    w, inp, gr = _case(mode, "f32", 32, 32, 96, 32, 1, seed=77, s_in=False, ds_out=False)
+    ref = _oracle(w, inp, gr, 1)
+    d = to_dev(inp)
+    g = to_dev(gr)
+    dq, dk, dv, dd, ds_in = lb.la_chunk_bwd(d["q"], d["k"], d["v"], g["d_o"], d["decay"], None, None, mode=w.mode,
+                                            chunk=32, want_decay=False, want_ds_in=False)
+    torch.cuda.synchronize()
+    assert dd is None and ds_in is None
+    for got, r in zip((dq, dk, dv), ref[:3]):
+        assert rel_err(got, r) <= TOL["f32"]
+
+
+def test_bwd_empty_and_zero_length():
+    """L = 0: ds_in = ds_out, the head-decay derivative is zero; B = 0: zero derivative."""
+    note("la_chunk_bwd empty shapes")
+    w, inp, gr = _case("head", "f32", 16, 16, 0, 16, 2, seed=5)
+    out = _gpu(w, inp, gr, 2)
+    assert torch.equal(out[4].cpu(), gr["ds_out"])
+    assert torch.count_nonzero(out[3]) == 0
+    w, inp, gr = _case("head", "f32", 16, 16, 32, 16, 1, seed=6, B=0)
+    out = _gpu(w, inp, gr, 1)
+    assert out[3].shape == (2,) and torch.count_nonzero(out[3]) == 0
+
+
+def test_bwd_chunk_invariance():
+    """The chunk length changes the rounding order only."""
+    note("la_chunk_bwd chunk 16 / 32 / 64 agree")
+    w, inp, gr = _case("gate", "f32", 32, 32, 192, 64, 1, seed=88)
+    ref = _oracle(w, inp, gr, 1)
+    for c in (16, 32, 64):
+        d = to_dev(inp)
+        g = to_dev(gr)
+        got = lb.la_chunk_bwd(d["q"], d["k"], d["v"], g["d_o"], d["decay"], d["s_in"], g["ds_out"], mode="gate",
+                              chunk=c, gate_norm=w.gate_norm)
+        torch.cuda.synchronize()
+        _compare(got, ref, "f32", "gate")
