@@ -1,0 +1,570 @@
+// chunk_bwd_mfma.hip -- bf16 matrix-core (MFMA) backward pass for dk = dv = 128, chunk 64, with no
+// decay or one decay per head (the backward pass the ZeCO review page lists as a consequence of the
+// forward design, pith_extraction.forward_implications).  With a scalar decay per head the weight
+// of token j in output t is a^{t-j} whatever the key dim.
+//
+// dq runs forwards in time with the forward state S (dq_t = S_t d_o_t); dk and dv run backwards
+// with the state derivative D (G_t of the recurrence).  Each segment is split into G sub-segments
+// so that about 256 workgroups share the work; the decomposition identity of the same page
+// (pith_extraction.key_machinery) joins them: a state pass leaves each sub-segment's local state
+// (forwards: from zero, sub-segment 0 from s_in) or local derivative (backwards: from zero, the last
+// sub-segment from ds_out), a scan over them with each sub-segment's total decay (in reverse order
+// for D) gives every sub-segment its exact incoming state or derivative, and the output pass walks
+// each sub-segment from it.  Per chunk of n tokens:
+//   forwards (S = the state before the chunk):
+//     P'[i][j] = d_o_i . v_j a^{i-j}  (j <= i),      dq_i = sum_j P'[i][j] k_j + a^{i+1} S d_o_i
+//     S <- a^n S + sum_j a^{n-1-j} k_j v_j^T
+//   backwards (D = the derivative at the chunk's end):
+//     P'[i][j] as above, P[i][j] = q_i . k_j a^{i-j}  (j <= i)
+//     dk_j = sum_{i>=j} P'[i][j] q_i + a^{n-1-j} D v_j,   dv_j = sum_{i>=j} P[i][j] d_o_i + a^{n-1-j} D^T k_j
+//     D <- a^n D + sum_i a^{i+1} q_i d_o_i^T
+// The decay derivative is not formed here: written through q . dq - k . dk its terms cancel by a
+// factor that grows with the sequence length over the decay length, which the bf16 operands of the
+// matrix-core products (scores, state) cannot carry; callers that ask for it take the fp32 path.
+//
+// Wave roles (both directions): wave w keeps value columns 32w..32w+31 of S or D (all 128 key rows)
+// in MFMA accumulators and computes the 32-wide column block w of dq / dk / dv; the causal 32x32
+// score blocks are shared out; the state's transpose reaches the products that need it through a
+// bf16 copy in LDS.
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int C = 64;          // chunk length
+constexpr int D = 128;         // head dim (dk = dv)
+constexpr int NT = 256;        // lanes per workgroup
+constexpr int PITCH = D + 8;   // bf16 row pitch of the tiles: 16-byte aligned, conflict-free rows
+constexpr int PPITCH = C + 8;  // bf16 row pitch of the transposed score tiles
+constexpr int TILE = C * PITCH;
+constexpr int PR = C * D / 8 / NT;  // 16-byte pieces of a bf16 chunk tile per lane (4)
+constexpr int PIECES_ROW = D / 8;
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ bf16x4 lds_tr16(const __bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((__attribute__((address_space(3))) __bf16*)p));
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ u32x4 scale8s(u32x4 w, float f) {
+    const float ff[8] = {f, f, f, f, f, f, f, f};
+    return scale8(w, ff);
+}
+// Operand of 16 consecutive tile rows (the contraction index) and 32 columns starting at col0,
+// read transposed: element e of lane (G16, i16) is tile[16 ks + (G16 >> 1) 8 + (i16 >> 2) + 4 (e >> 2)]
+// [col0 + (G16 & 1) 16 + (i16 & 3) 4 + (e & 3)].
+__device__ __forceinline__ bf16x8 tr_operand(const __bf16* tile, int pitch, int ks, int col0, int lane) {
+    const int G16 = lane >> 4, i16 = lane & 15;
+    const int col = col0 + (G16 & 1) * 16 + (i16 & 3) * 4;
+    const int tb = 16 * ks + (G16 >> 1) * 8 + (i16 >> 2);
+    return cat(lds_tr16(&tile[tb * pitch + col]), lds_tr16(&tile[(tb + 4) * pitch + col]));
+}
+
+struct BwdSmem {
+    __bf16 q[TILE];    // q
+    __bf16 qs[TILE];   // q_i a^{i+1} (head mode; the D update)
+    __bf16 k[TILE];
+    __bf16 v[TILE];
+    __bf16 o[TILE];    // d_o
+    __bf16 dm[D * PITCH];  // D as bf16, [key row][value column]
+    __bf16 pt[C * PPITCH];  // (P' w)^T: [j][i]
+    __bf16 pv[C * PPITCH];  // (P w)^T:  [j][i]
+};
+
+template <int MODE, bool STATE_ONLY>
+__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ ds_out,
+    int64_t sstride, __bf16* __restrict__ dk_out, __bf16* __restrict__ dv_out, float* __restrict__ ds_in,
+    float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
+    const float* __restrict__ init_state,                            // output pass: scanned D^(g)
+    int64_t H, int64_t L, int nseg, int G, int cps) {
+    __shared__ __attribute__((aligned(16))) BwdSmem sm;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int n32 = lane & 31;
+    const int kg = lane >> 5;
+    const int64_t u = blockIdx.x;
+    const int gper = STATE_ONLY ? (G - 1) : G;
+    const int g = STATE_ONLY ? (int)(u % gper) + 1 : (int)(u % gper);  // the state pass covers 1..G-1
+    const int64_t ub = u / gper;  // (bh, seg)
+    const int seg = (int)(ub % nseg);
+    const int64_t bh = ub / nseg;
+    const int64_t h = bh % H;
+    const int64_t Lseg = L / nseg;
+    const int64_t tseg = (int64_t)seg * Lseg;
+    const int64_t t_begin = tseg + (int64_t)g * cps * C;
+    const int64_t t_end = min(t_begin + (int64_t)cps * C, tseg + Lseg);
+    const int64_t row_base = bh * L;
+    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
+
+    // ---- D at the sub-segment's end: key rows 32 m + (i / 4) 8 + kg 4 + i % 4, value column 32 w + n32
+    f32x16 Dm[4];
+    {
+        const float* src = nullptr;
+        if (g == G - 1) {
+            if (ds_out) src = ds_out + bh * sstride + (int64_t)seg * D * D;
+        } else if (!STATE_ONLY) {
+            src = init_state + (ub * (G - 1) + (G - 2 - g)) * (int64_t)D * D;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                Dm[m][i] = src ? src[r * D + 32 * w + n32] : 0.f;
+            }
+    }
+
+    const int nchunks = (int)((t_end - t_begin + C - 1) / C);
+    for (int c = nchunks - 1; c >= 0; c--) {
+        const int64_t t0 = t_begin + (int64_t)c * C;
+        const int n = (int)min((int64_t)C, t_end - t0);
+        __syncthreads();  // the previous chunk is done with every LDS tile
+
+        // ---- stage the chunk (rows past the end as zero) and D as bf16
+#pragma unroll
+        for (int r = 0; r < PR; r++) {
+            const int p = tid + NT * r;
+            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+            const int64_t off = (row_base + t0 + row) * D + c8;
+            const bool ok = row < n;
+            const u32x4 z = {0, 0, 0, 0};
+            const u32x4 xq = ok ? *(const u32x4*)(q + off) : z;
+            const u32x4 xo = ok ? *(const u32x4*)(d_o + off) : z;
+            if (MODE == DECAY_HEAD) *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(xq, decay_pow(lam, row + 1));
+            else if (STATE_ONLY) *(u32x4*)(&sm.qs[row * PITCH + c8]) = xq;
+            *(u32x4*)(&sm.o[row * PITCH + c8]) = xo;
+            if (!STATE_ONLY) {
+                *(u32x4*)(&sm.q[row * PITCH + c8]) = xq;
+                *(u32x4*)(&sm.k[row * PITCH + c8]) = ok ? *(const u32x4*)(k + off) : z;
+                *(u32x4*)(&sm.v[row * PITCH + c8]) = ok ? *(const u32x4*)(v + off) : z;
+            }
+        }
+        if (!STATE_ONLY) {
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                    sm.dm[r * PITCH + 32 * w + n32] = (__bf16)Dm[m][i];
+                }
+        }
+        __syncthreads();
+        // the q side of the D update: q a^{i+1} (head mode), else q itself
+        const __bf16* qsd = (MODE == DECAY_HEAD || STATE_ONLY) ? sm.qs : sm.q;
+
+        // d_o operands of this wave's value columns for the four 16-token slabs
+        bf16x8 ob[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) ob[ks] = tr_operand(sm.o, PITCH, ks, 32 * w, lane);
+
+        if (!STATE_ONLY) {
+            // ---- causal score blocks (row block = i, column block = j): P' on waves 0, 1, 3 and P on
+            // waves 0, 2, 3; written transposed with the weight a^{i-j} and the mask j <= i
+            auto score = [&](const __bf16* A, const __bf16* Bt, __bf16* dst, int ib, int jb) {
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ks++) {
+                    const bf16x8 a = *(const bf16x8*)(&A[(ib * 32 + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 b = *(const bf16x8*)(&Bt[(jb * 32 + n32) * PITCH + ks * 16 + kg * 8]);
+                    acc = mfma(a, b, acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);  // i index
+                    const int col = jb * 32 + n32;                               // j index
+                    float val = acc[i];
+                    if (MODE == DECAY_HEAD) val *= decay_pow(lam, max(row - col, 0));
+                    if (col > row) val = 0.f;
+                    dst[col * PPITCH + row] = (__bf16)val;
+                }
+            };
+            if (w == 0) {
+                score(sm.o, sm.v, sm.pt, 0, 0);
+                score(sm.q, sm.k, sm.pv, 0, 0);
+            } else if (w == 1) {
+                score(sm.o, sm.v, sm.pt, 1, 0);
+            } else if (w == 2) {
+                score(sm.q, sm.k, sm.pv, 1, 0);
+            } else {
+                score(sm.o, sm.v, sm.pt, 1, 1);
+                score(sm.q, sm.k, sm.pv, 1, 1);
+            }
+            __syncthreads();  // score tiles complete
+
+            // ---- dk, column block w (key dims 32 w ..), and dv, column block w (value columns 32 w ..)
+            bf16x8 qb[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) qb[ks] = tr_operand(sm.q, PITCH, ks, 32 * w, lane);
+            // D's own columns as B operands (key-row order permuted as the A reads below)
+            bf16x8 db[8];
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++) {
+                    bf16x8 x;
+#pragma unroll
+                    for (int j = 0; j < 8; j++) x[j] = (__bf16)Dm[m][8 * hh + j];
+                    db[2 * m + hh] = x;
+                }
+#pragma unroll
+            for (int jb = 0; jb < 2; jb++) {
+                // dk: a^{n-1-j} (V D^T) + (P' w)^T Q
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ks++) {
+                    const bf16x8 a = *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 b = *(const bf16x8*)(&sm.dm[(32 * w + n32) * PITCH + ks * 16 + kg * 8]);
+                    acc = mfma(a, b, acc);
+                }
+                if (MODE == DECAY_HEAD) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const int j = jb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
+                        acc[i] *= decay_pow(lam, max(n - 1 - j, 0));
+                    }
+                }
+#pragma unroll
+                for (int ks = 2 * jb; ks < 4; ks++) {
+                    const bf16x8 a = *(const bf16x8*)(&sm.pt[(jb * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
+                    acc = mfma(a, qb[ks], acc);
+                }
+                __bf16* drow = dk_out + (row_base + t0 + jb * 32) * D + 32 * w + n32;
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int j = (i >> 2) * 8 + kg * 4 + (i & 3);
+                    if (jb * 32 + j < n) drow[j * D] = (__bf16)acc[i];
+                }
+                // dv: a^{n-1-j} (K D) + (P w)^T d_o
+                acc = f32x16{};
+                const __bf16* krow = &sm.k[(jb * 32 + n32) * PITCH + kg * 4];
+#pragma unroll
+                for (int m = 0; m < 4; m++)
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++) {
+                        const int d0 = 32 * m + 16 * hh;
+                        acc = mfma(cat(*(const bf16x4*)(krow + d0), *(const bf16x4*)(krow + d0 + 8)), db[2 * m + hh],
+                                   acc);
+                    }
+                if (MODE == DECAY_HEAD) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const int j = jb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
+                        acc[i] *= decay_pow(lam, max(n - 1 - j, 0));
+                    }
+                }
+#pragma unroll
+                for (int ks = 2 * jb; ks < 4; ks++) {
+                    const bf16x8 a = *(const bf16x8*)(&sm.pv[(jb * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
+                    acc = mfma(a, ob[ks], acc);
+                }
+                __bf16* vrow = dv_out + (row_base + t0 + jb * 32) * D + 32 * w + n32;
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int j = (i >> 2) * 8 + kg * 4 + (i & 3);
+                    if (jb * 32 + j < n) vrow[j * D] = (__bf16)acc[i];
+                }
+            }
+        }
+
+        // ---- D <- a^n D + (q a^{i+1})^T d_o
+        {
+            const float fh = (MODE == DECAY_HEAD) ? decay_pow(lam, n) : 1.f;
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                if (MODE == DECAY_HEAD) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) Dm[m][i] *= fh;
+                }
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) Dm[m] = mfma(tr_operand(qsd, PITCH, ks, 32 * m, lane), ob[ks], Dm[m]);
+            }
+        }
+    }
+
+    // ---- the derivative at the sub-segment's start
+    float* dst = nullptr;
+    if (STATE_ONLY) dst = part_state + (ub * (G - 1) + (G - 1 - g)) * (int64_t)D * D;
+    else if (g == 0 && ds_in) dst = ds_in + bh * sstride + (int64_t)seg * D * D;
+    if (dst) {
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                dst[r * D + 32 * w + n32] = Dm[m][i];
+            }
+    }
+    if (STATE_ONLY && tid < D) {  // the total decay over this sub-segment, per key dim
+        const float tot = (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
+        part_decay[(ub * (G - 1) + (G - 1 - g)) * D + tid] = tot;
+    }
+}
+
+
+struct DqSmem {
+    __bf16 o[TILE];   // d_o
+    __bf16 v[TILE];
+    __bf16 k[TILE];   // k (the P' K product)
+    __bf16 kt[TILE];  // k_j a^{n-1-j} (the state update)
+    __bf16 sm[D * PITCH];   // S as bf16, [key row][value column]
+    __bf16 p[C * PPITCH];   // P' w, [i][j]
+};
+
+template <int MODE, bool STATE_ONLY>
+__global__ __launch_bounds__(NT) void bwd_dq_kernel(
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ s_in,
+    const float* __restrict__ ds_out, int64_t sstride, __bf16* __restrict__ dq,
+    float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
+    const float* __restrict__ init_state,                            // output pass: scanned states
+    int64_t H, int64_t L, int nseg, int G, int cps) {
+    __shared__ __attribute__((aligned(16))) DqSmem sm;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int n32 = lane & 31;
+    const int kg = lane >> 5;
+    const int64_t u = blockIdx.x;
+    const int gper = STATE_ONLY ? (G - 1) : G;
+    const int g = (int)(u % gper);  // the state pass covers 0..G-2
+    const int64_t ub = u / gper;
+    const int seg = (int)(ub % nseg);
+    const int64_t bh = ub / nseg;
+    const int64_t h = bh % H;
+    const int64_t Lseg = L / nseg;
+    const int64_t tseg = (int64_t)seg * Lseg;
+    const int64_t t_begin = tseg + (int64_t)g * cps * C;
+    const int64_t t_end = min(t_begin + (int64_t)cps * C, tseg + Lseg);
+    const int64_t row_base = bh * L;
+    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
+
+    // ---- the state entering the sub-segment: key rows 32 m + (i / 4) 8 + kg 4 + i % 4, column 32 w + n32
+    f32x16 Sm[4];
+    {
+        const float* src = nullptr;
+        if (g == 0) {
+            if (seg == 0 && s_in) src = s_in + bh * (int64_t)D * D;
+        } else if (!STATE_ONLY) {
+            src = init_state + (ub * (G - 1) + (g - 1)) * (int64_t)D * D;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                Sm[m][i] = src ? src[r * D + 32 * w + n32] : 0.f;
+            }
+    }
+
+    const int nchunks = (int)((t_end - t_begin + C - 1) / C);
+    for (int c = 0; c < nchunks; c++) {
+        const int64_t t0 = t_begin + (int64_t)c * C;
+        const int n = (int)min((int64_t)C, t_end - t0);
+        __syncthreads();  // the previous chunk is done with every LDS tile
+#pragma unroll
+        for (int r = 0; r < PR; r++) {
+            const int p = tid + NT * r;
+            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+            const int64_t off = (row_base + t0 + row) * D + c8;
+            const bool ok = row < n;
+            const u32x4 z = {0, 0, 0, 0};
+            const u32x4 xk = ok ? *(const u32x4*)(k + off) : z;
+            *(u32x4*)(&sm.v[row * PITCH + c8]) = ok ? *(const u32x4*)(v + off) : z;
+            if (MODE == DECAY_HEAD) *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(xk, decay_pow(lam, max(n - 1 - row, 0)));
+            else *(u32x4*)(&sm.kt[row * PITCH + c8]) = xk;
+            if (!STATE_ONLY) {
+                *(u32x4*)(&sm.k[row * PITCH + c8]) = xk;
+                *(u32x4*)(&sm.o[row * PITCH + c8]) = ok ? *(const u32x4*)(d_o + off) : z;
+            }
+        }
+        if (!STATE_ONLY) {
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                    sm.sm[r * PITCH + 32 * w + n32] = (__bf16)Sm[m][i];
+                }
+        }
+        __syncthreads();
+
+        bf16x8 vb[4];  // v operands of this wave's value columns, four 16-token slabs
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) vb[ks] = tr_operand(sm.v, PITCH, ks, 32 * w, lane);
+
+        if (!STATE_ONLY) {
+            // ---- P' blocks (0,0), (1,0), (1,1) on waves 0, 2, 3: weight a^{i-j}, mask j <= i
+            if (w != 1) {
+                const int ib = w >> 1, jb = (w == 3) ? 1 : 0;
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ks++) {
+                    const bf16x8 a = *(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 b = *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ks * 16 + kg * 8]);
+                    acc = mfma(a, b, acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
+                    const int col = jb * 32 + n32;
+                    float val = acc[i];
+                    if (MODE == DECAY_HEAD) val *= decay_pow(lam, max(row - col, 0));
+                    if (col > row) val = 0.f;
+                    sm.p[row * PPITCH + col] = (__bf16)val;
+                }
+            }
+            __syncthreads();  // P' complete
+
+            // ---- dq, column block w (key dims 32 w ..): a^{i+1} (d_o S^T) + P' K
+            bf16x8 kb[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) kb[ks] = tr_operand(sm.k, PITCH, ks, 32 * w, lane);
+#pragma unroll
+            for (int ib = 0; ib < 2; ib++) {
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ks++) {
+                    const bf16x8 a = *(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 b = *(const bf16x8*)(&sm.sm[(32 * w + n32) * PITCH + ks * 16 + kg * 8]);
+                    acc = mfma(a, b, acc);
+                }
+                if (MODE == DECAY_HEAD) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
+                        acc[i] *= decay_pow(lam, row + 1);
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2 * (ib + 1); ks++) {
+                    const bf16x8 a = *(const bf16x8*)(&sm.p[(ib * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
+                    acc = mfma(a, kb[ks], acc);
+                }
+                const int64_t rbase = row_base + t0 + ib * 32;
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int row = (i >> 2) * 8 + kg * 4 + (i & 3);
+                    if (ib * 32 + row < n) dq[(rbase + row) * D + 32 * w + n32] = (__bf16)acc[i];
+                }
+            }
+        }
+
+        // ---- S <- a^n S + (K a^{n-1-j})^T V
+        {
+            const float fh = (MODE == DECAY_HEAD) ? decay_pow(lam, n) : 1.f;
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                if (MODE == DECAY_HEAD) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) Sm[m][i] *= fh;
+                }
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) Sm[m] = mfma(tr_operand(sm.kt, PITCH, ks, 32 * m, lane), vb[ks], Sm[m]);
+            }
+        }
+    }
+
+    if (STATE_ONLY) {
+        float* dst = part_state + (ub * (G - 1) + g) * (int64_t)D * D;
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                dst[r * D + 32 * w + n32] = Sm[m][i];
+            }
+        if (tid < D) {
+            const float tot = (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
+            part_decay[(ub * (G - 1) + g) * D + tid] = tot;
+        }
+    }
+}
+
+template <int MODE>
+hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* f_decay, float* b_state,
+                       float* b_decay) {
+    const int64_t units = a.B * a.H * a.nseg;
+    const __bf16* q = (const __bf16*)a.q;
+    const __bf16* k = (const __bf16*)a.k;
+    const __bf16* v = (const __bf16*)a.v;
+    const __bf16* d_o = (const __bf16*)a.d_o;
+    hipError_t e;
+    // dq: forward state pass, scan, output pass
+    if (G > 1) {
+        LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
+                  bwd_dq_kernel<MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                      k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr,
+                      a.H, a.L, a.nseg, G, cps));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_state_scan(f_state, f_decay, f_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
+            return e;
+    }
+    LA_TRACED(a.tr, "chunk_bwd_dq",
+              bwd_dq_kernel<MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                  k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, f_state,
+                  a.H, a.L, a.nseg, G, cps));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // dk, dv: backward state pass, reverse-order scan, output pass
+    if (G > 1) {
+        LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass",
+                  bwd_dkdv_kernel<MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                      q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state, b_decay,
+                      nullptr, a.H, a.L, a.nseg, G, cps));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_state_scan(b_state, b_decay, b_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
+            return e;
+    }
+    LA_TRACED(a.tr, "chunk_bwd_dkdv",
+              bwd_dkdv_kernel<MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                  q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out, a.ds_in,
+                  nullptr, nullptr, b_state, a.H, a.L, a.nseg, G, cps));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunk_bwd_mfma_supported(const BwdArgs& a) {
+    return a.bf16 && a.dk == D && a.dv == D && a.chunk == C && a.L > 0 && a.B * a.H > 0 &&
+           (a.mode == DECAY_NONE || (a.mode == DECAY_HEAD && !a.d_decay));
+}
+
+hipError_t launch_chunk_bwd_mfma(const BwdArgs& a) {
+    FwdArgs sp;
+    sp.B = a.B; sp.H = a.H; sp.L = a.L; sp.nseg = a.nseg; sp.subseg_chunks = 0;
+    int G, cps;
+    mfma_split(sp, &G, &cps);
+    const int64_t units = a.B * a.H * a.nseg;
+    // workspace: the forward and backward sub-segment states and decays
+    const size_t n_state = (size_t)units * (G - 1) * D * D, n_decay = (size_t)units * (G - 1) * D;
+    const size_t bytes = sizeof(float) * 2 * (n_state + n_decay);
+    char* ws = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    hipMemPool_t pool = workspace_pool(dev);
+    if (!pool) return hipErrorOutOfMemory;
+    if (bytes > 0 && (e = hipMallocFromPoolAsync((void**)&ws, bytes, pool, a.stream)) != hipSuccess) return e;
+    float* fp = (float*)ws;
+    float* f_state = n_state ? fp : nullptr;
+    float* b_state = n_state ? fp + n_state : nullptr;
+    float* f_decay = n_decay ? fp + 2 * n_state : nullptr;
+    float* b_decay = n_decay ? fp + 2 * n_state + n_decay : nullptr;
+    e = a.mode == DECAY_HEAD ? launch_mode<DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay)
+                             : launch_mode<DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay);
+    if (ws) {
+        hipError_t f = hipFreeAsync(ws, a.stream);
+        if (e == hipSuccess) e = f;
+    }
+    return e;
+}
+
+}  // namespace la

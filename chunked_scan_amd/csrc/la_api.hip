@@ -387,7 +387,7 @@ la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float*
     a.inv_norm = s->decay_mode == LA_DECAY_GATE ? 1.f / s->gate_norm : 1.f;
     a.stream = (hipStream_t)s->stream;
     a.tr = &tr;
-    return from_hip(la::launch_chunk_bwd_generic(a));
+    return from_hip(la::chunk_bwd_mfma_supported(a) ? la::launch_chunk_bwd_mfma(a) : la::launch_chunk_bwd_generic(a));
 }
 
 }  // extern "C"

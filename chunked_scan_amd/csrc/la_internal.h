@@ -106,6 +106,9 @@ hipMemPool_t workspace_pool(int dev);
 // Chunked backward with fp32 arithmetic on VALU (chunk_bwd_generic.hip): every shape the generic
 // forward takes.
 hipError_t launch_chunk_bwd_generic(const BwdArgs& a);
+// bf16 MFMA backward (chunk_bwd_mfma.hip): dk = dv = 128, chunk 64, no decay or head decay.
+bool chunk_bwd_mfma_supported(const BwdArgs& a);
+hipError_t launch_chunk_bwd_mfma(const BwdArgs& a);
 
 // Generic chunked forward: fp32 arithmetic on VALU, q/k/v/o in f32 or bf16, dk, dv in
 // {16,32,64,128}, chunk in {16,32,64}.
@@ -114,6 +117,8 @@ hipError_t launch_chunk_fwd_generic(const FwdArgs& a);
 // bf16 MFMA chunked forward for dk = dv in {32, 64, 128}, chunk = 64, with intra-GPU sub-segment
 // splitting (chunk_fwd_split.hip), all decay modes.
 hipError_t launch_chunk_fwd_mfma(const FwdArgs& a);
+// Its split of each segment into G sub-segments of cps chunks (uses B, H, L, nseg, subseg_chunks).
+void mfma_split(const FwdArgs& a, int* G_out, int* cps_out);
 // Its kernels: G sub-segments of cps chunks; part_state / part_decay the workspace of the
 // sub-segment scan (unused when G == 1).
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);

@@ -45,11 +45,11 @@ def _oracle(w, inp, gr, nseg):
                                  gate_norm=w.gate_norm)
 
 
-def _gpu(w, inp, gr, nseg):
+def _gpu(w, inp, gr, nseg, want_decay=True):
     d = to_dev(inp)
     g = to_dev(gr)
     out = lb.la_chunk_bwd(d["q"], d["k"], d["v"], g["d_o"], d["decay"], d["s_in"], g["ds_out"], mode=w.mode,
-                          nseg=nseg, chunk=w.chunk, gate_norm=w.gate_norm)
+                          nseg=nseg, chunk=w.chunk, gate_norm=w.gate_norm, want_decay=want_decay)
     torch.cuda.synchronize()
     return out
 
@@ -60,6 +60,8 @@ def _compare(got, ref, dtype, mode):
         if name == "d_decay":
             if mode == "none":
                 assert g is None and r is None
+                continue
+            if g is None:  # not requested
                 continue
             err = rel_err(g, r)
             assert err <= TOL_DECAY[dtype], (name, err)
@@ -125,3 +127,25 @@ def test_bwd_chunk_invariance():
                               chunk=c, gate_norm=w.gate_norm)
         torch.cuda.synchronize()
         _compare(got, ref, "f32", "gate")
+
+
+@pytest.mark.parametrize("mode", ["none", "head"])
+@pytest.mark.parametrize("L,nseg,H", [(192, 1, 2), (1000, 1, 2), (2048, 2, 2), (640, 1, 3)])
+def test_bwd_bf16_matrix_core_subsegments(mode, L, nseg, H):
+    """bf16, d = 128, chunk 64, no decay or a fixed head decay (no decay derivative requested) runs on
+    the matrix-core kernels, which split each segment into sub-segments (state passes, scans of the
+    state and of its derivative, output passes): lengths that give one or several sub-segments and a
+    ragged last chunk."""
+    note(f"la_chunk_bwd bf16 d=128 matrix-core mode={mode} L={L} nseg={nseg} H={H}")
+    w, inp, gr = _case(mode, "bf16", 128, 128, L, 64, nseg, seed=500 + L + H, B=1, H=H)
+    got = _gpu(w, inp, gr, nseg, want_decay=False)
+    assert got[3] is None
+    _compare(got, _oracle(w, inp, gr, nseg), "bf16", mode)
+
+
+@pytest.mark.parametrize("L", [192, 1000])
+def test_bwd_bf16_head_decay_derivative_takes_the_fp32_path(L):
+    """Asking for the head-decay derivative at bf16, d = 128 gives the fp32-accurate result."""
+    note(f"la_chunk_bwd bf16 d=128 head decay derivative L={L}")
+    w, inp, gr = _case("head", "bf16", 128, 128, L, 64, 1, seed=600 + L, B=1, H=2)
+    _compare(_gpu(w, inp, gr, 1), _oracle(w, inp, gr, 1), "bf16", "head")
