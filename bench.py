@@ -88,6 +88,31 @@ def kernel_roofline(w, step, kernels):
         d.update(algorithmic_bytes=by, gbps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
 
 
+class BackwardStep:
+    """One backward pass (la_chunk_bwd) over a workload's inputs with seeded d_o and ds_out, the
+    decays held fixed (no decay derivative).  Outputs are allocated once."""
+
+    def __init__(self, w):
+        import torch
+
+        from chunked_scan_amd.inputs import make_grads, make_inputs
+
+        self.w = w
+        self.inp = make_inputs(w, "cuda")
+        self.gr = make_grads(w, device="cuda")
+        self.dq = torch.empty_like(self.inp["q"])
+        self.dk = torch.empty_like(self.inp["k"])
+        self.dv = torch.empty_like(self.inp["v"])
+
+    def run(self, timers=None):
+        from chunked_scan_amd import binding
+
+        i, g = self.inp, self.gr
+        binding.la_chunk_bwd(i["q"], i["k"], i["v"], g["d_o"], i["decay"], i["s_in"], g["ds_out"], mode=self.w.mode,
+                             chunk=self.w.chunk, want_decay=False, dq=self.dq, dk=self.dk, dv=self.dv,
+                             timer=(timers or {}).get("fwd"))
+
+
 def step_stats(step, steps, stream, scratch=None):
     """Per-step times (us) with events around each step; with ``scratch``, the buffer is read
     before every step so that the step starts with a cold last-level cache."""
@@ -116,7 +141,7 @@ def kernel_stats(step, steps, stream):
 
     from chunked_scan_amd import binding
 
-    timers = [{c: binding.KernelTimer(4) for c in ("fwd", "cum", "scan", "corr")} for _ in range(steps)]
+    timers = [{c: binding.KernelTimer(8) for c in ("fwd", "cum", "scan", "corr")} for _ in range(steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -304,6 +329,33 @@ def main():
             del sa, ia
             torch.cuda.empty_cache()
 
+    backward = {}
+    if not args.no_alongside:
+        for wid in (1, 2):
+            wb = WORKLOADS[wid]
+            log(f"[bench] backward: workload {wid} {wb.name}")
+            sb = BackwardStep(wb)
+            for _ in range(60):  # >= 20 ms of work: settled clocks
+                sb.run()
+            torch.cuda.synchronize()
+            st = step_stats(sb, 30, stream)
+            ks, _ = kernel_stats(sb, 30, stream)
+            th = wb.B * wb.H * wb.L
+            # compulsory bytes (bf16): q, k, v, d_o read once, dq, dk, dv written once
+            comp = th * 2 * (wb.dk + wb.dk + wb.dv + wb.dv) + th * 2 * (wb.dk + wb.dk + wb.dv)
+            gbs = comp / (st["median_us"] * 1e-6) / 1e9
+            backward[wb.name] = dict(
+                what="la_chunk_bwd: dq, dk, dv, ds_in (decay held fixed)", B=wb.B, H=wb.H, L=wb.L, decay=wb.decay,
+                tokens_per_s=round(wb.B * wb.L / (st["median_us"] * 1e-6), 1), per_step_us=st,
+                compulsory_bytes=comp, gbps_on_compulsory_bytes=round(gbs, 1),
+                hbm_frac_on_compulsory_bytes=round(gbs / HBM_PEAK_GBS, 4),
+                kernels={n: {k: round(v, 2) for k, v in d.items()} for n, d in ks.items()})
+            log(f"[bench]   backward {wb.name}: median {st['median_us']:.1f} us, "
+                f"{backward[wb.name]['tokens_per_s']:.3e} tokens/s, {gbs:.0f} GB/s on compulsory bytes; " +
+                ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in ks.items()))
+            del sb
+            torch.cuda.empty_cache()
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -370,6 +422,7 @@ def main():
         "ms_per_step_with_kernel_events": round(ms_traced, 5),
         "overhead_one_gpu_us": eps,
         "alongside": alongside,
+        "backward": backward,
     }
     print(json.dumps(out), flush=True)
 
