@@ -66,17 +66,25 @@ __device__ __forceinline__ bf16x8 tr_operand(const __bf16* tile, int pitch, int 
     return cat(lds_tr16(&tile[tb * pitch + col]), lds_tr16(&tile[(tb + 4) * pitch + col]));
 }
 
+// LDS of the backward-direction kernel; the state pass keeps only the tiles of the D update.
+template <int MODE, bool SO>
 struct BwdSmem {
-    __bf16 q[TILE];    // q
-    __bf16 qs[TILE];   // q_i a^{i+1} (head mode; the D update)
-    __bf16 k[TILE];
-    __bf16 v[TILE];
-    __bf16 o[TILE];    // d_o
-    __bf16 dm[D * PITCH];  // D as bf16, [key row][value column]
-    __bf16 pt[C * PPITCH];  // (P' w)^T: [j][i]
-    __bf16 pv[C * PPITCH];  // (P w)^T:  [j][i]
+    // unused tiles shrink to 8 elements, which keeps every tile 16-byte aligned
+    __bf16 q[SO ? 8 : TILE];
+    __bf16 qs[(MODE == DECAY_HEAD || SO) ? TILE : 8];  // q_i a^{i+1} (head mode), q (state pass): the D update
+    __bf16 k[SO ? 8 : TILE];
+    __bf16 v[SO ? 8 : TILE];
+    __bf16 o[TILE];                  // d_o
+    __bf16 dm[SO ? 8 : D * PITCH];   // D as bf16, [key row][value column]
+    __bf16 pt[SO ? 8 : C * PPITCH];  // (P' w)^T: [j][i]
+    __bf16 pv[SO ? 8 : C * PPITCH];  // (P w)^T:  [j][i]
+    float apow[C + 1];               // a^m, m = 0..C (head mode)
 };
 
+static_assert(TILE % 8 == 0 && (D * PITCH) % 8 == 0 && (C * PPITCH) % 8 == 0, "16-byte tiles");
+
+// The chunk walk prefetches the next chunk (in walk order) into registers while the current one is
+// computed; the output passes, which hold more accumulators, load at the top of each chunk instead.
 template <int MODE, bool STATE_ONLY>
 __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -85,7 +93,8 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
     const float* __restrict__ init_state,                            // output pass: scanned D^(g)
     int64_t H, int64_t L, int nseg, int G, int cps) {
-    __shared__ __attribute__((aligned(16))) BwdSmem sm;
+    __shared__ __attribute__((aligned(16))) BwdSmem<MODE, STATE_ONLY> sm;
+    constexpr bool PF = STATE_ONLY;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -123,29 +132,47 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
             }
     }
 
+    if (MODE == DECAY_HEAD && tid <= C) sm.apow[tid] = decay_pow(lam, tid);  // read after the loop's first barrier
     const int nchunks = (int)((t_end - t_begin + C - 1) / C);
-    for (int c = nchunks - 1; c >= 0; c--) {
-        const int64_t t0 = t_begin + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, t_end - t0);
-        __syncthreads();  // the previous chunk is done with every LDS tile
-
-        // ---- stage the chunk (rows past the end as zero) and D as bf16
+    // one chunk's tiles in registers (rows past the end read as zero)
+    u32x4 rq[PR], ro[PR], rk[STATE_ONLY ? 1 : PR], rv[STATE_ONLY ? 1 : PR];
+    auto load_chunk = [&](int cc) {
+        const int64_t t0c = t_begin + (int64_t)cc * C;
+        const int nc = (int)min((int64_t)C, t_end - t0c);
+        const u32x4 z = {0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < PR; r++) {
             const int p = tid + NT * r;
             const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            const int64_t off = (row_base + t0 + row) * D + c8;
-            const bool ok = row < n;
-            const u32x4 z = {0, 0, 0, 0};
-            const u32x4 xq = ok ? *(const u32x4*)(q + off) : z;
-            const u32x4 xo = ok ? *(const u32x4*)(d_o + off) : z;
-            if (MODE == DECAY_HEAD) *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(xq, decay_pow(lam, row + 1));
-            else if (STATE_ONLY) *(u32x4*)(&sm.qs[row * PITCH + c8]) = xq;
-            *(u32x4*)(&sm.o[row * PITCH + c8]) = xo;
+            const int64_t off = (row_base + t0c + row) * D + c8;
+            const bool ok = row < nc;
+            rq[r] = ok ? *(const u32x4*)(q + off) : z;
+            ro[r] = ok ? *(const u32x4*)(d_o + off) : z;
             if (!STATE_ONLY) {
-                *(u32x4*)(&sm.q[row * PITCH + c8]) = xq;
-                *(u32x4*)(&sm.k[row * PITCH + c8]) = ok ? *(const u32x4*)(k + off) : z;
-                *(u32x4*)(&sm.v[row * PITCH + c8]) = ok ? *(const u32x4*)(v + off) : z;
+                rk[r] = ok ? *(const u32x4*)(k + off) : z;
+                rv[r] = ok ? *(const u32x4*)(v + off) : z;
+            }
+        }
+    };
+    if (PF && nchunks > 0) load_chunk(nchunks - 1);
+    for (int c = nchunks - 1; c >= 0; c--) {
+        const int64_t t0 = t_begin + (int64_t)c * C;
+        const int n = (int)min((int64_t)C, t_end - t0);
+        __syncthreads();  // the previous chunk is done with every LDS tile
+        if (!PF) load_chunk(c);
+
+        // ---- stage the chunk and D as bf16
+#pragma unroll
+        for (int r = 0; r < PR; r++) {
+            const int p = tid + NT * r;
+            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+            if (MODE == DECAY_HEAD) *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(rq[r], sm.apow[row + 1]);
+            else if (STATE_ONLY) *(u32x4*)(&sm.qs[row * PITCH + c8]) = rq[r];
+            *(u32x4*)(&sm.o[row * PITCH + c8]) = ro[r];
+            if (!STATE_ONLY) {
+                *(u32x4*)(&sm.q[row * PITCH + c8]) = rq[r];
+                *(u32x4*)(&sm.k[row * PITCH + c8]) = rk[r];
+                *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
             }
         }
         if (!STATE_ONLY) {
@@ -158,6 +185,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 }
         }
         __syncthreads();
+        if (PF && c > 0) load_chunk(c - 1);  // the previous chunk, while this one is computed
         // the q side of the D update: q a^{i+1} (head mode), else q itself
         const __bf16* qsd = (MODE == DECAY_HEAD || STATE_ONLY) ? sm.qs : sm.q;
 
@@ -182,7 +210,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                     const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);  // i index
                     const int col = jb * 32 + n32;                               // j index
                     float val = acc[i];
-                    if (MODE == DECAY_HEAD) val *= decay_pow(lam, max(row - col, 0));
+                    if (MODE == DECAY_HEAD) val *= sm.apow[max(row - col, 0)];
                     if (col > row) val = 0.f;
                     dst[col * PPITCH + row] = (__bf16)val;
                 }
@@ -229,7 +257,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
 #pragma unroll
                     for (int i = 0; i < 16; i++) {
                         const int j = jb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= decay_pow(lam, max(n - 1 - j, 0));
+                        acc[i] *= sm.apow[max(n - 1 - j, 0)];
                     }
                 }
 #pragma unroll
@@ -258,7 +286,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
 #pragma unroll
                     for (int i = 0; i < 16; i++) {
                         const int j = jb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= decay_pow(lam, max(n - 1 - j, 0));
+                        acc[i] *= sm.apow[max(n - 1 - j, 0)];
                     }
                 }
 #pragma unroll
@@ -277,7 +305,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
 
         // ---- D <- a^n D + (q a^{i+1})^T d_o
         {
-            const float fh = (MODE == DECAY_HEAD) ? decay_pow(lam, n) : 1.f;
+            const float fh = (MODE == DECAY_HEAD) ? sm.apow[n] : 1.f;
 #pragma unroll
             for (int m = 0; m < 4; m++) {
                 if (MODE == DECAY_HEAD) {
@@ -310,13 +338,17 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
 }
 
 
+// LDS of the forward-direction kernel; the state pass keeps only the tiles of the state update.
+template <bool SO>
 struct DqSmem {
-    __bf16 o[TILE];   // d_o
+    // unused tiles shrink to 8 elements, which keeps every tile 16-byte aligned
+    __bf16 o[SO ? 8 : TILE];  // d_o
     __bf16 v[TILE];
-    __bf16 k[TILE];   // k (the P' K product)
-    __bf16 kt[TILE];  // k_j a^{n-1-j} (the state update)
-    __bf16 sm[D * PITCH];   // S as bf16, [key row][value column]
-    __bf16 p[C * PPITCH];   // P' w, [i][j]
+    __bf16 k[SO ? 8 : TILE];  // k (the P' K product)
+    __bf16 kt[TILE];          // k_j a^{n-1-j} (the state update)
+    __bf16 sm[SO ? 8 : D * PITCH];  // S as bf16, [key row][value column]
+    __bf16 p[SO ? 8 : C * PPITCH];  // P' w, [i][j]
+    float apow[C + 1];              // a^m, m = 0..C (head mode)
 };
 
 template <int MODE, bool STATE_ONLY>
@@ -327,7 +359,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
     const float* __restrict__ init_state,                            // output pass: scanned states
     int64_t H, int64_t L, int nseg, int G, int cps) {
-    __shared__ __attribute__((aligned(16))) DqSmem sm;
+    __shared__ __attribute__((aligned(16))) DqSmem<STATE_ONLY> sm;
+    constexpr bool PF = STATE_ONLY;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -365,25 +398,41 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
             }
     }
 
+    if (MODE == DECAY_HEAD && tid <= C) sm.apow[tid] = decay_pow(lam, tid);  // read after the loop's first barrier
     const int nchunks = (int)((t_end - t_begin + C - 1) / C);
-    for (int c = 0; c < nchunks; c++) {
-        const int64_t t0 = t_begin + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, t_end - t0);
-        __syncthreads();  // the previous chunk is done with every LDS tile
+    // one chunk's tiles in registers (rows past the end read as zero)
+    u32x4 rk[PR], rv[PR], ro[STATE_ONLY ? 1 : PR];
+    auto load_chunk = [&](int cc) {
+        const int64_t t0c = t_begin + (int64_t)cc * C;
+        const int nc = (int)min((int64_t)C, t_end - t0c);
+        const u32x4 z = {0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < PR; r++) {
             const int p = tid + NT * r;
             const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            const int64_t off = (row_base + t0 + row) * D + c8;
-            const bool ok = row < n;
-            const u32x4 z = {0, 0, 0, 0};
-            const u32x4 xk = ok ? *(const u32x4*)(k + off) : z;
-            *(u32x4*)(&sm.v[row * PITCH + c8]) = ok ? *(const u32x4*)(v + off) : z;
-            if (MODE == DECAY_HEAD) *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(xk, decay_pow(lam, max(n - 1 - row, 0)));
-            else *(u32x4*)(&sm.kt[row * PITCH + c8]) = xk;
+            const int64_t off = (row_base + t0c + row) * D + c8;
+            const bool ok = row < nc;
+            rk[r] = ok ? *(const u32x4*)(k + off) : z;
+            rv[r] = ok ? *(const u32x4*)(v + off) : z;
+            if (!STATE_ONLY) ro[r] = ok ? *(const u32x4*)(d_o + off) : z;
+        }
+    };
+    if (PF && nchunks > 0) load_chunk(0);
+    for (int c = 0; c < nchunks; c++) {
+        const int64_t t0 = t_begin + (int64_t)c * C;
+        const int n = (int)min((int64_t)C, t_end - t0);
+        __syncthreads();  // the previous chunk is done with every LDS tile
+        if (!PF) load_chunk(c);
+#pragma unroll
+        for (int r = 0; r < PR; r++) {
+            const int p = tid + NT * r;
+            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+            *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
+            if (MODE == DECAY_HEAD) *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(rk[r], sm.apow[max(n - 1 - row, 0)]);
+            else *(u32x4*)(&sm.kt[row * PITCH + c8]) = rk[r];
             if (!STATE_ONLY) {
-                *(u32x4*)(&sm.k[row * PITCH + c8]) = xk;
-                *(u32x4*)(&sm.o[row * PITCH + c8]) = ok ? *(const u32x4*)(d_o + off) : z;
+                *(u32x4*)(&sm.k[row * PITCH + c8]) = rk[r];
+                *(u32x4*)(&sm.o[row * PITCH + c8]) = ro[r];
             }
         }
         if (!STATE_ONLY) {
@@ -396,6 +445,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
                 }
         }
         __syncthreads();
+        if (PF && c + 1 < nchunks) load_chunk(c + 1);  // the next chunk, while this one is computed
 
         bf16x8 vb[4];  // v operands of this wave's value columns, four 16-token slabs
 #pragma unroll
@@ -417,7 +467,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
                     const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
                     const int col = jb * 32 + n32;
                     float val = acc[i];
-                    if (MODE == DECAY_HEAD) val *= decay_pow(lam, max(row - col, 0));
+                    if (MODE == DECAY_HEAD) val *= sm.apow[max(row - col, 0)];
                     if (col > row) val = 0.f;
                     sm.p[row * PPITCH + col] = (__bf16)val;
                 }
@@ -441,7 +491,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
 #pragma unroll
                     for (int i = 0; i < 16; i++) {
                         const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= decay_pow(lam, row + 1);
+                        acc[i] *= sm.apow[row + 1];
                     }
                 }
 #pragma unroll
@@ -460,7 +510,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
 
         // ---- S <- a^n S + (K a^{n-1-j})^T V
         {
-            const float fh = (MODE == DECAY_HEAD) ? decay_pow(lam, n) : 1.f;
+            const float fh = (MODE == DECAY_HEAD) ? sm.apow[n] : 1.f;
 #pragma unroll
             for (int m = 0; m < 4; m++) {
                 if (MODE == DECAY_HEAD) {
