@@ -84,7 +84,7 @@ struct BwdSmem {
 static_assert(TILE % 8 == 0 && (D * PITCH) % 8 == 0 && (C * PPITCH) % 8 == 0, "16-byte tiles");
 
 // The chunk walk prefetches the next chunk (in walk order) into registers while the current one is
-// computed; the output passes, which hold more accumulators, load at the top of each chunk instead.
+// computed (PF; off, each chunk is loaded at its top).
 template <int MODE, bool STATE_ONLY>
 __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     const float* __restrict__ init_state,                            // output pass: scanned D^(g)
     int64_t H, int64_t L, int nseg, int G, int cps) {
     __shared__ __attribute__((aligned(16))) BwdSmem<MODE, STATE_ONLY> sm;
-    constexpr bool PF = STATE_ONLY;
+    constexpr bool PF = true;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     const float* __restrict__ init_state,                            // output pass: scanned states
     int64_t H, int64_t L, int nseg, int G, int cps) {
     __shared__ __attribute__((aligned(16))) DqSmem<STATE_ONLY> sm;
-    constexpr bool PF = STATE_ONLY;
+    constexpr bool PF = true;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
