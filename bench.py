@@ -113,6 +113,42 @@ class BackwardStep:
                              timer=(timers or {}).get("fwd"))
 
 
+def backward_legs(stream):
+    """la_chunk_bwd at the plain (B=1) and head-decay (B=2) shapes, decays fixed: median time,
+    tokens/s, GB/s on the compulsory bytes (q, k, v, d_o read once, dq, dk, dv written once) and
+    per-kernel means."""
+    import torch
+
+    from chunked_scan_amd.inputs import WORKLOADS
+
+    backward = {}
+    for wid in (1, 2):
+        wb = WORKLOADS[wid]
+        log(f"[bench] backward: workload {wid} {wb.name}")
+        sb = BackwardStep(wb)
+        for _ in range(60):  # >= 20 ms of work: settled clocks
+            sb.run()
+        torch.cuda.synchronize()
+        st = step_stats(sb, 30, stream)
+        ks, _ = kernel_stats(sb, 30, stream)
+        th = wb.B * wb.H * wb.L
+        # compulsory bytes (bf16): q, k, v, d_o read once, dq, dk, dv written once
+        comp = th * 2 * (wb.dk + wb.dk + wb.dv + wb.dv) + th * 2 * (wb.dk + wb.dk + wb.dv)
+        gbs = comp / (st["median_us"] * 1e-6) / 1e9
+        backward[wb.name] = dict(
+            what="la_chunk_bwd: dq, dk, dv, ds_in (decay held fixed)", B=wb.B, H=wb.H, L=wb.L, decay=wb.decay,
+            tokens_per_s=round(wb.B * wb.L / (st["median_us"] * 1e-6), 1), per_step_us=st,
+            compulsory_bytes=comp, gbps_on_compulsory_bytes=round(gbs, 1),
+            hbm_frac_on_compulsory_bytes=round(gbs / HBM_PEAK_GBS, 4),
+            kernels={n: {k: round(v, 2) for k, v in d.items()} for n, d in ks.items()})
+        log(f"[bench]   backward {wb.name}: median {st['median_us']:.1f} us, "
+            f"{backward[wb.name]['tokens_per_s']:.3e} tokens/s, {gbs:.0f} GB/s on compulsory bytes; " +
+            ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in ks.items()))
+        del sb
+        torch.cuda.empty_cache()
+    return backward
+
+
 def step_stats(step, steps, stream, scratch=None):
     """Per-step times (us) with events around each step; with ``scratch``, the buffer is read
     before every step so that the step starts with a cold last-level cache."""
@@ -232,6 +268,9 @@ def main():
     ap.add_argument("--no-alongside", action="store_true",
                     help="skip the decay and segmented workloads and the three-way comparison reported next "
                          "to the headline")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward legs (la_chunk_bwd at the plain and head-decay shapes) and exit; "
+                         "prints their JSON")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -246,8 +285,11 @@ def main():
     from chunked_scan_amd.inputs import WORKLOADS, make_inputs
     from chunked_scan_amd.pipeline import DeviceStep, SegmentedForward
 
-    w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.backward_only:
+        print(json.dumps(dict(backward=backward_legs(torch.cuda.current_stream()))))
+        return
+    w = WORKLOADS[args.workload]
     log(f"[bench] workload {args.workload} {w.name}: generating inputs on cuda:0")
     inp = make_inputs(w, "cuda")
     if w.nseg == 1:
@@ -331,30 +373,7 @@ def main():
 
     backward = {}
     if not args.no_alongside:
-        for wid in (1, 2):
-            wb = WORKLOADS[wid]
-            log(f"[bench] backward: workload {wid} {wb.name}")
-            sb = BackwardStep(wb)
-            for _ in range(60):  # >= 20 ms of work: settled clocks
-                sb.run()
-            torch.cuda.synchronize()
-            st = step_stats(sb, 30, stream)
-            ks, _ = kernel_stats(sb, 30, stream)
-            th = wb.B * wb.H * wb.L
-            # compulsory bytes (bf16): q, k, v, d_o read once, dq, dk, dv written once
-            comp = th * 2 * (wb.dk + wb.dk + wb.dv + wb.dv) + th * 2 * (wb.dk + wb.dk + wb.dv)
-            gbs = comp / (st["median_us"] * 1e-6) / 1e9
-            backward[wb.name] = dict(
-                what="la_chunk_bwd: dq, dk, dv, ds_in (decay held fixed)", B=wb.B, H=wb.H, L=wb.L, decay=wb.decay,
-                tokens_per_s=round(wb.B * wb.L / (st["median_us"] * 1e-6), 1), per_step_us=st,
-                compulsory_bytes=comp, gbps_on_compulsory_bytes=round(gbs, 1),
-                hbm_frac_on_compulsory_bytes=round(gbs / HBM_PEAK_GBS, 4),
-                kernels={n: {k: round(v, 2) for k, v in d.items()} for n, d in ks.items()})
-            log(f"[bench]   backward {wb.name}: median {st['median_us']:.1f} us, "
-                f"{backward[wb.name]['tokens_per_s']:.3e} tokens/s, {gbs:.0f} GB/s on compulsory bytes; " +
-                ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in ks.items()))
-            del sb
-            torch.cuda.empty_cache()
+        backward = backward_legs(stream)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
