@@ -18,9 +18,9 @@
 //     P'[i][j] as above, P[i][j] = q_i . k_j a^{i-j}  (j <= i)
 //     dk_j = sum_{i>=j} P'[i][j] q_i + a^{n-1-j} D v_j,   dv_j = sum_{i>=j} P[i][j] d_o_i + a^{n-1-j} D^T k_j
 //     D <- a^n D + sum_i a^{i+1} q_i d_o_i^T
-// The decay derivative is not formed here: written through q . dq - k . dk its terms cancel by a
-// factor that grows with the sequence length over the decay length, which the bf16 operands of the
-// matrix-core products (scores, state) cannot carry; callers that ask for it take the fp32 path.
+// The head-decay derivative is not taken from q . dq - k . dk (whose terms cancel by a factor that
+// grows with the sequence length over the decay length, beyond what the bf16 operands of these
+// products carry) but summed pair by pair with dS/dlambda carried beside S (bwd_dlam_kernel).
 //
 // Wave roles (both directions): wave w keeps value columns 32w..32w+31 of S or D (all 128 key rows)
 // in MFMA accumulators and computes the 32-wide column block w of dq / dk / dv; the causal 32x32
@@ -79,6 +79,7 @@ struct BwdSmem {
     __bf16 pt[SO ? 8 : C * PPITCH];  // (P' w)^T: [j][i]
     __bf16 pv[SO ? 8 : C * PPITCH];  // (P w)^T:  [j][i]
     float apow[C + 1];               // a^m, m = 0..C (head mode)
+    double red[NT / 64];
 };
 
 static_assert(TILE % 8 == 0 && (D * PITCH) % 8 == 0 && (C * PPITCH) % 8 == 0, "16-byte tiles");
@@ -92,6 +93,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     int64_t sstride, __bf16* __restrict__ dk_out, __bf16* __restrict__ dv_out, float* __restrict__ ds_in,
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
     const float* __restrict__ init_state,                            // output pass: scanned D^(g)
+    double* __restrict__ intra_part,  // head mode, output pass: the intra-chunk part of d lambda_h, or null
     int64_t H, int64_t L, int nseg, int G, int cps) {
     __shared__ __attribute__((aligned(16))) BwdSmem<MODE, STATE_ONLY> sm;
     constexpr bool PF = true;
@@ -133,6 +135,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     }
 
     if (MODE == DECAY_HEAD && tid <= C) sm.apow[tid] = decay_pow(lam, tid);  // read after the loop's first barrier
+    double hacc = 0.0;
     const int nchunks = (int)((t_end - t_begin + C - 1) / C);
     // one chunk's tiles in registers (rows past the end read as zero)
     u32x4 rq[PR], ro[PR], rk[STATE_ONLY ? 1 : PR], rv[STATE_ONLY ? 1 : PR];
@@ -195,36 +198,33 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
         for (int ks = 0; ks < 4; ks++) ob[ks] = tr_operand(sm.o, PITCH, ks, 32 * w, lane);
 
         if (!STATE_ONLY) {
-            // ---- causal score blocks (row block = i, column block = j): P' on waves 0, 1, 3 and P on
-            // waves 0, 2, 3; written transposed with the weight a^{i-j} and the mask j <= i
-            auto score = [&](const __bf16* A, const __bf16* Bt, __bf16* dst, int ib, int jb) {
-                f32x16 acc = {};
+            // ---- causal score blocks (row block = i, column block = j) (0,0), (1,0), (1,1) on waves 0, 1, 2,
+            // P' and P of a block on the same wave: written transposed with the weight a^{i-j} and the
+            // mask j <= i; head mode with intra_part also sums (i - j) a^{i-j} P[i][j] P'[i][j], the
+            // intra-chunk token pairs' share of d lambda_h, from the unrounded scores
+            if (w < 3) {
+                const int ib = (w == 0) ? 0 : 1, jb = (w == 2) ? 1 : 0;
+                f32x16 po = {}, pq = {};
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&A[(ib * 32 + n32) * PITCH + ks * 16 + kg * 8]);
-                    const bf16x8 b = *(const bf16x8*)(&Bt[(jb * 32 + n32) * PITCH + ks * 16 + kg * 8]);
-                    acc = mfma(a, b, acc);
+                    const int ka = ks * 16 + kg * 8;
+                    po = mfma(*(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ka]),
+                              *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ka]), po);
+                    pq = mfma(*(const bf16x8*)(&sm.q[(ib * 32 + n32) * PITCH + ka]),
+                              *(const bf16x8*)(&sm.k[(jb * 32 + n32) * PITCH + ka]), pq);
                 }
 #pragma unroll
                 for (int i = 0; i < 16; i++) {
                     const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);  // i index
                     const int col = jb * 32 + n32;                               // j index
-                    float val = acc[i];
-                    if (MODE == DECAY_HEAD) val *= sm.apow[max(row - col, 0)];
-                    if (col > row) val = 0.f;
-                    dst[col * PPITCH + row] = (__bf16)val;
+                    float wgt = (col > row) ? 0.f : 1.f;
+                    if (MODE == DECAY_HEAD) {
+                        wgt *= sm.apow[max(row - col, 0)];
+                        if (intra_part && col < row) hacc += (double)((float)(row - col) * wgt) * ((double)po[i] * (double)pq[i]);
+                    }
+                    sm.pt[col * PPITCH + row] = (__bf16)(po[i] * wgt);
+                    sm.pv[col * PPITCH + row] = (__bf16)(pq[i] * wgt);
                 }
-            };
-            if (w == 0) {
-                score(sm.o, sm.v, sm.pt, 0, 0);
-                score(sm.q, sm.k, sm.pv, 0, 0);
-            } else if (w == 1) {
-                score(sm.o, sm.v, sm.pt, 1, 0);
-            } else if (w == 2) {
-                score(sm.q, sm.k, sm.pv, 1, 0);
-            } else {
-                score(sm.o, sm.v, sm.pt, 1, 1);
-                score(sm.q, sm.k, sm.pv, 1, 1);
             }
             __syncthreads();  // score tiles complete
 
@@ -334,6 +334,14 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     if (STATE_ONLY && tid < D) {  // the total decay over this sub-segment, per key dim
         const float tot = (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
         part_decay[(ub * (G - 1) + (G - 1 - g)) * D + tid] = tot;
+    }
+    if (MODE == DECAY_HEAD && !STATE_ONLY && intra_part) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) hacc += __shfl_xor(hacc, off);
+        __syncthreads();
+        if (lane == 0) sm.red[w] = hacc;
+        __syncthreads();
+        if (tid == 0) intra_part[ub * G + g] = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
     }
 }
 
@@ -539,9 +547,245 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// The head-decay derivative, summed without cancellation.  Every pair of tokens j <= t contributes
+// (t - j) a^{t-j} (q_t . k_j)(v_j . d_o_t) to d lambda_h (and s_in, seen as a token before the
+// segment, and ds_out add their own terms).  Per chunk of n tokens, with S the state and
+// St = dS/dlambda before it:
+//   intra-chunk pairs  sum_{j<=i} (i - j) a^{i-j} P[i][j] P'[i][j]       (P = q k^T, P' = d_o v^T),
+//                      summed by the dk/dv output pass, which forms both score matrices anyway
+//   earlier tokens     <S, M'> + <St, M>,   M = sum_i a^{i+1} q_i d_o_i^T,   M' = sum_i (i+1) a^{i+1} q_i d_o_i^T
+//   St <- a^n St + n a^n S + sum_j (n-1-j) a^{n-1-j} k_j v_j^T,   S <- a^n S + sum_j a^{n-1-j} k_j v_j^T
+// and <ds_out, St> at the segment's end.  Sub-segments compose as S_out = A S_in + S_loc and
+// St_out = A St_in + l A S_in + St_loc (A = a^l over l tokens): a state pass leaves (S_loc, St_loc),
+// the S scan runs first, a fix-up adds l A S_in to each St_loc, and the St scan follows.
+struct DlamSmem {
+    __bf16 v[TILE], o[TILE];
+    __bf16 qs[TILE];   // q_i a^{i+1}
+    __bf16 qs2[TILE];  // q_i (i+1) a^{i+1}
+    __bf16 kt[TILE];   // k_j a^{n-1-j}
+    __bf16 kt2[TILE];  // k_j (n-1-j) a^{n-1-j}
+    float apow[C + 1];
+    double red[NT / 64];
+};
+
+template <bool STATE_ONLY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dlam_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ s_in,
+    const float* __restrict__ ds_out, int64_t sstride,
+    float* __restrict__ part_s, float* __restrict__ part_st, float* __restrict__ part_decay,  // state pass
+    const float* __restrict__ init_s, const float* __restrict__ init_st,                     // output pass
+    double* __restrict__ part, int64_t H, int64_t L, int nseg, int G, int cps) {
+    __shared__ __attribute__((aligned(16))) DlamSmem sm;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int n32 = lane & 31;
+    const int kg = lane >> 5;
+    const int64_t u = blockIdx.x;
+    const int gper = STATE_ONLY ? (G - 1) : G;
+    const int g = (int)(u % gper);  // the state pass covers 0..G-2
+    const int64_t ub = u / gper;
+    const int seg = (int)(ub % nseg);
+    const int64_t bh = ub / nseg;
+    const int64_t h = bh % H;
+    const int64_t Lseg = L / nseg;
+    const int64_t tseg = (int64_t)seg * Lseg;
+    const int64_t t_begin = tseg + (int64_t)g * cps * C;
+    const int64_t t_end = min(t_begin + (int64_t)cps * C, tseg + Lseg);
+    const int64_t row_base = bh * L;
+    const float lam = decay[h];
+    if (tid <= C) sm.apow[tid] = decay_pow(lam, tid);  // read after the loop's first barrier
+
+    // S and St entering the sub-segment (value columns 32 w + n32, key rows as the accumulators)
+    f32x16 Sm[4], St[4];
+    {
+        const float* src = nullptr;
+        const float* srct = nullptr;
+        if (g == 0) {
+            if (seg == 0 && s_in) src = s_in + bh * (int64_t)D * D;
+        } else if (!STATE_ONLY) {
+            src = init_s + (ub * (G - 1) + (g - 1)) * (int64_t)D * D;
+            srct = init_st + (ub * (G - 1) + (g - 1)) * (int64_t)D * D;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                Sm[m][i] = src ? src[r * D + 32 * w + n32] : 0.f;
+                St[m][i] = srct ? srct[r * D + 32 * w + n32] : 0.f;
+            }
+    }
+
+    double acc = 0.0;
+    const int nchunks = (int)((t_end - t_begin + C - 1) / C);
+    for (int c = 0; c < nchunks; c++) {
+        const int64_t t0 = t_begin + (int64_t)c * C;
+        const int n = (int)min((int64_t)C, t_end - t0);
+        __syncthreads();  // the previous chunk is done with every LDS tile
+#pragma unroll
+        for (int r = 0; r < PR; r++) {
+            const int p = tid + NT * r;
+            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+            const int64_t off = (row_base + t0 + row) * D + c8;
+            const bool ok = row < n;
+            const u32x4 z = {0, 0, 0, 0};
+            const u32x4 xk = ok ? *(const u32x4*)(k + off) : z;
+            const int jr = max(n - 1 - row, 0);
+            *(u32x4*)(&sm.v[row * PITCH + c8]) = ok ? *(const u32x4*)(v + off) : z;
+            *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(xk, sm.apow[jr]);
+            *(u32x4*)(&sm.kt2[row * PITCH + c8]) = scale8s(xk, (float)jr * sm.apow[jr]);
+            if (!STATE_ONLY) {
+                const u32x4 xq = ok ? *(const u32x4*)(q + off) : z;
+                *(u32x4*)(&sm.o[row * PITCH + c8]) = ok ? *(const u32x4*)(d_o + off) : z;
+                *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(xq, sm.apow[row + 1]);
+                *(u32x4*)(&sm.qs2[row * PITCH + c8]) = scale8s(xq, (float)(row + 1) * sm.apow[row + 1]);
+            }
+        }
+        __syncthreads();
+
+        if (!STATE_ONLY) {
+            // ---- earlier tokens: <S, M'> + <St, M> over this wave's value columns
+            bf16x8 ob[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) ob[ks] = tr_operand(sm.o, PITCH, ks, 32 * w, lane);
+#pragma unroll
+            for (int m = 0; m < 4; m++) {  // one 16-register product at a time: M' with S, then M with St
+                f32x16 M = {};
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) M = mfma(tr_operand(sm.qs2, PITCH, ks, 32 * m, lane), ob[ks], M);
+                double x = 0.0;
+#pragma unroll
+                for (int i = 0; i < 16; i++) x += (double)Sm[m][i] * (double)M[i];
+                M = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) M = mfma(tr_operand(sm.qs, PITCH, ks, 32 * m, lane), ob[ks], M);
+#pragma unroll
+                for (int i = 0; i < 16; i++) x += (double)St[m][i] * (double)M[i];
+                acc += x;
+            }
+        }
+
+        // ---- St <- a^n St + n a^n S + (k (n-1-j) a^{n-1-j})^T V, then S <- a^n S + (k a^{n-1-j})^T V
+        {
+            bf16x8 vb[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) vb[ks] = tr_operand(sm.v, PITCH, ks, 32 * w, lane);
+            const float an = sm.apow[n], nan_ = (float)n * sm.apow[n];
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+#pragma unroll
+                for (int i = 0; i < 16; i++) St[m][i] = an * St[m][i] + nan_ * Sm[m][i];
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) St[m] = mfma(tr_operand(sm.kt2, PITCH, ks, 32 * m, lane), vb[ks], St[m]);
+#pragma unroll
+                for (int i = 0; i < 16; i++) Sm[m][i] *= an;
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) Sm[m] = mfma(tr_operand(sm.kt, PITCH, ks, 32 * m, lane), vb[ks], Sm[m]);
+            }
+        }
+    }
+
+    if (STATE_ONLY) {
+        float* ds = part_s + (ub * (G - 1) + g) * (int64_t)D * D;
+        float* dt = part_st + (ub * (G - 1) + g) * (int64_t)D * D;
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                ds[r * D + 32 * w + n32] = Sm[m][i];
+                dt[r * D + 32 * w + n32] = St[m][i];
+            }
+        if (tid < D) part_decay[(ub * (G - 1) + g) * D + tid] = decay_pow(lam, (int)(t_end - t_begin));
+        return;
+    }
+    if (g == G - 1 && ds_out) {  // <ds_out, dS_out / dlambda>
+        const float* dso = ds_out + bh * sstride + (int64_t)seg * D * D;
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                acc += (double)St[m][i] * (double)dso[r * D + 32 * w + n32];
+            }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) sm.red[w] = acc;
+    __syncthreads();
+    if (tid == 0) part[ub * G + g] = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+}
+
+// St_loc[g] += l A S_end[g-1] for the state pass's slots g = 1..G-2 (S already scanned in place).
+__global__ __launch_bounds__(256) void dlam_fixup_kernel(float* __restrict__ part_st, const float* __restrict__ part_s,
+                                                         const float* __restrict__ decay, int64_t H, int nseg, int G,
+                                                         int ell) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // element of one state
+    const int g = blockIdx.y + 1;
+    const int64_t ub = blockIdx.z;
+    if (e >= (int64_t)D * D) return;
+    const int64_t h = (ub / nseg) % H;
+    const float f = (float)ell * decay_pow(decay[h], ell);
+    part_st[(ub * (G - 1) + g) * (int64_t)D * D + e] += f * part_s[(ub * (G - 1) + g - 1) * (int64_t)D * D + e];
+}
+
+// d lambda_h = sum over batch, segments and sub-segments of the inter-chunk and intra-chunk parts
+// (part and intra: [units][G] each).
+__global__ __launch_bounds__(256) void dlam_final_kernel(const double* __restrict__ part,
+                                                         const double* __restrict__ intra,
+                                                         float* __restrict__ d_decay, int64_t B, int64_t H, int nseg,
+                                                         int G) {
+    const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (h >= H) return;
+    double s = 0.0;
+    for (int64_t b = 0; b < B; b++)
+        for (int p = 0; p < nseg; p++) {
+            const int64_t o = ((b * H + h) * nseg + p) * (int64_t)G;
+            for (int y = 0; y < G; y++) s += part[o + y] + intra[o + y];
+        }
+    d_decay[h] = (float)s;
+}
+
+hipError_t launch_dlam(const BwdArgs& a, int G, int cps, float* ps, float* pst, float* pdec, double* part,
+                       const double* intra) {
+    const int64_t units = a.B * a.H * a.nseg;
+    const __bf16* q = (const __bf16*)a.q;
+    const __bf16* k = (const __bf16*)a.k;
+    const __bf16* v = (const __bf16*)a.v;
+    const __bf16* d_o = (const __bf16*)a.d_o;
+    hipError_t e;
+    if (G > 1) {
+        LA_TRACED(a.tr, "chunk_bwd_dlam_state_pass",
+                  bwd_dlam_kernel<true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                      q, k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, ps, pst, pdec, nullptr, nullptr,
+                      nullptr, a.H, a.L, a.nseg, G, cps));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_state_scan(ps, pdec, ps, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess) return e;
+        if (G > 2) {
+            LA_TRACED(a.tr, "chunk_bwd_dlam_fixup",
+                      dlam_fixup_kernel<<<dim3(D * D / 256, (unsigned)(G - 2), (unsigned)units), 256, 0, a.stream>>>(
+                          pst, ps, a.decay, a.H, a.nseg, G, cps * C));
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if ((e = launch_state_scan(pst, pdec, pst, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess) return e;
+    }
+    LA_TRACED(a.tr, "chunk_bwd_dlam",
+              bwd_dlam_kernel<false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                  q, k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, ps, pst, part,
+                  a.H, a.L, a.nseg, G, cps));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    LA_TRACED(a.tr, "chunk_bwd_dlam_final",
+              dlam_final_kernel<<<(unsigned)((a.H + 255) / 256), 256, 0, a.stream>>>(part, intra, a.d_decay, a.B, a.H,
+                                                                                     a.nseg, G));
+    return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* f_decay, float* b_state,
-                       float* b_decay) {
+                       float* b_decay, double* intra_part) {
     const int64_t units = a.B * a.H * a.nseg;
     const __bf16* q = (const __bf16*)a.q;
     const __bf16* k = (const __bf16*)a.k;
@@ -568,7 +812,7 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
         LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass",
                   bwd_dkdv_kernel<MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
                       q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state, b_decay,
-                      nullptr, a.H, a.L, a.nseg, G, cps));
+                      nullptr, nullptr, a.H, a.L, a.nseg, G, cps));
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_state_scan(b_state, b_decay, b_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
             return e;
@@ -576,7 +820,7 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
     LA_TRACED(a.tr, "chunk_bwd_dkdv",
               bwd_dkdv_kernel<MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
                   q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out, a.ds_in,
-                  nullptr, nullptr, b_state, a.H, a.L, a.nseg, G, cps));
+                  nullptr, nullptr, b_state, intra_part, a.H, a.L, a.nseg, G, cps));
     return hipGetLastError();
 }
 
@@ -584,7 +828,7 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
 
 bool chunk_bwd_mfma_supported(const BwdArgs& a) {
     return a.bf16 && a.dk == D && a.dv == D && a.chunk == C && a.L > 0 && a.B * a.H > 0 &&
-           (a.mode == DECAY_NONE || (a.mode == DECAY_HEAD && !a.d_decay));
+           (a.mode == DECAY_NONE || a.mode == DECAY_HEAD);
 }
 
 hipError_t launch_chunk_bwd_mfma(const BwdArgs& a) {
@@ -593,9 +837,13 @@ hipError_t launch_chunk_bwd_mfma(const BwdArgs& a) {
     int G, cps;
     mfma_split(sp, &G, &cps);
     const int64_t units = a.B * a.H * a.nseg;
-    // workspace: the forward and backward sub-segment states and decays
+    const bool dlam = a.mode == DECAY_HEAD && a.d_decay;
+    // workspace: fp64 partials of d lambda_h, then the sub-segment states and decays of the dq and
+    // dk/dv passes (and of S and dS/dlambda for d lambda_h)
+    const size_t n_dbl = dlam ? 2 * (size_t)units * G : 0;  // inter- and intra-chunk partials
     const size_t n_state = (size_t)units * (G - 1) * D * D, n_decay = (size_t)units * (G - 1) * D;
-    const size_t bytes = sizeof(float) * 2 * (n_state + n_decay);
+    const int nsets = dlam ? 4 : 2;  // state arrays: forward, backward (+ S, St)
+    const size_t bytes = sizeof(double) * n_dbl + sizeof(float) * (nsets * n_state + 3 * n_decay);
     char* ws = nullptr;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -603,13 +851,19 @@ hipError_t launch_chunk_bwd_mfma(const BwdArgs& a) {
     hipMemPool_t pool = workspace_pool(dev);
     if (!pool) return hipErrorOutOfMemory;
     if (bytes > 0 && (e = hipMallocFromPoolAsync((void**)&ws, bytes, pool, a.stream)) != hipSuccess) return e;
-    float* fp = (float*)ws;
+    double* part = n_dbl ? (double*)ws : nullptr;
+    double* intra = n_dbl ? part + (size_t)units * G : nullptr;
+    float* fp = (float*)(ws + sizeof(double) * n_dbl);
     float* f_state = n_state ? fp : nullptr;
     float* b_state = n_state ? fp + n_state : nullptr;
-    float* f_decay = n_decay ? fp + 2 * n_state : nullptr;
-    float* b_decay = n_decay ? fp + 2 * n_state + n_decay : nullptr;
-    e = a.mode == DECAY_HEAD ? launch_mode<DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay)
-                             : launch_mode<DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay);
+    float* l_state = (n_state && dlam) ? fp + 2 * n_state : nullptr;
+    float* lt_state = (n_state && dlam) ? fp + 3 * n_state : nullptr;
+    float* f_decay = n_decay ? fp + nsets * n_state : nullptr;
+    float* b_decay = n_decay ? fp + nsets * n_state + n_decay : nullptr;
+    float* l_decay = n_decay ? fp + nsets * n_state + 2 * n_decay : nullptr;
+    e = a.mode == DECAY_HEAD ? launch_mode<DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra)
+                             : launch_mode<DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr);
+    if (e == hipSuccess && dlam) e = launch_dlam(a, G, cps, l_state, lt_state, l_decay, part, intra);
     if (ws) {
         hipError_t f = hipFreeAsync(ws, a.stream);
         if (e == hipSuccess) e = f;

@@ -19,11 +19,13 @@ from gpu_util import ORC_MODE, TOL, host32, note, rel_err, to_dev
 pytestmark = pytest.mark.gpu
 
 W0 = WORKLOADS[0]
-# The decay derivative is formed from q dq - k dk, whose terms largely cancel: d lambda_h sums them
-# (t - t0 + 1)-weighted over whole segments (in fp64), the gate derivative takes reverse running sums
-# (in fp32).  The ~1e-7 relative rounding of dq and dk is magnified by that cancellation: measured up
-# to 7.4e-6 of max|ref| for d lambda_h at L = 192..2048 (1e-6 for the gate), hence 5e-5 here.
-TOL_DECAY = {"f32": 5e-5, "bf16": 5e-5}
+# fp32 path: the decay derivative is formed from q dq - k dk, whose terms largely cancel (d lambda_h
+# sums them (t - t0 + 1)-weighted over whole segments in fp64, the gate derivative takes reverse
+# running sums in fp32); the ~1e-7 relative rounding of dq and dk is magnified by that cancellation:
+# measured up to 7.4e-6 of max|ref| for d lambda_h at L = 192..2048 (1e-6 for the gate), hence 5e-5.
+# bf16 inputs: the general bf16 bound (the matrix-core d lambda_h, summed pair by pair with bf16
+# operands, measures about 1e-3).
+TOL_DECAY = {"f32": 5e-5, "bf16": 2e-2}
 
 
 def _case(mode, dtype, dk, dv, L, chunk, nseg, seed, B=2, H=2, s_in=True, ds_out=True):
@@ -143,9 +145,13 @@ def test_bwd_bf16_matrix_core_subsegments(mode, L, nseg, H):
     _compare(got, _oracle(w, inp, gr, nseg), "bf16", mode)
 
 
-@pytest.mark.parametrize("L", [192, 1000])
-def test_bwd_bf16_head_decay_derivative_takes_the_fp32_path(L):
-    """Asking for the head-decay derivative at bf16, d = 128 gives the fp32-accurate result."""
-    note(f"la_chunk_bwd bf16 d=128 head decay derivative L={L}")
-    w, inp, gr = _case("head", "bf16", 128, 128, L, 64, 1, seed=600 + L, B=1, H=2)
-    _compare(_gpu(w, inp, gr, 1), _oracle(w, inp, gr, 1), "bf16", "head")
+@pytest.mark.parametrize("L,nseg,B", [(192, 1, 1), (1000, 1, 1), (2048, 2, 2), (4096, 1, 1)])
+def test_bwd_bf16_matrix_core_head_decay_derivative(L, nseg, B):
+    """d lambda_h on the matrix-core path (bf16, d = 128): summed pair by pair with dS/dlambda carried
+    beside S, composed across sub-segments; one or several sub-segments, two segments, two batches."""
+    note(f"la_chunk_bwd bf16 d=128 head decay derivative L={L} nseg={nseg} B={B}")
+    w, inp, gr = _case("head", "bf16", 128, 128, L, 64, nseg, seed=600 + L, B=B, H=3)
+    got = _gpu(w, inp, gr, nseg)
+    ref = _oracle(w, inp, gr, nseg)
+    print(f"  d_decay rel err {rel_err(got[3], ref[3]):.2e}")
+    _compare(got, ref, "bf16", "head")
