@@ -89,10 +89,11 @@ def kernel_roofline(w, step, kernels):
 
 
 class BackwardStep:
-    """One backward pass (la_chunk_bwd) over a workload's inputs with seeded d_o and ds_out, the
-    decays held fixed (no decay derivative).  Outputs are allocated once."""
+    """One backward pass (la_chunk_bwd) over a workload's inputs with seeded d_o and ds_out; with
+    ``want_decay`` also the decay derivative (learned decays), else the decays are held fixed.
+    Outputs are allocated once."""
 
-    def __init__(self, w):
+    def __init__(self, w, want_decay=False):
         import torch
 
         from chunked_scan_amd.inputs import make_grads, make_inputs
@@ -103,46 +104,49 @@ class BackwardStep:
         self.dq = torch.empty_like(self.inp["q"])
         self.dk = torch.empty_like(self.inp["k"])
         self.dv = torch.empty_like(self.inp["v"])
+        self.want_decay = want_decay and w.mode != "none"
 
     def run(self, timers=None):
         from chunked_scan_amd import binding
 
         i, g = self.inp, self.gr
         binding.la_chunk_bwd(i["q"], i["k"], i["v"], g["d_o"], i["decay"], i["s_in"], g["ds_out"], mode=self.w.mode,
-                             chunk=self.w.chunk, want_decay=False, dq=self.dq, dk=self.dk, dv=self.dv,
+                             chunk=self.w.chunk, want_decay=self.want_decay, dq=self.dq, dk=self.dk, dv=self.dv,
                              timer=(timers or {}).get("fwd"))
 
 
 def backward_legs(stream):
-    """la_chunk_bwd at the plain (B=1) and head-decay (B=2) shapes, decays fixed: median time,
-    tokens/s, GB/s on the compulsory bytes (q, k, v, d_o read once, dq, dk, dv written once) and
-    per-kernel means."""
+    """la_chunk_bwd at the plain (B=1) and head-decay (B=2) shapes, decays fixed, and at the
+    head-decay shape with d lambda_h (learned decays): median time, tokens/s, GB/s on the compulsory
+    bytes (q, k, v, d_o read once, dq, dk, dv written once) and per-kernel means."""
     import torch
 
     from chunked_scan_amd.inputs import WORKLOADS
 
     backward = {}
-    for wid in (1, 2):
+    for wid, want_decay in ((1, False), (2, False), (2, True)):
         wb = WORKLOADS[wid]
-        log(f"[bench] backward: workload {wid} {wb.name}")
-        sb = BackwardStep(wb)
+        key = wb.name + (" + d_lambda" if want_decay else "")
+        log(f"[bench] backward: workload {wid} {key}")
+        sb = BackwardStep(wb, want_decay)
         for _ in range(60):  # >= 20 ms of work: settled clocks
             sb.run()
         torch.cuda.synchronize()
         st = step_stats(sb, 30, stream)
-        ks, _ = kernel_stats(sb, 30, stream)
+        ks, _ = kernel_stats(sb, 30, stream, capacity=16)
         th = wb.B * wb.H * wb.L
         # compulsory bytes (bf16): q, k, v, d_o read once, dq, dk, dv written once
         comp = th * 2 * (wb.dk + wb.dk + wb.dv + wb.dv) + th * 2 * (wb.dk + wb.dk + wb.dv)
         gbs = comp / (st["median_us"] * 1e-6) / 1e9
-        backward[wb.name] = dict(
-            what="la_chunk_bwd: dq, dk, dv, ds_in (decay held fixed)", B=wb.B, H=wb.H, L=wb.L, decay=wb.decay,
+        backward[key] = dict(
+            what="la_chunk_bwd: dq, dk, dv, ds_in" + (", d lambda_h" if want_decay else " (decay held fixed)"),
+            B=wb.B, H=wb.H, L=wb.L, decay=wb.decay,
             tokens_per_s=round(wb.B * wb.L / (st["median_us"] * 1e-6), 1), per_step_us=st,
             compulsory_bytes=comp, gbps_on_compulsory_bytes=round(gbs, 1),
             hbm_frac_on_compulsory_bytes=round(gbs / HBM_PEAK_GBS, 4),
             kernels={n: {k: round(v, 2) for k, v in d.items()} for n, d in ks.items()})
-        log(f"[bench]   backward {wb.name}: median {st['median_us']:.1f} us, "
-            f"{backward[wb.name]['tokens_per_s']:.3e} tokens/s, {gbs:.0f} GB/s on compulsory bytes; " +
+        log(f"[bench]   backward {key}: median {st['median_us']:.1f} us, "
+            f"{backward[key]['tokens_per_s']:.3e} tokens/s, {gbs:.0f} GB/s on compulsory bytes; " +
             ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in ks.items()))
         del sb
         torch.cuda.empty_cache()
@@ -170,14 +174,14 @@ def step_stats(step, steps, stream, scratch=None):
                 std_us=round(statistics.pstdev(t), 2), min_us=round(min(t), 2))
 
 
-def kernel_stats(step, steps, stream):
+def kernel_stats(step, steps, stream, capacity=8):
     """Mean duration of every library kernel over ``steps`` steps, from the events the library
     records around each kernel on its stream."""
     import torch
 
     from chunked_scan_amd import binding
 
-    timers = [{c: binding.KernelTimer(8) for c in ("fwd", "cum", "scan", "corr")} for _ in range(steps)]
+    timers = [{c: binding.KernelTimer(capacity) for c in ("fwd", "cum", "scan", "corr")} for _ in range(steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)

@@ -28,7 +28,7 @@ EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_decayed", "la_chunk_bwd", "la_state_sca
            "la_cumdecay", "la_status_str", "la_supported", "la_version")
 
 
-TRACE_MAX = 8
+TRACE_MAX = 16
 
 
 class Trace(ctypes.Structure):

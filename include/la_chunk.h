@@ -65,7 +65,7 @@ typedef enum la_decay_mode { LA_DECAY_NONE = 0, LA_DECAY_HEAD = 1, LA_DECAY_GATE
  * every kernel it enqueues (up to capacity) records start[i] just before and stop[i] just after
  * the launch on the call's stream and stores a static kernel name in name[i].  The events are
  * caller-created hipEvent_t handles; the caller reads them after synchronising. */
-#define LA_TRACE_MAX_KERNELS 8
+#define LA_TRACE_MAX_KERNELS 16
 typedef struct la_trace {
     void* start[LA_TRACE_MAX_KERNELS];
     void* stop[LA_TRACE_MAX_KERNELS];
@@ -187,9 +187,12 @@ la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, cons
  *            the others' is what a backward state scan carries between segments), in the
  *            state_stride layout, or NULL.
  *   chunk  : 16, 32 or 64.
- * No output may overlap an input or another output.  Arithmetic is fp32 with fp32 accumulation;
- * bf16 outputs are rounded once, to nearest even.  May allocate temporary device workspace from
- * the same stream-ordered pool as la_chunk_fwd (a float per token and key dim in gate mode).
+ * No output may overlap an input or another output.  bf16 inputs with dk = dv = 128, chunk 64 and
+ * no decay or head decay run on the matrix cores (bf16 operands, fp32 accumulation; the head-decay
+ * derivative summed token pair by token pair, in fp64 partial sums); every other shape, fp32 inputs
+ * and gate mode run in fp32 arithmetic.  bf16 outputs are rounded once, to nearest even.  May
+ * allocate temporary device workspace from the same stream-ordered pool as la_chunk_fwd (per
+ * sub-segment states; a float per token and key dim in gate mode).
  * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_DECAY, LA_ERR_ALIAS,
  * LA_ERR_UNSUPPORTED or LA_ERR_LAUNCH.
  */

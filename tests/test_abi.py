@@ -50,7 +50,7 @@ def test_shape_struct_layout():
     assert B.Shape.state_stride.offset == 56 and B.Shape.total_stride.offset == 64
     assert B.Shape.subseg_chunks.offset == 72
     assert B.Shape.stream.offset == 80 and B.Shape.trace.offset == 88 and ctypes.sizeof(B.Shape) == 96
-    assert B.Trace.capacity.offset == 128 and B.Trace.name.offset == 136 and ctypes.sizeof(B.Trace) == 200
+    assert B.Trace.capacity.offset == 256 and B.Trace.name.offset == 264 and ctypes.sizeof(B.Trace) == 392
 
 
 # fake device addresses, far apart, never dereferenced
@@ -160,7 +160,7 @@ def test_cumdecay_validation(lib):
 
 def test_trace_validation(lib):
     t = B.Trace()
-    t.capacity = 9  # more than LA_TRACE_MAX_KERNELS
+    t.capacity = 17  # more than LA_TRACE_MAX_KERNELS
     s = shape()
     s.trace = ctypes.pointer(t)
     assert fwd(lib, s) == SHAPE
