@@ -559,12 +559,15 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
 // and <ds_out, St> at the segment's end.  Sub-segments compose as S_out = A S_in + S_loc and
 // St_out = A St_in + l A S_in + St_loc (A = a^l over l tokens): a state pass leaves (S_loc, St_loc),
 // the S scan runs first, a fix-up adds l A S_in to each St_loc, and the St scan follows.
+template <bool SO>
 struct DlamSmem {
-    __bf16 v[TILE], o[TILE];
-    __bf16 qs[TILE];   // q_i a^{i+1}
-    __bf16 qs2[TILE];  // q_i (i+1) a^{i+1}
-    __bf16 kt[TILE];   // k_j a^{n-1-j}
-    __bf16 kt2[TILE];  // k_j (n-1-j) a^{n-1-j}
+    // the state pass keeps only v and the scaled k tiles (the others shrink to 16-byte stubs)
+    __bf16 v[TILE];
+    __bf16 o[SO ? 8 : TILE];
+    __bf16 qs[SO ? 8 : TILE];   // q_i a^{i+1}
+    __bf16 qs2[SO ? 8 : TILE];  // q_i (i+1) a^{i+1}
+    __bf16 kt[TILE];            // k_j a^{n-1-j}
+    __bf16 kt2[TILE];           // k_j (n-1-j) a^{n-1-j}
     float apow[C + 1];
     double red[NT / 64];
 };
@@ -577,7 +580,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     float* __restrict__ part_s, float* __restrict__ part_st, float* __restrict__ part_decay,  // state pass
     const float* __restrict__ init_s, const float* __restrict__ init_st,                     // output pass
     double* __restrict__ part, int64_t H, int64_t L, int nseg, int G, int cps) {
-    __shared__ __attribute__((aligned(16))) DlamSmem sm;
+    __shared__ __attribute__((aligned(16))) DlamSmem<STATE_ONLY> sm;
+    constexpr bool PF = true;  // (the output pass then spills 2 registers and is still ~20 us faster)
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -621,30 +625,48 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
     double acc = 0.0;
     const int nchunks = (int)((t_end - t_begin + C - 1) / C);
-    for (int c = 0; c < nchunks; c++) {
-        const int64_t t0 = t_begin + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, t_end - t0);
-        __syncthreads();  // the previous chunk is done with every LDS tile
+    // one chunk's tiles in registers (rows past the end read as zero)
+    u32x4 rk[PR], rv[PR], rq[STATE_ONLY ? 1 : PR], ro[STATE_ONLY ? 1 : PR];
+    auto load_chunk = [&](int cc) {
+        const int64_t t0c = t_begin + (int64_t)cc * C;
+        const int nc = (int)min((int64_t)C, t_end - t0c);
+        const u32x4 z = {0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < PR; r++) {
             const int p = tid + NT * r;
             const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            const int64_t off = (row_base + t0 + row) * D + c8;
-            const bool ok = row < n;
-            const u32x4 z = {0, 0, 0, 0};
-            const u32x4 xk = ok ? *(const u32x4*)(k + off) : z;
-            const int jr = max(n - 1 - row, 0);
-            *(u32x4*)(&sm.v[row * PITCH + c8]) = ok ? *(const u32x4*)(v + off) : z;
-            *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(xk, sm.apow[jr]);
-            *(u32x4*)(&sm.kt2[row * PITCH + c8]) = scale8s(xk, (float)jr * sm.apow[jr]);
+            const int64_t off = (row_base + t0c + row) * D + c8;
+            const bool ok = row < nc;
+            rk[r] = ok ? *(const u32x4*)(k + off) : z;
+            rv[r] = ok ? *(const u32x4*)(v + off) : z;
             if (!STATE_ONLY) {
-                const u32x4 xq = ok ? *(const u32x4*)(q + off) : z;
-                *(u32x4*)(&sm.o[row * PITCH + c8]) = ok ? *(const u32x4*)(d_o + off) : z;
-                *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(xq, sm.apow[row + 1]);
-                *(u32x4*)(&sm.qs2[row * PITCH + c8]) = scale8s(xq, (float)(row + 1) * sm.apow[row + 1]);
+                rq[r] = ok ? *(const u32x4*)(q + off) : z;
+                ro[r] = ok ? *(const u32x4*)(d_o + off) : z;
+            }
+        }
+    };
+    if (PF && nchunks > 0) load_chunk(0);
+    for (int c = 0; c < nchunks; c++) {
+        const int64_t t0 = t_begin + (int64_t)c * C;
+        const int n = (int)min((int64_t)C, t_end - t0);
+        __syncthreads();  // the previous chunk is done with every LDS tile
+        if (!PF) load_chunk(c);
+#pragma unroll
+        for (int r = 0; r < PR; r++) {
+            const int p = tid + NT * r;
+            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+            const int jr = max(n - 1 - row, 0);
+            *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
+            *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(rk[r], sm.apow[jr]);
+            *(u32x4*)(&sm.kt2[row * PITCH + c8]) = scale8s(rk[r], (float)jr * sm.apow[jr]);
+            if (!STATE_ONLY) {
+                *(u32x4*)(&sm.o[row * PITCH + c8]) = ro[r];
+                *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(rq[r], sm.apow[row + 1]);
+                *(u32x4*)(&sm.qs2[row * PITCH + c8]) = scale8s(rq[r], (float)(row + 1) * sm.apow[row + 1]);
             }
         }
         __syncthreads();
+        if (PF && c + 1 < nchunks) load_chunk(c + 1);  // the next chunk, while this one is computed
 
         if (!STATE_ONLY) {
             // ---- earlier tokens: <S, M'> + <St, M> over this wave's value columns
