@@ -232,6 +232,39 @@ def epsilon(w, inp, step, stream, steps: int = 20):
     return out
 
 
+def state_size_sweep(stream):
+    """The falsifier's question asked on one GPU: how the decomposition's cost (the device step
+    against one exact forward call, both on the same inputs) moves with the state size dk x dv at
+    a fixed token count (B1 H16 L16384, bf16, no decay, S_recv drawn N(0, 0.05)).  Median us."""
+    import math
+
+    import torch
+
+    from chunked_scan_amd.inputs import WORKLOADS, make_inputs
+    from chunked_scan_amd.pipeline import DeviceStep
+
+    out = {}
+    for d in (32, 64, 128):
+        w = WORKLOADS[1].scaled(dk=d, dv=d, qkv_std=1.0 / math.sqrt(d), s_in_std=0.05, seed=10 + d)
+        inp = make_inputs(w, "cuda")
+        step = DeviceStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk)
+        for _ in range(150):  # >= 20 ms of work: settled clocks
+            step.run()
+        torch.cuda.synchronize()
+        eps = epsilon(w, inp, step, stream, steps=30)
+        ks, _ = kernel_stats(step, 30, stream)
+        out[f"d{d}"] = dict(state_bytes=4 * d * d, zeco_step_us=eps["zeco_step"],
+                            one_call_exact_us=eps["one_call_exact"],
+                            overhead_us=round(eps["zeco_step"] - eps["one_call_exact"], 2),
+                            overhead_frac=round(eps["zeco_step"] / eps["one_call_exact"] - 1, 4),
+                            kernels={n: round(v["mean_us"], 2) for n, v in ks.items()})
+        log(f"[bench] state size d={d}: device step {eps['zeco_step']:.1f} us, one exact call "
+            f"{eps['one_call_exact']:.1f} us; " + ", ".join(f"{n} {v['mean_us']:.1f}" for n, v in ks.items()))
+        del step, inp
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, inp):
     import numpy as np
     import torch
@@ -376,8 +409,10 @@ def main():
             torch.cuda.empty_cache()
 
     backward = {}
+    sweep = {}
     if not args.no_alongside:
         backward = backward_legs(stream)
+        sweep = state_size_sweep(stream)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -446,6 +481,7 @@ def main():
         "overhead_one_gpu_us": eps,
         "alongside": alongside,
         "backward": backward,
+        "state_size_sweep": sweep,
     }
     print(json.dumps(out), flush=True)
 
