@@ -135,6 +135,16 @@ def backward_legs(stream):
         st = step_stats(sb, 30, stream)
         ks, _ = kernel_stats(sb, 30, stream, capacity=16)
         th = wb.B * wb.H * wb.L
+        # algorithmic bytes per token-head of each pass (bf16, d = 128): state passes read two tensors,
+        # the dq and d lambda output passes read three or four, the dk/dv output pass reads four and
+        # writes two
+        per_th = {"chunk_bwd_dq_state_pass": 512, "chunk_bwd_dq": 1024, "chunk_bwd_dkdv_state_pass": 512,
+                  "chunk_bwd_dkdv": 1536, "chunk_bwd_dlam_state_pass": 512, "chunk_bwd_dlam": 1024}
+        for name, d in ks.items():
+            if name in per_th and d["launches_per_step"] == 1:
+                by = per_th[name] * th
+                g = by / (d["mean_us"] * 1e-6) / 1e9
+                d.update(algorithmic_bytes=by, gbps=round(g, 1), hbm_frac=round(g / HBM_PEAK_GBS, 4))
         # compulsory bytes (bf16): q, k, v, d_o read once, dq, dk, dv written once
         comp = th * 2 * (wb.dk + wb.dk + wb.dv + wb.dv) + th * 2 * (wb.dk + wb.dk + wb.dv)
         gbs = comp / (st["median_us"] * 1e-6) / 1e9
@@ -294,6 +304,40 @@ def cpu_baseline(w, inp):
                        f"({platform.processor() or 'host'})"), (o_ref, s_ref)
 
 
+def cpu_baseline_backward(w, sample_len: int = 2048):
+    """The fp64 oracle's backward (token by token, whole state trajectory kept) timed on a bounded
+    sample of workload ``w``: every head, the first ``sample_len`` tokens, d_o and ds_out seeded as
+    on the GPU; repeated to about 5 s.  tokens/s = repetitions x B x sample_len / seconds."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import HEAD, NONE, GATE
+    from chunked_scan_amd.inputs import make_grads, make_inputs
+
+    ws = w.scaled(L=sample_len)
+    inp = make_inputs(ws, "cpu")
+    gr = make_grads(ws)
+    threads = min(16, oracle.default_threads())
+    f32 = lambda t: None if t is None else t.to(torch.float32).numpy()  # noqa: E731
+    mode = {"none": NONE, "head": HEAD, "gate": GATE}[w.mode]
+    s_in = None if inp["s_in"] is None else f32(inp["s_in"]).astype(np.float64)
+    ds_out = f32(gr["ds_out"]).astype(np.float64)
+    oracle.build(force=False)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.recurrence_bwd(f32(inp["q"]), f32(inp["k"]), f32(inp["v"]), f32(gr["d_o"]), mode, f32(inp["decay"]),
+                              s_in, ds_out, threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 5.0 or reps >= 100:
+            break
+    used = min(threads, ws.B * ws.H)
+    return dict(value=reps * ws.B * sample_len / dt, unit="tokens/s", cores=used, kind="oracle",
+                sample=f"backward of B={ws.B} H={ws.H} d={ws.dk}, first {sample_len} tokens x {reps} repetitions, "
+                       f"fp64 token-by-token derivatives in C, {dt:.1f} s on {used} threads")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,6 +456,9 @@ def main():
     sweep = {}
     if not args.no_alongside:
         backward = backward_legs(stream)
+        if not args.no_cpu_baseline and WORKLOADS[1].name in backward:
+            log("[bench] backward cpu_baseline (oracle, bounded sample)")
+            backward[WORKLOADS[1].name]["cpu_baseline"] = cpu_baseline_backward(WORKLOADS[1])
         sweep = state_size_sweep(stream)
 
     if args.calib_copy_mib:
