@@ -1,896 +1,23 @@
-// chunk_bwd_mfma.hip -- bf16 matrix-core (MFMA) backward pass for dk = dv = 128, chunk 64, with no
-// decay or one decay per head (the backward pass the ZeCO review page lists as a consequence of the
-// forward design, pith_extraction.forward_implications).  With a scalar decay per head the weight
-// of token j in output t is a^{t-j} whatever the key dim.
-//
-// dq runs forwards in time with the forward state S (dq_t = S_t d_o_t); dk and dv run backwards
-// with the state derivative D (G_t of the recurrence).  Each segment is split into G sub-segments
-// so that about 256 workgroups share the work; the decomposition identity of the same page
-// (pith_extraction.key_machinery) joins them: a state pass leaves each sub-segment's local state
-// (forwards: from zero, sub-segment 0 from s_in) or local derivative (backwards: from zero, the last
-// sub-segment from ds_out), a scan over them with each sub-segment's total decay (in reverse order
-// for D) gives every sub-segment its exact incoming state or derivative, and the output pass walks
-// each sub-segment from it.  Per chunk of n tokens:
-//   forwards (S = the state before the chunk):
-//     P'[i][j] = d_o_i . v_j a^{i-j}  (j <= i),      dq_i = sum_j P'[i][j] k_j + a^{i+1} S d_o_i
-//     S <- a^n S + sum_j a^{n-1-j} k_j v_j^T
-//   backwards (D = the derivative at the chunk's end):
-//     P'[i][j] as above, P[i][j] = q_i . k_j a^{i-j}  (j <= i)
-//     dk_j = sum_{i>=j} P'[i][j] q_i + a^{n-1-j} D v_j,   dv_j = sum_{i>=j} P[i][j] d_o_i + a^{n-1-j} D^T k_j
-//     D <- a^n D + sum_i a^{i+1} q_i d_o_i^T
-// The head-decay derivative is not taken from q . dq - k . dk (whose terms cancel by a factor that
-// grows with the sequence length over the decay length, beyond what the bf16 operands of these
-// products carry) but summed pair by pair with dS/dlambda carried beside S (bwd_dlam_kernel).
-//
-// Wave roles (both directions): wave w keeps value columns 32w..32w+31 of S or D (all 128 key rows)
-// in MFMA accumulators and computes the 32-wide column block w of dq / dk / dv; the causal 32x32
-// score blocks are shared out; the state's transpose reaches the products that need it through a
-// bf16 copy in LDS.
+// chunk_bwd_mfma.hip -- dispatch of the bf16 matrix-core backward (chunk_bwd_mfma_impl.h) over the
+// head dims it serves, each instantiated in its own translation unit (chunk_bwd_mfma_d<D>.hip).
 #include "la_device.h"
 #include "la_internal.h"
 
 namespace la {
-namespace {
 
-constexpr int C = 64;          // chunk length
-constexpr int D = 128;         // head dim (dk = dv)
-constexpr int NT = 256;        // lanes per workgroup
-constexpr int PITCH = D + 8;   // bf16 row pitch of the tiles: 16-byte aligned, conflict-free rows
-constexpr int PPITCH = C + 8;  // bf16 row pitch of the transposed score tiles
-constexpr int TILE = C * PITCH;
-constexpr int PR = C * D / 8 / NT;  // 16-byte pieces of a bf16 chunk tile per lane (4)
-constexpr int PIECES_ROW = D / 8;
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-__device__ __forceinline__ bf16x4 lds_tr16(const __bf16* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((__attribute__((address_space(3))) __bf16*)p));
-}
-__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ u32x4 scale8s(u32x4 w, float f) {
-    const float ff[8] = {f, f, f, f, f, f, f, f};
-    return scale8(w, ff);
-}
-// Operand of 16 consecutive tile rows (the contraction index) and 32 columns starting at col0,
-// read transposed: element e of lane (G16, i16) is tile[16 ks + (G16 >> 1) 8 + (i16 >> 2) + 4 (e >> 2)]
-// [col0 + (G16 & 1) 16 + (i16 & 3) 4 + (e & 3)].
-__device__ __forceinline__ bf16x8 tr_operand(const __bf16* tile, int pitch, int ks, int col0, int lane) {
-    const int G16 = lane >> 4, i16 = lane & 15;
-    const int col = col0 + (G16 & 1) * 16 + (i16 & 3) * 4;
-    const int tb = 16 * ks + (G16 >> 1) * 8 + (i16 >> 2);
-    return cat(lds_tr16(&tile[tb * pitch + col]), lds_tr16(&tile[(tb + 4) * pitch + col]));
-}
-
-// LDS of the backward-direction kernel; the state pass keeps only the tiles of the D update.
-template <int MODE, bool SO>
-struct BwdSmem {
-    // unused tiles shrink to 8 elements, which keeps every tile 16-byte aligned
-    __bf16 q[SO ? 8 : TILE];
-    __bf16 qs[(MODE == DECAY_HEAD || SO) ? TILE : 8];  // q_i a^{i+1} (head mode), q (state pass): the D update
-    __bf16 k[SO ? 8 : TILE];
-    __bf16 v[SO ? 8 : TILE];
-    __bf16 o[TILE];                  // d_o
-    __bf16 dm[SO ? 8 : D * PITCH];   // D as bf16, [key row][value column]
-    __bf16 pt[SO ? 8 : C * PPITCH];  // (P' w)^T: [j][i]
-    __bf16 pv[SO ? 8 : C * PPITCH];  // (P w)^T:  [j][i]
-    float apow[C + 1];               // a^m, m = 0..C (head mode)
-    double red[NT / 64];
-};
-
-static_assert(TILE % 8 == 0 && (D * PITCH) % 8 == 0 && (C * PPITCH) % 8 == 0, "16-byte tiles");
-
-// The chunk walk prefetches the next chunk (in walk order) into registers while the current one is
-// computed (PF; off, each chunk is loaded at its top).
-template <int MODE, bool STATE_ONLY>
-__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ ds_out,
-    int64_t sstride, __bf16* __restrict__ dk_out, __bf16* __restrict__ dv_out, float* __restrict__ ds_in,
-    float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
-    const float* __restrict__ init_state,                            // output pass: scanned D^(g)
-    double* __restrict__ intra_part,  // head mode, output pass: the intra-chunk part of d lambda_h, or null
-    int64_t H, int64_t L, int nseg, int G, int cps) {
-    __shared__ __attribute__((aligned(16))) BwdSmem<MODE, STATE_ONLY> sm;
-    constexpr bool PF = true;
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int lane = tid & 63;
-    const int n32 = lane & 31;
-    const int kg = lane >> 5;
-    const int64_t u = blockIdx.x;
-    const int gper = STATE_ONLY ? (G - 1) : G;
-    const int g = STATE_ONLY ? (int)(u % gper) + 1 : (int)(u % gper);  // the state pass covers 1..G-1
-    const int64_t ub = u / gper;  // (bh, seg)
-    const int seg = (int)(ub % nseg);
-    const int64_t bh = ub / nseg;
-    const int64_t h = bh % H;
-    const int64_t Lseg = L / nseg;
-    const int64_t tseg = (int64_t)seg * Lseg;
-    const int64_t t_begin = tseg + (int64_t)g * cps * C;
-    const int64_t t_end = min(t_begin + (int64_t)cps * C, tseg + Lseg);
-    const int64_t row_base = bh * L;
-    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
-
-    // ---- D at the sub-segment's end: key rows 32 m + (i / 4) 8 + kg 4 + i % 4, value column 32 w + n32
-    f32x16 Dm[4];
-    {
-        const float* src = nullptr;
-        if (g == G - 1) {
-            if (ds_out) src = ds_out + bh * sstride + (int64_t)seg * D * D;
-        } else if (!STATE_ONLY) {
-            src = init_state + (ub * (G - 1) + (G - 2 - g)) * (int64_t)D * D;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                Dm[m][i] = src ? src[r * D + 32 * w + n32] : 0.f;
-            }
-    }
-
-    if (MODE == DECAY_HEAD && tid <= C) sm.apow[tid] = decay_pow(lam, tid);  // read after the loop's first barrier
-    double hacc = 0.0;
-    const int nchunks = (int)((t_end - t_begin + C - 1) / C);
-    // one chunk's tiles in registers (rows past the end read as zero)
-    u32x4 rq[PR], ro[PR], rk[STATE_ONLY ? 1 : PR], rv[STATE_ONLY ? 1 : PR];
-    auto load_chunk = [&](int cc) {
-        const int64_t t0c = t_begin + (int64_t)cc * C;
-        const int nc = (int)min((int64_t)C, t_end - t0c);
-        const u32x4 z = {0, 0, 0, 0};
-#pragma unroll
-        for (int r = 0; r < PR; r++) {
-            const int p = tid + NT * r;
-            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            const int64_t off = (row_base + t0c + row) * D + c8;
-            const bool ok = row < nc;
-            rq[r] = ok ? *(const u32x4*)(q + off) : z;
-            ro[r] = ok ? *(const u32x4*)(d_o + off) : z;
-            if (!STATE_ONLY) {
-                rk[r] = ok ? *(const u32x4*)(k + off) : z;
-                rv[r] = ok ? *(const u32x4*)(v + off) : z;
-            }
-        }
-    };
-    if (PF && nchunks > 0) load_chunk(nchunks - 1);
-    for (int c = nchunks - 1; c >= 0; c--) {
-        const int64_t t0 = t_begin + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, t_end - t0);
-        __syncthreads();  // the previous chunk is done with every LDS tile
-        if (!PF) load_chunk(c);
-
-        // ---- stage the chunk and D as bf16
-#pragma unroll
-        for (int r = 0; r < PR; r++) {
-            const int p = tid + NT * r;
-            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            if (MODE == DECAY_HEAD) *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(rq[r], sm.apow[row + 1]);
-            else if (STATE_ONLY) *(u32x4*)(&sm.qs[row * PITCH + c8]) = rq[r];
-            *(u32x4*)(&sm.o[row * PITCH + c8]) = ro[r];
-            if (!STATE_ONLY) {
-                *(u32x4*)(&sm.q[row * PITCH + c8]) = rq[r];
-                *(u32x4*)(&sm.k[row * PITCH + c8]) = rk[r];
-                *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
-            }
-        }
-        if (!STATE_ONLY) {
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-#pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                    sm.dm[r * PITCH + 32 * w + n32] = (__bf16)Dm[m][i];
-                }
-        }
-        __syncthreads();
-        if (PF && c > 0) load_chunk(c - 1);  // the previous chunk, while this one is computed
-        // the q side of the D update: q a^{i+1} (head mode), else q itself
-        const __bf16* qsd = (MODE == DECAY_HEAD || STATE_ONLY) ? sm.qs : sm.q;
-
-        // d_o operands of this wave's value columns for the four 16-token slabs
-        bf16x8 ob[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++) ob[ks] = tr_operand(sm.o, PITCH, ks, 32 * w, lane);
-
-        if (!STATE_ONLY) {
-            // ---- causal score blocks (row block = i, column block = j) (0,0), (1,0), (1,1) on waves 0, 1, 2,
-            // P' and P of a block on the same wave: written transposed with the weight a^{i-j} and the
-            // mask j <= i; head mode with intra_part also sums (i - j) a^{i-j} P[i][j] P'[i][j], the
-            // intra-chunk token pairs' share of d lambda_h, from the unrounded scores
-            if (w < 3) {
-                const int ib = (w == 0) ? 0 : 1, jb = (w == 2) ? 1 : 0;
-                f32x16 po = {}, pq = {};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ks++) {
-                    const int ka = ks * 16 + kg * 8;
-                    po = mfma(*(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ka]),
-                              *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ka]), po);
-                    pq = mfma(*(const bf16x8*)(&sm.q[(ib * 32 + n32) * PITCH + ka]),
-                              *(const bf16x8*)(&sm.k[(jb * 32 + n32) * PITCH + ka]), pq);
-                }
-#pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);  // i index
-                    const int col = jb * 32 + n32;                               // j index
-                    float wgt = (col > row) ? 0.f : 1.f;
-                    if (MODE == DECAY_HEAD) {
-                        wgt *= sm.apow[max(row - col, 0)];
-                        if (intra_part && col < row) hacc += (double)((float)(row - col) * wgt) * ((double)po[i] * (double)pq[i]);
-                    }
-                    sm.pt[col * PPITCH + row] = (__bf16)(po[i] * wgt);
-                    sm.pv[col * PPITCH + row] = (__bf16)(pq[i] * wgt);
-                }
-            }
-            __syncthreads();  // score tiles complete
-
-            // ---- dk, column block w (key dims 32 w ..), and dv, column block w (value columns 32 w ..)
-            bf16x8 qb[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) qb[ks] = tr_operand(sm.q, PITCH, ks, 32 * w, lane);
-            // D's own columns as B operands (key-row order permuted as the A reads below)
-            bf16x8 db[8];
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-#pragma unroll
-                for (int hh = 0; hh < 2; hh++) {
-                    bf16x8 x;
-#pragma unroll
-                    for (int j = 0; j < 8; j++) x[j] = (__bf16)Dm[m][8 * hh + j];
-                    db[2 * m + hh] = x;
-                }
-#pragma unroll
-            for (int jb = 0; jb < 2; jb++) {
-                // dk: a^{n-1-j} (V D^T) + (P' w)^T Q
-                f32x16 acc = {};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ks * 16 + kg * 8]);
-                    const bf16x8 b = *(const bf16x8*)(&sm.dm[(32 * w + n32) * PITCH + ks * 16 + kg * 8]);
-                    acc = mfma(a, b, acc);
-                }
-                if (MODE == DECAY_HEAD) {
-#pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int j = jb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= sm.apow[max(n - 1 - j, 0)];
-                    }
-                }
-#pragma unroll
-                for (int ks = 2 * jb; ks < 4; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.pt[(jb * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
-                    acc = mfma(a, qb[ks], acc);
-                }
-                __bf16* drow = dk_out + (row_base + t0 + jb * 32) * D + 32 * w + n32;
-#pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int j = (i >> 2) * 8 + kg * 4 + (i & 3);
-                    if (jb * 32 + j < n) drow[j * D] = (__bf16)acc[i];
-                }
-                // dv: a^{n-1-j} (K D) + (P w)^T d_o
-                acc = f32x16{};
-                const __bf16* krow = &sm.k[(jb * 32 + n32) * PITCH + kg * 4];
-#pragma unroll
-                for (int m = 0; m < 4; m++)
-#pragma unroll
-                    for (int hh = 0; hh < 2; hh++) {
-                        const int d0 = 32 * m + 16 * hh;
-                        acc = mfma(cat(*(const bf16x4*)(krow + d0), *(const bf16x4*)(krow + d0 + 8)), db[2 * m + hh],
-                                   acc);
-                    }
-                if (MODE == DECAY_HEAD) {
-#pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int j = jb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= sm.apow[max(n - 1 - j, 0)];
-                    }
-                }
-#pragma unroll
-                for (int ks = 2 * jb; ks < 4; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.pv[(jb * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
-                    acc = mfma(a, ob[ks], acc);
-                }
-                __bf16* vrow = dv_out + (row_base + t0 + jb * 32) * D + 32 * w + n32;
-#pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int j = (i >> 2) * 8 + kg * 4 + (i & 3);
-                    if (jb * 32 + j < n) vrow[j * D] = (__bf16)acc[i];
-                }
-            }
-        }
-
-        // ---- D <- a^n D + (q a^{i+1})^T d_o
-        {
-            const float fh = (MODE == DECAY_HEAD) ? sm.apow[n] : 1.f;
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-                if (MODE == DECAY_HEAD) {
-#pragma unroll
-                    for (int i = 0; i < 16; i++) Dm[m][i] *= fh;
-                }
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) Dm[m] = mfma(tr_operand(qsd, PITCH, ks, 32 * m, lane), ob[ks], Dm[m]);
-            }
-        }
-    }
-
-    // ---- the derivative at the sub-segment's start
-    float* dst = nullptr;
-    if (STATE_ONLY) dst = part_state + (ub * (G - 1) + (G - 1 - g)) * (int64_t)D * D;
-    else if (g == 0 && ds_in) dst = ds_in + bh * sstride + (int64_t)seg * D * D;
-    if (dst) {
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                dst[r * D + 32 * w + n32] = Dm[m][i];
-            }
-    }
-    if (STATE_ONLY && tid < D) {  // the total decay over this sub-segment, per key dim
-        const float tot = (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
-        part_decay[(ub * (G - 1) + (G - 1 - g)) * D + tid] = tot;
-    }
-    if (MODE == DECAY_HEAD && !STATE_ONLY && intra_part) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) hacc += __shfl_xor(hacc, off);
-        __syncthreads();
-        if (lane == 0) sm.red[w] = hacc;
-        __syncthreads();
-        if (tid == 0) intra_part[ub * G + g] = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
-    }
-}
-
-
-// LDS of the forward-direction kernel; the state pass keeps only the tiles of the state update.
-template <bool SO>
-struct DqSmem {
-    // unused tiles shrink to 8 elements, which keeps every tile 16-byte aligned
-    __bf16 o[SO ? 8 : TILE];  // d_o
-    __bf16 v[TILE];
-    __bf16 k[SO ? 8 : TILE];  // k (the P' K product)
-    __bf16 kt[TILE];          // k_j a^{n-1-j} (the state update)
-    __bf16 sm[SO ? 8 : D * PITCH];  // S as bf16, [key row][value column]
-    __bf16 p[SO ? 8 : C * PPITCH];  // P' w, [i][j]
-    float apow[C + 1];              // a^m, m = 0..C (head mode)
-};
-
-template <int MODE, bool STATE_ONLY>
-__global__ __launch_bounds__(NT) void bwd_dq_kernel(
-    const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ s_in,
-    const float* __restrict__ ds_out, int64_t sstride, __bf16* __restrict__ dq,
-    float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
-    const float* __restrict__ init_state,                            // output pass: scanned states
-    int64_t H, int64_t L, int nseg, int G, int cps) {
-    __shared__ __attribute__((aligned(16))) DqSmem<STATE_ONLY> sm;
-    constexpr bool PF = true;
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int lane = tid & 63;
-    const int n32 = lane & 31;
-    const int kg = lane >> 5;
-    const int64_t u = blockIdx.x;
-    const int gper = STATE_ONLY ? (G - 1) : G;
-    const int g = (int)(u % gper);  // the state pass covers 0..G-2
-    const int64_t ub = u / gper;
-    const int seg = (int)(ub % nseg);
-    const int64_t bh = ub / nseg;
-    const int64_t h = bh % H;
-    const int64_t Lseg = L / nseg;
-    const int64_t tseg = (int64_t)seg * Lseg;
-    const int64_t t_begin = tseg + (int64_t)g * cps * C;
-    const int64_t t_end = min(t_begin + (int64_t)cps * C, tseg + Lseg);
-    const int64_t row_base = bh * L;
-    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
-
-    // ---- the state entering the sub-segment: key rows 32 m + (i / 4) 8 + kg 4 + i % 4, column 32 w + n32
-    f32x16 Sm[4];
-    {
-        const float* src = nullptr;
-        if (g == 0) {
-            if (seg == 0 && s_in) src = s_in + bh * (int64_t)D * D;
-        } else if (!STATE_ONLY) {
-            src = init_state + (ub * (G - 1) + (g - 1)) * (int64_t)D * D;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                Sm[m][i] = src ? src[r * D + 32 * w + n32] : 0.f;
-            }
-    }
-
-    if (MODE == DECAY_HEAD && tid <= C) sm.apow[tid] = decay_pow(lam, tid);  // read after the loop's first barrier
-    const int nchunks = (int)((t_end - t_begin + C - 1) / C);
-    // one chunk's tiles in registers (rows past the end read as zero)
-    u32x4 rk[PR], rv[PR], ro[STATE_ONLY ? 1 : PR];
-    auto load_chunk = [&](int cc) {
-        const int64_t t0c = t_begin + (int64_t)cc * C;
-        const int nc = (int)min((int64_t)C, t_end - t0c);
-        const u32x4 z = {0, 0, 0, 0};
-#pragma unroll
-        for (int r = 0; r < PR; r++) {
-            const int p = tid + NT * r;
-            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            const int64_t off = (row_base + t0c + row) * D + c8;
-            const bool ok = row < nc;
-            rk[r] = ok ? *(const u32x4*)(k + off) : z;
-            rv[r] = ok ? *(const u32x4*)(v + off) : z;
-            if (!STATE_ONLY) ro[r] = ok ? *(const u32x4*)(d_o + off) : z;
-        }
-    };
-    if (PF && nchunks > 0) load_chunk(0);
-    for (int c = 0; c < nchunks; c++) {
-        const int64_t t0 = t_begin + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, t_end - t0);
-        __syncthreads();  // the previous chunk is done with every LDS tile
-        if (!PF) load_chunk(c);
-#pragma unroll
-        for (int r = 0; r < PR; r++) {
-            const int p = tid + NT * r;
-            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
-            if (MODE == DECAY_HEAD) *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(rk[r], sm.apow[max(n - 1 - row, 0)]);
-            else *(u32x4*)(&sm.kt[row * PITCH + c8]) = rk[r];
-            if (!STATE_ONLY) {
-                *(u32x4*)(&sm.k[row * PITCH + c8]) = rk[r];
-                *(u32x4*)(&sm.o[row * PITCH + c8]) = ro[r];
-            }
-        }
-        if (!STATE_ONLY) {
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-#pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                    sm.sm[r * PITCH + 32 * w + n32] = (__bf16)Sm[m][i];
-                }
-        }
-        __syncthreads();
-        if (PF && c + 1 < nchunks) load_chunk(c + 1);  // the next chunk, while this one is computed
-
-        bf16x8 vb[4];  // v operands of this wave's value columns, four 16-token slabs
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++) vb[ks] = tr_operand(sm.v, PITCH, ks, 32 * w, lane);
-
-        if (!STATE_ONLY) {
-            // ---- P' blocks (0,0), (1,0), (1,1) on waves 0, 2, 3: weight a^{i-j}, mask j <= i
-            if (w != 1) {
-                const int ib = w >> 1, jb = (w == 3) ? 1 : 0;
-                f32x16 acc = {};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ks * 16 + kg * 8]);
-                    const bf16x8 b = *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ks * 16 + kg * 8]);
-                    acc = mfma(a, b, acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                    const int col = jb * 32 + n32;
-                    float val = acc[i];
-                    if (MODE == DECAY_HEAD) val *= sm.apow[max(row - col, 0)];
-                    if (col > row) val = 0.f;
-                    sm.p[row * PPITCH + col] = (__bf16)val;
-                }
-            }
-            __syncthreads();  // P' complete
-
-            // ---- dq, column block w (key dims 32 w ..): a^{i+1} (d_o S^T) + P' K
-            bf16x8 kb[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) kb[ks] = tr_operand(sm.k, PITCH, ks, 32 * w, lane);
-#pragma unroll
-            for (int ib = 0; ib < 2; ib++) {
-                f32x16 acc = {};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ks * 16 + kg * 8]);
-                    const bf16x8 b = *(const bf16x8*)(&sm.sm[(32 * w + n32) * PITCH + ks * 16 + kg * 8]);
-                    acc = mfma(a, b, acc);
-                }
-                if (MODE == DECAY_HEAD) {
-#pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= sm.apow[row + 1];
-                    }
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2 * (ib + 1); ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.p[(ib * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
-                    acc = mfma(a, kb[ks], acc);
-                }
-                const int64_t rbase = row_base + t0 + ib * 32;
-#pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int row = (i >> 2) * 8 + kg * 4 + (i & 3);
-                    if (ib * 32 + row < n) dq[(rbase + row) * D + 32 * w + n32] = (__bf16)acc[i];
-                }
-            }
-        }
-
-        // ---- S <- a^n S + (K a^{n-1-j})^T V
-        {
-            const float fh = (MODE == DECAY_HEAD) ? sm.apow[n] : 1.f;
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-                if (MODE == DECAY_HEAD) {
-#pragma unroll
-                    for (int i = 0; i < 16; i++) Sm[m][i] *= fh;
-                }
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) Sm[m] = mfma(tr_operand(sm.kt, PITCH, ks, 32 * m, lane), vb[ks], Sm[m]);
-            }
-        }
-    }
-
-    if (STATE_ONLY) {
-        float* dst = part_state + (ub * (G - 1) + g) * (int64_t)D * D;
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                dst[r * D + 32 * w + n32] = Sm[m][i];
-            }
-        if (tid < D) {
-            const float tot = (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
-            part_decay[(ub * (G - 1) + g) * D + tid] = tot;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
-// The head-decay derivative, summed without cancellation.  Every pair of tokens j <= t contributes
-// (t - j) a^{t-j} (q_t . k_j)(v_j . d_o_t) to d lambda_h (and s_in, seen as a token before the
-// segment, and ds_out add their own terms).  Per chunk of n tokens, with S the state and
-// St = dS/dlambda before it:
-//   intra-chunk pairs  sum_{j<=i} (i - j) a^{i-j} P[i][j] P'[i][j]       (P = q k^T, P' = d_o v^T),
-//                      summed by the dk/dv output pass, which forms both score matrices anyway
-//   earlier tokens     <S, M'> + <St, M>,   M = sum_i a^{i+1} q_i d_o_i^T,   M' = sum_i (i+1) a^{i+1} q_i d_o_i^T
-//   St <- a^n St + n a^n S + sum_j (n-1-j) a^{n-1-j} k_j v_j^T,   S <- a^n S + sum_j a^{n-1-j} k_j v_j^T
-// and <ds_out, St> at the segment's end.  Sub-segments compose as S_out = A S_in + S_loc and
-// St_out = A St_in + l A S_in + St_loc (A = a^l over l tokens): a state pass leaves (S_loc, St_loc),
-// the S scan runs first, a fix-up adds l A S_in to each St_loc, and the St scan follows.
-template <bool SO>
-struct DlamSmem {
-    // the state pass keeps only v and the scaled k tiles (the others shrink to 16-byte stubs)
-    __bf16 v[TILE];
-    __bf16 o[SO ? 8 : TILE];
-    __bf16 qs[SO ? 8 : TILE];   // q_i a^{i+1}
-    __bf16 qs2[SO ? 8 : TILE];  // q_i (i+1) a^{i+1}
-    __bf16 kt[TILE];            // k_j a^{n-1-j}
-    __bf16 kt2[TILE];           // k_j (n-1-j) a^{n-1-j}
-    float apow[C + 1];
-    double red[NT / 64];
-};
-
-template <bool STATE_ONLY>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dlam_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ s_in,
-    const float* __restrict__ ds_out, int64_t sstride,
-    float* __restrict__ part_s, float* __restrict__ part_st, float* __restrict__ part_decay,  // state pass
-    const float* __restrict__ init_s, const float* __restrict__ init_st,                     // output pass
-    double* __restrict__ part, int64_t H, int64_t L, int nseg, int G, int cps) {
-    __shared__ __attribute__((aligned(16))) DlamSmem<STATE_ONLY> sm;
-    constexpr bool PF = true;  // (the output pass then spills 2 registers and is still ~20 us faster)
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int lane = tid & 63;
-    const int n32 = lane & 31;
-    const int kg = lane >> 5;
-    const int64_t u = blockIdx.x;
-    const int gper = STATE_ONLY ? (G - 1) : G;
-    const int g = (int)(u % gper);  // the state pass covers 0..G-2
-    const int64_t ub = u / gper;
-    const int seg = (int)(ub % nseg);
-    const int64_t bh = ub / nseg;
-    const int64_t h = bh % H;
-    const int64_t Lseg = L / nseg;
-    const int64_t tseg = (int64_t)seg * Lseg;
-    const int64_t t_begin = tseg + (int64_t)g * cps * C;
-    const int64_t t_end = min(t_begin + (int64_t)cps * C, tseg + Lseg);
-    const int64_t row_base = bh * L;
-    const float lam = decay[h];
-    if (tid <= C) sm.apow[tid] = decay_pow(lam, tid);  // read after the loop's first barrier
-
-    // S and St entering the sub-segment (value columns 32 w + n32, key rows as the accumulators)
-    f32x16 Sm[4], St[4];
-    {
-        const float* src = nullptr;
-        const float* srct = nullptr;
-        if (g == 0) {
-            if (seg == 0 && s_in) src = s_in + bh * (int64_t)D * D;
-        } else if (!STATE_ONLY) {
-            src = init_s + (ub * (G - 1) + (g - 1)) * (int64_t)D * D;
-            srct = init_st + (ub * (G - 1) + (g - 1)) * (int64_t)D * D;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                Sm[m][i] = src ? src[r * D + 32 * w + n32] : 0.f;
-                St[m][i] = srct ? srct[r * D + 32 * w + n32] : 0.f;
-            }
-    }
-
-    double acc = 0.0;
-    const int nchunks = (int)((t_end - t_begin + C - 1) / C);
-    // one chunk's tiles in registers (rows past the end read as zero)
-    u32x4 rk[PR], rv[PR], rq[STATE_ONLY ? 1 : PR], ro[STATE_ONLY ? 1 : PR];
-    auto load_chunk = [&](int cc) {
-        const int64_t t0c = t_begin + (int64_t)cc * C;
-        const int nc = (int)min((int64_t)C, t_end - t0c);
-        const u32x4 z = {0, 0, 0, 0};
-#pragma unroll
-        for (int r = 0; r < PR; r++) {
-            const int p = tid + NT * r;
-            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            const int64_t off = (row_base + t0c + row) * D + c8;
-            const bool ok = row < nc;
-            rk[r] = ok ? *(const u32x4*)(k + off) : z;
-            rv[r] = ok ? *(const u32x4*)(v + off) : z;
-            if (!STATE_ONLY) {
-                rq[r] = ok ? *(const u32x4*)(q + off) : z;
-                ro[r] = ok ? *(const u32x4*)(d_o + off) : z;
-            }
-        }
-    };
-    if (PF && nchunks > 0) load_chunk(0);
-    for (int c = 0; c < nchunks; c++) {
-        const int64_t t0 = t_begin + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, t_end - t0);
-        __syncthreads();  // the previous chunk is done with every LDS tile
-        if (!PF) load_chunk(c);
-#pragma unroll
-        for (int r = 0; r < PR; r++) {
-            const int p = tid + NT * r;
-            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            const int jr = max(n - 1 - row, 0);
-            *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
-            *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(rk[r], sm.apow[jr]);
-            *(u32x4*)(&sm.kt2[row * PITCH + c8]) = scale8s(rk[r], (float)jr * sm.apow[jr]);
-            if (!STATE_ONLY) {
-                *(u32x4*)(&sm.o[row * PITCH + c8]) = ro[r];
-                *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(rq[r], sm.apow[row + 1]);
-                *(u32x4*)(&sm.qs2[row * PITCH + c8]) = scale8s(rq[r], (float)(row + 1) * sm.apow[row + 1]);
-            }
-        }
-        __syncthreads();
-        if (PF && c + 1 < nchunks) load_chunk(c + 1);  // the next chunk, while this one is computed
-
-        if (!STATE_ONLY) {
-            // ---- earlier tokens: <S, M'> + <St, M> over this wave's value columns
-            bf16x8 ob[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) ob[ks] = tr_operand(sm.o, PITCH, ks, 32 * w, lane);
-#pragma unroll
-            for (int m = 0; m < 4; m++) {  // one 16-register product at a time: M' with S, then M with St
-                f32x16 M = {};
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) M = mfma(tr_operand(sm.qs2, PITCH, ks, 32 * m, lane), ob[ks], M);
-                double x = 0.0;
-#pragma unroll
-                for (int i = 0; i < 16; i++) x += (double)Sm[m][i] * (double)M[i];
-                M = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) M = mfma(tr_operand(sm.qs, PITCH, ks, 32 * m, lane), ob[ks], M);
-#pragma unroll
-                for (int i = 0; i < 16; i++) x += (double)St[m][i] * (double)M[i];
-                acc += x;
-            }
-        }
-
-        // ---- St <- a^n St + n a^n S + (k (n-1-j) a^{n-1-j})^T V, then S <- a^n S + (k a^{n-1-j})^T V
-        {
-            bf16x8 vb[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) vb[ks] = tr_operand(sm.v, PITCH, ks, 32 * w, lane);
-            const float an = sm.apow[n], nan_ = (float)n * sm.apow[n];
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-#pragma unroll
-                for (int i = 0; i < 16; i++) St[m][i] = an * St[m][i] + nan_ * Sm[m][i];
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) St[m] = mfma(tr_operand(sm.kt2, PITCH, ks, 32 * m, lane), vb[ks], St[m]);
-#pragma unroll
-                for (int i = 0; i < 16; i++) Sm[m][i] *= an;
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) Sm[m] = mfma(tr_operand(sm.kt, PITCH, ks, 32 * m, lane), vb[ks], Sm[m]);
-            }
-        }
-    }
-
-    if (STATE_ONLY) {
-        float* ds = part_s + (ub * (G - 1) + g) * (int64_t)D * D;
-        float* dt = part_st + (ub * (G - 1) + g) * (int64_t)D * D;
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                ds[r * D + 32 * w + n32] = Sm[m][i];
-                dt[r * D + 32 * w + n32] = St[m][i];
-            }
-        if (tid < D) part_decay[(ub * (G - 1) + g) * D + tid] = decay_pow(lam, (int)(t_end - t_begin));
-        return;
-    }
-    if (g == G - 1 && ds_out) {  // <ds_out, dS_out / dlambda>
-        const float* dso = ds_out + bh * sstride + (int64_t)seg * D * D;
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                acc += (double)St[m][i] * (double)dso[r * D + 32 * w + n32];
-            }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) sm.red[w] = acc;
-    __syncthreads();
-    if (tid == 0) part[ub * G + g] = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
-}
-
-// St_loc[g] += l A S_end[g-1] for the state pass's slots g = 1..G-2 (S already scanned in place).
-__global__ __launch_bounds__(256) void dlam_fixup_kernel(float* __restrict__ part_st, const float* __restrict__ part_s,
-                                                         const float* __restrict__ decay, int64_t H, int nseg, int G,
-                                                         int ell) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // element of one state
-    const int g = blockIdx.y + 1;
-    const int64_t ub = blockIdx.z;
-    if (e >= (int64_t)D * D) return;
-    const int64_t h = (ub / nseg) % H;
-    const float f = (float)ell * decay_pow(decay[h], ell);
-    part_st[(ub * (G - 1) + g) * (int64_t)D * D + e] += f * part_s[(ub * (G - 1) + g - 1) * (int64_t)D * D + e];
-}
-
-// d lambda_h = sum over batch, segments and sub-segments of the inter-chunk and intra-chunk parts
-// (part and intra: [units][G] each).
-__global__ __launch_bounds__(256) void dlam_final_kernel(const double* __restrict__ part,
-                                                         const double* __restrict__ intra,
-                                                         float* __restrict__ d_decay, int64_t B, int64_t H, int nseg,
-                                                         int G) {
-    const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (h >= H) return;
-    double s = 0.0;
-    for (int64_t b = 0; b < B; b++)
-        for (int p = 0; p < nseg; p++) {
-            const int64_t o = ((b * H + h) * nseg + p) * (int64_t)G;
-            for (int y = 0; y < G; y++) s += part[o + y] + intra[o + y];
-        }
-    d_decay[h] = (float)s;
-}
-
-hipError_t launch_dlam(const BwdArgs& a, int G, int cps, float* ps, float* pst, float* pdec, double* part,
-                       const double* intra) {
-    const int64_t units = a.B * a.H * a.nseg;
-    const __bf16* q = (const __bf16*)a.q;
-    const __bf16* k = (const __bf16*)a.k;
-    const __bf16* v = (const __bf16*)a.v;
-    const __bf16* d_o = (const __bf16*)a.d_o;
-    hipError_t e;
-    if (G > 1) {
-        LA_TRACED(a.tr, "chunk_bwd_dlam_state_pass",
-                  bwd_dlam_kernel<true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                      q, k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, ps, pst, pdec, nullptr, nullptr,
-                      nullptr, a.H, a.L, a.nseg, G, cps));
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_state_scan(ps, pdec, ps, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess) return e;
-        if (G > 2) {
-            LA_TRACED(a.tr, "chunk_bwd_dlam_fixup",
-                      dlam_fixup_kernel<<<dim3(D * D / 256, (unsigned)(G - 2), (unsigned)units), 256, 0, a.stream>>>(
-                          pst, ps, a.decay, a.H, a.nseg, G, cps * C));
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
-        if ((e = launch_state_scan(pst, pdec, pst, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess) return e;
-    }
-    LA_TRACED(a.tr, "chunk_bwd_dlam",
-              bwd_dlam_kernel<false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                  q, k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, ps, pst, part,
-                  a.H, a.L, a.nseg, G, cps));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    LA_TRACED(a.tr, "chunk_bwd_dlam_final",
-              dlam_final_kernel<<<(unsigned)((a.H + 255) / 256), 256, 0, a.stream>>>(part, intra, a.d_decay, a.B, a.H,
-                                                                                     a.nseg, G));
-    return hipGetLastError();
-}
-
-template <int MODE>
-hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* f_decay, float* b_state,
-                       float* b_decay, double* intra_part) {
-    const int64_t units = a.B * a.H * a.nseg;
-    const __bf16* q = (const __bf16*)a.q;
-    const __bf16* k = (const __bf16*)a.k;
-    const __bf16* v = (const __bf16*)a.v;
-    const __bf16* d_o = (const __bf16*)a.d_o;
-    hipError_t e;
-    // dq: forward state pass, scan, output pass
-    if (G > 1) {
-        LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
-                  bwd_dq_kernel<MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                      k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr,
-                      a.H, a.L, a.nseg, G, cps));
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_state_scan(f_state, f_decay, f_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
-            return e;
-    }
-    LA_TRACED(a.tr, "chunk_bwd_dq",
-              bwd_dq_kernel<MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                  k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, f_state,
-                  a.H, a.L, a.nseg, G, cps));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // dk, dv: backward state pass, reverse-order scan, output pass
-    if (G > 1) {
-        LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass",
-                  bwd_dkdv_kernel<MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                      q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state, b_decay,
-                      nullptr, nullptr, a.H, a.L, a.nseg, G, cps));
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_state_scan(b_state, b_decay, b_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
-            return e;
-    }
-    LA_TRACED(a.tr, "chunk_bwd_dkdv",
-              bwd_dkdv_kernel<MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                  q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out, a.ds_in,
-                  nullptr, nullptr, b_state, intra_part, a.H, a.L, a.nseg, G, cps));
-    return hipGetLastError();
-}
-
-}  // namespace
+hipError_t launch_bwd_mfma_d32(const BwdArgs& a);
+hipError_t launch_bwd_mfma_d64(const BwdArgs& a);
+hipError_t launch_bwd_mfma_d128(const BwdArgs& a);
 
 bool chunk_bwd_mfma_supported(const BwdArgs& a) {
-    return a.bf16 && a.dk == D && a.dv == D && a.chunk == C && a.L > 0 && a.B * a.H > 0 &&
-           (a.mode == DECAY_NONE || a.mode == DECAY_HEAD);
+    return a.bf16 && a.dk == a.dv && (a.dk == 32 || a.dk == 64 || a.dk == 128) && a.chunk == 64 && a.L > 0 &&
+           a.B * a.H > 0 && (a.mode == DECAY_NONE || a.mode == DECAY_HEAD);
 }
 
 hipError_t launch_chunk_bwd_mfma(const BwdArgs& a) {
-    FwdArgs sp;
-    sp.B = a.B; sp.H = a.H; sp.L = a.L; sp.nseg = a.nseg; sp.subseg_chunks = 0;
-    int G, cps;
-    mfma_split(sp, &G, &cps);
-    const int64_t units = a.B * a.H * a.nseg;
-    const bool dlam = a.mode == DECAY_HEAD && a.d_decay;
-    // workspace: fp64 partials of d lambda_h, then the sub-segment states and decays of the dq and
-    // dk/dv passes (and of S and dS/dlambda for d lambda_h)
-    const size_t n_dbl = dlam ? 2 * (size_t)units * G : 0;  // inter- and intra-chunk partials
-    const size_t n_state = (size_t)units * (G - 1) * D * D, n_decay = (size_t)units * (G - 1) * D;
-    const int nsets = dlam ? 4 : 2;  // state arrays: forward, backward (+ S, St)
-    const size_t bytes = sizeof(double) * n_dbl + sizeof(float) * (nsets * n_state + 3 * n_decay);
-    char* ws = nullptr;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    hipMemPool_t pool = workspace_pool(dev);
-    if (!pool) return hipErrorOutOfMemory;
-    if (bytes > 0 && (e = hipMallocFromPoolAsync((void**)&ws, bytes, pool, a.stream)) != hipSuccess) return e;
-    double* part = n_dbl ? (double*)ws : nullptr;
-    double* intra = n_dbl ? part + (size_t)units * G : nullptr;
-    float* fp = (float*)(ws + sizeof(double) * n_dbl);
-    float* f_state = n_state ? fp : nullptr;
-    float* b_state = n_state ? fp + n_state : nullptr;
-    float* l_state = (n_state && dlam) ? fp + 2 * n_state : nullptr;
-    float* lt_state = (n_state && dlam) ? fp + 3 * n_state : nullptr;
-    float* f_decay = n_decay ? fp + nsets * n_state : nullptr;
-    float* b_decay = n_decay ? fp + nsets * n_state + n_decay : nullptr;
-    float* l_decay = n_decay ? fp + nsets * n_state + 2 * n_decay : nullptr;
-    e = a.mode == DECAY_HEAD ? launch_mode<DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra)
-                             : launch_mode<DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr);
-    if (e == hipSuccess && dlam) e = launch_dlam(a, G, cps, l_state, lt_state, l_decay, part, intra);
-    if (ws) {
-        hipError_t f = hipFreeAsync(ws, a.stream);
-        if (e == hipSuccess) e = f;
-    }
-    return e;
+    if (a.dk == 128) return launch_bwd_mfma_d128(a);
+    if (a.dk == 64) return launch_bwd_mfma_d64(a);
+    return launch_bwd_mfma_d32(a);
 }
 
 }  // namespace la

@@ -131,26 +131,28 @@ def test_bwd_chunk_invariance():
         _compare(got, ref, "f32", "gate")
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("mode", ["none", "head"])
 @pytest.mark.parametrize("L,nseg,H", [(192, 1, 2), (1000, 1, 2), (2048, 2, 2), (640, 1, 3)])
-def test_bwd_bf16_matrix_core_subsegments(mode, L, nseg, H):
-    """bf16, d = 128, chunk 64, no decay or a fixed head decay (no decay derivative requested) runs on
-    the matrix-core kernels, which split each segment into sub-segments (state passes, scans of the
-    state and of its derivative, output passes): lengths that give one or several sub-segments and a
-    ragged last chunk."""
-    note(f"la_chunk_bwd bf16 d=128 matrix-core mode={mode} L={L} nseg={nseg} H={H}")
-    w, inp, gr = _case(mode, "bf16", 128, 128, L, 64, nseg, seed=500 + L + H, B=1, H=H)
+def test_bwd_bf16_matrix_core_subsegments(mode, L, nseg, H, d):
+    """bf16, d = 32 / 64 / 128, chunk 64, no decay or a fixed head decay (no decay derivative
+    requested) runs on the matrix-core kernels, which split each segment into sub-segments (state
+    passes, scans of the state and of its derivative, output passes): lengths that give one or several
+    sub-segments and a ragged last chunk."""
+    note(f"la_chunk_bwd bf16 d={d} matrix-core mode={mode} L={L} nseg={nseg} H={H}")
+    w, inp, gr = _case(mode, "bf16", d, d, L, 64, nseg, seed=500 + L + H + d, B=1, H=H)
     got = _gpu(w, inp, gr, nseg, want_decay=False)
     assert got[3] is None
     _compare(got, _oracle(w, inp, gr, nseg), "bf16", mode)
 
 
-@pytest.mark.parametrize("L,nseg,B", [(192, 1, 1), (1000, 1, 1), (2048, 2, 2), (4096, 1, 1)])
-def test_bwd_bf16_matrix_core_head_decay_derivative(L, nseg, B):
-    """d lambda_h on the matrix-core path (bf16, d = 128): summed pair by pair with dS/dlambda carried
-    beside S, composed across sub-segments; one or several sub-segments, two segments, two batches."""
-    note(f"la_chunk_bwd bf16 d=128 head decay derivative L={L} nseg={nseg} B={B}")
-    w, inp, gr = _case("head", "bf16", 128, 128, L, 64, nseg, seed=600 + L, B=B, H=3)
+@pytest.mark.parametrize("d,L,nseg,B", [(128, 192, 1, 1), (128, 1000, 1, 1), (128, 2048, 2, 2), (128, 4096, 1, 1),
+                                        (64, 1000, 1, 1), (64, 2048, 2, 2), (32, 1000, 1, 1), (32, 640, 1, 2)])
+def test_bwd_bf16_matrix_core_head_decay_derivative(d, L, nseg, B):
+    """d lambda_h on the matrix-core path (bf16): summed pair by pair with dS/dlambda carried beside S,
+    composed across sub-segments; one or several sub-segments, two segments, two batches."""
+    note(f"la_chunk_bwd bf16 d={d} head decay derivative L={L} nseg={nseg} B={B}")
+    w, inp, gr = _case("head", "bf16", d, d, L, 64, nseg, seed=600 + L + d, B=B, H=3)
     got = _gpu(w, inp, gr, nseg)
     ref = _oracle(w, inp, gr, nseg)
     print(f"  d_decay rel err {rel_err(got[3], ref[3]):.2e}")
