@@ -263,13 +263,21 @@ def state_size_sweep(stream):
         torch.cuda.synchronize()
         eps = epsilon(w, inp, step, stream, steps=30)
         ks, _ = kernel_stats(step, 30, stream)
+        bw = BackwardStep(w)
+        for _ in range(40):
+            bw.run()
+        torch.cuda.synchronize()
+        bwd = step_stats(bw, 20, stream)["median_us"]
+        del bw
         out[f"d{d}"] = dict(state_bytes=4 * d * d, zeco_step_us=eps["zeco_step"],
                             one_call_exact_us=eps["one_call_exact"],
                             overhead_us=round(eps["zeco_step"] - eps["one_call_exact"], 2),
                             overhead_frac=round(eps["zeco_step"] / eps["one_call_exact"] - 1, 4),
+                            backward_us=bwd,
                             kernels={n: round(v["mean_us"], 2) for n, v in ks.items()})
         log(f"[bench] state size d={d}: device step {eps['zeco_step']:.1f} us, one exact call "
-            f"{eps['one_call_exact']:.1f} us; " + ", ".join(f"{n} {v['mean_us']:.1f}" for n, v in ks.items()))
+            f"{eps['one_call_exact']:.1f} us, backward {bwd:.1f} us; " +
+            ", ".join(f"{n} {v['mean_us']:.1f}" for n, v in ks.items()))
         del step, inp
         torch.cuda.empty_cache()
     return out

@@ -106,7 +106,7 @@ hipMemPool_t workspace_pool(int dev);
 // Chunked backward with fp32 arithmetic on VALU (chunk_bwd_generic.hip): every shape the generic
 // forward takes.
 hipError_t launch_chunk_bwd_generic(const BwdArgs& a);
-// bf16 MFMA backward (chunk_bwd_mfma.hip): dk = dv = 128, chunk 64, no decay or head decay.
+// bf16 MFMA backward (chunk_bwd_mfma*.hip): dk = dv in {32, 64, 128}, chunk 64, no decay or head decay.
 bool chunk_bwd_mfma_supported(const BwdArgs& a);
 hipError_t launch_chunk_bwd_mfma(const BwdArgs& a);
 

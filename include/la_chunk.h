@@ -187,8 +187,8 @@ la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, cons
  *            the others' is what a backward state scan carries between segments), in the
  *            state_stride layout, or NULL.
  *   chunk  : 16, 32 or 64.
- * No output may overlap an input or another output.  bf16 inputs with dk = dv = 128, chunk 64 and
- * no decay or head decay run on the matrix cores (bf16 operands, fp32 accumulation; the head-decay
+ * No output may overlap an input or another output.  bf16 inputs with dk = dv in {32, 64, 128},
+ * chunk 64 and no decay or head decay run on the matrix cores (bf16 operands, fp32 accumulation; the head-decay
  * derivative summed token pair by token pair, in fp64 partial sums); every other shape, fp32 inputs
  * and gate mode run in fp32 arithmetic.  bf16 outputs are rounded once, to nearest even.  May
  * allocate temporary device workspace from the same stream-ordered pool as la_chunk_fwd (per
