@@ -158,6 +158,47 @@ def test_cumdecay_validation(lib):
     assert lib.la_cumdecay(P(DEC), None, None, ctypes.byref(shape(mode=1))) == OK    # nothing requested
 
 
+# more fake addresses for the backward's derivative arguments
+DO, DSO, DQ, DK, DV, DDEC, DSIN = (0x10000000000 * (i + 8) for i in range(7))
+
+
+def bwd(lib, shp, q=Q, k=K, v=V, dec=None, s_in=None, d_o=DO, ds_out=None, dq=DQ, dk=DK, dv=DV, d_dec=None,
+        ds_in=None, chunk=64):
+    P = ctypes.c_void_p
+    return lib.la_chunk_bwd(P(q), P(k), P(v), P(dec), P(s_in), P(d_o), P(ds_out), P(dq), P(dk), P(dv), P(d_dec),
+                            P(ds_in), ctypes.byref(shp), chunk)
+
+
+def test_bwd_validation(lib):
+    assert lib.la_chunk_bwd(*([None] * 12), None, 64) == NULL
+    assert bwd(lib, shape(L=-1)) == SHAPE
+    assert bwd(lib, shape(nseg=0)) == SHAPE
+    assert bwd(lib, shape(L=100, nseg=3)) == SHAPE
+    assert bwd(lib, shape(), chunk=0) == SHAPE
+    assert bwd(lib, shape(), chunk=48) == UNSUP
+    assert bwd(lib, shape(dk=96)) == UNSUP
+    assert bwd(lib, shape(state_stride=64 * 64 - 1)) == SHAPE       # smaller than one segment's state
+    mixed = shape()
+    mixed.out_dtype = B.LA_F32
+    assert bwd(lib, mixed) == DTYPE
+    assert bwd(lib, shape(mode=3)) == DECAY
+    assert bwd(lib, shape(mode=0), dec=DEC) == DECAY                # none mode takes no decay
+    assert bwd(lib, shape(mode=0), d_dec=DDEC) == DECAY             # ... and returns no decay derivative
+    assert bwd(lib, shape(mode=1)) == NULL                          # head mode needs lambda_h
+    assert bwd(lib, shape(mode=2)) == NULL                          # gate mode needs g
+    for arg in ("q", "k", "v", "d_o", "dq", "dk", "dv"):
+        assert bwd(lib, shape(), **{arg: 0}) == NULL, arg
+    assert bwd(lib, shape(), dq=Q + 64) == ALIAS                    # dq overlaps q
+    assert bwd(lib, shape(), dv=DO) == ALIAS                        # dv overlaps d_o
+    assert bwd(lib, shape(), dk=DV + 128) == ALIAS                  # two outputs overlap
+    assert bwd(lib, shape(), ds_out=DSO, ds_in=DSO + 256) == ALIAS  # ds_in overlaps ds_out
+    assert bwd(lib, shape(mode=1), dec=DEC, d_dec=DEC) == ALIAS     # d lambda overwrites lambda
+    assert bwd(lib, shape(mode=2), dec=DEC, d_dec=DEC + 1024) == ALIAS
+    assert bwd(lib, shape(), s_in=S_IN, ds_in=S_IN) == ALIAS
+    # an empty problem validates and enqueues nothing
+    assert bwd(lib, shape(B=0), q=0, k=0, v=0, d_o=0, dq=0, dk=0, dv=0) == OK
+
+
 def test_trace_validation(lib):
     t = B.Trace()
     t.capacity = 17  # more than LA_TRACE_MAX_KERNELS
