@@ -20,6 +20,11 @@
 // to the segment's end.  GATE turns that into dg = d log a * (1 - sigmoid(g)) / gate_norm; HEAD
 // sums it over tokens, key dims, batch and segments: d lambda_h = sum (t - t0 + 1) dL/dB_t + Ls E.
 //
+// Gate mode factorises the pair weight, e^{B_i - B_j} = e^{B_i} e^{-B_j}, into q e^{B} and k e^{-B}
+// staged once per chunk, so the inner loops are plain multiply-adds; a chunk whose decay sum is below
+// -80 for one of the workgroup's key dims (where e^{-B} could leave fp32's range) keeps the
+// per-pair exponentials, so this path has no range restriction.
+//
 // Three sweeps, each workgroup owning a 32-wide slice of the state:
 //   bwd_dq_kernel  (forward in time, rows of dk): recomputes S, writes dq, q * dq (GATE) and
 //                  E = rowsum(S_out * ds_out);
@@ -33,7 +38,9 @@ namespace {
 
 constexpr int BC = 64;   // largest chunk
 constexpr int BD = 128;  // largest head dim
+constexpr int BDP = BD + 1;  // row pitch of [row][BD] tiles: odd, so rows a wave steps over fall in different banks
 constexpr int BS = 32;   // rows (dk) or columns (dv) of the state per workgroup
+constexpr float FACT_MIN = -80.f;  // lowest in-chunk log-decay sum for which e^{-B} is formed
 
 // Sum of x over the workgroup (256 threads), returned to thread 0.
 __device__ double block_sum(double x, double* red) {
@@ -53,8 +60,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const float* __restrict__ s_in, const T* __restrict__ d_o, const float* __restrict__ ds_out, int64_t sstride,
     T* __restrict__ dq, float* __restrict__ qdq, float* __restrict__ efin, double* __restrict__ hpart, int64_t H,
     int64_t L, int dk, int dv, int nseg, int C, float inv_norm) {
-    __shared__ float Vs[BC * BD], Os[BC * BD], Ks[BC * BS], Ps[BC * BC], Ss[BS * BD];
+    __shared__ float Vs[BC * BDP], Os[BC * BDP], Ks[BC * BS], Ps[BC * BC], Ss[BS * BDP];
     __shared__ float Bs[MODE == DECAY_GATE ? BC * BS : 1];
+    __shared__ float KH[MODE == DECAY_GATE ? BC * BS : 1], EB[MODE == DECAY_GATE ? BC * BS : 1];  // k e^{-B}, e^{B}
     __shared__ double red[256];
     const int tid = threadIdx.x;
     const int64_t unit = blockIdx.x;
@@ -63,10 +71,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const int r0 = blockIdx.y * BS, nr = min(BS, dk - r0);
     const int64_t Ls = L / nseg, t0 = (int64_t)seg * Ls;
     const float lam = MODE == DECAY_HEAD ? decay[h] : 0.f;
+    bool fact = false;  // gate mode: this chunk uses the factorised weights
 
     for (int e = tid; e < nr * dv; e += 256) {
         const int r = e / dv, c = e % dv;
-        Ss[r * BD + c] = (seg == 0 && s_in) ? s_in[(bh * dk + r0 + r) * dv + c] : 0.f;
+        Ss[r * BDP + c] = (seg == 0 && s_in) ? s_in[(bh * dk + r0 + r) * dv + c] : 0.f;
     }
     double hacc = 0.0;
     for (int64_t cs = 0; cs < Ls; cs += C) {
@@ -75,8 +84,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
         __syncthreads();
         for (int e = tid; e < n * dv; e += 256) {
             const int i = e / dv, c = e % dv;
-            Vs[i * BD + c] = io<T>::ld(v + (tb + i) * dv + c);
-            Os[i * BD + c] = io<T>::ld(d_o + (tb + i) * dv + c);
+            Vs[i * BDP + c] = io<T>::ld(v + (tb + i) * dv + c);
+            Os[i * BDP + c] = io<T>::ld(d_o + (tb + i) * dv + c);
         }
         for (int e = tid; e < n * nr; e += 256) {
             const int i = e / nr, r = e % nr;
@@ -86,36 +95,53 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
         }
         __syncthreads();
         if (MODE == DECAY_GATE) {
+            bool low = false;
             if (tid < nr) {
                 float run = 0.f;
                 for (int i = 0; i < n; i++) {
                     run += Bs[i * BS + tid];
                     Bs[i * BS + tid] = run;
                 }
+                low = run < FACT_MIN;
             }
-            __syncthreads();
+            fact = !__syncthreads_or(low);
+            if (fact) {
+                for (int e = tid; e < n * nr; e += 256) {
+                    const int i = e / nr, r = e % nr;
+                    const float b = Bs[i * BS + r];
+                    EB[i * BS + r] = expf(b);
+                    KH[i * BS + r] = Ks[i * BS + r] * expf(-b);
+                }
+                __syncthreads();
+            }
         }
         for (int e = tid; e < n * n; e += 256) {
             const int i = e / n, j = e % n;
             float p = 0.f;
             if (j <= i)
-                for (int c = 0; c < dv; c++) p += Os[i * BD + c] * Vs[j * BD + c];
+                for (int c = 0; c < dv; c++) p += Os[i * BDP + c] * Vs[j * BDP + c];
             Ps[i * BC + j] = p;
         }
         __syncthreads();
         for (int e = tid; e < n * nr; e += 256) {
             const int i = e / nr, r = e % nr;
             float acc = 0.f;
-            for (int j = 0; j <= i; j++) {
-                float w = Ps[i * BC + j] * Ks[j * BS + r];
-                if (MODE == DECAY_GATE) w *= expf(Bs[i * BS + r] - Bs[j * BS + r]);
-                if (MODE == DECAY_HEAD) w *= decay_pow(lam, i - j);
-                acc += w;
-            }
             float inter = 0.f;
-            for (int c = 0; c < dv; c++) inter += Ss[r * BD + c] * Os[i * BD + c];
-            if (MODE == DECAY_GATE) inter *= expf(Bs[i * BS + r]);
-            if (MODE == DECAY_HEAD) inter *= decay_pow(lam, i + 1);
+            for (int c = 0; c < dv; c++) inter += Ss[r * BDP + c] * Os[i * BDP + c];
+            if (MODE == DECAY_GATE && fact) {
+                for (int j = 0; j <= i; j++) acc += Ps[i * BC + j] * KH[j * BS + r];
+                acc = EB[i * BS + r] * (acc + inter);
+                inter = 0.f;
+            } else {
+                for (int j = 0; j <= i; j++) {
+                    float w = Ps[i * BC + j] * Ks[j * BS + r];
+                    if (MODE == DECAY_GATE) w *= expf(Bs[i * BS + r] - Bs[j * BS + r]);
+                    if (MODE == DECAY_HEAD) w *= decay_pow(lam, i - j);
+                    acc += w;
+                }
+                if (MODE == DECAY_GATE) inter *= expf(Bs[i * BS + r]);
+                if (MODE == DECAY_HEAD) inter *= decay_pow(lam, i + 1);
+            }
             const float g = acc + inter;
             const int64_t gi = (tb + i) * dk + r0 + r;
             io<T>::st(dq + gi, g);
@@ -125,18 +151,21 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
         __syncthreads();
         for (int e = tid; e < nr * dv; e += 256) {
             const int r = e / dv, c = e % dv;
-            float s = Ss[r * BD + c];
-            if (MODE == DECAY_GATE) {
+            float s = Ss[r * BDP + c];
+            if (MODE == DECAY_GATE && fact) {
+                for (int j = 0; j < n; j++) s += KH[j * BS + r] * Vs[j * BDP + c];
+                s *= EB[(n - 1) * BS + r];
+            } else if (MODE == DECAY_GATE) {
                 const float bl = Bs[(n - 1) * BS + r];
                 s *= expf(bl);
-                for (int j = 0; j < n; j++) s += Ks[j * BS + r] * expf(bl - Bs[j * BS + r]) * Vs[j * BD + c];
+                for (int j = 0; j < n; j++) s += Ks[j * BS + r] * expf(bl - Bs[j * BS + r]) * Vs[j * BDP + c];
             } else if (MODE == DECAY_HEAD) {
                 s *= decay_pow(lam, n);
-                for (int j = 0; j < n; j++) s += Ks[j * BS + r] * decay_pow(lam, n - 1 - j) * Vs[j * BD + c];
+                for (int j = 0; j < n; j++) s += Ks[j * BS + r] * decay_pow(lam, n - 1 - j) * Vs[j * BDP + c];
             } else {
-                for (int j = 0; j < n; j++) s += Ks[j * BS + r] * Vs[j * BD + c];
+                for (int j = 0; j < n; j++) s += Ks[j * BS + r] * Vs[j * BDP + c];
             }
-            Ss[r * BD + c] = s;
+            Ss[r * BDP + c] = s;
         }
     }
     __syncthreads();
@@ -146,7 +175,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
         float e = 0.f;
         if (ds_out) {
             const float* dso = ds_out + bh * sstride + ((int64_t)seg * dk + r0 + tid) * dv;
-            for (int c = 0; c < dv; c++) e += Ss[tid * BD + c] * dso[c];
+            for (int c = 0; c < dv; c++) e += Ss[tid * BDP + c] * dso[c];
         }
         if (MODE == DECAY_GATE && efin) efin[(bh * nseg + seg) * dk + r0 + tid] = e;
         if (MODE == DECAY_HEAD) hacc += (double)Ls * (double)e;
@@ -164,8 +193,10 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(
     float* __restrict__ ds_in, const float* __restrict__ qdq, const float* __restrict__ efin,
     float* __restrict__ d_decay, double* __restrict__ hpart, int64_t H, int64_t L, int dk, int dv, int nseg, int C,
     float inv_norm) {
-    __shared__ float Vs[BC * BD], Os[BC * BD], Qs[BC * BS], Ks[BC * BS], Ps[BC * BC], Ds[BS * BD];
+    __shared__ float Vs[BC * BDP], Os[BC * BDP], Qs[BC * BS], Ks[BC * BS], Ps[BC * BC], Ds[BS * BDP];
     __shared__ float Bs[MODE == DECAY_GATE ? BC * BS : 1], KD[MODE == DECAY_GATE ? BC * BS : 1];
+    __shared__ float QB[MODE == DECAY_GATE ? BC * BS : 1], EI[MODE == DECAY_GATE ? BC * BS : 1];  // q e^{B}, e^{-B}
+    __shared__ float ELs[MODE == DECAY_GATE ? BS : 1];  // e^{B_{n-1}}
     __shared__ double red[256];
     const int tid = threadIdx.x;
     const int64_t unit = blockIdx.x;
@@ -175,10 +206,11 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(
     const int64_t Ls = L / nseg, t0 = (int64_t)seg * Ls;
     const float lam = MODE == DECAY_HEAD ? decay[h] : 0.f;
     const bool want_gate = MODE == DECAY_GATE && d_decay && qdq && efin;
+    bool fact = false;  // gate mode: this chunk uses the factorised weights
 
     for (int e = tid; e < nr * dv; e += 256) {
         const int r = e / dv, c = e % dv;
-        Ds[r * BD + c] = ds_out ? ds_out[bh * sstride + ((int64_t)seg * dk + r0 + r) * dv + c] : 0.f;
+        Ds[r * BDP + c] = ds_out ? ds_out[bh * sstride + ((int64_t)seg * dk + r0 + r) * dv + c] : 0.f;
     }
     float carry = (want_gate && tid < nr) ? efin[(bh * nseg + seg) * dk + r0 + tid] : 0.f;
     double hacc = 0.0;
@@ -190,8 +222,8 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(
         __syncthreads();
         for (int e = tid; e < n * dv; e += 256) {
             const int i = e / dv, c = e % dv;
-            Vs[i * BD + c] = io<T>::ld(v + (tb + i) * dv + c);
-            Os[i * BD + c] = io<T>::ld(d_o + (tb + i) * dv + c);
+            Vs[i * BDP + c] = io<T>::ld(v + (tb + i) * dv + c);
+            Os[i * BDP + c] = io<T>::ld(d_o + (tb + i) * dv + c);
         }
         for (int e = tid; e < n * nr; e += 256) {
             const int i = e / nr, r = e % nr;
@@ -202,36 +234,54 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(
         }
         __syncthreads();
         if (MODE == DECAY_GATE) {
+            bool low = false;
             if (tid < nr) {
                 float run = 0.f;
                 for (int i = 0; i < n; i++) {
                     run += Bs[i * BS + tid];
                     Bs[i * BS + tid] = run;
                 }
+                low = run < FACT_MIN;
+                ELs[tid] = expf(run);
             }
-            __syncthreads();
+            fact = !__syncthreads_or(low);
+            if (fact) {
+                for (int e = tid; e < n * nr; e += 256) {
+                    const int i = e / nr, r = e % nr;
+                    const float b = Bs[i * BS + r];
+                    QB[i * BS + r] = Qs[i * BS + r] * expf(b);
+                    EI[i * BS + r] = expf(-b);
+                }
+                __syncthreads();
+            }
         }
         for (int e = tid; e < n * n; e += 256) {
             const int i = e / n, j = e % n;
             float p = 0.f;
             if (j <= i)
-                for (int c = 0; c < dv; c++) p += Os[i * BD + c] * Vs[j * BD + c];
+                for (int c = 0; c < dv; c++) p += Os[i * BDP + c] * Vs[j * BDP + c];
             Ps[i * BC + j] = p;
         }
         __syncthreads();
         for (int e = tid; e < n * nr; e += 256) {
             const int j = e / nr, r = e % nr;
             float acc = 0.f;
-            for (int i = j; i < n; i++) {
-                float w = Ps[i * BC + j] * Qs[i * BS + r];
-                if (MODE == DECAY_GATE) w *= expf(Bs[i * BS + r] - Bs[j * BS + r]);
-                if (MODE == DECAY_HEAD) w *= decay_pow(lam, i - j);
-                acc += w;
-            }
             float inter = 0.f;
-            for (int c = 0; c < dv; c++) inter += Ds[r * BD + c] * Vs[j * BD + c];
-            if (MODE == DECAY_GATE) inter *= expf(Bs[(n - 1) * BS + r] - Bs[j * BS + r]);
-            if (MODE == DECAY_HEAD) inter *= decay_pow(lam, n - 1 - j);
+            for (int c = 0; c < dv; c++) inter += Ds[r * BDP + c] * Vs[j * BDP + c];
+            if (MODE == DECAY_GATE && fact) {
+                for (int i = j; i < n; i++) acc += Ps[i * BC + j] * QB[i * BS + r];
+                acc = EI[j * BS + r] * (acc + ELs[r] * inter);
+                inter = 0.f;
+            } else {
+                for (int i = j; i < n; i++) {
+                    float w = Ps[i * BC + j] * Qs[i * BS + r];
+                    if (MODE == DECAY_GATE) w *= expf(Bs[i * BS + r] - Bs[j * BS + r]);
+                    if (MODE == DECAY_HEAD) w *= decay_pow(lam, i - j);
+                    acc += w;
+                }
+                if (MODE == DECAY_GATE) inter *= expf(Bs[(n - 1) * BS + r] - Bs[j * BS + r]);
+                if (MODE == DECAY_HEAD) inter *= decay_pow(lam, n - 1 - j);
+            }
             const float g = acc + inter;
             io<T>::st(dk_out + (tb + j) * dk + r0 + r, g);
             const float kg = Ks[j * BS + r] * g;
@@ -251,24 +301,27 @@ __global__ __launch_bounds__(256) void bwd_dk_kernel(
         // D rows carried to the previous chunk
         for (int e = tid; e < nr * dv; e += 256) {
             const int r = e / dv, c = e % dv;
-            float s = Ds[r * BD + c];
-            if (MODE == DECAY_GATE) {
+            float s = Ds[r * BDP + c];
+            if (MODE == DECAY_GATE && fact) {
+                s *= ELs[r];
+                for (int i = 0; i < n; i++) s += QB[i * BS + r] * Os[i * BDP + c];
+            } else if (MODE == DECAY_GATE) {
                 s *= expf(Bs[(n - 1) * BS + r]);
-                for (int i = 0; i < n; i++) s += Qs[i * BS + r] * expf(Bs[i * BS + r]) * Os[i * BD + c];
+                for (int i = 0; i < n; i++) s += Qs[i * BS + r] * expf(Bs[i * BS + r]) * Os[i * BDP + c];
             } else if (MODE == DECAY_HEAD) {
                 s *= decay_pow(lam, n);
-                for (int i = 0; i < n; i++) s += Qs[i * BS + r] * decay_pow(lam, i + 1) * Os[i * BD + c];
+                for (int i = 0; i < n; i++) s += Qs[i * BS + r] * decay_pow(lam, i + 1) * Os[i * BDP + c];
             } else {
-                for (int i = 0; i < n; i++) s += Qs[i * BS + r] * Os[i * BD + c];
+                for (int i = 0; i < n; i++) s += Qs[i * BS + r] * Os[i * BDP + c];
             }
-            Ds[r * BD + c] = s;
+            Ds[r * BDP + c] = s;
         }
     }
     __syncthreads();
     if (ds_in)
         for (int e = tid; e < nr * dv; e += 256) {
             const int r = e / dv, c = e % dv;
-            ds_in[bh * sstride + ((int64_t)seg * dk + r0 + r) * dv + c] = Ds[r * BD + c];
+            ds_in[bh * sstride + ((int64_t)seg * dk + r0 + r) * dv + c] = Ds[r * BDP + c];
         }
     if (MODE == DECAY_HEAD && hpart) {
         const double s = block_sum(hacc, red);
@@ -281,8 +334,10 @@ __global__ __launch_bounds__(256) void bwd_dv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ decay, const T* __restrict__ d_o,
     const float* __restrict__ ds_out, int64_t sstride, T* __restrict__ dv_out, int64_t H, int64_t L, int dk, int dv,
     int nseg, int C, float inv_norm) {
-    __shared__ float Qs[BC * BD], Ks[BC * BD], Os[BC * BS], Ps[BC * BC], Ds[BD * BS];
-    __shared__ float Bs[MODE == DECAY_GATE ? BC * BD : 1];
+    __shared__ float Qs[BC * BDP], Ks[BC * BDP], Os[BC * BS], Ps[BC * BC], Ds[BD * BS];
+    __shared__ float Bs[MODE == DECAY_GATE ? BC * BDP : 1];
+    __shared__ float ELd[MODE == DECAY_GATE ? BD : 1];  // e^{B_{n-1}} per key dim
+    bool fact = false;  // gate mode: this chunk's q, k tiles hold q e^{B} and k e^{-B}
     const int tid = threadIdx.x;
     const int64_t unit = blockIdx.x;
     const int seg = (int)(unit % nseg);
@@ -304,9 +359,9 @@ __global__ __launch_bounds__(256) void bwd_dv_kernel(
         for (int e = tid; e < n * dk; e += 256) {
             const int i = e / dk, d = e % dk;
             const int64_t gi = (tb + i) * dk + d;
-            Qs[i * BD + d] = io<T>::ld(q + gi);
-            Ks[i * BD + d] = io<T>::ld(k + gi);
-            if (MODE == DECAY_GATE) Bs[i * BD + d] = gate_logdecay(decay[gi], inv_norm);
+            Qs[i * BDP + d] = io<T>::ld(q + gi);
+            Ks[i * BDP + d] = io<T>::ld(k + gi);
+            if (MODE == DECAY_GATE) Bs[i * BDP + d] = gate_logdecay(decay[gi], inv_norm);
         }
         for (int e = tid; e < n * nc; e += 256) {
             const int i = e / nc, c = e % nc;
@@ -314,25 +369,37 @@ __global__ __launch_bounds__(256) void bwd_dv_kernel(
         }
         __syncthreads();
         if (MODE == DECAY_GATE) {
+            bool low = false;
             for (int d = tid; d < dk; d += 256) {
                 float run = 0.f;
                 for (int i = 0; i < n; i++) {
-                    run += Bs[i * BD + d];
-                    Bs[i * BD + d] = run;
+                    run += Bs[i * BDP + d];
+                    Bs[i * BDP + d] = run;
                 }
+                low = low || run < FACT_MIN;
+                ELd[d] = expf(run);
             }
-            __syncthreads();
+            fact = !__syncthreads_or(low);
+            if (fact) {
+                for (int e = tid; e < n * dk; e += 256) {
+                    const int i = e / dk, d = e % dk;
+                    const float b = Bs[i * BDP + d];
+                    Qs[i * BDP + d] *= expf(b);
+                    Ks[i * BDP + d] *= expf(-b);
+                }
+                __syncthreads();
+            }
         }
         // P[i][j] = sum_d q_i[d] k_j[d] e^{B_i[d] - B_j[d]}   (j <= i)
         for (int e = tid; e < n * n; e += 256) {
             const int i = e / n, j = e % n;
             float p = 0.f;
             if (j <= i) {
-                if (MODE == DECAY_GATE) {
+                if (MODE == DECAY_GATE && !fact) {
                     for (int d = 0; d < dk; d++)
-                        p += Qs[i * BD + d] * Ks[j * BD + d] * expf(Bs[i * BD + d] - Bs[j * BD + d]);
+                        p += Qs[i * BDP + d] * Ks[j * BDP + d] * expf(Bs[i * BDP + d] - Bs[j * BDP + d]);
                 } else {
-                    for (int d = 0; d < dk; d++) p += Qs[i * BD + d] * Ks[j * BD + d];
+                    for (int d = 0; d < dk; d++) p += Qs[i * BDP + d] * Ks[j * BDP + d];
                     if (MODE == DECAY_HEAD) p *= decay_pow(lam, i - j);
                 }
             }
@@ -344,11 +411,13 @@ __global__ __launch_bounds__(256) void bwd_dv_kernel(
             float acc = 0.f;
             for (int i = j; i < n; i++) acc += Ps[i * BC + j] * Os[i * BS + c];
             float inter = 0.f;
-            if (MODE == DECAY_GATE) {
-                const float* bl = Bs + (n - 1) * BD;
-                for (int d = 0; d < dk; d++) inter += Ks[j * BD + d] * expf(bl[d] - Bs[j * BD + d]) * Ds[d * BS + c];
+            if (MODE == DECAY_GATE && fact) {
+                for (int d = 0; d < dk; d++) inter += Ks[j * BDP + d] * ELd[d] * Ds[d * BS + c];
+            } else if (MODE == DECAY_GATE) {
+                const float* bl = Bs + (n - 1) * BDP;
+                for (int d = 0; d < dk; d++) inter += Ks[j * BDP + d] * expf(bl[d] - Bs[j * BDP + d]) * Ds[d * BS + c];
             } else {
-                for (int d = 0; d < dk; d++) inter += Ks[j * BD + d] * Ds[d * BS + c];
+                for (int d = 0; d < dk; d++) inter += Ks[j * BDP + d] * Ds[d * BS + c];
                 if (MODE == DECAY_HEAD) inter *= decay_pow(lam, n - 1 - j);
             }
             io<T>::st(dv_out + (tb + j) * dv + c0 + c, acc + inter);
@@ -357,14 +426,17 @@ __global__ __launch_bounds__(256) void bwd_dv_kernel(
         for (int e = tid; e < dk * nc; e += 256) {
             const int d = e / nc, c = e % nc;
             float s = Ds[d * BS + c];
-            if (MODE == DECAY_GATE) {
-                s *= expf(Bs[(n - 1) * BD + d]);
-                for (int i = 0; i < n; i++) s += Qs[i * BD + d] * expf(Bs[i * BD + d]) * Os[i * BS + c];
+            if (MODE == DECAY_GATE && fact) {
+                s *= ELd[d];
+                for (int i = 0; i < n; i++) s += Qs[i * BDP + d] * Os[i * BS + c];
+            } else if (MODE == DECAY_GATE) {
+                s *= expf(Bs[(n - 1) * BDP + d]);
+                for (int i = 0; i < n; i++) s += Qs[i * BDP + d] * expf(Bs[i * BDP + d]) * Os[i * BS + c];
             } else if (MODE == DECAY_HEAD) {
                 s *= decay_pow(lam, n);
-                for (int i = 0; i < n; i++) s += Qs[i * BD + d] * decay_pow(lam, i + 1) * Os[i * BS + c];
+                for (int i = 0; i < n; i++) s += Qs[i * BDP + d] * decay_pow(lam, i + 1) * Os[i * BS + c];
             } else {
-                for (int i = 0; i < n; i++) s += Qs[i * BD + d] * Os[i * BS + c];
+                for (int i = 0; i < n; i++) s += Qs[i * BDP + d] * Os[i * BS + c];
             }
             Ds[d * BS + c] = s;
         }

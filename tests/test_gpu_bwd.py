@@ -157,3 +157,15 @@ def test_bwd_bf16_matrix_core_head_decay_derivative(d, L, nseg, B):
     ref = _oracle(w, inp, gr, nseg)
     print(f"  d_decay rel err {rel_err(got[3], ref[3]):.2e}")
     _compare(got, ref, "bf16", "head")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_gate_strong_decay(dtype):
+    """Gate mode on the fp32 path factorises e^{B_i - B_j} into q e^{B} and k e^{-B} per chunk unless a
+    chunk's decay sum for one of the workgroup's key dims is below -80: here key dims 0..3 of every
+    head decay by about -2.5 per token (g = -40), so their slice keeps the per-pair exponentials, and
+    the other slices factorise."""
+    note(f"la_chunk_bwd gate with strong decay on some key dims, {dtype}")
+    w, inp, gr = _case("gate", dtype, 64, 32, 200, 64, 1, seed=91)
+    inp["decay"][..., :4] = -40.0
+    _compare(_gpu(w, inp, gr, 1), _oracle(w, inp, gr, 1), dtype, "gate")
