@@ -17,6 +17,7 @@ namespace {
 
 constexpr int GMAXC = 64;    // largest chunk
 constexpr int GMAXDK = 128;  // largest key dim
+constexpr int GKP = GMAXDK + 1;  // row pitch of the q, k, log-decay tiles: odd, so the score loop's rows fall in different banks
 constexpr int GDVT = 32;     // dv slice per workgroup
 
 template <typename T, int MODE>
@@ -25,9 +26,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_generic_kernel(
     const float* __restrict__ decay, const float* __restrict__ s_in, T* __restrict__ o,
     float* __restrict__ s_out, int64_t s_out_stride, int64_t H, int64_t L, int dk, int dv, int nseg, int C,
     float inv_norm) {
-    __shared__ float Qs[GMAXC * GMAXDK];
-    __shared__ float Ks[GMAXC * GMAXDK];
-    __shared__ float Bs[MODE == DECAY_GATE ? GMAXC * GMAXDK : 1];
+    __shared__ float Qs[GMAXC * GKP];
+    __shared__ float Ks[GMAXC * GKP];
+    __shared__ float Bs[MODE == DECAY_GATE ? GMAXC * GKP : 1];
     __shared__ float Vs[GMAXC * GDVT];
     __shared__ float Ps[GMAXC * GMAXC];
     __shared__ float Ss[GMAXDK * GDVT];
@@ -55,9 +56,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_generic_kernel(
         for (int e = tid; e < n * dk; e += 256) {
             int i = e / dk, d = e % dk;
             int64_t gi = (tb + i) * dk + d;
-            Qs[i * GMAXDK + d] = io<T>::ld(q + gi);
-            Ks[i * GMAXDK + d] = io<T>::ld(k + gi);
-            if (MODE == DECAY_GATE) Bs[i * GMAXDK + d] = gate_logdecay(decay[gi], inv_norm);
+            Qs[i * GKP + d] = io<T>::ld(q + gi);
+            Ks[i * GKP + d] = io<T>::ld(k + gi);
+            if (MODE == DECAY_GATE) Bs[i * GKP + d] = gate_logdecay(decay[gi], inv_norm);
         }
         for (int e = tid; e < n * nc; e += 256) {
             int i = e / nc, c = e % nc;
@@ -68,8 +69,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_generic_kernel(
             for (int d = tid; d < dk; d += 256) {
                 float run = 0.f;
                 for (int i = 0; i < n; i++) {
-                    run += Bs[i * GMAXDK + d];
-                    Bs[i * GMAXDK + d] = run;
+                    run += Bs[i * GKP + d];
+                    Bs[i * GKP + d] = run;
                 }
             }
             __syncthreads();
@@ -81,10 +82,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_generic_kernel(
             if (j <= i) {
                 if (MODE == DECAY_GATE) {
                     for (int d = 0; d < dk; d++)
-                        p += Qs[i * GMAXDK + d] * Ks[j * GMAXDK + d] *
-                             expf(Bs[i * GMAXDK + d] - Bs[j * GMAXDK + d]);
+                        p += Qs[i * GKP + d] * Ks[j * GKP + d] *
+                             expf(Bs[i * GKP + d] - Bs[j * GKP + d]);
                 } else {
-                    for (int d = 0; d < dk; d++) p += Qs[i * GMAXDK + d] * Ks[j * GMAXDK + d];
+                    for (int d = 0; d < dk; d++) p += Qs[i * GKP + d] * Ks[j * GKP + d];
                     if (MODE == DECAY_HEAD) p *= decay_pow(lam, i - j);
                 }
             }
@@ -99,9 +100,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_generic_kernel(
             float inter = 0.f;
             if (MODE == DECAY_GATE) {
                 for (int d = 0; d < dk; d++)
-                    inter += Qs[i * GMAXDK + d] * expf(Bs[i * GMAXDK + d]) * Ss[d * GDVT + c];
+                    inter += Qs[i * GKP + d] * expf(Bs[i * GKP + d]) * Ss[d * GDVT + c];
             } else {
-                for (int d = 0; d < dk; d++) inter += Qs[i * GMAXDK + d] * Ss[d * GDVT + c];
+                for (int d = 0; d < dk; d++) inter += Qs[i * GKP + d] * Ss[d * GDVT + c];
                 if (MODE == DECAY_HEAD) inter *= decay_pow(lam, i + 1);
             }
             io<T>::st(o + (tb + i) * dv + c0 + c, acc + inter);
@@ -112,15 +113,15 @@ __global__ __launch_bounds__(256) void chunk_fwd_generic_kernel(
             int d = e / nc, c = e % nc;
             float s = Ss[d * GDVT + c];
             if (MODE == DECAY_GATE) {
-                const float bl = Bs[(n - 1) * GMAXDK + d];
+                const float bl = Bs[(n - 1) * GKP + d];
                 s *= expf(bl);
                 for (int j = 0; j < n; j++)
-                    s += Ks[j * GMAXDK + d] * expf(bl - Bs[j * GMAXDK + d]) * Vs[j * GDVT + c];
+                    s += Ks[j * GKP + d] * expf(bl - Bs[j * GKP + d]) * Vs[j * GDVT + c];
             } else if (MODE == DECAY_HEAD) {
                 s *= decay_pow(lam, n);
-                for (int j = 0; j < n; j++) s += Ks[j * GMAXDK + d] * decay_pow(lam, n - 1 - j) * Vs[j * GDVT + c];
+                for (int j = 0; j < n; j++) s += Ks[j * GKP + d] * decay_pow(lam, n - 1 - j) * Vs[j * GDVT + c];
             } else {
-                for (int j = 0; j < n; j++) s += Ks[j * GMAXDK + d] * Vs[j * GDVT + c];
+                for (int j = 0; j < n; j++) s += Ks[j * GKP + d] * Vs[j * GDVT + c];
             }
             Ss[d * GDVT + c] = s;
         }
