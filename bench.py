@@ -116,15 +116,16 @@ class BackwardStep:
 
 
 def backward_legs(stream):
-    """la_chunk_bwd at the plain (B=1) and head-decay (B=2) shapes, decays fixed, and at the
-    head-decay shape with d lambda_h (learned decays): median time, tokens/s, GB/s on the compulsory
-    bytes (q, k, v, d_o read once, dq, dk, dv written once) and per-kernel means."""
+    """la_chunk_bwd at the plain (B=1), head-decay (B=2) and gate (B=4) shapes, decays fixed, and at
+    the head-decay shape with d lambda_h (learned decays): median time, tokens/s, GB/s on the
+    compulsory bytes (q, k, v, d_o and the gate read once, dq, dk, dv written once) and per-kernel
+    means."""
     import torch
 
     from chunked_scan_amd.inputs import WORKLOADS
 
     backward = {}
-    for wid, want_decay in ((1, False), (2, False), (2, True)):
+    for wid, want_decay in ((1, False), (2, False), (2, True), (3, False)):
         wb = WORKLOADS[wid]
         key = wb.name + (" + d_lambda" if want_decay else "")
         log(f"[bench] backward: workload {wid} {key}")
@@ -137,16 +138,18 @@ def backward_legs(stream):
         th = wb.B * wb.H * wb.L
         # algorithmic bytes per token-head of each pass (bf16, d = 128): state passes read two tensors,
         # the dq and d lambda output passes read three or four, the dk/dv output pass reads four and
-        # writes two
-        per_th = {"chunk_bwd_dq_state_pass": 512, "chunk_bwd_dq": 1024, "chunk_bwd_dkdv_state_pass": 512,
-                  "chunk_bwd_dkdv": 1536, "chunk_bwd_dlam_state_pass": 512, "chunk_bwd_dlam": 1024}
+        # writes two; in gate mode the dq and dk/dv passes also read the fp32 gate row (4 d bytes)
+        gate = 4 * wb.dk if wb.mode == "gate" else 0
+        per_th = {"chunk_bwd_dq_state_pass": 512 + gate, "chunk_bwd_dq": 1024 + gate,
+                  "chunk_bwd_dkdv_state_pass": 512 + gate, "chunk_bwd_dkdv": 1536 + gate,
+                  "chunk_bwd_dlam_state_pass": 512, "chunk_bwd_dlam": 1024}
         for name, d in ks.items():
             if name in per_th and d["launches_per_step"] == 1:
                 by = per_th[name] * th
                 g = by / (d["mean_us"] * 1e-6) / 1e9
                 d.update(algorithmic_bytes=by, gbps=round(g, 1), hbm_frac=round(g / HBM_PEAK_GBS, 4))
-        # compulsory bytes (bf16): q, k, v, d_o read once, dq, dk, dv written once
-        comp = th * 2 * (wb.dk + wb.dk + wb.dv + wb.dv) + th * 2 * (wb.dk + wb.dk + wb.dv)
+        # compulsory bytes (bf16): q, k, v, d_o (and the fp32 gate) read once, dq, dk, dv written once
+        comp = th * 2 * (wb.dk + wb.dk + wb.dv + wb.dv) + th * 2 * (wb.dk + wb.dk + wb.dv) + th * gate
         gbs = comp / (st["median_us"] * 1e-6) / 1e9
         backward[key] = dict(
             what="la_chunk_bwd: dq, dk, dv, ds_in" + (", d lambda_h" if want_decay else " (decay held fixed)"),

@@ -210,7 +210,7 @@ def la_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.T
                  ds_out: Optional[torch.Tensor] = None, *, mode: Optional[str] = None, nseg: int = 1,
                  chunk: int = 64, gate_norm: float = 16.0, want_decay: bool = True, want_ds_in: bool = True,
                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                 dv: Optional[torch.Tensor] = None, stream=None, timer=None):
+                 dv: Optional[torch.Tensor] = None, subseg_chunks: int = 0, stream=None, timer=None):
     """Backward of la_chunk_fwd.  d_o [B,H,L,dv] (q's dtype) and ds_out [B,H,nseg,dk,dv] f32 or None are
     the loss's derivatives with respect to o and to each segment's final state.  Returns
     (dq, dk, dv, d_decay, ds_in): dq, dk [B,H,L,dk] and dv [B,H,L,dv] in q's dtype; d_decay f32 [H]
@@ -240,7 +240,7 @@ def la_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.T
         d_decay = torch.empty(decay.shape, dtype=torch.float32, device=q.device)
     ds_in = torch.empty((B, H, nseg, dkk, dvv), dtype=torch.float32, device=q.device) if want_ds_in else None
     shp = make_shape(B, H, L, dkk, dvv, nseg=nseg, dtype=_dtype_code(q), mode=m, gate_norm=gate_norm,
-                     stream=_stream(stream), timer=timer)
+                     subseg_chunks=subseg_chunks, stream=_stream(stream), timer=timer)
     _check("la_chunk_bwd", lib().la_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(d_o),
                                               _ptr(ds_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_decay),
                                               _ptr(ds_in), ctypes.byref(shp), chunk))

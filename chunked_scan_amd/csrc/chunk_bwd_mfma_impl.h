@@ -81,19 +81,79 @@ __device__ __forceinline__ bf16x8 tr_operand(const __bf16* tile, int pitch, int 
     return cat(lds_tr16(&tile[tb * pitch + col]), lds_tr16(&tile[(tb + 4) * pitch + col]));
 }
 
+// Gate mode: a chunk's raw gate rows [C][D] (fp32) in registers, PG 16-byte pieces per lane, rows
+// past the chunk's end as zero.  The loads are issued together and converted only later (inside
+// the conversion each piece's use would follow its own load and wait).
+template <int D>
+struct GateTile {
+    static constexpr int PG = C * D / 4 / NT;
+};
+
+template <int D>
+__device__ __forceinline__ void gate_load(const float* __restrict__ g, int64_t row0, int n, f32x4* rg, int tid) {
+#pragma unroll
+    for (int r = 0; r < GateTile<D>::PG; r++) {
+        const int p = tid + NT * r;
+        const int row = p / (D / 4), c4 = (p % (D / 4)) * 4;
+        rg[r] = row < n ? *(const f32x4*)(g + (row0 + row) * D + c4) : f32x4{0, 0, 0, 0};
+    }
+}
+
+// The chunk's per-token log2-decay, log2 a = -softplus(-g) / gate_norm * log2(e), from the gate
+// tile rg, into gb[C][D] (rows past the chunk's end as 0), then replaced by its inclusive in-chunk
+// running sum B (per key dim), in NT / D parts of C * D / NT rows; gel[d] = 2^{B_last[d]} is the
+// chunk's total decay.  Every factor built from B later on is 2^{B} <= 1, 2^{-B} (bounded by the
+// chunk's decay sum, which must stay above -80 in natural log units as for the forward) or
+// 2^{B_last - B} <= 1.
+template <int D>
+__device__ __forceinline__ void gate_chunk_logdecay(const f32x4* rg, int n, float inv_norm, float* gb, float* gtot,
+                                                    float* gel, int tid) {
+#pragma unroll
+    for (int r = 0; r < GateTile<D>::PG; r++) {
+        const int p = tid + NT * r;
+        const int row = p / (D / 4), c4 = (p % (D / 4)) * 4;
+        const f32x4 x = rg[r];
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; e++) y[e] = row < n ? gate_logdecay(x[e], inv_norm) * LOG2E : 0.f;
+        *(f32x4*)(&gb[row * D + c4]) = y;
+    }
+    __syncthreads();
+    constexpr int NPART = NT / D, R = C / NPART;
+    const int d = tid % D, part = tid / D;
+    float vals[R];
+#pragma unroll
+    for (int i = 0; i < R; i++) vals[i] = gb[(part * R + i) * D + d];
+#pragma unroll
+    for (int i = 1; i < R; i++) vals[i] += vals[i - 1];
+    gtot[part * D + d] = vals[R - 1];
+    __syncthreads();
+    float off = 0.f;
+    for (int pp = 0; pp < part; pp++) off += gtot[pp * D + d];
+#pragma unroll
+    for (int i = 0; i < R; i++) gb[(part * R + i) * D + d] = vals[i] + off;
+    __syncthreads();
+    if (tid < D) gel[tid] = __builtin_amdgcn_exp2f(gb[(C - 1) * D + tid]);
+}
+
 // LDS of the backward-direction kernel; the state pass keeps only the tiles of the D update.
 template <int D, int MODE, bool SO>
 struct BwdSmem {
     static constexpr int TILE = Geo<D>::TILE, PITCH = Geo<D>::PITCH;
+    static constexpr bool GATE = MODE == DECAY_GATE;
     // unused tiles shrink to 8 elements, which keeps every tile 16-byte aligned
-    __bf16 q[SO ? 8 : TILE];
-    __bf16 qs[(MODE == DECAY_HEAD || SO) ? TILE : 8];  // q_i a^{i+1} (head mode), q (state pass): the D update
+    __bf16 q[(SO || GATE) ? 8 : TILE];
+    // q_i a^{i+1} (head mode), q 2^{B} (gate), q (state pass): the D update (and gate's P)
+    __bf16 qs[(MODE != DECAY_NONE || SO) ? TILE : 8];
     __bf16 k[SO ? 8 : TILE];
     __bf16 v[SO ? 8 : TILE];
     __bf16 o[TILE];                  // d_o
     __bf16 dm[SO ? 8 : D * PITCH];   // D as bf16, [key row][value column]
     __bf16 pt[SO ? 8 : C * PPITCH];  // (P' w)^T: [j][i]
     __bf16 pv[SO ? 8 : C * PPITCH];  // (P w)^T:  [j][i]
+    float gb[GATE ? C * D : 4];      // gate: in-chunk cumulative log2-decay B, then 2^{-B}
+    float gtot[GATE ? NT : 4];
+    float gel[GATE ? D : 4];         // gate: 2^{B_last}
     float apow[C + 1];               // a^m, m = 0..C (head mode)
     double red[NT / 64];
 };
@@ -108,7 +168,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
     const float* __restrict__ init_state,                            // output pass: scanned D^(g)
     double* __restrict__ intra_part,  // head mode, output pass: the intra-chunk part of d lambda_h, or null
-    int64_t H, int64_t L, int nseg, int G, int cps) {
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm) {
     __shared__ __attribute__((aligned(16))) BwdSmem<D, MODE, STATE_ONLY> sm;
     using Gm = Geo<D>;
     constexpr int PITCH = Gm::PITCH, PR = Gm::PR, PIECES_ROW = Gm::PIECES_ROW, NCB = Gm::NCB;
@@ -153,13 +213,19 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
 
     if (MODE == DECAY_HEAD && tid <= C) sm.apow[tid] = decay_pow(lam, tid);  // read after the loop's first barrier
     double hacc = 0.0;
+    float gate_total = 0.f;  // gate: log2 of the sub-segment's decay so far, key dim tid (tid < D)
     const int nchunks = (int)((t_end - t_begin + C - 1) / C);
-    // one chunk's tiles in registers (rows past the end read as zero)
+    // one chunk's tiles in registers (rows past the end read as zero); gate mode: the gate tile too,
+    // prefetched with the others except in the d = 128 output pass, which has no registers left for
+    // it (it would spill) and loads it at the chunk's start
+    constexpr bool GPF = MODE == DECAY_GATE && !(D == 128 && !STATE_ONLY);
     u32x4 rq[PR], ro[PR], rk[STATE_ONLY ? 1 : PR], rv[STATE_ONLY ? 1 : PR];
+    f32x4 rg[MODE == DECAY_GATE ? GateTile<D>::PG : 1];
     auto load_chunk = [&](int cc) {
         const int64_t t0c = t_begin + (int64_t)cc * C;
         const int nc = (int)min((int64_t)C, t_end - t0c);
         const u32x4 z = {0, 0, 0, 0};
+        if (GPF) gate_load<D>(decay, row_base + t0c, nc, rg, tid);
 #pragma unroll
         for (int r = 0; r < PR; r++) {
             const int p = tid + NT * r;
@@ -180,18 +246,39 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
         const int n = (int)min((int64_t)C, t_end - t0);
         __syncthreads();  // the previous chunk is done with every LDS tile
         if (!PF) load_chunk(c);
+        if (MODE == DECAY_GATE) {
+            if (!GPF) gate_load<D>(decay, row_base + t0, n, rg, tid);
+            gate_chunk_logdecay<D>(rg, n, inv_norm, sm.gb, sm.gtot, sm.gel, tid);
+            if (tid < D) gate_total += sm.gb[(C - 1) * D + tid];
+            __syncthreads();  // gel
+        }
 
         // ---- stage the chunk and D as bf16
 #pragma unroll
         for (int r = 0; r < PR; r++) {
             const int p = tid + NT * r;
             const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            if (MODE == DECAY_HEAD) *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(rq[r], sm.apow[row + 1]);
-            else if (STATE_ONLY) *(u32x4*)(&sm.qs[row * PITCH + c8]) = rq[r];
+            if (MODE == DECAY_GATE) {  // q 2^{B}; k 2^{-B}
+                float fq[8], fk[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float b = sm.gb[row * D + c8 + e];
+                    fq[e] = __builtin_amdgcn_exp2f(b);
+                    fk[e] = __builtin_amdgcn_exp2f(-b);
+                }
+                *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8(rq[r], fq);
+                if (!STATE_ONLY) *(u32x4*)(&sm.k[row * PITCH + c8]) = scale8(rk[r], fk);
+            } else if (MODE == DECAY_HEAD) {
+                *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(rq[r], sm.apow[row + 1]);
+            } else if (STATE_ONLY) {
+                *(u32x4*)(&sm.qs[row * PITCH + c8]) = rq[r];
+            }
             *(u32x4*)(&sm.o[row * PITCH + c8]) = ro[r];
             if (!STATE_ONLY) {
-                *(u32x4*)(&sm.q[row * PITCH + c8]) = rq[r];
-                *(u32x4*)(&sm.k[row * PITCH + c8]) = rk[r];
+                if (MODE != DECAY_GATE) {
+                    *(u32x4*)(&sm.q[row * PITCH + c8]) = rq[r];
+                    *(u32x4*)(&sm.k[row * PITCH + c8]) = rk[r];
+                }
                 *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
             }
         }
@@ -206,8 +293,12 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
         }
         __syncthreads();
         if (PF && c > 0) load_chunk(c - 1);  // the previous chunk, while this one is computed
+        if (MODE == DECAY_GATE && !STATE_ONLY) {  // B -> 2^{-B} (dk's per-key-dim factor); read after the next barrier
+#pragma unroll
+            for (int r = 0; r < C * D / NT; r++) sm.gb[tid + NT * r] = __builtin_amdgcn_exp2f(-sm.gb[tid + NT * r]);
+        }
         // the q side of the D update: q a^{i+1} (head mode), else q itself
-        const __bf16* qsd = (MODE == DECAY_HEAD || STATE_ONLY) ? sm.qs : sm.q;
+        const __bf16* qsd = (MODE != DECAY_NONE || STATE_ONLY) ? sm.qs : sm.q;
 
         // d_o operands of this wave's value columns for the four 16-token slabs
         bf16x8 ob[4];
@@ -227,7 +318,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                     const int ka = ks * 16 + kg * 8;
                     po = mfma(*(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ka]),
                               *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ka]), po);
-                    pq = mfma(*(const bf16x8*)(&sm.q[(ib * 32 + n32) * PITCH + ka]),
+                    pq = mfma(*(const bf16x8*)(&(MODE == DECAY_GATE ? sm.qs : sm.q)[(ib * 32 + n32) * PITCH + ka]),
                               *(const bf16x8*)(&sm.k[(jb * 32 + n32) * PITCH + ka]), pq);
                 }
 #pragma unroll
@@ -248,7 +339,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
             // ---- dk, column block w (key dims 32 w ..), and dv, column block w (value columns 32 w ..)
             bf16x8 qb[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) qb[ks] = tr_operand(sm.q, PITCH, ks, 32 * cb, lane);
+            for (int ks = 0; ks < 4; ks++) qb[ks] = tr_operand(MODE == DECAY_GATE ? sm.qs : sm.q, PITCH, ks, 32 * cb, lane);
             // D's own columns as B operands (key-row order permuted as the A reads below)
             bf16x8 db[2 * NCB];
 #pragma unroll
@@ -257,7 +348,12 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 for (int hh = 0; hh < 2; hh++) {
                     bf16x8 x;
 #pragma unroll
-                    for (int j = 0; j < 8; j++) x[j] = (__bf16)Dm[m][8 * hh + j];
+                    for (int j = 0; j < 8; j++) {
+                        float dv_ = Dm[m][8 * hh + j];
+                        if (MODE == DECAY_GATE)  // gate: D's rows times 2^{B_last}, so that K-hat D = K-tilde D
+                            dv_ *= sm.gel[32 * m + ((8 * hh + j) >> 2) * 8 + kg * 4 + (j & 3)];
+                        x[j] = (__bf16)dv_;
+                    }
                     db[2 * m + hh] = x;
                 }
 #pragma unroll
@@ -278,10 +374,21 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                         acc[i] *= sm.apow[max(n - 1 - j, 0)];
                     }
                 }
+                if (MODE == DECAY_GATE) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) acc[i] *= sm.gel[32 * cb + n32];
+                }
 #pragma unroll
                 for (int ks = 2 * jb; ks < 4; ks++) {
                     const bf16x8 a = *(const bf16x8*)(&sm.pt[(jb * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
                     acc = mfma(a, qb[ks], acc);
+                }
+                if (MODE == DECAY_GATE) {  // dk_j = 2^{-B_j} (2^{B_last} V D^T + P'^T Q-bar)_j, per key dim
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const int j = jb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
+                        acc[i] *= sm.gb[j * D + 32 * cb + n32];
+                    }
                 }
                 __bf16* drow = dk_out + (row_base + t0 + jb * 32) * D + 32 * cb + n32;
 #pragma unroll
@@ -330,6 +437,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
 #pragma unroll
                     for (int i = 0; i < 16; i++) Dm[m][i] *= fh;
                 }
+                if (MODE == DECAY_GATE) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) Dm[m][i] *= sm.gel[32 * m + (i >> 2) * 8 + kg * 4 + (i & 3)];
+                }
 #pragma unroll
                 for (int ks = 0; ks < 4; ks++) Dm[m] = mfma(tr_operand(qsd, PITCH, ks, 32 * m, lane), ob[ks], Dm[m]);
             }
@@ -350,7 +461,9 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
             }
     }
     if (STATE_ONLY && tid < D) {  // the total decay over this sub-segment, per key dim
-        const float tot = (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
+        float tot = 1.f;
+        if (MODE == DECAY_HEAD) tot = decay_pow(lam, (int)(t_end - t_begin));
+        if (MODE == DECAY_GATE) tot = __builtin_amdgcn_exp2f(gate_total);
         part_decay[(ub * (G - 1) + (G - 1 - g)) * D + tid] = tot;
     }
     if (MODE == DECAY_HEAD && !STATE_ONLY && intra_part) {
@@ -365,16 +478,20 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
 
 
 // LDS of the forward-direction kernel; the state pass keeps only the tiles of the state update.
-template <int D, bool SO>
+template <int D, int MODE, bool SO>
 struct DqSmem {
     static constexpr int TILE = Geo<D>::TILE, PITCH = Geo<D>::PITCH;
+    static constexpr bool GATE = MODE == DECAY_GATE;
     // unused tiles shrink to 8 elements, which keeps every tile 16-byte aligned
     __bf16 o[SO ? 8 : TILE];  // d_o
     __bf16 v[TILE];
-    __bf16 k[SO ? 8 : TILE];  // k (the P' K product)
-    __bf16 kt[TILE];          // k_j a^{n-1-j} (the state update)
+    __bf16 k[SO ? 8 : TILE];  // k (the P' K product); gate: k 2^{-B}
+    __bf16 kt[TILE];          // k_j a^{n-1-j} (the state update); gate: k 2^{B_last - B}
     __bf16 sm[SO ? 8 : D * PITCH];  // S as bf16, [key row][value column]
     __bf16 p[SO ? 8 : C * PPITCH];  // P' w, [i][j]
+    float gb[GATE ? C * D : 4];     // gate: in-chunk cumulative log2-decay
+    float gtot[GATE ? NT : 4];
+    float gel[GATE ? D : 4];        // gate: 2^{B_last}
     float apow[C + 1];              // a^m, m = 0..C (head mode)
 };
 
@@ -385,8 +502,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     const float* __restrict__ ds_out, int64_t sstride, __bf16* __restrict__ dq,
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
     const float* __restrict__ init_state,                            // output pass: scanned states
-    int64_t H, int64_t L, int nseg, int G, int cps) {
-    __shared__ __attribute__((aligned(16))) DqSmem<D, STATE_ONLY> sm;
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm) {
+    __shared__ __attribute__((aligned(16))) DqSmem<D, MODE, STATE_ONLY> sm;
     using Gm = Geo<D>;
     constexpr int PITCH = Gm::PITCH, PR = Gm::PR, PIECES_ROW = Gm::PIECES_ROW, NCB = Gm::NCB;
     constexpr bool PF = true;
@@ -409,6 +526,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     const int64_t t_end = min(t_begin + (int64_t)cps * C, tseg + Lseg);
     const int64_t row_base = bh * L;
     const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
+    float gate_total = 0.f;  // gate: log2 of the sub-segment's decay so far, key dim tid (tid < D)
 
     // ---- the state entering the sub-segment: key rows 32 m + (i / 4) 8 + kg 4 + i % 4, column 32 w + n32
     f32x16 Sm[NCB];
@@ -430,12 +548,15 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
 
     if (MODE == DECAY_HEAD && tid <= C) sm.apow[tid] = decay_pow(lam, tid);  // read after the loop's first barrier
     const int nchunks = (int)((t_end - t_begin + C - 1) / C);
-    // one chunk's tiles in registers (rows past the end read as zero)
+    // one chunk's tiles in registers (rows past the end read as zero); gate mode: the gate tile too,
+    // prefetched with the others
     u32x4 rk[PR], rv[PR], ro[STATE_ONLY ? 1 : PR];
+    f32x4 rg[MODE == DECAY_GATE ? GateTile<D>::PG : 1];
     auto load_chunk = [&](int cc) {
         const int64_t t0c = t_begin + (int64_t)cc * C;
         const int nc = (int)min((int64_t)C, t_end - t0c);
         const u32x4 z = {0, 0, 0, 0};
+        if (MODE == DECAY_GATE) gate_load<D>(decay, row_base + t0c, nc, rg, tid);
 #pragma unroll
         for (int r = 0; r < PR; r++) {
             const int p = tid + NT * r;
@@ -453,15 +574,33 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
         const int n = (int)min((int64_t)C, t_end - t0);
         __syncthreads();  // the previous chunk is done with every LDS tile
         if (!PF) load_chunk(c);
+        if (MODE == DECAY_GATE) {
+            gate_chunk_logdecay<D>(rg, n, inv_norm, sm.gb, sm.gtot, sm.gel, tid);
+            if (tid < D) gate_total += sm.gb[(C - 1) * D + tid];
+            __syncthreads();  // gel
+        }
 #pragma unroll
         for (int r = 0; r < PR; r++) {
             const int p = tid + NT * r;
             const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
             *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
-            if (MODE == DECAY_HEAD) *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(rk[r], sm.apow[max(n - 1 - row, 0)]);
-            else *(u32x4*)(&sm.kt[row * PITCH + c8]) = rk[r];
+            if (MODE == DECAY_GATE) {
+                float ft[8], fh[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float b = sm.gb[row * D + c8 + e];
+                    ft[e] = __builtin_amdgcn_exp2f(sm.gb[(C - 1) * D + c8 + e] - b);
+                    fh[e] = __builtin_amdgcn_exp2f(-b);
+                }
+                *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8(rk[r], ft);
+                if (!STATE_ONLY) *(u32x4*)(&sm.k[row * PITCH + c8]) = scale8(rk[r], fh);
+            } else if (MODE == DECAY_HEAD) {
+                *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(rk[r], sm.apow[max(n - 1 - row, 0)]);
+            } else {
+                *(u32x4*)(&sm.kt[row * PITCH + c8]) = rk[r];
+            }
             if (!STATE_ONLY) {
-                *(u32x4*)(&sm.k[row * PITCH + c8]) = rk[r];
+                if (MODE != DECAY_GATE) *(u32x4*)(&sm.k[row * PITCH + c8]) = rk[r];
                 *(u32x4*)(&sm.o[row * PITCH + c8]) = ro[r];
             }
         }
@@ -530,6 +669,13 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
                     const bf16x8 a = *(const bf16x8*)(&sm.p[(ib * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
                     acc = mfma(a, kb[ks], acc);
                 }
+                if (MODE == DECAY_GATE) {  // dq_i = 2^{B_i} (d_o S^T + P' Khat)_i, per key dim
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
+                        acc[i] *= __builtin_amdgcn_exp2f(sm.gb[row * D + 32 * cb + n32]);
+                    }
+                }
                 const int64_t rbase = row_base + t0 + ib * 32;
 #pragma unroll
                 for (int i = 0; i < 16; i++) {
@@ -539,7 +685,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
             }
         }
 
-        // ---- S <- a^n S + (K a^{n-1-j})^T V
+        // ---- S <- a^n S + (K a^{n-1-j})^T V  (gate: rows scaled by 2^{B_last})
         {
             const float fh = (MODE == DECAY_HEAD) ? sm.apow[n] : 1.f;
 #pragma unroll
@@ -547,6 +693,10 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
                 if (MODE == DECAY_HEAD) {
 #pragma unroll
                     for (int i = 0; i < 16; i++) Sm[m][i] *= fh;
+                }
+                if (MODE == DECAY_GATE) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) Sm[m][i] *= sm.gel[32 * m + (i >> 2) * 8 + kg * 4 + (i & 3)];
                 }
 #pragma unroll
                 for (int ks = 0; ks < 4; ks++) Sm[m] = mfma(tr_operand(sm.kt, PITCH, ks, 32 * m, lane), vb[ks], Sm[m]);
@@ -565,7 +715,9 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
             }
     }
     if (STATE_ONLY && tid < D) {
-        const float tot = (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
+        float tot = 1.f;
+        if (MODE == DECAY_HEAD) tot = decay_pow(lam, (int)(t_end - t_begin));
+        if (MODE == DECAY_GATE) tot = __builtin_amdgcn_exp2f(gate_total);
         part_decay[(ub * (G - 1) + g) * D + tid] = tot;
     }
 }
@@ -850,7 +1002,7 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
         LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
                   bwd_dq_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
                       k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr,
-                      a.H, a.L, a.nseg, G, cps));
+                      a.H, a.L, a.nseg, G, cps, a.inv_norm));
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_state_scan(f_state, f_decay, f_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
             return e;
@@ -858,14 +1010,14 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
     LA_TRACED(a.tr, "chunk_bwd_dq",
               bwd_dq_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
                   k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, f_state,
-                  a.H, a.L, a.nseg, G, cps));
+                  a.H, a.L, a.nseg, G, cps, a.inv_norm));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // dk, dv: backward state pass, reverse-order scan, output pass
     if (G > 1) {
         LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass",
                   bwd_dkdv_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
                       q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state, b_decay,
-                      nullptr, nullptr, a.H, a.L, a.nseg, G, cps));
+                      nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm));
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_state_scan(b_state, b_decay, b_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
             return e;
@@ -873,7 +1025,7 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
     LA_TRACED(a.tr, "chunk_bwd_dkdv",
               bwd_dkdv_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
                   q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out, a.ds_in,
-                  nullptr, nullptr, b_state, intra_part, a.H, a.L, a.nseg, G, cps));
+                  nullptr, nullptr, b_state, intra_part, a.H, a.L, a.nseg, G, cps, a.inv_norm));
     return hipGetLastError();
 }
 
@@ -883,7 +1035,7 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
 template <int D>
 hipError_t launch_d(const BwdArgs& a) {
     FwdArgs sp;
-    sp.B = a.B; sp.H = a.H; sp.L = a.L; sp.nseg = a.nseg; sp.subseg_chunks = 0;
+    sp.B = a.B; sp.H = a.H; sp.L = a.L; sp.nseg = a.nseg; sp.subseg_chunks = a.subseg_chunks;
     int G, cps;
     mfma_split(sp, &G, &cps);
     const int64_t units = a.B * a.H * a.nseg;
@@ -911,8 +1063,9 @@ hipError_t launch_d(const BwdArgs& a) {
     float* f_decay = n_decay ? fp + nsets * n_state : nullptr;
     float* b_decay = n_decay ? fp + nsets * n_state + n_decay : nullptr;
     float* l_decay = n_decay ? fp + nsets * n_state + 2 * n_decay : nullptr;
-    e = a.mode == DECAY_HEAD ? launch_mode<D, DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra)
-                             : launch_mode<D, DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr);
+    if (a.mode == DECAY_HEAD) e = launch_mode<D, DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra);
+    else if (a.mode == DECAY_GATE) e = launch_mode<D, DECAY_GATE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr);
+    else e = launch_mode<D, DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr);
     if (e == hipSuccess && dlam) e = launch_dlam<D>(a, G, cps, l_state, lt_state, l_decay, part, intra);
     if (ws) {
         hipError_t f = hipFreeAsync(ws, a.stream);

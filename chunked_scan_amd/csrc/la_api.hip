@@ -338,7 +338,7 @@ la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float*
                        float* ds_in, const la_shape* s, int32_t chunk) {
     la_status st = check_common(s);
     if (st != LA_OK) return st;
-    if (chunk <= 0 || s->state_stride < 0) return LA_ERR_SHAPE;
+    if (chunk <= 0 || s->state_stride < 0 || s->subseg_chunks < 0) return LA_ERR_SHAPE;
     const int64_t per_seg = (int64_t)s->dk * s->dv;
     if (s->state_stride && s->state_stride < (int64_t)s->nseg * per_seg) return LA_ERR_SHAPE;
     if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
@@ -385,6 +385,7 @@ la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float*
     a.bf16 = s->in_dtype == LA_BF16;
     a.mode = s->decay_mode;
     a.inv_norm = s->decay_mode == LA_DECAY_GATE ? 1.f / s->gate_norm : 1.f;
+    a.subseg_chunks = s->subseg_chunks;
     a.stream = (hipStream_t)s->stream;
     a.tr = &tr;
     return from_hip(la::chunk_bwd_mfma_supported(a) ? la::launch_chunk_bwd_mfma(a) : la::launch_chunk_bwd_generic(a));

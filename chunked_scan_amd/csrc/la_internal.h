@@ -96,6 +96,7 @@ struct BwdArgs {
     bool bf16;
     int mode;
     float inv_norm;
+    int subseg_chunks;     // matrix-core path: chunks per sub-segment, 0 = automatic
     hipStream_t stream;
     Tracer* tr;
 };

@@ -92,10 +92,11 @@ typedef struct la_shape {
                              local state land directly in a slot of a larger scan buffer. */
     int64_t total_stride; /* la_cumdecay and la_chunk_fwd_decayed: elements between consecutive
                              (b,h) blocks of total; 0 = dense, nseg*dk */
-    int32_t subseg_chunks;/* la_chunk_fwd only: chunks per internal sub-segment when one segment is
-                             split across compute units (the decomposition identity applied inside
-                             the GPU); 0 = choose automatically, >= 1 forces that length.  Changes
-                             the rounding order only, never the mathematical result. */
+    int32_t subseg_chunks;/* la_chunk_fwd and la_chunk_bwd (matrix-core kernels): chunks per internal
+                             sub-segment when one segment is split across compute units (the
+                             decomposition identity applied inside the GPU); 0 = choose
+                             automatically, >= 1 forces that length.  Changes the rounding order
+                             only, never the mathematical result. */
     void* stream;         /* hipStream_t the work is enqueued on; NULL = default stream */
     la_trace* trace;      /* optional per-kernel event recording (NULL = off); see la_trace */
 } la_shape;
@@ -187,12 +188,14 @@ la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, cons
  *            the others' is what a backward state scan carries between segments), in the
  *            state_stride layout, or NULL.
  *   chunk  : 16, 32 or 64.
- * No output may overlap an input or another output.  bf16 inputs with dk = dv in {32, 64, 128},
- * chunk 64 and no decay or head decay run on the matrix cores (bf16 operands, fp32 accumulation; the head-decay
- * derivative summed token pair by token pair, in fp64 partial sums); every other shape, fp32 inputs
- * and gate mode run in fp32 arithmetic.  bf16 outputs are rounded once, to nearest even.  May
+ * No output may overlap an input or another output.  bf16 inputs with dk = dv in {32, 64, 128}
+ * and chunk 64 run on the matrix cores (bf16 operands, fp32 accumulation) with no decay, with a head
+ * decay (its derivative summed token pair by token pair, in fp64 partial sums) and with a gate whose
+ * derivative is not requested (d_decay NULL); there, as in la_chunk_fwd, each chunk's per-key-dim
+ * log-decay sum must stay above -80.  Every other shape, fp32 inputs and the gate derivative run in
+ * fp32 arithmetic, with no such range limit.  bf16 outputs are rounded once, to nearest even.  May
  * allocate temporary device workspace from the same stream-ordered pool as la_chunk_fwd (per
- * sub-segment states; a float per token and key dim in gate mode).
+ * sub-segment states; a float per token and key dim for the gate derivative).
  * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_DECAY, LA_ERR_ALIAS,
  * LA_ERR_UNSUPPORTED or LA_ERR_LAUNCH.
  */

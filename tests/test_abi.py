@@ -178,6 +178,7 @@ def test_bwd_validation(lib):
     assert bwd(lib, shape(), chunk=48) == UNSUP
     assert bwd(lib, shape(dk=96)) == UNSUP
     assert bwd(lib, shape(state_stride=64 * 64 - 1)) == SHAPE       # smaller than one segment's state
+    assert bwd(lib, shape(subseg_chunks=-1)) == SHAPE
     mixed = shape()
     mixed.out_dtype = B.LA_F32
     assert bwd(lib, mixed) == DTYPE

@@ -132,13 +132,14 @@ def test_bwd_chunk_invariance():
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
-@pytest.mark.parametrize("mode", ["none", "head"])
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
 @pytest.mark.parametrize("L,nseg,H", [(192, 1, 2), (1000, 1, 2), (2048, 2, 2), (640, 1, 3)])
 def test_bwd_bf16_matrix_core_subsegments(mode, L, nseg, H, d):
-    """bf16, d = 32 / 64 / 128, chunk 64, no decay or a fixed head decay (no decay derivative
-    requested) runs on the matrix-core kernels, which split each segment into sub-segments (state
-    passes, scans of the state and of its derivative, output passes): lengths that give one or several
-    sub-segments and a ragged last chunk."""
+    """bf16, d = 32 / 64 / 128, chunk 64, with no decay, a fixed head decay or a fixed gate (no decay
+    derivative requested) runs on the matrix-core kernels, which split each segment into sub-segments
+    (state passes, scans of the state and of its derivative, output passes): lengths that give one or
+    several sub-segments and a ragged last chunk.  Gate mode there stages q 2^{B}, k 2^{-B} and
+    k 2^{B_last - B} per chunk (B the in-chunk cumulative log2-decay per key dim)."""
     note(f"la_chunk_bwd bf16 d={d} matrix-core mode={mode} L={L} nseg={nseg} H={H}")
     w, inp, gr = _case(mode, "bf16", d, d, L, 64, nseg, seed=500 + L + H + d, B=1, H=H)
     got = _gpu(w, inp, gr, nseg, want_decay=False)

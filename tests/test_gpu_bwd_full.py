@@ -7,7 +7,9 @@ fp64 oracle on a sampled (b, h) without a whole-sequence backward: the oracle's 
 first L - M tokens gives the state S before the window, its backward over the window (from S, with
 ds_out) gives dq, dk, dv there and G', the derivative with respect to S; every earlier token j has
 G_j = a^{L-M-1-j} G' (no d_o before the window), so dk_j = G_j v_j, dv_j = G_j^T k_j, dq_j = 0 and
-ds_in = a^{L-M} G'.  Every token of the sampled sequences is compared.  The head-decay derivative is
+ds_in = a^{L-M} G'.  In gate mode the decay differs per token and key dim, so the oracle's backward
+over the first L - M tokens with d_o = 0 and ds_out = G' gives those tokens' dk, dv and ds_in.  Every
+token of the sampled sequences is compared.  The head-decay derivative is
 checked against its definition as a sum over token pairs (numpy, fp64), over both batch entries.
 """
 import numpy as np
@@ -33,17 +35,32 @@ def _expected(inp, gr, d_o, w, b, h):
     """Exact dq, dk, dv [L, d] and ds_in [dk, dv] of sequence (b, h) (fp64)."""
     L = w.L
     q, k, v = (host32(inp[x][b, h]) for x in ("q", "k", "v"))
-    lam = None if w.mode == "none" else float(host32(inp["decay"])[h])
-    dec = None if w.mode == "none" else host32(inp["decay"])[h:h + 1]
+    gate = w.mode == "gate"
+    lam = None if w.mode in ("none", "gate") else float(host32(inp["decay"])[h])
+    win, pre = slice(L - M, L), slice(0, L - M)
+    if w.mode == "none":
+        dec_pre = dec_win = None
+    elif gate:  # per-token gate [B, H, L, dk]
+        g = host32(inp["decay"])[b:b + 1, h:h + 1]
+        dec_pre, dec_win = g[:, :, pre], g[:, :, win]
+    else:
+        dec_pre = dec_win = host32(inp["decay"])[h:h + 1]
     s_in = None if inp["s_in"] is None else _f64(inp["s_in"][b, h])[None, None]
     # forward state before the window
-    _, s_pre = oracle.recurrence(q[None, None, :L - M], k[None, None, :L - M], v[None, None, :L - M],
-                                 ORC_MODE[w.mode], dec, s_in)
-    win = slice(L - M, L)
+    _, s_pre = oracle.recurrence(q[None, None, pre], k[None, None, pre], v[None, None, pre],
+                                 ORC_MODE[w.mode], dec_pre, s_in, gate_norm=w.gate_norm)
     dqw, dkw, dvw, _, dsw = oracle.recurrence_bwd(
         q[None, None, win], k[None, None, win], v[None, None, win], host32(d_o[b, h])[None, None, win],
-        ORC_MODE[w.mode], dec, s_pre[:, :, 0], _f64(gr["ds_out"][b, h])[None, None])
+        ORC_MODE[w.mode], dec_win, s_pre[:, :, 0], _f64(gr["ds_out"][b, h])[None, None], gate_norm=w.gate_norm)
     G = dsw[0, 0, 0]  # derivative with respect to the state before the window
+    if gate:
+        _, dkp, dvp, _, dsp = oracle.recurrence_bwd(
+            q[None, None, pre], k[None, None, pre], v[None, None, pre], np.zeros((1, 1, L - M, w.dv), np.float32),
+            ORC_MODE[w.mode], dec_pre, s_in, G[None, None, None], gate_norm=w.gate_norm)
+        dq = np.zeros((L, w.dk))
+        dq[win] = dqw[0, 0]
+        return (dq, np.concatenate([dkp[0, 0], dkw[0, 0]]), np.concatenate([dvp[0, 0], dvw[0, 0]]),
+                dsp[0, 0, 0])
     j = np.arange(L - M)
     f = np.ones(L - M) if lam is None else np.exp(lam * (L - M - 1 - j))
     dq = np.zeros((L, w.dk))
@@ -79,7 +96,8 @@ def _dlambda_pairs(inp, gr, d_o, w, h):
 
 @pytest.mark.parametrize("wid,pairs,want_decay", [(1, [(0, 0), (0, 9)], False),
                                                   (2, [(0, 3), (1, 14)], False),
-                                                  (2, [(1, 0), (0, 12)], True)])
+                                                  (2, [(1, 0), (0, 12)], True),
+                                                  (3, [(0, 5), (3, 11)], False)])
 def test_backward_full_size(wid, pairs, want_decay):
     w = WORKLOADS[wid]
     note(f"la_chunk_bwd full size, workload {wid} {w.name}, d_lambda={want_decay}, sampled (b,h) {pairs}")
