@@ -117,17 +117,18 @@ class BackwardStep:
 
 def backward_legs(stream):
     """la_chunk_bwd at the plain (B=1), head-decay (B=2) and gate (B=4) shapes, decays fixed, and at
-    the head-decay shape with d lambda_h (learned decays): median time, tokens/s, GB/s on the
-    compulsory bytes (q, k, v, d_o and the gate read once, dq, dk, dv written once) and per-kernel
-    means."""
+    the head-decay and gate shapes with the decay derivative (learned decays): median time, tokens/s,
+    GB/s on the compulsory bytes (q, k, v, d_o and the gate read once, dq, dk, dv and dg written once)
+    and per-kernel means."""
     import torch
 
     from chunked_scan_amd.inputs import WORKLOADS
 
     backward = {}
-    for wid, want_decay in ((1, False), (2, False), (2, True), (3, False)):
+    for wid, want_decay in ((1, False), (2, False), (2, True), (3, False), (3, True)):
         wb = WORKLOADS[wid]
-        key = wb.name + (" + d_lambda" if want_decay else "")
+        dname = "dg" if wb.mode == "gate" else "d_lambda"
+        key = wb.name + (f" + {dname}" if want_decay else "")
         log(f"[bench] backward: workload {wid} {key}")
         sb = BackwardStep(wb, want_decay)
         for _ in range(60):  # >= 20 ms of work: settled clocks
@@ -140,19 +141,25 @@ def backward_legs(stream):
         # the dq and d lambda output passes read three or four, the dk/dv output pass reads four and
         # writes two; in gate mode the dq and dk/dv passes also read the fp32 gate row (4 d bytes)
         gate = 4 * wb.dk if wb.mode == "gate" else 0
-        per_th = {"chunk_bwd_dq_state_pass": 512 + gate, "chunk_bwd_dq": 1024 + gate,
-                  "chunk_bwd_dkdv_state_pass": 512 + gate, "chunk_bwd_dkdv": 1536 + gate,
-                  "chunk_bwd_dlam_state_pass": 512, "chunk_bwd_dlam": 1024}
+        # the gate derivative: D at every chunk's start (bf16 d x d per 64 tokens) written by the dk/dv
+        # pass and read by the dq pass; chunk_bwd_dg reads q, k, dq, dk and the gate, writes dg
+        dstart = 2 * wb.dk * wb.dv // 64 if (gate and want_decay) else 0
+        per_th = {"chunk_bwd_dq_state_pass": 512 + gate, "chunk_bwd_dq": 1024 + gate + dstart,
+                  "chunk_bwd_dkdv_state_pass": 512 + gate, "chunk_bwd_dkdv": 1536 + gate + dstart,
+                  "chunk_bwd_dlam_state_pass": 512, "chunk_bwd_dlam": 1024,
+                  "chunk_bwd_dg": 8 * wb.dk + 2 * gate}
         for name, d in ks.items():
             if name in per_th and d["launches_per_step"] == 1:
                 by = per_th[name] * th
                 g = by / (d["mean_us"] * 1e-6) / 1e9
                 d.update(algorithmic_bytes=by, gbps=round(g, 1), hbm_frac=round(g / HBM_PEAK_GBS, 4))
-        # compulsory bytes (bf16): q, k, v, d_o (and the fp32 gate) read once, dq, dk, dv written once
+        # compulsory bytes (bf16): q, k, v, d_o (and the fp32 gate) read once, dq, dk, dv (and dg) written once
         comp = th * 2 * (wb.dk + wb.dk + wb.dv + wb.dv) + th * 2 * (wb.dk + wb.dk + wb.dv) + th * gate
+        if gate and want_decay:
+            comp += th * gate
         gbs = comp / (st["median_us"] * 1e-6) / 1e9
         backward[key] = dict(
-            what="la_chunk_bwd: dq, dk, dv, ds_in" + (", d lambda_h" if want_decay else " (decay held fixed)"),
+            what="la_chunk_bwd: dq, dk, dv, ds_in" + (f", {dname}" if want_decay else " (decay held fixed)"),
             B=wb.B, H=wb.H, L=wb.L, decay=wb.decay,
             tokens_per_s=round(wb.B * wb.L / (st["median_us"] * 1e-6), 1), per_step_us=st,
             compulsory_bytes=comp, gbps_on_compulsory_bytes=round(gbs, 1),

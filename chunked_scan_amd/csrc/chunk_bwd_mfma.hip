@@ -11,7 +11,7 @@ hipError_t launch_bwd_mfma_d128(const BwdArgs& a);
 
 bool chunk_bwd_mfma_supported(const BwdArgs& a) {
     return a.bf16 && a.dk == a.dv && (a.dk == 32 || a.dk == 64 || a.dk == 128) && a.chunk == 64 && a.L > 0 &&
-           a.B * a.H > 0 && (a.mode == DECAY_NONE || a.mode == DECAY_HEAD || (a.mode == DECAY_GATE && !a.d_decay));
+           a.B * a.H > 0 && (a.mode == DECAY_NONE || a.mode == DECAY_HEAD || a.mode == DECAY_GATE);
 }
 
 hipError_t launch_chunk_bwd_mfma(const BwdArgs& a) {

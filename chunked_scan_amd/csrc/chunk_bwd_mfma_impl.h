@@ -168,6 +168,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
     const float* __restrict__ init_state,                            // output pass: scanned D^(g)
     double* __restrict__ intra_part,  // head mode, output pass: the intra-chunk part of d lambda_h, or null
+    __bf16* __restrict__ d_start,     // output pass, gate derivative: D at every chunk's start (bf16 [D][D]), or null
     int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm) {
     __shared__ __attribute__((aligned(16))) BwdSmem<D, MODE, STATE_ONLY> sm;
     using Gm = Geo<D>;
@@ -192,6 +193,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     const int64_t t_end = min(t_begin + (int64_t)cps * C, tseg + Lseg);
     const int64_t row_base = bh * L;
     const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
+    const int64_t nch_seg = (Lseg + C - 1) / C;
 
     // ---- D at the sub-segment's end: key rows 32 m + (i / 4) 8 + kg 4 + i % 4, value column 32 w + n32
     f32x16 Dm[NCB];
@@ -293,6 +295,17 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
         }
         __syncthreads();
         if (PF && c > 0) load_chunk(c - 1);  // the previous chunk, while this one is computed
+        if (!STATE_ONLY && d_start && c + 1 < nchunks) {  // D here = D at the start of chunk c + 1
+            __bf16* dst = d_start + (ub * nch_seg + (int64_t)g * cps + c + 1) * D * D;
+#pragma unroll
+            for (int r = 0; r < (D * D / 8 + NT - 1) / NT; r++) {
+                const int p = tid + NT * r;
+                if (p < D * D / 8) {
+                    const int row = p / (D / 8), c8 = (p % (D / 8)) * 8;
+                    *(u32x4*)(dst + row * D + c8) = *(const u32x4*)(&sm.dm[row * PITCH + c8]);
+                }
+            }
+        }
         if (MODE == DECAY_GATE && !STATE_ONLY) {  // B -> 2^{-B} (dk's per-key-dim factor); read after the next barrier
 #pragma unroll
             for (int r = 0; r < C * D / NT; r++) sm.gb[tid + NT * r] = __builtin_amdgcn_exp2f(-sm.gb[tid + NT * r]);
@@ -460,6 +473,16 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 dst[r * D + 32 * cb + n32] = Dm[m][i];
             }
     }
+    if (!STATE_ONLY && d_start && nchunks > 0 && rank == 0) {  // ... which is D at its first chunk's start
+        __bf16* dsd = d_start + (ub * nch_seg + (int64_t)g * cps) * D * D;
+#pragma unroll
+        for (int m = 0; m < NCB; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
+                dsd[r * D + 32 * cb + n32] = (__bf16)Dm[m][i];
+            }
+    }
     if (STATE_ONLY && tid < D) {  // the total decay over this sub-segment, per key dim
         float tot = 1.f;
         if (MODE == DECAY_HEAD) tot = decay_pow(lam, (int)(t_end - t_begin));
@@ -502,6 +525,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     const float* __restrict__ ds_out, int64_t sstride, __bf16* __restrict__ dq,
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
     const float* __restrict__ init_state,                            // output pass: scanned states
+    const __bf16* __restrict__ d_start,  // gate derivative: D at every chunk's start (bf16 [D][D]), or null
+    float* __restrict__ c0_out,          // gate derivative: rowsum(S (.) D) at every chunk's start ([D])
     int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm) {
     __shared__ __attribute__((aligned(16))) DqSmem<D, MODE, STATE_ONLY> sm;
     using Gm = Geo<D>;
@@ -525,6 +550,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     const int64_t t_begin = tseg + (int64_t)g * cps * C;
     const int64_t t_end = min(t_begin + (int64_t)cps * C, tseg + Lseg);
     const int64_t row_base = bh * L;
+    const int64_t nch_seg = (Lseg + C - 1) / C;
     const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
     float gate_total = 0.f;  // gate: log2 of the sub-segment's decay so far, key dim tid (tid < D)
 
@@ -615,6 +641,23 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
         }
         __syncthreads();
         if (PF && c + 1 < nchunks) load_chunk(c + 1);  // the next chunk, while this one is computed
+        if (!STATE_ONLY && c0_out) {  // rowsum(S (.) D) at this chunk's start, per key dim, from S's bf16 copy
+            constexpr int TPR = NT / D, CPT = D / TPR;  // threads per key row, columns per thread
+            const int r = tid / TPR, col0 = (tid % TPR) * CPT;
+            const int64_t ci = ub * nch_seg + (int64_t)g * cps + c;
+            const __bf16* src = d_start + (ci * D + r) * D + col0;
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < CPT; j += 4) {
+                const bf16x4 dd = *(const bf16x4*)(src + j);
+                const bf16x4 ss = *(const bf16x4*)(&sm.sm[r * PITCH + col0 + j]);
+#pragma unroll
+                for (int e = 0; e < 4; e++) acc += (float)ss[e] * (float)dd[e];
+            }
+#pragma unroll
+            for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off);
+            if (tid % TPR == 0) c0_out[ci * D + r] = acc;
+        }
 
         bf16x8 vb[4];  // v operands of this wave's value columns, four 16-token slabs
 #pragma unroll
@@ -988,44 +1031,126 @@ hipError_t launch_dlam(const BwdArgs& a, int G, int cps, float* ps, float* pst, 
     return hipGetLastError();
 }
 
+// Gate derivative, one chunk of one (b, h, segment) per workgroup.  With S the state entering the
+// chunk and D the derivative with respect to it (both from the chunk's start: c0 = rowsum(S (.) D)),
+// the derivative with respect to log a_s of a token s of the chunk is
+//     dlog a_s = c0 + sum over the chunk's tokens t < s of (k_t (.) dk_t - q_t (.) dq_t)
+// (every pair of tokens j < s <= i contributes q_i k_j e^{B_i - B_j} (v_j . d_o_i); the chunk's
+// dq, dk hold the pairs with one end in it, c0 those that cross its start), and log a = -softplus(-g)
+// / gate_norm gives dg = dlog a * sigmoid(-g) / gate_norm.  Lanes take column pairs, NT / (D / 2)
+// groups of C / groups rows each, whose totals are combined through LDS.
+template <int D>
+__global__ __launch_bounds__(NT) void dg_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                const __bf16* __restrict__ dq, const __bf16* __restrict__ dk,
+                                                const float* __restrict__ gate, const float* __restrict__ c0,
+                                                float* __restrict__ dg, int64_t L, int nseg, float inv_norm) {
+    constexpr int PAIRS = D / 2, GROUPS = NT / PAIRS, RPG = C / GROUPS;
+    __shared__ float tot[GROUPS * D];
+    const int tid = threadIdx.x;
+    const int64_t Lseg = L / nseg;
+    const int64_t nch_seg = (Lseg + C - 1) / C;
+    const int64_t ci = blockIdx.x;  // (b, h, segment) * nch_seg + chunk
+    const int64_t ub = ci / nch_seg, sc = ci % nch_seg;
+    const int seg = (int)(ub % nseg);
+    const int64_t bh = ub / nseg;
+    const int64_t t0 = (int64_t)seg * Lseg + sc * C;
+    const int n = (int)min((int64_t)C, (int64_t)seg * Lseg + Lseg - t0);
+    const int d0 = 2 * (tid % PAIRS), grp = tid / PAIRS;
+    float ex0[RPG], ex1[RPG];  // exclusive running sums inside the group
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPG; i++) {
+        const int row = grp * RPG + i;
+        ex0[i] = s0;
+        ex1[i] = s1;
+        if (row < n) {
+            const int64_t off = (bh * L + t0 + row) * D + d0;
+            const bf16x2 qq = *(const bf16x2*)(q + off), kk = *(const bf16x2*)(k + off);
+            const bf16x2 gq = *(const bf16x2*)(dq + off), gk = *(const bf16x2*)(dk + off);
+            s0 += (float)kk[0] * (float)gk[0] - (float)qq[0] * (float)gq[0];
+            s1 += (float)kk[1] * (float)gk[1] - (float)qq[1] * (float)gq[1];
+        }
+    }
+    tot[grp * D + d0] = s0;
+    tot[grp * D + d0 + 1] = s1;
+    __syncthreads();
+    float b0 = c0[ci * D + d0], b1 = c0[ci * D + d0 + 1];
+    for (int gg = 0; gg < grp; gg++) {
+        b0 += tot[gg * D + d0];
+        b1 += tot[gg * D + d0 + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < RPG; i++) {
+        const int row = grp * RPG + i;
+        if (row < n) {
+            const int64_t off = (bh * L + t0 + row) * D + d0;
+            const f32x2 gg = *(const f32x2*)(gate + off);
+            f32x2 out;
+            out[0] = (b0 + ex0[i]) * inv_norm / (1.f + __expf(gg[0]));
+            out[1] = (b1 + ex1[i]) * inv_norm / (1.f + __expf(gg[1]));
+            *(f32x2*)(dg + off) = out;
+        }
+    }
+}
+
 template <int D, int MODE>
 hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* f_decay, float* b_state,
-                       float* b_decay, double* intra_part) {
+                       float* b_decay, double* intra_part, __bf16* d_start, float* c0) {
     const int64_t units = a.B * a.H * a.nseg;
     const __bf16* q = (const __bf16*)a.q;
     const __bf16* k = (const __bf16*)a.k;
     const __bf16* v = (const __bf16*)a.v;
     const __bf16* d_o = (const __bf16*)a.d_o;
+    // dq: forward state pass, scan, output pass (with the gate derivative also rowsum(S (.) D) per chunk)
+    auto dq_passes = [&]() -> hipError_t {
+        hipError_t e;
+        if (G > 1) {
+            LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
+                      bwd_dq_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                          k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr,
+                          nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if ((e = launch_state_scan(f_state, f_decay, f_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
+                return e;
+        }
+        LA_TRACED(a.tr, "chunk_bwd_dq",
+                  bwd_dq_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                      k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, f_state,
+                      d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+        return hipGetLastError();
+    };
+    // dk, dv: backward state pass, reverse-order scan, output pass (with the gate derivative also D at
+    // every chunk's start)
+    auto dkdv_passes = [&]() -> hipError_t {
+        hipError_t e;
+        if (G > 1) {
+            LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass",
+                      bwd_dkdv_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                          q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state, b_decay,
+                          nullptr, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if ((e = launch_state_scan(b_state, b_decay, b_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
+                return e;
+        }
+        LA_TRACED(a.tr, "chunk_bwd_dkdv",
+                  bwd_dkdv_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                      q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out, a.ds_in,
+                      nullptr, nullptr, b_state, intra_part, d_start, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+        return hipGetLastError();
+    };
     hipError_t e;
-    // dq: forward state pass, scan, output pass
-    if (G > 1) {
-        LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
-                  bwd_dq_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                      k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr,
-                      a.H, a.L, a.nseg, G, cps, a.inv_norm));
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_state_scan(f_state, f_decay, f_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
-            return e;
+    if (!d_start) {
+        if ((e = dq_passes()) != hipSuccess) return e;
+        return dkdv_passes();
     }
-    LA_TRACED(a.tr, "chunk_bwd_dq",
-              bwd_dq_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                  k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, f_state,
-                  a.H, a.L, a.nseg, G, cps, a.inv_norm));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // dk, dv: backward state pass, reverse-order scan, output pass
-    if (G > 1) {
-        LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass",
-                  bwd_dkdv_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                      q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state, b_decay,
-                      nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm));
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_state_scan(b_state, b_decay, b_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
-            return e;
-    }
-    LA_TRACED(a.tr, "chunk_bwd_dkdv",
-              bwd_dkdv_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                  q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out, a.ds_in,
-                  nullptr, nullptr, b_state, intra_part, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+    // gate derivative: D per chunk first, then S with rowsum(S (.) D), then the in-chunk sums
+    if ((e = dkdv_passes()) != hipSuccess) return e;
+    if ((e = dq_passes()) != hipSuccess) return e;
+    const int64_t nch_seg = (a.L / a.nseg + C - 1) / C;
+    LA_TRACED(a.tr, "chunk_bwd_dg",
+              dg_kernel<D><<<(unsigned)(units * nch_seg), NT, 0, a.stream>>>(
+                  q, k, (const __bf16*)a.dq, (const __bf16*)a.dk_out, a.decay, c0, a.d_decay, a.L, a.nseg,
+                  a.inv_norm));
     return hipGetLastError();
 }
 
@@ -1040,12 +1165,17 @@ hipError_t launch_d(const BwdArgs& a) {
     mfma_split(sp, &G, &cps);
     const int64_t units = a.B * a.H * a.nseg;
     const bool dlam = a.mode == DECAY_HEAD && a.d_decay;
+    const bool dgate = a.mode == DECAY_GATE && a.d_decay;
     // workspace: fp64 partials of d lambda_h, then the sub-segment states and decays of the dq and
-    // dk/dv passes (and of S and dS/dlambda for d lambda_h)
+    // dk/dv passes (and of S and dS/dlambda for d lambda_h), then for the gate derivative
+    // rowsum(S (.) D) (fp32) and D (bf16) at every chunk's start
     const size_t n_dbl = dlam ? 2 * (size_t)units * G : 0;  // inter- and intra-chunk partials
     const size_t n_state = (size_t)units * (G - 1) * D * D, n_decay = (size_t)units * (G - 1) * D;
     const int nsets = dlam ? 4 : 2;  // state arrays: forward, backward (+ S, St)
-    const size_t bytes = sizeof(double) * n_dbl + sizeof(float) * (nsets * n_state + 3 * n_decay);
+    const size_t n_chunks = dgate ? (size_t)units * (size_t)((a.L / a.nseg + C - 1) / C) : 0;
+    const size_t f_bytes = sizeof(double) * n_dbl + sizeof(float) * (nsets * n_state + 3 * n_decay + n_chunks * D);
+    const size_t ds_off = (f_bytes + 255) / 256 * 256;
+    const size_t bytes = n_chunks ? ds_off + sizeof(__bf16) * n_chunks * D * D : f_bytes;
     char* ws = nullptr;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1063,9 +1193,14 @@ hipError_t launch_d(const BwdArgs& a) {
     float* f_decay = n_decay ? fp + nsets * n_state : nullptr;
     float* b_decay = n_decay ? fp + nsets * n_state + n_decay : nullptr;
     float* l_decay = n_decay ? fp + nsets * n_state + 2 * n_decay : nullptr;
-    if (a.mode == DECAY_HEAD) e = launch_mode<D, DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra);
-    else if (a.mode == DECAY_GATE) e = launch_mode<D, DECAY_GATE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr);
-    else e = launch_mode<D, DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr);
+    float* c0 = n_chunks ? fp + nsets * n_state + 3 * n_decay : nullptr;
+    __bf16* d_start = n_chunks ? (__bf16*)(ws + ds_off) : nullptr;
+    if (a.mode == DECAY_HEAD)
+        e = launch_mode<D, DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra, nullptr, nullptr);
+    else if (a.mode == DECAY_GATE)
+        e = launch_mode<D, DECAY_GATE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr, d_start, c0);
+    else
+        e = launch_mode<D, DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr, nullptr, nullptr);
     if (e == hipSuccess && dlam) e = launch_dlam<D>(a, G, cps, l_state, lt_state, l_decay, part, intra);
     if (ws) {
         hipError_t f = hipFreeAsync(ws, a.stream);

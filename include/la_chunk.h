@@ -189,13 +189,15 @@ la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, cons
  *            state_stride layout, or NULL.
  *   chunk  : 16, 32 or 64.
  * No output may overlap an input or another output.  bf16 inputs with dk = dv in {32, 64, 128}
- * and chunk 64 run on the matrix cores (bf16 operands, fp32 accumulation) with no decay, with a head
- * decay (its derivative summed token pair by token pair, in fp64 partial sums) and with a gate whose
- * derivative is not requested (d_decay NULL); there, as in la_chunk_fwd, each chunk's per-key-dim
- * log-decay sum must stay above -80.  Every other shape, fp32 inputs and the gate derivative run in
- * fp32 arithmetic, with no such range limit.  bf16 outputs are rounded once, to nearest even.  May
- * allocate temporary device workspace from the same stream-ordered pool as la_chunk_fwd (per
- * sub-segment states; a float per token and key dim for the gate derivative).
+ * and chunk 64 run on the matrix cores (bf16 operands, fp32 accumulation) in every decay mode: the
+ * head-decay derivative is summed token pair by token pair (fp64 partial sums), the gate derivative
+ * per chunk from rowsum(S (.) D) at the chunk's start plus an in-chunk running sum of
+ * k (.) dk - q (.) dq; in gate mode, as in la_chunk_fwd, each chunk's per-key-dim log-decay sum must
+ * stay above -80 there.  Every other shape and fp32 inputs run in fp32 arithmetic, with no such
+ * range limit.  bf16 outputs are rounded once, to nearest even.  May allocate temporary device
+ * workspace from the same stream-ordered pool as la_chunk_fwd (per sub-segment states; for the gate
+ * derivative a bf16 d_k x d_v matrix and d_k floats per chunk on the matrix cores, a float per token
+ * and key dim on the fp32 path).
  * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_DECAY, LA_ERR_ALIAS,
  * LA_ERR_UNSUPPORTED or LA_ERR_LAUNCH.
  */

@@ -160,6 +160,20 @@ def test_bwd_bf16_matrix_core_head_decay_derivative(d, L, nseg, B):
     _compare(got, ref, "bf16", "head")
 
 
+@pytest.mark.parametrize("d,L,nseg,B", [(128, 192, 1, 1), (128, 1000, 1, 1), (128, 2048, 2, 2), (128, 4096, 1, 1),
+                                        (64, 1000, 1, 1), (64, 2048, 2, 2), (32, 1000, 1, 1), (32, 640, 1, 2)])
+def test_bwd_bf16_matrix_core_gate_derivative(d, L, nseg, B):
+    """dg on the matrix-core path (bf16): per chunk, rowsum(S (.) D) at the chunk's start plus the
+    in-chunk running sum of k (.) dk - q (.) dq; one or several sub-segments, two segments, two
+    batches, ragged last chunks."""
+    note(f"la_chunk_bwd bf16 d={d} gate derivative L={L} nseg={nseg} B={B}")
+    w, inp, gr = _case("gate", "bf16", d, d, L, 64, nseg, seed=700 + L + d, B=B, H=3)
+    got = _gpu(w, inp, gr, nseg)
+    ref = _oracle(w, inp, gr, nseg)
+    print(f"  d_decay rel err {rel_err(got[3], ref[3]):.2e}")
+    _compare(got, ref, "bf16", "gate")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_bwd_gate_strong_decay(dtype):
     """Gate mode on the fp32 path factorises e^{B_i - B_j} into q e^{B} and k e^{-B} per chunk unless a

@@ -8,9 +8,9 @@ first L - M tokens gives the state S before the window, its backward over the wi
 ds_out) gives dq, dk, dv there and G', the derivative with respect to S; every earlier token j has
 G_j = a^{L-M-1-j} G' (no d_o before the window), so dk_j = G_j v_j, dv_j = G_j^T k_j, dq_j = 0 and
 ds_in = a^{L-M} G'.  In gate mode the decay differs per token and key dim, so the oracle's backward
-over the first L - M tokens with d_o = 0 and ds_out = G' gives those tokens' dk, dv and ds_in.  Every
-token of the sampled sequences is compared.  The head-decay derivative is
-checked against its definition as a sum over token pairs (numpy, fp64), over both batch entries.
+over the first L - M tokens with d_o = 0 and ds_out = G' gives those tokens' dk, dv, dg and ds_in.
+Every token of the sampled sequences is compared.  The head-decay derivative is checked against its
+definition as a sum over token pairs (numpy, fp64), over both batch entries.
 """
 import numpy as np
 import pytest
@@ -49,18 +49,18 @@ def _expected(inp, gr, d_o, w, b, h):
     # forward state before the window
     _, s_pre = oracle.recurrence(q[None, None, pre], k[None, None, pre], v[None, None, pre],
                                  ORC_MODE[w.mode], dec_pre, s_in, gate_norm=w.gate_norm)
-    dqw, dkw, dvw, _, dsw = oracle.recurrence_bwd(
+    dqw, dkw, dvw, dgw, dsw = oracle.recurrence_bwd(
         q[None, None, win], k[None, None, win], v[None, None, win], host32(d_o[b, h])[None, None, win],
         ORC_MODE[w.mode], dec_win, s_pre[:, :, 0], _f64(gr["ds_out"][b, h])[None, None], gate_norm=w.gate_norm)
     G = dsw[0, 0, 0]  # derivative with respect to the state before the window
     if gate:
-        _, dkp, dvp, _, dsp = oracle.recurrence_bwd(
+        _, dkp, dvp, dgp, dsp = oracle.recurrence_bwd(
             q[None, None, pre], k[None, None, pre], v[None, None, pre], np.zeros((1, 1, L - M, w.dv), np.float32),
             ORC_MODE[w.mode], dec_pre, s_in, G[None, None, None], gate_norm=w.gate_norm)
         dq = np.zeros((L, w.dk))
         dq[win] = dqw[0, 0]
         return (dq, np.concatenate([dkp[0, 0], dkw[0, 0]]), np.concatenate([dvp[0, 0], dvw[0, 0]]),
-                dsp[0, 0, 0])
+                dsp[0, 0, 0], np.concatenate([dgp[0, 0], dgw[0, 0]]))
     j = np.arange(L - M)
     f = np.ones(L - M) if lam is None else np.exp(lam * (L - M - 1 - j))
     dq = np.zeros((L, w.dk))
@@ -68,7 +68,7 @@ def _expected(inp, gr, d_o, w, b, h):
     dk = np.concatenate([f[:, None] * (v[:L - M].astype(np.float64) @ G.T), dkw[0, 0]])
     dv = np.concatenate([f[:, None] * (k[:L - M].astype(np.float64) @ G), dvw[0, 0]])
     ds_in = (1.0 if lam is None else np.exp(lam * (L - M))) * G
-    return dq, dk, dv, ds_in
+    return dq, dk, dv, ds_in, None
 
 
 def _dlambda_pairs(inp, gr, d_o, w, h):
@@ -97,7 +97,8 @@ def _dlambda_pairs(inp, gr, d_o, w, h):
 @pytest.mark.parametrize("wid,pairs,want_decay", [(1, [(0, 0), (0, 9)], False),
                                                   (2, [(0, 3), (1, 14)], False),
                                                   (2, [(1, 0), (0, 12)], True),
-                                                  (3, [(0, 5), (3, 11)], False)])
+                                                  (3, [(0, 5), (3, 11)], False),
+                                                  (3, [(2, 7), (1, 15)], True)])
 def test_backward_full_size(wid, pairs, want_decay):
     w = WORKLOADS[wid]
     note(f"la_chunk_bwd full size, workload {wid} {w.name}, d_lambda={want_decay}, sampled (b,h) {pairs}")
@@ -109,7 +110,7 @@ def test_backward_full_size(wid, pairs, want_decay):
                                             gr["ds_out"], mode=w.mode, chunk=w.chunk, want_decay=want_decay)
     torch.cuda.synchronize()
     for b, h in pairs:
-        e_dq, e_dk, e_dv, e_ds = _expected(inp, gr, d_o, w, b, h)
+        e_dq, e_dk, e_dv, e_ds, e_dg = _expected(inp, gr, d_o, w, b, h)
         assert rel_err(dq[b, h], e_dq) <= TOL["bf16"], ("dq", b, h)
         assert rel_err(dk[b, h], e_dk) <= TOL["bf16"], ("dk", b, h)
         assert rel_err(dv[b, h], e_dv) <= TOL["bf16"], ("dv", b, h)
@@ -117,7 +118,11 @@ def test_backward_full_size(wid, pairs, want_decay):
         # (head 0: a^16288 = e^-509), where the correctly rounded value is zero
         assert rel_err(ds_in[b, h, 0], e_ds.astype(np.float32)) <= TOL["bf16"], ("ds_in", b, h)
         assert torch.count_nonzero(dq[b, h, :w.L - M]) == 0  # no loss derivative before the window
-        if want_decay:
+        if want_decay and w.mode == "gate":  # dg of every token of the sequence (oracle, fp64)
+            err = rel_err(dd[b, h], e_dg)
+            print(f"  dg ({b},{h}) rel err {err:.2e}")
+            assert err <= TOL["bf16"], ("dg", b, h)
+        elif want_decay:
             ref = _dlambda_pairs(inp, gr, d_o, w, h)
             got = float(dd[h])
             print(f"  d_lambda[{h}] gpu {got:.6e} pairs {ref:.6e}")
