@@ -100,6 +100,11 @@ struct Dma {
     static constexpr int NDMA = (STATE_ONLY ? 2 : 3) * 4;  // DMA instructions per chunk per loader wave
     // Loader wave lw fills rows 16 lw .. 16 lw + 15 of each tile; rows past the chunk end re-read
     // the chunk's last valid row.
+    // Cache policy: the output pass is the last reader of k and v, so their loads are marked
+    // non-temporal (nt), which keeps them from displacing q and o in the last-level cache before
+    // the output correction reads those two again (head-decay step, B2: 206 -> 186 us); q keeps the
+    // default policy, and so does the state pass, whose k and v the output pass reads next.
+    static constexpr int KV_CPOL = STATE_ONLY ? 0 : 2;
     __device__ static __forceinline__ void issue(const __bf16* q, const __bf16* k, const __bf16* v, Ring r,
                                                  int64_t row0, int n, int lw, int lane) {
         // a wave-uniform base plus a 32-bit lane offset per instruction
@@ -111,8 +116,8 @@ struct Dma {
             const int dst = (4 * lw + j) * 512;
             if (!STATE_ONLY)
                 __builtin_amdgcn_global_load_lds((const void*)(q + base + off), (lds_void*)(r.q + dst), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(k + base + off), (lds_void*)(r.k + dst), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(v + base + off), (lds_void*)(r.v + dst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(k + base + off), (lds_void*)(r.k + dst), 16, 0, KV_CPOL);
+            __builtin_amdgcn_global_load_lds((const void*)(v + base + off), (lds_void*)(r.v + dst), 16, 0, KV_CPOL);
         }
     }
 };
