@@ -600,6 +600,16 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
         const int n = (int)min((int64_t)C, t_end - t0);
         __syncthreads();  // the previous chunk is done with every LDS tile
         if (!PF) load_chunk(c);
+        // gate derivative: this thread's part of D at the chunk's start (key row tid / TPR), loaded
+        // here so that it arrives while the chunk is staged
+        constexpr int TPR = NT / D, CPT = D / TPR;  // threads per key row, columns per thread
+        bf16x4 dst4[STATE_ONLY ? 1 : CPT / 4];
+        const int64_t ci = ub * nch_seg + (int64_t)g * cps + c;
+        if (!STATE_ONLY && c0_out) {
+            const __bf16* src = d_start + (ci * D + tid / TPR) * D + (tid % TPR) * CPT;
+#pragma unroll
+            for (int j = 0; j < CPT / 4; j++) dst4[j] = *(const bf16x4*)(src + 4 * j);
+        }
         if (MODE == DECAY_GATE) {
             gate_chunk_logdecay<D>(rg, n, inv_norm, sm.gb, sm.gtot, sm.gel, tid);
             if (tid < D) gate_total += sm.gb[(C - 1) * D + tid];
@@ -642,17 +652,13 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
         __syncthreads();
         if (PF && c + 1 < nchunks) load_chunk(c + 1);  // the next chunk, while this one is computed
         if (!STATE_ONLY && c0_out) {  // rowsum(S (.) D) at this chunk's start, per key dim, from S's bf16 copy
-            constexpr int TPR = NT / D, CPT = D / TPR;  // threads per key row, columns per thread
             const int r = tid / TPR, col0 = (tid % TPR) * CPT;
-            const int64_t ci = ub * nch_seg + (int64_t)g * cps + c;
-            const __bf16* src = d_start + (ci * D + r) * D + col0;
             float acc = 0.f;
 #pragma unroll
-            for (int j = 0; j < CPT; j += 4) {
-                const bf16x4 dd = *(const bf16x4*)(src + j);
-                const bf16x4 ss = *(const bf16x4*)(&sm.sm[r * PITCH + col0 + j]);
+            for (int j = 0; j < CPT / 4; j++) {
+                const bf16x4 ss = *(const bf16x4*)(&sm.sm[r * PITCH + col0 + 4 * j]);
 #pragma unroll
-                for (int e = 0; e < 4; e++) acc += (float)ss[e] * (float)dd[e];
+                for (int e = 0; e < 4; e++) acc += (float)ss[e] * (float)dst4[j][e];
             }
 #pragma unroll
             for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off);
