@@ -184,3 +184,18 @@ def test_bwd_gate_strong_decay(dtype):
     w, inp, gr = _case("gate", dtype, 64, 32, 200, 64, 1, seed=91)
     inp["decay"][..., :4] = -40.0
     _compare(_gpu(w, inp, gr, 1), _oracle(w, inp, gr, 1), dtype, "gate")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_matrix_core_gate_strong_decay_within_range(d):
+    """The matrix-core gate path factorises every chunk's pair weights, which bounds the chunk's
+    decay sum per key dim from below (-80): key dims 0..7 here decay by about -0.875 per token
+    (g = -14), -56 over a chunk, the others as drawn; every derivative, dg included, against the
+    oracle."""
+    note(f"la_chunk_bwd bf16 d={d} matrix-core gate, chunk decay sums near -56 on 8 key dims")
+    w, inp, gr = _case("gate", "bf16", d, d, 300, 64, 1, seed=93 + d, B=1, H=2)
+    inp["decay"][..., :8] = -14.0
+    got = _gpu(w, inp, gr, 1)
+    ref = _oracle(w, inp, gr, 1)
+    print(f"  d_decay rel err {rel_err(got[3], ref[3]):.2e}")
+    _compare(got, ref, "bf16", "gate")
