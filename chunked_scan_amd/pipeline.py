@@ -63,10 +63,15 @@ def _correct(step, s_recv, nseg, seg_begin, timers):
                          nseg=nseg, seg_begin=seg_begin, timer=timers.get("corr"))
 
 
-def subsegments(B: int, H: int, L: int, target_units: int = 256, min_len: int = 256) -> int:
+def subsegments(B: int, H: int, L: int, target_units: int = 0, min_len: int = 256, dk: int = 128) -> int:
     """Sub-segments per sequence for a device step: about ``target_units`` (b,h,sub-segment) units
-    in all (one round of workgroups on the compute units), each at least ``min_len`` tokens; G must
-    divide L, and lengths that are whole 64-token chunks are preferred."""
+    in all, each at least ``min_len`` tokens; G must divide L, and lengths that are whole 64-token
+    chunks are preferred.  By default 256 units (one workgroup per compute unit) at dk = 128 and
+    512 below: the small-head kernels are latency-bound and several of their workgroups share a
+    compute unit (B1 H16 L16k, G = 16 -> 32: dk = 64 step 61.9 -> 54.4 us, dk = 32 41.1 -> 40.4 us;
+    G = 64 gains no more at dk = 32, where its 65-entry scan leaves the scan's vector form)."""
+    if target_units <= 0:
+        target_units = 256 if dk >= 128 else 512
     want = max(1, -(-target_units // max(1, B * H)))
     cands = [g for g in range(1, want + 1) if L % g == 0 and (g == 1 or L // g >= min_len)]
     whole = [g for g in cands if (L // g) % 64 == 0]
@@ -82,7 +87,7 @@ class DeviceStep:
         B, H, L, dk = q.shape
         dv = v.shape[-1]
         dev = q.device
-        G = subseg or subsegments(B, H, L)
+        G = subseg or subsegments(B, H, L, dk=dk)
         if L % G:
             raise ValueError(f"{G} sub-segments do not divide L = {L}")
         self.q, self.k, self.v, self.decay = q, k, v, decay
