@@ -199,3 +199,20 @@ def test_bwd_matrix_core_gate_strong_decay_within_range(d):
     ref = _oracle(w, inp, gr, 1)
     print(f"  d_decay rel err {rel_err(got[3], ref[3]):.2e}")
     _compare(got, ref, "bf16", "gate")
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("subseg_chunks", [1, 3, 0])
+def test_bwd_matrix_core_subsegment_length(mode, subseg_chunks):
+    """The sub-segment length of the matrix-core backward changes the rounding order only: one chunk
+    per sub-segment (G = 71 here, so every scan of the backward, the d lambda_h ones included, runs
+    over more than 64 entries), three chunks, and the automatic choice, each against the oracle with
+    the decay derivative."""
+    note(f"la_chunk_bwd bf16 d=64 mode={mode} subseg_chunks={subseg_chunks}")
+    w, inp, gr = _case(mode, "bf16", 64, 64, 64 * 70 + 5, 64, 1, seed=800 + subseg_chunks, B=1, H=2)
+    d = to_dev(inp)
+    g = to_dev(gr)
+    got = lb.la_chunk_bwd(d["q"], d["k"], d["v"], g["d_o"], d["decay"], d["s_in"], g["ds_out"], mode=w.mode,
+                          chunk=64, gate_norm=w.gate_norm, subseg_chunks=subseg_chunks)
+    torch.cuda.synchronize()
+    _compare(got, _oracle(w, inp, gr, 1), "bf16", mode)
