@@ -255,7 +255,8 @@ def epsilon(w, inp, step, stream, steps: int = 20):
 def state_size_sweep(stream):
     """The falsifier's question asked on one GPU: how the decomposition's cost (the device step
     against one exact forward call, both on the same inputs) moves with the state size dk x dv at
-    a fixed token count (B1 H16 L16384, bf16, no decay, S_recv drawn N(0, 0.05)).  Median us."""
+    a fixed token count (B1 H16 L16384, bf16, no decay, S_recv drawn N(0, 0.05)).  Median us.
+    For d = 32 and 64 also the device step with 128-token chunks (the chunk-length variant)."""
     import math
 
     import torch
@@ -279,13 +280,22 @@ def state_size_sweep(stream):
         torch.cuda.synchronize()
         bwd = step_stats(bw, 20, stream)["median_us"]
         del bw
-        out[f"d{d}"] = dict(state_bytes=4 * d * d, zeco_step_us=eps["zeco_step"],
+        c128 = None
+        if d < 128:
+            s128 = DeviceStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=128)
+            for _ in range(150):
+                s128.run()
+            torch.cuda.synchronize()
+            c128 = step_stats(s128, 30, stream)["median_us"]
+            del s128
+        out[f"d{d}"] = dict(state_bytes=4 * d * d, zeco_step_us=eps["zeco_step"], chunk128_step_us=c128,
                             one_call_exact_us=eps["one_call_exact"],
                             overhead_us=round(eps["zeco_step"] - eps["one_call_exact"], 2),
                             overhead_frac=round(eps["zeco_step"] / eps["one_call_exact"] - 1, 4),
                             backward_us=bwd,
                             kernels={n: round(v["mean_us"], 2) for n, v in ks.items()})
-        log(f"[bench] state size d={d}: device step {eps['zeco_step']:.1f} us, one exact call "
+        log(f"[bench] state size d={d}: device step {eps['zeco_step']:.1f} us"
+            + (f" (128-token chunks {c128:.1f} us)" if c128 else "") + ", one exact call "
             f"{eps['one_call_exact']:.1f} us, backward {bwd:.1f} us; " +
             ", ".join(f"{n} {v['mean_us']:.1f}" for n, v in ks.items()))
         del step, inp

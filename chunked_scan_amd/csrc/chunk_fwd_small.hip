@@ -1,4 +1,5 @@
-// chunk_fwd_small.hip -- bf16 matrix-core (MFMA) chunked forward for dk = dv = 32 or 64, chunk 64.
+// chunk_fwd_small.hip -- bf16 matrix-core (MFMA) chunked forward for dk = dv = 32 or 64, chunks of 64
+// or 128 tokens.
 //
 // The same chunk algebra as the d = 128 kernel (chunk_fwd_pipe.hip), in a simpler shape sized for
 // small heads: one workgroup of 4 waves per (b, h, segment, sub-segment), the chunk's q, k, v (and
@@ -20,15 +21,21 @@
 // Each wave keeps the state columns of its block in MFMA accumulators, all D key rows, so waves
 // that share a column block update identical copies: extra matrix-core work, no state traffic
 // through LDS.  The causal score blocks (0,0), (1,0), (1,1) go to waves 0, 2, 3 through LDS.
+//
+// 128-token chunks (CH = 128; the chunk-length variant): four 32-row output blocks, wave w taking
+// those congruent to its rank modulo the waves of its column block, and the ten causal score
+// blocks dealt to the waves in turn; tiles, the score tile and the token slabs of the V and K
+// operands double.  The pair weights and the state update are the same algebra over the longer
+// chunk, so in gate mode the per-key-dim decay sum that must stay above -80 is the 128-token
+// chunk's.
 #include "la_device.h"
 #include "la_internal.h"
 
 namespace la {
 namespace {
 
-constexpr int C = 64;     // chunk length
+constexpr int C = 64;     // the tile length of the tile flags (and the default chunk length)
 constexpr int NT = 256;   // lanes per workgroup
-constexpr int PPITCH = 72;  // bf16 row pitch of P
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -46,26 +53,27 @@ __device__ __forceinline__ u32x4 scale8s(u32x4 w, float f) {
     return scale8(w, ff);
 }
 
-template <int D>
+template <int D, int CH>
 struct SmallSmem {
     static constexpr int PITCH = D + 8;  // bf16: 16-byte aligned rows, conflict-free 16-byte row reads
-    static constexpr int TILE = C * PITCH;
+    static constexpr int TILE = CH * PITCH;
+    static constexpr int PP = CH + 8;    // bf16 row pitch of P
     __bf16 q[TILE];   // qbar (gate) or q
     __bf16 kp[TILE];  // kbar (gate) or k: the K side of P
     __bf16 kt[TILE];  // ktilde: keys scaled by the decay to the chunk end
     __bf16 v[TILE];
-    __bf16 p[C * PPITCH];
+    __bf16 p[CH * PP];
 };
-template <int D>
+template <int D, int CH>
 struct SmallSmemGate {
-    float b[C * D];            // in-chunk inclusive cumulative log2-decay
+    float b[CH * D];           // in-chunk inclusive cumulative log2-decay
     float el[D];               // 2^{B_{n-1}}: the chunk's total decay per key dim
     float tot[(NT / D) * D];   // per-part totals of the cumsum
     float run[D];              // log2 decay from the segment start to the chunk start
     float cs[D];               // 2^{run}: the decay from the segment start to the chunk start
 };
 
-template <int D, int MODE, bool STATE_ONLY>
+template <int D, int MODE, bool STATE_ONLY, int CH>
 __global__ __launch_bounds__(NT) void small_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ decay, const float* __restrict__ s_in, __bf16* __restrict__ o,
@@ -77,14 +85,17 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
     constexpr int NCB = D / 32;       // 32-wide column blocks
     constexpr int WPC = 4 / NCB;      // waves per column block
     constexpr int KS = D / 16;        // 16-wide k slabs of a D-long contraction
-    constexpr int PR = C * D / 8 / NT;  // 16-byte pieces of a bf16 tile per lane
-    constexpr int PG = C * D / 4 / NT;  // 16-byte pieces of an fp32 g tile per lane
-    using Sm = SmallSmem<D>;
+    constexpr int PR = CH * D / 8 / NT;  // 16-byte pieces of a bf16 tile per lane
+    constexpr int PG = CH * D / 4 / NT;  // 16-byte pieces of an fp32 g tile per lane
+    constexpr int NSLAB = CH / 16;       // 16-token slabs of a chunk
+    constexpr int NRB = CH / 32;         // 32-row blocks of a chunk
+    using Sm = SmallSmem<D, CH>;
     constexpr int PITCH = Sm::PITCH;
+    constexpr int PPITCH = Sm::PP;
     constexpr int PIECES_ROW = D / 8;   // 16-byte pieces per bf16 row
     __shared__ __attribute__((aligned(16))) Sm sm;
-    __shared__ __attribute__((aligned(16))) SmallSmemGate<D> sg_[1];  // unused outside gate mode
-    SmallSmemGate<D>& sg = sg_[0];
+    __shared__ __attribute__((aligned(16))) SmallSmemGate<D, CH> sg_[1];  // unused outside gate mode
+    SmallSmemGate<D, CH>& sg = sg_[0];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -93,7 +104,7 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
     const int kg = lane >> 5;
     const int cb = w % NCB;    // this wave's value-column block
     const int rank = w / NCB;  // this wave's rank among the waves of that block
-    // output row blocks of this wave: rb = rank, rank + WPC, ... below 2
+    // output row blocks of this wave: rb = rank, rank + WPC, ... below NRB
     const int64_t u = blockIdx.x;
     const int gper = STATE_ONLY ? (G - 1) : G;
     const int g = (int)(u % gper);
@@ -102,8 +113,8 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
     const int64_t bh = ub / nseg;
     const int64_t h = bh % H;
     const int64_t Lseg = L / nseg;
-    const int64_t t_begin = (int64_t)seg * Lseg + (int64_t)g * cps * C;
-    const int64_t t_end = min(t_begin + (int64_t)cps * C, (int64_t)(seg + 1) * Lseg);
+    const int64_t t_begin = (int64_t)seg * Lseg + (int64_t)g * cps * CH;
+    const int64_t t_end = min(t_begin + (int64_t)cps * CH, (int64_t)(seg + 1) * Lseg);
     const int64_t row_base = bh * L;
     const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
 
@@ -159,13 +170,13 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
         for (int gg = 0; gg < g; gg++) r0 += __builtin_amdgcn_logf(part_decay[(ub * (G - 1) + gg) * D + tid]);
         sg.run[tid] = r0;
     }
-    const int64_t tps = (Lseg + C - 1) / C;
-    const int nchunks = (int)((t_end - t_begin + C - 1) / C);
-    if (nchunks > 0) load_chunk(t_begin, (int)min((int64_t)C, t_end - t_begin));
+    const int64_t tps = (Lseg + C - 1) / C;  // 64-token flag tiles per segment
+    const int nchunks = (int)((t_end - t_begin + CH - 1) / CH);
+    if (nchunks > 0) load_chunk(t_begin, (int)min((int64_t)CH, t_end - t_begin));
 
     for (int c = 0; c < nchunks; c++) {
-        const int64_t t0 = t_begin + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, t_end - t0);
+        const int64_t t0 = t_begin + (int64_t)c * CH;
+        const int n = (int)min((int64_t)CH, t_end - t0);
         __syncthreads();  // the previous chunk is done with every LDS tile
 
         // ---- stage the prefetched chunk into LDS, folding in the decay factors
@@ -180,8 +191,8 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
                 *(f32x4*)(&sg.b[row * D + c4]) = lg;
             }
             __syncthreads();
-            {   // inclusive cumsum over the 64 rows per key dim: NT / D parts of R rows each
-                constexpr int NPART = NT / D, R = C / NPART;
+            {   // inclusive cumsum over the chunk's rows per key dim: NT / D parts of R rows each
+                constexpr int NPART = NT / D, R = CH / NPART;
                 const int d = tid % D, part = tid / D;
                 float vals[R];
 #pragma unroll
@@ -210,8 +221,10 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
                 // the chunk's tile flag: q times the cumulative decay is exactly zero on the whole
                 // chunk when the decay to its start is zero for every key dim (it only shrinks)
                 const int any_live = __syncthreads_or(live);
-                if (qdec_out && tile_live && tid == 0)
-                    tile_live[(bh * nseg + seg) * tps + (int64_t)g * cps + c] = any_live ? 0x01010101u : 0u;
+                if (qdec_out && tile_live && tid < CH / C) {  // the chunk's 64-token flag tiles
+                    const int64_t tile = ((int64_t)g * cps + c) * (CH / C) + tid;
+                    if (tile < tps) tile_live[(bh * nseg + seg) * tps + tile] = any_live ? 0x01010101u : 0u;
+                }
             }
 #pragma unroll
             for (int r = 0; r < PR; r++) {
@@ -257,24 +270,24 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
         __syncthreads();
 
         // ---- prefetch the next chunk while this one is computed
-        if (c + 1 < nchunks) load_chunk(t0 + C, (int)min((int64_t)C, t_end - (t0 + C)));
+        if (c + 1 < nchunks) load_chunk(t0 + CH, (int)min((int64_t)CH, t_end - (t0 + CH)));
 
-        // ---- V operand of this wave's 32 value columns, for the 4 token slabs (P V and K^T V)
-        bf16x8 vb[4];
+        // ---- V operand of this wave's 32 value columns, for the chunk's token slabs (P V and K^T V)
+        bf16x8 vb[NSLAB];
         {
             const int G16 = lane >> 4, i16 = lane & 15;
             const int col = 32 * cb + (G16 & 1) * 16 + (i16 & 3) * 4;
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
+            for (int ks = 0; ks < NSLAB; ks++) {
                 const int tb = 16 * ks + (G16 >> 1) * 8 + (i16 >> 2);
                 vb[ks] = cat(lds_tr16(&sm.v[tb * PITCH + col]), lds_tr16(&sm.v[(tb + 4) * PITCH + col]));
             }
         }
 
         if (!STATE_ONLY) {
-            // ---- intra-chunk scores: causal 32x32 blocks (0,0), (1,0), (1,1) on waves 0, 2, 3
-            if (w != 1) {
-                const int rb = w >> 1, sb_ = (w == 3) ? 1 : 0;
+            // ---- intra-chunk scores: causal 32x32 blocks (0,0), (1,0), (1,1) on waves 0, 2, 3; with
+            // 128-token chunks the ten blocks (rb, sb), sb <= rb < 4, in turn over the four waves
+            auto score_block = [&](int rb, int sb_) {
                 f32x16 acc = {};
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) {
@@ -290,6 +303,15 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
                     if (MODE == DECAY_HEAD) val *= decay_pow(lam, max(row - col, 0));
                     if (col > row) val = 0.f;
                     sm.p[row * PPITCH + col] = (__bf16)val;
+                }
+            };
+            if constexpr (CH == 64) {
+                if (w != 1) score_block(w >> 1, (w == 3) ? 1 : 0);
+            } else {
+                for (int blk = w; blk < NRB * (NRB + 1) / 2; blk += 4) {
+                    int rb = 0;
+                    while ((rb + 1) * (rb + 2) / 2 <= blk) rb++;
+                    score_block(rb, blk - rb * (rb + 1) / 2);
                 }
             }
             // the state as bf16 B operands: slab (m, hh) covers key rows 32m + 16hh + {kg*4 + 0..3, 8 + kg*4 + 0..3}
@@ -307,8 +329,8 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
 
             // ---- outputs: this wave's column block, its row blocks
 #pragma unroll
-            for (int rb = 0; rb < 2; rb++) {
-                if (rb % WPC != rank % WPC || (WPC > 2 && rank >= 2)) continue;
+            for (int rb = 0; rb < NRB; rb++) {
+                if (rb % WPC != rank % WPC) continue;
                 f32x16 acc = {};
                 const __bf16* qrow = &sm.q[(rb * 32 + n32) * PITCH + kg * 4];
 #pragma unroll
@@ -357,7 +379,7 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
                 }
                 const int col = 32 * m + (G16 & 1) * 16 + (i16 & 3) * 4;
 #pragma unroll
-                for (int ks = 0; ks < 4; ks++) {
+                for (int ks = 0; ks < NSLAB; ks++) {
                     const int tb = 16 * ks + (G16 >> 1) * 8 + (i16 >> 2);
                     const bf16x8 a = cat(lds_tr16(&sm.kt[tb * PITCH + col]), lds_tr16(&sm.kt[(tb + 4) * PITCH + col]));
                     S[m] = mfma(a, vb[ks], S[m]);
@@ -390,7 +412,7 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
     }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, int CH>
 hipError_t launch_small_mode(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
     const int64_t ub = a.B * a.H * a.nseg;
     const bool fused = MODE == DECAY_GATE;  // q times cumulative decay, totals and tile flags from the staging
@@ -400,7 +422,7 @@ hipError_t launch_small_mode(const FwdArgs& a, int G, int cps, float* part_state
     __bf16* o = (__bf16*)a.o;
     if (G > 1) {
         LA_TRACED(a.tr, "chunk_fwd_small_state_pass",
-                  small_fwd_kernel<D, MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
+                  small_fwd_kernel<D, MODE, true, CH><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
                       q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
                       a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0, nullptr));
         hipError_t e = hipGetLastError();
@@ -409,27 +431,65 @@ hipError_t launch_small_mode(const FwdArgs& a, int G, int cps, float* part_state
         if (e != hipSuccess) return e;
     }
     LA_TRACED(a.tr, "chunk_fwd_small_output_pass",
-              small_fwd_kernel<D, MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
+              small_fwd_kernel<D, MODE, false, CH><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
                   q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, part_decay, part_state, a.H, a.L,
                   a.nseg, G, cps, a.inv_norm, fused ? (__bf16*)a.q_dec : nullptr, fused ? a.total : nullptr,
                   a.total_stride, fused ? a.tile_live : nullptr));
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, int CH>
 hipError_t launch_small_d(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
     switch (a.mode) {
-        case DECAY_HEAD: return launch_small_mode<D, DECAY_HEAD>(a, G, cps, part_state, part_decay);
-        case DECAY_GATE: return launch_small_mode<D, DECAY_GATE>(a, G, cps, part_state, part_decay);
-        default: return launch_small_mode<D, DECAY_NONE>(a, G, cps, part_state, part_decay);
+        case DECAY_HEAD: return launch_small_mode<D, DECAY_HEAD, CH>(a, G, cps, part_state, part_decay);
+        case DECAY_GATE: return launch_small_mode<D, DECAY_GATE, CH>(a, G, cps, part_state, part_decay);
+        default: return launch_small_mode<D, DECAY_NONE, CH>(a, G, cps, part_state, part_decay);
     }
 }
 
 }  // namespace
 
 hipError_t launch_chunk_fwd_small(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
-    if (a.dk == 64) return launch_small_d<64>(a, G, cps, part_state, part_decay);
-    return launch_small_d<32>(a, G, cps, part_state, part_decay);
+    if (a.dk == 64) return launch_small_d<64, 64>(a, G, cps, part_state, part_decay);
+    return launch_small_d<32, 64>(a, G, cps, part_state, part_decay);
+}
+
+// 128-token chunks: the same split as for 64-token chunks (about 256 workgroups, a fixed
+// sub-segment length when the caller gives one), counted in 128-token chunks, at least two each.
+hipError_t launch_chunk_fwd_small128(const FwdArgs& a) {
+    constexpr int CH = 128;
+    const int64_t units = a.B * a.H * a.nseg;
+    const int64_t nch = (a.L / a.nseg + CH - 1) / CH;
+    int64_t cps;
+    if (a.subseg_chunks > 0) {
+        cps = a.subseg_chunks;
+    } else {
+        const int64_t g_want = (256 + units - 1) / units;
+        cps = max((int64_t)2, (nch + g_want - 1) / g_want);
+    }
+    if (cps > nch) cps = nch > 0 ? nch : 1;
+    const int G = (int)max((int64_t)1, (nch + cps - 1) / cps);
+    float* part_state = nullptr;
+    float* part_decay = nullptr;
+    hipError_t e = hipSuccess;
+    if (G > 1) {
+        int dev = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+        hipMemPool_t pool = workspace_pool(dev);
+        if (!pool) return hipErrorOutOfMemory;
+        const size_t n = (size_t)units * (G - 1), D = (size_t)a.dk;
+        e = hipMallocFromPoolAsync((void**)&part_state, n * D * D * sizeof(float) + n * D * sizeof(float), pool,
+                                   a.stream);
+        if (e != hipSuccess) return e;
+        part_decay = part_state + n * D * D;
+    }
+    e = a.dk == 64 ? launch_small_d<64, CH>(a, G, (int)cps, part_state, part_decay)
+                   : launch_small_d<32, CH>(a, G, (int)cps, part_state, part_decay);
+    if (part_state) {
+        hipError_t f = hipFreeAsync(part_state, a.stream);
+        if (e == hipSuccess) e = f;
+    }
+    return e;
 }
 
 }  // namespace la

@@ -18,6 +18,11 @@ constexpr int64_t kMaxElems = (int64_t)1 << 60;  // keeps every byte count below
 
 bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+// The forward also takes 128-token chunks on the small-head matrix-core kernels (bf16, dk = dv in
+// {32, 64}).
+bool fwd_chunk_ok(const la_shape* s, int c) {
+    return chunk_ok(c) || (c == 128 && s->in_dtype == LA_BF16 && s->dk == s->dv && (s->dk == 32 || s->dk == 64));
+}
 size_t esize(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
 
 // Overflow-safe product of non-negative sizes; -1 if it exceeds kMaxElems.
@@ -87,7 +92,7 @@ la_status validate_fwd(const void* q, const void* k, const void* v, const float*
     if (st != LA_OK) return st;
     if (chunk <= 0 || s->subseg_chunks < 0 || s->state_stride < 0) return LA_ERR_SHAPE;
     if (s->state_stride && s->state_stride < (int64_t)s->nseg * s->dk * s->dv) return LA_ERR_SHAPE;
-    if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
+    if (!fwd_chunk_ok(s, chunk)) return LA_ERR_UNSUPPORTED;
     if ((st = check_dtype(s)) != LA_OK) return st;
     if ((st = check_decay_mode(s)) != LA_OK) return st;
     if (s->decay_mode == LA_DECAY_NONE && decay) return LA_ERR_DECAY;
@@ -161,7 +166,7 @@ const char* la_status_str(la_status s) {
 }
 
 int32_t la_supported(const la_shape* s, int32_t chunk) {
-    if (check_common(s) != LA_OK || chunk <= 0 || !chunk_ok(chunk) || s->subseg_chunks < 0) return 0;
+    if (check_common(s) != LA_OK || chunk <= 0 || !fwd_chunk_ok(s, chunk) || s->subseg_chunks < 0) return 0;
     if (check_dtype(s) != LA_OK || check_decay_mode(s) != LA_OK) return 0;
     return 1;
 }
@@ -203,6 +208,9 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const floa
     } else if (a.bf16 && a.dk == a.dv && (a.dk == 32 || a.dk == 64 || a.dk == 128) && chunk == 64) {
         e = la::launch_chunk_fwd_mfma(a);
         fused = a.mode == LA_DECAY_GATE;  // the gate kernels emit q_dec, totals and tile flags themselves
+    } else if (chunk == 128) {  // bf16, dk = dv in {32, 64} (validated)
+        e = la::launch_chunk_fwd_small128(a);
+        fused = a.mode == LA_DECAY_GATE;
     } else {
         e = la::launch_chunk_fwd_generic(a);
     }

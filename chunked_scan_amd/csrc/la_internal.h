@@ -118,6 +118,8 @@ hipError_t launch_chunk_fwd_generic(const FwdArgs& a);
 // bf16 MFMA chunked forward for dk = dv in {32, 64, 128}, chunk = 64, with intra-GPU sub-segment
 // splitting (chunk_fwd_split.hip), all decay modes.
 hipError_t launch_chunk_fwd_mfma(const FwdArgs& a);
+// The same for 128-token chunks, dk = dv in {32, 64} (bf16): its own split into sub-segments.
+hipError_t launch_chunk_fwd_small128(const FwdArgs& a);
 // Its split of each segment into G sub-segments of cps chunks (uses B, H, L, nseg, subseg_chunks).
 void mfma_split(const FwdArgs& a, int* G_out, int* cps_out);
 // Its kernels: G sub-segments of cps chunks; part_state / part_decay the workspace of the

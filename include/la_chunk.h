@@ -123,7 +123,9 @@ typedef struct la_shape {
  *   s_out  : float, final local state of every segment, or NULL to skip it: segment p of (b,h)
  *            at s_out + (b*H + h) * state_stride + p * dk * dv (dense [B,H,nseg,dk,dv] when
  *            state_stride = 0); must not overlap any other argument.
- *   chunk  : chunk length in tokens: 16, 32 or 64 (64 is the production size).
+ *   chunk  : chunk length in tokens: 16, 32 or 64 (64 is the production size), or 128 for bf16
+ *            with dk = dv in {32, 64} (the chunk-length variant, on the matrix-core kernels; in
+ *            gate mode the -80 bound below then applies to each 128-token chunk).
  * A partial last chunk (L/nseg not a multiple of chunk) is allowed.  In gate mode the
  * per-chunk, per-key-dim log-decay sum must stay above -80 (strong enough decays would push the
  * chunk-relative key scaling outside float range).

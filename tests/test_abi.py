@@ -79,7 +79,11 @@ def test_fwd_validation(lib):
     assert fwd(lib, shape(dv=256)) == UNSUP
     assert fwd(lib, shape(), chunk=0) == SHAPE
     assert fwd(lib, shape(), chunk=48) == UNSUP
-    assert fwd(lib, shape(), chunk=128) == UNSUP
+    # 128-token chunks: bf16 with dk = dv in {32, 64} only
+    assert fwd(lib, shape(dk=128, dv=128), chunk=128) == UNSUP
+    assert fwd(lib, shape(dtype=B.LA_F32), chunk=128) == UNSUP
+    assert fwd(lib, shape(dk=64, dv=32), chunk=128) == UNSUP
+    assert fwd(lib, shape(dk=16, dv=16), chunk=128) == UNSUP
     assert fwd(lib, shape(subseg_chunks=-1)) == SHAPE
     bad = shape()
     bad.in_dtype = 7
@@ -111,7 +115,11 @@ def test_supported(lib):
     assert lib.la_supported(ctypes.byref(shape(dk=128, dv=128)), 64) == 1
     assert lib.la_supported(ctypes.byref(shape(dtype=B.LA_F32, dk=16, dv=16)), 16) == 1
     assert lib.la_supported(ctypes.byref(shape(dk=256)), 64) == 0
-    assert lib.la_supported(ctypes.byref(shape()), 128) == 0
+    assert lib.la_supported(ctypes.byref(shape()), 128) == 1
+    assert lib.la_supported(ctypes.byref(shape(dk=32, dv=32)), 128) == 1
+    assert lib.la_supported(ctypes.byref(shape(dk=128, dv=128)), 128) == 0
+    assert lib.la_supported(ctypes.byref(shape(dtype=B.LA_F32)), 128) == 0
+    assert lib.la_supported(ctypes.byref(shape()), 256) == 0
     assert lib.la_supported(None, 64) == 0
 
 
@@ -176,6 +184,7 @@ def test_bwd_validation(lib):
     assert bwd(lib, shape(L=100, nseg=3)) == SHAPE
     assert bwd(lib, shape(), chunk=0) == SHAPE
     assert bwd(lib, shape(), chunk=48) == UNSUP
+    assert bwd(lib, shape(), chunk=128) == UNSUP  # 128-token chunks: forward only
     assert bwd(lib, shape(dk=96)) == UNSUP
     assert bwd(lib, shape(state_stride=64 * 64 - 1)) == SHAPE       # smaller than one segment's state
     assert bwd(lib, shape(subseg_chunks=-1)) == SHAPE

@@ -499,3 +499,61 @@ def test_edge_cases():
                                          host32(inp["s_in"]).astype(np.float64))
         assert rel_err(o, o_ref) <= TOL["bf16"], lam
         assert rel_err(s, s_ref) <= TOL["bf16"], lam
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("L,nseg,subseg", [(128 * 9 + 17, 1, 0), (128 * 6, 1, 1), (128 * 7 + 40, 1, 3), (300, 1, 0),
+                                           (2 * (128 * 4 + 70), 2, 2)])
+def test_chunk128_small_heads(mode, d, L, nseg, subseg):
+    """128-token chunks (bf16, d = 32 / 64, the matrix-core kernels' chunk-length variant): o and the
+    segment states against the oracle; ragged tails, one chunk per sub-segment, several segments."""
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    w = W2.scaled(B=2, H=3, L=L, dk=d, dv=d, decay=decay, s_in_std=0.05, qkv_std=d ** -0.5, seed=900 + L + d)
+    note(f"bf16 d{d} chunk128 mode={mode} L={L} nseg={nseg} subseg_chunks={subseg}")
+    inp = make_inputs(w, "cpu")
+    o_ref, s_ref = oracle_run(inp, w, nseg=nseg)
+    o, s = _fwd(to_dev(inp), w, nseg=nseg, chunk=128, subseg=subseg)
+    torch.cuda.synchronize()
+    assert rel_err(o, o_ref) <= TOL["bf16"]
+    assert rel_err(s, s_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["head", "gate"])
+@pytest.mark.parametrize("d", [32, 64])
+def test_chunk128_decayed_and_device_step(mode, d):
+    """128-token chunks through la_chunk_fwd_decayed (q_decayed, segment totals, 64-token tile flags:
+    a tile flagged zero holds only zero rows) and through the device step, against the oracle."""
+    decay = {"head": "head_pow2", "gate": "gate"}[mode]
+    L, nseg = 3 * (128 * 5 + 33), 3
+    w = W2.scaled(B=2, H=3, L=L, dk=d, dv=d, decay=decay, s_in_std=0.05, qkv_std=d ** -0.5, seed=950 + d)
+    note(f"la_chunk_fwd_decayed / device step, bf16 d{d} chunk128 mode={mode}")
+    inp = make_inputs(w, "cpu")
+    dv_ = to_dev(inp)
+    o, s, qd, tot, live = lb.la_chunk_fwd_decayed(dv_["q"], dv_["k"], dv_["v"], dv_["decay"], dv_["s_in"], mode=w.mode,
+                                                  nseg=nseg, chunk=128, gate_norm=w.gate_norm, want_tile_live=True)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_run(inp, w, nseg=nseg)
+    assert rel_err(o, o_ref) <= TOL["bf16"] and rel_err(s, s_ref) <= TOL["bf16"]
+    Ls = L // nseg
+    assert live.shape[-1] == (Ls + 63) // 64
+    qz = torch.nn.functional.pad(qd.reshape(w.B, w.H, nseg, Ls, d), (0, 0, 0, live.shape[-1] * 64 - Ls))
+    assert not torch.any(qz.reshape(w.B, w.H, nseg, -1, 64 * d).ne(0).any(-1) & (live == 0))
+    cref, tref = oracle.cumdecay(w.B, w.H, w.L, d, ORC_MODE[w.mode], host32(inp["decay"]), nseg=nseg,
+                                 gate_norm=w.gate_norm)
+    ref = host32(inp["q"]).astype(np.float64) * cref
+    assert np.all(np.abs(qd.cpu().double().numpy() - ref) <= (2.0 ** -8 + 2e-4) * np.abs(ref) + 1e-35)
+    assert np.max(np.abs(tot.cpu().double().numpy() - tref) / np.maximum(np.abs(tref), 1e-30)) < 2e-4
+    # device step: S_recv drawn, the whole sequence as one device's share
+    w1 = w.scaled(L=128 * 12 + 64)
+    inp1 = make_inputs(w1, "cpu")
+    s_recv = torch.randn((w1.B, w1.H, d, d), generator=torch.Generator().manual_seed(5)) * 0.05
+    d1 = to_dev(inp1)
+    step = pipeline.DeviceStep(d1["q"], d1["k"], d1["v"], d1["decay"], s_recv.cuda(), mode=w1.mode, chunk=128,
+                               gate_norm=w1.gate_norm)
+    o1, s_out = step.run()
+    torch.cuda.synchronize()
+    inp1 = dict(inp1, s_in=s_recv)
+    o1_ref, s1_ref = oracle_run(inp1, w1)
+    assert rel_err(o1, o1_ref) <= TOL["bf16"]
+    assert rel_err(s_out, s1_ref[:, :, 0]) <= TOL["bf16"]
