@@ -93,10 +93,11 @@ class BackwardStep:
     ``want_decay`` also the decay derivative (learned decays), else the decays are held fixed.
     Outputs are allocated once."""
 
-    def __init__(self, w, want_decay=False):
+    def __init__(self, w, want_decay=False, forward_states=False):
         import torch
 
         from chunked_scan_amd.inputs import make_grads, make_inputs
+        from chunked_scan_amd.pipeline import DeviceStep
 
         self.w = w
         self.inp = make_inputs(w, "cuda")
@@ -105,6 +106,15 @@ class BackwardStep:
         self.dk = torch.empty_like(self.inp["k"])
         self.dv = torch.empty_like(self.inp["v"])
         self.want_decay = want_decay and w.mode != "none"
+        self.s_sub, self.sub_len = None, 0
+        if forward_states:  # training order: the device step's scan buffer (s_in as S_recv) is reused
+            i = self.inp
+            step = DeviceStep(i["q"], i["k"], i["v"], i["decay"], i["s_in"], mode=w.mode, chunk=w.chunk,
+                              gate_norm=w.gate_norm)
+            step.run()
+            torch.cuda.synchronize()
+            self.s_sub, self.sub_len = step.states[:, :, :step.G], w.L // step.G
+            self._keep = step
 
     def run(self, timers=None):
         from chunked_scan_amd import binding
@@ -112,7 +122,7 @@ class BackwardStep:
         i, g = self.inp, self.gr
         binding.la_chunk_bwd(i["q"], i["k"], i["v"], g["d_o"], i["decay"], i["s_in"], g["ds_out"], mode=self.w.mode,
                              chunk=self.w.chunk, want_decay=self.want_decay, dq=self.dq, dk=self.dk, dv=self.dv,
-                             timer=(timers or {}).get("fwd"))
+                             s_sub=self.s_sub, sub_len=self.sub_len, timer=(timers or {}).get("fwd"))
 
 
 def backward_legs(stream):
@@ -125,12 +135,14 @@ def backward_legs(stream):
     from chunked_scan_amd.inputs import WORKLOADS
 
     backward = {}
-    for wid, want_decay in ((1, False), (2, False), (2, True), (3, False), (3, True)):
+    legs = ((1, False, False), (2, False, False), (2, True, False), (3, False, False), (3, True, False),
+            (1, False, True), (2, True, True), (3, True, True))
+    for wid, want_decay, fstates in legs:
         wb = WORKLOADS[wid]
         dname = "dg" if wb.mode == "gate" else "d_lambda"
-        key = wb.name + (f" + {dname}" if want_decay else "")
+        key = wb.name + (f" + {dname}" if want_decay else "") + (", forward's sub-segment states" if fstates else "")
         log(f"[bench] backward: workload {wid} {key}")
-        sb = BackwardStep(wb, want_decay)
+        sb = BackwardStep(wb, want_decay, fstates)
         for _ in range(60):  # >= 20 ms of work: settled clocks
             sb.run()
         torch.cuda.synchronize()
@@ -159,7 +171,9 @@ def backward_legs(stream):
             comp += th * gate
         gbs = comp / (st["median_us"] * 1e-6) / 1e9
         backward[key] = dict(
-            what="la_chunk_bwd: dq, dk, dv, ds_in" + (f", {dname}" if want_decay else " (decay held fixed)"),
+            what=("la_chunk_bwd_states" if fstates else "la_chunk_bwd") + ": dq, dk, dv, ds_in"
+            + (f", {dname}" if want_decay else " (decay held fixed)")
+            + (" (the states entering the sub-segments from the device step's scan)" if fstates else ""),
             B=wb.B, H=wb.H, L=wb.L, decay=wb.decay,
             tokens_per_s=round(wb.B * wb.L / (st["median_us"] * 1e-6), 1), per_step_us=st,
             compulsory_bytes=comp, gbps_on_compulsory_bytes=round(gbs, 1),

@@ -24,7 +24,7 @@ LA_F32, LA_BF16 = 0, 1
 MODES = {"none": 0, "head": 1, "gate": 2}
 STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_SHAPE", -3: "LA_ERR_DTYPE", -4: "LA_ERR_ALIAS",
           -5: "LA_ERR_UNSUPPORTED", -6: "LA_ERR_LAUNCH", -7: "LA_ERR_DECAY"}
-EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_decayed", "la_chunk_bwd", "la_state_scan", "la_state_correct", "la_state_correct_live",
+EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_decayed", "la_chunk_bwd", "la_chunk_bwd_states", "la_state_scan", "la_state_correct", "la_state_correct_live",
            "la_cumdecay", "la_status_str", "la_supported", "la_version")
 
 
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.la_chunk_fwd.argtypes = [P, P, P, P, P, P, P, S, ctypes.c_int32]
         L.la_chunk_fwd_decayed.argtypes = [P, P, P, P, P, P, P, P, P, P, S, ctypes.c_int32]
         L.la_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, S, ctypes.c_int32]
+        L.la_chunk_bwd_states.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P, P, P, P, P, S,
+                                          ctypes.c_int32]
         L.la_state_correct_live.argtypes = [P, P, P, P, P, S]
         L.la_state_scan.argtypes = [P, P, ctypes.c_int32, P, S]
         L.la_state_correct.argtypes = [P, P, P, P, S]
@@ -210,12 +212,16 @@ def la_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.T
                  ds_out: Optional[torch.Tensor] = None, *, mode: Optional[str] = None, nseg: int = 1,
                  chunk: int = 64, gate_norm: float = 16.0, want_decay: bool = True, want_ds_in: bool = True,
                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                 dv: Optional[torch.Tensor] = None, subseg_chunks: int = 0, stream=None, timer=None):
+                 dv: Optional[torch.Tensor] = None, subseg_chunks: int = 0, s_sub: Optional[torch.Tensor] = None,
+                 sub_len: int = 0, stream=None, timer=None):
     """Backward of la_chunk_fwd.  d_o [B,H,L,dv] (q's dtype) and ds_out [B,H,nseg,dk,dv] f32 or None are
     the loss's derivatives with respect to o and to each segment's final state.  Returns
     (dq, dk, dv, d_decay, ds_in): dq, dk [B,H,L,dk] and dv [B,H,L,dv] in q's dtype; d_decay f32 [H]
     (head decay: with respect to lambda_h) or [B,H,L,dk] (gate: with respect to g) or None; ds_in
-    f32 [B,H,nseg,dk,dv] with respect to each segment's initial state, or None."""
+    f32 [B,H,nseg,dk,dv] with respect to each segment's initial state, or None.
+    With ``s_sub`` (f32 [B,H,nseg*nsub,dk,dv] or a view whose last three dims are dense, e.g. the
+    device step's scan buffer without its last entry) the states entering every sub-segment of
+    ``sub_len`` tokens are taken from it (la_chunk_bwd_states) instead of being recomputed."""
     B, H, L, dkk = q.shape
     dvv = v.shape[-1]
     _dev(q, "q")
@@ -241,9 +247,23 @@ def la_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.T
     ds_in = torch.empty((B, H, nseg, dkk, dvv), dtype=torch.float32, device=q.device) if want_ds_in else None
     shp = make_shape(B, H, L, dkk, dvv, nseg=nseg, dtype=_dtype_code(q), mode=m, gate_norm=gate_norm,
                      subseg_chunks=subseg_chunks, stream=_stream(stream), timer=timer)
-    _check("la_chunk_bwd", lib().la_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(d_o),
-                                              _ptr(ds_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_decay),
-                                              _ptr(ds_in), ctypes.byref(shp), chunk))
+    if s_sub is None:
+        _check("la_chunk_bwd", lib().la_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(d_o),
+                                                  _ptr(ds_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_decay),
+                                                  _ptr(ds_in), ctypes.byref(shp), chunk))
+    else:
+        nsub = -(-(L // nseg) // sub_len) if sub_len > 0 else 0
+        if (s_sub.dtype != torch.float32 or s_sub.device != q.device or s_sub.dim() != 5
+                or s_sub.shape[:2] != (B, H) or s_sub.shape[2] < nseg * nsub or s_sub.shape[3:] != (dkk, dvv)
+                or s_sub.stride()[2:] != (dkk * dvv, dvv, 1)):
+            raise ValueError("s_sub: float32 [B, H, >= nseg * nsub, dk, dv] with dense states on q's device")
+        bh_stride = s_sub.stride(1) if H > 1 else (s_sub.stride(0) if B > 1 else 0)
+        if B > 1 and H > 1 and s_sub.stride(0) != H * bh_stride:
+            raise ValueError("s_sub: the (b, h) blocks must be evenly spaced")
+        _check("la_chunk_bwd_states", lib().la_chunk_bwd_states(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(s_sub), sub_len, bh_stride,
+            _ptr(d_o), _ptr(ds_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_decay), _ptr(ds_in), ctypes.byref(shp),
+            chunk))
     return dq, dk, dv, d_decay, ds_in
 
 

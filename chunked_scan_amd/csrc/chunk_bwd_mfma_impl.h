@@ -524,7 +524,9 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ s_in,
     const float* __restrict__ ds_out, int64_t sstride, __bf16* __restrict__ dq,
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
-    const float* __restrict__ init_state,                            // output pass: scanned states
+    // output pass: the state entering sub-segment g >= 1 of (bh, seg) at
+    // init_state + bh * ist_bh + (seg * ist_g + g + ist_off) * D * D (the scan buffer, or states the caller gives)
+    const float* __restrict__ init_state, int64_t ist_bh, int ist_g, int ist_off,
     const __bf16* __restrict__ d_start,  // gate derivative: D at every chunk's start (bf16 [D][D]), or null
     float* __restrict__ c0_out,          // gate derivative: rowsum(S (.) D) at every chunk's start ([D])
     int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm) {
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
         if (g == 0) {
             if (seg == 0 && s_in) src = s_in + bh * (int64_t)D * D;
         } else if (!STATE_ONLY) {
-            src = init_state + (ub * (G - 1) + (g - 1)) * (int64_t)D * D;
+            src = init_state + bh * ist_bh + ((int64_t)seg * ist_g + g + ist_off) * D * D;
         }
 #pragma unroll
         for (int m = 0; m < NCB; m++)
@@ -1108,21 +1110,30 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
     const __bf16* v = (const __bf16*)a.v;
     const __bf16* d_o = (const __bf16*)a.d_o;
     // dq: forward state pass, scan, output pass (with the gate derivative also rowsum(S (.) D) per chunk)
+    // (the states entering the sub-segments given by the caller: no state pass, no scan)
     auto dq_passes = [&]() -> hipError_t {
         hipError_t e;
-        if (G > 1) {
+        const float* init = f_state;
+        int64_t ist_bh = (int64_t)a.nseg * (G - 1) * D * D;
+        int ist_g = G - 1, ist_off = -1;
+        if (a.s_sub) {
+            init = a.s_sub;
+            ist_bh = a.sub_stride;
+            ist_g = G;
+            ist_off = 0;
+        } else if (G > 1) {
             LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
                       bwd_dq_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                          k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr,
-                          nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+                          k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr, 0,
+                          0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm));
             if ((e = hipGetLastError()) != hipSuccess) return e;
             if ((e = launch_state_scan(f_state, f_decay, f_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
                 return e;
         }
         LA_TRACED(a.tr, "chunk_bwd_dq",
                   bwd_dq_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                      k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, f_state,
-                      d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+                      k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, init,
+                      ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm));
         return hipGetLastError();
     };
     // dk, dv: backward state pass, reverse-order scan, output pass (with the gate derivative also D at
@@ -1168,7 +1179,9 @@ hipError_t launch_d(const BwdArgs& a) {
     FwdArgs sp;
     sp.B = a.B; sp.H = a.H; sp.L = a.L; sp.nseg = a.nseg; sp.subseg_chunks = a.subseg_chunks;
     int G, cps;
-    if (D == 32 && a.subseg_chunks == 0) {
+    if (a.s_sub) {
+        sp.subseg_chunks = a.sub_len / C;  // the caller's sub-segments (validated: a multiple of 64)
+    } else if (D == 32 && a.subseg_chunks == 0) {
         // d = 32: sub-segments for about 512 workgroups rather than the forward's 256 (several share
         // a compute unit; B1 H16 L16k: 120 -> 96 us without decay, 217 -> 205 us with d lambda_h);
         // d = 64 and 128 gain nothing from more

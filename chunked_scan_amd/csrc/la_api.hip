@@ -339,11 +339,12 @@ la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const l
 
 }  // extern "C"
 
-extern "C" {
+namespace {
 
-la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
-                       const void* d_o, const float* ds_out, void* dq, void* dk, void* dv, float* d_decay,
-                       float* ds_in, const la_shape* s, int32_t chunk) {
+la_status chunk_bwd_impl(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
+                         const float* s_sub, int32_t sub_len, int64_t sub_stride, const void* d_o,
+                         const float* ds_out, void* dq, void* dk, void* dv, float* d_decay, float* ds_in,
+                         const la_shape* s, int32_t chunk) {
     la_status st = check_common(s);
     if (st != LA_OK) return st;
     if (chunk <= 0 || s->state_stride < 0 || s->subseg_chunks < 0) return LA_ERR_SHAPE;
@@ -362,11 +363,21 @@ la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float*
     const size_t es = esize(s->in_dtype);
     const int64_t sstride = s->state_stride ? s->state_stride : (int64_t)s->nseg * per_seg;
     const size_t st_bytes = BH > 0 ? sizeof(float) * (size_t)((BH - 1) * sstride + s->nseg * per_seg) : 0;
+    // states entering the sub-segments: sub_len a positive multiple of the chunk (64 on the
+    // matrix-core path that uses them), (b,h) blocks of sub_stride floats (0 = dense)
+    const int64_t Lseg = s->nseg > 0 ? s->L / s->nseg : 0;
+    const int64_t nsub = s_sub && sub_len > 0 ? (Lseg + sub_len - 1) / sub_len : 0;
+    if (s_sub && (sub_len <= 0 || sub_len % chunk != 0 || sub_stride < 0)) return LA_ERR_SHAPE;
+    if (s_sub && sub_stride && sub_stride < (int64_t)s->nseg * nsub * per_seg) return LA_ERR_SHAPE;
+    const int64_t substride = s_sub ? (sub_stride ? sub_stride : (int64_t)s->nseg * nsub * per_seg) : 0;
+    const size_t sub_bytes =
+        s_sub && BH > 0 ? sizeof(float) * (size_t)((BH - 1) * substride + s->nseg * nsub * per_seg) : 0;
     const Span ins[] = {{q, es * nqk},
                         {k, es * nqk},
                         {v, es * nv},
                         {decay, decay ? decay_bytes(s) : 0},
                         {s_in, s_in ? sizeof(float) * (size_t)(BH * per_seg) : 0},
+                        {s_sub, sub_bytes},
                         {d_o, es * nv},
                         {ds_out, ds_out ? st_bytes : 0}};
     const Span outs[] = {{dq, es * nqk},
@@ -394,9 +405,34 @@ la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float*
     a.mode = s->decay_mode;
     a.inv_norm = s->decay_mode == LA_DECAY_GATE ? 1.f / s->gate_norm : 1.f;
     a.subseg_chunks = s->subseg_chunks;
+    // the given sub-segment states serve the matrix-core path with 64-token chunks; elsewhere the
+    // backward does not split segments and they are not needed
+    const bool use_sub = s_sub && chunk == 64 && sub_len % 64 == 0 && nsub > 1;
+    a.s_sub = use_sub ? s_sub : nullptr;
+    a.sub_stride = substride;
+    a.sub_len = sub_len;
     a.stream = (hipStream_t)s->stream;
     a.tr = &tr;
     return from_hip(la::chunk_bwd_mfma_supported(a) ? la::launch_chunk_bwd_mfma(a) : la::launch_chunk_bwd_generic(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
+                       const void* d_o, const float* ds_out, void* dq, void* dk, void* dv, float* d_decay,
+                       float* ds_in, const la_shape* s, int32_t chunk) {
+    return chunk_bwd_impl(q, k, v, decay, s_in, nullptr, 0, 0, d_o, ds_out, dq, dk, dv, d_decay, ds_in, s, chunk);
+}
+
+la_status la_chunk_bwd_states(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
+                              const float* s_sub, int32_t sub_len, int64_t sub_stride, const void* d_o,
+                              const float* ds_out, void* dq, void* dk, void* dv, float* d_decay, float* ds_in,
+                              const la_shape* s, int32_t chunk) {
+    if (!s_sub) return LA_ERR_NULL;
+    return chunk_bwd_impl(q, k, v, decay, s_in, s_sub, sub_len, sub_stride, d_o, ds_out, dq, dk, dv, d_decay, ds_in,
+                          s, chunk);
 }
 
 }  // extern "C"

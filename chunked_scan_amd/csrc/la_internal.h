@@ -97,6 +97,13 @@ struct BwdArgs {
     int mode;
     float inv_norm;
     int subseg_chunks;     // matrix-core path: chunks per sub-segment, 0 = automatic
+    // optional: the state entering every sub-segment of sub_len tokens of every segment, (b,h)
+    // blocks of sub_stride floats, segment p's sub-segment j at (p * ceil(Lseg / sub_len) + j) * dk * dv
+    // (j = 0 unused: the segment's initial state is s_in or zero); the matrix-core path then splits
+    // at those sub-segments and needs no forward state pass
+    const float* s_sub;
+    int64_t sub_stride;
+    int sub_len;
     hipStream_t stream;
     Tracer* tr;
 };

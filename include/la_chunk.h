@@ -208,6 +208,34 @@ la_status la_chunk_bwd(const void* q, const void* k, const void* v, const float*
                        void* dv, float* d_decay, float* ds_in, const la_shape* shape, int32_t chunk);
 
 /*
+ * la_chunk_bwd, reusing states the forward already has: the state entering every sub-segment of
+ * sub_len tokens of every segment (the ZeCO review page notes that the backward reuses the global
+ * states of the forward instead of exchanging or recomputing them,
+ * pith_extraction.forward_implications; within one device the same holds for the states that the
+ * device step's scan leaves at its sub-segment boundaries).  On the matrix-core path the backward
+ * then splits every segment at those sub-segments and runs no forward state pass and no scan for
+ * dq; the results are those of la_chunk_bwd up to rounding order.
+ *
+ *   s_sub      : float, read only: for (b,h) block b*H + h at s_sub + (b*H + h) * sub_stride,
+ *                segment p's sub-segment j (tokens p*Lseg + j*sub_len ..) at
+ *                (p * ceil(Lseg / sub_len) + j) * dk * dv, a [dk][dv] state.  Entry j = 0 of every
+ *                segment is not read (segment 0 starts from s_in, the others from zero).  Must not
+ *                overlap an output.  Not NULL.
+ *   sub_len    : tokens per sub-segment, a positive multiple of chunk (64 on the matrix-core path;
+ *                with other shapes the states are validated but not needed).
+ *   sub_stride : floats between consecutive (b,h) blocks of s_sub, 0 = dense
+ *                (nseg * ceil(Lseg / sub_len) * dk * dv); lets the device step's scan buffer, which
+ *                holds one more state per (b,h), be passed as is.
+ * Every other argument, the results and the return codes are those of la_chunk_bwd; a bad sub_len
+ * or sub_stride returns LA_ERR_SHAPE.
+ */
+la_status la_chunk_bwd_states(const void* q, const void* k, const void* v, const float* decay,
+                              const float* s_in, const float* s_sub, int32_t sub_len,
+                              int64_t sub_stride, const void* d_o, const float* ds_out, void* dq,
+                              void* dk, void* dv, float* d_decay, float* ds_in,
+                              const la_shape* shape, int32_t chunk);
+
+/*
  * Segmented state scan: the All-Scan of ZeCO reproduced on one GPU (page "ZeCO ...",
  * pith_extraction.key_machinery: each device applies the update
  * S_p = (segment decay) * S_{p-1} + S_local,p to the state it receives and passes the result on;

@@ -177,6 +177,25 @@ def bwd(lib, shp, q=Q, k=K, v=V, dec=None, s_in=None, d_o=DO, ds_out=None, dq=DQ
                             P(ds_in), ctypes.byref(shp), chunk)
 
 
+def bwd_states(lib, shp, s_sub, sub_len, sub_stride=0, dq=DQ, chunk=64):
+    P = ctypes.c_void_p
+    return lib.la_chunk_bwd_states(P(Q), P(K), P(V), P(None), P(None), P(s_sub), sub_len, sub_stride, P(DO), P(None),
+                                   P(dq), P(DK), P(DV), P(None), P(None), ctypes.byref(shp), chunk)
+
+
+def test_bwd_states_validation(lib):
+    SSUB = 0x10000000000 * 20
+    shp = shape(L=512)  # B1 H2 d64 bf16: 2 sub-segments of 256 tokens per (b, h)
+    assert bwd_states(lib, shp, None, 256) == NULL
+    assert bwd_states(lib, shp, SSUB, 0) == SHAPE
+    assert bwd_states(lib, shp, SSUB, -64) == SHAPE
+    assert bwd_states(lib, shp, SSUB, 100) == SHAPE                    # not a multiple of the chunk
+    assert bwd_states(lib, shp, SSUB, 256, sub_stride=-1) == SHAPE
+    assert bwd_states(lib, shp, SSUB, 256, sub_stride=2 * 64 * 64 - 1) == SHAPE  # below one (b,h) block
+    assert bwd_states(lib, shp, SSUB, 256, dq=SSUB + 64) == ALIAS       # dq overlaps the states
+    assert bwd_states(lib, shape(L=512, dk=96), SSUB, 256) == UNSUP
+
+
 def test_bwd_validation(lib):
     assert lib.la_chunk_bwd(*([None] * 12), None, 64) == NULL
     assert bwd(lib, shape(L=-1)) == SHAPE

@@ -12,6 +12,7 @@ import torch
 
 import oracle
 from chunked_scan_amd import binding as lb
+from chunked_scan_amd import pipeline
 from chunked_scan_amd.inputs import WORKLOADS, make_grads, make_inputs
 
 from gpu_util import ORC_MODE, TOL, host32, note, rel_err, to_dev
@@ -215,4 +216,61 @@ def test_bwd_matrix_core_subsegment_length(mode, subseg_chunks):
     got = lb.la_chunk_bwd(d["q"], d["k"], d["v"], g["d_o"], d["decay"], d["s_in"], g["ds_out"], mode=w.mode,
                           chunk=64, gate_norm=w.gate_norm, subseg_chunks=subseg_chunks)
     torch.cuda.synchronize()
+    _compare(got, _oracle(w, inp, gr, 1), "bf16", mode)
+
+
+def _sub_states(w, inp, nseg, sub_len):
+    """The exact state entering every sub-segment of sub_len tokens of every segment (oracle, fp64,
+    stored fp32): [B, H, nseg * nsub, dk, dv]."""
+    Ls = w.L // nseg
+    nsub = -(-Ls // sub_len)
+    q, k, v = host32(inp["q"]), host32(inp["k"]), host32(inp["v"])
+    dec = host32(inp["decay"])
+    out = np.zeros((w.B, w.H, nseg * nsub, w.dk, w.dv), np.float32)
+    for p in range(nseg):
+        s_in = host32(inp["s_in"]).astype(np.float64) if (p == 0 and inp["s_in"] is not None) else None
+        for j in range(1, nsub):
+            sl = slice(p * Ls, p * Ls + j * sub_len)
+            dj = None if dec is None else (dec[:, :, sl] if w.mode == "gate" else dec)
+            _, so = oracle.recurrence(q[:, :, sl], k[:, :, sl], v[:, :, sl], ORC_MODE[w.mode], dj, s_in,
+                                      gate_norm=w.gate_norm)
+            out[:, :, p * nsub + j] = so[:, :, 0]
+    return torch.from_numpy(out)
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+@pytest.mark.parametrize("d,L,nseg,sub_len", [(128, 1000, 1, 256), (64, 2 * 700, 2, 192), (32, 1300, 1, 320)])
+def test_bwd_with_forward_states(mode, d, L, nseg, sub_len):
+    """la_chunk_bwd_states: the states entering the sub-segments are given (here the oracle's exact
+    ones), so the matrix-core backward splits at them and runs no forward state pass; every
+    derivative, the decay's included, against the oracle; ragged last sub-segments."""
+    note(f"la_chunk_bwd_states bf16 d={d} mode={mode} L={L} nseg={nseg} sub_len={sub_len}")
+    w, inp, gr = _case(mode, "bf16", d, d, L, 64, nseg, seed=1000 + L + d, B=2, H=2)
+    s_sub = _sub_states(w, inp, nseg, sub_len).cuda()
+    dd = to_dev(inp)
+    g = to_dev(gr)
+    got = lb.la_chunk_bwd(dd["q"], dd["k"], dd["v"], g["d_o"], dd["decay"], dd["s_in"], g["ds_out"], mode=w.mode,
+                          nseg=nseg, chunk=64, gate_norm=w.gate_norm, s_sub=s_sub, sub_len=sub_len)
+    torch.cuda.synchronize()
+    _compare(got, _oracle(w, inp, gr, nseg), "bf16", mode)
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+def test_bwd_after_device_step(mode):
+    """Training order on one device: the device step (local forward, scan with S_recv, correction),
+    then the backward with the step's own scan buffer as the sub-segment states and S_recv as s_in,
+    against the oracle's derivatives of the recurrence started from S_recv."""
+    note(f"device step then la_chunk_bwd_states, bf16 d=128 mode={mode}")
+    w, inp, gr = _case(mode, "bf16", 128, 128, 2048, 64, 1, seed=1100, B=1, H=3)
+    dd = to_dev(inp)
+    g = to_dev(gr)
+    step = pipeline.DeviceStep(dd["q"], dd["k"], dd["v"], dd["decay"], dd["s_in"], mode=w.mode, chunk=64,
+                               gate_norm=w.gate_norm, subseg=4)
+    step.run()
+    timer = lb.KernelTimer()
+    got = lb.la_chunk_bwd(dd["q"], dd["k"], dd["v"], g["d_o"], dd["decay"], dd["s_in"], g["ds_out"], mode=w.mode,
+                          chunk=64, gate_norm=w.gate_norm, s_sub=step.states[:, :, 0:4], sub_len=512, timer=timer)
+    torch.cuda.synchronize()
+    names = [n for n, _ in timer.harvest()]
+    assert "chunk_bwd_dq" in names and "chunk_bwd_dq_state_pass" not in names, names
     _compare(got, _oracle(w, inp, gr, 1), "bf16", mode)
