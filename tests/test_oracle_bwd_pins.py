@@ -10,9 +10,12 @@
   jointly linear in (k, s_in) and in (v, s_in), so <dq, q> = <W, o> and <dk, k> + <ds_in, s_in> =
   <dv, v> + <ds_in, s_in> = L.
 * Segments are independent sequences: cutting one run in two must give the two runs' results.
+* A hand-derived worked example (tests/golden/worked_example_backward_gate_half.txt), exact in binary.
 A dropped term (the diagonal, the s_in path, the ds_out path), a decay applied on the wrong side
 of the add, a transposed gradient or a wrong chain-rule factor fails at least one of these.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -165,3 +168,22 @@ def test_bwd_segments_are_independent_runs(mode):
                                        s_in if p == 0 else None, Ws[:, :, p:p + 1])[3]
                  for p, sl in enumerate((slice(0, 8), slice(8, 16)))]
         assert np.array_equal(both[3], parts[0] + parts[1])
+
+
+def test_golden_hand_backward_example():
+    """Every derivative of the hand-worked two-token, 2 x 2 example, exactly."""
+    rows = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example_backward_gate_half.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            key, *vals = line.split()
+            rows[key] = np.array([float(x) for x in vals])
+    tok = lambda x: rows[x].reshape(1, 1, 2, 2).astype(np.float32)  # noqa: E731
+    dq, dk, dv, dg, ds_in = oracle.recurrence_bwd(tok("q"), tok("k"), tok("v"), tok("d_o"), GATE,
+                                                  np.zeros((1, 1, 2, 2), np.float32),
+                                                  rows["s_in"].reshape(1, 1, 2, 2),
+                                                  rows["ds_out"].reshape(1, 1, 1, 2, 2), gate_norm=1.0)
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv), ("dg", dg)):
+        assert np.array_equal(got.reshape(-1), rows[name]), name
+    assert np.array_equal(ds_in.reshape(-1), rows["ds_in"])
