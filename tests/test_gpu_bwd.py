@@ -274,3 +274,18 @@ def test_bwd_after_device_step(mode):
     names = [n for n, _ in timer.harvest()]
     assert "chunk_bwd_dq" in names and "chunk_bwd_dq_state_pass" not in names, names
     _compare(got, _oracle(w, inp, gr, 1), "bf16", mode)
+
+
+@pytest.mark.parametrize("dtype,d,L,sub_len", [("f32", 32, 300, 128), ("bf16", 128, 500, 512), ("bf16", 64, 256, 1024)])
+def test_bwd_with_forward_states_unused(dtype, d, L, sub_len):
+    """la_chunk_bwd_states where the states are not needed: the fp32 path (no sub-segment split), and
+    one sub-segment covering the whole segment; the results are la_chunk_bwd's, against the oracle."""
+    note(f"la_chunk_bwd_states, states unused: {dtype} d={d} L={L} sub_len={sub_len}")
+    w, inp, gr = _case("gate", dtype, d, d, L, 64, 1, seed=1200 + L, B=1, H=2)
+    s_sub = _sub_states(w, inp, 1, sub_len).cuda()
+    dd = to_dev(inp)
+    g = to_dev(gr)
+    got = lb.la_chunk_bwd(dd["q"], dd["k"], dd["v"], g["d_o"], dd["decay"], dd["s_in"], g["ds_out"], mode=w.mode,
+                          chunk=64, gate_norm=w.gate_norm, s_sub=s_sub, sub_len=sub_len)
+    torch.cuda.synchronize()
+    _compare(got, _oracle(w, inp, gr, 1), dtype, "gate")
