@@ -45,9 +45,9 @@ hipMemPool_t workspace_pool(int dev) {
     return pools[dev];
 }
 
-// Sub-segments: about 256 workgroups in total (one round on the compute units), at least 4
-// chunks each, unless the caller fixes the sub-segment length.
-void mfma_split(const FwdArgs& a, int* G_out, int* cps_out) {
+// Sub-segments: about `target` workgroups in total (256: one round on the compute units), at
+// least 4 chunks each, unless the caller fixes the sub-segment length.
+void mfma_split(const FwdArgs& a, int* G_out, int* cps_out, int64_t target) {
     const int64_t units = a.B * a.H * a.nseg;
     const int64_t Lseg = a.L / a.nseg;
     const int64_t nch = (Lseg + C - 1) / C;
@@ -55,7 +55,6 @@ void mfma_split(const FwdArgs& a, int* G_out, int* cps_out) {
     if (a.subseg_chunks > 0) {
         cps = a.subseg_chunks;
     } else {
-        const int64_t target = 256;
         const int64_t g_want = (target + units - 1) / units;
         cps = (nch + g_want - 1) / g_want;
         if (cps < 4) cps = 4;
@@ -68,7 +67,8 @@ void mfma_split(const FwdArgs& a, int* G_out, int* cps_out) {
 
 hipError_t launch_chunk_fwd_mfma(const FwdArgs& a) {
     int G, cps;
-    mfma_split(a, &G, &cps);
+    // small heads: 512 workgroups (latency-bound kernels, several share a compute unit)
+    mfma_split(a, &G, &cps, a.dk < 128 ? 512 : 256);
     float* part_state = nullptr;
     float* part_decay = nullptr;
     if (G > 1) {

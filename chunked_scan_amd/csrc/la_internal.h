@@ -128,7 +128,8 @@ hipError_t launch_chunk_fwd_mfma(const FwdArgs& a);
 // The same for 128-token chunks, dk = dv in {32, 64} (bf16): its own split into sub-segments.
 hipError_t launch_chunk_fwd_small128(const FwdArgs& a);
 // Its split of each segment into G sub-segments of cps chunks (uses B, H, L, nseg, subseg_chunks).
-void mfma_split(const FwdArgs& a, int* G_out, int* cps_out);
+// target: about how many workgroups to aim for when the length is chosen automatically.
+void mfma_split(const FwdArgs& a, int* G_out, int* cps_out, int64_t target = 256);
 // Its kernels: G sub-segments of cps chunks; part_state / part_decay the workspace of the
 // sub-segment scan (unused when G == 1).
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
