@@ -383,8 +383,8 @@ def cpu_baseline_backward(w, sample_len: int = 2048):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200,
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=400,
                     help="untimed steps first; the GPU's clocks take ~10 ms of sustained work to settle")
     ap.add_argument("--workload", type=int, default=1, help="index into chunked_scan_amd.inputs.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
