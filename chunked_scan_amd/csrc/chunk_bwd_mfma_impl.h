@@ -1004,6 +1004,27 @@ __global__ __launch_bounds__(256) void dlam_final_kernel(const double* __restric
     d_decay[h] = (float)s;
 }
 
+// d lambda_h, first part: the local S and dS/dlambda of every sub-segment but the last, and the
+// scan of S, which leaves the state entering every sub-segment after the first in ps (the same
+// values, in the same layout, as the dq passes' own scan, which it then replaces).
+template <int D>
+hipError_t launch_dlam_states(const BwdArgs& a, int G, int cps, float* ps, float* pst, float* pdec) {
+    const int64_t units = a.B * a.H * a.nseg;
+    hipError_t e;
+    if (G > 1) {
+        LA_TRACED(a.tr, "chunk_bwd_dlam_state_pass",
+                  bwd_dlam_kernel<D, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.d_o, a.decay,
+                      a.s_in, a.ds_out, a.state_stride, ps, pst, pdec, nullptr, nullptr, nullptr, a.H, a.L, a.nseg, G,
+                      cps));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_state_scan(ps, pdec, ps, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// d lambda_h, second part: dS/dlambda across sub-segments (fix-up and scan), the output pass and the
+// final sum.
 template <int D>
 hipError_t launch_dlam(const BwdArgs& a, int G, int cps, float* ps, float* pst, float* pdec, double* part,
                        const double* intra) {
@@ -1014,12 +1035,6 @@ hipError_t launch_dlam(const BwdArgs& a, int G, int cps, float* ps, float* pst, 
     const __bf16* d_o = (const __bf16*)a.d_o;
     hipError_t e;
     if (G > 1) {
-        LA_TRACED(a.tr, "chunk_bwd_dlam_state_pass",
-                  bwd_dlam_kernel<D, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                      q, k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, ps, pst, pdec, nullptr, nullptr,
-                      nullptr, a.H, a.L, a.nseg, G, cps));
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_state_scan(ps, pdec, ps, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess) return e;
         if (G > 2) {
             LA_TRACED(a.tr, "chunk_bwd_dlam_fixup",
                       dlam_fixup_kernel<D><<<dim3(D * D / 256, (unsigned)(G - 2), (unsigned)units), 256, 0, a.stream>>>(
@@ -1103,7 +1118,8 @@ __global__ __launch_bounds__(NT) void dg_kernel(const __bf16* __restrict__ q, co
 
 template <int D, int MODE>
 hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* f_decay, float* b_state,
-                       float* b_decay, double* intra_part, __bf16* d_start, float* c0) {
+                       float* b_decay, double* intra_part, __bf16* d_start, float* c0,
+                       const float* s_scanned = nullptr) {
     const int64_t units = a.B * a.H * a.nseg;
     const __bf16* q = (const __bf16*)a.q;
     const __bf16* k = (const __bf16*)a.k;
@@ -1121,6 +1137,8 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
             ist_bh = a.sub_stride;
             ist_g = G;
             ist_off = 0;
+        } else if (s_scanned) {  // the scanned states of the d lambda_h pipeline, same layout as f_state
+            init = s_scanned;
         } else if (G > 1) {
             LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
                       bwd_dq_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
@@ -1223,12 +1241,18 @@ hipError_t launch_d(const BwdArgs& a) {
     float* l_decay = n_decay ? fp + nsets * n_state + 2 * n_decay : nullptr;
     float* c0 = n_chunks ? fp + nsets * n_state + 3 * n_decay : nullptr;
     __bf16* d_start = n_chunks ? (__bf16*)(ws + ds_off) : nullptr;
-    if (a.mode == DECAY_HEAD)
+    if (dlam && !a.s_sub) {  // the S scan of the d lambda_h pipeline replaces the dq passes' own
+        e = launch_dlam_states<D>(a, G, cps, l_state, lt_state, l_decay);
+        if (e == hipSuccess)
+            e = launch_mode<D, DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra, nullptr, nullptr,
+                                           l_state);
+    } else if (a.mode == DECAY_HEAD)
         e = launch_mode<D, DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra, nullptr, nullptr);
     else if (a.mode == DECAY_GATE)
         e = launch_mode<D, DECAY_GATE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr, d_start, c0);
     else
         e = launch_mode<D, DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr, nullptr, nullptr);
+    if (e == hipSuccess && dlam && a.s_sub) e = launch_dlam_states<D>(a, G, cps, l_state, lt_state, l_decay);
     if (e == hipSuccess && dlam) e = launch_dlam<D>(a, G, cps, l_state, lt_state, l_decay, part, intra);
     if (ws) {
         hipError_t f = hipFreeAsync(ws, a.stream);
