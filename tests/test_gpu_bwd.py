@@ -289,3 +289,27 @@ def test_bwd_with_forward_states_unused(dtype, d, L, sub_len):
                           chunk=64, gate_norm=w.gate_norm, s_sub=s_sub, sub_len=sub_len)
     torch.cuda.synchronize()
     _compare(got, _oracle(w, inp, gr, 1), dtype, "gate")
+
+
+def test_bwd_pass_structure():
+    """Which passes run (la_trace names), several sub-segments: with d lambda_h the d lambda state
+    pass's scanned S serves the dq output pass (no dq state pass); held fixed, the dq passes build
+    their own; with dg the dk/dv passes run before the dq passes and dg comes last."""
+    note("la_chunk_bwd pass structure, bf16 d=64 L=2048")
+
+    def names(mode, want):
+        w, inp, gr = _case(mode, "bf16", 64, 64, 2048, 64, 1, seed=1300, B=1, H=2)
+        dd, g = to_dev(inp), to_dev(gr)
+        timer = lb.KernelTimer()
+        lb.la_chunk_bwd(dd["q"], dd["k"], dd["v"], g["d_o"], dd["decay"], dd["s_in"], g["ds_out"], mode=w.mode,
+                        chunk=64, gate_norm=w.gate_norm, want_decay=want, timer=timer)
+        torch.cuda.synchronize()
+        return [n for n, _ in timer.harvest()]
+
+    n = names("head", True)
+    assert "chunk_bwd_dlam_state_pass" in n and "chunk_bwd_dq_state_pass" not in n, n
+    assert n.index("chunk_bwd_dlam_state_pass") < n.index("chunk_bwd_dq"), n
+    n = names("head", False)
+    assert "chunk_bwd_dq_state_pass" in n and "chunk_bwd_dlam_state_pass" not in n, n
+    n = names("gate", True)
+    assert n.index("chunk_bwd_dkdv") < n.index("chunk_bwd_dq") < n.index("chunk_bwd_dg"), n
