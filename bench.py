@@ -187,6 +187,30 @@ def backward_legs(stream):
     return backward
 
 
+def copy_rate_gbs(mib: int = 1024, reps: int = 10) -> float:
+    """This GPU's rate for a plain device-to-device copy of ``mib`` MiB (bytes read + written over
+    time, median of ``reps``): context for the roofline fraction, whose peak is the datasheet's."""
+    import statistics
+
+    import torch
+
+    a = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * mib * (1 << 20) / statistics.median(ts) / 1e9, 1)
+
+
 def step_stats(step, steps, stream, scratch=None):
     """Per-step times (us) with events around each step; with ``scratch``, the buffer is read
     before every step so that the step starts with a cold last-level cache."""
@@ -530,7 +554,8 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=dom,
                     kernel_mean_us=round(dom_us, 2), algorithmic_bytes=alg_bytes,
-                    mfma_frac=round(tokens * w.H * fl_tok / (dom_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4))
+                    mfma_frac=round(tokens * w.H * fl_tok / (dom_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    measured_copy_GBps=copy_rate_gbs())
 
     cpu = None
     if not args.no_cpu_baseline:
