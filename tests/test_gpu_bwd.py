@@ -313,3 +313,34 @@ def test_bwd_pass_structure():
     assert "chunk_bwd_dq_state_pass" in n and "chunk_bwd_dlam_state_pass" not in n, n
     n = names("gate", True)
     assert n.index("chunk_bwd_dkdv") < n.index("chunk_bwd_dq") < n.index("chunk_bwd_dg"), n
+
+
+def test_concurrent_streams_bit_identical():
+    """Two different problems on two streams at once (forward with internal sub-segments, then the
+    backward with the decay derivative, both drawing workspace from the stream-ordered pool) give
+    bit for bit what each gives alone."""
+    note("la_chunk_fwd + la_chunk_bwd on two streams concurrently, bf16 d=128 head decay")
+    cases = [_case("head", "bf16", 128, 128, 3000, 64, 1, seed=1400 + i, B=1, H=2) for i in range(2)]
+    devs = [(to_dev(inp), to_dev(gr), w) for w, inp, gr in cases]
+
+    def run(d, g, w):
+        o, s_out = lb.la_chunk_fwd(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode=w.mode, chunk=64)
+        grads = lb.la_chunk_bwd(d["q"], d["k"], d["v"], g["d_o"], d["decay"], d["s_in"], g["ds_out"], mode=w.mode,
+                                chunk=64)
+        return (o, s_out) + tuple(grads)
+
+    alone = []
+    for d, g, w in devs:
+        alone.append(run(d, g, w))
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        together = []
+        for (d, g, w), st in zip(devs, streams):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                together.append(run(d, g, w))
+        torch.cuda.synchronize()
+        for a, b in zip(alone, together):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y)
