@@ -557,3 +557,36 @@ def test_chunk128_decayed_and_device_step(mode, d):
     o1_ref, s1_ref = oracle_run(inp1, w1)
     assert rel_err(o1, o1_ref) <= TOL["bf16"]
     assert rel_err(s_out, s1_ref[:, :, 0]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["none", "head", "gate"])
+def test_device_step_graph_replay(mode):
+    """The device step captured in a HIP graph (through torch.cuda.graph) and replayed several times,
+    with eager work and synchronisations between the replays: every replay's O and outgoing state
+    equal the eager step's bit for bit (the library enqueues kernels only: no memsets, no host sync)."""
+    decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
+    w = W2.scaled(B=1, H=4, L=64 * 40, decay=decay, s_in_std=0.05, seed=1500)
+    note(f"device step graph replay, bf16 d128 mode={mode}")
+    d = to_dev(make_inputs(w, "cpu"))
+    step = pipeline.DeviceStep(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode=w.mode, chunk=64,
+                               gate_norm=w.gate_norm, subseg=4)
+    o_ref, s_ref = (x.clone() for x in step.run())
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream, as graph capture asks
+        step.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        o_g, s_g = step.run()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for rep in range(4):
+        step.o.zero_()  # eager work between the replays
+        scratch.add_(1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_ref), rep
+        assert torch.equal(s_g, s_ref), rep
