@@ -23,8 +23,9 @@ LIB_PATH = os.path.join(_HERE, "liblachunk.so")
 LA_F32, LA_BF16 = 0, 1
 MODES = {"none": 0, "head": 1, "gate": 2}
 STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_SHAPE", -3: "LA_ERR_DTYPE", -4: "LA_ERR_ALIAS",
-          -5: "LA_ERR_UNSUPPORTED", -6: "LA_ERR_LAUNCH", -7: "LA_ERR_DECAY"}
-EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_decayed", "la_chunk_bwd", "la_chunk_bwd_states", "la_state_scan", "la_state_correct", "la_state_correct_live",
+          -5: "LA_ERR_UNSUPPORTED", -6: "LA_ERR_LAUNCH", -7: "LA_ERR_DECAY", -8: "LA_ERR_WORKSPACE"}
+NOALLOC_SCRATCH_BYTES = 32 << 20  # LA_NOALLOC_SCRATCH_BYTES of la_chunk.h
+EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_noalloc", "la_chunk_fwd_decayed", "la_chunk_bwd", "la_chunk_bwd_states", "la_state_scan", "la_state_correct", "la_state_correct_live",
            "la_cumdecay", "la_status_str", "la_supported", "la_version")
 
 
@@ -89,6 +90,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, S = ctypes.c_void_p, ctypes.POINTER(Shape)
         L.la_chunk_fwd.argtypes = [P, P, P, P, P, P, P, S, ctypes.c_int32]
+        L.la_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, S, ctypes.c_int32]
         L.la_chunk_fwd_decayed.argtypes = [P, P, P, P, P, P, P, P, P, P, S, ctypes.c_int32]
         L.la_chunk_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, S, ctypes.c_int32]
         L.la_chunk_bwd_states.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P, P, P, P, P, S,
@@ -100,7 +102,7 @@ def lib() -> ctypes.CDLL:
         L.la_supported.argtypes = [S, ctypes.c_int32]
         L.la_status_str.argtypes = [ctypes.c_int]
         L.la_status_str.restype = ctypes.c_char_p
-        for f in (L.la_chunk_fwd, L.la_chunk_fwd_decayed, L.la_state_scan, L.la_state_correct,
+        for f in (L.la_chunk_fwd, L.la_chunk_fwd_noalloc, L.la_chunk_fwd_decayed, L.la_state_scan, L.la_state_correct,
                   L.la_state_correct_live, L.la_cumdecay, L.la_supported, L.la_version):
             f.restype = ctypes.c_int
         _lib = L
@@ -181,6 +183,24 @@ def la_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optio
     """Chunkwise forward.  q, k [B,H,L,dk], v [B,H,L,dv] (f32 or bf16); decay None / [H] / [B,H,L,dk];
     s_in [B,H,dk,dv] f32 or None.  Returns (o [B,H,L,dv], s_out [B,H,nseg,dk,dv] f32 or None);
     s_out may be a view with evenly spaced dense (b,h) blocks."""
+    return _chunk_fwd("la_chunk_fwd", q, k, v, decay, s_in, o, s_out, mode, nseg, chunk, gate_norm, subseg_chunks,
+                      want_state, stream, timer)
+
+
+def la_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch.Tensor] = None,
+                         s_in: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                         s_out: Optional[torch.Tensor] = None, *, mode: Optional[str] = None, nseg: int = 1,
+                         chunk: int = 64, gate_norm: float = 16.0, subseg_chunks: int = 0, want_state: bool = True,
+                         stream=None, timer=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """la_chunk_fwd whose workspace is the library's fixed device array (the library allocates
+    nothing).  Pass o (and s_out, or want_state=False) to keep the whole call free of allocations:
+    the outputs this wrapper creates when they are not given come from torch's allocator."""
+    return _chunk_fwd("la_chunk_fwd_noalloc", q, k, v, decay, s_in, o, s_out, mode, nseg, chunk, gate_norm,
+                      subseg_chunks, want_state, stream, timer)
+
+
+def _chunk_fwd(fn, q, k, v, decay, s_in, o, s_out, mode, nseg, chunk, gate_norm, subseg_chunks, want_state, stream,
+               timer):
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     _dev(q, "q")
@@ -202,8 +222,8 @@ def la_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optio
         stride = _bh_stride(s_out, "s_out", dk * dv)
     shp = make_shape(B, H, L, dk, dv, nseg=nseg, dtype=_dtype_code(q), mode=m, gate_norm=gate_norm,
                      state_stride=stride, subseg_chunks=subseg_chunks, stream=_stream(stream), timer=timer)
-    _check("la_chunk_fwd", lib().la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(o),
-                                              _ptr(s_out), ctypes.byref(shp), chunk))
+    _check(fn, getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(o), _ptr(s_out),
+                                  ctypes.byref(shp), chunk))
     return o, s_out
 
 

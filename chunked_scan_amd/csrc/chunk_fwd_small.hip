@@ -454,42 +454,11 @@ hipError_t launch_chunk_fwd_small(const FwdArgs& a, int G, int cps, float* part_
     return launch_small_d<32, 64>(a, G, cps, part_state, part_decay);
 }
 
-// 128-token chunks: the same split as for 64-token chunks (about 256 workgroups, a fixed
-// sub-segment length when the caller gives one), counted in 128-token chunks, at least two each.
-hipError_t launch_chunk_fwd_small128(const FwdArgs& a) {
-    constexpr int CH = 128;
-    const int64_t units = a.B * a.H * a.nseg;
-    const int64_t nch = (a.L / a.nseg + CH - 1) / CH;
-    int64_t cps;
-    if (a.subseg_chunks > 0) {
-        cps = a.subseg_chunks;
-    } else {
-        const int64_t g_want = (256 + units - 1) / units;
-        cps = max((int64_t)2, (nch + g_want - 1) / g_want);
-    }
-    if (cps > nch) cps = nch > 0 ? nch : 1;
-    const int G = (int)max((int64_t)1, (nch + cps - 1) / cps);
-    float* part_state = nullptr;
-    float* part_decay = nullptr;
-    hipError_t e = hipSuccess;
-    if (G > 1) {
-        int dev = 0;
-        if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-        hipMemPool_t pool = workspace_pool(dev);
-        if (!pool) return hipErrorOutOfMemory;
-        const size_t n = (size_t)units * (G - 1), D = (size_t)a.dk;
-        e = hipMallocFromPoolAsync((void**)&part_state, n * D * D * sizeof(float) + n * D * sizeof(float), pool,
-                                   a.stream);
-        if (e != hipSuccess) return e;
-        part_decay = part_state + n * D * D;
-    }
-    e = a.dk == 64 ? launch_small_d<64, CH>(a, G, (int)cps, part_state, part_decay)
-                   : launch_small_d<32, CH>(a, G, (int)cps, part_state, part_decay);
-    if (part_state) {
-        hipError_t f = hipFreeAsync(part_state, a.stream);
-        if (e == hipSuccess) e = f;
-    }
-    return e;
+// 128-token chunks: G sub-segments of cps 128-token chunks (the split is chosen by the caller,
+// chunk_fwd_split.hip).
+hipError_t launch_chunk_fwd_small_ch128(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
+    return a.dk == 64 ? launch_small_d<64, 128>(a, G, cps, part_state, part_decay)
+                      : launch_small_d<32, 128>(a, G, cps, part_state, part_decay);
 }
 
 }  // namespace la

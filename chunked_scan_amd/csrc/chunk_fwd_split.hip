@@ -65,32 +65,131 @@ void mfma_split(const FwdArgs& a, int* G_out, int* cps_out, int64_t target) {
     *cps_out = (int)cps;
 }
 
+// The split of the matrix-core forward.  64-token chunks: 512 workgroups for small heads (their
+// kernels are latency-bound and several share a compute unit), 256 for d = 128.  128-token
+// chunks (small heads): about 256 workgroups, at least two chunks per sub-segment; the
+// sub-segment length a caller gives counts chunks of the call's own length.
+void fwd_split_plan(const FwdArgs& a, int* G_out, int* cps_out) {
+    if (a.chunk != 128) {
+        mfma_split(a, G_out, cps_out, a.dk < 128 ? 512 : 256);
+        return;
+    }
+    constexpr int CH = 128;
+    const int64_t units = a.B * a.H * a.nseg;
+    const int64_t nch = (a.L / a.nseg + CH - 1) / CH;
+    int64_t cps;
+    if (a.subseg_chunks > 0) {
+        cps = a.subseg_chunks;
+    } else {
+        const int64_t g_want = (256 + units - 1) / units;
+        cps = max((int64_t)2, (nch + g_want - 1) / g_want);
+    }
+    if (cps > nch) cps = nch > 0 ? nch : 1;
+    *G_out = (int)max((int64_t)1, (nch + cps - 1) / cps);
+    *cps_out = (int)cps;
+}
+
+// Floats of workspace for G sub-segments per segment: a state and a decay vector for every
+// sub-segment but the last of every (b, h, segment).
+size_t fwd_split_workspace_floats(const FwdArgs& a, int G) {
+    if (G <= 1) return 0;
+    const size_t n = (size_t)(a.B * a.H * a.nseg) * (size_t)(G - 1);
+    const size_t D = (size_t)a.dk;
+    return n * D * D + n * D;
+}
+
+namespace {
+
+// The kernels of the split forward with the workspace at ws (fwd_split_workspace_floats floats;
+// unused when G == 1).
+hipError_t fwd_split_run(const FwdArgs& a, int G, int cps, float* ws) {
+    float* part_state = G > 1 ? ws : nullptr;
+    float* part_decay = G > 1 ? ws + (size_t)(a.B * a.H * a.nseg) * (size_t)(G - 1) * a.dk * a.dk : nullptr;
+    if (a.chunk == 128) return launch_chunk_fwd_small_ch128(a, G, cps, part_state, part_decay);
+    return a.dk == 128 ? launch_chunk_fwd_pipe(a, G, cps, part_state, part_decay)
+                       : launch_chunk_fwd_small(a, G, cps, part_state, part_decay);
+}
+
+}  // namespace
+
 hipError_t launch_chunk_fwd_mfma(const FwdArgs& a) {
     int G, cps;
-    // small heads: 512 workgroups (latency-bound kernels, several share a compute unit)
-    mfma_split(a, &G, &cps, a.dk < 128 ? 512 : 256);
-    float* part_state = nullptr;
-    float* part_decay = nullptr;
-    if (G > 1) {
+    fwd_split_plan(a, &G, &cps);
+    const size_t nf = fwd_split_workspace_floats(a, G);
+    float* ws = nullptr;
+    if (nf > 0) {
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return e;
         hipMemPool_t pool = workspace_pool(dev);
         if (!pool) return hipErrorOutOfMemory;
-        const size_t n = (size_t)(a.B * a.H * a.nseg) * (G - 1);
-        const size_t D = (size_t)a.dk;
-        e = hipMallocFromPoolAsync((void**)&part_state, n * D * D * sizeof(float) + n * D * sizeof(float), pool,
-                                   a.stream);
+        e = hipMallocFromPoolAsync((void**)&ws, nf * sizeof(float), pool, a.stream);
         if (e != hipSuccess) return e;
-        part_decay = part_state + n * D * D;
     }
-    hipError_t e = a.dk == 128 ? launch_chunk_fwd_pipe(a, G, cps, part_state, part_decay)
-                               : launch_chunk_fwd_small(a, G, cps, part_state, part_decay);
-    if (part_state) {
-        hipError_t f = hipFreeAsync(part_state, a.stream);
+    hipError_t e = fwd_split_run(a, G, cps, ws);
+    if (ws) {
+        hipError_t f = hipFreeAsync(ws, a.stream);
         if (e == hipSuccess) e = f;
     }
     return e;
+}
+
+// ---- the allocation-free forward (la_chunk_fwd_noalloc)
+//
+// Its workspace is this fixed device array: every device the library runs on holds one copy,
+// from the code object's load until the process ends.  Host code never uses the array's name
+// as an address (on the host it only names the symbol): the device address of each device's
+// copy is looked up once per device and kept in noalloc_ptr.  Every call on a device shares that
+// copy; nothing in it needs to start at zero (the state pass writes every entry the scan and the
+// output pass read), and calls that overlap in time on one device race on it.
+static __device__ __align__(256) float scratch[LA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+// The device address of `scratch` on the current device (looked up on the first call for that
+// device), or null if the lookup failed.
+float* noalloc_ptr(hipError_t* err) {
+    static std::mutex mu;
+    static float* ptrs[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        ptrs[dev] = (float*)p;
+    }
+    *err = hipSuccess;
+    return ptrs[dev];
+}
+
+}  // namespace
+
+size_t fwd_noalloc_bytes(const FwdArgs& a) {
+    int G, cps;
+    fwd_split_plan(a, &G, &cps);
+    return fwd_split_workspace_floats(a, G) * sizeof(float);
+}
+
+hipError_t launch_chunk_fwd_mfma_noalloc(const FwdArgs& a) {
+    int G, cps;
+    fwd_split_plan(a, &G, &cps);
+    if (fwd_split_workspace_floats(a, G) * sizeof(float) > LA_NOALLOC_SCRATCH_BYTES) return hipErrorInvalidValue;
+    float* ws = nullptr;
+    if (G > 1) {
+        hipError_t e = hipSuccess;
+        ws = noalloc_ptr(&e);
+        if (!ws) return e;
+    }
+    return fwd_split_run(a, G, cps, ws);
 }
 
 }  // namespace la

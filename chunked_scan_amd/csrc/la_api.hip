@@ -161,6 +161,7 @@ const char* la_status_str(la_status s) {
         case LA_ERR_UNSUPPORTED: return "no kernel for this head dim / chunk / layout";
         case LA_ERR_LAUNCH: return "HIP launch or workspace allocation failed";
         case LA_ERR_DECAY: return "invalid decay mode or gate_norm";
+        case LA_ERR_WORKSPACE: return "the call needs more workspace than the allocation-free entry point holds";
     }
     return "unknown status";
 }
@@ -175,10 +176,12 @@ int32_t la_supported(const la_shape* s, int32_t chunk) {
 
 namespace {
 
-// The forward of la_chunk_fwd, plus the optional outputs of la_chunk_fwd_decayed (q_dec, total).
+// The forward of la_chunk_fwd, plus the optional outputs of la_chunk_fwd_decayed (q_dec, total);
+// noalloc: the workspace of the matrix-core split comes from the library's fixed device array
+// (la_chunk_fwd_noalloc), and a call that needs more than it holds is rejected.
 la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* decay, const float* s_in, void* o,
                          float* s_out, void* q_dec, float* total, uint32_t* tile_live, const la_shape* s,
-                         int32_t chunk) {
+                         int32_t chunk, bool noalloc = false) {
     la_status st = validate_fwd(q, k, v, decay, s_in, o, s_out, s, chunk, q_dec, total, tile_live);
     if (st != LA_OK) return st;
     if ((st = check_trace(s)) != LA_OK) return st;
@@ -201,16 +204,18 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const floa
     a.total = total;
     a.total_stride = s->total_stride ? s->total_stride : (int64_t)s->nseg * s->dk;
     a.tile_live = tile_live;
+    // matrix cores: bf16 with dk = dv in {32, 64, 128} and 64-token chunks, or 128-token chunks
+    // (bf16, dk = dv in {32, 64}, validated)
+    const bool mfma = s->L > 0 && ((a.bf16 && a.dk == a.dv && (a.dk == 32 || a.dk == 64 || a.dk == 128) && chunk == 64) ||
+                                   chunk == 128);
+    if (noalloc && mfma && la::fwd_noalloc_bytes(a) > LA_NOALLOC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;
     hipError_t e = hipSuccess;
     bool fused = false;  // the forward itself wrote q_dec and total
     if (s->L == 0) {
         if (s_out) e = la::launch_empty_states(s_in, s_out, so_stride, s->B * s->H, s->nseg, s->dk, s->dv, stream, &tr);
-    } else if (a.bf16 && a.dk == a.dv && (a.dk == 32 || a.dk == 64 || a.dk == 128) && chunk == 64) {
-        e = la::launch_chunk_fwd_mfma(a);
+    } else if (mfma) {
+        e = noalloc ? la::launch_chunk_fwd_mfma_noalloc(a) : la::launch_chunk_fwd_mfma(a);
         fused = a.mode == LA_DECAY_GATE;  // the gate kernels emit q_dec, totals and tile flags themselves
-    } else if (chunk == 128) {  // bf16, dk = dv in {32, 64} (validated)
-        e = la::launch_chunk_fwd_small128(a);
-        fused = a.mode == LA_DECAY_GATE;
     } else {
         e = la::launch_chunk_fwd_generic(a);
     }
@@ -225,6 +230,11 @@ extern "C" {
 la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in, void* o,
                        float* s_out, const la_shape* s, int32_t chunk) {
     return chunk_fwd_impl(q, k, v, decay, s_in, o, s_out, nullptr, nullptr, nullptr, s, chunk);
+}
+
+la_status la_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
+                               void* o, float* s_out, const la_shape* s, int32_t chunk) {
+    return chunk_fwd_impl(q, k, v, decay, s_in, o, s_out, nullptr, nullptr, nullptr, s, chunk, true);
 }
 
 la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, const float* decay, const float* s_in,

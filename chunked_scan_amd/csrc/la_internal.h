@@ -122,19 +122,28 @@ hipError_t launch_chunk_bwd_mfma(const BwdArgs& a);
 // {16,32,64,128}, chunk in {16,32,64}.
 hipError_t launch_chunk_fwd_generic(const FwdArgs& a);
 
-// bf16 MFMA chunked forward for dk = dv in {32, 64, 128}, chunk = 64, with intra-GPU sub-segment
-// splitting (chunk_fwd_split.hip), all decay modes.
+// bf16 MFMA chunked forward for dk = dv in {32, 64, 128} with chunk = 64, or dk = dv in {32, 64}
+// with chunk = 128, with intra-GPU sub-segment splitting (chunk_fwd_split.hip), all decay modes.
+// The workspace of the split comes from the device's workspace pool.
 hipError_t launch_chunk_fwd_mfma(const FwdArgs& a);
-// The same for 128-token chunks, dk = dv in {32, 64} (bf16): its own split into sub-segments.
-hipError_t launch_chunk_fwd_small128(const FwdArgs& a);
-// Its split of each segment into G sub-segments of cps chunks (uses B, H, L, nseg, subseg_chunks).
+// The same with the workspace in the library's fixed device array (nothing allocated): fails with
+// hipErrorInvalidValue when fwd_noalloc_bytes(a) exceeds LA_NOALLOC_SCRATCH_BYTES.
+hipError_t launch_chunk_fwd_mfma_noalloc(const FwdArgs& a);
+// Workspace bytes the matrix-core forward needs for this call (0 when it does not split).
+size_t fwd_noalloc_bytes(const FwdArgs& a);
+// A split of each segment into G sub-segments of cps chunks (uses B, H, L, nseg, subseg_chunks).
 // target: about how many workgroups to aim for when the length is chosen automatically.
 void mfma_split(const FwdArgs& a, int* G_out, int* cps_out, int64_t target = 256);
+// The matrix-core forward's own split (by chunk length and head dim) and its workspace size.
+void fwd_split_plan(const FwdArgs& a, int* G_out, int* cps_out);
+size_t fwd_split_workspace_floats(const FwdArgs& a, int G);
 // Its kernels: G sub-segments of cps chunks; part_state / part_decay the workspace of the
 // sub-segment scan (unused when G == 1).
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
 // The same for dk = dv = 32 or 64 (chunk_fwd_small.hip).
 hipError_t launch_chunk_fwd_small(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
+// The same with 128-token chunks (cps counts 128-token chunks).
+hipError_t launch_chunk_fwd_small_ch128(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
 
 // out[n,p] = diag(lam[n,p]) out[n,p-1] + x[n,p] for n < nstates, p < P.  x may equal out.
 hipError_t launch_state_scan(const float* x, const float* lam, float* out, int64_t nstates, int P,

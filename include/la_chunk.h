@@ -47,7 +47,8 @@ typedef enum la_status {
     LA_ERR_ALIAS = -4,       /* an output overlaps an input it may not overlap */
     LA_ERR_UNSUPPORTED = -5, /* valid request that this build has no kernel for (e.g. dk > 128) */
     LA_ERR_LAUNCH = -6,      /* the HIP runtime refused a launch or a workspace allocation */
-    LA_ERR_DECAY = -7        /* unknown decay mode, or gate_norm <= 0 in gate mode */
+    LA_ERR_DECAY = -7,       /* unknown decay mode, or gate_norm <= 0 in gate mode */
+    LA_ERR_WORKSPACE = -8    /* la_chunk_fwd_noalloc: the call needs more than LA_NOALLOC_SCRATCH_BYTES */
 } la_status;
 
 typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
@@ -135,6 +136,25 @@ typedef struct la_shape {
 la_status la_chunk_fwd(const void* q, const void* k, const void* v, const float* decay,
                        const float* s_in, void* o, float* s_out, const la_shape* shape,
                        int32_t chunk);
+
+/*
+ * la_chunk_fwd for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments, results and rounding as
+ * la_chunk_fwd (the same kernels with the same split into sub-segments); the only difference is
+ * where the workspace of that split lives.  It is a fixed device array of
+ * LA_NOALLOC_SCRATCH_BYTES in the library, one per device the library runs on, held from its first
+ * use until the process ends; the call itself allocates nothing (no hipMalloc, no pool).  Every
+ * call on a device shares that device's array, so calls that may overlap in time on one device
+ * (other streams, other host threads) race on it and must be ordered by the caller.  Nothing in it
+ * needs to be cleared between calls.  The automatic split (subseg_chunks = 0) always fits; a call
+ * whose caller-chosen subseg_chunks would need more workspace returns LA_ERR_WORKSPACE and
+ * enqueues nothing.
+ * Returns the codes of la_chunk_fwd, or LA_ERR_WORKSPACE.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES ((uint64_t)32 << 20)
+la_status la_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* decay,
+                               const float* s_in, void* o, float* s_out, const la_shape* shape,
+                               int32_t chunk);
 
 /*
  * la_chunk_fwd plus the two decay quantities that the rest of a device's step needs, emitted by

@@ -15,7 +15,7 @@ from chunked_scan_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "la_chunk.h")
 
-OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, LAUNCH, DECAY = 0, -1, -2, -3, -4, -5, -6, -7
+OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, LAUNCH, DECAY, WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 1
-    for code in (OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, LAUNCH, DECAY, 12345):
+    for code in (OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, LAUNCH, DECAY, WORKSPACE, 12345):
         assert lib.la_status_str(code)
 
 
@@ -243,3 +243,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+def test_noalloc_validation_and_workspace_bound(lib):
+    P = ctypes.c_void_p
+
+    def call(shp, chunk=64, dec=None):
+        return lib.la_chunk_fwd_noalloc(P(Q), P(K), P(V), P(dec), None, P(O), P(S_OUT), ctypes.byref(shp), chunk)
+
+    # the same validation as la_chunk_fwd, before anything else
+    assert lib.la_chunk_fwd_noalloc(None, None, None, None, None, None, None, None, 64) == NULL
+    assert call(shape(L=100, nseg=3)) == SHAPE
+    assert call(shape(dk=96)) == UNSUP
+    assert call(shape(), dec=DEC) == DECAY
+    # one 64-token chunk per sub-segment over 16 heads x 16k tokens at d = 128 needs 255 x 16
+    # sub-segment states of 64 KiB (+ decay vectors): far beyond the fixed workspace, rejected on
+    # the host (nothing is enqueued, so no GPU is needed to see it)
+    big = shape(H=16, L=16384, dk=128, dv=128, subseg_chunks=1)
+    assert call(big) == WORKSPACE
+    assert 255 * 16 * (128 * 128 + 128) * 4 > B.NOALLOC_SCRATCH_BYTES
+    # 128-token chunks with one chunk per sub-segment: 127 x 64 states of 16 KiB at d = 64
+    assert call(shape(H=64, L=16384, dk=64, dv=64, subseg_chunks=1), chunk=128) == WORKSPACE
