@@ -285,3 +285,30 @@ def test_state_correct_cases():
     # seg_begin skips earlier segments bit-exactly
     got = oracle.state_correct(q, ones, S, o, nseg=2, seg_begin=1)
     assert np.array_equal(got[:, :, :10], o[:, :, :10])
+
+
+def test_gate_reset_tokens_restart_the_recurrence():
+    """A gate of -inf gives a = sigmoid(-inf)^(1/16) = 0 exactly: at such a token every key dim's state
+    forgets everything before it.  So with g = -inf on all key dims of token t0, the outputs from t0
+    on and S_out equal a fresh run over tokens t0.. from a zero state (the prefix changes nothing),
+    and g = -1e3 (sigmoid underflows to 0 in fp64) behaves the same.  With g = -inf on one key dim
+    only, that dim's row of S_out is k_L[d] v_L (every earlier term of the row is cut)."""
+    rng = np.random.default_rng(21)
+    B, H, L, dk, dv, t0 = 1, 2, 50, 4, 3, 19
+    q, k, v = _rand(rng, B, H, L, dk), _rand(rng, B, H, L, dk), _rand(rng, B, H, L, dv)
+    g = _rand(rng, B, H, L, dk)
+    s_in = rng.standard_normal((B, H, dk, dv))
+    for reset in (-np.inf, -1e3):
+        gr = g.copy()
+        gr[:, :, t0, :] = reset
+        o, s = oracle.recurrence(q, k, v, GATE, gr, s_in, gate_norm=16.0)
+        o2, s2 = oracle.recurrence(q[:, :, t0:].copy(), k[:, :, t0:].copy(), v[:, :, t0:].copy(), GATE,
+                                   gr[:, :, t0:].copy(), None, gate_norm=16.0)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(s))
+        assert np.array_equal(o[:, :, t0:], o2) and np.array_equal(s, s2)
+    # one dim reset on every token: its row of the state is the last token's k v only
+    gd = g.copy()
+    gd[..., 2] = -np.inf
+    _, s = oracle.recurrence(q, k, v, GATE, gd, s_in, gate_norm=16.0)
+    K, V = k.astype(np.float64), v.astype(np.float64)
+    assert np.allclose(s[:, :, 0, 2, :], K[:, :, -1, 2, None] * V[:, :, -1, :], rtol=0, atol=1e-15)
