@@ -99,24 +99,26 @@ __device__ __forceinline__ void gate_load(const float* __restrict__ g, int64_t r
     }
 }
 
-// The chunk's per-token log2-decay, log2 a = -softplus(-g) / gate_norm * log2(e), from the gate
-// tile rg, into gb[C][D] (rows past the chunk's end as 0), then replaced by its inclusive in-chunk
-// running sum B (per key dim), in NT / D parts of C * D / NT rows; gel[d] = 2^{B_last[d]} is the
-// chunk's total decay.  Every factor built from B later on is 2^{B} <= 1, 2^{-B} (bounded by the
-// chunk's decay sum, which must stay above -80 in natural log units as for the forward) or
-// 2^{B_last - B} <= 1.
+// The per-token log2-decay, log2 a = -softplus(-g) / gate_norm * log2(e), of the chunk's rows s0 ..
+// s1 - 1 from its gate tile rg (rows past the chunk's end read as zero), into gb rows 0 .. s1 - s0 - 1
+// (chunk row r at row (r - s0) mod C; every other row 0), then replaced by its inclusive running sum
+// B (per key dim), in NT / D parts of C * D / NT rows; gel[d] = 2^{B_last[d]} is the decay over the
+// rows.  A whole chunk is s0 = 0, s1 = n.  Every factor built from B later on is 2^{B} <= 1, 2^{-B}
+// or 2^{B_last - B} <= 1; 2^{-B} stays within 2^GATE_SPAN_LOG2 when the rows' decay does, which
+// the callers ensure by cutting a chunk into windows where it does not (chunk_gate_windows).
 template <int D>
-__device__ __forceinline__ void gate_chunk_logdecay(const f32x4* rg, int n, float inv_norm, float* gb, float* gtot,
-                                                    float* gel, int tid) {
+__device__ __forceinline__ void gate_chunk_logdecay(const f32x4* rg, int s0, int s1, float inv_norm, float* gb,
+                                                    float* gtot, float* gel, int tid) {
 #pragma unroll
     for (int r = 0; r < GateTile<D>::PG; r++) {
         const int p = tid + NT * r;
         const int row = p / (D / 4), c4 = (p % (D / 4)) * 4;
         const f32x4 x = rg[r];
+        const bool in = row >= s0 && row < s1;
         f32x4 y;
 #pragma unroll
-        for (int e = 0; e < 4; e++) y[e] = row < n ? gate_logdecay(x[e], inv_norm) * LOG2E : 0.f;
-        *(f32x4*)(&gb[row * D + c4]) = y;
+        for (int e = 0; e < 4; e++) y[e] = in ? gate_logdecay(x[e], inv_norm) * LOG2E : 0.f;
+        *(f32x4*)(&gb[((row - s0) & (C - 1)) * D + c4]) = y;
     }
     __syncthreads();
     constexpr int NPART = NT / D, R = C / NPART;
@@ -134,6 +136,27 @@ __device__ __forceinline__ void gate_chunk_logdecay(const f32x4* rg, int n, floa
     for (int i = 0; i < R; i++) gb[(part * R + i) * D + d] = vals[i] + off;
     __syncthreads();
     if (tid < D) gel[tid] = __builtin_amdgcn_exp2f(gb[(C - 1) * D + tid]);
+}
+
+// The window length (tokens) at which a gate chunk of n tokens is taken, from its whole-chunk running
+// sums gb (gate_chunk_logdecay over rows 0 .. n - 1): the chunk itself when its decay stays within
+// 2^GATE_SPAN_LOG2 on every key dim (the common case), else the longest C >> lv whose windows' decays,
+// their first token included, each stay within it (two tokens always do, given the floor on log a).
+// The result is read from *lvl after the caller's next barrier; *lvl must be 0 before this call.
+template <int D>
+__device__ __forceinline__ void chunk_gate_windows(const float* gb, int n, int* lvl, int tid) {
+    if (tid >= D || gb[(C - 1) * D + tid] >= -GATE_SPAN_LOG2) return;
+    int lv = 1;
+    for (; (C >> lv) > 1; lv++) {
+        const int wl = C >> lv;
+        bool fits = true;
+        for (int s0 = 0; s0 < n && fits; s0 += wl) {
+            const float base = s0 ? gb[(s0 - 1) * D + tid] : 0.f;
+            fits = gb[(min(s0 + wl, n) - 1) * D + tid] - base >= -GATE_SPAN_LOG2;
+        }
+        if (fits) break;
+    }
+    atomicMax(lvl, lv);
 }
 
 // LDS of the backward-direction kernel; the state pass keeps only the tiles of the D update.
@@ -156,11 +179,15 @@ struct BwdSmem {
     float gel[GATE ? D : 4];         // gate: 2^{B_last}
     float apow[C + 1];               // a^m, m = 0..C (head mode)
     double red[NT / 64];
+    int lvl;                         // gate: the chunk is taken in windows of C >> lvl tokens
 };
 
 // The chunk walk prefetches the next chunk (in walk order) into registers while the current one is
 // computed (PF; off, each chunk is loaded at its top).
-template <int D, int MODE, bool STATE_ONLY>
+// WIN (gate mode): the instance that cuts chunks into windows; it redoes only the units (workgroups)
+// whose wide[] flag the plain instance set when it met a chunk too wide for one piece, and the plain
+// instance stops such a unit there (the redo overwrites everything the unit writes).
+template <int D, int MODE, bool STATE_ONLY, bool WIN = false>
 __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ ds_out,
@@ -169,8 +196,15 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     const float* __restrict__ init_state,                            // output pass: scanned D^(g)
     double* __restrict__ intra_part,  // head mode, output pass: the intra-chunk part of d lambda_h, or null
     __bf16* __restrict__ d_start,     // output pass, gate derivative: D at every chunk's start (bf16 [D][D]), or null
-    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm) {
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
     __shared__ __attribute__((aligned(16))) BwdSmem<D, MODE, STATE_ONLY> sm;
+    if constexpr (MODE == DECAY_GATE) {
+        if constexpr (WIN) {
+            if (wide[blockIdx.x] == 0) return;
+        } else if (threadIdx.x == 0) {
+            wide[blockIdx.x] = 0;
+        }
+    }
     using Gm = Geo<D>;
     constexpr int PITCH = Gm::PITCH, PR = Gm::PR, PIECES_ROW = Gm::PIECES_ROW, NCB = Gm::NCB;
     constexpr bool PF = true;
@@ -244,46 +278,91 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     };
     if (PF && nchunks > 0) load_chunk(nchunks - 1);
     for (int c = nchunks - 1; c >= 0; c--) {
-        const int64_t t0 = t_begin + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, t_end - t0);
+        const int64_t t0c = t_begin + (int64_t)c * C;
+        const int nc = (int)min((int64_t)C, t_end - t0c);
         __syncthreads();  // the previous chunk is done with every LDS tile
         if (!PF) load_chunk(c);
+        // gate mode: the chunk's running log2-decay, and the windows it is taken in (one, unless its
+        // decay is too wide for the factorised pair weights; chunk_gate_windows)
+        int ws = C;
         if (MODE == DECAY_GATE) {
-            if (!GPF) gate_load<D>(decay, row_base + t0, n, rg, tid);
-            gate_chunk_logdecay<D>(rg, n, inv_norm, sm.gb, sm.gtot, sm.gel, tid);
+            if (WIN && tid == 0) sm.lvl = 0;
+            if (!GPF) gate_load<D>(decay, row_base + t0c, nc, rg, tid);
+            gate_chunk_logdecay<D>(rg, 0, nc, inv_norm, sm.gb, sm.gtot, sm.gel, tid);
             if (tid < D) gate_total += sm.gb[(C - 1) * D + tid];
+            if constexpr (WIN) {
+                chunk_gate_windows<D>(sm.gb, nc, &sm.lvl, tid);
+                __syncthreads();  // gel, lvl
+                ws = C >> sm.lvl;
+            } else {
+                // a chunk too wide for one piece sends the unit to the windowed instance, which
+                // overwrites all it writes (this instance finishes the unit all the same: its register
+                // allocation is left exactly as without the check)
+                if (tid < D && sm.gb[(C - 1) * D + tid] < -GATE_SPAN_LOG2) wide[blockIdx.x] = 1;
+                __syncthreads();  // gel
+            }
+        }
+        // The windows run backwards in time, each staged as a ragged chunk of its own (chunk row r at
+        // tile row (r - s0) mod C, the rest zero) with its first token as the decay reference, from the
+        // registers, which keep the chunk until its last window is staged (the next chunk's prefetch
+        // waits until then).
+        const int nwin = (MODE == DECAY_GATE && WIN) ? (nc + ws - 1) / ws : 1;
+        for (int wi = 0; wi < nwin; wi++) {
+        const int s0 = (MODE == DECAY_GATE && WIN) ? (nwin - 1 - wi) * ws : 0;
+        const int n = (MODE == DECAY_GATE && WIN) ? min(s0 + ws, nc) - s0 : nc;
+        const int64_t t0 = t0c + s0;
+        if (MODE == DECAY_GATE && WIN && nwin > 1) {
+            if (wi > 0) __syncthreads();  // the previous window is done with every LDS tile
+            f32x4 xg[GateTile<D>::PG];  // the gate rows again (cached), not held across the windows
+            gate_load<D>(decay, row_base + t0c, nc, xg, tid);
+            gate_chunk_logdecay<D>(xg, s0, s0 + n, inv_norm, sm.gb, sm.gtot, sm.gel, tid);
             __syncthreads();  // gel
         }
 
-        // ---- stage the chunk and D as bf16
+        // ---- stage the chunk (window) and D as bf16
+        auto stage = [&](auto fetch) {
 #pragma unroll
-        for (int r = 0; r < PR; r++) {
-            const int p = tid + NT * r;
-            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            if (MODE == DECAY_GATE) {  // q 2^{B}; k 2^{-B}
-                float fq[8], fk[8];
+            for (int r = 0; r < PR; r++) {
+                const int p = tid + NT * r;
+                const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+                const int tr = (MODE == DECAY_GATE && WIN) ? (row - s0) & (C - 1) : row;
+                const bool in = !(MODE == DECAY_GATE && WIN) || (row >= s0 && row < s0 + n);
+                u32x4 xq, xo, xk, xv;
+                fetch(r, row, c8, xq, xo, xk, xv);
+                const u32x4 z = {0, 0, 0, 0};
+                if (MODE == DECAY_GATE) {  // q 2^{B}; k 2^{-B}
+                    float fq[8], fk[8];
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const float b = sm.gb[row * D + c8 + e];
-                    fq[e] = __builtin_amdgcn_exp2f(b);
-                    fk[e] = __builtin_amdgcn_exp2f(-b);
+                    for (int e = 0; e < 8; e++) {
+                        const float b = sm.gb[tr * D + c8 + e];
+                        fq[e] = __builtin_amdgcn_exp2f(b);
+                        fk[e] = __builtin_amdgcn_exp2f(-b);
+                    }
+                    *(u32x4*)(&sm.qs[tr * PITCH + c8]) = in ? scale8(xq, fq) : z;
+                    if (!STATE_ONLY) *(u32x4*)(&sm.k[tr * PITCH + c8]) = in ? scale8(xk, fk) : z;
+                } else if (MODE == DECAY_HEAD) {
+                    *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(xq, sm.apow[row + 1]);
+                } else if (STATE_ONLY) {
+                    *(u32x4*)(&sm.qs[row * PITCH + c8]) = xq;
                 }
-                *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8(rq[r], fq);
-                if (!STATE_ONLY) *(u32x4*)(&sm.k[row * PITCH + c8]) = scale8(rk[r], fk);
-            } else if (MODE == DECAY_HEAD) {
-                *(u32x4*)(&sm.qs[row * PITCH + c8]) = scale8s(rq[r], sm.apow[row + 1]);
-            } else if (STATE_ONLY) {
-                *(u32x4*)(&sm.qs[row * PITCH + c8]) = rq[r];
+                *(u32x4*)(&sm.o[tr * PITCH + c8]) = in ? xo : z;
+                if (!STATE_ONLY) {
+                    if (MODE != DECAY_GATE) {
+                        *(u32x4*)(&sm.q[row * PITCH + c8]) = xq;
+                        *(u32x4*)(&sm.k[row * PITCH + c8]) = xk;
+                    }
+                    *(u32x4*)(&sm.v[tr * PITCH + c8]) = in ? xv : z;
+                }
             }
-            *(u32x4*)(&sm.o[row * PITCH + c8]) = ro[r];
+        };
+        stage([&](int r, int, int, u32x4& xq, u32x4& xo, u32x4& xk, u32x4& xv) {
+            xq = rq[r];
+            xo = ro[r];
             if (!STATE_ONLY) {
-                if (MODE != DECAY_GATE) {
-                    *(u32x4*)(&sm.q[row * PITCH + c8]) = rq[r];
-                    *(u32x4*)(&sm.k[row * PITCH + c8]) = rk[r];
-                }
-                *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
+                xk = rk[r];
+                xv = rv[r];
             }
-        }
+        });
         if (!STATE_ONLY && rank == 0) {
 #pragma unroll
             for (int m = 0; m < NCB; m++)
@@ -294,8 +373,8 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 }
         }
         __syncthreads();
-        if (PF && c > 0) load_chunk(c - 1);  // the previous chunk, while this one is computed
-        if (!STATE_ONLY && d_start && c + 1 < nchunks) {  // D here = D at the start of chunk c + 1
+        if (PF && c > 0 && wi == nwin - 1) load_chunk(c - 1);  // the previous chunk, while this one is computed
+        if (!STATE_ONLY && d_start && c + 1 < nchunks && wi == 0) {  // D here = D at the start of chunk c + 1
             __bf16* dst = d_start + (ub * nch_seg + (int64_t)g * cps + c + 1) * D * D;
 #pragma unroll
             for (int r = 0; r < (D * D / 8 + NT - 1) / NT; r++) {
@@ -458,6 +537,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 for (int ks = 0; ks < 4; ks++) Dm[m] = mfma(tr_operand(qsd, PITCH, ks, 32 * m, lane), ob[ks], Dm[m]);
             }
         }
+        }  // windows
     }
 
     // ---- the derivative at the sub-segment's start
@@ -516,9 +596,11 @@ struct DqSmem {
     float gtot[GATE ? NT : 4];
     float gel[GATE ? D : 4];        // gate: 2^{B_last}
     float apow[C + 1];              // a^m, m = 0..C (head mode)
+    int lvl;                        // gate: the chunk is taken in windows of C >> lvl tokens
 };
 
-template <int D, int MODE, bool STATE_ONLY>
+// WIN: as for bwd_dkdv_kernel.
+template <int D, int MODE, bool STATE_ONLY, bool WIN = false>
 __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ s_in,
@@ -529,8 +611,15 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     const float* __restrict__ init_state, int64_t ist_bh, int ist_g, int ist_off,
     const __bf16* __restrict__ d_start,  // gate derivative: D at every chunk's start (bf16 [D][D]), or null
     float* __restrict__ c0_out,          // gate derivative: rowsum(S (.) D) at every chunk's start ([D])
-    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm) {
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
     __shared__ __attribute__((aligned(16))) DqSmem<D, MODE, STATE_ONLY> sm;
+    if constexpr (MODE == DECAY_GATE) {
+        if constexpr (WIN) {
+            if (wide[blockIdx.x] == 0) return;
+        } else if (threadIdx.x == 0) {
+            wide[blockIdx.x] = 0;
+        }
+    }
     using Gm = Geo<D>;
     constexpr int PITCH = Gm::PITCH, PR = Gm::PR, PIECES_ROW = Gm::PIECES_ROW, NCB = Gm::NCB;
     constexpr bool PF = true;
@@ -598,8 +687,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     };
     if (PF && nchunks > 0) load_chunk(0);
     for (int c = 0; c < nchunks; c++) {
-        const int64_t t0 = t_begin + (int64_t)c * C;
-        const int n = (int)min((int64_t)C, t_end - t0);
+        const int64_t t0c = t_begin + (int64_t)c * C;
+        const int nc = (int)min((int64_t)C, t_end - t0c);
         __syncthreads();  // the previous chunk is done with every LDS tile
         if (!PF) load_chunk(c);
         // gate derivative: this thread's part of D at the chunk's start (key row tid / TPR), loaded
@@ -612,36 +701,77 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
 #pragma unroll
             for (int j = 0; j < CPT / 4; j++) dst4[j] = *(const bf16x4*)(src + 4 * j);
         }
+        // gate mode: the chunk's running log2-decay, and the windows it is taken in (one, unless its
+        // decay is too wide for the factorised pair weights; chunk_gate_windows)
+        int ws = C;
         if (MODE == DECAY_GATE) {
-            gate_chunk_logdecay<D>(rg, n, inv_norm, sm.gb, sm.gtot, sm.gel, tid);
+            if (WIN && tid == 0) sm.lvl = 0;
+            gate_chunk_logdecay<D>(rg, 0, nc, inv_norm, sm.gb, sm.gtot, sm.gel, tid);
             if (tid < D) gate_total += sm.gb[(C - 1) * D + tid];
+            if constexpr (WIN) {
+                chunk_gate_windows<D>(sm.gb, nc, &sm.lvl, tid);
+                __syncthreads();  // gel, lvl
+                ws = C >> sm.lvl;
+            } else {
+                // a chunk too wide for one piece sends the unit to the windowed instance, which
+                // overwrites all it writes (this instance finishes the unit all the same: its register
+                // allocation is left exactly as without the check)
+                if (tid < D && sm.gb[(C - 1) * D + tid] < -GATE_SPAN_LOG2) wide[blockIdx.x] = 1;
+                __syncthreads();  // gel
+            }
+        }
+        // The windows run forwards, each staged as a ragged chunk of its own (chunk row r at tile row
+        // (r - s0) mod C, the rest zero) with its first token as the decay reference, from the
+        // registers, which keep the chunk until its last window is staged.
+        const int nwin = (MODE == DECAY_GATE && WIN) ? (nc + ws - 1) / ws : 1;
+        for (int wi = 0; wi < nwin; wi++) {
+        const int s0 = (MODE == DECAY_GATE && WIN) ? wi * ws : 0;
+        const int n = (MODE == DECAY_GATE && WIN) ? min(s0 + ws, nc) - s0 : nc;
+        const int64_t t0 = t0c + s0;
+        if (MODE == DECAY_GATE && WIN && nwin > 1) {
+            if (wi > 0) __syncthreads();  // the previous window is done with every LDS tile
+            f32x4 xg[GateTile<D>::PG];  // the gate rows again (cached), not held across the windows
+            gate_load<D>(decay, row_base + t0c, nc, xg, tid);
+            gate_chunk_logdecay<D>(xg, s0, s0 + n, inv_norm, sm.gb, sm.gtot, sm.gel, tid);
             __syncthreads();  // gel
         }
+        auto stage = [&](auto fetch) {
 #pragma unroll
-        for (int r = 0; r < PR; r++) {
-            const int p = tid + NT * r;
-            const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-            *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
-            if (MODE == DECAY_GATE) {
-                float ft[8], fh[8];
+            for (int r = 0; r < PR; r++) {
+                const int p = tid + NT * r;
+                const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+                const int tr = (MODE == DECAY_GATE && WIN) ? (row - s0) & (C - 1) : row;
+                const bool in = !(MODE == DECAY_GATE && WIN) || (row >= s0 && row < s0 + n);
+                u32x4 xk, xv, xo;
+                fetch(r, row, c8, xk, xv, xo);
+                const u32x4 z = {0, 0, 0, 0};
+                *(u32x4*)(&sm.v[tr * PITCH + c8]) = in ? xv : z;
+                if (MODE == DECAY_GATE) {
+                    float ft[8], fh[8];
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const float b = sm.gb[row * D + c8 + e];
-                    ft[e] = __builtin_amdgcn_exp2f(sm.gb[(C - 1) * D + c8 + e] - b);
-                    fh[e] = __builtin_amdgcn_exp2f(-b);
+                    for (int e = 0; e < 8; e++) {
+                        const float b = sm.gb[tr * D + c8 + e];
+                        ft[e] = __builtin_amdgcn_exp2f(sm.gb[(C - 1) * D + c8 + e] - b);
+                        fh[e] = __builtin_amdgcn_exp2f(-b);
+                    }
+                    *(u32x4*)(&sm.kt[tr * PITCH + c8]) = in ? scale8(xk, ft) : z;
+                    if (!STATE_ONLY) *(u32x4*)(&sm.k[tr * PITCH + c8]) = in ? scale8(xk, fh) : z;
+                } else if (MODE == DECAY_HEAD) {
+                    *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(xk, sm.apow[max(n - 1 - row, 0)]);
+                } else {
+                    *(u32x4*)(&sm.kt[row * PITCH + c8]) = xk;
                 }
-                *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8(rk[r], ft);
-                if (!STATE_ONLY) *(u32x4*)(&sm.k[row * PITCH + c8]) = scale8(rk[r], fh);
-            } else if (MODE == DECAY_HEAD) {
-                *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(rk[r], sm.apow[max(n - 1 - row, 0)]);
-            } else {
-                *(u32x4*)(&sm.kt[row * PITCH + c8]) = rk[r];
+                if (!STATE_ONLY) {
+                    if (MODE != DECAY_GATE) *(u32x4*)(&sm.k[row * PITCH + c8]) = xk;
+                    *(u32x4*)(&sm.o[tr * PITCH + c8]) = in ? xo : z;
+                }
             }
-            if (!STATE_ONLY) {
-                if (MODE != DECAY_GATE) *(u32x4*)(&sm.k[row * PITCH + c8]) = rk[r];
-                *(u32x4*)(&sm.o[row * PITCH + c8]) = ro[r];
-            }
-        }
+        };
+        stage([&](int r, int, int, u32x4& xk, u32x4& xv, u32x4& xo) {
+            xk = rk[r];
+            xv = rv[r];
+            if (!STATE_ONLY) xo = ro[r];
+        });
         if (!STATE_ONLY && rank == 0) {
 #pragma unroll
             for (int m = 0; m < NCB; m++)
@@ -652,8 +782,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
                 }
         }
         __syncthreads();
-        if (PF && c + 1 < nchunks) load_chunk(c + 1);  // the next chunk, while this one is computed
-        if (!STATE_ONLY && c0_out) {  // rowsum(S (.) D) at this chunk's start, per key dim, from S's bf16 copy
+        if (PF && c + 1 < nchunks && wi == nwin - 1) load_chunk(c + 1);  // the next chunk, while this one is computed
+        if (!STATE_ONLY && c0_out && wi == 0) {  // rowsum(S (.) D) at this chunk's start, per key dim, from S's bf16 copy
             const int r = tid / TPR, col0 = (tid % TPR) * CPT;
             float acc = 0.f;
 #pragma unroll
@@ -753,6 +883,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
                 for (int ks = 0; ks < 4; ks++) Sm[m] = mfma(tr_operand(sm.kt, PITCH, ks, 32 * m, lane), vb[ks], Sm[m]);
             }
         }
+        }  // windows
     }
 
     if (STATE_ONLY && rank == 0) {
@@ -1116,9 +1247,11 @@ __global__ __launch_bounds__(NT) void dg_kernel(const __bf16* __restrict__ q, co
     }
 }
 
+// wide: gate mode, one int per workgroup of the largest pass (B*H*nseg*G), the flags that send a unit
+// of a pass to its windowed redo (each pass and its redo run before the next pass writes them).
 template <int D, int MODE>
 hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* f_decay, float* b_state,
-                       float* b_decay, double* intra_part, __bf16* d_start, float* c0,
+                       float* b_decay, double* intra_part, __bf16* d_start, float* c0, int* wide,
                        const float* s_scanned = nullptr) {
     const int64_t units = a.B * a.H * a.nseg;
     const __bf16* q = (const __bf16*)a.q;
@@ -1143,15 +1276,27 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
             LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
                       bwd_dq_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
                           k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr, 0,
-                          0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+                          0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
             if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (MODE == DECAY_GATE) {
+                LA_TRACED(a.tr, "chunk_bwd_dq_state_pass_windows",
+                          bwd_dq_kernel<D, MODE, true, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                              k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr,
+                              0, 0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
             if ((e = launch_state_scan(f_state, f_decay, f_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
                 return e;
         }
         LA_TRACED(a.tr, "chunk_bwd_dq",
                   bwd_dq_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
                       k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, init,
-                      ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+                      ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+        if ((e = hipGetLastError()) != hipSuccess || MODE != DECAY_GATE) return e;
+        LA_TRACED(a.tr, "chunk_bwd_dq_windows",
+                  bwd_dq_kernel<D, MODE, false, true><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                      k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, init,
+                      ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
         return hipGetLastError();
     };
     // dk, dv: backward state pass, reverse-order scan, output pass (with the gate derivative also D at
@@ -1162,15 +1307,27 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
             LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass",
                       bwd_dkdv_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
                           q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state, b_decay,
-                          nullptr, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+                          nullptr, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
             if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (MODE == DECAY_GATE) {
+                LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass_windows",
+                          bwd_dkdv_kernel<D, MODE, true, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                              q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state,
+                              b_decay, nullptr, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
             if ((e = launch_state_scan(b_state, b_decay, b_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
                 return e;
         }
         LA_TRACED(a.tr, "chunk_bwd_dkdv",
                   bwd_dkdv_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
                       q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out, a.ds_in,
-                      nullptr, nullptr, b_state, intra_part, d_start, a.H, a.L, a.nseg, G, cps, a.inv_norm));
+                      nullptr, nullptr, b_state, intra_part, d_start, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+        if ((e = hipGetLastError()) != hipSuccess || MODE != DECAY_GATE) return e;
+        LA_TRACED(a.tr, "chunk_bwd_dkdv_windows",
+                  bwd_dkdv_kernel<D, MODE, false, true><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                      q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out, a.ds_in,
+                      nullptr, nullptr, b_state, intra_part, d_start, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
         return hipGetLastError();
     };
     hipError_t e;
@@ -1219,7 +1376,9 @@ hipError_t launch_d(const BwdArgs& a) {
     const size_t n_state = (size_t)units * (G - 1) * D * D, n_decay = (size_t)units * (G - 1) * D;
     const int nsets = dlam ? 4 : 2;  // state arrays: forward, backward (+ S, St)
     const size_t n_chunks = dgate ? (size_t)units * (size_t)((a.L / a.nseg + C - 1) / C) : 0;
-    const size_t f_bytes = sizeof(double) * n_dbl + sizeof(float) * (nsets * n_state + 3 * n_decay + n_chunks * D);
+    const size_t n_wide = a.mode == DECAY_GATE ? (size_t)units * G : 0;  // the gate passes' redo flags
+    const size_t f_bytes =
+        sizeof(double) * n_dbl + sizeof(float) * (nsets * n_state + 3 * n_decay + n_chunks * D) + sizeof(int) * n_wide;
     const size_t ds_off = (f_bytes + 255) / 256 * 256;
     const size_t bytes = n_chunks ? ds_off + sizeof(__bf16) * n_chunks * D * D : f_bytes;
     char* ws = nullptr;
@@ -1240,18 +1399,21 @@ hipError_t launch_d(const BwdArgs& a) {
     float* b_decay = n_decay ? fp + nsets * n_state + n_decay : nullptr;
     float* l_decay = n_decay ? fp + nsets * n_state + 2 * n_decay : nullptr;
     float* c0 = n_chunks ? fp + nsets * n_state + 3 * n_decay : nullptr;
+    int* wide = n_wide ? (int*)(fp + nsets * n_state + 3 * n_decay + n_chunks * D) : nullptr;
     __bf16* d_start = n_chunks ? (__bf16*)(ws + ds_off) : nullptr;
     if (dlam && !a.s_sub) {  // the S scan of the d lambda_h pipeline replaces the dq passes' own
         e = launch_dlam_states<D>(a, G, cps, l_state, lt_state, l_decay);
         if (e == hipSuccess)
             e = launch_mode<D, DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra, nullptr, nullptr,
-                                           l_state);
+                                           nullptr, l_state);
     } else if (a.mode == DECAY_HEAD)
-        e = launch_mode<D, DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra, nullptr, nullptr);
+        e = launch_mode<D, DECAY_HEAD>(a, G, cps, f_state, f_decay, b_state, b_decay, intra, nullptr, nullptr,
+                                       nullptr);
     else if (a.mode == DECAY_GATE)
-        e = launch_mode<D, DECAY_GATE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr, d_start, c0);
+        e = launch_mode<D, DECAY_GATE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr, d_start, c0, wide);
     else
-        e = launch_mode<D, DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr, nullptr, nullptr);
+        e = launch_mode<D, DECAY_NONE>(a, G, cps, f_state, f_decay, b_state, b_decay, nullptr, nullptr, nullptr,
+                                       nullptr);
     if (e == hipSuccess && dlam && a.s_sub) e = launch_dlam_states<D>(a, G, cps, l_state, lt_state, l_decay);
     if (e == hipSuccess && dlam) e = launch_dlam<D>(a, G, cps, l_state, lt_state, l_decay, part, intra);
     if (ws) {

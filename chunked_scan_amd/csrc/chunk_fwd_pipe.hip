@@ -13,7 +13,10 @@
 // the per-key-dim decay inside the contraction: qbar = q*exp(B_i) (<= 1), kbar = k*exp(-B_j)
 // (>= 1, bounded by the chunk's decay span), as in the K-bar / Lambda / Gamma vectors that the
 // ZeCO review page discusses (referee_report.minor_comments[3]); its state update is written
-// S <- diag(exp(B_{n-1})) (S + Kbar^T V), which needs no third key tile.
+// S <- diag(exp(B_{n-1})) (S + Kbar^T V), which needs no third key tile.  That factorisation holds
+// while a chunk's decay stays within 2^-96 on every key dim; the loaders check each chunk, and a
+// unit (workgroup) that meets one beyond is flagged and redone by the small-head kernel
+// instantiated at d = 128, which cuts such chunks into windows (chunk_fwd_small.hip).
 //
 // The data path is designed around the MFMA register layouts so that almost nothing but MFMA
 // operands moves per chunk:
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     float* __restrict__ s_out, int64_t s_out_stride, float* __restrict__ part_state,
     float* __restrict__ part_decay, const float* __restrict__ init_state, int64_t H, int64_t L, int nseg, int G,
     int cps, float inv_norm, __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride,
-    uint8_t* __restrict__ tile_live) {
+    uint8_t* __restrict__ tile_live, int* __restrict__ wide_out) {
     constexpr bool GATE = MODE == DECAY_GATE;
     constexpr bool OTILE = !STATE_ONLY && !GATE;  // outputs leave through an LDS tile stored by the loaders
     constexpr int SLOT = STATE_ONLY ? 2 : 3;      // tiles per stage
@@ -204,6 +207,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
             if (__ballot(__builtin_amdgcn_exp2f(m) != 0.f) == 0 && lane == 0) atomicMin(&first_dead[lw], c);
         };
         int issued = 0;
+        bool wide = false;  // a chunk of this unit had a decay too wide for the one-piece factorisation
         // token row r of chunk `issued` into x (5 loads); the chunk counts as issued after row 3
         auto load_row = [&](Raw& x, int r) {
             const int n = chunk_len(issued);
@@ -283,6 +287,13 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                 *(f32x4*)(st.el + 8 * o8) = e0;
                 *(f32x4*)(st.el + 8 * o8 + 4) = e1;
             }
+            // k 2^{-B} stays within 2^96 (and q 2^{B} a normal float) only while the chunk's decay
+            // does on every key dim; a unit with a chunk beyond that is flagged and redone by a
+            // kernel that cuts such chunks into windows
+            bool fits = true;
+#pragma unroll
+            for (int e = 0; e < 8; e++) fits = fits && bl[e] >= -GATE_SPAN_LOG2;
+            wide = wide || __ballot(!fits) != 0;
             // decay from the segment start to this chunk's start (for q times the cumulative decay)
             float cf[8];
 #pragma unroll
@@ -346,6 +357,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 #pragma unroll
             for (int e = 0; e < 8; e++) tt[e] = __builtin_amdgcn_exp2f(run[e]);
         }
+        if (lane == 0) wide_out[u * 4 + lw] = wide;
         return;
     }
     if (wave >= 4) {
@@ -644,7 +656,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 }
 
 template <int MODE>
-hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
+hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay, int* wide) {
     const int64_t ub = a.B * a.H * a.nseg;
     const bool fused = MODE == DECAY_GATE;  // q times cumulative decay and the segment totals come from the loaders
     const __bf16* q = (const __bf16*)a.q;
@@ -655,9 +667,12 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
         LA_TRACED(a.tr, "chunk_fwd_pipe_state_pass",
                   pipe_fwd_kernel<MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
                       q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
-                      a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0, nullptr));
+                      a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0, nullptr, wide ? wide + 4 * ub * G : nullptr));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (MODE == DECAY_GATE &&
+            (e = launch_small_gate128_redo(a, G, cps, part_state, part_decay, true, wide + 4 * ub * G)) != hipSuccess)
+            return e;
         e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream, a.tr);
         if (e != hipSuccess) return e;
     }
@@ -665,17 +680,19 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
               pipe_fwd_kernel<MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
                   q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, part_decay, part_state, a.H, a.L,
                   a.nseg, G, cps, a.inv_norm, fused ? (__bf16*)a.q_dec : nullptr, fused ? a.total : nullptr,
-                  a.total_stride, fused ? (uint8_t*)a.tile_live : nullptr));
-    return hipGetLastError();
+                  a.total_stride, fused ? (uint8_t*)a.tile_live : nullptr, wide));
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && MODE == DECAY_GATE) e = launch_small_gate128_redo(a, G, cps, part_state, part_decay, false, wide);
+    return e;
 }
 
 }  // namespace
 
-hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
+hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay, int* wide) {
     switch (a.mode) {
-        case DECAY_HEAD: return launch_mode<DECAY_HEAD>(a, G, cps, part_state, part_decay);
-        case DECAY_GATE: return launch_mode<DECAY_GATE>(a, G, cps, part_state, part_decay);
-        default: return launch_mode<DECAY_NONE>(a, G, cps, part_state, part_decay);
+        case DECAY_HEAD: return launch_mode<DECAY_HEAD>(a, G, cps, part_state, part_decay, nullptr);
+        case DECAY_GATE: return launch_mode<DECAY_GATE>(a, G, cps, part_state, part_decay, wide);
+        default: return launch_mode<DECAY_NONE>(a, G, cps, part_state, part_decay, nullptr);
     }
 }
 

@@ -13,7 +13,10 @@
 // Gamma vectors, referee_report.minor_comments[3].)  Head and no-decay modes compute P from raw
 // q, k and apply exp(lambda (i - j)) to the scores and exp(lambda (i + 1)) to the rows of Q S, so
 // every factor is <= 1; gate mode folds the per-key-dim decay into qbar = q exp(B_i) and
-// kbar = k exp(-B_j), which bounds each chunk's per-dim log-decay sum as in the d = 128 kernel.
+// kbar = k exp(-B_j), which needs the decay over the chunk to stay within 2^-96 on every key dim:
+// a chunk beyond that is cut into the longest equal windows within it, each staged and computed as
+// a chunk of its own (with the floor on log a two-token windows always fit).  At d = 128 this
+// kernel also redoes, in windows, the units the d = 128 pipeline kernel flags as too wide.
 //
 // Wave roles.  The D / 32 value-column blocks of the outputs and of the state are spread over the
 // four waves: wave w takes column block w % (D / 32) and, of the chunk's two 32-row output blocks,
@@ -26,8 +29,7 @@
 // those congruent to its rank modulo the waves of its column block, and the ten causal score
 // blocks dealt to the waves in turn; tiles, the score tile and the token slabs of the V and K
 // operands double.  The pair weights and the state update are the same algebra over the longer
-// chunk, so in gate mode the per-key-dim decay sum that must stay above -80 is the 128-token
-// chunk's.
+// chunk (and its windows).
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -67,10 +69,12 @@ struct SmallSmem {
 template <int D, int CH>
 struct SmallSmemGate {
     float b[CH * D];           // in-chunk inclusive cumulative log2-decay
-    float el[D];               // 2^{B_{n-1}}: the chunk's total decay per key dim
+    float el[D];               // the current window's total decay per key dim
     float tot[(NT / D) * D];   // per-part totals of the cumsum
     float run[D];              // log2 decay from the segment start to the chunk start
     float cs[D];               // 2^{run}: the decay from the segment start to the chunk start
+    float wbase[D];            // B at the token before the current window (its decay reference)
+    int lvl;                   // the chunk's windows are CH >> lvl tokens long
 };
 
 template <int D, int MODE, bool STATE_ONLY, int CH>
@@ -81,7 +85,14 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
     const float* __restrict__ init_state,                            // output pass inputs (scanned)
     int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm,
-    __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride, uint32_t* __restrict__ tile_live) {
+    __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride, uint32_t* __restrict__ tile_live,
+    const int* __restrict__ only_flagged) {
+    // only_flagged (or null): redo just the units whose four flags are not all zero (the d = 128
+    // gate kernel's verdicts); the others keep what that kernel wrote
+    if (only_flagged) {
+        const int* fl = only_flagged + (int64_t)blockIdx.x * 4;
+        if ((fl[0] | fl[1] | fl[2] | fl[3]) == 0) return;
+    }
     constexpr int NCB = D / 32;       // 32-wide column blocks
     constexpr int WPC = 4 / NCB;      // waves per column block
     constexpr int KS = D / 16;        // 16-wide k slabs of a D-long contraction
@@ -179,8 +190,17 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
         const int n = (int)min((int64_t)CH, t_end - t0);
         __syncthreads();  // the previous chunk is done with every LDS tile
 
-        // ---- stage the prefetched chunk into LDS, folding in the decay factors
+        // ---- gate mode: the chunk's in-chunk cumulative log2-decay, its chunk-level outputs (the
+        // segment's running decay, q times it, the tile flag) and the window length.  A chunk whose
+        // decay over its whole length stays within GATE_SPAN_LOG2 on every key dim is one window
+        // (the common case); otherwise it is cut into the longest equal windows that each stay
+        // within it, and every window is staged and computed as a chunk of its own, from the state
+        // the previous window leaves (the per-token floor on log a makes two-token windows always
+        // fit).  The pair weights 2^{B_i - B_j} of a window are then exact products of
+        // q 2^{B_i} <= 1 and k 2^{-B_j} <= 2^{GATE_SPAN_LOG2}.
+        int ws = CH;
         if (MODE == DECAY_GATE) {
+            if (tid == 0) sg.lvl = 0;
 #pragma unroll
             for (int r = 0; r < PG; r++) {
                 const int p = tid + NT * r;
@@ -209,13 +229,26 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
                 bool live = false;
                 if (tid < D) {
                     const float bl = sg.b[(n - 1) * D + tid];
-                    sg.el[tid] = __builtin_amdgcn_exp2f(bl);
                     gate_total += bl;
                     if (qdec_out) {
                         const float cs = __builtin_amdgcn_exp2f(sg.run[tid]);
                         sg.cs[tid] = cs;
                         sg.run[tid] += bl;
                         live = cs != 0.f;
+                    }
+                    // the window length this key dim needs
+                    int lv = 0;
+                    if (bl < -GATE_SPAN_LOG2) {
+                        for (lv = 1; (CH >> lv) > 1; lv++) {
+                            const int wl = CH >> lv;
+                            bool fits = true;
+                            for (int s0 = 0; s0 < n && fits; s0 += wl) {
+                                const float base = s0 ? sg.b[(s0 - 1) * D + tid] : 0.f;
+                                fits = sg.b[(min(s0 + wl, n) - 1) * D + tid] - base >= -GATE_SPAN_LOG2;
+                            }
+                            if (fits) break;
+                        }
+                        atomicMax(&sg.lvl, lv);
                     }
                 }
                 // the chunk's tile flag: q times the cumulative decay is exactly zero on the whole
@@ -226,30 +259,73 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
                     if (tile < tps) tile_live[(bh * nseg + seg) * tps + tile] = any_live ? 0x01010101u : 0u;
                 }
             }
+            ws = CH >> sg.lvl;
+        }
+
+        const int nwin = (MODE == DECAY_GATE) ? (n + ws - 1) / ws : 1;
+        for (int wi = 0; wi < nwin; wi++) {
+        const int s0 = wi * ws, s1 = min(s0 + ws, n);  // this window: the chunk's rows s0 .. s1 - 1
+        const int nw = (MODE == DECAY_GATE) ? s1 - s0 : n;
+        const int64_t tw = t0 + s0;
+        if (wi > 0) __syncthreads();  // the previous window is done with every LDS tile
+
+        // ---- stage the window into LDS tile rows 0 .. nw - 1 (the rest zero), folding in the decay
+        // factors; chunk row `row` goes to tile row (row - s0) mod CH.  The first window comes from
+        // the prefetch registers, later ones (a chunk cut into windows) reload their rows, which the
+        // prefetch of the next chunk has replaced by then.
+        if (MODE == DECAY_GATE) {
+            if (tid < D) {  // the window's decay reference and total decay
+                const float base = s0 ? sg.b[(s0 - 1) * D + tid] : 0.f;
+                sg.wbase[tid] = base;
+                sg.el[tid] = __builtin_amdgcn_exp2f(sg.b[(s1 - 1) * D + tid] - base);
+            }
+            __syncthreads();
+            auto stage_gate = [&](const u32x4* xq, const u32x4* xk, const u32x4* xv) {
 #pragma unroll
-            for (int r = 0; r < PR; r++) {
-                const int p = tid + NT * r;
-                const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
-                float eb[8], einv[8], et[8];
+                for (int r = 0; r < PR; r++) {
+                    const int p = tid + NT * r;
+                    const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+                    const int tr = (row - s0) & (CH - 1);
+                    const bool in = row >= s0 && row < s1;
+                    float eb[8], einv[8], et[8];
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const float bi = sg.b[row * D + c8 + e];
-                    eb[e] = __builtin_amdgcn_exp2f(bi);
-                    einv[e] = __builtin_amdgcn_exp2f(-bi);
-                    et[e] = sg.el[c8 + e] * einv[e];
-                }
-                if (!STATE_ONLY) {
-                    *(u32x4*)(&sm.q[row * PITCH + c8]) = scale8(rq[r], eb);
-                    *(u32x4*)(&sm.kp[row * PITCH + c8]) = scale8(rk[r], einv);
-                    if (q_dec && row < n) {  // q times its cumulative decay from the segment start
-                        float fd[8];
-#pragma unroll
-                        for (int e = 0; e < 8; e++) fd[e] = eb[e] * sg.cs[c8 + e];
-                        *(u32x4*)(q_dec + (row_base + t0) * D + (row * D + c8)) = scale8(rq[r], fd);
+                    for (int e = 0; e < 8; e++) {
+                        const float bi = sg.b[row * D + c8 + e] - sg.wbase[c8 + e];
+                        eb[e] = __builtin_amdgcn_exp2f(bi);
+                        einv[e] = __builtin_amdgcn_exp2f(-bi);
+                        et[e] = sg.el[c8 + e] * einv[e];
                     }
+                    const u32x4 z = {0, 0, 0, 0};
+                    if (!STATE_ONLY) {
+                        *(u32x4*)(&sm.q[tr * PITCH + c8]) = in ? scale8(xq[r], eb) : z;
+                        *(u32x4*)(&sm.kp[tr * PITCH + c8]) = in ? scale8(xk[r], einv) : z;
+                        if (q_dec && in) {  // q times its cumulative decay from the segment start
+                            float fd[8];
+#pragma unroll
+                            for (int e = 0; e < 8; e++)
+                                fd[e] = (s0 ? __builtin_amdgcn_exp2f(sg.b[row * D + c8 + e]) : eb[e]) * sg.cs[c8 + e];
+                            *(u32x4*)(q_dec + (row_base + t0) * D + (row * D + c8)) = scale8(xq[r], fd);
+                        }
+                    }
+                    *(u32x4*)(&sm.kt[tr * PITCH + c8]) = in ? scale8(xk[r], et) : z;
+                    *(u32x4*)(&sm.v[tr * PITCH + c8]) = in ? xv[r] : z;
                 }
-                *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8(rk[r], et);
-                *(u32x4*)(&sm.v[row * PITCH + c8]) = rv[r];
+            };
+            if (wi == 0) {
+                stage_gate(rq, rk, rv);
+            } else {
+                u32x4 xq[PR], xk[PR], xv[PR];
+#pragma unroll
+                for (int r = 0; r < PR; r++) {
+                    const int p = tid + NT * r;
+                    const int row = p / PIECES_ROW, c8 = (p % PIECES_ROW) * 8;
+                    const int64_t off = (row_base + t0 + row) * D + c8;
+                    const bool ok = row >= s0 && row < s1;
+                    xq[r] = (ok && !STATE_ONLY) ? *(const u32x4*)(q + off) : u32x4{0, 0, 0, 0};
+                    xk[r] = ok ? *(const u32x4*)(k + off) : u32x4{0, 0, 0, 0};
+                    xv[r] = ok ? *(const u32x4*)(v + off) : u32x4{0, 0, 0, 0};
+                }
+                stage_gate(xq, xk, xv);
             }
         } else {
 #pragma unroll
@@ -270,7 +346,7 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
         __syncthreads();
 
         // ---- prefetch the next chunk while this one is computed
-        if (c + 1 < nchunks) load_chunk(t0 + CH, (int)min((int64_t)CH, t_end - (t0 + CH)));
+        if (wi == 0 && c + 1 < nchunks) load_chunk(t0 + CH, (int)min((int64_t)CH, t_end - (t0 + CH)));
 
         // ---- V operand of this wave's 32 value columns, for the chunk's token slabs (P V and K^T V)
         bf16x8 vb[NSLAB];
@@ -355,16 +431,16 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
                     acc = mfma(a, vb[ks], acc);
                 }
                 // accumulator i: row rb*32 + (i/4)*8 + kg*4 + i%4, column 32 cb + n32
-                __bf16* orow = o + (row_base + t0 + rb * 32) * D + 32 * cb + n32;
+                __bf16* orow = o + (row_base + tw + rb * 32) * D + 32 * cb + n32;
 #pragma unroll
                 for (int i = 0; i < 16; i++) {
                     const int row = (i >> 2) * 8 + kg * 4 + (i & 3);
-                    if (rb * 32 + row < n) orow[row * D] = (__bf16)acc[i];
+                    if (rb * 32 + row < nw) orow[row * D] = (__bf16)acc[i];
                 }
             }
         }
 
-        // ---- state update: S <- diag(decay over the chunk) S + Ktilde^T V
+        // ---- state update: S <- diag(decay over the window) S + Ktilde^T V
         {
             const float fh = (MODE == DECAY_HEAD) ? decay_pow(lam, n) : 1.f;
             const int G16 = lane >> 4, i16 = lane & 15;
@@ -386,6 +462,7 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
                 }
             }
         }
+        }  // windows
     }
 
     // ---- the final state, from one wave per column block
@@ -424,7 +501,7 @@ hipError_t launch_small_mode(const FwdArgs& a, int G, int cps, float* part_state
         LA_TRACED(a.tr, "chunk_fwd_small_state_pass",
                   small_fwd_kernel<D, MODE, true, CH><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
                       q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
-                      a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0, nullptr));
+                      a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0, nullptr, nullptr));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream, a.tr);
@@ -434,7 +511,7 @@ hipError_t launch_small_mode(const FwdArgs& a, int G, int cps, float* part_state
               small_fwd_kernel<D, MODE, false, CH><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
                   q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, part_decay, part_state, a.H, a.L,
                   a.nseg, G, cps, a.inv_norm, fused ? (__bf16*)a.q_dec : nullptr, fused ? a.total : nullptr,
-                  a.total_stride, fused ? a.tile_live : nullptr));
+                  a.total_stride, fused ? a.tile_live : nullptr, nullptr));
     return hipGetLastError();
 }
 
@@ -452,6 +529,32 @@ hipError_t launch_small_d(const FwdArgs& a, int G, int cps, float* part_state, f
 hipError_t launch_chunk_fwd_small(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay) {
     if (a.dk == 64) return launch_small_d<64, 64>(a, G, cps, part_state, part_decay);
     return launch_small_d<32, 64>(a, G, cps, part_state, part_decay);
+}
+
+// The d = 128 gate pass (state pass when state_only) again for the units whose flags are set: the
+// units where the matrix-core d = 128 kernel met a chunk whose decay is too wide for its one-piece
+// factorisation (this kernel cuts such chunks into windows).  Same grid and arguments as that pass.
+hipError_t launch_small_gate128_redo(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay,
+                                     bool state_only, const int* flags) {
+    constexpr int D = 128;
+    const int64_t ub = a.B * a.H * a.nseg;
+    const __bf16* q = (const __bf16*)a.q;
+    const __bf16* k = (const __bf16*)a.k;
+    const __bf16* v = (const __bf16*)a.v;
+    __bf16* o = (__bf16*)a.o;
+    if (state_only) {
+        LA_TRACED(a.tr, "chunk_fwd_gate_redo_state_pass",
+                  small_fwd_kernel<D, DECAY_GATE, true, 64><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
+                      q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
+                      a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0, nullptr, flags));
+    } else {
+        LA_TRACED(a.tr, "chunk_fwd_gate_redo_output_pass",
+                  small_fwd_kernel<D, DECAY_GATE, false, 64><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
+                      q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, part_decay, part_state, a.H,
+                      a.L, a.nseg, G, cps, a.inv_norm, (__bf16*)a.q_dec, a.total, a.total_stride, a.tile_live,
+                      flags));
+    }
+    return hipGetLastError();
 }
 
 // 128-token chunks: G sub-segments of cps 128-token chunks (the split is chosen by the caller,

@@ -90,12 +90,18 @@ void fwd_split_plan(const FwdArgs& a, int* G_out, int* cps_out) {
 }
 
 // Floats of workspace for G sub-segments per segment: a state and a decay vector for every
-// sub-segment but the last of every (b, h, segment).
+// sub-segment but the last of every (b, h, segment); with the d = 128 gate kernel also four int flags
+// per workgroup of its two passes (the units it hands to the windowed redo).
+static size_t gate_flag_words(const FwdArgs& a, int G) {
+    return (a.mode == DECAY_GATE && a.dk == 128 && a.chunk == 64) ? 4 * (size_t)(a.B * a.H * a.nseg) * (2 * G - 1)
+                                                                   : 0;
+}
 size_t fwd_split_workspace_floats(const FwdArgs& a, int G) {
-    if (G <= 1) return 0;
+    const size_t flags = gate_flag_words(a, G);
+    if (G <= 1) return flags;
     const size_t n = (size_t)(a.B * a.H * a.nseg) * (size_t)(G - 1);
     const size_t D = (size_t)a.dk;
-    return n * D * D + n * D;
+    return n * D * D + n * D + flags;
 }
 
 namespace {
@@ -103,10 +109,12 @@ namespace {
 // The kernels of the split forward with the workspace at ws (fwd_split_workspace_floats floats;
 // unused when G == 1).
 hipError_t fwd_split_run(const FwdArgs& a, int G, int cps, float* ws) {
+    const size_t n = G > 1 ? (size_t)(a.B * a.H * a.nseg) * (size_t)(G - 1) : 0;
     float* part_state = G > 1 ? ws : nullptr;
-    float* part_decay = G > 1 ? ws + (size_t)(a.B * a.H * a.nseg) * (size_t)(G - 1) * a.dk * a.dk : nullptr;
+    float* part_decay = G > 1 ? ws + n * a.dk * a.dk : nullptr;
+    int* flags = gate_flag_words(a, G) ? (int*)(ws + n * a.dk * a.dk + n * a.dk) : nullptr;
     if (a.chunk == 128) return launch_chunk_fwd_small_ch128(a, G, cps, part_state, part_decay);
-    return a.dk == 128 ? launch_chunk_fwd_pipe(a, G, cps, part_state, part_decay)
+    return a.dk == 128 ? launch_chunk_fwd_pipe(a, G, cps, part_state, part_decay, flags)
                        : launch_chunk_fwd_small(a, G, cps, part_state, part_decay);
 }
 
@@ -184,7 +192,7 @@ hipError_t launch_chunk_fwd_mfma_noalloc(const FwdArgs& a) {
     fwd_split_plan(a, &G, &cps);
     if (fwd_split_workspace_floats(a, G) * sizeof(float) > LA_NOALLOC_SCRATCH_BYTES) return hipErrorInvalidValue;
     float* ws = nullptr;
-    if (G > 1) {
+    if (fwd_split_workspace_floats(a, G) > 0) {
         hipError_t e = hipSuccess;
         ws = noalloc_ptr(&e);
         if (!ws) return e;

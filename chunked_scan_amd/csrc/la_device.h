@@ -49,15 +49,27 @@ template <> struct io<__bf16> {
     __device__ static __forceinline__ void st(__bf16* p, float x) { *p = (__bf16)x; }
 };
 
+// Floor on the per-token log-decay of the gate mode (natural log): a_t >= e^-33 ~ 4.7e-15.  A
+// decay below it (down to a = 0, g = -inf) is raised to it, which moves every token-pair weight
+// prod a_s by at most e^-33 in absolute terms -- far below fp32 resolution of any output -- and
+// keeps every cumulative log-decay finite, so no difference of two of them is -inf - -inf.  With
+// it, any two consecutive tokens decay by at least 2^-95.3, inside the 2^-96 span the
+// matrix-core kernels' factorised pair weights accept (GATE_SPAN_LOG2).
+constexpr float GATE_LOG_FLOOR = -33.f;
+// Largest decay span, in log2, that one factorisation reference may cover: a key scaled by
+// 2^{+96} and a query by 2^{-96} stay normal floats (and bf16) for |q|, |k| in [2^-30, 2^31].
+constexpr float GATE_SPAN_LOG2 = 96.f;
+
 // Per-token log-decay of the gate mode: log sigmoid(g) / norm = -softplus(-g) / norm, written
 // so that neither branch overflows: softplus(x) = max(x, 0) + log(1 + exp(-|x|)).  The hardware
 // base-2 exponential and logarithm (about 1 ulp each) evaluate it; 1 + exp(-|x|) lies in (1, 2],
 // so rounding it costs at most 2^-24 in absolute terms, which is what the cumulative sums see.
+// The result is floored at GATE_LOG_FLOOR (g = -inf gives the floor, not -inf).
 __device__ __forceinline__ float gate_logdecay(float g, float inv_norm) {
     const float x = -g;
     const float y = __builtin_amdgcn_exp2f(-fabsf(x) * LOG2E);
     const float sp = fmaxf(x, 0.f) + LN2 * __builtin_amdgcn_logf(1.f + y);
-    return -sp * inv_norm;
+    return fmaxf(-sp * inv_norm, GATE_LOG_FLOOR);
 }
 
 // a^m for a per-token log-decay lam and a token distance m >= 0, with a^0 = 1 exactly even when

@@ -138,10 +138,15 @@ void mfma_split(const FwdArgs& a, int* G_out, int* cps_out, int64_t target = 256
 void fwd_split_plan(const FwdArgs& a, int* G_out, int* cps_out);
 size_t fwd_split_workspace_floats(const FwdArgs& a, int G);
 // Its kernels: G sub-segments of cps chunks; part_state / part_decay the workspace of the
-// sub-segment scan (unused when G == 1).
-hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
+// sub-segment scan (unused when G == 1); gate mode: wide the 4 * B*H*nseg * (2G - 1) ints of the
+// per-unit flags that send a unit to the windowed redo (unused otherwise).
+hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay, int* wide);
 // The same for dk = dv = 32 or 64 (chunk_fwd_small.hip).
 hipError_t launch_chunk_fwd_small(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
+// The d = 128 gate output pass (or state pass) on the small-head kernel for the units whose four
+// int flags (flags + 4 * unit) are not all zero; the others are left as they are.
+hipError_t launch_small_gate128_redo(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay,
+                                     bool state_only, const int* flags);
 // The same with 128-token chunks (cps counts 128-token chunks).
 hipError_t launch_chunk_fwd_small_ch128(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
 

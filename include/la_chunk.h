@@ -125,11 +125,12 @@ typedef struct la_shape {
  *            at s_out + (b*H + h) * state_stride + p * dk * dv (dense [B,H,nseg,dk,dv] when
  *            state_stride = 0); must not overlap any other argument.
  *   chunk  : chunk length in tokens: 16, 32 or 64 (64 is the production size), or 128 for bf16
- *            with dk = dv in {32, 64} (the chunk-length variant, on the matrix-core kernels; in
- *            gate mode the -80 bound below then applies to each 128-token chunk).
- * A partial last chunk (L/nseg not a multiple of chunk) is allowed.  In gate mode the
- * per-chunk, per-key-dim log-decay sum must stay above -80 (strong enough decays would push the
- * chunk-relative key scaling outside float range).
+ *            with dk = dv in {32, 64} (the chunk-length variant, on the matrix-core kernels).
+ * A partial last chunk (L/nseg not a multiple of chunk) is allowed.  Gate mode takes any gate
+ * value, g = -inf (a = 0) included: each token's log-decay is floored at -33 (a >= e^-33, which
+ * moves every token-pair weight by at most e^-33), and a chunk whose decay is too wide for the
+ * matrix-core kernels' factorised pair weights (beyond 2^-96 on some key dim) is taken in shorter
+ * windows (down to two tokens) by a windowed variant of the same kernels.
  * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_DECAY, LA_ERR_ALIAS,
  * LA_ERR_UNSUPPORTED or LA_ERR_LAUNCH.
  */
@@ -214,9 +215,9 @@ la_status la_chunk_fwd_decayed(const void* q, const void* k, const void* v, cons
  * and chunk 64 run on the matrix cores (bf16 operands, fp32 accumulation) in every decay mode: the
  * head-decay derivative is summed token pair by token pair (fp64 partial sums), the gate derivative
  * per chunk from rowsum(S (.) D) at the chunk's start plus an in-chunk running sum of
- * k (.) dk - q (.) dq; in gate mode, as in la_chunk_fwd, each chunk's per-key-dim log-decay sum must
- * stay above -80 there.  Every other shape and fp32 inputs run in fp32 arithmetic, with no such
- * range limit.  bf16 outputs are rounded once, to nearest even.  May allocate temporary device
+ * k (.) dk - q (.) dq; gate mode takes any gate value as in la_chunk_fwd (the same floor on log a,
+ * the same windows for chunks too wide for one factorisation).  Every other shape and fp32 inputs
+ * run in fp32 arithmetic.  bf16 outputs are rounded once, to nearest even.  May allocate temporary device
  * workspace from the same stream-ordered pool as la_chunk_fwd (per sub-segment states; for the gate
  * derivative a bf16 d_k x d_v matrix and d_k floats per chunk on the matrix cores, a float per token
  * and key dim on the fp32 path).

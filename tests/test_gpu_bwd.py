@@ -1,10 +1,13 @@
 """GPU parity of the backward pass (la_chunk_bwd) against the fp64 oracle's token-by-token
 derivatives (oracle.recurrence_bwd), on the same seeded inputs.
 
-The kernels form the decay derivative from q * dq - k * dk and reverse running sums; the oracle
-takes it from the definition (da_t = rowsum(G_t * S_{t-1}) and the chain rule), so these tests
-also check that identity.  Sizes span several chunks, a ragged last chunk, both slicings of the
-state (dk, dv up to 128) and two segments.
+The kernels form the decay derivative in three ways: the fp32 path from q * dq - k * dk and reverse
+running sums over the segment; the matrix-core path for a head decay pair by pair of tokens (with
+dS/dlambda carried beside S); the matrix-core path for the gate per chunk, from rowsum(S * D) at the
+chunk's start plus an in-chunk running sum of k * dk - q * dq.  The oracle takes it from the
+definition (da_t = rowsum(G_t * S_{t-1}) and the chain rule), so these tests also check those
+identities.  Sizes span several chunks, a ragged last chunk, both slicings of the state (dk, dv up
+to 128) and two segments.
 """
 import numpy as np
 import pytest
@@ -189,10 +192,10 @@ def test_bwd_gate_strong_decay(dtype):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_matrix_core_gate_strong_decay_within_range(d):
-    """The matrix-core gate path factorises every chunk's pair weights, which bounds the chunk's
-    decay sum per key dim from below (-80): key dims 0..7 here decay by about -0.875 per token
-    (g = -14), -56 over a chunk, the others as drawn; every derivative, dg included, against the
-    oracle."""
+    """Key dims 0..7 here decay by about -0.875 per token (g = -14), -56 over a chunk (2^-80.8),
+    the others as drawn: still inside the span one factorisation reference covers (2^-96), so every
+    chunk stays in one piece; every derivative, dg included, against the oracle (wider decays:
+    test_gpu_gate_range.py)."""
     note(f"la_chunk_bwd bf16 d={d} matrix-core gate, chunk decay sums near -56 on 8 key dims")
     w, inp, gr = _case("gate", "bf16", d, d, 300, 64, 1, seed=93 + d, B=1, H=2)
     inp["decay"][..., :8] = -14.0
