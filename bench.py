@@ -61,7 +61,29 @@ def algorithmic(w, mode_bytes_gate: int):
     return by, fl
 
 
-def kernel_roofline(w, step, kernels):
+def live_correction_tokens(w, seg_len: int, nseg_corr: int, inp=None) -> int:
+    """Tokens the head-decay correction actually touches: per segment and head, the 64-token tiles
+    whose cumulative decay exp(lambda (64 i + 1)) at their first token is nonzero in fp32 (the
+    kernel's own test; the others' correction is exactly zero and they are skipped).  Other modes:
+    every token."""
+    import numpy as np
+
+    total = w.B * w.H * seg_len * nseg_corr
+    if w.mode != "head" or inp is None:
+        return total
+    lam = inp["decay"].float().cpu().numpy()
+    tiles = (seg_len + 63) // 64
+    tau0 = (np.arange(tiles, dtype=np.float32) * 64 + 1).astype(np.float32)
+    live = 0
+    for h in range(w.H):
+        with np.errstate(under="ignore"):
+            alive = np.exp(np.float32(lam[h]) * tau0) != 0
+        n = int(alive.sum())
+        live += min(n * 64, seg_len)
+    return w.B * live * nseg_corr
+
+
+def kernel_roofline(w, step, kernels, inp=None):
     """Adds algorithmic bytes per launch, achieved GB/s and the fraction of the 8 TB/s peak to the
     forward's output pass, the state scan and the correction (their per-unit figures: q, k, v read
     and o written (+ g in gate mode) per token-head; P states read and written (+ their decay
@@ -70,10 +92,12 @@ def kernel_roofline(w, step, kernels):
     bh = w.B * w.H
     state = w.dk * w.dv * 4
     nseg = getattr(step, "nseg", None)
-    if nseg is None:  # device step: G sub-segments, scan over G + 1 entries, every token corrected
-        P, corrected, nstates = step.G + 1, w.B * w.H * w.L, step.G
-    else:             # segmented pass: P segments, segments 1.. corrected
-        P, corrected, nstates = nseg, w.B * w.H * (w.L // nseg) * (nseg - 1), nseg - 1
+    if nseg is None:  # device step: G sub-segments, scan over G + 1 entries, every live token corrected
+        P, nstates = step.G + 1, step.G
+        corrected = live_correction_tokens(w, w.L // step.G, step.G, inp)
+    else:             # segmented pass: P segments, the live tokens of segments 1.. corrected
+        P, nstates = nseg, nseg - 1
+        corrected = live_correction_tokens(w, w.L // nseg, nseg - 1, inp)
     fwd = w.B * w.H * w.L * (es * (2 * w.dk + 2 * w.dv) + (4 * w.dk if w.mode == "gate" else 0))
     scan = bh * P * (2 * state + (4 * w.dk if w.mode != "none" else 0))
     corr = corrected * es * (w.dk + 2 * w.dv) + bh * nstates * state
@@ -341,6 +365,29 @@ def state_size_sweep(stream):
     return out
 
 
+def host_cpu():
+    """(threads to use, cores in this process's affinity mask, CPU model name): the oracle runs on
+    every core of the affinity mask, or on the job's CPU share when OMP_NUM_THREADS states one."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = os.cpu_count() or 1
+    threads = aff
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and 0 < int(share) < aff:
+        threads = int(share)
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, aff, model
+
+
 def cpu_baseline(w, inp):
     import numpy as np
     import torch
@@ -348,7 +395,7 @@ def cpu_baseline(w, inp):
     import oracle
     from oracle import HEAD, NONE, GATE
 
-    threads = min(16, oracle.default_threads())
+    threads, aff, model = host_cpu()
     f32 = lambda t: None if t is None else t.to("cpu", torch.float32).numpy()  # noqa: E731
     q, k, v = f32(inp["q"]), f32(inp["k"]), f32(inp["v"])
     mode = {"none": NONE, "head": HEAD, "gate": GATE}[w.mode]
@@ -365,9 +412,10 @@ def cpu_baseline(w, inp):
     items = w.B * w.H * ((w.dv + 15) // 16)
     used = min(threads, items)
     return dict(value=reps * w.B * w.L / dt, unit="tokens/s", cores=used, kind="oracle",
+                affinity_cores=aff, cpu_model=model,
                 sample=f"whole workload (B={w.B} H={w.H} L={w.L} d={w.dk}) x {reps} repetitions, fp64 "
-                       f"token-by-token recurrence in C, {dt:.1f} s on {used} threads "
-                       f"({platform.processor() or 'host'})"), (o_ref, s_ref)
+                       f"token-by-token recurrence in C, {dt:.1f} s on {used} threads ({aff} cores in the "
+                       f"affinity mask; {model})"), (o_ref, s_ref)
 
 
 def cpu_baseline_backward(w, sample_len: int = 2048):
@@ -384,7 +432,7 @@ def cpu_baseline_backward(w, sample_len: int = 2048):
     ws = w.scaled(L=sample_len)
     inp = make_inputs(ws, "cpu")
     gr = make_grads(ws)
-    threads = min(16, oracle.default_threads())
+    threads, aff, model = host_cpu()
     f32 = lambda t: None if t is None else t.to(torch.float32).numpy()  # noqa: E731
     mode = {"none": NONE, "head": HEAD, "gate": GATE}[w.mode]
     s_in = None if inp["s_in"] is None else f32(inp["s_in"]).astype(np.float64)
@@ -400,8 +448,9 @@ def cpu_baseline_backward(w, sample_len: int = 2048):
             break
     used = min(threads, ws.B * ws.H)
     return dict(value=reps * ws.B * sample_len / dt, unit="tokens/s", cores=used, kind="oracle",
+                affinity_cores=aff, cpu_model=model,
                 sample=f"backward of B={ws.B} H={ws.H} d={ws.dk}, first {sample_len} tokens x {reps} repetitions, "
-                       f"fp64 token-by-token derivatives in C, {dt:.1f} s on {used} threads")
+                       f"fp64 token-by-token derivatives in C, {dt:.1f} s on {used} threads ({model})")
 
 
 def main():
@@ -472,7 +521,7 @@ def main():
 
     # --- the same steps with HIP events around every kernel (la_trace)
     kernels, ms_traced = kernel_stats(step, args.steps, stream)
-    kernel_roofline(w, step, kernels)
+    kernel_roofline(w, step, kernels, inp)
     log("[bench] per kernel: " + ", ".join(f"{n} {d['mean_us']:.1f} us" + (f" ({d['hbm_frac']:.2f} of HBM peak)"
                                                                          if "hbm_frac" in d else "")
                                           for n, d in kernels.items()))
@@ -507,7 +556,7 @@ def main():
             n_al = 10 if wa.nseg > 1 else 50
             st = step_stats(sa, n_al, stream)
             ks, _ = kernel_stats(sa, n_al, stream)
-            kernel_roofline(wa, sa, ks)
+            kernel_roofline(wa, sa, ks, ia)
             alongside[wa.name] = dict(
                 step=("segmented pass over %d segments" % wa.nseg) if wa.nseg > 1 else "device step",
                 B=wa.B, H=wa.H, L=wa.L, decay=wa.decay, tokens_per_s=round(wa.B * wa.L / (st["median_us"] * 1e-6), 1),

@@ -26,7 +26,7 @@ STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_SHAPE", -3: "LA_ERR_DTYPE",
           -5: "LA_ERR_UNSUPPORTED", -6: "LA_ERR_LAUNCH", -7: "LA_ERR_DECAY", -8: "LA_ERR_WORKSPACE"}
 NOALLOC_SCRATCH_BYTES = 32 << 20  # LA_NOALLOC_SCRATCH_BYTES of la_chunk.h
 EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_noalloc", "la_chunk_fwd_decayed", "la_chunk_bwd", "la_chunk_bwd_states", "la_state_scan", "la_state_correct", "la_state_correct_live",
-           "la_cumdecay", "la_status_str", "la_supported", "la_version")
+           "la_cumdecay", "la_trim_workspace", "la_status_str", "la_supported", "la_version")
 
 
 TRACE_MAX = 16
@@ -102,7 +102,8 @@ def lib() -> ctypes.CDLL:
         L.la_supported.argtypes = [S, ctypes.c_int32]
         L.la_status_str.argtypes = [ctypes.c_int]
         L.la_status_str.restype = ctypes.c_char_p
-        for f in (L.la_chunk_fwd, L.la_chunk_fwd_noalloc, L.la_chunk_fwd_decayed, L.la_state_scan, L.la_state_correct,
+        L.la_trim_workspace.argtypes = []
+        for f in (L.la_chunk_fwd, L.la_chunk_fwd_noalloc, L.la_chunk_fwd_decayed, L.la_trim_workspace, L.la_state_scan, L.la_state_correct,
                   L.la_state_correct_live, L.la_cumdecay, L.la_supported, L.la_version):
             f.restype = ctypes.c_int
         _lib = L
@@ -413,3 +414,8 @@ def la_cumdecay(decay: Optional[torch.Tensor], B: int, H: int, L: int, dk: int, 
                      stream=_stream(stream), timer=timer)
     _check("la_cumdecay", lib().la_cumdecay(_ptr(decay), _ptr(cum), _ptr(total), ctypes.byref(shp)))
     return cum, total
+
+
+def la_trim_workspace() -> None:
+    """Return the current device's unused workspace-pool memory to the device."""
+    _check("la_trim_workspace", lib().la_trim_workspace())

@@ -507,12 +507,7 @@ hipError_t launch_chunk_bwd_generic(const BwdArgs& a) {
     if (a.d_decay && a.mode == DECAY_HEAD) nfloat = (size_t)(units * nsl * 4);  // two doubles per workgroup
     float* ws = nullptr;
     if (nfloat > 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        hipMemPool_t pool = workspace_pool(dev);
-        if (!pool) return hipErrorOutOfMemory;
-        e = hipMallocFromPoolAsync((void**)&ws, nfloat * sizeof(float), pool, a.stream);
+        hipError_t e = workspace_alloc((void**)&ws, nfloat * sizeof(float), a.stream);
         if (e != hipSuccess) return e;
     }
     float *qdq = nullptr, *efin = nullptr;

@@ -1382,12 +1382,8 @@ hipError_t launch_d(const BwdArgs& a) {
     const size_t ds_off = (f_bytes + 255) / 256 * 256;
     const size_t bytes = n_chunks ? ds_off + sizeof(__bf16) * n_chunks * D * D : f_bytes;
     char* ws = nullptr;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    hipMemPool_t pool = workspace_pool(dev);
-    if (!pool) return hipErrorOutOfMemory;
-    if (bytes > 0 && (e = hipMallocFromPoolAsync((void**)&ws, bytes, pool, a.stream)) != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (bytes > 0 && (e = workspace_alloc((void**)&ws, bytes, a.stream)) != hipSuccess) return e;
     double* part = n_dbl ? (double*)ws : nullptr;
     double* intra = n_dbl ? part + (size_t)units * G : nullptr;
     float* fp = (float*)(ws + sizeof(double) * n_dbl);

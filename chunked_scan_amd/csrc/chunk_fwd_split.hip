@@ -25,6 +25,7 @@ constexpr int C = 64;  // chunk length
 
 // One stream-ordered memory pool per device for temporary workspace; it keeps what it has
 // allocated (release threshold = max), so after the first call no allocation reaches the driver.
+// la_trim_workspace hands what is not in use back to the device.
 hipMemPool_t workspace_pool(int dev) {
     static std::mutex mu;
     static hipMemPool_t pools[64] = {};
@@ -43,6 +44,24 @@ hipMemPool_t workspace_pool(int dev) {
         pools[dev] = p;
     }
     return pools[dev];
+}
+
+hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    hipMemPool_t pool = workspace_pool(dev);
+    if (!pool) return hipErrorOutOfMemory;
+    return hipMallocFromPoolAsync(p, bytes, pool, stream);
+}
+
+hipError_t workspace_trim() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    hipMemPool_t pool = workspace_pool(dev);
+    if (!pool) return hipErrorOutOfMemory;
+    return hipMemPoolTrimTo(pool, 0);
 }
 
 // Sub-segments: about `target` workgroups in total (256: one round on the compute units), at
@@ -126,12 +145,7 @@ hipError_t launch_chunk_fwd_mfma(const FwdArgs& a) {
     const size_t nf = fwd_split_workspace_floats(a, G);
     float* ws = nullptr;
     if (nf > 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        hipMemPool_t pool = workspace_pool(dev);
-        if (!pool) return hipErrorOutOfMemory;
-        e = hipMallocFromPoolAsync((void**)&ws, nf * sizeof(float), pool, a.stream);
+        hipError_t e = workspace_alloc((void**)&ws, nf * sizeof(float), a.stream);
         if (e != hipSuccess) return e;
     }
     hipError_t e = fwd_split_run(a, G, cps, ws);

@@ -149,7 +149,9 @@ la::Tracer make_tracer(const la_shape* s) {
 
 extern "C" {
 
-int32_t la_version(void) { return (1 << 16) | 0; }
+int32_t la_version(void) { return (1 << 16) | 1; }
+
+la_status la_trim_workspace(void) { return from_hip(la::workspace_trim()); }
 
 const char* la_status_str(la_status s) {
     switch (s) {

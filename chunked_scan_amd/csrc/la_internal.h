@@ -108,8 +108,13 @@ struct BwdArgs {
     Tracer* tr;
 };
 
-// Stream-ordered workspace pool of a device (chunk_fwd_split.hip).
+// Stream-ordered workspace pool of a device (chunk_fwd_split.hip), which keeps its memory.
 hipMemPool_t workspace_pool(int dev);
+// Temporary workspace on the current device's pool, stream-ordered on `stream` (free it with
+// hipFreeAsync on the same stream).
+hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t stream);
+// Returns the current device's pool memory not in use to the device.
+hipError_t workspace_trim();
 
 // Chunked backward with fp32 arithmetic on VALU (chunk_bwd_generic.hip): every shape the generic
 // forward takes.

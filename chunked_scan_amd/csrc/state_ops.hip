@@ -538,7 +538,7 @@ hipError_t decayed_q_typed(const FwdArgs& a) {
     const int nblk = (int)tps;
     const int64_t nthreads = BH * a.nseg * nblk * a.dk;
     float* partial = nullptr;
-    e = hipMallocAsync((void**)&partial, sizeof(float) * (size_t)nthreads, a.stream);
+    e = workspace_alloc((void**)&partial, sizeof(float) * (size_t)nthreads, a.stream);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((nthreads + 255) / 256);
     if (a.tile_live)
@@ -599,7 +599,7 @@ hipError_t launch_cumdecay(const float* decay, float* cum, float* total, int64_t
     const int64_t nthreads = B * H * (int64_t)nseg * nblk * dk;
     if (nthreads == 0) return hipSuccess;
     float* partial = nullptr;
-    hipError_t e = hipMallocAsync((void**)&partial, sizeof(float) * (size_t)nthreads, stream);
+    hipError_t e = workspace_alloc((void**)&partial, sizeof(float) * (size_t)nthreads, stream);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((nthreads + 255) / 256);
     LA_TRACED(tr, "cumdecay_gate_blocksum",

@@ -17,16 +17,23 @@
  *
  * Memory.  Every pointer is a device pointer (HBM) owned by the caller; the library never
  * frees or keeps one past the call.  Tensors are dense, row-major, in the layouts stated per
- * argument.  la_chunk_fwd may allocate temporary device workspace, stream-ordered on the
- * caller's stream, and returns it to the pool before returning; the other calls allocate
+ * argument.  Calls that need temporary device workspace take it from a stream-ordered memory
+ * pool the library keeps per device, on the caller's stream, and free it (stream-ordered) before
+ * returning: la_chunk_fwd and la_chunk_fwd_decayed (per sub-segment states when a segment is split
+ * across compute units; in gate mode a few flags per workgroup; la_chunk_fwd_decayed on the shapes
+ * whose forward does not emit its outputs, one float per 64 tokens and key dim in gate mode),
+ * la_chunk_bwd and la_chunk_bwd_states (per sub-segment states, and the decay derivative's
+ * partials), and la_cumdecay in gate mode (one float per 64 tokens and key dim).  The pool keeps
+ * the memory it has obtained (so repeated calls never reach the driver) until la_trim_workspace.
+ * la_chunk_fwd_noalloc, la_state_scan, la_state_correct and la_state_correct_live allocate
  * nothing.
  *
  * Execution.  Calls validate every argument on the host first, then enqueue kernels on
  * shape->stream (a hipStream_t; NULL = the default stream) and return without waiting.  A
  * fault inside a kernel is reported by the caller's next synchronisation, not by the call.
  * Calls touching the same buffers must be ordered by the caller (same stream or events).
- * The library holds no mutable global state; concurrent calls from several host threads are
- * safe.
+ * Apart from the workspace pools (and the fixed array of la_chunk_fwd_noalloc) the library holds
+ * no mutable global state; concurrent calls from several host threads are safe.
  *
  * Errors.  A call returns LA_OK or a negative la_status and, on error, enqueues nothing.
  */
@@ -328,6 +335,11 @@ la_status la_state_correct_live(const void* q, const float* cumdecay, const floa
  * Returns LA_OK, LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DECAY, LA_ERR_ALIAS or LA_ERR_LAUNCH.
  */
 la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const la_shape* shape);
+
+/* Returns the memory of the current device's workspace pool that no enqueued call still uses to
+ * the device (the pool keeps what it has obtained until then; later calls obtain it again).
+ * Returns LA_OK or LA_ERR_LAUNCH. */
+la_status la_trim_workspace(void);
 
 /* Static description of a status code; never NULL. */
 const char* la_status_str(la_status s);

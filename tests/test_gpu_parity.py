@@ -590,3 +590,19 @@ def test_device_step_graph_replay(mode):
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_ref), rep
         assert torch.equal(s_g, s_ref), rep
+
+
+def test_trim_workspace_between_calls():
+    """la_trim_workspace hands the pool's unused memory back; the next calls obtain it again and
+    give bit-identical results (forward with its sub-segment split, backward, gate cumulative decay)."""
+    w = W3.scaled(B=1, H=4, L=4096, seed=77)
+    note("la_trim_workspace between calls")
+    d = to_dev(make_inputs(w, "cpu"))
+    o1, s1 = lb.la_chunk_fwd(d["q"], d["k"], d["v"], d["decay"], None, mode="gate")
+    c1, t1 = lb.la_cumdecay(d["decay"], w.B, w.H, w.L, w.dk, mode="gate")
+    torch.cuda.synchronize()
+    lb.la_trim_workspace()
+    o2, s2 = lb.la_chunk_fwd(d["q"], d["k"], d["v"], d["decay"], None, mode="gate")
+    c2, t2 = lb.la_cumdecay(d["decay"], w.B, w.H, w.L, w.dk, mode="gate")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(c1, c2) and torch.equal(t1, t2)
