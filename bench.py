@@ -61,14 +61,18 @@ def algorithmic(w, mode_bytes_gate: int):
     return by, fl
 
 
-def live_correction_tokens(w, seg_len: int, nseg_corr: int, inp=None) -> int:
-    """Tokens the head-decay correction actually touches: per segment and head, the 64-token tiles
-    whose cumulative decay exp(lambda (64 i + 1)) at their first token is nonzero in fp32 (the
-    kernel's own test; the others' correction is exactly zero and they are skipped).  Other modes:
-    every token."""
+def live_correction_tokens(w, seg_len: int, nseg_corr: int, inp=None, step=None) -> int:
+    """Tokens the correction actually touches.  Head decay: per segment and head, the 64-token
+    tiles whose cumulative decay exp(lambda (64 i + 1)) at their first token is nonzero in fp32
+    (the kernel's own test; the others' correction is exactly zero and they are skipped).  Gate
+    decay: the tiles the forward flagged live in its last run (the correction skips the rest).
+    No decay: every token."""
     import numpy as np
 
     total = w.B * w.H * seg_len * nseg_corr
+    if w.mode == "gate" and step is not None and getattr(step, "live", None) is not None:
+        flags = step.live[:, :, -nseg_corr:] if nseg_corr < step.live.shape[2] else step.live
+        return min(total, int((flags != 0).sum().item()) * 64)
     if w.mode != "head" or inp is None:
         return total
     lam = inp["decay"].float().cpu().numpy()
@@ -94,16 +98,17 @@ def kernel_roofline(w, step, kernels, inp=None):
     nseg = getattr(step, "nseg", None)
     if nseg is None:  # device step: G sub-segments, scan over G + 1 entries, every live token corrected
         P, nstates = step.G + 1, step.G
-        corrected = live_correction_tokens(w, w.L // step.G, step.G, inp)
+        corrected = live_correction_tokens(w, w.L // step.G, step.G, inp, step)
     else:             # segmented pass: P segments, the live tokens of segments 1.. corrected
         P, nstates = nseg, nseg - 1
-        corrected = live_correction_tokens(w, w.L // nseg, nseg - 1, inp)
+        corrected = live_correction_tokens(w, w.L // nseg, nseg - 1, inp, step)
     fwd = w.B * w.H * w.L * (es * (2 * w.dk + 2 * w.dv) + (4 * w.dk if w.mode == "gate" else 0))
     scan = bh * P * (2 * state + (4 * w.dk if w.mode != "none" else 0))
     corr = corrected * es * (w.dk + 2 * w.dv) + bh * nstates * state
     for name, d in kernels.items():
-        by = fwd if name.endswith("_output_pass") else scan if name == "state_scan" else \
-            corr if name.startswith("state_correct") else None
+        # the gate mode's redo launch reruns only flagged units (none in these workloads): no figure
+        by = None if "redo" in name else fwd if name.endswith("_output_pass") else \
+            scan if name == "state_scan" else corr if name.startswith("state_correct") else None
         if by is None:
             continue
         if name == "state_scan" and d["launches_per_step"] > 1:

@@ -18,7 +18,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblachunk.so")
+# LACHUNK_LIB names another build of the same library (the host-sanitized build of build.py's
+# build_sanitized()).
+LIB_PATH = os.environ.get("LACHUNK_LIB") or os.path.join(_HERE, "liblachunk.so")
 
 LA_F32, LA_BF16 = 0, 1
 MODES = {"none": 0, "head": 1, "gate": 2}

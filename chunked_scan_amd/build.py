@@ -53,5 +53,48 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(ROOT, "_build", "san")
+SAN_LIB = os.path.join(SAN_DIR, "liblachunk.so")
+# clang's shared AddressSanitizer runtime (it carries UndefinedBehaviorSanitizer too); a process
+# that loads SAN_LIB needs it preloaded: LD_PRELOAD=<asan_runtime()>
+def asan_runtime() -> str:
+    out = subprocess.run([HIPCC, "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = out.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang's AddressSanitizer runtime was not found")
+    return path
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """The library with its host code built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (device code as in build(), uninstrumented) into _build/san/liblachunk.so: the argument
+    validation, the planning arithmetic and the error paths of every entry point run under the
+    sanitizers, also on a machine without a GPU.  Run a program against it with LACHUNK_LIB=<path>, LD_PRELOAD=<asan_runtime()>
+    and ASAN_OPTIONS=detect_leaks=0 (the Python interpreter itself is not instrumented)."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    flags = ["-O3", "-std=c++17", "-fPIC", "-Xarch_host", "-g", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-shared-libsan",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
+
+    def one(src):
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", *flags, "-c", src, "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc (sanitized host build) failed for %s:\n%s" % (src, r.stdout + r.stderr))
+        return obj
+
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(one, srcs))
+    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+                           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                           "-shared-libsan", "-o", SAN_LIB, *objs])
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build()

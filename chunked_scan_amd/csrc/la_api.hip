@@ -84,17 +84,30 @@ size_t tile_flag_bytes(const la_shape* s) {
     return sizeof(uint32_t) * (size_t)(s->B * s->H * s->nseg * ((s->L / s->nseg + 63) / 64));
 }
 
+// A caller's per-(b,h) stride (0: dense) over blocks of `min` elements: at least `min`, and
+// B*H strides within the element bound, so that no byte count derived from it overflows.
+bool stride_ok(int64_t stride, int64_t min, const la_shape* s) {
+    if (stride == 0) return true;
+    return stride >= min && prod(s->B * s->H, stride) >= 0;
+}
+
+// Everything la_chunk_fwd checks that does not depend on the pointers.
+la_status check_fwd_shape(const la_shape* s, int chunk) {
+    la_status st = check_common(s);
+    if (st != LA_OK) return st;
+    if (chunk <= 0 || s->subseg_chunks < 0 || s->state_stride < 0) return LA_ERR_SHAPE;
+    if (!stride_ok(s->state_stride, (int64_t)s->nseg * s->dk * s->dv, s)) return LA_ERR_SHAPE;
+    if (!fwd_chunk_ok(s, chunk)) return LA_ERR_UNSUPPORTED;
+    if ((st = check_dtype(s)) != LA_OK) return st;
+    return check_decay_mode(s);
+}
+
 la_status validate_fwd(const void* q, const void* k, const void* v, const float* decay, const float* s_in,
                        const void* o, const float* s_out, const la_shape* s, int chunk,
                        const void* q_dec = nullptr, const float* total = nullptr,
                        const uint32_t* tile_live = nullptr) {
-    la_status st = check_common(s);
+    la_status st = check_fwd_shape(s, chunk);
     if (st != LA_OK) return st;
-    if (chunk <= 0 || s->subseg_chunks < 0 || s->state_stride < 0) return LA_ERR_SHAPE;
-    if (s->state_stride && s->state_stride < (int64_t)s->nseg * s->dk * s->dv) return LA_ERR_SHAPE;
-    if (!fwd_chunk_ok(s, chunk)) return LA_ERR_UNSUPPORTED;
-    if ((st = check_dtype(s)) != LA_OK) return st;
-    if ((st = check_decay_mode(s)) != LA_OK) return st;
     if (s->decay_mode == LA_DECAY_NONE && decay) return LA_ERR_DECAY;
     const int64_t nqk = s->B * s->H * s->L * s->dk;
     const int64_t nv = s->B * s->H * s->L * s->dv;
@@ -113,11 +126,11 @@ la_status validate_fwd(const void* q, const void* k, const void* v, const float*
         if (overlap(so, in) || overlap(sso, in)) return LA_ERR_ALIAS;
     if (overlap(so, sso)) return LA_ERR_ALIAS;
     // the optional outputs of la_chunk_fwd_decayed
-    if (total && (s->total_stride < 0 || (s->total_stride && s->total_stride < (int64_t)s->nseg * s->dk)))
+    if (total && (s->total_stride < 0 || !stride_ok(s->total_stride, (int64_t)s->nseg * s->dk, s)))
         return LA_ERR_SHAPE;
     const int64_t tstride = s->total_stride ? s->total_stride : (int64_t)s->nseg * s->dk;
     Span sqd{q_dec, q_dec ? es * nqk : 0};
-    Span stt{total, (total && BH > 0) ? sizeof(float) * (size_t)((BH - 1) * tstride + s->nseg * s->dk) : 0};
+    Span stt{total, (total && BH > 0) ? sizeof(float) * (size_t)((BH - 1) * tstride + (int64_t)s->nseg * s->dk) : 0};
     Span stl{tile_live, tile_live ? tile_flag_bytes(s) : 0};
     for (Span x : {sq, sk, sv, sd, si, so, sso})
         if (overlap(sqd, x) || overlap(stt, x) || overlap(stl, x)) return LA_ERR_ALIAS;
@@ -153,8 +166,8 @@ int32_t la_version(void) { return (1 << 16) | 1; }
 
 la_status la_trim_workspace(void) { return from_hip(la::workspace_trim()); }
 
-const char* la_status_str(la_status s) {
-    switch (s) {
+const char* la_status_str(int32_t status) {
+    switch (status) {
         case LA_OK: return "ok";
         case LA_ERR_NULL: return "a required pointer is NULL";
         case LA_ERR_SHAPE: return "invalid or inconsistent sizes";
@@ -168,11 +181,7 @@ const char* la_status_str(la_status s) {
     return "unknown status";
 }
 
-int32_t la_supported(const la_shape* s, int32_t chunk) {
-    if (check_common(s) != LA_OK || chunk <= 0 || !fwd_chunk_ok(s, chunk) || s->subseg_chunks < 0) return 0;
-    if (check_dtype(s) != LA_OK || check_decay_mode(s) != LA_OK) return 0;
-    return 1;
-}
+int32_t la_supported(const la_shape* s, int32_t chunk) { return check_fwd_shape(s, chunk) == LA_OK ? 1 : 0; }
 
 }  // extern "C"
 
@@ -281,7 +290,7 @@ la_status state_correct_impl(const void* q, const float* cumdecay, const float* 
     const int64_t np = s->nseg - s->seg_begin;
     const int64_t per_state = (int64_t)s->dk * s->dv;
     const int64_t stride = s->state_stride ? s->state_stride : np * per_state;
-    if (s->state_stride && s->state_stride < np * per_state) return LA_ERR_SHAPE;
+    if (!stride_ok(s->state_stride, np * per_state, s)) return LA_ERR_SHAPE;
     const int64_t BH = s->B * s->H;
     const int64_t Ls = s->L / s->nseg;
     const int64_t nq = BH * s->L * s->dk;
@@ -333,13 +342,13 @@ la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const l
     const int64_t BH = s->B * s->H;
     const int64_t ncum = BH * s->L * s->dk;
     const int64_t ntot = BH * s->nseg * s->dk;
-    if (s->total_stride < 0 || (s->total_stride && s->total_stride < (int64_t)s->nseg * s->dk)) return LA_ERR_SHAPE;
+    if (s->total_stride < 0 || !stride_ok(s->total_stride, (int64_t)s->nseg * s->dk, s)) return LA_ERR_SHAPE;
     const int64_t tstride = s->total_stride ? s->total_stride : (int64_t)s->nseg * s->dk;
     const bool need = (cumdecay && ncum > 0) || (total && ntot > 0);
     if (need && s->decay_mode == LA_DECAY_HEAD && !decay) return LA_ERR_NULL;
     if (need && s->decay_mode == LA_DECAY_GATE && ncum > 0 && !decay) return LA_ERR_NULL;
     Span sd{decay, decay_bytes(s)}, sc{cumdecay, cumdecay ? sizeof(float) * (size_t)ncum : 0};
-    Span stt{total, (total && BH > 0) ? sizeof(float) * (size_t)((BH - 1) * tstride + s->nseg * s->dk) : 0};
+    Span stt{total, (total && BH > 0) ? sizeof(float) * (size_t)((BH - 1) * tstride + (int64_t)s->nseg * s->dk) : 0};
     if (overlap(sc, sd) || overlap(stt, sd) || overlap(sc, stt)) return LA_ERR_ALIAS;
     if ((st = check_trace(s)) != LA_OK) return st;
     la::Tracer tr = make_tracer(s);
@@ -361,7 +370,7 @@ la_status chunk_bwd_impl(const void* q, const void* k, const void* v, const floa
     if (st != LA_OK) return st;
     if (chunk <= 0 || s->state_stride < 0 || s->subseg_chunks < 0) return LA_ERR_SHAPE;
     const int64_t per_seg = (int64_t)s->dk * s->dv;
-    if (s->state_stride && s->state_stride < (int64_t)s->nseg * per_seg) return LA_ERR_SHAPE;
+    if (!stride_ok(s->state_stride, (int64_t)s->nseg * per_seg, s)) return LA_ERR_SHAPE;
     if (!chunk_ok(chunk)) return LA_ERR_UNSUPPORTED;
     if ((st = check_dtype(s)) != LA_OK) return st;
     if ((st = check_decay_mode(s)) != LA_OK) return st;
@@ -380,7 +389,7 @@ la_status chunk_bwd_impl(const void* q, const void* k, const void* v, const floa
     const int64_t Lseg = s->nseg > 0 ? s->L / s->nseg : 0;
     const int64_t nsub = s_sub && sub_len > 0 ? (Lseg + sub_len - 1) / sub_len : 0;
     if (s_sub && (sub_len <= 0 || sub_len % chunk != 0 || sub_stride < 0)) return LA_ERR_SHAPE;
-    if (s_sub && sub_stride && sub_stride < (int64_t)s->nseg * nsub * per_seg) return LA_ERR_SHAPE;
+    if (s_sub && !stride_ok(sub_stride, (int64_t)s->nseg * nsub * per_seg, s)) return LA_ERR_SHAPE;
     const int64_t substride = s_sub ? (sub_stride ? sub_stride : (int64_t)s->nseg * nsub * per_seg) : 0;
     const size_t sub_bytes =
         s_sub && BH > 0 ? sizeof(float) * (size_t)((BH - 1) * substride + s->nseg * nsub * per_seg) : 0;

@@ -341,8 +341,9 @@ la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const l
  * Returns LA_OK or LA_ERR_LAUNCH. */
 la_status la_trim_workspace(void);
 
-/* Static description of a status code; never NULL. */
-const char* la_status_str(la_status s);
+/* Static description of a status code (any int32_t: codes that are not a la_status give
+ * "unknown status"); never NULL. */
+const char* la_status_str(int32_t status);
 
 /* 1 if la_chunk_fwd has a kernel for this shape and chunk (validation passes), else 0. */
 int32_t la_supported(const la_shape* shape, int32_t chunk);

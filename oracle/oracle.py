@@ -11,7 +11,13 @@ NONE, HEAD, GATE = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "la_oracle.c")
-_LIB = os.path.join(_HERE, "libla_oracle.so")
+# LA_ORACLE_SANITIZE=1 selects the build with AddressSanitizer and UndefinedBehaviorSanitizer
+# (libla_oracle_san.so; the process must preload gcc's libasan: LD_PRELOAD=$(gcc
+# -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0).
+SANITIZE = os.environ.get("LA_ORACLE_SANITIZE", "") not in ("", "0")
+_LIB = os.path.join(_HERE, "libla_oracle_san.so" if SANITIZE else "libla_oracle.so")
+_FLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread"]
+_SAN_FLAGS = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
 _lib = None
 
 
@@ -20,11 +26,11 @@ def lib_path() -> str:
 
 
 def build(force: bool = True) -> str:
-    """Compile la_oracle.c with gcc (no fast-math, no FMA contraction) into libla_oracle.so."""
+    """Compile la_oracle.c with gcc (no fast-math, no FMA contraction) into libla_oracle.so (with
+    LA_ORACLE_SANITIZE=1: libla_oracle_san.so, built with the sanitizers as well)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
-                               "-fPIC", "-shared", "-pthread", "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", *_FLAGS, *(_SAN_FLAGS if SANITIZE else []), "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
