@@ -1,24 +1,29 @@
 """Throughput of one device's share of ZeCO causal linear attention on one MI355X.
 
 A step is one pass of the whole per-device path over one batch of synthetic input at the
-pages' per-device shape (B=1, H=16, L=16384, dk=dv=128, bf16, chunk 64, no decay, S_recv = 0),
-with the device's segment cut into G sub-segments (G = 16 here, one workgroup each per head):
-  la_chunk_fwd     local chunked forward of every sub-segment from a zero state -> O_local, S_loc
-  la_cumdecay      each sub-segment's total decay Lambda (head decay; gate decay takes it and
-                   Q * cumulative decay from la_chunk_fwd_decayed; without decay Lambda = 1)
-  la_state_scan    All-Scan over [S_recv, S_loc,1..G]: every sub-segment's incoming state, and
-                   S_out = Lambda S_recv + S_loc as its last entry
-  la_state_correct O += (Q * cumulative decay) S_in for every sub-segment
+pages' per-device shape (B=1, H=16, L=16384, dk=dv=128, bf16, chunk 64, no decay), for a device
+that receives the state S_recv (drawn N(0, 0.05) where the workload has one, else 0): the exact
+outputs O and the outgoing state S_out = Lambda S_recv + S_loc.  The headline step computes them
+with one la_chunk_fwd call from S_recv; inside it the library cuts the segment into G
+sub-segments (G = 16 here, one workgroup each per head) and applies the ZeCO decomposition
+between them:
+  state pass       every sub-segment but the last: its local end state from zero (k, v read)
+  la_state_scan    the scan over [S_recv, S_loc,1..G-1]: every sub-segment's exact incoming state
+  output pass      every sub-segment from its exact incoming state: O, and S_out from the last
+Alongside, the same result is timed in the pages' decomposed form (local forward of every
+sub-segment from zero, the All-Scan over [S_recv, S_loc,1..G], output correction
+O += (Q * cumulative decay) S_in), with the library's chained single launch (the state pass,
+scan and output pass in one kernel, la_shape.fwd_schedule = 2), and with the pages' two-pass
+schedule (every chunk's state stored, scanned and reloaded).
 Prints one JSON line.  Per-kernel durations come from HIP events that the library records
 around every kernel on the stream it launches them on (la_trace); the dominant kernel's
 roofline uses its algorithmic bytes (q, k, v read + o written) over its mean duration.
 Per-step statistics (median, mean, std, min) are given warm and cold (a 512 MiB buffer read
 before each step evicts the 256 MB last-level cache; reading, not writing, so that the step does
 not also pay for writing back someone else's dirty lines).  The head-decay and gate workloads
-(device step, B = 2 and 4) and the 1M-token 64-segment pass are timed alongside, unless
---no-alongside.  Every workload is warmed up with at least ~20 ms of steps first: the GPU's
-clocks take about 10 ms of sustained work to settle (the plain step runs ~105 us before, ~93 us
-after).
+(B = 2 and 4) and the 1M-token 64-segment pass are timed alongside, unless --no-alongside.
+Every workload is warmed up with at least ~20 ms of steps first: the GPU's clocks take about
+10 ms of sustained work to settle.
 """
 from __future__ import annotations
 
@@ -87,6 +92,18 @@ def live_correction_tokens(w, seg_len: int, nseg_corr: int, inp=None, step=None)
     return w.B * live * nseg_corr
 
 
+def split_plan(w):
+    """(G, chunks per sub-segment) of the library's split of one segment for the bf16 matrix-core
+    forward with 64-token chunks: about 256 workgroups at dk = 128 (512 below), at least four
+    chunks per sub-segment (the same rule as fwd_split_plan in chunk_fwd_split.hip; used here
+    for byte accounting only)."""
+    units = w.B * w.H * w.nseg
+    nch = -(-(w.L // w.nseg) // 64)
+    g_want = -(-(256 if w.dk >= 128 else 512) // units)
+    cps = min(max(4, -(-nch // g_want)), nch)
+    return -(-nch // cps), cps
+
+
 def kernel_roofline(w, step, kernels, inp=None):
     """Adds algorithmic bytes per launch, achieved GB/s and the fraction of the 8 TB/s peak to the
     forward's output pass, the state scan and the correction (their per-unit figures: q, k, v read
@@ -96,6 +113,18 @@ def kernel_roofline(w, step, kernels, inp=None):
     bh = w.B * w.H
     state = w.dk * w.dv * 4
     nseg = getattr(step, "nseg", None)
+    if hasattr(step, "schedule"):  # one exact call: state pass over G - 1 sub-segments, scan over G - 1
+        G, cps = split_plan(w)
+        fwd = w.B * w.H * w.L * (es * (2 * w.dk + 2 * w.dv) + (4 * w.dk if w.mode == "gate" else 0))
+        spass = bh * (G - 1) * (cps * 64 * es * (w.dk + w.dv) + state + 4 * w.dk)
+        scan = bh * (G - 1) * (2 * state + (4 * w.dk if w.mode != "none" else 0))
+        for name, d in kernels.items():
+            by = None if "redo" in name else fwd if name.endswith("_output_pass") else \
+                spass if name.endswith("_state_pass") else scan if name == "state_scan" else None
+            if by is not None and d["launches_per_step"] == 1:
+                gbs = by / (d["mean_us"] * 1e-6) / 1e9
+                d.update(algorithmic_bytes=by, gbps=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+        return
     if nseg is None:  # device step: G sub-segments, scan over G + 1 entries, every live token corrected
         P, nstates = step.G + 1, step.G
         corrected = live_correction_tokens(w, w.L // step.G, step.G, inp, step)
@@ -286,36 +315,32 @@ def kernel_stats(step, steps, stream, capacity=8):
     return kernels, e0.elapsed_time(e1) / steps
 
 
-def epsilon(w, inp, step, stream, steps: int = 20):
+def epsilon(w, inp, stream, steps: int = 20):
     """The single-GPU analogue of the reviewers' overhead question on this workload: the same
-    exact result three ways, each step timed with events (median us).
-      zeco_step        the device step (local forward from zero, scan, correction by S_recv)
-      one_call_exact   one la_chunk_fwd from S_recv (what a single device without sequence
-                       parallelism runs; intra-GPU split with exact incoming states, no correction)
+    exact result (O and S_out from S_recv) four ways, each step timed with events (median us).
+      decomposed        the pages' device step: local forward of every sub-segment from zero, the
+                        All-Scan over [S_recv, S_loc,1..G], output correction by each S_in
+      exact_passes      one la_chunk_fwd from S_recv (state pass, scan, output pass from the exact
+                        incoming states; no correction)
+      exact_chained     the same in one launch with the chained state hand-off (where it exists)
       two_pass_chunk_states  la_chunk_fwd from S_recv with every chunk's state stored to HBM, scanned
-                       and reloaded (the pages' two-pass schedule, one sub-segment per chunk)"""
+                        and reloaded (the pages' two-pass schedule, one sub-segment per chunk)"""
     import torch
 
-    from chunked_scan_amd import binding
+    from chunked_scan_amd.pipeline import DeviceStep, ExactStep
 
-    s_recv = step.states[:, :, 0].clone()
-    o = torch.empty_like(step.o)
-    s_out = torch.empty((w.B, w.H, 1, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    def med(st):
+        for _ in range(3):
+            st.run()
+        torch.cuda.synchronize()
+        return step_stats(st, steps, stream)["median_us"]
 
-    class Call:
-        def __init__(self, subseg):
-            self.subseg = subseg
-
-        def run(self):
-            binding.la_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["decay"], s_recv, o, s_out, mode=w.mode,
-                                 chunk=w.chunk, gate_norm=w.gate_norm, subseg_chunks=self.subseg)
-
-    out = {"zeco_step": step_stats(step, steps, stream)["median_us"]}
-    for name, sub in (("one_call_exact", 0), ("two_pass_chunk_states", 1)):
-        c = Call(sub)
-        for _ in range(2):
-            c.run()
-        out[name] = step_stats(c, steps, stream)["median_us"]
+    kw = dict(mode=w.mode, chunk=w.chunk, gate_norm=w.gate_norm)
+    args = (inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"])
+    out = {"decomposed": med(DeviceStep(*args, **kw)), "exact_passes": med(ExactStep(*args, schedule="passes", **kw))}
+    chained = w.dtype == "bf16" and w.dk == w.dv == 128 and w.chunk == 64 and w.mode != "gate"
+    out["exact_chained"] = med(ExactStep(*args, schedule="chained", **kw)) if chained else None
+    out["two_pass_chunk_states"] = med(ExactStep(*args, schedule="passes", subseg_chunks=1, **kw))
     return out
 
 
@@ -329,17 +354,17 @@ def state_size_sweep(stream):
     import torch
 
     from chunked_scan_amd.inputs import WORKLOADS, make_inputs
-    from chunked_scan_amd.pipeline import DeviceStep
+    from chunked_scan_amd.pipeline import DeviceStep, ExactStep
 
     out = {}
     for d in (32, 64, 128):
         w = WORKLOADS[1].scaled(dk=d, dv=d, qkv_std=1.0 / math.sqrt(d), s_in_std=0.05, seed=10 + d)
         inp = make_inputs(w, "cuda")
-        step = DeviceStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk)
+        step = ExactStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk)
         for _ in range(150):  # >= 20 ms of work: settled clocks
             step.run()
         torch.cuda.synchronize()
-        eps = epsilon(w, inp, step, stream, steps=30)
+        eps = epsilon(w, inp, stream, steps=30)
         ks, _ = kernel_stats(step, 30, stream)
         bw = BackwardStep(w)
         for _ in range(40):
@@ -349,22 +374,22 @@ def state_size_sweep(stream):
         del bw
         c128 = None
         if d < 128:
-            s128 = DeviceStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=128)
+            s128 = ExactStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=128)
             for _ in range(150):
                 s128.run()
             torch.cuda.synchronize()
             c128 = step_stats(s128, 30, stream)["median_us"]
             del s128
-        out[f"d{d}"] = dict(state_bytes=4 * d * d, zeco_step_us=eps["zeco_step"], chunk128_step_us=c128,
-                            one_call_exact_us=eps["one_call_exact"],
-                            overhead_us=round(eps["zeco_step"] - eps["one_call_exact"], 2),
-                            overhead_frac=round(eps["zeco_step"] / eps["one_call_exact"] - 1, 4),
+        out[f"d{d}"] = dict(state_bytes=4 * d * d, decomposed_step_us=eps["decomposed"], chunk128_step_us=c128,
+                            exact_step_us=eps["exact_passes"], exact_chained_us=eps["exact_chained"],
+                            decomposition_overhead_us=round(eps["decomposed"] - eps["exact_passes"], 2),
+                            decomposition_overhead_frac=round(eps["decomposed"] / eps["exact_passes"] - 1, 4),
                             backward_us=bwd,
                             kernels={n: round(v["mean_us"], 2) for n, v in ks.items()})
-        log(f"[bench] state size d={d}: device step {eps['zeco_step']:.1f} us"
+        log(f"[bench] state size d={d}: decomposed step {eps['decomposed']:.1f} us"
             + (f" (128-token chunks {c128:.1f} us)" if c128 else "") + ", one exact call "
-            f"{eps['one_call_exact']:.1f} us, backward {bwd:.1f} us; " +
-            ", ".join(f"{n} {v['mean_us']:.1f}" for n, v in ks.items()))
+            f"{eps['exact_passes']:.1f} us" + (f" (chained {eps['exact_chained']:.1f} us)" if eps["exact_chained"] else "")
+            + f", backward {bwd:.1f} us; " + ", ".join(f"{n} {v['mean_us']:.1f}" for n, v in ks.items()))
         del step, inp
         torch.cuda.empty_cache()
     return out
@@ -465,6 +490,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=400,
                     help="untimed steps first; the GPU's clocks take ~10 ms of sustained work to settle")
     ap.add_argument("--workload", type=int, default=1, help="index into chunked_scan_amd.inputs.WORKLOADS")
+    ap.add_argument("--step", choices=("auto", "exact", "decomposed", "chained"), default="auto",
+                    help="form of the device step (one-segment workloads): one exact la_chunk_fwd from S_recv "
+                         "(the library's separate passes, or its chained single launch), or the pages' local "
+                         "forward + All-Scan + output correction; auto = the faster on MI355X: exact without "
+                         "decay and with head decay, decomposed with the gate (its correction skips the tiles "
+                         "whose cumulative decay has underflowed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alongside", action="store_true",
                     help="skip the decay and segmented workloads and the three-way comparison reported next "
@@ -484,7 +515,19 @@ def main():
 
     from chunked_scan_amd import binding
     from chunked_scan_amd.inputs import WORKLOADS, make_inputs
-    from chunked_scan_amd.pipeline import DeviceStep, SegmentedForward
+    from chunked_scan_amd.pipeline import DeviceStep, ExactStep, SegmentedForward
+
+    def form_of(wx):
+        if args.step == "auto":
+            return "decomposed" if wx.mode == "gate" else "exact"
+        return "exact" if args.step == "chained" and wx.mode == "gate" else args.step
+
+    def one_segment_step(wx, ix, form):
+        a = (ix["q"], ix["k"], ix["v"], ix["decay"], ix["s_in"])
+        kw = dict(mode=wx.mode, chunk=wx.chunk, gate_norm=wx.gate_norm)
+        if form == "decomposed":
+            return DeviceStep(*a, **kw)
+        return ExactStep(*a, schedule="chained" if form == "chained" else "auto", **kw)
 
     torch.cuda.set_device(0)
     if args.backward_only:
@@ -494,8 +537,7 @@ def main():
     log(f"[bench] workload {args.workload} {w.name}: generating inputs on cuda:0")
     inp = make_inputs(w, "cuda")
     if w.nseg == 1:
-        step = DeviceStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk,
-                          gate_norm=w.gate_norm)
+        step = one_segment_step(w, inp, form_of(w))
     else:  # a sequence split into segments, all on this device: the All-Scan as a segmented scan
         if not args.no_cpu_baseline:
             raise SystemExit("the CPU baseline is timed on the one-segment device step only")
@@ -538,7 +580,7 @@ def main():
 
     eps = None
     if w.nseg == 1 and not args.no_alongside:
-        eps = epsilon(w, inp, step, stream)
+        eps = epsilon(w, inp, stream)
         log("[bench] same result three ways (median us/step): " + ", ".join(f"{k} {v:.1f}" for k, v in eps.items()))
 
     alongside = {}
@@ -550,8 +592,7 @@ def main():
             log(f"[bench] alongside: workload {wid} {wa.name}")
             ia = make_inputs(wa, "cuda")
             if wa.nseg == 1:
-                sa = DeviceStep(ia["q"], ia["k"], ia["v"], ia["decay"], ia["s_in"], mode=wa.mode, chunk=wa.chunk,
-                                gate_norm=wa.gate_norm)
+                sa = one_segment_step(wa, ia, form_of(wa))
             else:
                 sa = SegmentedForward(ia["q"], ia["k"], ia["v"], ia["decay"], ia["s_in"], mode=wa.mode,
                                       nseg=wa.nseg, chunk=wa.chunk, gate_norm=wa.gate_norm)
@@ -563,9 +604,11 @@ def main():
             ks, _ = kernel_stats(sa, n_al, stream)
             kernel_roofline(wa, sa, ks, ia)
             alongside[wa.name] = dict(
-                step=("segmented pass over %d segments" % wa.nseg) if wa.nseg > 1 else "device step",
+                step=("segmented pass over %d segments" % wa.nseg) if wa.nseg > 1 else f"device step ({form_of(wa)})",
                 B=wa.B, H=wa.H, L=wa.L, decay=wa.decay, tokens_per_s=round(wa.B * wa.L / (st["median_us"] * 1e-6), 1),
                 per_step_us=st, kernels={n: {k: round(v, 2) for k, v in d.items()} for n, d in ks.items()})
+            if wa.nseg == 1:  # the same result in the other forms
+                alongside[wa.name]["same_result_us"] = epsilon(wa, ia, stream, steps=20)
             log(f"[bench]   {wa.name}: median {st['median_us']:.1f} us/step, "
                 f"{alongside[wa.name]['tokens_per_s']:.3e} tokens/s; " +
                 ", ".join(f"{n} {d['mean_us']:.1f} us" for n, d in ks.items()))
@@ -636,8 +679,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": (f"{w.name}: device step = local chunked fwd + All-Scan state combine + "
-                                f"output correction") if w.nseg == 1 else
+        "config": {"workload": ({"exact": f"{w.name}: device step = exact O and S_out from S_recv in one la_chunk_fwd "
+                                          f"call (sub-segment state pass, scan with S_recv as its first entry, "
+                                          f"output pass from the exact incoming states)",
+                                 "chained": f"{w.name}: device step = exact O and S_out from S_recv in one chained "
+                                            f"launch (state pass, flag hand-off scan, output pass)",
+                                 "decomposed": f"{w.name}: device step = local chunked fwd + All-Scan state combine "
+                                               f"+ output correction"}[form_of(w)]) if w.nseg == 1 else
                                (f"{w.name}: {w.nseg} segments on one device = local chunked fwd + segmented "
                                 f"state scan + output correction"), "B": w.B, "H": w.H, "L": w.L, "dk": w.dk, "dv": w.dv,
                    "chunk": w.chunk, "decay": w.decay, "parallelism": "single GPU"},

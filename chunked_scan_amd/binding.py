@@ -46,7 +46,8 @@ class Shape(ctypes.Structure):
         ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("nseg", ctypes.c_int32),
         ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("decay_mode", ctypes.c_int32),
         ("gate_norm", ctypes.c_float), ("seg_begin", ctypes.c_int32), ("state_stride", ctypes.c_int64),
-        ("total_stride", ctypes.c_int64), ("subseg_chunks", ctypes.c_int32), ("stream", ctypes.c_void_p),
+        ("total_stride", ctypes.c_int64), ("subseg_chunks", ctypes.c_int32), ("fwd_schedule", ctypes.c_int32),
+        ("stream", ctypes.c_void_p),
         ("trace", ctypes.POINTER(Trace)),
     ]
 
@@ -170,9 +171,9 @@ def mode_code(mode: Optional[str], decay: Optional[torch.Tensor]) -> int:
 
 
 def make_shape(B, H, L, dk, dv, *, nseg=1, dtype=LA_BF16, mode=0, gate_norm=16.0, seg_begin=0,
-               state_stride=0, total_stride=0, subseg_chunks=0, stream=None, timer=None) -> Shape:
+               state_stride=0, total_stride=0, subseg_chunks=0, fwd_schedule=0, stream=None, timer=None) -> Shape:
     s = Shape(B, H, L, dk, dv, nseg, dtype, dtype, mode, gate_norm, seg_begin, state_stride,
-              total_stride, subseg_chunks, stream)
+              total_stride, subseg_chunks, fwd_schedule, stream)
     if timer is not None:
         s.trace = ctypes.pointer(timer.trace)
     return s
@@ -182,28 +183,34 @@ def la_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optio
                  s_in: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
                  s_out: Optional[torch.Tensor] = None, *, mode: Optional[str] = None, nseg: int = 1,
                  chunk: int = 64, gate_norm: float = 16.0, subseg_chunks: int = 0, want_state: bool = True,
-                 stream=None, timer=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                 schedule: str = "auto", stream=None, timer=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise forward.  q, k [B,H,L,dk], v [B,H,L,dv] (f32 or bf16); decay None / [H] / [B,H,L,dk];
     s_in [B,H,dk,dv] f32 or None.  Returns (o [B,H,L,dv], s_out [B,H,nseg,dk,dv] f32 or None);
-    s_out may be a view with evenly spaced dense (b,h) blocks."""
+    s_out may be a view with evenly spaced dense (b,h) blocks.  schedule: "auto" (the library's
+    choice), "passes" or "chained" (la_shape.fwd_schedule 0 / 1 / 2)."""
     return _chunk_fwd("la_chunk_fwd", q, k, v, decay, s_in, o, s_out, mode, nseg, chunk, gate_norm, subseg_chunks,
-                      want_state, stream, timer)
+                      want_state, stream, timer, schedule)
 
 
 def la_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, decay: Optional[torch.Tensor] = None,
                          s_in: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
                          s_out: Optional[torch.Tensor] = None, *, mode: Optional[str] = None, nseg: int = 1,
                          chunk: int = 64, gate_norm: float = 16.0, subseg_chunks: int = 0, want_state: bool = True,
-                         stream=None, timer=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                         schedule: str = "auto", stream=None, timer=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """la_chunk_fwd whose workspace is the library's fixed device array (the library allocates
     nothing).  Pass o (and s_out, or want_state=False) to keep the whole call free of allocations:
     the outputs this wrapper creates when they are not given come from torch's allocator."""
     return _chunk_fwd("la_chunk_fwd_noalloc", q, k, v, decay, s_in, o, s_out, mode, nseg, chunk, gate_norm,
-                      subseg_chunks, want_state, stream, timer)
+                      subseg_chunks, want_state, stream, timer, schedule)
+
+
+SCHEDULES = {"auto": 0, "passes": 1, "chained": 2}
 
 
 def _chunk_fwd(fn, q, k, v, decay, s_in, o, s_out, mode, nseg, chunk, gate_norm, subseg_chunks, want_state, stream,
-               timer):
+               timer, schedule="auto"):
+    if schedule not in SCHEDULES:
+        raise ValueError(f"schedule must be one of {sorted(SCHEDULES)}, not {schedule!r}")
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     _dev(q, "q")
@@ -224,7 +231,8 @@ def _chunk_fwd(fn, q, k, v, decay, s_in, o, s_out, mode, nseg, chunk, gate_norm,
         _dev(s_out, "s_out", torch.float32, (B, H, nseg, dk, dv), contiguous=False)
         stride = _bh_stride(s_out, "s_out", dk * dv)
     shp = make_shape(B, H, L, dk, dv, nseg=nseg, dtype=_dtype_code(q), mode=m, gate_norm=gate_norm,
-                     state_stride=stride, subseg_chunks=subseg_chunks, stream=_stream(stream), timer=timer)
+                     state_stride=stride, subseg_chunks=subseg_chunks, fwd_schedule=SCHEDULES[schedule],
+                     stream=_stream(stream), timer=timer)
     _check(fn, getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(s_in), _ptr(o), _ptr(s_out),
                                   ctypes.byref(shp), chunk))
     return o, s_out

@@ -125,6 +125,312 @@ struct Dma {
     }
 };
 
+// LDS layout of one pass: SLOT tiles per ring stage (k, v; q too in the output pass), gate mode's
+// chunk decay after the tiles, NST stages (NST - 1 chunks in flight; gate: the loaders prepare one
+// stage ahead, so three), and in the output pass without gate an output tile after the ring.
+template <int MODE, bool STATE_ONLY>
+struct Layout {
+    static constexpr bool GATE = MODE == DECAY_GATE;
+    static constexpr bool OTILE = !STATE_ONLY && !GATE;  // outputs leave through an LDS tile stored by the loaders
+    static constexpr int SLOT = STATE_ONLY ? 2 : 3;
+    static constexpr int STAGE = SLOT * TE + (GATE ? 2 * D : 0);  // gate: D floats of chunk decay after the tiles
+    static constexpr int NST = GATE ? 3 : (LDS_TILES - (OTILE ? 1 : 0)) / SLOT;
+    static constexpr int RING = NST * STAGE;
+    __device__ static __forceinline__ Ring stage(__bf16* ring, int c) {
+        __bf16* b = ring + (c % NST) * STAGE;
+        // q is unused in the state pass
+        return Ring{b, b + (SLOT - 2) * TE, b + (SLOT - 1) * TE, (float*)(b + SLOT * TE)};
+    }
+};
+
+// The tokens [t_begin, t_end) of one (b, h) row block that a workgroup walks, in 64-token chunks.
+struct Walk {
+    int64_t row_base, t_begin, t_end;
+    int nch;
+    __device__ __forceinline__ int chunk_len(int c) const {
+        return (int)min((int64_t)C, t_end - t_begin - (int64_t)c * C);
+    }
+};
+
+// Loader wave lw of the no-decay and head-decay modes: chunk c + NST - 1 is requested as soon as
+// every wave is done with chunk c - 1; in the output pass it also stores each chunk's output tile.
+// One s_barrier per chunk (two in the output pass), matching compute_walk.
+template <int MODE, bool STATE_ONLY>
+__device__ __forceinline__ void loader_walk(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o,
+                                            __bf16* ring, const __bf16* otile, const Walk& wk, int lw, int lane) {
+    using LY = Layout<MODE, STATE_ONLY>;
+    using DM = Dma<STATE_ONLY>;
+    const int nch = wk.nch;
+    int issued = 0;
+    for (; issued < LY::NST - 1 && issued < nch; issued++)
+        DM::issue(q, k, v, LY::stage(ring, issued), wk.row_base + wk.t_begin + (int64_t)issued * C,
+                  wk.chunk_len(issued), lw, lane);
+    for (int c = 0; c < nch; c++) {
+        // this wave's part of chunk c has landed.  Only the younger DMA batches are allowed to be
+        // outstanding: loads complete in order, so while any load of chunk c is pending all
+        // younger loads are too and the count cannot drop that low, whatever the stores do.
+        wait_batches<DM::NDMA>(issued - c - 1);
+        __builtin_amdgcn_s_barrier();  // chunk c is handed to the compute waves
+        if (issued < nch) {
+            DM::issue(q, k, v, LY::stage(ring, issued), wk.row_base + wk.t_begin + (int64_t)issued * C,
+                      wk.chunk_len(issued), lw, lane);
+            issued++;
+        }
+        if (LY::OTILE) {
+            lds_barrier_keep_dma();  // the compute waves have written chunk c's outputs
+            const int n = wk.chunk_len(c);
+            const int64_t r0 = wk.row_base + wk.t_begin + (int64_t)c * C;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int pc = (threadIdx.x - 256) + 256 * r;
+                const int row = pc >> 4, sl = pc & 15;
+                const u32x4 y = *(const u32x4*)(otile + row * D + ((sl ^ (row & 15)) << 3));
+                if (row < n) *(u32x4*)(o + (r0 + row) * D + sl * 8) = y;
+            }
+        }
+    }
+}
+
+// Compute wave w (value columns 32 w + sigma(0..31)) over the walk's chunks, with the state S in
+// its accumulators on entry and on return; lam is the head's log-decay (head mode).  One
+// lds_barrier per chunk (two in the output pass without gate), matching the loader waves.
+template <int MODE, bool STATE_ONLY>
+__device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf16* otile, __bf16* o, float lam,
+                                             const Walk& wk, int w, int lane) {
+    using LY = Layout<MODE, STATE_ONLY>;
+    constexpr bool GATE = LY::GATE, OTILE = LY::OTILE;
+    const int n32 = lane & 31, kg = lane >> 5;
+    const int G16 = lane >> 4, i16 = lane & 15;
+
+    // per-lane LDS offsets of the transposing reads for the first 16-token slab (tokens kg*8 +
+    // {0..3 | 4..7}); slab ks adds 16 ks rows, which leaves the swizzle (row bits 0-3) unchanged.
+    // The 4-column group a = i16 % 4 that a read fetches is placed at 4 (bits of a swapped), the
+    // sigma order.
+    const int quad = 4 * (((i16 & 1) << 1) | ((i16 >> 1) & 1));
+    const int tb = (G16 >> 1) * 8 + (i16 >> 2);
+    int voff[2];      // V: value column vcol_lane
+    int ktoff[4][2];  // K for the state: key column 32m + sigma(n32)
+    {
+        const int vcol = 32 * w + (G16 & 1) * 16 + quad;
+        voff[0] = sw(tb, vcol);
+        voff[1] = sw(tb + 4, vcol);
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const int kcol = 32 * m + (G16 & 1) * 16 + quad;
+            ktoff[m][0] = sw(tb, kcol);
+            ktoff[m][1] = sw(tb + 4, kcol);
+        }
+    }
+
+    for (int c = 0; c < wk.nch; c++) {
+        const Ring cur = LY::stage(ring, c);
+        const int n = wk.chunk_len(c);
+        // Head decay: the factors exp(lambda d) are recomputed every chunk from a few base-2
+        // exponentials and chains of multiplications by exp(lambda) (every factor <= 1).  Hiding
+        // lambda's value from the optimiser each chunk keeps these loop invariants from being
+        // hoisted into registers for the whole loop.
+        float lamc = lam;
+        if (MODE == DECAY_HEAD) asm volatile("" : "+s"(lamc));
+        lamc *= LOG2E;
+        const float e1 = (MODE == DECAY_HEAD) ? decay_pow2(lamc, 1) : 1.f;
+        lds_barrier();  // chunk c has landed; every wave is done with chunk c - 1
+
+        // V operand: tokens 16ks + kg*8 + jj (plain order), value column vcol_lane
+        bf16x8 vb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+            vb[ks] = cat(lds_tr16(cur.v + 16 * ks * D + voff[0]), lds_tr16(cur.v + 16 * ks * D + voff[1]));
+
+        if (!STATE_ONLY) {
+            // the state as A operands of S^T Qbar^T: slab (m, hh) holds key dims 32m + 16hh + kg*8 + jj
+            bf16x8 sa[4][2];
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++) {
+                    bf16x8 x;
+#pragma unroll
+                    for (int jj = 0; jj < 8; jj++) x[jj] = (__bf16)S[m][8 * hh + jj];
+                    sa[m][hh] = x;
+                }
+#pragma unroll
+            for (int ib = 0; ib < 2; ib++) {
+                const int itok = ib * 32 + n32;
+                // the diagonal block's decay factors are the same for both halves: recomputing them
+                // is cheaper than keeping them live
+                float lamb = lam;
+                if (MODE == DECAY_HEAD) asm volatile("" : "+s"(lamb));
+                lamb *= LOG2E;
+                const float e1b = (MODE == DECAY_HEAD) ? decay_pow2(lamb, 1) : 1.f;
+                const float einv = (MODE == DECAY_HEAD) ? __builtin_amdgcn_exp2f(-lamb) : 1.f;
+                // the upward chain below needs exp(31 lambda) to stay a normal float
+                const bool up = lamb >= -4.f;
+                // Q operand (B of both products): token itok, key dims ks*16 + kg*8 .. +8
+                bf16x8 qb[8];
+#pragma unroll
+                for (int ks = 0; ks < 8; ks++) qb[ks] = *(const bf16x8*)(cur.q + sw(itok, ks * 16 + kg * 8));
+                // scores P^T = K Q^T on the causal blocks (jb <= ib); key rows in sigma order, so
+                // element 8hh + jj of lane (itok, kg) is key jb*32 + 16hh + kg*8 + jj
+                bf16x8 pt[4];  // 16-key slabs: B operand of V^T P^T
+#pragma unroll
+                for (int jb = 0; jb <= ib; jb++) {
+                    f32x16 sc = {};
+                    const int krow = jb * 32 + sigma(n32);
+#pragma unroll
+                    for (int ks = 0; ks < 8; ks++)
+                        sc = mfma(*(const bf16x8*)(cur.k + sw(krow, ks * 16 + kg * 8)), qb[ks], sc);
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++) {
+                        // head decay: fac[jj] = exp(lambda (itok - jtok)) where itok >= jtok.  The distance
+                        // shrinks by one per jj.  Off the diagonal it is always positive: a plain chain.
+                        // On the diagonal, for moderate decay, the chain starts at jj = 0 (the largest
+                        // distance, at most 31) and multiplies by exp(-lambda): every kept element is
+                        // reached before any masked one (negative distance), whose factor may grow but is
+                        // discarded by the causal mask below.  For stronger decay (exp(31 lambda) could
+                        // underflow) the chain runs downward and restarts at 1 where the distance
+                        // reaches 0.
+                        float fac[8];
+                        if (MODE == DECAY_HEAD) {
+                            const int d0 = 32 * (ib - jb) + n32 - 16 * hh - 8 * kg;
+                            if (jb < ib) {
+                                float gch = decay_pow2(lamb, d0 - 7);
+#pragma unroll
+                                for (int jj = 7; jj >= 0; jj--) {
+                                    fac[jj] = gch;
+                                    gch *= e1b;
+                                }
+                            } else if (up) {
+                                float gch = decay_pow2(lamb, max(d0, 0));
+#pragma unroll
+                                for (int jj = 0; jj < 8; jj++) {
+                                    fac[jj] = gch;
+                                    gch *= einv;
+                                }
+                            } else {
+                                const int d7 = d0 - 7;
+                                float gch = decay_pow2(lamb, max(d7, 0));
+                                fac[7] = gch;
+#pragma unroll
+                                for (int jj = 6; jj >= 0; jj--) {
+                                    gch = (d7 + 7 - jj > 0) ? gch * e1b : 1.f;
+                                    fac[jj] = gch;
+                                }
+                            }
+                        }
+                        bf16x8 x;
+#pragma unroll
+                        for (int jj = 0; jj < 8; jj++) {
+                            const int jtok = jb * 32 + 16 * hh + kg * 8 + jj;
+                            float val = sc[8 * hh + jj];
+                            if (MODE == DECAY_HEAD) val *= fac[jj];
+                            if (jb == ib && jtok > itok) val = 0.f;
+                            x[jj] = (__bf16)val;
+                        }
+                        pt[2 * jb + hh] = x;
+                    }
+                }
+                // O^T for this wave's 32 value columns and the 32 tokens of block ib
+                f32x16 acc = {};
+#pragma unroll
+                for (int m = 0; m < 4; m++)
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++) acc = mfma(sa[m][hh], qb[2 * m + hh], acc);
+                if (MODE == DECAY_HEAD) {
+                    const float f = decay_pow2(lamb, itok + 1);
+#pragma unroll
+                    for (int i = 0; i < 16; i++) acc[i] *= f;
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 2 * (ib + 1); s2++) acc = mfma(vb[s2], pt[s2], acc);
+                // accumulators 0..7 are value columns 32w + 8kg + 0..7 (slot 4w + kg), 8..15 are
+                // 32w + 16 + 8kg + 0..7 (slot 4w + 2 + kg)
+                {
+                    bf16x8 x0, x1;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        x0[e] = (__bf16)acc[e];
+                        x1[e] = (__bf16)acc[8 + e];
+                    }
+                    if (OTILE) {
+                        __bf16* orow = otile + itok * D;
+                        *(bf16x8*)(orow + (((4 * w + kg) ^ (itok & 15)) << 3)) = x0;
+                        *(bf16x8*)(orow + (((4 * w + 2 + kg) ^ (itok & 15)) << 3)) = x1;
+                    } else if (itok < n) {  // gate mode: no room for the tile beside the prepared stages
+                        __bf16* orow = o + (wk.row_base + wk.t_begin + (int64_t)c * C + itok) * D + 32 * w + 8 * kg;
+                        *(bf16x8*)orow = x0;
+                        *(bf16x8*)(orow + 16) = x1;
+                    }
+                }
+            }
+        }
+
+        if (OTILE) lds_barrier();  // the output tile is complete; the loader waves store it
+
+        // state: S <- decay(chunk) S + K^T diag(w) V over the chunk's n tokens
+        if (MODE == DECAY_HEAD) {
+            const float fh = decay_pow2(lamc, n);
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) S[m][i] *= fh;
+            // token t = 16 ks + kg*8 + jj gets exp(lambda (n - 1 - t)), or 0 past the chunk's end;
+            // the exponent grows by one from jj = 7 down to jj = 0
+            if (n == C) {  // every chunk but a ragged last one: no token past the end
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) {
+                    float gch = decay_pow2(lamc, C - 1 - (16 * ks + kg * 8 + 7));
+                    float f[8];
+#pragma unroll
+                    for (int jj = 7; jj >= 0; jj--) {
+                        f[jj] = gch;
+                        gch *= e1;
+                    }
+                    vb[ks] = __builtin_bit_cast(bf16x8, scale8(__builtin_bit_cast(u32x4, vb[ks]), f));
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) {
+                    const int e7 = n - 1 - (16 * ks + kg * 8 + 7);
+                    float gch = decay_pow2(lamc, max(e7, 0));
+#pragma unroll
+                    for (int jj = 7; jj >= 0; jj--) {
+                        const int e = e7 + 7 - jj;
+                        if (jj < 7) gch = (e > 0) ? gch * e1 : 1.f;
+                        vb[ks][jj] = (e >= 0) ? (__bf16)((float)vb[ks][jj] * gch) : (__bf16)0.f;
+                    }
+                }
+            }
+        } else if (n < C) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+                for (int jj = 0; jj < 8; jj++)
+                    if (16 * ks + kg * 8 + jj >= n) vb[ks][jj] = (__bf16)0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {
+                const bf16x8 a = cat(lds_tr16(cur.k + 16 * ks * D + ktoff[m][0]), lds_tr16(cur.k + 16 * ks * D + ktoff[m][1]));
+                S[m] = mfma(a, vb[ks], S[m]);
+            }
+        if (GATE) {
+            // S <- diag(exp(B_end)) (S + Kbar^T V), Kbar = K exp(-B): the same as decaying S and adding
+            // (K exp(B_end - B))^T V.  Rows 4 at a time: element 4 g4 + e of tile m is key row
+            // 32m + sigma(8 g4 + 4 kg) + e.
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; g4++) {
+                    const f32x4 f = *(const f32x4*)(cur.el + 32 * m + sigma(8 * g4 + 4 * kg));
+#pragma unroll
+                    for (int e = 0; e < 4; e++) S[m][4 * g4 + e] *= f[e];
+                }
+        }
+    }
+
+}
+
 template <int MODE, bool STATE_ONLY>
 __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -133,17 +439,12 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     float* __restrict__ part_decay, const float* __restrict__ init_state, int64_t H, int64_t L, int nseg, int G,
     int cps, float inv_norm, __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride,
     uint8_t* __restrict__ tile_live, int* __restrict__ wide_out) {
-    constexpr bool GATE = MODE == DECAY_GATE;
-    constexpr bool OTILE = !STATE_ONLY && !GATE;  // outputs leave through an LDS tile stored by the loaders
-    constexpr int SLOT = STATE_ONLY ? 2 : 3;      // tiles per stage
-    constexpr int STAGE = SLOT * TE + (GATE ? 2 * D : 0);  // gate: D floats of chunk decay after the tiles
-    // ring stages: NST - 1 chunks in flight (gate: the loaders prepare one stage ahead, so three)
-    constexpr int NST = GATE ? 3 : (LDS_TILES - (OTILE ? 1 : 0)) / SLOT;
-    __shared__ __attribute__((aligned(16))) __bf16 ring[NST * STAGE];
+    using LY = Layout<MODE, STATE_ONLY>;
+    constexpr bool GATE = LY::GATE, OTILE = LY::OTILE;
+    __shared__ __attribute__((aligned(16))) __bf16 ring[LY::RING];
     // the chunk's outputs, rows unpadded with 16-byte slot s of row r at s ^ (r % 16)
     __shared__ __attribute__((aligned(16))) __bf16 otile[OTILE ? TE : 8];
     __shared__ int first_dead[4];  // gate loader wave lw: its first chunk with zero cumulative decay
-    using DM = Dma<STATE_ONLY>;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t u = blockIdx.x;
@@ -158,12 +459,9 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     const int64_t t_end = min(t_begin + (int64_t)cps * C, (int64_t)(seg + 1) * Lseg);
     const int64_t row_base = bh * L;
     const int nch = (int)((t_end - t_begin + C - 1) / C);
-    auto stage = [&](int c) {
-        __bf16* b = ring + (c % NST) * STAGE;
-        // q is unused in the state pass
-        return Ring{b, b + (SLOT - 2) * TE, b + (SLOT - 1) * TE, (float*)(b + SLOT * TE)};
-    };
-    auto chunk_len = [&](int c) { return (int)min((int64_t)C, t_end - t_begin - (int64_t)c * C); };
+    const Walk wk{row_base, t_begin, t_end, nch};
+    auto stage = [&](int c) { return LY::stage(ring, c); };
+    auto chunk_len = [&](int c) { return wk.chunk_len(c); };
 
     if (wave >= 4 && GATE) {
         // ---- gate-mode loader wave lw.  Its lanes load q, k, v and g two chunks ahead into
@@ -361,41 +659,12 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
         return;
     }
     if (wave >= 4) {
-        // ---- loader wave: chunk c + 2 is requested as soon as every wave is done with chunk c - 1
-        const int lw = wave - 4;
-        int issued = 0;
-        for (; issued < NST - 1 && issued < nch; issued++)
-            DM::issue(q, k, v, stage(issued), row_base + t_begin + (int64_t)issued * C, chunk_len(issued), lw, lane);
-        for (int c = 0; c < nch; c++) {
-            // this wave's part of chunk c has landed.  Only the younger DMA batches are allowed to be
-            // outstanding: loads complete in order, so while any load of chunk c is pending all
-            // younger loads are too and the count cannot drop that low, whatever the stores do.
-            wait_batches<DM::NDMA>(issued - c - 1);
-            __builtin_amdgcn_s_barrier();  // chunk c is handed to the compute waves
-            if (issued < nch) {
-                DM::issue(q, k, v, stage(issued), row_base + t_begin + (int64_t)issued * C, chunk_len(issued), lw,
-                          lane);
-                issued++;
-            }
-            if (OTILE) {
-                lds_barrier_keep_dma();  // the compute waves have written chunk c's outputs
-                const int n = chunk_len(c);
-                const int64_t r0 = row_base + t_begin + (int64_t)c * C;
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int pc = (threadIdx.x - 256) + 256 * r;
-                    const int row = pc >> 4, sl = pc & 15;
-                    const u32x4 y = *(const u32x4*)(otile + row * D + ((sl ^ (row & 15)) << 3));
-                    if (row < n) *(u32x4*)(o + (r0 + row) * D + sl * 8) = y;
-                }
-            }
-        }
+        loader_walk<MODE, STATE_ONLY>(q, k, v, o, ring, otile, wk, wave - 4, lane);
         return;
     }
 
     // ---- compute wave w: value columns 32 w + sigma(0..31)
     const int w = wave, n32 = lane & 31, kg = lane >> 5;
-    const int G16 = lane >> 4, i16 = lane & 15;
     const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
     const int vcol_lane = 32 * w + sigma(n32);
 
@@ -414,232 +683,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
             for (int i = 0; i < 16; i++) S[m][i] = src ? src[(32 * m + sigma(acc_row(i, kg))) * D + vcol_lane] : 0.f;
     }
 
-    // per-lane LDS offsets of the transposing reads for the first 16-token slab (tokens kg*8 +
-    // {0..3 | 4..7}); slab ks adds 16 ks rows, which leaves the swizzle (row bits 0-3) unchanged.
-    // The 4-column group a = i16 % 4 that a read fetches is placed at 4 (bits of a swapped), the
-    // sigma order.
-    const int quad = 4 * (((i16 & 1) << 1) | ((i16 >> 1) & 1));
-    const int tb = (G16 >> 1) * 8 + (i16 >> 2);
-    int voff[2];      // V: value column vcol_lane
-    int ktoff[4][2];  // K for the state: key column 32m + sigma(n32)
-    {
-        const int vcol = 32 * w + (G16 & 1) * 16 + quad;
-        voff[0] = sw(tb, vcol);
-        voff[1] = sw(tb + 4, vcol);
-#pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const int kcol = 32 * m + (G16 & 1) * 16 + quad;
-            ktoff[m][0] = sw(tb, kcol);
-            ktoff[m][1] = sw(tb + 4, kcol);
-        }
-    }
-
-    for (int c = 0; c < nch; c++) {
-        const Ring cur = stage(c);
-        const int n = chunk_len(c);
-        // Head decay: the factors exp(lambda d) are recomputed every chunk from a few base-2
-        // exponentials and chains of multiplications by exp(lambda) (every factor <= 1).  Hiding
-        // lambda's value from the optimiser each chunk keeps these loop invariants from being
-        // hoisted into registers for the whole loop.
-        float lamc = lam;
-        if (MODE == DECAY_HEAD) asm volatile("" : "+s"(lamc));
-        lamc *= LOG2E;
-        const float e1 = (MODE == DECAY_HEAD) ? decay_pow2(lamc, 1) : 1.f;
-        lds_barrier();  // chunk c has landed; every wave is done with chunk c - 1
-
-        // V operand: tokens 16ks + kg*8 + jj (plain order), value column vcol_lane
-        bf16x8 vb[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-            vb[ks] = cat(lds_tr16(cur.v + 16 * ks * D + voff[0]), lds_tr16(cur.v + 16 * ks * D + voff[1]));
-
-        if (!STATE_ONLY) {
-            // the state as A operands of S^T Qbar^T: slab (m, hh) holds key dims 32m + 16hh + kg*8 + jj
-            bf16x8 sa[4][2];
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-#pragma unroll
-                for (int hh = 0; hh < 2; hh++) {
-                    bf16x8 x;
-#pragma unroll
-                    for (int jj = 0; jj < 8; jj++) x[jj] = (__bf16)S[m][8 * hh + jj];
-                    sa[m][hh] = x;
-                }
-#pragma unroll
-            for (int ib = 0; ib < 2; ib++) {
-                const int itok = ib * 32 + n32;
-                // the diagonal block's decay factors are the same for both halves: recomputing them
-                // is cheaper than keeping them live
-                float lamb = lam;
-                if (MODE == DECAY_HEAD) asm volatile("" : "+s"(lamb));
-                lamb *= LOG2E;
-                const float e1b = (MODE == DECAY_HEAD) ? decay_pow2(lamb, 1) : 1.f;
-                const float einv = (MODE == DECAY_HEAD) ? __builtin_amdgcn_exp2f(-lamb) : 1.f;
-                // the upward chain below needs exp(31 lambda) to stay a normal float
-                const bool up = lamb >= -4.f;
-                // Q operand (B of both products): token itok, key dims ks*16 + kg*8 .. +8
-                bf16x8 qb[8];
-#pragma unroll
-                for (int ks = 0; ks < 8; ks++) qb[ks] = *(const bf16x8*)(cur.q + sw(itok, ks * 16 + kg * 8));
-                // scores P^T = K Q^T on the causal blocks (jb <= ib); key rows in sigma order, so
-                // element 8hh + jj of lane (itok, kg) is key jb*32 + 16hh + kg*8 + jj
-                bf16x8 pt[4];  // 16-key slabs: B operand of V^T P^T
-#pragma unroll
-                for (int jb = 0; jb <= ib; jb++) {
-                    f32x16 sc = {};
-                    const int krow = jb * 32 + sigma(n32);
-#pragma unroll
-                    for (int ks = 0; ks < 8; ks++)
-                        sc = mfma(*(const bf16x8*)(cur.k + sw(krow, ks * 16 + kg * 8)), qb[ks], sc);
-#pragma unroll
-                    for (int hh = 0; hh < 2; hh++) {
-                        // head decay: fac[jj] = exp(lambda (itok - jtok)) where itok >= jtok.  The distance
-                        // shrinks by one per jj.  Off the diagonal it is always positive: a plain chain.
-                        // On the diagonal, for moderate decay, the chain starts at jj = 0 (the largest
-                        // distance, at most 31) and multiplies by exp(-lambda): every kept element is
-                        // reached before any masked one (negative distance), whose factor may grow but is
-                        // discarded by the causal mask below.  For stronger decay (exp(31 lambda) could
-                        // underflow) the chain runs downward and restarts at 1 where the distance
-                        // reaches 0.
-                        float fac[8];
-                        if (MODE == DECAY_HEAD) {
-                            const int d0 = 32 * (ib - jb) + n32 - 16 * hh - 8 * kg;
-                            if (jb < ib) {
-                                float gch = decay_pow2(lamb, d0 - 7);
-#pragma unroll
-                                for (int jj = 7; jj >= 0; jj--) {
-                                    fac[jj] = gch;
-                                    gch *= e1b;
-                                }
-                            } else if (up) {
-                                float gch = decay_pow2(lamb, max(d0, 0));
-#pragma unroll
-                                for (int jj = 0; jj < 8; jj++) {
-                                    fac[jj] = gch;
-                                    gch *= einv;
-                                }
-                            } else {
-                                const int d7 = d0 - 7;
-                                float gch = decay_pow2(lamb, max(d7, 0));
-                                fac[7] = gch;
-#pragma unroll
-                                for (int jj = 6; jj >= 0; jj--) {
-                                    gch = (d7 + 7 - jj > 0) ? gch * e1b : 1.f;
-                                    fac[jj] = gch;
-                                }
-                            }
-                        }
-                        bf16x8 x;
-#pragma unroll
-                        for (int jj = 0; jj < 8; jj++) {
-                            const int jtok = jb * 32 + 16 * hh + kg * 8 + jj;
-                            float val = sc[8 * hh + jj];
-                            if (MODE == DECAY_HEAD) val *= fac[jj];
-                            if (jb == ib && jtok > itok) val = 0.f;
-                            x[jj] = (__bf16)val;
-                        }
-                        pt[2 * jb + hh] = x;
-                    }
-                }
-                // O^T for this wave's 32 value columns and the 32 tokens of block ib
-                f32x16 acc = {};
-#pragma unroll
-                for (int m = 0; m < 4; m++)
-#pragma unroll
-                    for (int hh = 0; hh < 2; hh++) acc = mfma(sa[m][hh], qb[2 * m + hh], acc);
-                if (MODE == DECAY_HEAD) {
-                    const float f = decay_pow2(lamb, itok + 1);
-#pragma unroll
-                    for (int i = 0; i < 16; i++) acc[i] *= f;
-                }
-#pragma unroll
-                for (int s2 = 0; s2 < 2 * (ib + 1); s2++) acc = mfma(vb[s2], pt[s2], acc);
-                // accumulators 0..7 are value columns 32w + 8kg + 0..7 (slot 4w + kg), 8..15 are
-                // 32w + 16 + 8kg + 0..7 (slot 4w + 2 + kg)
-                {
-                    bf16x8 x0, x1;
-#pragma unroll
-                    for (int e = 0; e < 8; e++) {
-                        x0[e] = (__bf16)acc[e];
-                        x1[e] = (__bf16)acc[8 + e];
-                    }
-                    if (OTILE) {
-                        __bf16* orow = otile + itok * D;
-                        *(bf16x8*)(orow + (((4 * w + kg) ^ (itok & 15)) << 3)) = x0;
-                        *(bf16x8*)(orow + (((4 * w + 2 + kg) ^ (itok & 15)) << 3)) = x1;
-                    } else if (itok < n) {  // gate mode: no room for the tile beside the prepared stages
-                        __bf16* orow = o + (row_base + t_begin + (int64_t)c * C + itok) * D + 32 * w + 8 * kg;
-                        *(bf16x8*)orow = x0;
-                        *(bf16x8*)(orow + 16) = x1;
-                    }
-                }
-            }
-        }
-
-        if (OTILE) lds_barrier();  // the output tile is complete; the loader waves store it
-
-        // state: S <- decay(chunk) S + K^T diag(w) V over the chunk's n tokens
-        if (MODE == DECAY_HEAD) {
-            const float fh = decay_pow2(lamc, n);
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-#pragma unroll
-                for (int i = 0; i < 16; i++) S[m][i] *= fh;
-            // token t = 16 ks + kg*8 + jj gets exp(lambda (n - 1 - t)), or 0 past the chunk's end;
-            // the exponent grows by one from jj = 7 down to jj = 0
-            if (n == C) {  // every chunk but a ragged last one: no token past the end
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) {
-                    float gch = decay_pow2(lamc, C - 1 - (16 * ks + kg * 8 + 7));
-                    float f[8];
-#pragma unroll
-                    for (int jj = 7; jj >= 0; jj--) {
-                        f[jj] = gch;
-                        gch *= e1;
-                    }
-                    vb[ks] = __builtin_bit_cast(bf16x8, scale8(__builtin_bit_cast(u32x4, vb[ks]), f));
-                }
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) {
-                    const int e7 = n - 1 - (16 * ks + kg * 8 + 7);
-                    float gch = decay_pow2(lamc, max(e7, 0));
-#pragma unroll
-                    for (int jj = 7; jj >= 0; jj--) {
-                        const int e = e7 + 7 - jj;
-                        if (jj < 7) gch = (e > 0) ? gch * e1 : 1.f;
-                        vb[ks][jj] = (e >= 0) ? (__bf16)((float)vb[ks][jj] * gch) : (__bf16)0.f;
-                    }
-                }
-            }
-        } else if (n < C) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++)
-#pragma unroll
-                for (int jj = 0; jj < 8; jj++)
-                    if (16 * ks + kg * 8 + jj >= n) vb[ks][jj] = (__bf16)0.f;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                const bf16x8 a = cat(lds_tr16(cur.k + 16 * ks * D + ktoff[m][0]), lds_tr16(cur.k + 16 * ks * D + ktoff[m][1]));
-                S[m] = mfma(a, vb[ks], S[m]);
-            }
-        if (GATE) {
-            // S <- diag(exp(B_end)) (S + Kbar^T V), Kbar = K exp(-B): the same as decaying S and adding
-            // (K exp(B_end - B))^T V.  Rows 4 at a time: element 4 g4 + e of tile m is key row
-            // 32m + sigma(8 g4 + 4 kg) + e.
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; g4++) {
-                    const f32x4 f = *(const f32x4*)(cur.el + 32 * m + sigma(8 * g4 + 4 * kg));
-#pragma unroll
-                    for (int e = 0; e < 4; e++) S[m][4 * g4 + e] *= f[e];
-                }
-        }
-    }
+    compute_walk<MODE, STATE_ONLY>(S, ring, otile, o, lam, wk, w, lane);
 
     float* dst = nullptr;
     if (STATE_ONLY) dst = part_state + (ub * (G - 1) + g) * (int64_t)D * D;
@@ -653,6 +697,219 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     if (STATE_ONLY && !GATE && threadIdx.x < D)
         part_decay[(ub * (G - 1) + g) * D + threadIdx.x] =
             (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;
+}
+
+// ---- the chained forward: the whole split in one launch
+//
+// The split forward's three launches (state pass, scan over the sub-segments, output pass) fused
+// into one.  A workgroup takes a ticket (an atomic counter) that names its unit -- sub-segment j
+// of chain (b, h, segment), j-major -- and then
+//   1. (j < G - 1) walks the sub-segment's k, v from a zero state: its aggregate A_j, the local
+//      end state, which each compute wave stores (its 32 value columns) and flags;
+//   2. once every aggregate of its chain is flagged, scans its 1/G slice of the state elements
+//      over the chain in order, I_k = Lambda_k I_{k-1} + A_k from I_{-1} = s_in (the state-combine
+//      rule of the ZeCO review page, pith_extraction.key_machinery, applied between sub-segments),
+//      and stores the slice of every I_k, the exact state at the end of sub-segment k;
+//   3. once every slice is flagged, reads its incoming state I_{j-1} (s_in for j = 0);
+//   4. walks the sub-segment again from I_{j-1} and writes its outputs (the output pass); the last
+//      sub-segment writes s_out.
+// Each element's scan runs in one thread in one fixed order, so the result does not depend on
+// timing.  The loader waves start the output pass's loads while the compute waves hand off.  The
+// waits in steps 2 and 3 span the whole chain, so every workgroup of the launch must be resident
+// at once: the launcher uses this kernel only when the grid fits the device's compute units (one
+// workgroup each).  Waits are bounded as well: a wave that polls a flag spin_limit times without
+// seeing it set gives up and makes its state NaN, so the outputs show it rather than the GPU
+// hanging.
+// Workspace (per chain, per sub-segment but the last, per compute wave): 16 KiB of aggregate and
+// 16 KiB of scanned state; int flags for the aggregates and for the slices; the ticket counter.
+// Flags and ticket start at zero (chain_reset_kernel).
+constexpr int CH_WAVE_FLOATS = 64 * 64;  // one compute wave's part of a state
+
+__global__ __launch_bounds__(256) void chain_reset_kernel(int* __restrict__ flags, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) flags[i] = 0;
+}
+
+// The hand-off data and flags are read and written as device-scope (agent) relaxed atomics: each
+// access is coherent across the XCDs' separate L2 caches by itself (the sc1 bit), so publishing a
+// state needs no write-back of the whole L2 and reading one no invalidation of it -- the release
+// and acquire fences that would do that cost more than the rest of the kernel here.  Ordering:
+// a publisher waits until its data stores are acknowledged before it stores the flag; a reader
+// issues its data loads only after the flag load has returned (the loop below exits on its value).
+__device__ __forceinline__ float ld_dev(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_dev(float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Polls the n flags f[0], f[stride], ... (lane l reads flags l, l + 64, ...) until all are nonzero,
+// at most `limit` times; true when they all were.
+__device__ __forceinline__ bool chain_wait_all(const int* f, int64_t stride, int n, int limit, int lane) {
+    for (int it = 0; it < limit; it++) {
+        bool mine = true;
+        for (int i = lane; i < n; i += 64)
+            mine = mine && __hip_atomic_load(f + i * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+        if (__all(mine)) {
+            asm volatile("" ::: "memory");  // no later load moves above the flags'
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
+
+// Sets *f = v once every earlier store of the wave has completed.
+__device__ __forceinline__ void chain_publish(int* f, int v, int lane) {
+    asm volatile("" ::: "memory");
+    waitcnt<0, 0>();
+    if (lane == 0) __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One compute wave's 64 state elements per lane: element (m, i) of lane l at (16 m + i) * 64 + l,
+// so that each access instruction covers 256 contiguous bytes.
+__device__ __forceinline__ void chain_store(float* buf, const f32x16 (&X)[4], int lane) {
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) st_dev(buf + (16 * m + i) * 64 + lane, X[m][i]);
+}
+
+__device__ __forceinline__ void chain_load(f32x16 (&X)[4], const float* buf, int lane) {
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) X[m][i] = ld_dev(buf + (16 * m + i) * 64 + lane);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT, 1) void pipe_chain_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const float* __restrict__ decay, const float* __restrict__ s_in, __bf16* __restrict__ o,
+    float* __restrict__ s_out, int64_t s_out_stride, float* __restrict__ agg, float* __restrict__ incl,
+    int* __restrict__ flags, int* __restrict__ ticket, int64_t H, int64_t L, int nseg, int G, int cps,
+    int spin_limit) {
+    static_assert(MODE != DECAY_GATE, "the chained forward covers the no-decay and head-decay modes");
+    using LS = Layout<MODE, true>;
+    using LO = Layout<MODE, false>;
+    static_assert(LS::RING <= LDS_TILES * TE && LO::RING + TE <= LDS_TILES * TE, "LDS budget");
+    // one LDS block: the state pass's ring, then the output pass's ring and output tile
+    __shared__ __attribute__((aligned(16))) __bf16 lds[LDS_TILES * TE];
+    __bf16* const otile = lds + LO::RING;
+
+    // the ticket passes through the first word of the ring, which every wave reads before any
+    // wave goes on to fill the ring
+    if (threadIdx.x == 0) *(int*)lds = atomicAdd(ticket, 1);
+    __syncthreads();
+    const int tk = *(const int*)lds;
+    __syncthreads();
+    const int64_t units = (int64_t)gridDim.x / G;  // chains: B * H * nseg
+    const int j = (int)(tk / units);
+    const int64_t ub = tk % units;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int seg = (int)(ub % nseg);
+    const int64_t bh = ub / nseg;
+    const int64_t h = bh % H;
+    const int64_t Lseg = L / nseg;
+    const int64_t t_begin = (int64_t)seg * Lseg + (int64_t)j * cps * C;
+    const int64_t t_end = min(t_begin + (int64_t)cps * C, (int64_t)(seg + 1) * Lseg);
+    const Walk wk{bh * L, t_begin, t_end, (int)((t_end - t_begin + C - 1) / C)};
+    const bool publish = j < G - 1;
+
+    if (wave >= 4) {
+        if (publish) loader_walk<MODE, true>(q, k, v, o, lds, nullptr, wk, wave - 4, lane);
+        __builtin_amdgcn_s_barrier();  // every wave is done with the state pass's stages
+        loader_walk<MODE, false>(q, k, v, o, lds, otile, wk, wave - 4, lane);
+        return;
+    }
+
+    const int w = wave, n32 = lane & 31, kg = lane >> 5;
+    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
+    const int vcol_lane = 32 * w + sigma(n32);
+    // every published sub-segment is cps whole chunks long, so one decay serves them all
+    const float lam_sub = (MODE == DECAY_HEAD) ? decay_pow(lam, cps * C) : 1.f;
+    auto wave_buf = [&](float* base, int jj) { return base + ((ub * (G - 1) + jj) * 4 + w) * (int64_t)CH_WAVE_FLOATS; };
+    // flags: the aggregates' (sub-segment jj <= G - 2, wave w), then the scan slices' (unit jj, wave w)
+    auto agg_flag = [&](int jj) { return flags + (ub * (G - 1) + jj) * 4 + w; };
+    auto slice_flag = [&](int jj) { return flags + units * (G - 1) * 4 + (ub * G + jj) * 4 + w; };
+
+    // 1. the aggregate (accumulator element i of tile m <-> key row 32m + sigma(acc_row(i)), value
+    // column vcol_lane, as in the split forward)
+    f32x16 S[4];
+#pragma unroll
+    for (int m = 0; m < 4; m++) S[m] = f32x16{};
+    if (publish) compute_walk<MODE, true>(S, lds, nullptr, o, lam, wk, w, lane);
+    lds_barrier();  // the state pass's stages are free for the output pass's loads
+    if (publish) {
+        chain_store(wave_buf(agg, j), S, lane);
+        chain_publish(agg_flag(j), 1, lane);
+    }
+
+    // 2. this unit's slice of the scan over the chain: wave w folds the elements [lo, hi) of every
+    // state's wave-w part (element x = 64 (16 m + i) + lane'), over the sub-segments in order,
+    // I_k = Lambda I_{k-1} + A_k from I_{-1} = s_in, and stores I_0 .. I_{G-2} there
+    bool ok = chain_wait_all(agg_flag(0), 4, G - 1, spin_limit, lane);
+    {
+        const int per = (CH_WAVE_FLOATS + G - 1) / G;
+        const int lo = min(j * per, CH_WAVE_FLOATS), hi = min(lo + per, CH_WAVE_FLOATS);
+        const float* src = (seg == 0 && s_in) ? s_in + bh * (int64_t)D * D : nullptr;
+        // four elements x0 + 64 r of the lane at a time, 16 aggregates each: up to 64 loads in flight
+        for (int x0 = lo + lane; x0 < hi; x0 += 256) {
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int x = x0 + 64 * r, mi = x >> 6, l2 = x & 63;
+                y[r] = (src && x < hi)
+                           ? src[(32 * (mi >> 4) + sigma(acc_row(mi & 15, l2 >> 5))) * D + 32 * w + sigma(l2 & 31)]
+                           : 0.f;
+            }
+            for (int k0 = 0; k0 < G - 1; k0 += 16) {
+                float a[4][16];
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+#pragma unroll
+                    for (int b = 0; b < 16; b++)
+                        a[r][b] = (k0 + b < G - 1 && x0 + 64 * r < hi) ? ld_dev(wave_buf(agg, k0 + b) + x0 + 64 * r) : 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+#pragma unroll
+                    for (int b = 0; b < 16; b++) {
+                        if (k0 + b < G - 1 && x0 + 64 * r < hi) {
+                            y[r] = (MODE == DECAY_HEAD) ? lam_sub * y[r] + a[r][b] : y[r] + a[r][b];
+                            st_dev(wave_buf(incl, k0 + b) + x0 + 64 * r, ok ? y[r] : __builtin_nanf(""));
+                        }
+                    }
+            }
+        }
+        chain_publish(slice_flag(j), 1, lane);
+    }
+
+    // 3. the incoming state I_{j-1}, once every unit of the chain has stored its slice
+    f32x16 I[4];
+    if (j == 0) {
+        const float* src = (seg == 0 && s_in) ? s_in + bh * (int64_t)D * D : nullptr;
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) I[m][i] = src ? src[(32 * m + sigma(acc_row(i, kg))) * D + vcol_lane] : 0.f;
+    } else {
+        ok = ok && chain_wait_all(slice_flag(0), 4, G, spin_limit, lane);
+        chain_load(I, wave_buf(incl, j - 1), lane);
+        if (!ok) {
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) I[m][e] = __builtin_nanf("");
+        }
+    }
+
+    // 4. the outputs, from the exact incoming state
+#pragma unroll
+    for (int m = 0; m < 4; m++) S[m] = I[m];
+    compute_walk<MODE, false>(S, lds, otile, o, lam, wk, w, lane);
+    if (j == G - 1 && s_out) {
+        float* dst = s_out + bh * s_out_stride + (int64_t)seg * D * D;
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) dst[(32 * m + sigma(acc_row(i, kg))) * D + vcol_lane] = S[m][i];
+    }
 }
 
 template <int MODE>
@@ -686,7 +943,38 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
     return e;
 }
 
+template <int MODE>
+hipError_t launch_chain_mode(const FwdArgs& a, int G, int cps, float* ws) {
+    const int64_t units = a.B * a.H * a.nseg;
+    const size_t nst = (size_t)units * (G - 1) * 4 * CH_WAVE_FLOATS;
+    float* agg = ws;
+    float* incl = ws + nst;
+    int* flags = (int*)(ws + 2 * nst);
+    const int64_t nflags = units * (G - 1) * 4 + units * G * 4;
+    int* ticket = flags + nflags;
+    LA_TRACED(a.tr, "chunk_fwd_chain_reset",
+              chain_reset_kernel<<<(unsigned)((nflags + 1 + 255) / 256), 256, 0, a.stream>>>(flags, nflags + 1));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // about four seconds of polling before a wave gives up on a flag
+    constexpr int SPIN_LIMIT = 1 << 22;
+    LA_TRACED(a.tr, "chunk_fwd_chain_output_pass",
+              pipe_chain_kernel<MODE><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                  (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.decay, a.s_in, (__bf16*)a.o,
+                  a.s_out, a.s_out_stride, agg, incl, flags, ticket, a.H, a.L, a.nseg, G, cps, SPIN_LIMIT));
+    return hipGetLastError();
+}
+
 }  // namespace
+
+size_t chain_workspace_floats(const FwdArgs& a, int G) {
+    const size_t units = (size_t)(a.B * a.H * a.nseg);
+    return 2 * units * (G - 1) * 4 * CH_WAVE_FLOATS + units * (G - 1) * 4 + units * G * 4 + 1;
+}
+
+hipError_t launch_chunk_fwd_chain(const FwdArgs& a, int G, int cps, float* ws) {
+    return a.mode == DECAY_HEAD ? launch_chain_mode<DECAY_HEAD>(a, G, cps, ws) : launch_chain_mode<DECAY_NONE>(a, G, cps, ws);
+}
 
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay, int* wide) {
     switch (a.mode) {

@@ -115,7 +115,28 @@ static size_t gate_flag_words(const FwdArgs& a, int G) {
     return (a.mode == DECAY_GATE && a.dk == 128 && a.chunk == 64) ? 4 * (size_t)(a.B * a.H * a.nseg) * (2 * G - 1)
                                                                    : 0;
 }
+// The chained single launch replaces the passes when the caller asks for it (fwd_schedule 2) and
+// it exists: bf16 d = 128, 64-token chunks, no or head decay, a segment split at all.  It is not
+// the default: on MI355X at B1 H16 L16384 the passes take 84.5 us (state pass, scan, output pass)
+// and the chained kernel 84.8 us plus its flag reset, about 6 us.
+// Its workgroups wait on one another across the whole chain, so all of them must be resident at
+// once: one per compute unit.
+static int compute_units() {
+    static std::mutex mu;
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus[dev] = 0;
+    return cus[dev];
+}
+static bool use_chain(const FwdArgs& a, int G) {
+    return G > 1 && a.schedule == 2 && a.dk == 128 && a.dv == 128 && a.chunk == 64 && a.mode != DECAY_GATE &&
+           a.B * a.H * a.nseg * G <= compute_units();
+}
 size_t fwd_split_workspace_floats(const FwdArgs& a, int G) {
+    if (use_chain(a, G)) return chain_workspace_floats(a, G);
     const size_t flags = gate_flag_words(a, G);
     if (G <= 1) return flags;
     const size_t n = (size_t)(a.B * a.H * a.nseg) * (size_t)(G - 1);
@@ -128,6 +149,7 @@ namespace {
 // The kernels of the split forward with the workspace at ws (fwd_split_workspace_floats floats;
 // unused when G == 1).
 hipError_t fwd_split_run(const FwdArgs& a, int G, int cps, float* ws) {
+    if (use_chain(a, G)) return launch_chunk_fwd_chain(a, G, cps, ws);
     const size_t n = G > 1 ? (size_t)(a.B * a.H * a.nseg) * (size_t)(G - 1) : 0;
     float* part_state = G > 1 ? ws : nullptr;
     float* part_decay = G > 1 ? ws + n * a.dk * a.dk : nullptr;

@@ -96,6 +96,7 @@ la_status check_fwd_shape(const la_shape* s, int chunk) {
     la_status st = check_common(s);
     if (st != LA_OK) return st;
     if (chunk <= 0 || s->subseg_chunks < 0 || s->state_stride < 0) return LA_ERR_SHAPE;
+    if (s->fwd_schedule < 0 || s->fwd_schedule > 2) return LA_ERR_SHAPE;
     if (!stride_ok(s->state_stride, (int64_t)s->nseg * s->dk * s->dv, s)) return LA_ERR_SHAPE;
     if (!fwd_chunk_ok(s, chunk)) return LA_ERR_UNSUPPORTED;
     if ((st = check_dtype(s)) != LA_OK) return st;
@@ -209,6 +210,7 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const floa
     a.mode = s->decay_mode;
     a.inv_norm = s->decay_mode == LA_DECAY_GATE ? 1.f / s->gate_norm : 1.f;
     a.subseg_chunks = s->subseg_chunks;
+    a.schedule = s->fwd_schedule;
     a.stream = stream;
     a.tr = &tr;
     a.q_dec = q_dec;

@@ -54,6 +54,7 @@ struct FwdArgs {
     int mode;
     float inv_norm;      // 1 / gate_norm (gate mode)
     int subseg_chunks;   // 0 = automatic
+    int schedule = 0;    // la_shape.fwd_schedule: 0 = library choice (passes), 1 = passes, 2 = chained where available
     hipStream_t stream;
     Tracer* tr;
     void* q_dec = nullptr;     // optional: q times its cumulative decay from the segment start
@@ -145,6 +146,11 @@ size_t fwd_split_workspace_floats(const FwdArgs& a, int G);
 // Its kernels: G sub-segments of cps chunks; part_state / part_decay the workspace of the
 // sub-segment scan (unused when G == 1); gate mode: wide the 4 * B*H*nseg * (2G - 1) ints of the
 // per-unit flags that send a unit to the windowed redo (unused otherwise).
+// The chained d = 128 forward (no decay or head decay, G > 1 sub-segments): one launch (after a
+// small flag reset) whose workgroups hand their sub-segment states on through the workspace
+// (chain_workspace_floats floats).
+size_t chain_workspace_floats(const FwdArgs& a, int G);
+hipError_t launch_chunk_fwd_chain(const FwdArgs& a, int G, int cps, float* ws);
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay, int* wide);
 // The same for dk = dv = 32 or 64 (chunk_fwd_small.hip).
 hipError_t launch_chunk_fwd_small(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);

@@ -20,6 +20,11 @@ correction.
                      the closed form, the cumulative decay formed inside the correction.  Gate
                      decay: the forward itself emits Q * cumulative decay and Lambda
                      (la_chunk_fwd_decayed), and the correction adds a plain product.
+``ExactStep``     -- the same outputs and S_out from one la_chunk_fwd call that starts from S_recv: the
+                     library splits the segment into sub-segments itself, scans their local states
+                     with S_recv as the first entry and runs every sub-segment's outputs from its
+                     exact incoming state (no correction pass); ``schedule`` picks the library's
+                     separate passes or its chained single launch.
 ``segmented_forward`` -- P devices emulated on one GPU: the local forward of all P segments in
                      one launch, the P-entry state scan, and the correction of segments 1..P-1.
 """
@@ -113,6 +118,30 @@ class DeviceStep:
         la_state_scan(self.states, self.totals if self.mode != "none" else None, self.states, timer=t.get("scan"))
         _correct(self, self.states[:, :, 0:G], G, 0, t)
         return self.o, self.states[:, :, G]
+
+
+class ExactStep:
+    """One device step as a single exact forward from S_recv (la_chunk_fwd with s_in = S_recv);
+    ``run()`` may be timed or graph-captured.  Returns (o, s_out [B,H,dk,dv])."""
+
+    def __init__(self, q, k, v, decay, s_recv, *, mode: str, chunk: int = 64, gate_norm: float = 16.0,
+                 subseg_chunks: int = 0, schedule: str = "auto"):
+        B, H, L, dk = q.shape
+        dv = v.shape[-1]
+        self.q, self.k, self.v, self.decay, self.s_recv = q, k, v, decay, s_recv
+        self.mode, self.chunk, self.gate_norm = mode, chunk, gate_norm
+        self.subseg_chunks, self.schedule = subseg_chunks, schedule
+        self.shape = (B, H, L, dk, dv)
+        self.o = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+        self.s_out = torch.empty((B, H, 1, dk, dv), dtype=torch.float32, device=q.device)
+
+    def run(self, timers: Optional[dict] = None):
+        """One step.  ``timers`` optionally maps "fwd" to a KernelTimer."""
+        t = timers or {}
+        la_chunk_fwd(self.q, self.k, self.v, self.decay, self.s_recv, self.o, self.s_out, mode=self.mode,
+                     chunk=self.chunk, gate_norm=self.gate_norm, subseg_chunks=self.subseg_chunks,
+                     schedule=self.schedule, timer=t.get("fwd"))
+        return self.o, self.s_out[:, :, 0]
 
 
 def device_step(q, k, v, decay, s_recv, *, mode: str, chunk: int = 64, gate_norm: float = 16.0,

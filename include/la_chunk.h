@@ -105,6 +105,14 @@ typedef struct la_shape {
                              decomposition identity applied inside the GPU); 0 = choose
                              automatically, >= 1 forces that length.  Changes the rounding order
                              only, never the mathematical result. */
+    int32_t fwd_schedule; /* la_chunk_fwd / la_chunk_fwd_noalloc, matrix-core kernels, when a
+                             segment is split into sub-segments: 0 = the library's choice (on this
+                             build: 1), 1 = separate passes (local states, a scan over them, then
+                             the outputs from the exact incoming states), 2 = one launch whose
+                             workgroups hand the sub-segment states on through flags (bf16,
+                             dk = dv = 128, chunk 64, no or per-head decay, and only when every
+                             workgroup fits on the device at once; otherwise 1).  Changes the
+                             rounding order only. */
     void* stream;         /* hipStream_t the work is enqueued on; NULL = default stream */
     la_trace* trace;      /* optional per-kernel event recording (NULL = off); see la_trace */
 } la_shape;

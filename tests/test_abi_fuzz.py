@@ -53,6 +53,7 @@ def _random_shape(rng):
     s.state_stride = _pick(rng, [0], I64)
     s.total_stride = _pick(rng, [0], I64)
     s.subseg_chunks = _pick(rng, [0, 1, 4], I32)
+    s.fwd_schedule = _pick(rng, [0, 1, 2], [3, -1, 1 << 30], 0.1)
     s.stream = None
     return s
 

@@ -127,3 +127,46 @@ def test_backward_full_size(wid, pairs, want_decay):
             got = float(dd[h])
             print(f"  d_lambda[{h}] gpu {got:.6e} pairs {ref:.6e}")
             assert abs(got - ref) <= TOL["bf16"] * abs(ref), h
+
+
+@pytest.mark.parametrize("wid,b_list,h,want_decay", [(1, [0], 9, False),
+                                                     (2, [0, 1], 14, True),
+                                                     (3, [2], 7, True)])
+def test_backward_full_size_dense_d_o(wid, b_list, h, want_decay):
+    """The same sizes and launch configuration with d_o drawn on every token: the oracle's backward
+    runs over the whole 16384-token sequence of every sampled (b, h) (its state trajectory kept
+    whole, about 2 GB per sequence), and every token of dq, dk, dv (and dg) is compared, with
+    ds_in.  Head decay: both batch entries of head h are sampled, so the oracle's d lambda_h is
+    complete and is compared too."""
+    w = WORKLOADS[wid]
+    note(f"la_chunk_bwd full size, dense d_o, workload {wid} {w.name}, d_decay={want_decay}, b {b_list} h {h}")
+    inp = make_inputs(w, "cuda")
+    gr = make_grads(w, device="cuda")
+    dq, dk, dv, dd, ds_in = lb.la_chunk_bwd(inp["q"], inp["k"], inp["v"], gr["d_o"], inp["decay"], inp["s_in"],
+                                            gr["ds_out"], mode=w.mode, chunk=w.chunk, want_decay=want_decay)
+    torch.cuda.synchronize()
+    sel = lambda t: host32(t[b_list, h][:, None])  # noqa: E731  [nb, 1, ...]
+    if w.mode == "none":
+        dec = None
+    elif w.mode == "gate":
+        dec = sel(inp["decay"])
+    else:
+        dec = host32(inp["decay"])[h:h + 1]
+    s_in = None if inp["s_in"] is None else sel(inp["s_in"]).astype(np.float64)
+    e_dq, e_dk, e_dv, e_dd, e_ds = oracle.recurrence_bwd(
+        sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(gr["d_o"]), ORC_MODE[w.mode], dec, s_in,
+        host32(gr["ds_out"][b_list, h][:, None]).astype(np.float64), gate_norm=w.gate_norm, threads=len(b_list))
+    for i, b in enumerate(b_list):
+        for name, got, ref in (("dq", dq, e_dq), ("dk", dk, e_dk), ("dv", dv, e_dv)):
+            err = rel_err(got[b, h], ref[i, 0])
+            print(f"  {name} ({b},{h}) rel err {err:.2e}")
+            assert err <= TOL["bf16"], (name, b, h, err)
+        assert rel_err(ds_in[b, h, 0], e_ds[i, 0, 0].astype(np.float32)) <= TOL["bf16"], ("ds_in", b, h)
+        if want_decay and w.mode == "gate":
+            err = rel_err(dd[b, h], e_dd[i, 0])
+            print(f"  dg ({b},{h}) rel err {err:.2e}")
+            assert err <= TOL["bf16"], ("dg", b, h, err)
+    if want_decay and w.mode == "head":
+        got, ref = float(dd[h]), float(e_dd[0])
+        print(f"  d_lambda[{h}] gpu {got:.6e} oracle {ref:.6e}")
+        assert abs(got - ref) <= TOL["bf16"] * abs(ref), (h, got, ref)

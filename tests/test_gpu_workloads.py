@@ -10,7 +10,7 @@ import torch
 import oracle
 from chunked_scan_amd import binding as lb
 from chunked_scan_amd.inputs import WORKLOADS, make_inputs
-from chunked_scan_amd.pipeline import DeviceStep, SegmentedForward
+from chunked_scan_amd.pipeline import DeviceStep, ExactStep, SegmentedForward
 
 from gpu_util import ORC_MODE, TOL, host32, note, rel_err
 
@@ -50,13 +50,16 @@ def test_workload_device_step(wid, pairs):
     for n, (b, h) in enumerate(pairs):
         assert rel_err(o[b, h], o_ref[n]) <= TOL["bf16"], (b, h)
         assert rel_err(s_out[b, h], s_ref[n]) <= TOL["bf16"], (b, h)
-    # the direct route (s_in given to the local forward) agrees with the decomposed one
-    o2, s2 = lb.la_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode,
-                             gate_norm=w.gate_norm)
-    torch.cuda.synchronize()
-    for n, (b, h) in enumerate(pairs):
-        assert rel_err(o2[b, h], o_ref[n]) <= TOL["bf16"], (b, h)
-        assert rel_err(s2[b, h, 0], s_ref[n]) <= TOL["bf16"], (b, h)
+    # the exact form (one la_chunk_fwd from S_recv: the benchmark's headline step), with the
+    # library's default schedule and, where it exists, the chained single launch
+    for schedule in ("auto", "chained") if w.mode != "gate" else ("auto",):
+        note(f"workload {wid}: exact step, schedule {schedule}")
+        o2, s2 = ExactStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk,
+                           gate_norm=w.gate_norm, schedule=schedule).run()
+        torch.cuda.synchronize()
+        for n, (b, h) in enumerate(pairs):
+            assert rel_err(o2[b, h], o_ref[n]) <= TOL["bf16"], (schedule, b, h)
+            assert rel_err(s2[b, h], s_ref[n]) <= TOL["bf16"], (schedule, b, h)
 
 
 def test_workload4_segmented_1M():
