@@ -337,7 +337,9 @@ def epsilon(w, inp, stream, steps: int = 20):
 
     kw = dict(mode=w.mode, chunk=w.chunk, gate_norm=w.gate_norm)
     args = (inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"])
-    out = {"decomposed": med(DeviceStep(*args, **kw)), "exact_passes": med(ExactStep(*args, schedule="passes", **kw))}
+    # (the output correction takes head dims up to 128: no decomposed step at d = 256)
+    out = {"decomposed": med(DeviceStep(*args, **kw)) if w.dk <= 128 else None,
+           "exact_passes": med(ExactStep(*args, schedule="passes", **kw))}
     chained = w.dtype == "bf16" and w.dk == w.dv == 128 and w.chunk == 64 and w.mode != "gate"
     out["exact_chained"] = med(ExactStep(*args, schedule="chained", **kw)) if chained else None
     out["two_pass_chunk_states"] = med(ExactStep(*args, schedule="passes", subseg_chunks=1, **kw))
@@ -345,10 +347,11 @@ def epsilon(w, inp, stream, steps: int = 20):
 
 
 def state_size_sweep(stream):
-    """The falsifier's question asked on one GPU: how the decomposition's cost (the device step
-    against one exact forward call, both on the same inputs) moves with the state size dk x dv at
-    a fixed token count (B1 H16 L16384, bf16, no decay, S_recv drawn N(0, 0.05)).  Median us.
-    For d = 32 and 64 also the device step with 128-token chunks (the chunk-length variant)."""
+    """The falsifier's question asked on one GPU: how the decomposition's cost (the decomposed
+    device step against one exact forward call, both on the same inputs) moves with the state size
+    dk x dv at a fixed token count (B1 H16 L16384, bf16, no decay, S_recv drawn N(0, 0.05)), d = 32
+    to 256.  Median us.  For d = 32, 64 and 128 also the exact step with 128-token chunks (the
+    chunk-length variant); d = 256 has no decomposed step and no backward."""
     import math
 
     import torch
@@ -357,7 +360,7 @@ def state_size_sweep(stream):
     from chunked_scan_amd.pipeline import DeviceStep, ExactStep
 
     out = {}
-    for d in (32, 64, 128):
+    for d in (32, 64, 128, 256):
         w = WORKLOADS[1].scaled(dk=d, dv=d, qkv_std=1.0 / math.sqrt(d), s_in_std=0.05, seed=10 + d)
         inp = make_inputs(w, "cuda")
         step = ExactStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk)
@@ -366,30 +369,35 @@ def state_size_sweep(stream):
         torch.cuda.synchronize()
         eps = epsilon(w, inp, stream, steps=30)
         ks, _ = kernel_stats(step, 30, stream)
-        bw = BackwardStep(w)
-        for _ in range(40):
-            bw.run()
-        torch.cuda.synchronize()
-        bwd = step_stats(bw, 20, stream)["median_us"]
-        del bw
+        bwd = None
+        if d <= 128:
+            bw = BackwardStep(w)
+            for _ in range(40):
+                bw.run()
+            torch.cuda.synchronize()
+            bwd = step_stats(bw, 20, stream)["median_us"]
+            del bw
         c128 = None
-        if d < 128:
+        if d <= 128:
             s128 = ExactStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=128)
             for _ in range(150):
                 s128.run()
             torch.cuda.synchronize()
             c128 = step_stats(s128, 30, stream)["median_us"]
             del s128
-        out[f"d{d}"] = dict(state_bytes=4 * d * d, decomposed_step_us=eps["decomposed"], chunk128_step_us=c128,
+        dec = eps["decomposed"]
+        out[f"d{d}"] = dict(state_bytes=4 * d * d, decomposed_step_us=dec, chunk128_step_us=c128,
                             exact_step_us=eps["exact_passes"], exact_chained_us=eps["exact_chained"],
-                            decomposition_overhead_us=round(eps["decomposed"] - eps["exact_passes"], 2),
-                            decomposition_overhead_frac=round(eps["decomposed"] / eps["exact_passes"] - 1, 4),
+                            decomposition_overhead_us=round(dec - eps["exact_passes"], 2) if dec else None,
+                            decomposition_overhead_frac=round(dec / eps["exact_passes"] - 1, 4) if dec else None,
                             backward_us=bwd,
                             kernels={n: round(v["mean_us"], 2) for n, v in ks.items()})
-        log(f"[bench] state size d={d}: decomposed step {eps['decomposed']:.1f} us"
-            + (f" (128-token chunks {c128:.1f} us)" if c128 else "") + ", one exact call "
-            f"{eps['exact_passes']:.1f} us" + (f" (chained {eps['exact_chained']:.1f} us)" if eps["exact_chained"] else "")
-            + f", backward {bwd:.1f} us; " + ", ".join(f"{n} {v['mean_us']:.1f}" for n, v in ks.items()))
+        log(f"[bench] state size d={d}: " + (f"decomposed step {dec:.1f} us, " if dec else "")
+            + f"one exact call {eps['exact_passes']:.1f} us"
+            + (f" (128-token chunks {c128:.1f} us)" if c128 else "")
+            + (f" (chained {eps['exact_chained']:.1f} us)" if eps["exact_chained"] else "")
+            + (f", backward {bwd:.1f} us" if bwd else "") + "; "
+            + ", ".join(f"{n} {v['mean_us']:.1f}" for n, v in ks.items()))
         del step, inp
         torch.cuda.empty_cache()
     return out

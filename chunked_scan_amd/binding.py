@@ -308,8 +308,8 @@ def la_chunk_fwd_decayed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, deca
     """la_chunk_fwd plus q_decayed [B,H,L,dk] (q times its cumulative decay from the segment start,
     q's dtype), total [B,H,nseg,dk] f32 (each segment's total decay; may be a view with evenly
     spaced dense (b,h) blocks) and tile_live [B,H,nseg,ceil(L/nseg/64)] int32 (0: the 64-token tile
-    of q_decayed is exactly zero).  Returns (o, s_out, q_decayed, total, tile_live); unrequested
-    ones are None."""
+    of q_decayed is exactly zero; with tile_live, a q_decayed passed in keeps its old contents on
+    such tiles).  Returns (o, s_out, q_decayed, total, tile_live); unrequested ones are None."""
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     _dev(q, "q")
@@ -330,7 +330,9 @@ def la_chunk_fwd_decayed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, deca
         _dev(s_out, "s_out", torch.float32, (B, H, nseg, dk, dv), contiguous=False)
         stride = _bh_stride(s_out, "s_out", dk * dv)
     if q_decayed is None and want_q_decayed:
-        q_decayed = torch.empty_like(q)
+        # with tile flags the library leaves the rows of tiles flagged zero unwritten (they would be
+        # zero); an array created here starts at zero so that it holds the full q * cum
+        q_decayed = torch.zeros_like(q) if (tile_live is not None or want_tile_live) else torch.empty_like(q)
     if q_decayed is not None:
         _dev(q_decayed, "q_decayed", q.dtype, (B, H, L, dk))
     if total is None and want_total:

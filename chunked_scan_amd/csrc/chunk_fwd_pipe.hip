@@ -31,11 +31,13 @@
 //   instruction).  Per chunk one barrier hands a landed stage to the compute waves and frees the
 //   stage they finished, and (in the output pass) a second one hands the output tile over.
 // * Gate mode.  The loader waves load q, k, v and g into registers two chunks ahead and, while
-//   the compute waves work on chunk c, prepare chunk c + 1 in its stage: the in-chunk cumulative
-//   log-decay (a per-lane prefix plus a DPP scan across lanes), qbar, kbar, v and the chunk's
-//   decay per key dim.  The compute waves then run the no-decay products and scale their state
-//   rows by the chunk decay; they store their outputs themselves (the prepared stages leave no
-//   room for an output tile).
+//   the compute waves work on chunk c, prepare chunk c + 1 in its stage (two stages: chunk c + 1
+//   goes where chunk c - 1 was): the in-chunk cumulative log-decay (a per-lane prefix plus a DPP
+//   scan across lanes), qbar, kbar, v and the chunk's decay per key dim.  The compute waves then
+//   run the no-decay products and scale their state rows by the chunk decay; their outputs go
+//   through two LDS output tiles, and at the top of chunk c they store chunk c - 1's tile as
+//   whole rows (stored 32 bytes per row piece directly, the outputs cost twice their bytes in
+//   writes; the loaders, at their register limit, cannot take the stores over).
 // * Ragged chunks.  DMA rows past a chunk's end re-read its last row, which only reaches output
 //   rows that are never stored; the state update zeroes those tokens' V operand in registers.
 // * Swizzle.  Tiles are unpadded (one DMA instruction writes 1 KiB contiguous), so the 16-byte
@@ -132,10 +134,15 @@ template <int MODE, bool STATE_ONLY>
 struct Layout {
     static constexpr bool GATE = MODE == DECAY_GATE;
     static constexpr bool OTILE = !STATE_ONLY && !GATE;  // outputs leave through an LDS tile stored by the loaders
+    // gate output pass: the same, with two output tiles (the loaders store chunk c - 1's while the
+    // compute waves fill chunk c's)
+    static constexpr bool GTILE = !STATE_ONLY && GATE;
     static constexpr int SLOT = STATE_ONLY ? 2 : 3;
     static constexpr int STAGE = SLOT * TE + (GATE ? 2 * D : 0);  // gate: D floats of chunk decay after the tiles
-    static constexpr int NST = GATE ? 3 : (LDS_TILES - (OTILE ? 1 : 0)) / SLOT;
+    // gate: the loaders prepare chunk c + 1 while chunk c is computed, in the stage chunk c - 1 left
+    static constexpr int NST = GATE ? 2 : (LDS_TILES - (OTILE ? 1 : 0)) / SLOT;
     static constexpr int RING = NST * STAGE;
+    static constexpr int OTILES = OTILE ? 1 : GTILE ? 2 : 0;
     __device__ static __forceinline__ Ring stage(__bf16* ring, int c) {
         __bf16* b = ring + (c % NST) * STAGE;
         // q is unused in the state pass
@@ -151,6 +158,22 @@ struct Walk {
         return (int)min((int64_t)C, t_end - t_begin - (int64_t)c * C);
     }
 };
+
+// Four waves (thread t of them) store an output tile (rows unpadded, 16-byte slot s of row r at
+// s ^ (r % 16)) of chunk rows r0 .. r0 + n - 1 row-major: 1 KiB contiguous per instruction.
+// ONE: one piece in registers at a time (for a caller at its register limit).
+template <bool ONE = false>
+__device__ __forceinline__ void store_otile(__bf16* o, const __bf16* otile, int64_t r0, int n, int t) {
+    __bf16* const base = o + r0 * D;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int pc = t + 256 * r;
+        const int row = pc >> 4, sl = pc & 15;
+        const u32x4 y = *(const u32x4*)(otile + row * D + ((sl ^ (row & 15)) << 3));
+        if (row < n) *(u32x4*)(base + (row * D + sl * 8)) = y;
+        if (ONE) __builtin_amdgcn_sched_barrier(0);
+    }
+}
 
 // Loader wave lw of the no-decay and head-decay modes: chunk c + NST - 1 is requested as soon as
 // every wave is done with chunk c - 1; in the output pass it also stores each chunk's output tile.
@@ -178,15 +201,7 @@ __device__ __forceinline__ void loader_walk(const __bf16* q, const __bf16* k, co
         }
         if (LY::OTILE) {
             lds_barrier_keep_dma();  // the compute waves have written chunk c's outputs
-            const int n = wk.chunk_len(c);
-            const int64_t r0 = wk.row_base + wk.t_begin + (int64_t)c * C;
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int pc = (threadIdx.x - 256) + 256 * r;
-                const int row = pc >> 4, sl = pc & 15;
-                const u32x4 y = *(const u32x4*)(otile + row * D + ((sl ^ (row & 15)) << 3));
-                if (row < n) *(u32x4*)(o + (r0 + row) * D + sl * 8) = y;
-            }
+            store_otile(o, otile, wk.row_base + wk.t_begin + (int64_t)c * C, wk.chunk_len(c), threadIdx.x - 256);
         }
     }
 }
@@ -351,15 +366,9 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
                         x0[e] = (__bf16)acc[e];
                         x1[e] = (__bf16)acc[8 + e];
                     }
-                    if (OTILE) {
-                        __bf16* orow = otile + itok * D;
-                        *(bf16x8*)(orow + (((4 * w + kg) ^ (itok & 15)) << 3)) = x0;
-                        *(bf16x8*)(orow + (((4 * w + 2 + kg) ^ (itok & 15)) << 3)) = x1;
-                    } else if (itok < n) {  // gate mode: no room for the tile beside the prepared stages
-                        __bf16* orow = o + (wk.row_base + wk.t_begin + (int64_t)c * C + itok) * D + 32 * w + 8 * kg;
-                        *(bf16x8*)orow = x0;
-                        *(bf16x8*)(orow + 16) = x1;
-                    }
+                    __bf16* orow = otile + (LY::GTILE ? (c & 1) * TE : 0) + itok * D;
+                    *(bf16x8*)(orow + (((4 * w + kg) ^ (itok & 15)) << 3)) = x0;
+                    *(bf16x8*)(orow + (((4 * w + 2 + kg) ^ (itok & 15)) << 3)) = x1;
                 }
             }
         }
@@ -427,8 +436,21 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
                     for (int e = 0; e < 4; e++) S[m][4 * g4 + e] *= f[e];
                 }
         }
+        // gate: chunk c - 1's output tile has been complete since the top of this chunk, and chunk
+        // c + 1 overwrites it only after the next barrier (the loaders are at their register
+        // limit, so the compute waves store it, here, where only the state is live)
+        if (LY::GTILE && c > 0) {
+            // the lane offsets are recomputed here rather than hoisted out of the loop (which spills)
+            int t = threadIdx.x;
+            asm volatile("" : "+v"(t));
+            store_otile<true>(o, otile + ((c - 1) & 1) * TE, wk.row_base + wk.t_begin + (int64_t)(c - 1) * C, C, t);
+        }
     }
-
+    if (LY::GTILE) {
+        lds_barrier();  // the last chunk's output tile is complete
+        const int c = wk.nch - 1;
+        store_otile(o, otile + (c & 1) * TE, wk.row_base + wk.t_begin + (int64_t)c * C, wk.chunk_len(c), threadIdx.x);
+    }
 }
 
 template <int MODE, bool STATE_ONLY>
@@ -443,7 +465,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     constexpr bool GATE = LY::GATE, OTILE = LY::OTILE;
     __shared__ __attribute__((aligned(16))) __bf16 ring[LY::RING];
     // the chunk's outputs, rows unpadded with 16-byte slot s of row r at s ^ (r % 16)
-    __shared__ __attribute__((aligned(16))) __bf16 otile[OTILE ? TE : 8];
+    __shared__ __attribute__((aligned(16))) __bf16 otile[LY::OTILES ? LY::OTILES * TE : 8];
     __shared__ int first_dead[4];  // gate loader wave lw: its first chunk with zero cumulative decay
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -592,6 +614,11 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 #pragma unroll
             for (int e = 0; e < 8; e++) fits = fits && bl[e] >= -GATE_SPAN_LOG2;
             wide = wide || __ballot(!fits) != 0;
+            // With tile flags, q times the cumulative decay is not written on a chunk that every
+            // loader wave had already found dead at the chunk before (its tile flag is zero and the
+            // values would be exactly zero); every wave flagged that chunk before the last barrier.
+            const bool skip_qd =
+                flags && cc > 0 && max(max(first_dead[0], first_dead[1]), max(first_dead[2], first_dead[3])) <= cc - 1;
             // decay from the segment start to this chunk's start (for q times the cumulative decay)
             float cf[8];
 #pragma unroll
@@ -618,7 +645,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
                 *(u32x4*)(st.k + off) = scale8(x.k[r], fk);
                 *(u32x4*)(st.v + off) = in ? x.v[r] : u32x4{0, 0, 0, 0};
                 if (!STATE_ONLY) *(u32x4*)(st.q + off) = scale8(x.q[r], fq);
-                if (!STATE_ONLY && q_dec && in) {
+                if (!STATE_ONLY && q_dec && in && !skip_qd) {
                     // q times its cumulative decay from the segment start, rounded once
                     float fd[8];
 #pragma unroll
@@ -640,6 +667,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
             step(c, rA, rB);
             if (c + 1 < nch) step(c + 1, rB, rA);
         }
+        if (!STATE_ONLY) lds_barrier();  // the compute waves' last output tile is complete
         if (STATE_ONLY && tg == 0) {
             float* pd = part_decay + (ub * (G - 1) + g) * D + 8 * o8;
 #pragma unroll

@@ -85,12 +85,14 @@ void mfma_split(const FwdArgs& a, int* G_out, int* cps_out, int64_t target) {
 }
 
 // The split of the matrix-core forward.  64-token chunks: 512 workgroups for small heads (their
-// kernels are latency-bound and several share a compute unit), 256 for d = 128.  128-token
+// kernels are latency-bound and several share a compute unit), 256 for d = 128 and for d = 256
+// (whose sub-segments take four workgroups each, one per value tile).  128-token
 // chunks (small heads): about 256 workgroups, at least two chunks per sub-segment; the
 // sub-segment length a caller gives counts chunks of the call's own length.
 void fwd_split_plan(const FwdArgs& a, int* G_out, int* cps_out) {
     if (a.chunk != 128) {
-        mfma_split(a, G_out, cps_out, a.dk < 128 ? 512 : 256);
+        // d = 256: four value tiles per sub-segment, so a quarter as many sub-segments
+        mfma_split(a, G_out, cps_out, a.dk < 128 ? 512 : a.dk == 256 ? 64 : 256);
         return;
     }
     constexpr int CH = 128;
@@ -154,6 +156,7 @@ hipError_t fwd_split_run(const FwdArgs& a, int G, int cps, float* ws) {
     float* part_state = G > 1 ? ws : nullptr;
     float* part_decay = G > 1 ? ws + n * a.dk * a.dk : nullptr;
     int* flags = gate_flag_words(a, G) ? (int*)(ws + n * a.dk * a.dk + n * a.dk) : nullptr;
+    if (a.dk == 256 || (a.chunk == 128 && a.dk == 128)) return launch_chunk_fwd_tiled(a, G, cps, part_state, part_decay);
     if (a.chunk == 128) return launch_chunk_fwd_small_ch128(a, G, cps, part_state, part_decay);
     return a.dk == 128 ? launch_chunk_fwd_pipe(a, G, cps, part_state, part_decay, flags)
                        : launch_chunk_fwd_small(a, G, cps, part_state, part_decay);

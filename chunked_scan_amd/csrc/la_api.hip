@@ -18,10 +18,15 @@ constexpr int64_t kMaxElems = (int64_t)1 << 60;  // keeps every byte count below
 
 bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
-// The forward also takes 128-token chunks on the small-head matrix-core kernels (bf16, dk = dv in
-// {32, 64}).
+// The forward's further variants, on matrix-core kernels only (bf16, dk = dv): 128-token chunks
+// for d = 32 and 64 (every decay mode) and d = 128 (no or head decay), and d = 256 with 64-token
+// chunks (no or head decay).
+bool fwd_wide(const la_shape* s) { return s->dk == 256 || s->dv == 256; }
 bool fwd_chunk_ok(const la_shape* s, int c) {
-    return chunk_ok(c) || (c == 128 && s->in_dtype == LA_BF16 && s->dk == s->dv && (s->dk == 32 || s->dk == 64));
+    const bool bf = s->in_dtype == LA_BF16 && s->dk == s->dv;
+    if (fwd_wide(s)) return bf && s->dk == 256 && c == 64 && s->decay_mode != LA_DECAY_GATE;
+    return chunk_ok(c) ||
+           (c == 128 && bf && (s->dk == 32 || s->dk == 64 || (s->dk == 128 && s->decay_mode != LA_DECAY_GATE)));
 }
 size_t esize(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
 
@@ -49,12 +54,14 @@ bool overlap(Span a, Span b) {
     return x < y + b.bytes && y < x + a.bytes;
 }
 
-la_status check_common(const la_shape* s) {
+// wide_ok: the forward, which also takes dk = dv = 256 (checked with the chunk length)
+la_status check_common(const la_shape* s, bool wide_ok = false) {
     if (!s) return LA_ERR_NULL;
     if (s->B < 0 || s->H < 0 || s->L < 0 || s->nseg < 1 || s->dk <= 0 || s->dv <= 0) return LA_ERR_SHAPE;
     if (s->L % s->nseg != 0) return LA_ERR_SHAPE;
     if (prod4(s->B, s->H, s->L, s->dk > s->dv ? s->dk : s->dv) < 0) return LA_ERR_SHAPE;
     if (prod4(s->B, s->H, s->nseg, (int64_t)s->dk * s->dv) < 0) return LA_ERR_SHAPE;
+    if (wide_ok && fwd_wide(s)) return LA_OK;
     if (!head_dim_ok(s->dk) || !head_dim_ok(s->dv)) return LA_ERR_UNSUPPORTED;
     return LA_OK;
 }
@@ -93,7 +100,7 @@ bool stride_ok(int64_t stride, int64_t min, const la_shape* s) {
 
 // Everything la_chunk_fwd checks that does not depend on the pointers.
 la_status check_fwd_shape(const la_shape* s, int chunk) {
-    la_status st = check_common(s);
+    la_status st = check_common(s, true);
     if (st != LA_OK) return st;
     if (chunk <= 0 || s->subseg_chunks < 0 || s->state_stride < 0) return LA_ERR_SHAPE;
     if (s->fwd_schedule < 0 || s->fwd_schedule > 2) return LA_ERR_SHAPE;
@@ -196,6 +203,7 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const floa
                          int32_t chunk, bool noalloc = false) {
     la_status st = validate_fwd(q, k, v, decay, s_in, o, s_out, s, chunk, q_dec, total, tile_live);
     if (st != LA_OK) return st;
+    if (fwd_wide(s) && (q_dec || total || tile_live)) return LA_ERR_UNSUPPORTED;  // la_chunk_fwd only
     if ((st = check_trace(s)) != LA_OK) return st;
     la::Tracer tr = make_tracer(s);
     hipStream_t stream = (hipStream_t)s->stream;
@@ -220,7 +228,7 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, const floa
     // matrix cores: bf16 with dk = dv in {32, 64, 128} and 64-token chunks, or 128-token chunks
     // (bf16, dk = dv in {32, 64}, validated)
     const bool mfma = s->L > 0 && ((a.bf16 && a.dk == a.dv && (a.dk == 32 || a.dk == 64 || a.dk == 128) && chunk == 64) ||
-                                   chunk == 128);
+                                   chunk == 128 || a.dk == 256);
     if (noalloc && mfma && la::fwd_noalloc_bytes(a) > LA_NOALLOC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;
     hipError_t e = hipSuccess;
     bool fused = false;  // the forward itself wrote q_dec and total

@@ -146,6 +146,10 @@ size_t fwd_split_workspace_floats(const FwdArgs& a, int G);
 // Its kernels: G sub-segments of cps chunks; part_state / part_decay the workspace of the
 // sub-segment scan (unused when G == 1); gate mode: wide the 4 * B*H*nseg * (2G - 1) ints of the
 // per-unit flags that send a unit to the windowed redo (unused otherwise).
+// The dv-tiled matrix-core forward (no decay or head decay): dk = dv = 256 with 64-token chunks
+// (four 64-column value tiles), and dk = dv = 128 with 128-token chunks.  Same split and workspace
+// as the other matrix-core kernels.
+hipError_t launch_chunk_fwd_tiled(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
 // The chained d = 128 forward (no decay or head decay, G > 1 sub-segments): one launch (after a
 // small flag reset) whose workgroups hand their sub-segment states on through the workspace
 // (chain_workspace_floats floats).

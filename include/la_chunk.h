@@ -86,8 +86,8 @@ typedef struct la_shape {
     int64_t B;            /* batch size, >= 0 */
     int64_t H;            /* heads, >= 0 */
     int64_t L;            /* tokens per (b,h) sequence, >= 0; L % nseg == 0 */
-    int32_t dk;           /* key/query head dim: 16, 32, 64 or 128 */
-    int32_t dv;           /* value head dim: 16, 32, 64 or 128 */
+    int32_t dk;           /* key/query head dim: 16, 32, 64 or 128 (la_chunk_fwd also 256) */
+    int32_t dv;           /* value head dim: 16, 32, 64 or 128 (la_chunk_fwd also 256) */
     int32_t nseg;         /* independent segments per sequence, >= 1, each L/nseg tokens */
     int32_t in_dtype;     /* la_dtype of q, k, v */
     int32_t out_dtype;    /* la_dtype of o (must equal in_dtype in this build) */
@@ -140,7 +140,11 @@ typedef struct la_shape {
  *            at s_out + (b*H + h) * state_stride + p * dk * dv (dense [B,H,nseg,dk,dv] when
  *            state_stride = 0); must not overlap any other argument.
  *   chunk  : chunk length in tokens: 16, 32 or 64 (64 is the production size), or 128 for bf16
- *            with dk = dv in {32, 64} (the chunk-length variant, on the matrix-core kernels).
+ *            with dk = dv in {32, 64}, and with dk = dv = 128 without gate decay (the chunk-length
+ *            variants, on the matrix-core kernels).
+ * Head dims: dk, dv in {16, 32, 64, 128}, and dk = dv = 256 for bf16 with 64-token chunks and no
+ * or per-head decay (the state-size variant: the value dims are tiled across workgroups; only
+ * la_chunk_fwd, la_chunk_fwd_noalloc and la_state_scan take it).
  * A partial last chunk (L/nseg not a multiple of chunk) is allowed.  Gate mode takes any gate
  * value, g = -inf (a = 0) included: each token's log-decay is floored at -33 (a >= e^-33, which
  * moves every token-pair weight by at most e^-33), and a chunk whose decay is too wide for the
@@ -189,7 +193,10 @@ la_status la_chunk_fwd_noalloc(const void* q, const void* k, const void* v, cons
  *   tile_live          = uint32[B,H,nseg,ceil(L/nseg/64)] or NULL: entry i of segment p covers the
  *                        segment's tokens 64i .. 64i+63.  Zero promises that q_t (*) cum_t is exactly
  *                        zero on every one of them (the cumulative decay has underflowed for every
- *                        key dim); nonzero promises nothing.  For la_state_correct_live.
+ *                        key dim); nonzero promises nothing.  For la_state_correct_live.  When
+ *                        tile_live is given, q_decayed may be left unwritten on the tiles whose
+ *                        entry is zero (the values there would be zero, and la_state_correct_live
+ *                        does not read them); without tile_live every q_decayed row is written.
  * Every other argument, and every result la_chunk_fwd writes, is as for la_chunk_fwd.  In gate
  * mode with bf16, dk = dv = 128 and chunk 64 all three come out of the forward's own decay
  * preparation (cum = exp2 of an fp32 running sum of log2 a); otherwise one extra streaming pass

@@ -76,11 +76,16 @@ def test_fwd_validation(lib):
     assert fwd(lib, shape(L=100, nseg=3)) == SHAPE          # L % nseg != 0
     assert fwd(lib, shape(dk=0)) == SHAPE
     assert fwd(lib, shape(dk=96)) == UNSUP
-    assert fwd(lib, shape(dv=256)) == UNSUP
+    assert fwd(lib, shape(dv=256)) == UNSUP                    # 256 only with dk = dv
+    assert fwd(lib, shape(dk=256, dv=256), chunk=32) == UNSUP  # d = 256: 64-token chunks
+    assert fwd(lib, shape(dk=256, dv=256, dtype=B.LA_F32)) == UNSUP
+    assert fwd(lib, shape(dk=256, dv=256, mode=2), dec=DEC) == UNSUP  # no gate at d = 256
+    assert lib.la_supported(ctypes.byref(shape(dk=256, dv=256, mode=1)), 64) == 1
     assert fwd(lib, shape(), chunk=0) == SHAPE
     assert fwd(lib, shape(), chunk=48) == UNSUP
-    # 128-token chunks: bf16 with dk = dv in {32, 64} only
-    assert fwd(lib, shape(dk=128, dv=128), chunk=128) == UNSUP
+    # 128-token chunks: bf16 with dk = dv in {32, 64}, and 128 without gate decay
+    assert fwd(lib, shape(dk=128, dv=128, mode=2), dec=DEC, chunk=128) == UNSUP
+    assert lib.la_supported(ctypes.byref(shape(dk=128, dv=128)), 128) == 1
     assert fwd(lib, shape(dtype=B.LA_F32), chunk=128) == UNSUP
     assert fwd(lib, shape(dk=64, dv=32), chunk=128) == UNSUP
     assert fwd(lib, shape(dk=16, dv=16), chunk=128) == UNSUP
@@ -117,7 +122,8 @@ def test_supported(lib):
     assert lib.la_supported(ctypes.byref(shape(dk=256)), 64) == 0
     assert lib.la_supported(ctypes.byref(shape()), 128) == 1
     assert lib.la_supported(ctypes.byref(shape(dk=32, dv=32)), 128) == 1
-    assert lib.la_supported(ctypes.byref(shape(dk=128, dv=128)), 128) == 0
+    assert lib.la_supported(ctypes.byref(shape(dk=128, dv=128)), 128) == 1
+    assert lib.la_supported(ctypes.byref(shape(dk=128, dv=128, mode=2)), 128) == 0
     assert lib.la_supported(ctypes.byref(shape(dtype=B.LA_F32)), 128) == 0
     assert lib.la_supported(ctypes.byref(shape()), 256) == 0
     assert lib.la_supported(None, 64) == 0

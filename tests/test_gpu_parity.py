@@ -324,8 +324,22 @@ def test_chunk_fwd_decayed(mode, path, L, nseg, subseg):
     assert none_tot is None and none_qd is None
     assert torch.equal(o, o0) and torch.equal(s, s0)
     assert torch.equal(qd_only, qd) and torch.equal(tot_only, tot) and torch.equal(live_only, live)
-    # a tile flagged zero holds exactly zero rows of q_decayed
+    # with tile flags, the rows of a tile flagged zero are left as they were (a sentinel here), the
+    # others are written exactly as without flags
+    sentinel = torch.full_like(d["q"], float("nan"))
+    _, _, qd_s, _, live_s = lb.la_chunk_fwd_decayed(d["q"], d["k"], d["v"], d["decay"], d["s_in"], q_decayed=sentinel,
+                                                    want_tile_live=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(live_s, live)
     Ls = L // nseg
+    pad = live.shape[-1] * 64 - Ls
+    tiles = lambda x: torch.nn.functional.pad(x.reshape(w.B, w.H, nseg, Ls, dk).float(), (0, 0, 0, pad)).reshape(  # noqa: E731
+        w.B, w.H, nseg, -1, 64 * dk)
+    ts, tq = tiles(qd_s), tiles(qd_only)
+    livem = (live != 0)[..., None].expand_as(ts)
+    assert torch.equal(ts[livem], tq[livem])
+    assert torch.all(torch.isnan(ts[~livem]) | (ts[~livem] == 0))
+    # a tile flagged zero holds exactly zero rows of q_decayed
     qz = torch.nn.functional.pad(qd.reshape(w.B, w.H, nseg, Ls, dk), (0, 0, 0, live.shape[-1] * 64 - Ls))
     nonzero = qz.reshape(w.B, w.H, nseg, -1, 64 * dk).ne(0).any(-1)
     assert not torch.any(nonzero & (live == 0))
