@@ -413,17 +413,27 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                     pq = mfma(*(const bf16x8*)(&(MODE == DECAY_GATE ? sm.qs : sm.q)[(ib * 32 + n32) * PITCH + ka]),
                               *(const bf16x8*)(&sm.k[(jb * 32 + n32) * PITCH + ka]), pq);
                 }
+                // a lane holds column j = jb 32 + n32 and rows i in four runs of four: one 8-byte
+                // store per run into the transposed tiles
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);  // i index
-                    const int col = jb * 32 + n32;                               // j index
-                    float wgt = (col > row) ? 0.f : 1.f;
-                    if (MODE == DECAY_HEAD) {
-                        wgt *= sm.apow[max(row - col, 0)];
-                        if (intra_part && col < row) hacc += (double)((float)(row - col) * wgt) * ((double)po[i] * (double)pq[i]);
+                for (int g4 = 0; g4 < 4; g4++) {
+                    bf16x4 xo, xq;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int i = 4 * g4 + e;
+                        const int row = ib * 32 + g4 * 8 + kg * 4 + e;  // i index
+                        const int col = jb * 32 + n32;                   // j index
+                        float wgt = (col > row) ? 0.f : 1.f;
+                        if (MODE == DECAY_HEAD) {
+                            wgt *= sm.apow[max(row - col, 0)];
+                            if (intra_part && col < row) hacc += (double)((float)(row - col) * wgt) * ((double)po[i] * (double)pq[i]);
+                        }
+                        xo[e] = (__bf16)(po[i] * wgt);
+                        xq[e] = (__bf16)(pq[i] * wgt);
                     }
-                    sm.pt[col * PPITCH + row] = (__bf16)(po[i] * wgt);
-                    sm.pv[col * PPITCH + row] = (__bf16)(pq[i] * wgt);
+                    const int off = (jb * 32 + n32) * PPITCH + ib * 32 + g4 * 8 + kg * 4;
+                    *(bf16x4*)(&sm.pt[off]) = xo;
+                    *(bf16x4*)(&sm.pv[off]) = xq;
                 }
             }
             __syncthreads();  // score tiles complete
@@ -448,74 +458,72 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                     }
                     db[2 * m + hh] = x;
                 }
+            // dk and dv are formed transposed (feature dims x tokens), with the operands of each
+            // product swapped: a lane then holds token j = jb 32 + n32 and 16 feature dims in four
+            // runs of four, stored 8 bytes at a time
 #pragma unroll
             for (int jb = 0; jb < 2; jb++) {
                 if (!Gm::owns_rows(jb, rank)) continue;
-                // dk: a^{n-1-j} (V D^T) + (P' w)^T Q
+                const int jt = jb * 32 + n32;  // this lane's token
+                const float wj = (MODE == DECAY_HEAD) ? sm.apow[max(n - 1 - jt, 0)] : 1.f;
+                // dk^T: a^{n-1-j} (D V^T) + Q^T (P' w)
                 f32x16 acc = {};
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ks * 16 + kg * 8]);
-                    const bf16x8 b = *(const bf16x8*)(&sm.dm[(32 * cb + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 a = *(const bf16x8*)(&sm.dm[(32 * cb + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 b = *(const bf16x8*)(&sm.v[jt * PITCH + ks * 16 + kg * 8]);
                     acc = mfma(a, b, acc);
                 }
                 if (MODE == DECAY_HEAD) {
 #pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int j = jb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= sm.apow[max(n - 1 - j, 0)];
-                    }
+                    for (int i = 0; i < 16; i++) acc[i] *= wj;
                 }
                 if (MODE == DECAY_GATE) {
 #pragma unroll
-                    for (int i = 0; i < 16; i++) acc[i] *= sm.gel[32 * cb + n32];
+                    for (int i = 0; i < 16; i++) acc[i] *= sm.gel[32 * cb + (i >> 2) * 8 + kg * 4 + (i & 3)];
                 }
 #pragma unroll
                 for (int ks = 2 * jb; ks < 4; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.pt[(jb * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
-                    acc = mfma(a, qb[ks], acc);
+                    const bf16x8 b = *(const bf16x8*)(&sm.pt[jt * PPITCH + ks * 16 + kg * 8]);
+                    acc = mfma(qb[ks], b, acc);
                 }
-                if (MODE == DECAY_GATE) {  // dk_j = 2^{-B_j} (2^{B_last} V D^T + P'^T Q-bar)_j, per key dim
+                if (MODE == DECAY_GATE) {  // dk_j = 2^{-B_j} (2^{B_last} D V^T + Q-bar^T P')_j, per key dim
 #pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int j = jb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= sm.gb[j * D + 32 * cb + n32];
-                    }
+                    for (int i = 0; i < 16; i++) acc[i] *= sm.gb[jt * D + 32 * cb + (i >> 2) * 8 + kg * 4 + (i & 3)];
                 }
-                __bf16* drow = dk_out + (row_base + t0 + jb * 32) * D + 32 * cb + n32;
+                if (jt < n) {
+                    __bf16* drow = dk_out + (row_base + t0 + jt) * D + 32 * cb + kg * 4;
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int j = (i >> 2) * 8 + kg * 4 + (i & 3);
-                    if (jb * 32 + j < n) drow[j * D] = (__bf16)acc[i];
+                    for (int g4 = 0; g4 < 4; g4++)
+                        *(bf16x4*)(drow + g4 * 8) = bf16x4{(__bf16)acc[4 * g4], (__bf16)acc[4 * g4 + 1],
+                                                           (__bf16)acc[4 * g4 + 2], (__bf16)acc[4 * g4 + 3]};
                 }
-                // dv: a^{n-1-j} (K D) + (P w)^T d_o
+                // dv^T: a^{n-1-j} (D^T K^T) + d_o^T (P w)
                 acc = f32x16{};
-                const __bf16* krow = &sm.k[(jb * 32 + n32) * PITCH + kg * 4];
+                const __bf16* krow = &sm.k[jt * PITCH + kg * 4];
 #pragma unroll
                 for (int m = 0; m < NCB; m++)
 #pragma unroll
                     for (int hh = 0; hh < 2; hh++) {
                         const int d0 = 32 * m + 16 * hh;
-                        acc = mfma(cat(*(const bf16x4*)(krow + d0), *(const bf16x4*)(krow + d0 + 8)), db[2 * m + hh],
+                        acc = mfma(db[2 * m + hh], cat(*(const bf16x4*)(krow + d0), *(const bf16x4*)(krow + d0 + 8)),
                                    acc);
                     }
                 if (MODE == DECAY_HEAD) {
 #pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int j = jb * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= sm.apow[max(n - 1 - j, 0)];
-                    }
+                    for (int i = 0; i < 16; i++) acc[i] *= wj;
                 }
 #pragma unroll
                 for (int ks = 2 * jb; ks < 4; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.pv[(jb * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
-                    acc = mfma(a, ob[ks], acc);
+                    const bf16x8 b = *(const bf16x8*)(&sm.pv[jt * PPITCH + ks * 16 + kg * 8]);
+                    acc = mfma(ob[ks], b, acc);
                 }
-                __bf16* vrow = dv_out + (row_base + t0 + jb * 32) * D + 32 * cb + n32;
+                if (jt < n) {
+                    __bf16* vrow = dv_out + (row_base + t0 + jt) * D + 32 * cb + kg * 4;
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int j = (i >> 2) * 8 + kg * 4 + (i & 3);
-                    if (jb * 32 + j < n) vrow[j * D] = (__bf16)acc[i];
+                    for (int g4 = 0; g4 < 4; g4++)
+                        *(bf16x4*)(vrow + g4 * 8) = bf16x4{(__bf16)acc[4 * g4], (__bf16)acc[4 * g4 + 1],
+                                                           (__bf16)acc[4 * g4 + 2], (__bf16)acc[4 * g4 + 3]};
                 }
             }
         }
@@ -805,21 +813,28 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
             // ---- P' blocks (0,0), (1,0), (1,1) on waves 0, 2, 3: weight a^{i-j}, mask j <= i
             if (w != 1) {
                 const int ib = w >> 1, jb = (w == 3) ? 1 : 0;
+                // the block transposed (V d_o^T), so that a lane holds row i = ib 32 + n32 and columns
+                // j in four runs of four: one 8-byte store per run
                 f32x16 acc = {};
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ks * 16 + kg * 8]);
-                    const bf16x8 b = *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 a = *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 b = *(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ks * 16 + kg * 8]);
                     acc = mfma(a, b, acc);
                 }
+                const int row = ib * 32 + n32;
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                    const int col = jb * 32 + n32;
-                    float val = acc[i];
-                    if (MODE == DECAY_HEAD) val *= sm.apow[max(row - col, 0)];
-                    if (col > row) val = 0.f;
-                    sm.p[row * PPITCH + col] = (__bf16)val;
+                for (int g4 = 0; g4 < 4; g4++) {
+                    bf16x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int col = jb * 32 + g4 * 8 + kg * 4 + e;
+                        float val = acc[4 * g4 + e];
+                        if (MODE == DECAY_HEAD) val *= sm.apow[max(row - col, 0)];
+                        if (col > row) val = 0.f;
+                        x[e] = (__bf16)val;
+                    }
+                    *(bf16x4*)(&sm.p[row * PPITCH + jb * 32 + g4 * 8 + kg * 4]) = x;
                 }
             }
             __syncthreads();  // P' complete
@@ -828,40 +843,40 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
             bf16x8 kb[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) kb[ks] = tr_operand(sm.k, PITCH, ks, 32 * cb, lane);
+            // dq is formed transposed (key dims x tokens), the operands of each product swapped: a
+            // lane holds token i = ib 32 + n32 and 16 key dims in four runs of four (8-byte stores)
 #pragma unroll
             for (int ib = 0; ib < 2; ib++) {
                 if (!Gm::owns_rows(ib, rank)) continue;
+                const int it = ib * 32 + n32;  // this lane's token
                 f32x16 acc = {};
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ks * 16 + kg * 8]);
-                    const bf16x8 b = *(const bf16x8*)(&sm.sm[(32 * cb + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 a = *(const bf16x8*)(&sm.sm[(32 * cb + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 b = *(const bf16x8*)(&sm.o[it * PITCH + ks * 16 + kg * 8]);
                     acc = mfma(a, b, acc);
                 }
                 if (MODE == DECAY_HEAD) {
+                    const float f = sm.apow[it + 1];
 #pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= sm.apow[row + 1];
-                    }
+                    for (int i = 0; i < 16; i++) acc[i] *= f;
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2 * (ib + 1); ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.p[(ib * 32 + n32) * PPITCH + ks * 16 + kg * 8]);
-                    acc = mfma(a, kb[ks], acc);
+                    const bf16x8 b = *(const bf16x8*)(&sm.p[it * PPITCH + ks * 16 + kg * 8]);
+                    acc = mfma(kb[ks], b, acc);
                 }
-                if (MODE == DECAY_GATE) {  // dq_i = 2^{B_i} (d_o S^T + P' Khat)_i, per key dim
+                if (MODE == DECAY_GATE) {  // dq_i = 2^{B_i} (S d_o^T + Khat^T P'^T)_i, per key dim
 #pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int row = ib * 32 + (i >> 2) * 8 + kg * 4 + (i & 3);
-                        acc[i] *= __builtin_amdgcn_exp2f(sm.gb[row * D + 32 * cb + n32]);
-                    }
+                    for (int i = 0; i < 16; i++)
+                        acc[i] *= __builtin_amdgcn_exp2f(sm.gb[it * D + 32 * cb + (i >> 2) * 8 + kg * 4 + (i & 3)]);
                 }
-                const int64_t rbase = row_base + t0 + ib * 32;
+                if (it < n) {
+                    __bf16* qrow = dq + (row_base + t0 + it) * D + 32 * cb + kg * 4;
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int row = (i >> 2) * 8 + kg * 4 + (i & 3);
-                    if (ib * 32 + row < n) dq[(rbase + row) * D + 32 * cb + n32] = (__bf16)acc[i];
+                    for (int g4 = 0; g4 < 4; g4++)
+                        *(bf16x4*)(qrow + g4 * 8) = bf16x4{(__bf16)acc[4 * g4], (__bf16)acc[4 * g4 + 1],
+                                                           (__bf16)acc[4 * g4 + 2], (__bf16)acc[4 * g4 + 3]};
                 }
             }
         }
