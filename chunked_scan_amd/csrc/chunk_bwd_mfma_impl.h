@@ -171,7 +171,7 @@ struct BwdSmem {
     __bf16 k[SO ? 8 : TILE];
     __bf16 v[SO ? 8 : TILE];
     __bf16 o[TILE];                  // d_o
-    __bf16 dm[SO ? 8 : D * PITCH];   // D as bf16, [key row][value column]
+    __bf16 dm[SO ? 8 : D * PITCH];   // D^T as bf16, [value column][key row]
     __bf16 pt[SO ? 8 : C * PPITCH];  // (P' w)^T: [j][i]
     __bf16 pv[SO ? 8 : C * PPITCH];  // (P w)^T:  [j][i]
     float gb[GATE ? C * D : 4];      // gate: in-chunk cumulative log2-decay B, then 2^{-B}
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
     const float* __restrict__ init_state,                            // output pass: scanned D^(g)
     double* __restrict__ intra_part,  // head mode, output pass: the intra-chunk part of d lambda_h, or null
-    __bf16* __restrict__ d_start,     // output pass, gate derivative: D at every chunk's start (bf16 [D][D]), or null
+    __bf16* __restrict__ d_start,     // output pass, gate derivative: D^T at every chunk's start (bf16 [D][D]), or null
     int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
     __shared__ __attribute__((aligned(16))) BwdSmem<D, MODE, STATE_ONLY> sm;
     if constexpr (MODE == DECAY_GATE) {
@@ -363,18 +363,18 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 xv = rv[r];
             }
         });
-        if (!STATE_ONLY && rank == 0) {
+        if (!STATE_ONLY && rank == 0) {  // D^T as bf16: this lane's value column, key rows in runs of four
 #pragma unroll
             for (int m = 0; m < NCB; m++)
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                    sm.dm[r * PITCH + 32 * cb + n32] = (__bf16)Dm[m][i];
-                }
+                for (int g4 = 0; g4 < 4; g4++)
+                    *(bf16x4*)(&sm.dm[(32 * cb + n32) * PITCH + 32 * m + g4 * 8 + kg * 4]) =
+                        bf16x4{(__bf16)Dm[m][4 * g4], (__bf16)Dm[m][4 * g4 + 1], (__bf16)Dm[m][4 * g4 + 2],
+                               (__bf16)Dm[m][4 * g4 + 3]};
         }
         __syncthreads();
         if (PF && c > 0 && wi == nwin - 1) load_chunk(c - 1);  // the previous chunk, while this one is computed
-        if (!STATE_ONLY && d_start && c + 1 < nchunks && wi == 0) {  // D here = D at the start of chunk c + 1
+        if (!STATE_ONLY && d_start && c + 1 < nchunks && wi == 0) {  // D^T here = D^T at the start of chunk c + 1
             __bf16* dst = d_start + (ub * nch_seg + (int64_t)g * cps + c + 1) * D * D;
 #pragma unroll
             for (int r = 0; r < (D * D / 8 + NT - 1) / NT; r++) {
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 f32x16 acc = {};
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.dm[(32 * cb + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 a = tr_operand(sm.dm, PITCH, ks, 32 * cb, lane);  // D rows, from D^T
                     const bf16x8 b = *(const bf16x8*)(&sm.v[jt * PITCH + ks * 16 + kg * 8]);
                     acc = mfma(a, b, acc);
                 }
@@ -561,15 +561,15 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 dst[r * D + 32 * cb + n32] = Dm[m][i];
             }
     }
-    if (!STATE_ONLY && d_start && nchunks > 0 && rank == 0) {  // ... which is D at its first chunk's start
+    if (!STATE_ONLY && d_start && nchunks > 0 && rank == 0) {  // ... which is D at its first chunk's start (D^T)
         __bf16* dsd = d_start + (ub * nch_seg + (int64_t)g * cps) * D * D;
 #pragma unroll
         for (int m = 0; m < NCB; m++)
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                dsd[r * D + 32 * cb + n32] = (__bf16)Dm[m][i];
-            }
+            for (int g4 = 0; g4 < 4; g4++)
+                *(bf16x4*)(dsd + (32 * cb + n32) * D + 32 * m + g4 * 8 + kg * 4) =
+                    bf16x4{(__bf16)Dm[m][4 * g4], (__bf16)Dm[m][4 * g4 + 1], (__bf16)Dm[m][4 * g4 + 2],
+                           (__bf16)Dm[m][4 * g4 + 3]};
     }
     if (STATE_ONLY && tid < D) {  // the total decay over this sub-segment, per key dim
         float tot = 1.f;
@@ -598,7 +598,7 @@ struct DqSmem {
     __bf16 v[TILE];
     __bf16 k[SO ? 8 : TILE];  // k (the P' K product); gate: k 2^{-B}
     __bf16 kt[TILE];          // k_j a^{n-1-j} (the state update); gate: k 2^{B_last - B}
-    __bf16 sm[SO ? 8 : D * PITCH];  // S as bf16, [key row][value column]
+    __bf16 sm[SO ? 8 : D * PITCH];  // S^T as bf16, [value column][key row]
     __bf16 p[SO ? 8 : C * PPITCH];  // P' w, [i][j]
     float gb[GATE ? C * D : 4];     // gate: in-chunk cumulative log2-decay
     float gtot[GATE ? NT : 4];
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     // output pass: the state entering sub-segment g >= 1 of (bh, seg) at
     // init_state + bh * ist_bh + (seg * ist_g + g + ist_off) * D * D (the scan buffer, or states the caller gives)
     const float* __restrict__ init_state, int64_t ist_bh, int ist_g, int ist_off,
-    const __bf16* __restrict__ d_start,  // gate derivative: D at every chunk's start (bf16 [D][D]), or null
+    const __bf16* __restrict__ d_start,  // gate derivative: D^T at every chunk's start (bf16 [D][D]), or null
     float* __restrict__ c0_out,          // gate derivative: rowsum(S (.) D) at every chunk's start ([D])
     int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
     __shared__ __attribute__((aligned(16))) DqSmem<D, MODE, STATE_ONLY> sm;
@@ -699,15 +699,16 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
         const int nc = (int)min((int64_t)C, t_end - t0c);
         __syncthreads();  // the previous chunk is done with every LDS tile
         if (!PF) load_chunk(c);
-        // gate derivative: this thread's part of D at the chunk's start (key row tid / TPR), loaded
-        // here so that it arrives while the chunk is staged
-        constexpr int TPR = NT / D, CPT = D / TPR;  // threads per key row, columns per thread
-        bf16x4 dst4[STATE_ONLY ? 1 : CPT / 4];
+        // gate derivative: this thread's part of D^T at the chunk's start (key dims 4 (tid % (D / 4))
+        // .. + 3, value rows of part tid / (D / 4)), loaded here so that it arrives while the chunk
+        // is staged
+        constexpr int NPART = NT / (D / 4), RPP = D / NPART;  // parts of the value rows, rows per part
+        bf16x4 dst4[STATE_ONLY ? 1 : RPP];
         const int64_t ci = ub * nch_seg + (int64_t)g * cps + c;
         if (!STATE_ONLY && c0_out) {
-            const __bf16* src = d_start + (ci * D + tid / TPR) * D + (tid % TPR) * CPT;
+            const __bf16* src = d_start + (ci * D + (tid / (D / 4)) * RPP) * D + (tid % (D / 4)) * 4;
 #pragma unroll
-            for (int j = 0; j < CPT / 4; j++) dst4[j] = *(const bf16x4*)(src + 4 * j);
+            for (int j = 0; j < RPP; j++) dst4[j] = *(const bf16x4*)(src + j * D);
         }
         // gate mode: the chunk's running log2-decay, and the windows it is taken in (one, unless its
         // decay is too wide for the factorised pair weights; chunk_gate_windows)
@@ -780,29 +781,37 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
             xv = rv[r];
             if (!STATE_ONLY) xo = ro[r];
         });
-        if (!STATE_ONLY && rank == 0) {
+        if (!STATE_ONLY && rank == 0) {  // S^T as bf16: this lane's value column, key rows in runs of four
 #pragma unroll
             for (int m = 0; m < NCB; m++)
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int r = 32 * m + (i >> 2) * 8 + kg * 4 + (i & 3);
-                    sm.sm[r * PITCH + 32 * cb + n32] = (__bf16)Sm[m][i];
-                }
+                for (int g4 = 0; g4 < 4; g4++)
+                    *(bf16x4*)(&sm.sm[(32 * cb + n32) * PITCH + 32 * m + g4 * 8 + kg * 4]) =
+                        bf16x4{(__bf16)Sm[m][4 * g4], (__bf16)Sm[m][4 * g4 + 1], (__bf16)Sm[m][4 * g4 + 2],
+                               (__bf16)Sm[m][4 * g4 + 3]};
         }
         __syncthreads();
         if (PF && c + 1 < nchunks && wi == nwin - 1) load_chunk(c + 1);  // the next chunk, while this one is computed
         if (!STATE_ONLY && c0_out && wi == 0) {  // rowsum(S (.) D) at this chunk's start, per key dim, from S's bf16 copy
-            const int r = tid / TPR, col0 = (tid % TPR) * CPT;
-            float acc = 0.f;
+            // partial sums over this thread's value rows for its four key dims, then summed over the
+            // parts through the score tile's LDS (free until the scores below are written)
+            const int r4 = (tid % (D / 4)) * 4, part = tid / (D / 4);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < CPT / 4; j++) {
-                const bf16x4 ss = *(const bf16x4*)(&sm.sm[r * PITCH + col0 + 4 * j]);
+            for (int j = 0; j < RPP; j++) {
+                const bf16x4 ss = *(const bf16x4*)(&sm.sm[(part * RPP + j) * PITCH + r4]);
 #pragma unroll
-                for (int e = 0; e < 4; e++) acc += (float)ss[e] * (float)dst4[j][e];
+                for (int e = 0; e < 4; e++) acc[e] += (float)ss[e] * (float)dst4[j][e];
             }
-#pragma unroll
-            for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off);
-            if (tid % TPR == 0) c0_out[ci * D + r] = acc;
+            float* red = (float*)sm.p;  // [NPART][D]
+            *(f32x4*)(&red[part * D + r4]) = acc;
+            __syncthreads();
+            if (tid < D) {
+                float t = 0.f;
+                for (int pp = 0; pp < NPART; pp++) t += red[pp * D + tid];
+                c0_out[ci * D + tid] = t;
+            }
+            __syncthreads();  // the score tile is free again
         }
 
         bf16x8 vb[4];  // v operands of this wave's value columns, four 16-token slabs
@@ -852,7 +861,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
                 f32x16 acc = {};
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ks++) {
-                    const bf16x8 a = *(const bf16x8*)(&sm.sm[(32 * cb + n32) * PITCH + ks * 16 + kg * 8]);
+                    const bf16x8 a = tr_operand(sm.sm, PITCH, ks, 32 * cb, lane);  // S rows, from S^T
                     const bf16x8 b = *(const bf16x8*)(&sm.o[it * PITCH + ks * 16 + kg * 8]);
                     acc = mfma(a, b, acc);
                 }
