@@ -28,7 +28,6 @@ Every workload is warmed up with at least ~20 ms of steps first: the GPU's clock
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -41,20 +40,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_output_pass_plain_B1_H16_L16k_d128.json")
-KERNEL_SRCS = [os.path.join(ROOT, "chunked_scan_amd", "csrc", f) for f in ("chunk_fwd_split.hip", "chunk_fwd_pipe.hip")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def source_hash() -> str:
-    """Hash of the forward-kernel sources: counter data taken on other sources is stale."""
-    h = hashlib.sha256()
-    for p in KERNEL_SRCS:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def algorithmic(w, mode_bytes_gate: int):
@@ -320,6 +309,8 @@ def epsilon(w, inp, stream, steps: int = 20):
     exact result (O and S_out from S_recv) four ways, each step timed with events (median us).
       decomposed        the pages' device step: local forward of every sub-segment from zero, the
                         All-Scan over [S_recv, S_loc,1..G], output correction by each S_in
+      recv_first        the decomposed step with S_recv as the first sub-segment's initial state
+                        (no correction of that sub-segment)
       exact_passes      one la_chunk_fwd from S_recv (state pass, scan, output pass from the exact
                         incoming states; no correction)
       exact_chained     the same in one launch with the chained state hand-off (where it exists)
@@ -327,7 +318,8 @@ def epsilon(w, inp, stream, steps: int = 20):
                         and reloaded (the pages' two-pass schedule, one sub-segment per chunk)"""
     import torch
 
-    from chunked_scan_amd.pipeline import DeviceStep, ExactStep
+    from chunked_scan_amd import binding
+    from chunked_scan_amd.pipeline import DeviceStep, ExactStep, RecvFirstStep
 
     def med(st):
         for _ in range(3):
@@ -339,9 +331,12 @@ def epsilon(w, inp, stream, steps: int = 20):
     args = (inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"])
     # (the output correction takes head dims up to 128: no decomposed step at d = 256)
     out = {"decomposed": med(DeviceStep(*args, **kw)) if w.dk <= 128 else None,
+           "recv_first": med(RecvFirstStep(*args, **kw)) if w.dk <= 128 else None,
            "exact_passes": med(ExactStep(*args, schedule="passes", **kw))}
     chained = w.dtype == "bf16" and w.dk == w.dv == 128 and w.chunk == 64 and w.mode != "gate"
     out["exact_chained"] = med(ExactStep(*args, schedule="chained", **kw)) if chained else None
+    if chained:
+        binding.la_chain_status()  # raises if a chained wave gave up on a wait (NaN outputs)
     out["two_pass_chunk_states"] = med(ExactStep(*args, schedule="passes", subseg_chunks=1, **kw))
     return out
 
@@ -498,7 +493,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=400,
                     help="untimed steps first; the GPU's clocks take ~10 ms of sustained work to settle")
     ap.add_argument("--workload", type=int, default=1, help="index into chunked_scan_amd.inputs.WORKLOADS")
-    ap.add_argument("--step", choices=("auto", "exact", "decomposed", "chained"), default="auto",
+    ap.add_argument("--step", choices=("auto", "exact", "decomposed", "recv_first", "chained"), default="auto",
                     help="form of the device step (one-segment workloads): one exact la_chunk_fwd from S_recv "
                          "(the library's separate passes, or its chained single launch), or the pages' local "
                          "forward + All-Scan + output correction; auto = the faster on MI355X: exact without "
@@ -521,9 +516,9 @@ def main():
 
     import torch
 
-    from chunked_scan_amd import binding
+    from chunked_scan_amd import binding, profsum
     from chunked_scan_amd.inputs import WORKLOADS, make_inputs
-    from chunked_scan_amd.pipeline import DeviceStep, ExactStep, SegmentedForward
+    from chunked_scan_amd.pipeline import DeviceStep, ExactStep, RecvFirstStep, SegmentedForward
 
     def form_of(wx):
         if args.step == "auto":
@@ -535,9 +530,21 @@ def main():
         kw = dict(mode=wx.mode, chunk=wx.chunk, gate_norm=wx.gate_norm)
         if form == "decomposed":
             return DeviceStep(*a, **kw)
+        if form == "recv_first":
+            return RecvFirstStep(*a, **kw)
         return ExactStep(*a, schedule="chained" if form == "chained" else "auto", **kw)
 
     torch.cuda.set_device(0)
+    if args.calib_copy_mib:  # counter runs (chunked_scan_amd.profsum) scale FETCH/WRITE_SIZE by this copy
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
     if args.backward_only:
         print(json.dumps(dict(backward=backward_legs(torch.cuda.current_stream()))))
         return
@@ -584,6 +591,8 @@ def main():
     # --- cold: the last-level cache evicted before every step (last: the 512 MiB reads between
     # steps change the GPU's power state for the regions after them)
     cold = step_stats(step, args.steps, stream, scratch)
+    if w.nseg == 1 and form_of(w) == "chained":
+        binding.la_chain_status()  # raises if a chained wave gave up on a wait (NaN outputs)
     log(f"[bench] per step: warm median {warm['median_us']:.1f} us, cold median {cold['median_us']:.1f} us")
 
     eps = None
@@ -632,15 +641,6 @@ def main():
             backward[WORKLOADS[1].name]["cpu_baseline"] = cpu_baseline_backward(WORKLOADS[1])
         sweep = state_size_sweep(stream)
 
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
-
     tokens = w.B * w.L
     gate_bytes = 4 * w.dk if w.mode == "gate" else 0
     by_tok, fl_tok = algorithmic(w, gate_bytes)
@@ -650,7 +650,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("source_sha256_16") == source_hash() and tr.get("workload") == w.name and tr.get("kernel") == dom:
+        if tr.get("source_sha256_16") == profsum.source_hash() and tr.get("workload") == w.name and tr.get("kernel") == dom:
             traffic = tr["bytes_per_launch"]
     alg_bytes = tokens * w.H * by_tok if dom.endswith("_output_pass") else None
     roof = None

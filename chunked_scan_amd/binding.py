@@ -25,10 +25,12 @@ LIB_PATH = os.environ.get("LACHUNK_LIB") or os.path.join(_HERE, "liblachunk.so")
 LA_F32, LA_BF16 = 0, 1
 MODES = {"none": 0, "head": 1, "gate": 2}
 STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_SHAPE", -3: "LA_ERR_DTYPE", -4: "LA_ERR_ALIAS",
-          -5: "LA_ERR_UNSUPPORTED", -6: "LA_ERR_LAUNCH", -7: "LA_ERR_DECAY", -8: "LA_ERR_WORKSPACE"}
+          -5: "LA_ERR_UNSUPPORTED", -6: "LA_ERR_LAUNCH", -7: "LA_ERR_DECAY", -8: "LA_ERR_WORKSPACE",
+          -9: "LA_ERR_TIMEOUT"}
 NOALLOC_SCRATCH_BYTES = 32 << 20  # LA_NOALLOC_SCRATCH_BYTES of la_chunk.h
 EXPORTS = ("la_chunk_fwd", "la_chunk_fwd_noalloc", "la_chunk_fwd_decayed", "la_chunk_bwd", "la_chunk_bwd_states", "la_state_scan", "la_state_correct", "la_state_correct_live",
-           "la_cumdecay", "la_trim_workspace", "la_status_str", "la_supported", "la_version")
+           "la_cumdecay", "la_trim_workspace", "la_chain_status", "la_set_chain_spin_limit", "la_status_str", "la_supported",
+           "la_version")
 
 
 TRACE_MAX = 16
@@ -106,8 +108,11 @@ def lib() -> ctypes.CDLL:
         L.la_status_str.argtypes = [ctypes.c_int]
         L.la_status_str.restype = ctypes.c_char_p
         L.la_trim_workspace.argtypes = []
+        L.la_chain_status.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
+        L.la_set_chain_spin_limit.argtypes = [ctypes.c_int32]
         for f in (L.la_chunk_fwd, L.la_chunk_fwd_noalloc, L.la_chunk_fwd_decayed, L.la_trim_workspace, L.la_state_scan, L.la_state_correct,
-                  L.la_state_correct_live, L.la_cumdecay, L.la_supported, L.la_version):
+                  L.la_state_correct_live, L.la_cumdecay, L.la_supported, L.la_version, L.la_chain_status,
+                  L.la_set_chain_spin_limit):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -431,3 +436,18 @@ def la_cumdecay(decay: Optional[torch.Tensor], B: int, H: int, L: int, dk: int, 
 def la_trim_workspace() -> None:
     """Return the current device's unused workspace-pool memory to the device."""
     _check("la_trim_workspace", lib().la_trim_workspace())
+
+
+def la_chain_status(clear: bool = True) -> int:
+    """Synchronise the current device and return how many chained-forward waves gave up on a wait
+    since the counter was last cleared (raises LaError(LA_ERR_TIMEOUT) when any did)."""
+    n = ctypes.c_int64(0)
+    st = lib().la_chain_status(1 if clear else 0, ctypes.byref(n))
+    _check("la_chain_status", st)
+    return n.value
+
+
+def la_set_chain_spin_limit(limit: int) -> int:
+    """Polls per flag before a chained wave gives up, for later launches; returns the previous value
+    (a negative limit only reads it)."""
+    return lib().la_set_chain_spin_limit(limit)

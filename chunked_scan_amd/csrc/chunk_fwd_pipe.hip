@@ -746,12 +746,20 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 // waits in steps 2 and 3 span the whole chain, so every workgroup of the launch must be resident
 // at once: the launcher uses this kernel only when the grid fits the device's compute units (one
 // workgroup each).  Waits are bounded as well: a wave that polls a flag spin_limit times without
-// seeing it set gives up and makes its state NaN, so the outputs show it rather than the GPU
-// hanging.
+// seeing it set gives up, makes its state NaN (so the outputs show it rather than the GPU
+// hanging) and adds one to the device's give-up counter, which the host reads and clears.
 // Workspace (per chain, per sub-segment but the last, per compute wave): 16 KiB of aggregate and
 // 16 KiB of scanned state; int flags for the aggregates and for the slices; the ticket counter.
 // Flags and ticket start at zero (chain_reset_kernel).
 constexpr int CH_WAVE_FLOATS = 64 * 64;  // one compute wave's part of a state
+
+}  // namespace
+
+// Waits of the chained forward that gave up since the host last cleared the counter (one copy
+// per device; written only by device atomics, read and cleared by chain_status).
+__device__ unsigned int chain_give_ups;
+
+namespace {
 
 __global__ __launch_bounds__(256) void chain_reset_kernel(int* __restrict__ flags, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -930,6 +938,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_chain_kernel(
     // 4. the outputs, from the exact incoming state
 #pragma unroll
     for (int m = 0; m < 4; m++) S[m] = I[m];
+    if (!ok && lane == 0) atomicAdd(&chain_give_ups, 1u);
     compute_walk<MODE, false>(S, lds, otile, o, lam, wk, w, lane);
     if (j == G - 1 && s_out) {
         float* dst = s_out + bh * s_out_stride + (int64_t)seg * D * D;
@@ -984,16 +993,25 @@ hipError_t launch_chain_mode(const FwdArgs& a, int G, int cps, float* ws) {
               chain_reset_kernel<<<(unsigned)((nflags + 1 + 255) / 256), 256, 0, a.stream>>>(flags, nflags + 1));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // about four seconds of polling before a wave gives up on a flag
-    constexpr int SPIN_LIMIT = 1 << 22;
     LA_TRACED(a.tr, "chunk_fwd_chain_output_pass",
               pipe_chain_kernel<MODE><<<(unsigned)(units * G), NT, 0, a.stream>>>(
                   (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.decay, a.s_in, (__bf16*)a.o,
-                  a.s_out, a.s_out_stride, agg, incl, flags, ticket, a.H, a.L, a.nseg, G, cps, SPIN_LIMIT));
+                  a.s_out, a.s_out_stride, agg, incl, flags, ticket, a.H, a.L, a.nseg, G, cps, chain_spin_limit));
     return hipGetLastError();
 }
 
 }  // namespace
+
+// Polls per flag before a chained wave gives up: about four seconds by default.
+int chain_spin_limit = 1 << 22;
+
+hipError_t chain_status(unsigned int* give_ups, bool clear) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpyFromSymbol(give_ups, HIP_SYMBOL(chain_give_ups), sizeof(unsigned int));
+    const unsigned int zero = 0;
+    if (e == hipSuccess && clear) e = hipMemcpyToSymbol(HIP_SYMBOL(chain_give_ups), &zero, sizeof(unsigned int));
+    return e;
+}
 
 size_t chain_workspace_floats(const FwdArgs& a, int G) {
     const size_t units = (size_t)(a.B * a.H * a.nseg);

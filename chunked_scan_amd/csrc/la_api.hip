@@ -170,7 +170,7 @@ la::Tracer make_tracer(const la_shape* s) {
 
 extern "C" {
 
-int32_t la_version(void) { return (1 << 16) | 1; }
+int32_t la_version(void) { return (1 << 16) | 2; }
 
 la_status la_trim_workspace(void) { return from_hip(la::workspace_trim()); }
 
@@ -185,11 +185,25 @@ const char* la_status_str(int32_t status) {
         case LA_ERR_LAUNCH: return "HIP launch or workspace allocation failed";
         case LA_ERR_DECAY: return "invalid decay mode or gate_norm";
         case LA_ERR_WORKSPACE: return "the call needs more workspace than the allocation-free entry point holds";
+        case LA_ERR_TIMEOUT: return "a chained forward's bounded wait gave up; its outputs hold NaN";
     }
     return "unknown status";
 }
 
 int32_t la_supported(const la_shape* s, int32_t chunk) { return check_fwd_shape(s, chunk) == LA_OK ? 1 : 0; }
+
+la_status la_chain_status(int32_t clear, int64_t* give_ups) {
+    unsigned int n = 0;
+    if (la::chain_status(&n, clear != 0) != hipSuccess) return LA_ERR_LAUNCH;
+    if (give_ups) *give_ups = n;
+    return n ? LA_ERR_TIMEOUT : LA_OK;
+}
+
+int32_t la_set_chain_spin_limit(int32_t limit) {
+    const int32_t prev = la::chain_spin_limit;
+    if (limit >= 0) la::chain_spin_limit = limit;
+    return prev;
+}
 
 }  // extern "C"
 

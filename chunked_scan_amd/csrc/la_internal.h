@@ -155,6 +155,10 @@ hipError_t launch_chunk_fwd_tiled(const FwdArgs& a, int G, int cps, float* part_
 // (chain_workspace_floats floats).
 size_t chain_workspace_floats(const FwdArgs& a, int G);
 hipError_t launch_chunk_fwd_chain(const FwdArgs& a, int G, int cps, float* ws);
+// polls per flag before a chained wave gives up (host-side setting, read at each launch)
+extern int chain_spin_limit;
+// synchronises the current device, then reads (and optionally clears) its give-up counter
+hipError_t chain_status(unsigned int* give_ups, bool clear);
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay, int* wide);
 // The same for dk = dv = 32 or 64 (chunk_fwd_small.hip).
 hipError_t launch_chunk_fwd_small(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);

@@ -25,6 +25,12 @@ correction.
                      with S_recv as the first entry and runs every sub-segment's outputs from its
                      exact incoming state (no correction pass); ``schedule`` picks the library's
                      separate passes or its chained single launch.
+``RecvFirstStep`` -- the decomposed step with S_recv taken in at the start of the first sub-segment:
+                     the segment is cut into G segments of one segmented forward, the first of
+                     which starts from S_recv (it is then exact), the others from zero; the scan
+                     over their G local states yields every incoming state, and the correction
+                     covers sub-segments 1..G-1 only.  It saves the first sub-segment's correction
+                     and one scan entry, at the price of a local forward that needs S_recv.
 ``segmented_forward`` -- P devices emulated on one GPU: the local forward of all P segments in
                      one launch, the P-entry state scan, and the correction of segments 1..P-1.
 """
@@ -142,6 +148,27 @@ class ExactStep:
                      chunk=self.chunk, gate_norm=self.gate_norm, subseg_chunks=self.subseg_chunks,
                      schedule=self.schedule, timer=t.get("fwd"))
         return self.o, self.s_out[:, :, 0]
+
+
+class RecvFirstStep:
+    """One device step as a segmented forward over G sub-segments whose first starts from S_recv;
+    ``run()`` may be timed or graph-captured.  Returns (o, s_out [B,H,dk,dv])."""
+
+    def __init__(self, q, k, v, decay, s_recv, *, mode: str, chunk: int = 64, gate_norm: float = 16.0,
+                 subseg_chunks: int = 0, subseg: int = 0):
+        B, H, L, dk = q.shape
+        G = subseg or subsegments(B, H, L, dk=dk)
+        if L % G:
+            raise ValueError(f"{G} sub-segments do not divide L = {L}")
+        self.G = self.nseg = G
+        self.seg = SegmentedForward(q, k, v, decay, s_recv, mode=mode, nseg=G, chunk=chunk, gate_norm=gate_norm,
+                                    subseg_chunks=subseg_chunks)
+        self.live = self.seg.live  # gate mode: the forward's tile flags of q * cumulative decay
+
+    def run(self, timers: Optional[dict] = None):
+        """One step.  ``timers`` optionally maps "fwd", "cum", "scan", "corr" to KernelTimers."""
+        o, states = self.seg.run(timers)
+        return o, states[:, :, -1]
 
 
 def device_step(q, k, v, decay, s_recv, *, mode: str, chunk: int = 64, gate_norm: float = 16.0,

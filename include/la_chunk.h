@@ -55,7 +55,8 @@ typedef enum la_status {
     LA_ERR_UNSUPPORTED = -5, /* valid request that this build has no kernel for (e.g. dk > 128) */
     LA_ERR_LAUNCH = -6,      /* the HIP runtime refused a launch or a workspace allocation */
     LA_ERR_DECAY = -7,       /* unknown decay mode, or gate_norm <= 0 in gate mode */
-    LA_ERR_WORKSPACE = -8    /* la_chunk_fwd_noalloc: the call needs more than LA_NOALLOC_SCRATCH_BYTES */
+    LA_ERR_WORKSPACE = -8,   /* la_chunk_fwd_noalloc: the call needs more than LA_NOALLOC_SCRATCH_BYTES */
+    LA_ERR_TIMEOUT = -9      /* la_chain_status: a chained forward's bounded wait gave up */
 } la_status;
 
 typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
@@ -355,6 +356,23 @@ la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const l
  * the device (the pool keeps what it has obtained until then; later calls obtain it again).
  * Returns LA_OK or LA_ERR_LAUNCH. */
 la_status la_trim_workspace(void);
+
+/* Give-up counter of the chained forward (fwd_schedule = 2).  Its workgroups wait for each other's
+ * flags; every wait is bounded, and a compute wave that polls a flag la_set_chain_spin_limit's
+ * number of times without seeing it set stops waiting, computes on a NaN state (so its outputs are
+ * NaN rather than the GPU hanging) and adds one to a per-device counter.  This call synchronises
+ * the current device (do not call it while a stream of that device is being captured), stores the
+ * counter in *give_ups (if not NULL) and, when clear != 0, resets it to zero.  A chained launch
+ * whose workgroups are all resident (the library only chains grids that fit the device) does not
+ * give up at the default limit.
+ * Returns LA_OK if the counter was zero, LA_ERR_TIMEOUT if not, LA_ERR_LAUNCH if the runtime failed. */
+la_status la_chain_status(int32_t clear, int64_t* give_ups);
+
+/* Polls per flag before a chained wave gives up (default 4194304, about four seconds); limit >= 0
+ * sets it for launches enqueued afterwards in this process, a negative limit only reads it.
+ * Returns the previous value.  A small limit forces the give-up path (failure-handling tests: with
+ * 0 every wave that waits gives up at once).  Not synchronised with concurrent launching threads. */
+int32_t la_set_chain_spin_limit(int32_t limit);
 
 /* Static description of a status code (any int32_t: codes that are not a la_status give
  * "unknown status"); never NULL. */

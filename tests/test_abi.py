@@ -15,7 +15,7 @@ from chunked_scan_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "la_chunk.h")
 
-OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, LAUNCH, DECAY, WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, LAUNCH, DECAY, WORKSPACE, TIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 
 @pytest.fixture(scope="module")
@@ -40,8 +40,19 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.la_version() >> 16 == 1
-    for code in (OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, LAUNCH, DECAY, WORKSPACE, 12345):
-        assert lib.la_status_str(code)
+    for code in (OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, LAUNCH, DECAY, WORKSPACE, TIMEOUT):
+        assert lib.la_status_str(code) and lib.la_status_str(code) != b"unknown status", code
+        assert B.STATUS[code]
+    assert lib.la_status_str(12345) == b"unknown status"
+
+
+def test_chain_spin_limit_setting(lib):
+    # host-side setting only: no launch, no device
+    default = lib.la_set_chain_spin_limit(-1)
+    assert default == 1 << 22
+    assert lib.la_set_chain_spin_limit(7) == default
+    assert lib.la_set_chain_spin_limit(-5) == 7  # negative: read only
+    assert lib.la_set_chain_spin_limit(default) == 7
 
 
 def test_shape_struct_layout():

@@ -138,3 +138,31 @@ def test_chain_noalloc_and_graph_replay():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(s, s_ref), rep
+
+
+def test_chain_give_up_is_reported():
+    """Failure handling, forced from the host: with a spin limit of 0 every chained wave that waits
+    gives up at once.  The kernel still ends normally; the sub-segments after the first compute on
+    NaN states; la_chain_status reports the give-ups as LA_ERR_TIMEOUT and clears the counter.  With
+    the default limit the same call gives up nowhere and matches the passes."""
+    w = W2.scaled(B=1, H=2, L=64 * 8, s_in_std=0.05, seed=3400)
+    note("chained forward: forced give-up (spin limit 0) and its status")
+    d = to_dev(make_inputs(w, "cpu"))
+    assert lb.la_chain_status() == 0
+    prev = lb.la_set_chain_spin_limit(0)
+    try:
+        o, s = _fwd(d, w, subseg=2)  # four sub-segments of 128 tokens
+        with pytest.raises(lb.LaError) as err:
+            lb.la_chain_status()
+        assert err.value.status == -9
+    finally:
+        assert lb.la_set_chain_spin_limit(prev) == 0
+    assert lb.la_chain_status() == 0  # cleared by the call that reported
+    of = o.float()
+    assert torch.isfinite(of[:, :, :128]).all()  # the first sub-segment starts from s_in
+    assert torch.isnan(of[:, :, 128:]).all() and torch.isnan(s).all()
+    oc, sc = _fwd(d, w, subseg=2)
+    op, sp = _fwd(d, w, "passes", subseg=2)
+    assert lb.la_chain_status() == 0
+    assert rel_err(oc, op.double().cpu().numpy()) <= 2e-2
+    assert rel_err(sc, sp.double().cpu().numpy()) <= 1e-4
