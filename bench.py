@@ -496,8 +496,9 @@ def main():
     ap.add_argument("--step", choices=("auto", "exact", "decomposed", "recv_first", "chained"), default="auto",
                     help="form of the device step (one-segment workloads): one exact la_chunk_fwd from S_recv "
                          "(the library's separate passes, or its chained single launch), or the pages' local "
-                         "forward + All-Scan + output correction; auto = the faster on MI355X: exact without "
-                         "decay and with head decay, decomposed with the gate (its correction skips the tiles "
+                         "forward + All-Scan + output correction (recv_first: with S_recv taken in by the first "
+                         "sub-segment, whose correction then drops); auto = the faster on MI355X: exact without "
+                         "decay and with head decay, recv_first with the gate (its correction skips the tiles "
                          "whose cumulative decay has underflowed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alongside", action="store_true",
@@ -522,7 +523,7 @@ def main():
 
     def form_of(wx):
         if args.step == "auto":
-            return "decomposed" if wx.mode == "gate" else "exact"
+            return "recv_first" if wx.mode == "gate" else "exact"
         return "exact" if args.step == "chained" and wx.mode == "gate" else args.step
 
     def one_segment_step(wx, ix, form):
@@ -693,7 +694,10 @@ def main():
                                  "chained": f"{w.name}: device step = exact O and S_out from S_recv in one chained "
                                             f"launch (state pass, flag hand-off scan, output pass)",
                                  "decomposed": f"{w.name}: device step = local chunked fwd + All-Scan state combine "
-                                               f"+ output correction"}[form_of(w)]) if w.nseg == 1 else
+                                               f"+ output correction",
+                                 "recv_first": f"{w.name}: device step = local chunked fwd with S_recv taken in by the "
+                                               f"first sub-segment + All-Scan state combine + output correction of "
+                                               f"the others"}[form_of(w)]) if w.nseg == 1 else
                                (f"{w.name}: {w.nseg} segments on one device = local chunked fwd + segmented "
                                 f"state scan + output correction"), "B": w.B, "H": w.H, "L": w.L, "dk": w.dk, "dv": w.dv,
                    "chunk": w.chunk, "decay": w.decay, "parallelism": "single GPU"},

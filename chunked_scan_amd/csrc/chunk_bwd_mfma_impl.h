@@ -597,7 +597,9 @@ struct DqSmem {
     __bf16 o[SO ? 8 : TILE];  // d_o
     __bf16 v[TILE];
     __bf16 k[SO ? 8 : TILE];  // k (the P' K product); gate: k 2^{-B}
-    __bf16 kt[TILE];          // k_j a^{n-1-j} (the state update); gate: k 2^{B_last - B}
+    // k_j a^{n-1-j} (the state update); gate: k 2^{B_last - B}; without decay the output pass
+    // reads k itself
+    __bf16 kt[(MODE == DECAY_NONE && !SO) ? 8 : TILE];
     __bf16 sm[SO ? 8 : D * PITCH];  // S^T as bf16, [value column][key row]
     __bf16 p[SO ? 8 : C * PPITCH];  // P' w, [i][j]
     float gb[GATE ? C * D : 4];     // gate: in-chunk cumulative log2-decay
@@ -767,7 +769,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
                     if (!STATE_ONLY) *(u32x4*)(&sm.k[tr * PITCH + c8]) = in ? scale8(xk, fh) : z;
                 } else if (MODE == DECAY_HEAD) {
                     *(u32x4*)(&sm.kt[row * PITCH + c8]) = scale8s(xk, sm.apow[max(n - 1 - row, 0)]);
-                } else {
+                } else if (STATE_ONLY) {
                     *(u32x4*)(&sm.kt[row * PITCH + c8]) = xk;
                 }
                 if (!STATE_ONLY) {
@@ -904,7 +906,9 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
                     for (int i = 0; i < 16; i++) Sm[m][i] *= sm.gel[32 * m + (i >> 2) * 8 + kg * 4 + (i & 3)];
                 }
 #pragma unroll
-                for (int ks = 0; ks < 4; ks++) Sm[m] = mfma(tr_operand(sm.kt, PITCH, ks, 32 * m, lane), vb[ks], Sm[m]);
+                for (int ks = 0; ks < 4; ks++)
+                    Sm[m] = mfma(tr_operand((MODE == DECAY_NONE && !STATE_ONLY) ? sm.k : sm.kt, PITCH, ks, 32 * m, lane),
+                                 vb[ks], Sm[m]);
             }
         }
         }  // windows

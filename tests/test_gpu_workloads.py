@@ -10,7 +10,7 @@ import torch
 import oracle
 from chunked_scan_amd import binding as lb
 from chunked_scan_amd.inputs import WORKLOADS, make_inputs
-from chunked_scan_amd.pipeline import DeviceStep, ExactStep, SegmentedForward
+from chunked_scan_amd.pipeline import DeviceStep, ExactStep, RecvFirstStep, SegmentedForward
 
 from gpu_util import ORC_MODE, TOL, host32, note, rel_err
 
@@ -60,6 +60,14 @@ def test_workload_device_step(wid, pairs):
         for n, (b, h) in enumerate(pairs):
             assert rel_err(o2[b, h], o_ref[n]) <= TOL["bf16"], (schedule, b, h)
             assert rel_err(s2[b, h], s_ref[n]) <= TOL["bf16"], (schedule, b, h)
+    # the decomposed form with S_recv taken in by the first sub-segment
+    note(f"workload {wid}: decomposed step, first sub-segment from S_recv")
+    o3, s3 = RecvFirstStep(inp["q"], inp["k"], inp["v"], inp["decay"], inp["s_in"], mode=w.mode, chunk=w.chunk,
+                           gate_norm=w.gate_norm).run()
+    torch.cuda.synchronize()
+    for n, (b, h) in enumerate(pairs):
+        assert rel_err(o3[b, h], o_ref[n]) <= TOL["bf16"], ("recv_first", b, h)
+        assert rel_err(s3[b, h], s_ref[n]) <= TOL["bf16"], ("recv_first", b, h)
 
 
 def test_workload4_segmented_1M():
