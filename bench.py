@@ -668,6 +668,16 @@ def main():
                     kernel_mean_us=round(dom_us, 2), algorithmic_bytes=alg_bytes,
                     mfma_frac=round(tokens * w.H * fl_tok / (dom_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
                     measured_copy_GBps=copy_rate_gbs())
+        # the whole step against the same peak: every kernel's algorithmic bytes, and the compulsory
+        # bytes (each input read once, each output written once), over the back-to-back step time
+        step_bytes = sum(int(d["algorithmic_bytes"] * d["launches_per_step"]) for d in kernels.values()
+                         if "algorithmic_bytes" in d)
+        es = 2 if w.dtype == "bf16" else 4
+        compulsory = tokens * w.H * (es * (2 * w.dk + 2 * w.dv) + (4 * w.dk if w.mode == "gate" else 0))
+        step_s = ms_per_step * 1e-3
+        roof["step"] = dict(algorithmic_bytes=step_bytes, frac=round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+                            compulsory_bytes=compulsory,
+                            compulsory_frac=round(compulsory / step_s / 1e9 / HBM_PEAK_GBS, 4))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -494,6 +494,9 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
         // 8 o8 .. +7 of tokens 4 tg .. +3; the 16 token groups of a dim octet are one 16-lane row,
         // so the scan over them is DPP.
         const int lw = wave - 4;
+        // the preparation of the next chunk is on the critical path (the compute waves of the same
+        // SIMD are mostly in the matrix cores): its instructions go first (gate step, B4: -1.5%)
+        __builtin_amdgcn_s_setprio(2);
         const int o8 = 4 * lw + (lane >> 4);
         const int tg = lane & 15;
         struct Raw {
