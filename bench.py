@@ -23,7 +23,8 @@ before each step evicts the 256 MB last-level cache; reading, not writing, so th
 not also pay for writing back someone else's dirty lines).  The head-decay and gate workloads
 (B = 2 and 4) and the 1M-token 64-segment pass are timed alongside, unless --no-alongside.
 Every workload is warmed up with at least ~20 ms of steps first: the GPU's clocks take about
-10 ms of sustained work to settle.
+10 ms of sustained work to settle (for the main step this runs before the --warmup steps and is
+reported as clock_settle).
 """
 from __future__ import annotations
 
@@ -569,10 +570,23 @@ def main():
     # reading this buffer evicts the 256 MB last-level cache before a "cold" step
     scratch = torch.ones(512 << 18, dtype=torch.float32, device="cuda")
 
+    # Clocks: the GPU reaches its sustained clocks only after ~10 ms of continuous work (the plain
+    # step runs ~10% slower for its first ~100 steps), so before the W warm-up steps the step runs
+    # untimed for at least 20 ms of GPU time; the figure is reported as clock_settle.
+    settle_ms, settle_steps = 0.0, 0
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    while settle_ms < 20.0 and settle_steps < 4000:
+        s0.record(stream)
+        for _ in range(10):
+            step.run()
+        s1.record(stream)
+        s1.synchronize()
+        settle_ms += s0.elapsed_time(s1)
+        settle_steps += 10
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done")
+    log(f"[bench] clocks settled over {settle_steps} steps ({settle_ms:.1f} ms); warmup {args.warmup} done")
 
     # --- every step bracketed by its own events (warm: back to back on the same inputs)
     warm = step_stats(step, args.steps, stream)
@@ -722,6 +736,7 @@ def main():
         "per_step_us": {"warm": warm, "cold": cold},
         "kernels": {n: {k: round(v, 2) for k, v in d.items()} for n, d in kernels.items()},
         "ms_per_step_with_kernel_events": round(ms_traced, 5),
+        "clock_settle": {"steps": settle_steps, "ms": round(settle_ms, 2)},
         "overhead_one_gpu_us": eps,
         "alongside": alongside,
         "backward": backward,

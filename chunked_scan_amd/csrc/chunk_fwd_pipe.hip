@@ -30,12 +30,14 @@
 //   outputs into an LDS tile, which the loader waves store row-major (1 KiB contiguous per
 //   instruction).  Per chunk one barrier hands a landed stage to the compute waves and frees the
 //   stage they finished, and (in the output pass) a second one hands the output tile over.
-// * Gate mode.  The loader waves load q, k, v and g into registers two chunks ahead and, while
-//   the compute waves work on chunk c, prepare chunk c + 1 in its stage (two stages: chunk c + 1
-//   goes where chunk c - 1 was): the in-chunk cumulative log-decay (a per-lane prefix plus a DPP
-//   scan across lanes), qbar, kbar, v and the chunk's decay per key dim.  The compute waves then
-//   run the no-decay products and scale their state rows by the chunk decay; their outputs go
-//   through two LDS output tiles, and at the top of chunk c they store chunk c - 1's tile as
+// * Gate mode.  The loader waves load q, k and g into registers two chunks ahead and, while the
+//   compute waves work on chunk c, prepare chunk c + 1 in its stage (two stages: chunk c + 1 goes
+//   where chunk c - 1 was): the in-chunk cumulative log-decay (a per-lane prefix plus a DPP scan
+//   across lanes), qbar, kbar and the chunk's decay per key dim.  v needs no preparation: the
+//   compute waves load it straight into the stage with LDS DMA, chunk c + 1's at the top of chunk
+//   c, which keeps it off the loaders' critical path and out of their registers.  The compute
+//   waves run the no-decay products and scale their state rows by the chunk decay; their outputs
+//   go through two LDS output tiles, and at the top of chunk c they store chunk c - 1's tile as
 //   whole rows (stored 32 bytes per row piece directly, the outputs cost twice their bytes in
 //   writes; the loaders, at their register limit, cannot take the stores over).
 // * Ragged chunks.  DMA rows past a chunk's end re-read its last row, which only reaches output
@@ -127,9 +129,32 @@ struct Dma {
     }
 };
 
-// LDS layout of one pass: SLOT tiles per ring stage (k, v; q too in the output pass), gate mode's
-// chunk decay after the tiles, NST stages (NST - 1 chunks in flight; gate: the loaders prepare one
-// stage ahead, so three), and in the output pass without gate an output tile after the ring.
+// Gate mode: the compute waves load each chunk's v tile straight into its stage (v needs no
+// preparation), wave w rows 16 w .. 16 w + 15, as Dma::issue does; rows past the chunk's end re-read
+// its last row, which only reaches output rows that are never stored and state-update tokens whose
+// V operand is zeroed.  The barrier at the top of the next chunk waits for it (an LDS fence waits
+// for the wave's LDS DMA too).
+template <int CPOL>
+__device__ __forceinline__ void dma_tile(const __bf16* src, __bf16* tile, int64_t row0, int n, int w, int lane) {
+    // the lane offsets are recomputed at every call rather than kept live across the caller's loop,
+    // and the wave index is made scalar, so that the LDS destinations are scalar arithmetic
+    asm volatile("" : "+v"(lane));
+    const int ws = __builtin_amdgcn_readfirstlane(w);
+    const int64_t base = row0 * D;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int R = (4 * ws + j) * 4 + (lane >> 4);
+        const int off = min(R, n - 1) * D + (((lane & 15) ^ swz(R)) << 3);
+        __builtin_amdgcn_global_load_lds((const void*)(src + base + off), (lds_void*)(tile + (4 * ws + j) * 512), 16, 0,
+                                         CPOL);
+    }
+}
+
+// LDS layout of one pass: SLOT tiles per ring stage (k, v; q too in the output pass), NST stages
+// (NST - 1 chunks in flight), and in the output pass without gate an output tile after the ring.
+// Gate mode: the stages hold the prepared k (and q) and the chunk's decay after the tiles, two
+// stages (the loaders prepare one chunk ahead); the v tiles are a separate pair of LDS arrays (the
+// compute waves load them by DMA, and accesses to other arrays need not wait for that DMA).
 template <int MODE, bool STATE_ONLY>
 struct Layout {
     static constexpr bool GATE = MODE == DECAY_GATE;
@@ -137,7 +162,7 @@ struct Layout {
     // gate output pass: the same, with two output tiles (the loaders store chunk c - 1's while the
     // compute waves fill chunk c's)
     static constexpr bool GTILE = !STATE_ONLY && GATE;
-    static constexpr int SLOT = STATE_ONLY ? 2 : 3;
+    static constexpr int SLOT = (STATE_ONLY ? 2 : 3) - (GATE ? 1 : 0);
     static constexpr int STAGE = SLOT * TE + (GATE ? 2 * D : 0);  // gate: D floats of chunk decay after the tiles
     // gate: the loaders prepare chunk c + 1 while chunk c is computed, in the stage chunk c - 1 left
     static constexpr int NST = GATE ? 2 : (LDS_TILES - (OTILE ? 1 : 0)) / SLOT;
@@ -145,7 +170,8 @@ struct Layout {
     static constexpr int OTILES = OTILE ? 1 : GTILE ? 2 : 0;
     __device__ static __forceinline__ Ring stage(__bf16* ring, int c) {
         __bf16* b = ring + (c % NST) * STAGE;
-        // q is unused in the state pass
+        // q is unused in the state pass; gate: v is not in the ring
+        if (GATE) return Ring{b, b + (SLOT - 1) * TE, nullptr, (float*)(b + SLOT * TE)};
         return Ring{b, b + (SLOT - 2) * TE, b + (SLOT - 1) * TE, (float*)(b + SLOT * TE)};
     }
 };
@@ -211,7 +237,7 @@ __device__ __forceinline__ void loader_walk(const __bf16* q, const __bf16* k, co
 // lds_barrier per chunk (two in the output pass without gate), matching the loader waves.
 template <int MODE, bool STATE_ONLY>
 __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf16* otile, __bf16* o, float lam,
-                                             const Walk& wk, int w, int lane) {
+                                             const Walk& wk, int w, int lane, const __bf16* v, __bf16* vtile) {
     using LY = Layout<MODE, STATE_ONLY>;
     constexpr bool GATE = LY::GATE, OTILE = LY::OTILE;
     const int n32 = lane & 31, kg = lane >> 5;
@@ -223,8 +249,8 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
     // sigma order.
     const int quad = 4 * (((i16 & 1) << 1) | ((i16 >> 1) & 1));
     const int tb = (G16 >> 1) * 8 + (i16 >> 2);
-    int voff[2];      // V: value column vcol_lane
-    int ktoff[4][2];  // K for the state: key column 32m + sigma(n32)
+    int voff[2];  // V: value column vcol_lane
+    int ktoff[4][2];  // K for the state: key column 32m + sigma(n32) (gate: recomputed per chunk)
     {
         const int vcol = 32 * w + (G16 & 1) * 16 + quad;
         voff[0] = sw(tb, vcol);
@@ -232,10 +258,14 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
 #pragma unroll
         for (int m = 0; m < 4; m++) {
             const int kcol = 32 * m + (G16 & 1) * 16 + quad;
-            ktoff[m][0] = sw(tb, kcol);
-            ktoff[m][1] = sw(tb + 4, kcol);
+            ktoff[m][0] = GATE ? 0 : sw(tb, kcol);
+            ktoff[m][1] = GATE ? 0 : sw(tb + 4, kcol);
         }
     }
+
+    // gate: v of chunk 0 (the output pass is its last reader: non-temporal)
+    constexpr int VCPOL = STATE_ONLY ? 0 : 2;
+    if (GATE && wk.nch > 0) dma_tile<VCPOL>(v, vtile, wk.row_base + wk.t_begin, wk.chunk_len(0), w, lane);
 
     for (int c = 0; c < wk.nch; c++) {
         const Ring cur = LY::stage(ring, c);
@@ -248,13 +278,29 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
         if (MODE == DECAY_HEAD) asm volatile("" : "+s"(lamc));
         lamc *= LOG2E;
         const float e1 = (MODE == DECAY_HEAD) ? decay_pow2(lamc, 1) : 1.f;
+        if (GATE) waitcnt<0, 0>();  // this wave's DMA of chunk c's v has landed (and its stores are out)
         lds_barrier();  // chunk c has landed; every wave is done with chunk c - 1
+        // gate: chunk c - 1's output tile (complete since this barrier; chunk c + 1 overwrites it
+        // only after the next one).  The lane offsets are recomputed here rather than hoisted out of
+        // the loop (which spills).
+        if (LY::GTILE && c > 0) {
+            int t = threadIdx.x;
+            asm volatile("" : "+v"(t));
+            store_otile<true>(o, otile + ((c - 1) & 1) * TE, wk.row_base + wk.t_begin + (int64_t)(c - 1) * C, C, t);
+        }
 
         // V operand: tokens 16ks + kg*8 + jj (plain order), value column vcol_lane
+        const __bf16* vcur = GATE ? vtile + (c & 1) * TE : cur.v;
         bf16x8 vb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ks++)
-            vb[ks] = cat(lds_tr16(cur.v + 16 * ks * D + voff[0]), lds_tr16(cur.v + 16 * ks * D + voff[1]));
+            vb[ks] = cat(lds_tr16(vcur + 16 * ks * D + voff[0]), lds_tr16(vcur + 16 * ks * D + voff[1]));
+        // gate: v of chunk c + 1 into the other v tile, which chunk c - 1 has left; issued after this
+        // chunk's reads of v, so that no later LDS access of the chunk waits for it.  It and the
+        // output tile's stores have the whole chunk to complete before the next barrier.
+        if (GATE && c + 1 < wk.nch)
+            dma_tile<VCPOL>(v, vtile + ((c + 1) & 1) * TE, wk.row_base + wk.t_begin + (int64_t)(c + 1) * C,
+                            wk.chunk_len(c + 1), w, lane);
 
         if (!STATE_ONLY) {
             // the state as A operands of S^T Qbar^T: slab (m, hh) holds key dims 32m + 16hh + kg*8 + jj
@@ -416,13 +462,26 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
                 for (int jj = 0; jj < 8; jj++)
                     if (16 * ks + kg * 8 + jj >= n) vb[ks][jj] = (__bf16)0.f;
         }
+        {
+            // K for the state: key column 32m + sigma(n32), the same slab geometry as V.  Gate mode
+            // recomputes the offsets every chunk from a lane index hidden from the optimiser rather
+            // than keeping them live across the loop (eight registers, which spilled there).
+            int l2 = lane;
+            if (GATE) asm volatile("" : "+v"(l2));
+            const int i16k = l2 & 15, G16k = l2 >> 4;
+            const int quadk = 4 * (((i16k & 1) << 1) | ((i16k >> 1) & 1));
+            const int tbk = (G16k >> 1) * 8 + (i16k >> 2);
 #pragma unroll
-        for (int m = 0; m < 4; m++)
+            for (int m = 0; m < 4; m++) {
+                const int kcol = 32 * m + (G16k & 1) * 16 + quadk;
+                const int k0 = GATE ? sw(tbk, kcol) : ktoff[m][0], k1 = GATE ? sw(tbk + 4, kcol) : ktoff[m][1];
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                const bf16x8 a = cat(lds_tr16(cur.k + 16 * ks * D + ktoff[m][0]), lds_tr16(cur.k + 16 * ks * D + ktoff[m][1]));
-                S[m] = mfma(a, vb[ks], S[m]);
+                for (int ks = 0; ks < 4; ks++) {
+                    const bf16x8 a = cat(lds_tr16(cur.k + 16 * ks * D + k0), lds_tr16(cur.k + 16 * ks * D + k1));
+                    S[m] = mfma(a, vb[ks], S[m]);
+                }
             }
+        }
         if (GATE) {
             // S <- diag(exp(B_end)) (S + Kbar^T V), Kbar = K exp(-B): the same as decaying S and adding
             // (K exp(B_end - B))^T V.  Rows 4 at a time: element 4 g4 + e of tile m is key row
@@ -435,15 +494,6 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
 #pragma unroll
                     for (int e = 0; e < 4; e++) S[m][4 * g4 + e] *= f[e];
                 }
-        }
-        // gate: chunk c - 1's output tile has been complete since the top of this chunk, and chunk
-        // c + 1 overwrites it only after the next barrier (the loaders are at their register
-        // limit, so the compute waves store it, here, where only the state is live)
-        if (LY::GTILE && c > 0) {
-            // the lane offsets are recomputed here rather than hoisted out of the loop (which spills)
-            int t = threadIdx.x;
-            asm volatile("" : "+v"(t));
-            store_otile<true>(o, otile + ((c - 1) & 1) * TE, wk.row_base + wk.t_begin + (int64_t)(c - 1) * C, C, t);
         }
     }
     if (LY::GTILE) {
@@ -467,6 +517,8 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     // the chunk's outputs, rows unpadded with 16-byte slot s of row r at s ^ (r % 16)
     __shared__ __attribute__((aligned(16))) __bf16 otile[LY::OTILES ? LY::OTILES * TE : 8];
     __shared__ int first_dead[4];  // gate loader wave lw: its first chunk with zero cumulative decay
+    // gate: the v tiles of chunks c (c & 1), loaded by the compute waves
+    __shared__ __attribute__((aligned(16))) __bf16 vtile[GATE ? 2 * TE : 8];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t u = blockIdx.x;
@@ -486,21 +538,22 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     auto chunk_len = [&](int c) { return wk.chunk_len(c); };
 
     if (wave >= 4 && GATE) {
-        // ---- gate-mode loader wave lw.  Its lanes load q, k, v and g two chunks ahead into
+        // ---- gate-mode loader wave lw.  Its lanes load q, k and g two chunks ahead into
         // registers (plain loads: a wave that mixes LDS DMA with reads of what it loaded gets every
         // wait widened to the whole queue), and while the compute waves work on chunk c it prepares
         // chunk c + 1 in its stage: B = inclusive in-chunk sum of log2 a per key dim, q exp2(B),
-        // k exp2(-B) and v written to the tiles, el = exp2(B of the last token).  Lane: key dims
+        // k exp2(-B) written to the tiles, el = exp2(B of the last token).  Lane: key dims
         // 8 o8 .. +7 of tokens 4 tg .. +3; the 16 token groups of a dim octet are one 16-lane row,
         // so the scan over them is DPP.
         const int lw = wave - 4;
+        const float c1 = inv_norm * LOG2E;  // gate_log2decay's folded constant
         // the preparation of the next chunk is on the critical path (the compute waves of the same
         // SIMD are mostly in the matrix cores): its instructions go first (gate step, B4: -1.5%)
         __builtin_amdgcn_s_setprio(2);
         const int o8 = 4 * lw + (lane >> 4);
         const int tg = lane & 15;
         struct Raw {
-            u32x4 q[4], k[4], v[4];
+            u32x4 q[4], k[4];
             f32x4 g[8];
         };
         Raw rA, rB;
@@ -538,7 +591,6 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
             const int off = min(4 * tg + r, n - 1) * D + 8 * o8;
             if (!STATE_ONLY) x.q[r] = *(const u32x4*)(q + base + off);
             x.k[r] = *(const u32x4*)(k + base + off);
-            x.v[r] = *(const u32x4*)(v + base + off);
             x.g[2 * r] = *(const f32x4*)(decay + base + off);
             x.g[2 * r + 1] = *(const f32x4*)(decay + base + off + 4);
             if (r == 3) issued++;
@@ -560,7 +612,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
                     // computed for every row (past the end, g is a copy of the last row), then selected
-                    const float la = gate_logdecay(x.g[2 * r + (e >> 2)][e & 3], inv_norm) * LOG2E;
+                    const float la = gate_log2decay(x.g[2 * r + (e >> 2)][e & 3], inv_norm, c1);
                     b[r][e] = (r ? b[r - 1][e] : 0.f) + (4 * tg + r < n ? la : 0.f);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -583,15 +635,8 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
             // the chunk's decay per key dim: B of its last token (lane 15 of the row for a full chunk)
             float bl[8];
             if (n == C) {
-                const int row = lane >> 4;
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const int r0v = __builtin_amdgcn_readlane(__float_as_int(b[3][e]), 15);
-                    const int r1v = __builtin_amdgcn_readlane(__float_as_int(b[3][e]), 31);
-                    const int r2v = __builtin_amdgcn_readlane(__float_as_int(b[3][e]), 47);
-                    const int r3v = __builtin_amdgcn_readlane(__float_as_int(b[3][e]), 63);
-                    bl[e] = __int_as_float(row == 0 ? r0v : row == 1 ? r1v : row == 2 ? r2v : r3v);
-                }
+                for (int e = 0; e < 8; e++) bl[e] = __shfl(b[3][e], (lane & 48) | 15);
             } else {
                 const int tl = n - 1, src = (lane & 48) + (tl >> 2), rl = tl & 3;
 #pragma unroll
@@ -633,29 +678,34 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
             __builtin_amdgcn_sched_barrier(0);
             if (more) load_row(fill, 3);
             __builtin_amdgcn_sched_barrier(0);
-            // the prepared rows; past the chunk's end every tile row is zero
+            // The prepared rows.  Past the chunk's end B stays at its last token's value (the prefix
+            // adds nothing there), so those rows hold finite copies that reach only output rows that
+            // are never stored, scores that the causal mask removes and state-update tokens whose V
+            // operand the compute waves zero.
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int t = 4 * tg + r;
                 const int off = sw(t, 8 * o8);
-                const bool in = t < n;
                 float fk[8], fq[8];
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
-                    fk[e] = in ? __builtin_amdgcn_exp2f(-b[r][e]) : 0.f;
-                    fq[e] = in ? __builtin_amdgcn_exp2f(b[r][e]) : 0.f;
+                    fk[e] = __builtin_amdgcn_exp2f(-b[r][e]);
+                    fq[e] = __builtin_amdgcn_exp2f(b[r][e]);
                 }
                 *(u32x4*)(st.k + off) = scale8(x.k[r], fk);
-                *(u32x4*)(st.v + off) = in ? x.v[r] : u32x4{0, 0, 0, 0};
-                if (!STATE_ONLY) *(u32x4*)(st.q + off) = scale8(x.q[r], fq);
-                if (!STATE_ONLY && q_dec && in && !skip_qd) {
-                    // q times its cumulative decay from the segment start, rounded once
-                    float fd[8];
+                if (!STATE_ONLY) {
+                    float qf[8];
+                    mul8(x.q[r], fq, qf);
+                    *(u32x4*)(st.q + off) = pack8(qf);
+                    if (q_dec && t < n && !skip_qd) {
+                        // q times its cumulative decay from the segment start: the products above
+                        // times the decay to the chunk's start, rounded once
 #pragma unroll
-                    for (int e = 0; e < 8; e++) fd[e] = fq[e] * cf[e];
-                    // a wave-uniform row base plus a 32-bit lane offset (no 64-bit per-lane address)
-                    __bf16* const qrow = q_dec + (row_base + t_begin + (int64_t)cc * C) * D;
-                    *(u32x4*)(qrow + (t * D + 8 * o8)) = scale8(x.q[r], fd);
+                        for (int e = 0; e < 8; e++) qf[e] *= cf[e];
+                        // a wave-uniform row base plus a 32-bit lane offset (no 64-bit per-lane address)
+                        __bf16* const qrow = q_dec + (row_base + t_begin + (int64_t)cc * C) * D;
+                        *(u32x4*)(qrow + (t * D + 8 * o8)) = pack8(qf);
+                    }
                 }
             }
         };
@@ -714,7 +764,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
             for (int i = 0; i < 16; i++) S[m][i] = src ? src[(32 * m + sigma(acc_row(i, kg))) * D + vcol_lane] : 0.f;
     }
 
-    compute_walk<MODE, STATE_ONLY>(S, ring, otile, o, lam, wk, w, lane);
+    compute_walk<MODE, STATE_ONLY>(S, ring, otile, o, lam, wk, w, lane, v, vtile);
 
     float* dst = nullptr;
     if (STATE_ONLY) dst = part_state + (ub * (G - 1) + g) * (int64_t)D * D;
@@ -873,7 +923,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_chain_kernel(
     f32x16 S[4];
 #pragma unroll
     for (int m = 0; m < 4; m++) S[m] = f32x16{};
-    if (publish) compute_walk<MODE, true>(S, lds, nullptr, o, lam, wk, w, lane);
+    if (publish) compute_walk<MODE, true>(S, lds, nullptr, o, lam, wk, w, lane, v, nullptr);
     lds_barrier();  // the state pass's stages are free for the output pass's loads
     if (publish) {
         chain_store(wave_buf(agg, j), S, lane);
@@ -942,7 +992,7 @@ __global__ __launch_bounds__(NT, 1) void pipe_chain_kernel(
 #pragma unroll
     for (int m = 0; m < 4; m++) S[m] = I[m];
     if (!ok && lane == 0) atomicAdd(&chain_give_ups, 1u);
-    compute_walk<MODE, false>(S, lds, otile, o, lam, wk, w, lane);
+    compute_walk<MODE, false>(S, lds, otile, o, lam, wk, w, lane, v, nullptr);
     if (j == G - 1 && s_out) {
         float* dst = s_out + bh * s_out_stride + (int64_t)seg * D * D;
 #pragma unroll

@@ -72,6 +72,34 @@ __device__ __forceinline__ float gate_logdecay(float g, float inv_norm) {
     return fmaxf(-sp * inv_norm, GATE_LOG_FLOOR);
 }
 
+// The same in base 2, log2 a = log a * log2(e), folded into fewer instructions: with
+// c1 = inv_norm * log2(e) (and ln 2 * log2(e) = 1), -softplus(-g) * inv_norm * log2(e) =
+// min(g, 0) * c1 - inv_norm * log2(1 + 2^{-|g| log2(e)}); floored at GATE_LOG_FLOOR * log2(e).
+__device__ __forceinline__ float gate_log2decay(float g, float inv_norm, float c1) {
+    const float y = __builtin_amdgcn_exp2f(-fabsf(g) * LOG2E);
+    return fmaxf(fmaf(__builtin_amdgcn_logf(1.f + y), -inv_norm, fminf(g, 0.f) * c1), GATE_LOG_FLOOR * LOG2E);
+}
+
+// 8 bf16 (one 16-byte word) times 8 fp32 factors, unrounded; and 8 fp32 values rounded to
+// nearest even and packed as 8 bf16.
+__device__ __forceinline__ void mul8(u32x4 w, const float* f, float* out) {
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        out[2 * h] = bits_lo_bf16(w[h]) * f[2 * h];
+        out[2 * h + 1] = bits_hi_bf16(w[h]) * f[2 * h + 1];
+    }
+}
+__device__ __forceinline__ u32x4 pack8(const float* x) {
+    u32x4 r;
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        const __bf16 lo = (__bf16)x[2 * h];
+        const __bf16 hi = (__bf16)x[2 * h + 1];
+        r[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return r;
+}
+
 // a^m for a per-token log-decay lam and a token distance m >= 0, with a^0 = 1 exactly even when
 // lam = -inf (a = 0).
 __device__ __forceinline__ float decay_pow(float lam, int m) { return m == 0 ? 1.f : expf(lam * (float)m); }
