@@ -234,7 +234,9 @@ __device__ __forceinline__ void loader_walk(const __bf16* q, const __bf16* k, co
 
 // Compute wave w (value columns 32 w + sigma(0..31)) over the walk's chunks, with the state S in
 // its accumulators on entry and on return; lam is the head's log-decay (head mode).  One
-// lds_barrier per chunk (two in the output pass without gate), matching the loader waves.
+// lds_barrier per chunk (two in the output pass without gate), matching the loader waves.  Gate
+// mode: the wave also loads its rows of every chunk's v tile (from v into vtile, two tiles) and
+// stores the finished output tiles to o.
 template <int MODE, bool STATE_ONLY>
 __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf16* otile, __bf16* o, float lam,
                                              const Walk& wk, int w, int lane, const __bf16* v, __bf16* vtile) {
