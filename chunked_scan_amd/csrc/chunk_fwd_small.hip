@@ -88,7 +88,7 @@ __global__ __launch_bounds__(NT) void small_fwd_kernel(
     __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride, uint32_t* __restrict__ tile_live,
     const int* __restrict__ only_flagged) {
     // only_flagged (or null): redo just the units whose four flags are not all zero (the d = 128
-    // gate kernel's verdicts); the others keep what that kernel wrote
+    // gate kernel's flags); the others keep what that kernel wrote
     if (only_flagged) {
         const int* fl = only_flagged + (int64_t)blockIdx.x * 4;
         if ((fl[0] | fl[1] | fl[2] | fl[3]) == 0) return;
