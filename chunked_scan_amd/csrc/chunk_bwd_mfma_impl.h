@@ -1289,7 +1289,6 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
     // dq: forward state pass, scan, output pass (with the gate derivative also rowsum(S (.) D) per chunk)
     // (the states entering the sub-segments given by the caller: no state pass, no scan)
     auto dq_passes = [&]() -> hipError_t {
-        hipError_t e;
         const float* init = f_state;
         int64_t ist_bh = (int64_t)a.nseg * (G - 1) * D * D;
         int ist_g = G - 1, ist_off = -1;
@@ -1300,32 +1299,39 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
             ist_off = 0;
         } else if (s_scanned) {  // the scanned states of the d lambda_h pipeline, same layout as f_state
             init = s_scanned;
-        } else if (G > 1) {
-            LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
-                      bwd_dq_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                          k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr, 0,
-                          0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            if (MODE == DECAY_GATE) {
-                LA_TRACED(a.tr, "chunk_bwd_dq_state_pass_windows",
-                          bwd_dq_kernel<D, MODE, true, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                              k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay, nullptr,
-                              0, 0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
-                if ((e = hipGetLastError()) != hipSuccess) return e;
-            }
-            if ((e = launch_state_scan(f_state, f_decay, f_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
-                return e;
         }
-        LA_TRACED(a.tr, "chunk_bwd_dq",
-                  bwd_dq_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                      k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, init,
-                      ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
-        if ((e = hipGetLastError()) != hipSuccess || MODE != DECAY_GATE) return e;
-        LA_TRACED(a.tr, "chunk_bwd_dq_windows",
-                  bwd_dq_kernel<D, MODE, false, true><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                      k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, init,
-                      ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
-        return hipGetLastError();
+        if constexpr (D == 128 && MODE != DECAY_GATE) {  // on the forward's kernel (chunk_fwd_pipe.hip)
+            return launch_pipe_dq(a, G, cps, f_state, f_decay, init == f_state ? nullptr : init, ist_bh, ist_g,
+                                  ist_off);
+        } else {
+            hipError_t e;
+            if (init == f_state && G > 1) {
+                LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
+                          bwd_dq_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                              k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay,
+                              nullptr, 0, 0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                if (MODE == DECAY_GATE) {
+                    LA_TRACED(a.tr, "chunk_bwd_dq_state_pass_windows",
+                              bwd_dq_kernel<D, MODE, true, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                                  k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay,
+                                  nullptr, 0, 0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+                    if ((e = hipGetLastError()) != hipSuccess) return e;
+                }
+                e = launch_state_scan(f_state, f_decay, f_state, units, G - 1, D, D, a.stream, a.tr);
+                if (e != hipSuccess) return e;
+            }
+            LA_TRACED(a.tr, "chunk_bwd_dq",
+                      bwd_dq_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                          k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, init,
+                          ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+            if ((e = hipGetLastError()) != hipSuccess || MODE != DECAY_GATE) return e;
+            LA_TRACED(a.tr, "chunk_bwd_dq_windows",
+                      bwd_dq_kernel<D, MODE, false, true><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                          k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, init,
+                          ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+            return hipGetLastError();
+        }
     };
     // dk, dv: backward state pass, reverse-order scan, output pass (with the gate derivative also D at
     // every chunk's start)

@@ -505,16 +505,23 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
     }
 }
 
-template <int MODE, bool STATE_ONLY>
+// TRANS: every state in memory (s_in, the incoming states, the partial states, s_out) is the
+// transpose of the state the kernel walks with, as when the kernel computes dq of the backward
+// (queries d_o, keys v, values k: its state is the forward's state transposed).
+// The incoming state of sub-segment g >= 1 of (bh, seg) is at
+// init_state + bh * ist_bh + (seg * ist_g + g + ist_off) * D * D (the scan buffer, or states a
+// caller gives).
+template <int MODE, bool STATE_ONLY, bool TRANS = false>
 __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ decay, const float* __restrict__ s_in, __bf16* __restrict__ o,
     float* __restrict__ s_out, int64_t s_out_stride, float* __restrict__ part_state,
-    float* __restrict__ part_decay, const float* __restrict__ init_state, int64_t H, int64_t L, int nseg, int G,
+    float* __restrict__ part_decay, const float* __restrict__ init_state, int64_t ist_bh, int ist_g, int ist_off,
+    int64_t H, int64_t L, int nseg, int G,
     int cps, float inv_norm, __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride,
     uint8_t* __restrict__ tile_live, int* __restrict__ wide_out) {
     using LY = Layout<MODE, STATE_ONLY>;
-    constexpr bool GATE = LY::GATE, OTILE = LY::OTILE;
+    constexpr bool GATE = LY::GATE;
     __shared__ __attribute__((aligned(16))) __bf16 ring[LY::RING];
     // the chunk's outputs, rows unpadded with 16-byte slot s of row r at s ^ (r % 16)
     __shared__ __attribute__((aligned(16))) __bf16 otile[LY::OTILES ? LY::OTILES * TE : 8];
@@ -758,12 +765,15 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
         if (g == 0) {
             if (seg == 0 && s_in) src = s_in + bh * (int64_t)D * D;
         } else if (!STATE_ONLY) {
-            src = init_state + (ub * (G - 1) + (g - 1)) * (int64_t)D * D;
+            src = init_state + bh * ist_bh + ((int64_t)seg * ist_g + g + ist_off) * (int64_t)D * D;
         }
 #pragma unroll
         for (int m = 0; m < 4; m++)
 #pragma unroll
-            for (int i = 0; i < 16; i++) S[m][i] = src ? src[(32 * m + sigma(acc_row(i, kg))) * D + vcol_lane] : 0.f;
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + sigma(acc_row(i, kg));
+                S[m][i] = src ? src[TRANS ? vcol_lane * D + r : r * D + vcol_lane] : 0.f;
+            }
     }
 
     compute_walk<MODE, STATE_ONLY>(S, ring, otile, o, lam, wk, w, lane, v, vtile);
@@ -775,7 +785,10 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
 #pragma unroll
         for (int m = 0; m < 4; m++)
 #pragma unroll
-            for (int i = 0; i < 16; i++) dst[(32 * m + sigma(acc_row(i, kg))) * D + vcol_lane] = S[m][i];
+            for (int i = 0; i < 16; i++) {
+                const int r = 32 * m + sigma(acc_row(i, kg));
+                dst[TRANS ? vcol_lane * D + r : r * D + vcol_lane] = S[m][i];
+            }
     }
     if (STATE_ONLY && !GATE && threadIdx.x < D)
         part_decay[(ub * (G - 1) + g) * D + threadIdx.x] =
@@ -1015,8 +1028,8 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
     if (G > 1) {
         LA_TRACED(a.tr, "chunk_fwd_pipe_state_pass",
                   pipe_fwd_kernel<MODE, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
-                      q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, a.H,
-                      a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0, nullptr, wide ? wide + 4 * ub * G : nullptr));
+                      q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, part_state, part_decay, nullptr, 0, 0,
+                      0, a.H, a.L, a.nseg, G, cps, a.inv_norm, nullptr, nullptr, 0, nullptr, wide ? wide + 4 * ub * G : nullptr));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (MODE == DECAY_GATE &&
@@ -1027,8 +1040,8 @@ hipError_t launch_mode(const FwdArgs& a, int G, int cps, float* part_state, floa
     }
     LA_TRACED(a.tr, "chunk_fwd_pipe_output_pass",
               pipe_fwd_kernel<MODE, false><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
-                  q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, part_decay, part_state, a.H, a.L,
-                  a.nseg, G, cps, a.inv_norm, fused ? (__bf16*)a.q_dec : nullptr, fused ? a.total : nullptr,
+                  q, k, v, a.decay, a.s_in, o, a.s_out, a.s_out_stride, nullptr, part_decay, part_state,
+                  a.nseg * (int64_t)(G - 1) * D * D, G - 1, -1, a.H, a.L, a.nseg, G, cps, a.inv_norm, fused ? (__bf16*)a.q_dec : nullptr, fused ? a.total : nullptr,
                   a.total_stride, fused ? (uint8_t*)a.tile_live : nullptr, wide));
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && MODE == DECAY_GATE) e = launch_small_gate128_redo(a, G, cps, part_state, part_decay, false, wide);
@@ -1083,6 +1096,46 @@ hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_s
         case DECAY_GATE: return launch_mode<DECAY_GATE>(a, G, cps, part_state, part_decay, wide);
         default: return launch_mode<DECAY_NONE>(a, G, cps, part_state, part_decay, nullptr);
     }
+}
+
+namespace {
+
+template <int MODE>
+hipError_t launch_dq_mode(const BwdArgs& a, int G, int cps, float* part_state, float* part_decay,
+                          const float* init, int64_t ist_bh, int ist_g, int ist_off) {
+    const int64_t ub = a.B * a.H * a.nseg;
+    const __bf16* q = (const __bf16*)a.d_o;  // queries d_o, keys v, values k
+    const __bf16* k = (const __bf16*)a.v;
+    const __bf16* v = (const __bf16*)a.k;
+    if (!init && G > 1) {
+        LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
+                  pipe_fwd_kernel<MODE, true, true><<<(unsigned)(ub * (G - 1)), NT, 0, a.stream>>>(
+                      q, k, v, a.decay, a.s_in, nullptr, nullptr, 0, part_state, part_decay, nullptr, 0, 0, 0, a.H,
+                      a.L, a.nseg, G, cps, 0.f, nullptr, nullptr, 0, nullptr, nullptr));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = launch_state_scan(part_state, part_decay, part_state, ub, G - 1, D, D, a.stream, a.tr);
+        if (e != hipSuccess) return e;
+        init = part_state;
+        ist_bh = a.nseg * (int64_t)(G - 1) * D * D;
+        ist_g = G - 1;
+        ist_off = -1;
+    }
+    LA_TRACED(a.tr, "chunk_bwd_dq",
+              pipe_fwd_kernel<MODE, false, true><<<(unsigned)(ub * G), NT, 0, a.stream>>>(
+                  q, k, v, a.decay, a.s_in, (__bf16*)a.dq, nullptr, 0, nullptr, part_decay, init, ist_bh, ist_g,
+                  ist_off, a.H, a.L, a.nseg, G, cps, 0.f, nullptr, nullptr, 0, nullptr, nullptr));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pipe_dq(const BwdArgs& a, int G, int cps, float* part_state, float* part_decay,
+                          const float* init, int64_t ist_bh, int ist_g, int ist_off) {
+    if (a.dk != D || a.dv != D || a.mode == DECAY_GATE) return hipErrorInvalidValue;
+    return a.mode == DECAY_HEAD
+               ? launch_dq_mode<DECAY_HEAD>(a, G, cps, part_state, part_decay, init, ist_bh, ist_g, ist_off)
+               : launch_dq_mode<DECAY_NONE>(a, G, cps, part_state, part_decay, init, ist_bh, ist_g, ist_off);
 }
 
 }  // namespace la

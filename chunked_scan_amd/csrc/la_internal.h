@@ -160,6 +160,15 @@ extern int chain_spin_limit;
 // synchronises the current device, then reads (and optionally clears) its give-up counter
 hipError_t chain_status(unsigned int* give_ups, bool clear);
 hipError_t launch_chunk_fwd_pipe(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay, int* wide);
+// dq of the bf16 matrix-core backward at dk = dv = 128 with no or head decay, on the forward's
+// d = 128 kernel: dq_t = S_t d_o_t with S_t = a S_{t-1} + k_t v_t^T is this forward with queries
+// d_o, keys v and values k, whose state is S^T.  G sub-segments of cps chunks per (b, h, segment).
+// With init null (and G > 1): a state pass into part_state / part_decay (units * (G - 1) states
+// and decay vectors), their scan, then the output pass; else the output pass alone from the
+// states entering sub-segments g >= 1 at init + bh * ist_bh + (seg * ist_g + g + ist_off) * 128 * 128.
+// Every state in memory is in the forward's layout (key rows, value columns).
+hipError_t launch_pipe_dq(const BwdArgs& a, int G, int cps, float* part_state, float* part_decay,
+                          const float* init, int64_t ist_bh, int ist_g, int ist_off);
 // The same for dk = dv = 32 or 64 (chunk_fwd_small.hip).
 hipError_t launch_chunk_fwd_small(const FwdArgs& a, int G, int cps, float* part_state, float* part_decay);
 // The d = 128 gate output pass (or state pass) on the small-head kernel for the units whose four

@@ -129,6 +129,13 @@ def label(demangled: str):
     so = si is not None and si < len(args) and args[si] in ("true", "1")
     if si is not None and si < len(shown):
         shown[si] = "state pass" if so else "outputs"
+    if base == "pipe_fwd_kernel" and len(args) > 2:
+        # the forward kernel on transposed states computes dq of the backward
+        dq = args[2] in ("true", "1")
+        inst = base + "<" + ", ".join(shown[:2] + (["dq"] if dq else [])) + ">"
+        if dq:
+            return "chunk_bwd_dq" + ("_state_pass" if so else ""), inst
+        return name + ("_state_pass" if so else "_output_pass"), inst
     if si is not None:
         if name.startswith("chunk_bwd"):
             name += "_state_pass" if so else ""
