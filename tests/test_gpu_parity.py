@@ -387,6 +387,43 @@ def test_state_correct_head_live_ranges(H):
     assert torch.equal(o[:, :, :Ls], o0[:, :, :Ls])
 
 
+@pytest.mark.parametrize("pattern", ["none_live", "one_live", "last_segment", "sparse", "segment_starts"])
+def test_state_correct_live_any_pattern(pattern):
+    """la_state_correct_live skips the tiles flagged dead inside each workgroup's range of tiles;
+    any pattern of live tiles -- none, a single one, all in the last segment, scattered, or
+    clustered at each segment's start as a decay leaves them -- gives O bit-identical to
+    la_state_correct over q whose rows are zero on the dead tiles."""
+    B, H, nseg, seg_begin, Ls, d = 2, 8, 3, 1, 4096 + 40, 128
+    L, tps = nseg * Ls, (Ls + 63) // 64
+    note(f"la_state_correct_live pattern={pattern} B={B} H={H} nseg={nseg} Ls={Ls}")
+    rng = np.random.default_rng(77)
+    live = np.zeros((B, H, nseg, tps), np.int32)
+    if pattern == "one_live":
+        live[1, 5, 2, 17] = 1
+    elif pattern == "last_segment":
+        live[:, :, nseg - 1, :] = 1
+    elif pattern == "sparse":
+        live[:, :, seg_begin:, :] = rng.random((B, H, nseg - seg_begin, tps)) < 0.07
+    elif pattern == "segment_starts":
+        for b in range(B):
+            for h in range(H):
+                live[b, h, :, :rng.integers(0, tps + 1)] = 1
+    g = torch.Generator().manual_seed(78)
+    q = (torch.randn((B, H, L, d), generator=g) * 0.1).to(torch.bfloat16)
+    rows = np.repeat(live, 64, axis=-1)[..., :Ls].reshape(B, H, L)
+    q[torch.from_numpy(rows == 0)] = 0
+    o = (torch.randn((B, H, L, d), generator=g) * 0.1).to(torch.bfloat16).cuda()
+    s_recv = (torch.randn((B, H, nseg - seg_begin, d, d), generator=g) * 0.05).cuda()
+    qd, flags = q.cuda(), torch.from_numpy(live).cuda()
+    o1, o2 = o.clone(), o.clone()
+    lb.la_state_correct(qd, None, s_recv, o1, mode="none", nseg=nseg, seg_begin=seg_begin)
+    lb.la_state_correct(qd, None, s_recv, o2, mode="none", nseg=nseg, seg_begin=seg_begin, tile_live=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    if pattern != "none_live" and live[:, :, seg_begin:].any():
+        assert not torch.equal(o2, o)
+
+
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("nseg,seg_begin", [(1, 0), (2, 1)])
 def test_state_correct_live_skips_dead_tiles(nseg, seg_begin, d):
