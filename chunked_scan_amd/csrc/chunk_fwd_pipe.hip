@@ -62,6 +62,8 @@
 // * Head decay: scores get exp(lambda (i-j)), the inter-chunk part of output column i gets the
 //   per-lane scalar exp(lambda (i+1)), and K^T V becomes K^T diag(w) V with the key-to-chunk-end
 //   weights w_j = exp(lambda (n-1-j)) on the V operand.  Every factor is <= 1.
+#include <type_traits>
+
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -155,23 +157,28 @@ __device__ __forceinline__ void dma_tile(const __bf16* src, __bf16* tile, int64_
 // Gate mode: the stages hold the prepared k (and q) and the chunk's decay after the tiles, two
 // stages (the loaders prepare one chunk ahead); the v tiles are a separate pair of LDS arrays (the
 // compute waves load them by DMA, and accesses to other arrays need not wait for that DMA).
-template <int MODE, bool STATE_ONLY>
+// VSEP (head-decay output pass): the v tiles in an array of their own, one per stage (vring), so
+// that loader waves writing them through registers need not wait for the DMA of q and k.
+template <int MODE, bool STATE_ONLY, bool VSEP = false>
 struct Layout {
     static constexpr bool GATE = MODE == DECAY_GATE;
+    static_assert(!(VSEP && (GATE || STATE_ONLY)), "separate v tiles: output pass without gate only");
     static constexpr bool OTILE = !STATE_ONLY && !GATE;  // outputs leave through an LDS tile stored by the loaders
     // gate output pass: the same, with two output tiles (the loaders store chunk c - 1's while the
     // compute waves fill chunk c's)
     static constexpr bool GTILE = !STATE_ONLY && GATE;
-    static constexpr int SLOT = (STATE_ONLY ? 2 : 3) - (GATE ? 1 : 0);
+    static constexpr int SLOT = (STATE_ONLY ? 2 : 3) - (GATE ? 1 : 0) - (VSEP ? 1 : 0);
     static constexpr int STAGE = SLOT * TE + (GATE ? 2 * D : 0);  // gate: D floats of chunk decay after the tiles
     // gate: the loaders prepare chunk c + 1 while chunk c is computed, in the stage chunk c - 1 left
-    static constexpr int NST = GATE ? 2 : (LDS_TILES - (OTILE ? 1 : 0)) / SLOT;
+    static constexpr int NST = GATE ? 2 : VSEP ? (LDS_TILES - 1) / (SLOT + 1) : (LDS_TILES - (OTILE ? 1 : 0)) / SLOT;
     static constexpr int RING = NST * STAGE;
+    static constexpr int VRING = VSEP ? NST * TE : 0;
     static constexpr int OTILES = OTILE ? 1 : GTILE ? 2 : 0;
-    __device__ static __forceinline__ Ring stage(__bf16* ring, int c) {
+    __device__ static __forceinline__ Ring stage(__bf16* ring, int c, __bf16* vring = nullptr) {
         __bf16* b = ring + (c % NST) * STAGE;
         // q is unused in the state pass; gate: v is not in the ring
         if (GATE) return Ring{b, b + (SLOT - 1) * TE, nullptr, (float*)(b + SLOT * TE)};
+        if (VSEP) return Ring{b, b + TE, vring + (c % NST) * TE, nullptr};
         return Ring{b, b + (SLOT - 2) * TE, b + (SLOT - 1) * TE, (float*)(b + SLOT * TE)};
     }
 };
@@ -204,15 +211,16 @@ __device__ __forceinline__ void store_otile(__bf16* o, const __bf16* otile, int6
 // Loader wave lw of the no-decay and head-decay modes: chunk c + NST - 1 is requested as soon as
 // every wave is done with chunk c - 1; in the output pass it also stores each chunk's output tile.
 // One s_barrier per chunk (two in the output pass), matching compute_walk.
-template <int MODE, bool STATE_ONLY>
+template <int MODE, bool STATE_ONLY, bool VSEP = false>
 __device__ __forceinline__ void loader_walk(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o,
-                                            __bf16* ring, const __bf16* otile, const Walk& wk, int lw, int lane) {
-    using LY = Layout<MODE, STATE_ONLY>;
+                                            __bf16* ring, const __bf16* otile, const Walk& wk, int lw, int lane,
+                                            __bf16* vring = nullptr) {
+    using LY = Layout<MODE, STATE_ONLY, VSEP>;
     using DM = Dma<STATE_ONLY>;
     const int nch = wk.nch;
     int issued = 0;
     for (; issued < LY::NST - 1 && issued < nch; issued++)
-        DM::issue(q, k, v, LY::stage(ring, issued), wk.row_base + wk.t_begin + (int64_t)issued * C,
+        DM::issue(q, k, v, LY::stage(ring, issued, vring), wk.row_base + wk.t_begin + (int64_t)issued * C,
                   wk.chunk_len(issued), lw, lane);
     for (int c = 0; c < nch; c++) {
         // this wave's part of chunk c has landed.  Only the younger DMA batches are allowed to be
@@ -221,7 +229,7 @@ __device__ __forceinline__ void loader_walk(const __bf16* q, const __bf16* k, co
         wait_batches<DM::NDMA>(issued - c - 1);
         __builtin_amdgcn_s_barrier();  // chunk c is handed to the compute waves
         if (issued < nch) {
-            DM::issue(q, k, v, LY::stage(ring, issued), wk.row_base + wk.t_begin + (int64_t)issued * C,
+            DM::issue(q, k, v, LY::stage(ring, issued, vring), wk.row_base + wk.t_begin + (int64_t)issued * C,
                       wk.chunk_len(issued), lw, lane);
             issued++;
         }
@@ -232,15 +240,135 @@ __device__ __forceinline__ void loader_walk(const __bf16* q, const __bf16* k, co
     }
 }
 
+// Loader wave lw of the head-decay output pass with the factorised walk: q and k by LDS DMA as in
+// loader_walk, its 16 rows of v through registers (two chunks in flight, the loop unrolled by two so
+// that the register sets alternate), each row scaled by exp(lambda (n - 1 - R)) (zero past the
+// chunk's end) on its way into the chunk's v tile -- vhat of the factorised walk, prepared by waves
+// that would otherwise only wait.  The v tiles are an LDS array apart from the DMA's destinations,
+// so these stores need not wait for the DMA in flight.  Per chunk the same 12 vector memory
+// operations as loader_walk (8 DMA, 4 loads), so its batch waits hold as they are.
+template <int MODE>
+__device__ __forceinline__ void loader_walk_vhat(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o,
+                                                 __bf16* ring, const __bf16* otile, __bf16* vring, const Walk& wk,
+                                                 int lw, int lane, float lam) {
+    using LY = Layout<MODE, false, true>;
+    static_assert(LY::NST == 3, "two chunks in flight");
+    constexpr int NOPS = 12;
+    const float lam2 = lam * LOG2E;
+    const int nch = wk.nch;
+    u32x4 va[4], vb[4];
+    auto issue = [&](int c, u32x4 (&x)[4]) {
+        const Ring r = LY::stage(ring, c, vring);
+        const int64_t base = (wk.row_base + wk.t_begin + (int64_t)c * C) * D;
+        const int n = wk.chunk_len(c);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int R = (4 * lw + j) * 4 + (lane >> 4);
+            const int off = min(R, n - 1) * D + (((lane & 15) ^ swz(R)) << 3);
+            const int dst = (4 * lw + j) * 512;
+            __builtin_amdgcn_global_load_lds((const void*)(q + base + off), (lds_void*)(r.q + dst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(k + base + off), (lds_void*)(r.k + dst), 16, 0, 2);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int R = (4 * lw + j) * 4 + (lane >> 4);
+            const int off = min(R, n - 1) * D + (((lane & 15) ^ swz(R)) << 3);
+            x[j] = __builtin_nontemporal_load((const u32x4*)(v + base + off));
+        }
+    };
+    // chunk c: its v rows scaled into its tile, handed over, chunk c + 2 requested into the same
+    // registers (STEADY: it exists, and so does one younger chunk in flight now), its output stored
+    auto step = [&](int c, int& issued, u32x4 (&x)[4], auto steady) {
+        // this wave's part of chunk c has landed; waits of fixed counts only, so that the
+        // compiler's own accounting of the register loads agrees (at most one younger chunk)
+        if (decltype(steady)::value || issued > c + 1) waitcnt<NOPS, 15>();
+        else waitcnt<0, 15>();
+        {
+            __bf16* vt = LY::stage(ring, c, vring).v;
+            const int n = wk.chunk_len(c);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int R = (4 * lw + j) * 4 + (lane >> 4);
+                const float f = R < n ? decay_pow2(lam2, n - 1 - R) : 0.f;
+                float fs[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++) fs[e] = f;
+                *(u32x4*)(vt + (4 * lw + j) * 512 + lane * 8) = scale8(x[j], fs);
+            }
+        }
+        lds_barrier_keep_dma();  // chunk c (its v tile complete) is handed to the compute waves
+        if (decltype(steady)::value || issued < nch) {
+            issue(issued, x);
+            issued++;
+        }
+        lds_barrier_keep_dma();  // the compute waves have written chunk c's outputs
+        store_otile(o, otile, wk.row_base + wk.t_begin + (int64_t)c * C, wk.chunk_len(c), threadIdx.x - 256);
+    };
+    int issued = 0, c = 0;
+    if (nch >= 4) {  // two chunks requested on every path into the loop
+        issue(0, va);
+        issue(1, vb);
+        issued = 2;
+        for (; c + 3 < nch; c += 2) {  // both steps request a chunk
+            step(c, issued, va, std::true_type{});
+            step(c + 1, issued, vb, std::true_type{});
+        }
+    } else {
+        if (nch > 0) issue(issued++, va);
+        if (nch > 1) issue(issued++, vb);
+    }
+    if (c < nch) step(c, issued, va, std::false_type{});
+    if (c + 1 < nch) step(c + 1, issued, vb, std::false_type{});
+    if (c + 2 < nch) step(c + 2, issued, va, std::false_type{});
+}
+
+// Head decay: the V operand of the state update, token t = 16 ks + kg*8 + jj of the lane's slabs,
+// scaled by exp(lambda (n - 1 - t)), or zero past the chunk's end (lam2 = lambda log2(e), e1 =
+// exp(lambda)); the exponent grows by one from jj = 7 down to jj = 0.
+__device__ __forceinline__ void scale_state_v(bf16x8 (&vb)[4], float lam2, float e1, int n, int kg) {
+    if (n == C) {  // every chunk but a ragged last one: no token past the end
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+            float gch = decay_pow2(lam2, C - 1 - (16 * ks + kg * 8 + 7));
+            float f[8];
+#pragma unroll
+            for (int jj = 7; jj >= 0; jj--) {
+                f[jj] = gch;
+                gch *= e1;
+            }
+            vb[ks] = __builtin_bit_cast(bf16x8, scale8(__builtin_bit_cast(u32x4, vb[ks]), f));
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+            const int e7 = n - 1 - (16 * ks + kg * 8 + 7);
+            float gch = decay_pow2(lam2, max(e7, 0));
+#pragma unroll
+            for (int jj = 7; jj >= 0; jj--) {
+                const int e = e7 + 7 - jj;
+                if (jj < 7) gch = (e > 0) ? gch * e1 : 1.f;
+                vb[ks][jj] = (e >= 0) ? (__bf16)((float)vb[ks][jj] * gch) : (__bf16)0.f;
+            }
+        }
+    }
+}
+
 // Compute wave w (value columns 32 w + sigma(0..31)) over the walk's chunks, with the state S in
 // its accumulators on entry and on return; lam is the head's log-decay (head mode).  One
 // lds_barrier per chunk (two in the output pass without gate), matching the loader waves.  Gate
 // mode: the wave also loads its rows of every chunk's v tile (from v into vtile, two tiles) and
 // stores the finished output tiles to o.
-template <int MODE, bool STATE_ONLY>
+// FACT (head-decay output pass, for a decay with a^-(C-1) finite): the chunk's v rows, scaled once
+// by the state update's weights, vhat_j = v_j a^(n-1-j) (the loader waves do it, loader_walk_vhat),
+// serve the intra-chunk product as well: with the state decayed first (S' = a^n S),
+//   o_i = a^(i+1) S^T q_i + sum_{j<=i} a^(i-j) p_ij v_j = a^(i-n+1) (S'^T q_i + sum_{j<=i} p_ij vhat_j),
+// so the scores need no per-pair factor, only the causal mask, and each output row one scale.
+template <int MODE, bool STATE_ONLY, bool FACT = false, bool VSEP = false>
 __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf16* otile, __bf16* o, float lam,
-                                             const Walk& wk, int w, int lane, const __bf16* v, __bf16* vtile) {
-    using LY = Layout<MODE, STATE_ONLY>;
+                                             const Walk& wk, int w, int lane, const __bf16* v, __bf16* vtile,
+                                             __bf16* vring = nullptr) {
+    static_assert(!FACT || VSEP, "the factorised walk reads the loaders' vhat tiles");
+    using LY = Layout<MODE, STATE_ONLY, VSEP>;
     constexpr bool GATE = LY::GATE, OTILE = LY::OTILE;
     const int n32 = lane & 31, kg = lane >> 5;
     const int G16 = lane >> 4, i16 = lane & 15;
@@ -270,7 +398,7 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
     if (GATE && wk.nch > 0) dma_tile<VCPOL>(v, vtile, wk.row_base + wk.t_begin, wk.chunk_len(0), w, lane);
 
     for (int c = 0; c < wk.nch; c++) {
-        const Ring cur = LY::stage(ring, c);
+        const Ring cur = LY::stage(ring, c, vring);
         const int n = wk.chunk_len(c);
         // Head decay: the factors exp(lambda d) are recomputed every chunk from a few base-2
         // exponentials and chains of multiplications by exp(lambda) (every factor <= 1).  Hiding
@@ -303,6 +431,13 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
         if (GATE && c + 1 < wk.nch)
             dma_tile<VCPOL>(v, vtile + ((c + 1) & 1) * TE, wk.row_base + wk.t_begin + (int64_t)(c + 1) * C,
                             wk.chunk_len(c + 1), w, lane);
+        if constexpr (FACT) {  // vb is vhat already (the loader waves scaled it); S' = a^n S
+            const float fh = decay_pow2(lamc, n);
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) S[m][i] *= fh;
+        }
 
         if (!STATE_ONLY) {
             // the state as A operands of S^T Qbar^T: slab (m, hh) holds key dims 32m + 16hh + kg*8 + jj
@@ -353,7 +488,7 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
                         // underflow) the chain runs downward and restarts at 1 where the distance
                         // reaches 0.
                         float fac[8];
-                        if (MODE == DECAY_HEAD) {
+                        if (MODE == DECAY_HEAD && !FACT) {
                             const int d0 = 32 * (ib - jb) + n32 - 16 * hh - 8 * kg;
                             if (jb < ib) {
                                 float gch = decay_pow2(lamb, d0 - 7);
@@ -385,7 +520,7 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
                         for (int jj = 0; jj < 8; jj++) {
                             const int jtok = jb * 32 + 16 * hh + kg * 8 + jj;
                             float val = sc[8 * hh + jj];
-                            if (MODE == DECAY_HEAD) val *= fac[jj];
+                            if (MODE == DECAY_HEAD && !FACT) val *= fac[jj];
                             if (jb == ib && jtok > itok) val = 0.f;
                             x[jj] = (__bf16)val;
                         }
@@ -398,13 +533,18 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
                 for (int m = 0; m < 4; m++)
 #pragma unroll
                     for (int hh = 0; hh < 2; hh++) acc = mfma(sa[m][hh], qb[2 * m + hh], acc);
-                if (MODE == DECAY_HEAD) {
+                if (MODE == DECAY_HEAD && !FACT) {
                     const float f = decay_pow2(lamb, itok + 1);
 #pragma unroll
                     for (int i = 0; i < 16; i++) acc[i] *= f;
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < 2 * (ib + 1); s2++) acc = mfma(vb[s2], pt[s2], acc);
+                if constexpr (FACT) {  // both terms: a^(i-n+1) (S'^T q_i + sum p_ij vhat_j)
+                    const float f = decay_pow2(lamb, itok - n + 1);
+#pragma unroll
+                    for (int i = 0; i < 16; i++) acc[i] *= f;
+                }
                 // accumulators 0..7 are value columns 32w + 8kg + 0..7 (slot 4w + kg), 8..15 are
                 // 32w + 16 + 8kg + 0..7 (slot 4w + 2 + kg)
                 {
@@ -423,41 +563,15 @@ __device__ __forceinline__ void compute_walk(f32x16 (&S)[4], __bf16* ring, __bf1
 
         if (OTILE) lds_barrier();  // the output tile is complete; the loader waves store it
 
-        // state: S <- decay(chunk) S + K^T diag(w) V over the chunk's n tokens
-        if (MODE == DECAY_HEAD) {
+        // state: S <- decay(chunk) S + K^T diag(w) V over the chunk's n tokens (FACT: done above)
+        if (MODE == DECAY_HEAD && !FACT) {
             const float fh = decay_pow2(lamc, n);
 #pragma unroll
             for (int m = 0; m < 4; m++)
 #pragma unroll
                 for (int i = 0; i < 16; i++) S[m][i] *= fh;
-            // token t = 16 ks + kg*8 + jj gets exp(lambda (n - 1 - t)), or 0 past the chunk's end;
-            // the exponent grows by one from jj = 7 down to jj = 0
-            if (n == C) {  // every chunk but a ragged last one: no token past the end
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) {
-                    float gch = decay_pow2(lamc, C - 1 - (16 * ks + kg * 8 + 7));
-                    float f[8];
-#pragma unroll
-                    for (int jj = 7; jj >= 0; jj--) {
-                        f[jj] = gch;
-                        gch *= e1;
-                    }
-                    vb[ks] = __builtin_bit_cast(bf16x8, scale8(__builtin_bit_cast(u32x4, vb[ks]), f));
-                }
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) {
-                    const int e7 = n - 1 - (16 * ks + kg * 8 + 7);
-                    float gch = decay_pow2(lamc, max(e7, 0));
-#pragma unroll
-                    for (int jj = 7; jj >= 0; jj--) {
-                        const int e = e7 + 7 - jj;
-                        if (jj < 7) gch = (e > 0) ? gch * e1 : 1.f;
-                        vb[ks][jj] = (e >= 0) ? (__bf16)((float)vb[ks][jj] * gch) : (__bf16)0.f;
-                    }
-                }
-            }
-        } else if (n < C) {
+            scale_state_v(vb, lamc, e1, n, kg);
+        } else if (MODE != DECAY_HEAD && n < C) {
 #pragma unroll
             for (int ks = 0; ks < 4; ks++)
 #pragma unroll
@@ -520,9 +634,12 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
     int64_t H, int64_t L, int nseg, int G,
     int cps, float inv_norm, __bf16* __restrict__ q_dec, float* __restrict__ total, int64_t total_stride,
     uint8_t* __restrict__ tile_live, int* __restrict__ wide_out) {
-    using LY = Layout<MODE, STATE_ONLY>;
+    // head decay's output pass keeps its v tiles apart (the factorised walk's loaders write them)
+    constexpr bool VSEP = MODE == DECAY_HEAD && !STATE_ONLY;
+    using LY = Layout<MODE, STATE_ONLY, VSEP>;
     constexpr bool GATE = LY::GATE;
     __shared__ __attribute__((aligned(16))) __bf16 ring[LY::RING];
+    __shared__ __attribute__((aligned(16))) __bf16 vring[VSEP ? LY::VRING : 8];
     // the chunk's outputs, rows unpadded with 16-byte slot s of row r at s ^ (r % 16)
     __shared__ __attribute__((aligned(16))) __bf16 otile[LY::OTILES ? LY::OTILES * TE : 8];
     __shared__ int first_dead[4];  // gate loader wave lw: its first chunk with zero cumulative decay
@@ -748,48 +865,70 @@ __global__ __launch_bounds__(NT, 1) void pipe_fwd_kernel(
         if (lane == 0) wide_out[u * 4 + lw] = wide;
         return;
     }
+    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
+    // head decay's output pass takes the factorised walk when a^-(C-1) is finite and a^(C-1) a
+    // normal float (a bound of 2^-100 leaves room for the inputs' magnitudes); stronger decays
+    // (a = 0 included) keep the per-pair factors
+    const bool fact = VSEP && lam * LOG2E * (float)(C - 1) >= -100.f;
     if (wave >= 4) {
-        loader_walk<MODE, STATE_ONLY>(q, k, v, o, ring, otile, wk, wave - 4, lane);
+        if constexpr (VSEP) {
+            if (fact) {
+                loader_walk_vhat<MODE>(q, k, v, o, ring, otile, vring, wk, wave - 4, lane, lam);
+                return;
+            }
+        }
+        loader_walk<MODE, STATE_ONLY, VSEP>(q, k, v, o, ring, otile, wk, wave - 4, lane, vring);
         return;
     }
 
     // ---- compute wave w: value columns 32 w + sigma(0..31)
     const int w = wave, n32 = lane & 31, kg = lane >> 5;
-    const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
     const int vcol_lane = 32 * w + sigma(n32);
 
-    // state tile m: accumulator element i <-> key row 32m + sigma(acc_row(i)), value column vcol_lane
-    f32x16 S[4];
-    {
-        const float* src = nullptr;
-        if (g == 0) {
-            if (seg == 0 && s_in) src = s_in + bh * (int64_t)D * D;
-        } else if (!STATE_ONLY) {
-            src = init_state + bh * ist_bh + ((int64_t)seg * ist_g + g + ist_off) * (int64_t)D * D;
+    // the state in, the walk, the state out, factorised or not; the branch spans the whole section
+    // so that each path gets its own register allocation
+    auto section = [&](auto fact) {
+        constexpr bool FACT = decltype(fact)::value;
+        // state tile m: accumulator element i <-> key row 32m + sigma(acc_row(i)), value column vcol_lane
+        f32x16 S[4];
+        {
+            const float* src = nullptr;
+            if (g == 0) {
+                if (seg == 0 && s_in) src = s_in + bh * (int64_t)D * D;
+            } else if (!STATE_ONLY) {
+                src = init_state + bh * ist_bh + ((int64_t)seg * ist_g + g + ist_off) * (int64_t)D * D;
+            }
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int r = 32 * m + sigma(acc_row(i, kg));
+                    S[m][i] = src ? src[TRANS ? vcol_lane * D + r : r * D + vcol_lane] : 0.f;
+                }
         }
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 32 * m + sigma(acc_row(i, kg));
-                S[m][i] = src ? src[TRANS ? vcol_lane * D + r : r * D + vcol_lane] : 0.f;
-            }
-    }
 
-    compute_walk<MODE, STATE_ONLY>(S, ring, otile, o, lam, wk, w, lane, v, vtile);
+        compute_walk<MODE, STATE_ONLY, FACT, VSEP>(S, ring, otile, o, lam, wk, w, lane, v, vtile, vring);
 
-    float* dst = nullptr;
-    if (STATE_ONLY) dst = part_state + (ub * (G - 1) + g) * (int64_t)D * D;
-    else if (g == G - 1 && s_out) dst = s_out + bh * s_out_stride + (int64_t)seg * D * D;
-    if (dst) {
+        float* dst = nullptr;
+        if (STATE_ONLY) dst = part_state + (ub * (G - 1) + g) * (int64_t)D * D;
+        else if (g == G - 1 && s_out) dst = s_out + bh * s_out_stride + (int64_t)seg * D * D;
+        if (dst) {
 #pragma unroll
-        for (int m = 0; m < 4; m++)
+            for (int m = 0; m < 4; m++)
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int r = 32 * m + sigma(acc_row(i, kg));
-                dst[TRANS ? vcol_lane * D + r : r * D + vcol_lane] = S[m][i];
-            }
+                for (int i = 0; i < 16; i++) {
+                    const int r = 32 * m + sigma(acc_row(i, kg));
+                    dst[TRANS ? vcol_lane * D + r : r * D + vcol_lane] = S[m][i];
+                }
+        }
+    };
+    if constexpr (VSEP) {
+        if (fact) {
+            section(std::true_type{});
+            return;  // (part_decay below is the state pass's)
+        }
     }
+    section(std::false_type{});
     if (STATE_ONLY && !GATE && threadIdx.x < D)
         part_decay[(ub * (G - 1) + g) * D + threadIdx.x] =
             (MODE == DECAY_HEAD) ? decay_pow(lam, (int)(t_end - t_begin)) : 1.f;

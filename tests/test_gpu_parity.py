@@ -552,6 +552,28 @@ def test_edge_cases():
         assert rel_err(s, s_ref) <= TOL["bf16"], lam
 
 
+@pytest.mark.parametrize("subseg", [0, 2])
+def test_head_decay_both_walks(subseg):
+    """d = 128 head decay: the output pass takes its factorised walk (the intra-chunk product on v
+    scaled by the state update's weights, one scale per output row) while lambda (C - 1) log2(e)
+    >= -100, and keeps per-pair factors for stronger decays; heads on both sides of that bound
+    (lambda = -1.0 and -1.2 straddle it), with lambda = 0, -inf and the workload's weakest decay,
+    in one launch, against the oracle (ragged length, several sub-segments, s_in)."""
+    lams = np.array([-1e-4, -0.02, -0.5, -1.0, -1.2, -3.0, 0.0, -np.inf], np.float32)
+    w = W2.scaled(B=1, H=len(lams), L=64 * 9 + 19, s_in_std=0.05, seed=777 + subseg)
+    note(f"head decay both walks, d=128 subseg_chunks={subseg} lambdas={lams.tolist()}")
+    inp = make_inputs(w, "cpu")
+    inp["decay"] = torch.from_numpy(lams)
+    d = to_dev(inp)
+    o, s = lb.la_chunk_fwd(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode="head", subseg_chunks=subseg)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence(host32(inp["q"]), host32(inp["k"]), host32(inp["v"]), oracle.HEAD, lams,
+                                     host32(inp["s_in"]).astype(np.float64))
+    for h in range(len(lams)):
+        assert rel_err(o[:, h:h + 1], o_ref[:, h:h + 1]) <= TOL["bf16"], lams[h]
+        assert rel_err(s[:, h:h + 1], s_ref[:, h:h + 1]) <= TOL["bf16"], lams[h]
+
+
 @pytest.mark.parametrize("mode", ["none", "head", "gate"])
 @pytest.mark.parametrize("d", [32, 64])
 @pytest.mark.parametrize("L,nseg,subseg", [(128 * 9 + 17, 1, 0), (128 * 6, 1, 1), (128 * 7 + 40, 1, 3), (300, 1, 0),
