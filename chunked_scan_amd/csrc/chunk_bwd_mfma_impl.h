@@ -187,7 +187,14 @@ struct BwdSmem {
 // WIN (gate mode): the instance that cuts chunks into windows; it redoes only the units (workgroups)
 // whose wide[] flag the plain instance set when it met a chunk too wide for one piece, and the plain
 // instance stops such a unit there (the redo overwrites everything the unit writes).
-template <int D, int MODE, bool STATE_ONLY, bool WIN = false>
+// FACT (head decay, output pass, no d lambda_h): the factorised walk, for the heads whose a^-C is
+// finite (lambda C log2(e) >= -100); the instance without it takes the other heads (and all of them
+// when d lambda_h is wanted), every workgroup leaving at once when its head is the other instance's.
+// With q~_i = q_i a^{i+1} (already staged for the D update) and D first decayed, D' = a^n D:
+//   dk_j = a^{-(j+1)} (D' v_j + sum_{i>=j} p'_ij q~_i),  dv_j = a^{-(j+1)} (D'^T k_j + sum_{i>=j} (q~_i . k_j) d_o_i),
+//   D <- D' + q~^T d_o,
+// so the scores take only the causal mask, and q itself need not be staged.
+template <int D, int MODE, bool STATE_ONLY, bool WIN = false, bool FACT = false>
 __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ ds_out,
@@ -228,6 +235,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     const int64_t row_base = bh * L;
     const float lam = (MODE == DECAY_HEAD) ? decay[h] : 0.f;
     const int64_t nch_seg = (Lseg + C - 1) / C;
+    static_assert(!FACT || (MODE == DECAY_HEAD && !STATE_ONLY && !WIN), "the factorised walk: head output pass");
+    if constexpr (MODE == DECAY_HEAD && !STATE_ONLY) {
+        if ((!intra_part && lam * LOG2E * (float)C >= -100.f) != FACT) return;  // the other instance's head
+    }
 
     // ---- D at the sub-segment's end: key rows 32 m + (i / 4) 8 + kg 4 + i % 4, value column 32 w + n32
     f32x16 Dm[NCB];
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 *(u32x4*)(&sm.o[tr * PITCH + c8]) = in ? xo : z;
                 if (!STATE_ONLY) {
                     if (MODE != DECAY_GATE) {
-                        *(u32x4*)(&sm.q[row * PITCH + c8]) = xq;
+                        if (!FACT) *(u32x4*)(&sm.q[row * PITCH + c8]) = xq;
                         *(u32x4*)(&sm.k[row * PITCH + c8]) = xk;
                     }
                     *(u32x4*)(&sm.v[tr * PITCH + c8]) = in ? xv : z;
@@ -363,6 +374,13 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 xv = rv[r];
             }
         });
+        if constexpr (FACT) {  // D' = a^n D: the chunk's outputs and the update start from it
+            const float fh = sm.apow[n];
+#pragma unroll
+            for (int m = 0; m < NCB; m++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) Dm[m][i] *= fh;
+        }
         if (!STATE_ONLY && rank == 0) {  // D^T as bf16: this lane's value column, key rows in runs of four
 #pragma unroll
             for (int m = 0; m < NCB; m++)
@@ -410,7 +428,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                     const int ka = ks * 16 + kg * 8;
                     po = mfma(*(const bf16x8*)(&sm.o[(ib * 32 + n32) * PITCH + ka]),
                               *(const bf16x8*)(&sm.v[(jb * 32 + n32) * PITCH + ka]), po);
-                    pq = mfma(*(const bf16x8*)(&(MODE == DECAY_GATE ? sm.qs : sm.q)[(ib * 32 + n32) * PITCH + ka]),
+                    pq = mfma(*(const bf16x8*)(&(MODE == DECAY_GATE || FACT ? sm.qs : sm.q)[(ib * 32 + n32) * PITCH + ka]),
                               *(const bf16x8*)(&sm.k[(jb * 32 + n32) * PITCH + ka]), pq);
                 }
                 // a lane holds column j = jb 32 + n32 and rows i in four runs of four: one 8-byte
@@ -424,7 +442,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                         const int row = ib * 32 + g4 * 8 + kg * 4 + e;  // i index
                         const int col = jb * 32 + n32;                   // j index
                         float wgt = (col > row) ? 0.f : 1.f;
-                        if (MODE == DECAY_HEAD) {
+                        if (MODE == DECAY_HEAD && !FACT) {
                             wgt *= sm.apow[max(row - col, 0)];
                             if (intra_part && col < row) hacc += (double)((float)(row - col) * wgt) * ((double)po[i] * (double)pq[i]);
                         }
@@ -441,7 +459,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
             // ---- dk, column block w (key dims 32 w ..), and dv, column block w (value columns 32 w ..)
             bf16x8 qb[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ks++) qb[ks] = tr_operand(MODE == DECAY_GATE ? sm.qs : sm.q, PITCH, ks, 32 * cb, lane);
+            for (int ks = 0; ks < 4; ks++) qb[ks] = tr_operand(MODE == DECAY_GATE || FACT ? sm.qs : sm.q, PITCH, ks, 32 * cb, lane);
             // D's own columns as B operands (key-row order permuted as the A reads below)
             bf16x8 db[2 * NCB];
 #pragma unroll
@@ -466,6 +484,8 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 if (!Gm::owns_rows(jb, rank)) continue;
                 const int jt = jb * 32 + n32;  // this lane's token
                 const float wj = (MODE == DECAY_HEAD) ? sm.apow[max(n - 1 - jt, 0)] : 1.f;
+                // FACT: a^-(j+1), at most 2^100 by the bound on lambda
+                const float ainv = FACT ? __builtin_amdgcn_exp2f(-lam * LOG2E * (float)(jt + 1)) : 1.f;
                 // dk^T: a^{n-1-j} (D V^T) + Q^T (P' w)
                 f32x16 acc = {};
 #pragma unroll
@@ -474,7 +494,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                     const bf16x8 b = *(const bf16x8*)(&sm.v[jt * PITCH + ks * 16 + kg * 8]);
                     acc = mfma(a, b, acc);
                 }
-                if (MODE == DECAY_HEAD) {
+                if (MODE == DECAY_HEAD && !FACT) {
 #pragma unroll
                     for (int i = 0; i < 16; i++) acc[i] *= wj;
                 }
@@ -490,6 +510,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 if (MODE == DECAY_GATE) {  // dk_j = 2^{-B_j} (2^{B_last} D V^T + Q-bar^T P')_j, per key dim
 #pragma unroll
                     for (int i = 0; i < 16; i++) acc[i] *= sm.gb[jt * D + 32 * cb + (i >> 2) * 8 + kg * 4 + (i & 3)];
+                }
+                if constexpr (FACT) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) acc[i] *= ainv;
                 }
                 if (jt < n) {
                     __bf16* drow = dk_out + (row_base + t0 + jt) * D + 32 * cb + kg * 4;
@@ -509,7 +533,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                         acc = mfma(db[2 * m + hh], cat(*(const bf16x4*)(krow + d0), *(const bf16x4*)(krow + d0 + 8)),
                                    acc);
                     }
-                if (MODE == DECAY_HEAD) {
+                if (MODE == DECAY_HEAD && !FACT) {
 #pragma unroll
                     for (int i = 0; i < 16; i++) acc[i] *= wj;
                 }
@@ -517,6 +541,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
                 for (int ks = 2 * jb; ks < 4; ks++) {
                     const bf16x8 b = *(const bf16x8*)(&sm.pv[jt * PPITCH + ks * 16 + kg * 8]);
                     acc = mfma(ob[ks], b, acc);
+                }
+                if constexpr (FACT) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) acc[i] *= ainv;
                 }
                 if (jt < n) {
                     __bf16* vrow = dv_out + (row_base + t0 + jt) * D + 32 * cb + kg * 4;
@@ -528,12 +556,12 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
             }
         }
 
-        // ---- D <- a^n D + (q a^{i+1})^T d_o
+        // ---- D <- a^n D + (q a^{i+1})^T d_o (FACT: D is a^n D already)
         {
             const float fh = (MODE == DECAY_HEAD) ? sm.apow[n] : 1.f;
 #pragma unroll
             for (int m = 0; m < NCB; m++) {
-                if (MODE == DECAY_HEAD) {
+                if (MODE == DECAY_HEAD && !FACT) {
 #pragma unroll
                     for (int i = 0; i < 16; i++) Dm[m][i] *= fh;
                 }
@@ -1352,6 +1380,22 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
             }
             if ((e = launch_state_scan(b_state, b_decay, b_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
                 return e;
+        }
+        if constexpr (MODE == DECAY_HEAD) {
+            if (!intra_part) {  // the factorised walk, then the heads with a stronger decay
+                LA_TRACED(a.tr, "chunk_bwd_dkdv",
+                          bwd_dkdv_kernel<D, MODE, false, false, true><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                              q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out,
+                              a.ds_in, nullptr, nullptr, b_state, nullptr, nullptr, a.H, a.L, a.nseg, G, cps,
+                              a.inv_norm, wide));
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                LA_TRACED(a.tr, "chunk_bwd_dkdv_strong_decay",
+                          bwd_dkdv_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                              q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out,
+                              a.ds_in, nullptr, nullptr, b_state, nullptr, nullptr, a.H, a.L, a.nseg, G, cps,
+                              a.inv_norm, wide));
+                return hipGetLastError();
+            }
         }
         LA_TRACED(a.tr, "chunk_bwd_dkdv",
                   bwd_dkdv_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
