@@ -76,25 +76,34 @@ def _compare(got, ref, dtype, mode):
             assert err <= TOL[dtype], (name, err)
 
 
+@pytest.mark.parametrize("want_decay", [False, True])
 @pytest.mark.parametrize("d", [128, 64])
-def test_bwd_head_decay_both_walks(d):
-    """bf16 head decay without d lambda_h: the matrix-core passes take their factorised walks (dq on
-    the forward's kernel, dk/dv's own) for heads with lambda C log2(e) >= -100 and the per-pair
-    weights for stronger decays, both in one call (lambda = -1.0 and -1.6 straddle the bounds,
-    -inf is a = 0); every derivative against the oracle (ragged length, several sub-segments)."""
+def test_bwd_head_decay_both_walks(d, want_decay):
+    """bf16 head decay: the matrix-core passes take their factorised walks (dq on the forward's
+    kernel; dk/dv's own unless d lambda_h is wanted, whose pair sums keep the per-pair weights) for
+    heads with lambda C log2(e) >= -100 and the per-pair weights for stronger decays, both in one
+    call (lambda = -1.0 and -1.6 straddle the bounds, -inf is a = 0); every derivative against the
+    oracle (ragged length, several sub-segments), d lambda_h too when requested.  The lambda = -inf
+    head is left out of d lambda_h: its derivative there is not defined."""
     lams = np.array([-1e-4, -0.02, -0.5, -1.0, -1.6, -3.0, 0.0, -np.inf], np.float32)
+    if want_decay:
+        lams = lams[:-1]
     w, inp, gr = _case("head", "bf16", d, d, 64 * 9 + 21, 64, 1, seed=880 + d, B=1, H=len(lams))
     inp["decay"] = torch.from_numpy(lams)
-    note(f"la_chunk_bwd head decay both walks d={d} lambdas={lams.tolist()}")
+    note(f"la_chunk_bwd head decay both walks d={d} want_decay={want_decay} lambdas={lams.tolist()}")
     dd, g = to_dev(inp), to_dev(gr)
     got = lb.la_chunk_bwd(dd["q"], dd["k"], dd["v"], g["d_o"], dd["decay"], dd["s_in"], g["ds_out"], mode="head",
-                          want_decay=False, subseg_chunks=2)
+                          want_decay=want_decay, subseg_chunks=2)
     torch.cuda.synchronize()
     ref = _oracle(w, inp, gr, 1)
     for name, x, r in zip(("dq", "dk", "dv", "ds_in"), (got[0], got[1], got[2], got[4]),
                           (ref[0], ref[1], ref[2], ref[4])):
         for h in range(len(lams)):
             assert rel_err(x[:, h:h + 1], r[:, h:h + 1]) <= TOL["bf16"], (name, float(lams[h]))
+    if want_decay:
+        for h in range(len(lams)):
+            assert abs(float(got[3][h]) - ref[3][h]) <= TOL_DECAY["bf16"] * max(1e-12, np.max(np.abs(ref[3]))), \
+                float(lams[h])
 
 
 @pytest.mark.parametrize("mode", ["none", "head", "gate"])
