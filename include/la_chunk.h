@@ -52,7 +52,7 @@ typedef enum la_status {
     LA_ERR_SHAPE = -2,       /* a size is negative / zero where it must not be, or does not divide */
     LA_ERR_DTYPE = -3,       /* unknown dtype, or a dtype combination that is not supported */
     LA_ERR_ALIAS = -4,       /* an output overlaps an input it may not overlap */
-    LA_ERR_UNSUPPORTED = -5, /* valid request that this build has no kernel for (e.g. dk > 128) */
+    LA_ERR_UNSUPPORTED = -5, /* valid request that the library has no kernel for (e.g. dk > 128) */
     LA_ERR_LAUNCH = -6,      /* the HIP runtime refused a launch or a workspace allocation */
     LA_ERR_DECAY = -7,       /* unknown decay mode, or gate_norm <= 0 in gate mode */
     LA_ERR_WORKSPACE = -8,   /* la_chunk_fwd_noalloc: the call needs more than LA_NOALLOC_SCRATCH_BYTES */
@@ -91,7 +91,7 @@ typedef struct la_shape {
     int32_t dv;           /* value head dim: 16, 32, 64 or 128 (la_chunk_fwd also 256) */
     int32_t nseg;         /* independent segments per sequence, >= 1, each L/nseg tokens */
     int32_t in_dtype;     /* la_dtype of q, k, v */
-    int32_t out_dtype;    /* la_dtype of o (must equal in_dtype in this build) */
+    int32_t out_dtype;    /* la_dtype of o (must equal in_dtype in this version) */
     int32_t decay_mode;   /* la_decay_mode */
     float gate_norm;      /* LA_DECAY_GATE only: exponent 1/gate_norm on the sigmoid, > 0 */
     int32_t seg_begin;    /* la_state_correct only: first segment to correct, 0 <= seg_begin <= nseg */
