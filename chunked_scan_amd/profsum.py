@@ -136,6 +136,12 @@ def label(demangled: str):
         if dq:
             return "chunk_bwd_dq" + ("_state_pass" if so else ""), inst
         return name + ("_state_pass" if so else "_output_pass"), inst
+    if base in ("bwd_dq_kernel", "bwd_dkdv_kernel") and len(args) > 3:
+        # WIN: the gate's windowed redo; FACT (dk/dv, head decay): the factorised walk
+        extra = ["windows"] if args[3] in ("true", "1") else []
+        if len(args) > 4 and args[4] in ("true", "1"):
+            extra.append("factorised")
+        shown = shown[:3] + extra
     if si is not None:
         if name.startswith("chunk_bwd"):
             name += "_state_pass" if so else ""
