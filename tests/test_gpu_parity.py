@@ -552,13 +552,15 @@ def test_edge_cases():
         assert rel_err(s, s_ref) <= TOL["bf16"], lam
 
 
-@pytest.mark.parametrize("subseg", [0, 2])
+@pytest.mark.parametrize("subseg", [0, 1, 2, 3, 5])
 def test_head_decay_both_walks(subseg):
     """d = 128 head decay: the output pass takes its factorised walk (the intra-chunk product on v
     scaled by the state update's weights, one scale per output row) while lambda (C - 1) log2(e)
     >= -100, and keeps per-pair factors for stronger decays; heads on both sides of that bound
     (lambda = -1.0 and -1.2 straddle it), with lambda = 0, -inf and the workload's weakest decay,
-    in one launch, against the oracle (ragged length, several sub-segments, s_in)."""
+    in one launch, against the oracle (ragged length, several sub-segments, s_in).  The sub-segment
+    lengths give walks of 1 to 5 chunks, so the factorised walk's loaders run every form of their
+    loop (two chunks in flight, the peeled tail, walks shorter than four chunks)."""
     lams = np.array([-1e-4, -0.02, -0.5, -1.0, -1.2, -3.0, 0.0, -np.inf], np.float32)
     w = W2.scaled(B=1, H=len(lams), L=64 * 9 + 19, s_in_std=0.05, seed=777 + subseg)
     note(f"head decay both walks, d=128 subseg_chunks={subseg} lambdas={lams.tolist()}")
