@@ -1461,7 +1461,9 @@ hipError_t launch_d(const BwdArgs& a) {
     const size_t bytes = n_chunks ? ds_off + sizeof(__bf16) * n_chunks * D * D : f_bytes;
     char* ws = nullptr;
     hipError_t e = hipSuccess;
-    if (bytes > 0 && (e = workspace_alloc((void**)&ws, bytes, a.stream)) != hipSuccess) return e;
+    bool owned = false;
+    if (bytes > 0 && (e = workspace_acquire(WS_BACKWARD, (void**)&ws, bytes, a.stream, &owned)) != hipSuccess)
+        return e;
     double* part = n_dbl ? (double*)ws : nullptr;
     double* intra = n_dbl ? part + (size_t)units * G : nullptr;
     float* fp = (float*)(ws + sizeof(double) * n_dbl);
@@ -1490,11 +1492,8 @@ hipError_t launch_d(const BwdArgs& a) {
                                        nullptr);
     if (e == hipSuccess && dlam && a.s_sub) e = launch_dlam_states<D>(a, G, cps, l_state, lt_state, l_decay);
     if (e == hipSuccess && dlam) e = launch_dlam<D>(a, G, cps, l_state, lt_state, l_decay, part, intra);
-    if (ws) {
-        hipError_t f = hipFreeAsync(ws, a.stream);
-        if (e == hipSuccess) e = f;
-    }
-    return e;
+    const hipError_t f = workspace_release(ws, a.stream, owned);
+    return e == hipSuccess ? f : e;
 }
 
 }  // namespace

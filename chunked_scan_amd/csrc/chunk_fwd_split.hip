@@ -15,6 +15,7 @@
 #include "la_internal.h"
 
 #include <mutex>
+#include <vector>
 
 namespace la {
 namespace {
@@ -55,12 +56,83 @@ hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t stream) {
     return hipMallocFromPoolAsync(p, bytes, pool, stream);
 }
 
+// Workspace kept between calls, one buffer per (device, stream, call site), grown when a call
+// needs more.  Calls on one stream run in order, so the buffer a call leaves is free for the next
+// call on that stream; calls on different streams get different buffers.  Taking it costs nothing
+// on the GPU, where a pool allocation and its stream-ordered free per call put ≈2.5 µs of queue
+// bubbles into the headline step (82.5 against 85 µs).  A stream under graph capture takes a
+// per-call pool allocation instead (owned: the caller frees it), so a graph never holds a cached
+// buffer.  A slot is taken by one call site only, so nested calls never share a buffer.
+namespace {
+struct CachedWorkspace {
+    int dev, slot;
+    hipStream_t stream;
+    void* p;
+    size_t bytes;
+};
+std::mutex cache_mu;
+std::vector<CachedWorkspace> cache;
+}  // namespace
+
+hipError_t workspace_acquire(int slot, void** p, size_t bytes, hipStream_t stream, bool* owned) {
+    *owned = true;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone)
+        return workspace_alloc(p, bytes, stream);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(cache_mu);
+    for (size_t i = 0; i < cache.size(); i++) {
+        CachedWorkspace& c = cache[i];
+        if (c.dev != dev || c.slot != slot || c.stream != stream) continue;
+        if (c.bytes < bytes) {  // grow: the old buffer goes back once the stream's earlier work is done
+            e = hipFreeAsync(c.p, stream);
+            if (e == hipSuccess) e = workspace_alloc(&c.p, bytes, stream);
+            if (e != hipSuccess) {
+                cache.erase(cache.begin() + i);
+                return e;
+            }
+            c.bytes = bytes;
+        }
+        *p = c.p;
+        *owned = false;
+        return hipSuccess;
+    }
+    void* q = nullptr;
+    e = workspace_alloc(&q, bytes, stream);
+    if (e != hipSuccess) return e;
+    cache.push_back({dev, slot, stream, q, bytes});
+    *p = q;
+    *owned = false;
+    return hipSuccess;
+}
+
+hipError_t workspace_release(void* p, hipStream_t stream, bool owned) {
+    return owned && p ? hipFreeAsync(p, stream) : hipSuccess;
+}
+
 hipError_t workspace_trim() {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     hipMemPool_t pool = workspace_pool(dev);
     if (!pool) return hipErrorOutOfMemory;
+    {
+        // the cached buffers of this device: once the device is idle none is in use
+        std::lock_guard<std::mutex> lock(cache_mu);
+        bool any = false;
+        for (const CachedWorkspace& c : cache) any |= c.dev == dev;
+        if (any) {
+            if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
+            for (size_t i = cache.size(); i-- > 0;)
+                if (cache[i].dev == dev) {
+                    if ((e = hipFreeAsync(cache[i].p, nullptr)) != hipSuccess) return e;
+                    cache.erase(cache.begin() + i);
+                }
+            if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
+        }
+    }
     return hipMemPoolTrimTo(pool, 0);
 }
 
@@ -169,16 +241,14 @@ hipError_t launch_chunk_fwd_mfma(const FwdArgs& a) {
     fwd_split_plan(a, &G, &cps);
     const size_t nf = fwd_split_workspace_floats(a, G);
     float* ws = nullptr;
+    bool owned = false;
     if (nf > 0) {
-        hipError_t e = workspace_alloc((void**)&ws, nf * sizeof(float), a.stream);
+        hipError_t e = workspace_acquire(WS_FORWARD, (void**)&ws, nf * sizeof(float), a.stream, &owned);
         if (e != hipSuccess) return e;
     }
     hipError_t e = fwd_split_run(a, G, cps, ws);
-    if (ws) {
-        hipError_t f = hipFreeAsync(ws, a.stream);
-        if (e == hipSuccess) e = f;
-    }
-    return e;
+    const hipError_t f = workspace_release(ws, a.stream, owned);
+    return e == hipSuccess ? f : e;
 }
 
 // ---- the allocation-free forward (la_chunk_fwd_noalloc)

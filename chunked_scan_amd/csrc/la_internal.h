@@ -114,7 +114,15 @@ hipMemPool_t workspace_pool(int dev);
 // Temporary workspace on the current device's pool, stream-ordered on `stream` (free it with
 // hipFreeAsync on the same stream).
 hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t stream);
-// Returns the current device's pool memory not in use to the device.
+// Workspace that stays with (current device, stream, slot) between calls (chunk_fwd_split.hip):
+// *owned = false, and the next call on that stream with the same slot gets the same memory; on a
+// stream under graph capture a per-call pool allocation, *owned = true.  Release with
+// workspace_release either way.  Each call site has its own slot.
+enum WorkspaceSlot { WS_FORWARD = 0, WS_BACKWARD = 1 };
+hipError_t workspace_acquire(int slot, void** p, size_t bytes, hipStream_t stream, bool* owned);
+hipError_t workspace_release(void* p, hipStream_t stream, bool owned);
+// Synchronises the device if it holds cached workspace, frees that, and returns the pool memory
+// not in use to the device.
 hipError_t workspace_trim();
 
 // Chunked backward with fp32 arithmetic on VALU (chunk_bwd_generic.hip): every shape the generic

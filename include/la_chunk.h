@@ -17,16 +17,20 @@
  *
  * Memory.  Every pointer is a device pointer (HBM) owned by the caller; the library never
  * frees or keeps one past the call.  Tensors are dense, row-major, in the layouts stated per
- * argument.  Calls that need temporary device workspace take it from a stream-ordered memory
- * pool the library keeps per device, on the caller's stream, and free it (stream-ordered) before
- * returning: la_chunk_fwd and la_chunk_fwd_decayed (per sub-segment states when a segment is split
- * across compute units; in gate mode a few flags per workgroup; la_chunk_fwd_decayed on the shapes
- * whose forward does not emit its outputs, one float per 64 tokens and key dim in gate mode),
- * la_chunk_bwd and la_chunk_bwd_states (per sub-segment states, and the decay derivative's
- * partials), and la_cumdecay in gate mode (one float per 64 tokens and key dim).  The pool keeps
- * the memory it has obtained (so repeated calls never reach the driver) until la_trim_workspace.
- * la_chunk_fwd_noalloc, la_state_scan, la_state_correct and la_state_correct_live allocate
- * nothing.
+ * argument.  Temporary device workspace comes from a stream-ordered memory pool the library keeps
+ * per device.  The matrix-core forward and backward (la_chunk_fwd, la_chunk_fwd_decayed,
+ * la_chunk_bwd, la_chunk_bwd_states: per sub-segment states when a segment is split across
+ * compute units, in gate mode a few flags per workgroup, the decay derivative's partials) keep
+ * theirs between calls: one buffer per device, stream and call, taken from the pool on the
+ * stream's first call and replaced by a larger one when a call needs more, so repeated calls on a
+ * stream allocate nothing; calls on different streams use different buffers.  On a stream under
+ * graph capture they take it per call and free it (stream-ordered) before returning, so a graph
+ * holds no kept buffer.  Per call, freed the same way: la_cumdecay in gate mode and
+ * la_chunk_fwd_decayed on the shapes whose forward does not emit its outputs (one float per 64
+ * tokens and key dim in gate mode), and the fp32 backward's decay-derivative partials.  The pool
+ * keeps the memory it has obtained (so repeated calls never reach the driver); la_trim_workspace
+ * releases the kept buffers and that memory.  la_chunk_fwd_noalloc, la_state_scan,
+ * la_state_correct and la_state_correct_live allocate nothing.
  *
  * Execution.  Calls validate every argument on the host first, then enqueue kernels on
  * shape->stream (a hipStream_t; NULL = the default stream) and return without waiting.  A
@@ -352,8 +356,10 @@ la_status la_state_correct_live(const void* q, const float* cumdecay, const floa
  */
 la_status la_cumdecay(const float* decay, float* cumdecay, float* total, const la_shape* shape);
 
-/* Returns the memory of the current device's workspace pool that no enqueued call still uses to
- * the device (the pool keeps what it has obtained until then; later calls obtain it again).
+/* Releases the current device's workspace: when the device holds buffers kept between calls, it
+ * waits for the device to be idle and frees them; then it returns the pool's memory that no
+ * enqueued call still uses to the device (later calls obtain it again).  Not to be called while
+ * another thread enqueues work on the device or during graph capture.
  * Returns LA_OK or LA_ERR_LAUNCH. */
 la_status la_trim_workspace(void);
 

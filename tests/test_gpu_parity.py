@@ -667,6 +667,39 @@ def test_device_step_graph_replay(mode):
         assert torch.equal(s_g, s_ref), rep
 
 
+def test_kept_workspace_grows_and_follows_streams():
+    """The forward's workspace stays with its stream between calls: calls of growing and shrinking
+    sizes on one stream, and calls on two streams in flight together, each give the result of the
+    allocation-free forward (same kernels) bit for bit; so do the calls after la_trim_workspace."""
+    note("kept workspace: sizes and streams")
+    ws = [W2.scaled(B=1, H=h, L=L, decay="head_pow2", s_in_std=0.05, seed=2100 + L)
+          for h, L in ((2, 64 * 6), (4, 64 * 40 + 17), (3, 64 * 20))]
+    ins = [to_dev(make_inputs(w, "cpu")) for w in ws]
+
+    def outs(w):
+        return (torch.empty((w.B, w.H, w.L, w.dv), dtype=torch.bfloat16, device="cuda"),
+                torch.empty((w.B, w.H, 1, w.dk, w.dv), dtype=torch.float32, device="cuda"))
+
+    refs = []
+    for w, d in zip(ws, ins):
+        o, s_ = outs(w)
+        lb.la_chunk_fwd_noalloc(d["q"], d["k"], d["v"], d["decay"], d["s_in"], o, s_, mode=w.mode)
+        refs.append((o, s_))
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for rnd in range(2):
+        plan = [(sa, 0), (sb, 1), (sa, 1), (sb, 2), (sa, 2), (sb, 0), (sa, 0)]
+        res = [outs(ws[i]) for _, i in plan]
+        torch.cuda.synchronize()
+        for (st, i), (o, s_) in zip(plan, res):
+            d = ins[i]
+            lb.la_chunk_fwd(d["q"], d["k"], d["v"], d["decay"], d["s_in"], o, s_, mode=ws[i].mode, stream=st)
+        torch.cuda.synchronize()
+        for n, ((st, i), (o, s_)) in enumerate(zip(plan, res)):
+            assert torch.equal(o, refs[i][0]) and torch.equal(s_, refs[i][1]), (rnd, n)
+        lb.la_trim_workspace()
+
+
 def test_trim_workspace_between_calls():
     """la_trim_workspace hands the pool's unused memory back; the next calls obtain it again and
     give bit-identical results (forward with its sub-segment split, backward, gate cumulative decay)."""
