@@ -634,17 +634,23 @@ def test_chunk128_decayed_and_device_step(mode, d):
     assert rel_err(s_out, s1_ref[:, :, 0]) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("mode", ["none", "head", "gate"])
-def test_device_step_graph_replay(mode):
+@pytest.mark.parametrize("mode,form", [("none", "decomposed"), ("head", "decomposed"), ("gate", "decomposed"),
+                                       ("none", "exact"), ("head", "exact"), ("gate", "exact")])
+def test_device_step_graph_replay(mode, form):
     """The device step captured in a HIP graph (through torch.cuda.graph) and replayed several times,
     with eager work and synchronisations between the replays: every replay's O and outgoing state
-    equal the eager step's bit for bit (the library enqueues kernels only: no memsets, no host sync)."""
+    equal the eager step's bit for bit (the library enqueues kernels only: no memsets, no host sync).
+    The warm-up leaves a kept workspace on the side stream; the captured calls allocate per call."""
     decay = {"none": "none", "head": "head_pow2", "gate": "gate"}[mode]
     w = W2.scaled(B=1, H=4, L=64 * 40, decay=decay, s_in_std=0.05, seed=1500)
-    note(f"device step graph replay, bf16 d128 mode={mode}")
+    note(f"device step graph replay, bf16 d128 mode={mode} form={form}")
     d = to_dev(make_inputs(w, "cpu"))
-    step = pipeline.DeviceStep(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode=w.mode, chunk=64,
-                               gate_norm=w.gate_norm, subseg=4)
+    if form == "exact":
+        step = pipeline.ExactStep(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode=w.mode, chunk=64,
+                                  gate_norm=w.gate_norm)
+    else:
+        step = pipeline.DeviceStep(d["q"], d["k"], d["v"], d["decay"], d["s_in"], mode=w.mode, chunk=64,
+                                   gate_norm=w.gate_norm, subseg=4)
     o_ref, s_ref = (x.clone() for x in step.run())
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
