@@ -194,8 +194,9 @@ struct BwdSmem {
 //   dk_j = a^{-(j+1)} (D' v_j + sum_{i>=j} p'_ij q~_i),  dv_j = a^{-(j+1)} (D'^T k_j + sum_{i>=j} (q~_i . k_j) d_o_i),
 //   D <- D' + q~^T d_o,
 // so the scores take only the causal mask, and q itself need not be staged.
-template <int D, int MODE, bool STATE_ONLY, bool WIN = false, bool FACT = false>
-__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
+template <int D, int MODE, bool STATE_ONLY, bool WIN, bool FACT>
+__device__ __forceinline__ void bwd_dkdv_body(
+    BwdSmem<D, MODE, STATE_ONLY>& sm,
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ ds_out,
     int64_t sstride, __bf16* __restrict__ dk_out, __bf16* __restrict__ dv_out, float* __restrict__ ds_in,
@@ -204,7 +205,6 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
     double* __restrict__ intra_part,  // head mode, output pass: the intra-chunk part of d lambda_h, or null
     __bf16* __restrict__ d_start,     // output pass, gate derivative: D^T at every chunk's start (bf16 [D][D]), or null
     int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
-    __shared__ __attribute__((aligned(16))) BwdSmem<D, MODE, STATE_ONLY> sm;
     if constexpr (MODE == DECAY_GATE) {
         if constexpr (WIN) {
             if (wide[blockIdx.x] == 0) return;
@@ -613,6 +613,44 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
         __syncthreads();
         if (tid == 0) intra_part[ub * G + g] = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
     }
+}
+
+template <int D, int MODE, bool STATE_ONLY, bool WIN = false, bool FACT = false>
+__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ ds_out,
+    int64_t sstride, __bf16* __restrict__ dk_out, __bf16* __restrict__ dv_out, float* __restrict__ ds_in,
+    float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
+    const float* __restrict__ init_state,                            // output pass: scanned D^(g)
+    double* __restrict__ intra_part,  // head mode, output pass: the intra-chunk part of d lambda_h, or null
+    __bf16* __restrict__ d_start,     // output pass, gate derivative: D^T at every chunk's start (bf16 [D][D]), or null
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
+    __shared__ __attribute__((aligned(16))) BwdSmem<D, MODE, STATE_ONLY> sm;
+    bwd_dkdv_body<D, MODE, STATE_ONLY, WIN, FACT>(sm, q, k, v, d_o, decay, ds_out, sstride, dk_out, dv_out, ds_in, part_state, part_decay, init_state, intra_part,
+        d_start, H, L, nseg, G, cps, inv_norm, wide);
+}
+
+// Head decay, output pass, d lambda_h not wanted: both walks in one launch, every workgroup taking
+// the one its head's decay allows (the factorised walk when lambda C log2(e) >= -100, the test the
+// body itself makes), so no launch is spent on workgroups that all leave.
+template <int D>
+__global__ __launch_bounds__(NT) void bwd_dkdv_head_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ ds_out,
+    int64_t sstride, __bf16* __restrict__ dk_out, __bf16* __restrict__ dv_out, float* __restrict__ ds_in,
+    float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
+    const float* __restrict__ init_state,                            // output pass: scanned D^(g)
+    double* __restrict__ intra_part,  // head mode, output pass: the intra-chunk part of d lambda_h, or null
+    __bf16* __restrict__ d_start,     // output pass, gate derivative: D^T at every chunk's start (bf16 [D][D]), or null
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
+    __shared__ __attribute__((aligned(16))) BwdSmem<D, DECAY_HEAD, false> sm;
+    const int64_t h = ((int64_t)blockIdx.x / G / nseg) % H;  // unit (bh, seg, g) of the output pass
+    if (decay[h] * LOG2E * (float)C >= -100.f)
+        bwd_dkdv_body<D, DECAY_HEAD, false, false, true>(sm, q, k, v, d_o, decay, ds_out, sstride, dk_out, dv_out, ds_in, part_state, part_decay, init_state, intra_part,
+        d_start, H, L, nseg, G, cps, inv_norm, wide);
+    else
+        bwd_dkdv_body<D, DECAY_HEAD, false, false, false>(sm, q, k, v, d_o, decay, ds_out, sstride, dk_out, dv_out, ds_in, part_state, part_decay, init_state, intra_part,
+        d_start, H, L, nseg, G, cps, inv_norm, wide);
 }
 
 
@@ -1382,15 +1420,9 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
                 return e;
         }
         if constexpr (MODE == DECAY_HEAD) {
-            if (!intra_part) {  // the factorised walk, then the heads with a stronger decay
+            if (!intra_part) {  // the factorised walk, or the per-pair one for heads with a stronger decay
                 LA_TRACED(a.tr, "chunk_bwd_dkdv",
-                          bwd_dkdv_kernel<D, MODE, false, false, true><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                              q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out,
-                              a.ds_in, nullptr, nullptr, b_state, nullptr, nullptr, a.H, a.L, a.nseg, G, cps,
-                              a.inv_norm, wide));
-                if ((e = hipGetLastError()) != hipSuccess) return e;
-                LA_TRACED(a.tr, "chunk_bwd_dkdv_strong_decay",
-                          bwd_dkdv_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                          bwd_dkdv_head_kernel<D><<<(unsigned)(units * G), NT, 0, a.stream>>>(
                               q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out,
                               a.ds_in, nullptr, nullptr, b_state, nullptr, nullptr, a.H, a.L, a.nseg, G, cps,
                               a.inv_norm, wide));
