@@ -630,6 +630,27 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(
         d_start, H, L, nseg, G, cps, inv_norm, wide);
 }
 
+// Gate mode: the plain walk, then the windowed one for a unit the plain walk flagged (as for
+// bwd_dq_gate_kernel).
+template <int D, bool STATE_ONLY>
+__global__ __launch_bounds__(NT) void bwd_dkdv_gate_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ ds_out,
+    int64_t sstride, __bf16* __restrict__ dk_out, __bf16* __restrict__ dv_out, float* __restrict__ ds_in,
+    float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
+    const float* __restrict__ init_state,                            // output pass: scanned D^(g)
+    double* __restrict__ intra_part,  // head mode, output pass: the intra-chunk part of d lambda_h, or null
+    __bf16* __restrict__ d_start,     // output pass, gate derivative: D^T at every chunk's start (bf16 [D][D]), or null
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
+    __shared__ __attribute__((aligned(16))) BwdSmem<D, DECAY_GATE, STATE_ONLY> sm;
+    bwd_dkdv_body<D, DECAY_GATE, STATE_ONLY, false, false>(sm, q, k, v, d_o, decay, ds_out, sstride, dk_out, dv_out, ds_in, part_state, part_decay, init_state, intra_part,
+        d_start, H, L, nseg, G, cps, inv_norm, wide);
+    __syncthreads();
+    if (__hip_atomic_load(wide + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+        bwd_dkdv_body<D, DECAY_GATE, STATE_ONLY, true, false>(sm, q, k, v, d_o, decay, ds_out, sstride, dk_out, dv_out, ds_in, part_state, part_decay, init_state, intra_part,
+        d_start, H, L, nseg, G, cps, inv_norm, wide);
+}
+
 // Head decay, output pass, d lambda_h not wanted: both walks in one launch, every workgroup taking
 // the one its head's decay allows (the factorised walk when lambda C log2(e) >= -100, the test the
 // body itself makes), so no launch is spent on workgroups that all leave.
@@ -676,8 +697,9 @@ struct DqSmem {
 };
 
 // WIN: as for bwd_dkdv_kernel.
-template <int D, int MODE, bool STATE_ONLY, bool WIN = false>
-__global__ __launch_bounds__(NT) void bwd_dq_kernel(
+template <int D, int MODE, bool STATE_ONLY, bool WIN>
+__device__ __forceinline__ void bwd_dq_body(
+    DqSmem<D, MODE, STATE_ONLY>& sm,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ s_in,
     const float* __restrict__ ds_out, int64_t sstride, __bf16* __restrict__ dq,
@@ -688,7 +710,6 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
     const __bf16* __restrict__ d_start,  // gate derivative: D^T at every chunk's start (bf16 [D][D]), or null
     float* __restrict__ c0_out,          // gate derivative: rowsum(S (.) D) at every chunk's start ([D])
     int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
-    __shared__ __attribute__((aligned(16))) DqSmem<D, MODE, STATE_ONLY> sm;
     if constexpr (MODE == DECAY_GATE) {
         if constexpr (WIN) {
             if (wide[blockIdx.x] == 0) return;
@@ -996,6 +1017,48 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(
         if (MODE == DECAY_GATE) tot = __builtin_amdgcn_exp2f(gate_total);
         part_decay[(ub * (G - 1) + g) * D + tid] = tot;
     }
+}
+
+template <int D, int MODE, bool STATE_ONLY, bool WIN = false>
+__global__ __launch_bounds__(NT) void bwd_dq_kernel(
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ s_in,
+    const float* __restrict__ ds_out, int64_t sstride, __bf16* __restrict__ dq,
+    float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
+    // output pass: the state entering sub-segment g >= 1 of (bh, seg) at
+    // init_state + bh * ist_bh + (seg * ist_g + g + ist_off) * D * D (the scan buffer, or states the caller gives)
+    const float* __restrict__ init_state, int64_t ist_bh, int ist_g, int ist_off,
+    const __bf16* __restrict__ d_start,  // gate derivative: D^T at every chunk's start (bf16 [D][D]), or null
+    float* __restrict__ c0_out,          // gate derivative: rowsum(S (.) D) at every chunk's start ([D])
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
+    __shared__ __attribute__((aligned(16))) DqSmem<D, MODE, STATE_ONLY> sm;
+    bwd_dq_body<D, MODE, STATE_ONLY, WIN>(sm, k, v, d_o, decay, s_in, ds_out, sstride, dq, part_state, part_decay, init_state, ist_bh, ist_g,
+        ist_off, d_start, c0_out, H, L, nseg, G, cps, inv_norm, wide);
+}
+
+// Gate mode: the plain walk and, for a unit it flagged as holding a chunk too wide for one piece,
+// the windowed walk after it in the same workgroup (which overwrites all the plain walk wrote for
+// the unit), instead of a second launch whose workgroups almost all leave.  The flag is read at
+// device scope after the barrier that ends the plain walk.
+template <int D, bool STATE_ONLY>
+__global__ __launch_bounds__(NT) void bwd_dq_gate_kernel(
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ d_o, const float* __restrict__ decay, const float* __restrict__ s_in,
+    const float* __restrict__ ds_out, int64_t sstride, __bf16* __restrict__ dq,
+    float* __restrict__ part_state, float* __restrict__ part_decay,  // state pass outputs
+    // output pass: the state entering sub-segment g >= 1 of (bh, seg) at
+    // init_state + bh * ist_bh + (seg * ist_g + g + ist_off) * D * D (the scan buffer, or states the caller gives)
+    const float* __restrict__ init_state, int64_t ist_bh, int ist_g, int ist_off,
+    const __bf16* __restrict__ d_start,  // gate derivative: D^T at every chunk's start (bf16 [D][D]), or null
+    float* __restrict__ c0_out,          // gate derivative: rowsum(S (.) D) at every chunk's start ([D])
+    int64_t H, int64_t L, int nseg, int G, int cps, float inv_norm, int* __restrict__ wide) {
+    __shared__ __attribute__((aligned(16))) DqSmem<D, DECAY_GATE, STATE_ONLY> sm;
+    bwd_dq_body<D, DECAY_GATE, STATE_ONLY, false>(sm, k, v, d_o, decay, s_in, ds_out, sstride, dq, part_state, part_decay, init_state, ist_bh, ist_g,
+        ist_off, d_start, c0_out, H, L, nseg, G, cps, inv_norm, wide);
+    __syncthreads();
+    if (__hip_atomic_load(wide + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+        bwd_dq_body<D, DECAY_GATE, STATE_ONLY, true>(sm, k, v, d_o, decay, s_in, ds_out, sstride, dq, part_state, part_decay, init_state, ist_bh, ist_g,
+        ist_off, d_start, c0_out, H, L, nseg, G, cps, inv_norm, wide);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1372,30 +1435,30 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
         } else {
             hipError_t e;
             if (init == f_state && G > 1) {
-                LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
-                          bwd_dq_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                              k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay,
-                              nullptr, 0, 0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
-                if ((e = hipGetLastError()) != hipSuccess) return e;
-                if (MODE == DECAY_GATE) {
-                    LA_TRACED(a.tr, "chunk_bwd_dq_state_pass_windows",
-                              bwd_dq_kernel<D, MODE, true, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                if constexpr (MODE == DECAY_GATE)  // the plain walk and the windowed one in one launch
+                    LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
+                              bwd_dq_gate_kernel<D, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
                                   k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay,
                                   nullptr, 0, 0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
-                    if ((e = hipGetLastError()) != hipSuccess) return e;
-                }
+                else
+                    LA_TRACED(a.tr, "chunk_bwd_dq_state_pass",
+                              bwd_dq_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                                  k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, nullptr, f_state, f_decay,
+                                  nullptr, 0, 0, 0, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+                if ((e = hipGetLastError()) != hipSuccess) return e;
                 e = launch_state_scan(f_state, f_decay, f_state, units, G - 1, D, D, a.stream, a.tr);
                 if (e != hipSuccess) return e;
             }
-            LA_TRACED(a.tr, "chunk_bwd_dq",
-                      bwd_dq_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                          k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, init,
-                          ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
-            if ((e = hipGetLastError()) != hipSuccess || MODE != DECAY_GATE) return e;
-            LA_TRACED(a.tr, "chunk_bwd_dq_windows",
-                      bwd_dq_kernel<D, MODE, false, true><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                          k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr, init,
-                          ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+            if constexpr (MODE == DECAY_GATE)
+                LA_TRACED(a.tr, "chunk_bwd_dq",
+                          bwd_dq_gate_kernel<D, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                              k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr,
+                              init, ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+            else
+                LA_TRACED(a.tr, "chunk_bwd_dq",
+                          bwd_dq_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                              k, v, d_o, a.decay, a.s_in, a.ds_out, a.state_stride, (__bf16*)a.dq, nullptr, nullptr,
+                              init, ist_bh, ist_g, ist_off, d_start, c0, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
             return hipGetLastError();
         }
     };
@@ -1404,18 +1467,17 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
     auto dkdv_passes = [&]() -> hipError_t {
         hipError_t e;
         if (G > 1) {
-            LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass",
-                      bwd_dkdv_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
-                          q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state, b_decay,
-                          nullptr, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            if (MODE == DECAY_GATE) {
-                LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass_windows",
-                          bwd_dkdv_kernel<D, MODE, true, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+            if constexpr (MODE == DECAY_GATE)  // the plain walk and the windowed one in one launch
+                LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass",
+                          bwd_dkdv_gate_kernel<D, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
                               q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state,
                               b_decay, nullptr, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
-                if ((e = hipGetLastError()) != hipSuccess) return e;
-            }
+            else
+                LA_TRACED(a.tr, "chunk_bwd_dkdv_state_pass",
+                          bwd_dkdv_kernel<D, MODE, true><<<(unsigned)(units * (G - 1)), NT, 0, a.stream>>>(
+                              q, k, v, d_o, a.decay, a.ds_out, a.state_stride, nullptr, nullptr, nullptr, b_state,
+                              b_decay, nullptr, nullptr, nullptr, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+            if ((e = hipGetLastError()) != hipSuccess) return e;
             if ((e = launch_state_scan(b_state, b_decay, b_state, units, G - 1, D, D, a.stream, a.tr)) != hipSuccess)
                 return e;
         }
@@ -1429,15 +1491,18 @@ hipError_t launch_mode(const BwdArgs& a, int G, int cps, float* f_state, float* 
                 return hipGetLastError();
             }
         }
-        LA_TRACED(a.tr, "chunk_bwd_dkdv",
-                  bwd_dkdv_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                      q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out, a.ds_in,
-                      nullptr, nullptr, b_state, intra_part, d_start, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
-        if ((e = hipGetLastError()) != hipSuccess || MODE != DECAY_GATE) return e;
-        LA_TRACED(a.tr, "chunk_bwd_dkdv_windows",
-                  bwd_dkdv_kernel<D, MODE, false, true><<<(unsigned)(units * G), NT, 0, a.stream>>>(
-                      q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out, a.ds_in,
-                      nullptr, nullptr, b_state, intra_part, d_start, a.H, a.L, a.nseg, G, cps, a.inv_norm, wide));
+        if constexpr (MODE == DECAY_GATE)
+            LA_TRACED(a.tr, "chunk_bwd_dkdv",
+                      bwd_dkdv_gate_kernel<D, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                          q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out,
+                          a.ds_in, nullptr, nullptr, b_state, intra_part, d_start, a.H, a.L, a.nseg, G, cps,
+                          a.inv_norm, wide));
+        else
+            LA_TRACED(a.tr, "chunk_bwd_dkdv",
+                      bwd_dkdv_kernel<D, MODE, false><<<(unsigned)(units * G), NT, 0, a.stream>>>(
+                          q, k, v, d_o, a.decay, a.ds_out, a.state_stride, (__bf16*)a.dk_out, (__bf16*)a.dv_out,
+                          a.ds_in, nullptr, nullptr, b_state, intra_part, d_start, a.H, a.L, a.nseg, G, cps,
+                          a.inv_norm, wide));
         return hipGetLastError();
     };
     hipError_t e;

@@ -43,6 +43,8 @@ _KERNELS = {
     "bwd_dq_kernel": (1, 2, "chunk_bwd_dq"),
     "bwd_dkdv_kernel": (1, 2, "chunk_bwd_dkdv"),
     "bwd_dkdv_head_kernel": (None, None, "chunk_bwd_dkdv"),
+    "bwd_dq_gate_kernel": (None, 1, "chunk_bwd_dq"),
+    "bwd_dkdv_gate_kernel": (None, 1, "chunk_bwd_dkdv"),
     "bwd_dlam_kernel": (None, 1, "chunk_bwd_dlam"),
     "dg_kernel": (None, None, "chunk_bwd_dg"),
 }

@@ -14,12 +14,13 @@ DQ_ST = "_ZN2la12_GLOBAL__N_115pipe_fwd_kernelILi0ELb1ELb1" + _PIPE_ARGS
 DKDV_WIN = "_ZN2la12_GLOBAL__N_115bwd_dkdv_kernelILi128ELi1ELb0ELb1EEEvPKDF16bS3_S3_S3_PKfS5_lPDF16bS6_PfS7_S7_S5_PdS6_lliiifPi"
 DKDV_FACT = "_ZN2la12_GLOBAL__N_115bwd_dkdv_kernelILi128ELi1ELb0ELb0ELb1EEEvPKDF16bS3_S3_S3_PKfS5_lPDF16bS6_PfS7_S7_S5_PdS6_lliiifPi"
 DKDV_HEAD = "_ZN2la12_GLOBAL__N_120bwd_dkdv_head_kernelILi128EEEvPKDF16bS3_S3_S3_PKfS5_lPDF16bS6_PfS7_S7_S5_PdS6_lliiifPi"
+DQ_GATE_ST = "_ZN2la12_GLOBAL__N_118bwd_dq_gate_kernelILi128ELb1EEEvPKDF16bS3_S3_PKfS5_S5_lPDF16bPfS7_S5_liiS3_S7_lliiifPi"
 SCAN = "void la::(anonymous namespace)::state_scan_vec_kernel<5, 4>(float const*, float const*, float*, int, int, int, long, int)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
 def test_labels():
-    names = profsum._demangle([PIPE_OUT, PIPE_ST, DQ_OUT, DQ_ST, DKDV_WIN, DKDV_FACT, DKDV_HEAD, SCAN, COPY])
+    names = profsum._demangle([PIPE_OUT, PIPE_ST, DQ_OUT, DQ_ST, DKDV_WIN, DKDV_FACT, DKDV_HEAD, DQ_GATE_ST, SCAN, COPY])
     assert profsum.label(names[PIPE_OUT]) == ("chunk_fwd_pipe_output_pass", "pipe_fwd_kernel<NONE, outputs>")
     assert profsum.label(names[PIPE_ST]) == ("chunk_fwd_pipe_state_pass", "pipe_fwd_kernel<GATE, state pass>")
     assert profsum.label(names[DQ_OUT]) == ("chunk_bwd_dq", "pipe_fwd_kernel<HEAD, outputs, dq>")
@@ -27,6 +28,7 @@ def test_labels():
     assert profsum.label(names[DKDV_WIN]) == ("chunk_bwd_dkdv_windows", "bwd_dkdv_kernel<128, HEAD, outputs, windows>")
     assert profsum.label(names[DKDV_FACT]) == ("chunk_bwd_dkdv", "bwd_dkdv_kernel<128, HEAD, outputs, factorised>")
     assert profsum.label(names[DKDV_HEAD]) == ("chunk_bwd_dkdv", "bwd_dkdv_head_kernel<128>")
+    assert profsum.label(names[DQ_GATE_ST]) == ("chunk_bwd_dq_state_pass", "bwd_dq_gate_kernel<128, state pass>")
     assert profsum.label(names[SCAN]) == ("state_scan", "state_scan_vec_kernel<5, 4>")
     assert profsum.label(names[COPY])[0] is None
 
